@@ -1,0 +1,216 @@
+"""Planted mistakes in the oracle, on the CPU: each mutant below is a
+plausible slip (a dropped term, a wrong sign or index, min for max, an
+off-by-one window) and must make at least one of the pins fail.  This shows
+the pins can catch what they are meant to catch."""
+from fractions import Fraction
+
+import numpy as np
+import pytest
+
+import oracle.lsa_oracle as O
+import tests.test_oracle_pins as P
+
+
+def _fails(fn, *args):
+    try:
+        fn(*args)
+    except (AssertionError, IndexError, ValueError):
+        return True
+    return False
+
+
+# --- scores ----------------------------------------------------------------
+
+def score_min_not_max(q, kmin, kmax):
+    q = np.asarray(q, float)
+    return sum(np.sum(np.minimum(q[h] * kmax, q[h] * kmin), axis=1) for h in range(q.shape[0]))
+
+
+def score_drops_last_head(q, kmin, kmax):
+    q = np.asarray(q, float)
+    return sum((np.sum(np.maximum(q[h] * kmax, q[h] * kmin), axis=1) for h in range(q.shape[0] - 1)),
+               np.zeros(kmin.shape[0]))
+
+
+def score_kmax_only(q, kmin, kmax):
+    q = np.asarray(q, float)
+    return sum(kmax @ q[h] for h in range(q.shape[0]))
+
+
+def score_max_over_heads(q, kmin, kmax):
+    q = np.asarray(q, float)
+    return np.max([np.sum(np.maximum(q[h] * kmax, q[h] * kmin), axis=1) for h in range(q.shape[0])], axis=0)
+
+
+def score_mean_center(q, kmin, kmax):
+    q = np.asarray(q, float)
+    return sum(((kmin + kmax) / 2) @ q[h] for h in range(q.shape[0]))
+
+
+@pytest.mark.parametrize("mutant", [score_min_not_max, score_drops_last_head, score_kmax_only,
+                                    score_max_over_heads, score_mean_center])
+def test_score_mutants_caught(mutant):
+    caught = (_fails(P.pin_score_is_box_support, mutant)
+              or _fails(P.pin_score_upper_bound, mutant, O.page_stats)
+              or _fails(P.pin_score_special_cases, mutant))
+    assert caught
+
+
+# --- stats -----------------------------------------------------------------
+
+def stats_shifted(keys, n_l):
+    L, D = keys.shape
+    n = -(-L // n_l)
+    kmin = np.array([keys[j * n_l + 1: min((j + 1) * n_l + 1, L)].min(0) if j * n_l + 1 < L
+                     else keys[-1] for j in range(n)])
+    kmax = np.array([keys[j * n_l + 1: min((j + 1) * n_l + 1, L)].max(0) if j * n_l + 1 < L
+                     else keys[-1] for j in range(n)])
+    return kmin, kmax
+
+
+def stats_drop_tail(keys, n_l):
+    L, D = keys.shape
+    n = L // n_l
+    return (np.array([keys[j * n_l:(j + 1) * n_l].min(0) for j in range(n)]),
+            np.array([keys[j * n_l:(j + 1) * n_l].max(0) for j in range(n)]))
+
+
+@pytest.mark.parametrize("mutant", [stats_shifted, stats_drop_tail])
+def test_stats_mutants_caught(mutant):
+    assert _fails(P.pin_stats_brute_force, mutant) or _fails(P.pin_score_upper_bound, O.logical_scores, mutant)
+
+
+# --- physical max ----------------------------------------------------------
+
+def phys_mean(S, g):
+    n = len(S)
+    return np.array([np.mean(S[m * g:min((m + 1) * g, n)]) for m in range(-(-n // g))])
+
+
+def phys_off_by_one(S, g):
+    n = len(S)
+    return np.array([np.max(S[m * g:min((m + 1) * g + 1, n)]) for m in range(-(-n // g))])
+
+
+def phys_drop_tail(S, g):
+    n = len(S)
+    return np.array([np.max(S[m * g:(m + 1) * g]) for m in range(n // g)])
+
+
+@pytest.mark.parametrize("mutant", [phys_mean, phys_off_by_one, phys_drop_tail])
+def test_physical_mutants_caught(mutant):
+    assert _fails(P.pin_physical_is_max, mutant)
+
+
+# --- top-K -----------------------------------------------------------------
+
+def topk_ties_high(P_, k):
+    n = len(P_)
+    order = sorted(range(n), key=lambda m: (-P_[m], -m))
+    out = np.full(k, -1, np.int32)
+    ch = sorted(order[:k])
+    out[:len(ch)] = ch
+    return out
+
+
+def topk_descending_output(P_, k):
+    n = len(P_)
+    order = sorted(range(n), key=lambda m: (-P_[m], m))[:k]
+    out = np.full(k, -1, np.int32)
+    out[:len(order)] = order
+    return out
+
+
+def topk_smallest(P_, k):
+    return O.topk_pages(-np.asarray(P_), k)
+
+
+def topk_k_minus_one(P_, k):
+    out = O.topk_pages(P_, k - 1)
+    return np.concatenate([out, [-1]]).astype(np.int32)
+
+
+@pytest.mark.parametrize("mutant", [topk_ties_high, topk_descending_output, topk_smallest, topk_k_minus_one])
+def test_topk_mutants_caught(mutant):
+    assert _fails(P.pin_topk, mutant)
+
+
+# --- attention and masks ---------------------------------------------------
+
+def attn_no_scale(q, k, v, mask, scale):
+    return O.masked_attention(q, k, v, mask, 1.0)
+
+
+def attn_ignores_mask(q, k, v, mask, scale):
+    return O.masked_attention(q, k, v, np.ones_like(mask), scale)
+
+
+def attn_keys_as_values(q, k, v, mask, scale):
+    idx = np.nonzero(mask)[0]
+    lg = scale * (k[idx] @ q)
+    w = np.exp(lg - lg.max())
+    return (w @ k[idx]) / w.sum()
+
+
+@pytest.mark.parametrize("mutant", [attn_no_scale, attn_ignores_mask, attn_keys_as_values])
+def test_attention_mutants_caught(mutant):
+    assert _fails(P.pin_masked_attention, mutant)
+
+
+def stream_off_by_one(t, ns, nl):
+    p = np.arange(t + 1)
+    return (p < ns) | ((t - p) <= nl)
+
+
+def stream_no_sink(t, ns, nl):
+    p = np.arange(t + 1)
+    return (t - p) < nl
+
+
+def retrieval_without_current(t, sel, n_p):
+    pages = set(int(m) for m in sel if m >= 0)
+    return np.array([(p // n_p) in pages for p in range(t + 1)], dtype=bool)
+
+
+def test_mask_mutants_caught():
+    assert _fails(P.pin_streaming_mask, stream_off_by_one)
+    assert _fails(P.pin_streaming_mask, stream_no_sink)
+    assert _fails(P.pin_retrieval_set, retrieval_without_current)
+
+
+def prefill_local_off_by_one(q, k, v, kind, B, sb, lb, sc, rows=None):
+    return O.prefill_attention(q, k, v, kind, B, sb, lb + 1, sc, rows)
+
+
+def prefill_no_diag_causal(q, k, v, kind, B, sb, lb, sc, rows=None):
+    T, D = q.shape
+    out = np.empty((T, D))
+    n = -(-T // B)
+    for t in range(T):
+        a = t // B
+        cols = [c for c in range(n) if O.tile_visible(a, c, kind, sb, lb)]
+        idx = np.concatenate([np.arange(c * B, min((c + 1) * B, T)) for c in cols])
+        lg = sc * (k[idx] @ q[t])
+        w = np.exp(lg - lg.max())
+        out[t] = (w @ v[idx]) / w.sum()
+    return out
+
+
+@pytest.mark.parametrize("mutant", [prefill_local_off_by_one, prefill_no_diag_causal])
+def test_prefill_mutants_caught(mutant):
+    assert _fails(P.pin_prefill, mutant)
+
+
+def counts_square(n, kind, sb, lb):
+    nnz, _ = O.block_counts(n, kind, sb, lb)
+    return nnz, n * n
+
+
+def speedup_inverted(nnz, dense):
+    r = Fraction(nnz, dense)
+    return r, 1 / (1 - r)
+
+
+def test_accounting_mutants_caught():
+    assert _fails(P.pin_block_accounting, counts_square, O.sparsity_and_speedup)
+    assert _fails(P.pin_block_accounting, O.block_counts, speedup_inverted)

@@ -1,0 +1,361 @@
+"""Pins of the fp64 oracle against facts that do not come from the oracle
+itself: closed forms, brute force, library routines (torch SDPA on the CPU in
+float64), the worked example the LServe explainer prints, and invariants the
+pages state.  Each pin is also run against planted mistakes (see
+test_oracle_mutants.py) to show that it can fail.
+
+CPU only.
+"""
+import itertools
+import json
+import os
+from fractions import Fraction
+
+import numpy as np
+import pytest
+import torch
+
+import oracle.lsa_oracle as O
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+# ---------------------------------------------------------------------------
+# pin helpers (each returns None or raises AssertionError); reused by mutants
+# ---------------------------------------------------------------------------
+
+def pin_score_is_box_support(logical_scores, seed=0):
+    """S^j equals the support function of the box [kmin, kmax] summed over the
+    group's heads: sum_h max over the 2^D box corners x of q_h . x (closed
+    form; checked by enumeration at D <= 9)."""
+    rng = np.random.default_rng(seed)
+    for D, G, n_tok in [(5, 1, 7), (7, 2, 16), (9, 3, 4), (6, 4, 1)]:
+        keys = rng.standard_normal((n_tok, D))
+        q = rng.standard_normal((G, D))
+        kmin, kmax = keys.min(0, keepdims=True), keys.max(0, keepdims=True)
+        corners = np.array(list(itertools.product(*[(kmin[0, i], kmax[0, i]) for i in range(D)])))
+        expect = sum(np.max(corners @ q[h]) for h in range(G))
+        got = logical_scores(q, kmin, kmax)[0]
+        assert abs(got - expect) <= 1e-12 * max(1.0, abs(expect)), (D, G, got, expect)
+
+
+def pin_score_upper_bound(logical_scores, page_stats, seed=1):
+    """The page score upper-bounds sum_h q_h . k for every key of the page
+    (the pages call the score an upper-bound estimate)."""
+    rng = np.random.default_rng(seed)
+    keys = rng.standard_normal((16 * 9 + 5, 24)) * rng.uniform(0.5, 3, size=24)
+    q = rng.standard_normal((4, 24))
+    kmin, kmax = page_stats(keys, 16)
+    S = logical_scores(q, kmin, kmax)
+    for p in range(keys.shape[0]):
+        dot = float(np.sum(q @ keys[p]))
+        assert S[p // 16] >= dot - 1e-9, (p, S[p // 16], dot)
+
+
+def pin_score_special_cases(logical_scores):
+    rng = np.random.default_rng(2)
+    # one-token page: the bound is tight, S = q . k
+    k = rng.standard_normal((1, 32))
+    q = rng.standard_normal((1, 32))
+    assert abs(logical_scores(q, k, k)[0] - float(q[0] @ k[0])) < 1e-12
+    # non-negative query: S = q . kmax
+    keys = rng.standard_normal((16, 32))
+    qp = np.abs(rng.standard_normal((1, 32)))
+    kmin, kmax = keys.min(0, keepdims=True), keys.max(0, keepdims=True)
+    assert abs(logical_scores(qp, kmin, kmax)[0] - float(qp[0] @ kmax[0])) < 1e-12
+    # non-positive query: S = q . kmin
+    assert abs(logical_scores(-qp, kmin, kmax)[0] - float(-qp[0] @ kmin[0])) < 1e-12
+    # a hand example, D = 2, G = 2
+    kmin2 = np.array([[-1.0, 2.0]])
+    kmax2 = np.array([[3.0, 5.0]])
+    q2 = np.array([[2.0, -1.0], [-0.5, 0.25]])
+    # head 0: max(6,-2) + max(-5,-2) = 6 - 2 = 4 ; head 1: max(-1.5,0.5) + max(1.25,0.5) = 0.5+1.25
+    assert logical_scores(q2, kmin2, kmax2)[0] == 4.0 + 1.75
+
+
+def pin_stats_brute_force(page_stats):
+    """Channel min/max per 16-token logical page equal a scalar loop; every
+    key lies inside its page's box; the ragged tail covers only valid tokens."""
+    rng = np.random.default_rng(3)
+    keys = rng.standard_normal((16 * 3 + 7, 5))
+    kmin, kmax = page_stats(keys, 16)
+    assert kmin.shape == (4, 5)
+    for j in range(4):
+        for i in range(5):
+            vals = [keys[p, i] for p in range(keys.shape[0]) if p // 16 == j]
+            assert kmin[j, i] == min(vals) and kmax[j, i] == max(vals)
+    for p in range(keys.shape[0]):
+        assert np.all(kmin[p // 16] <= keys[p]) and np.all(keys[p] <= kmax[p // 16])
+
+
+def pin_physical_is_max(physical_scores):
+    S = np.array([1.0, 5.0, -2.0, 3.0, 7.0, 0.5, 0.25, -9.0, 4.0, 4.0])
+    # g = 4: pages {0..3}, {4..7}, {8, 9} (ragged tail)
+    assert list(physical_scores(S, 4)) == [5.0, 7.0, 4.0]
+    # g = 1 is the page-size-16 special case: physical == logical
+    assert list(physical_scores(S, 1)) == list(S)
+    # g >= n: a single physical page
+    assert list(physical_scores(S, 16)) == [7.0]
+
+
+def _rank_rule(P, K):
+    """Page m is selected iff fewer than K pages beat it, where m' beats m when
+    P[m'] > P[m], or P[m'] == P[m] and m' < m."""
+    n = len(P)
+    chosen = [m for m in range(n)
+              if sum(1 for mm in range(n) if P[mm] > P[m] or (P[mm] == P[m] and mm < m)) < K]
+    out = np.full(K, -1, dtype=np.int32)
+    out[:len(chosen)] = chosen
+    return out
+
+
+def pin_topk(topk_pages, seed=4):
+    rng = np.random.default_rng(seed)
+    for n, K in [(1, 4), (3, 4), (4, 4), (9, 4), (17, 4), (40, 7), (100, 64)]:
+        for trial in range(5):
+            if trial % 2:
+                P = rng.integers(-3, 4, size=n).astype(np.float64)   # many ties
+            else:
+                P = rng.standard_normal(n)
+            assert list(topk_pages(P, K)) == list(_rank_rule(P, K)), (n, K, P)
+    # equal scores everywhere: the K lowest pages
+    assert list(topk_pages(np.zeros(10), 3)) == [0, 1, 2]
+    # K >= n: every page, padded with -1
+    assert list(topk_pages(np.array([2.0, 1.0]), 4)) == [0, 1, -1, -1]
+    # signed zeros are equal scores
+    assert list(topk_pages(np.array([0.0, -0.0, 0.0, -1.0]), 2)) == [0, 1]
+    # brute force over all subsets on a tiny input with distinct scores: the
+    # top-K set is the unique K-subset of maximal score sum
+    P = rng.standard_normal(8)
+    best = max(itertools.combinations(range(8), 3), key=lambda s: sum(P[list(s)]))
+    assert list(topk_pages(P, 3)) == sorted(best)
+
+
+def _sdpa(q, k, v, mask=None, causal=False):
+    """torch's scaled_dot_product_attention on the CPU in float64."""
+    qt = torch.from_numpy(np.ascontiguousarray(q))[None, None]
+    kt = torch.from_numpy(np.ascontiguousarray(k))[None, None]
+    vt = torch.from_numpy(np.ascontiguousarray(v))[None, None]
+    m = None if mask is None else torch.from_numpy(mask)[None, None]
+    o = torch.nn.functional.scaled_dot_product_attention(qt, kt, vt, attn_mask=m, is_causal=causal)
+    return o[0, 0].numpy()
+
+
+def pin_masked_attention(masked_attention, seed=5):
+    rng = np.random.default_rng(seed)
+    L, D = 77, 16
+    k = rng.standard_normal((L, D)) * 2
+    v = rng.standard_normal((L, D))
+    q = rng.standard_normal(D)
+    mask = rng.random(L) < 0.4
+    mask[L - 1] = True
+    got = masked_attention(q, k, v, mask, 1 / np.sqrt(D))
+    ref = _sdpa(q[None], k, v, mask=mask[None])[0]
+    assert np.max(np.abs(got - ref)) < 1e-12
+    # a single visible key returns its value
+    one = np.zeros(L, dtype=bool)
+    one[10] = True
+    assert np.allclose(masked_attention(q, k, v, one, 0.3), v[10], atol=0, rtol=0)
+
+
+def pin_streaming_mask(attended_streaming):
+    for t, ns, nl in [(0, 4, 8), (5, 16, 128), (200, 16, 128), (143, 16, 128), (1039, 16, 128), (50, 0, 1)]:
+        got = attended_streaming(t, ns, nl)
+        expect = np.zeros(t + 1, dtype=bool)
+        expect[:min(ns, t + 1)] = True
+        expect[max(0, t - nl + 1):] = True
+        assert np.array_equal(got, expect), (t, ns, nl)
+        assert got.sum() == min(t + 1, ns + nl) or (ns + nl > t + 1 and got.all())
+
+
+def pin_retrieval_set(attended_retrieval):
+    m = attended_retrieval(200, np.array([0, 2, -1, -1]), 64)
+    expect = np.zeros(201, dtype=bool)
+    expect[0:64] = True
+    expect[128:192] = True
+    expect[192:201] = True        # the current page 200 // 64 = 3 is always read
+    assert np.array_equal(m, expect)
+
+
+def pin_prefill(prefill_attention, seed=6):
+    rng = np.random.default_rng(seed)
+    T, D, B = 200, 8, 16          # 13 tiles, ragged last tile
+    q = rng.standard_normal((T, D))
+    k = rng.standard_normal((T, D))
+    v = rng.standard_normal((T, D))
+    sc = 1 / np.sqrt(D)
+    # retrieval head: dense causal
+    got = prefill_attention(q, k, v, O.RETRIEVAL, B, 1, 2, sc)
+    assert np.max(np.abs(got - _sdpa(q, k, v, causal=True))) < 1e-12
+    # streaming with a local window covering all tiles: dense causal
+    got = prefill_attention(q, k, v, O.STREAMING, B, 0, 13, sc)
+    assert np.max(np.abs(got - _sdpa(q, k, v, causal=True))) < 1e-12
+    # streaming Lambda (1 sink tile, 3 local tiles): explicit boolean mask
+    tq = np.arange(T)[:, None]
+    tk = np.arange(T)[None, :]
+    a, c = tq // B, tk // B
+    mask = (tk <= tq) & ((c < 1) | ((a - c) < 3))
+    got = prefill_attention(q, k, v, O.STREAMING, B, 1, 3, sc)
+    assert np.max(np.abs(got - _sdpa(q, k, v, mask=mask))) < 1e-12
+
+
+def pin_block_accounting(block_counts, sparsity_and_speedup):
+    with open(os.path.join(GOLDEN, "block_mask_10_of_21.json")) as f:
+        g = json.load(f)
+    n = g["n_blocks"]
+    nnz = len(g["nonempty"])
+    assert n * (n + 1) // 2 == g["expected_total"] and nnz == g["expected_nonempty"]
+    r, speed = sparsity_and_speedup(nnz, n * (n + 1) // 2)
+    assert speed == Fraction(g["expected_speedup_num"], g["expected_speedup_den"])
+    assert r == Fraction(11, 21)
+    # causal retrieval heads: every causal tile
+    assert block_counts(2048, O.RETRIEVAL, 1, 16) == (2048 * 2049 // 2, 2048 * 2049 // 2)
+    # Lambda with 1 sink + 16 local tiles: rows 0..15 keep all a+1 tiles, later rows 17
+    assert block_counts(2048, O.STREAMING, 1, 16)[0] == sum(range(1, 17)) + (2048 - 16) * 17
+
+
+# ---------------------------------------------------------------------------
+# the pins on the real oracle
+# ---------------------------------------------------------------------------
+
+def test_score_is_box_support():
+    pin_score_is_box_support(O.logical_scores)
+
+
+def test_score_upper_bound():
+    pin_score_upper_bound(O.logical_scores, O.page_stats)
+
+
+def test_score_special_cases():
+    pin_score_special_cases(O.logical_scores)
+
+
+def test_stats_brute_force():
+    pin_stats_brute_force(O.page_stats)
+
+
+def test_physical_is_max():
+    pin_physical_is_max(O.physical_scores)
+
+
+def test_topk():
+    pin_topk(O.topk_pages)
+
+
+def test_masked_attention_vs_sdpa():
+    pin_masked_attention(O.masked_attention)
+
+
+def test_streaming_mask():
+    pin_streaming_mask(O.attended_streaming)
+
+
+def test_retrieval_set():
+    pin_retrieval_set(O.attended_retrieval)
+
+
+def test_prefill_vs_sdpa():
+    pin_prefill(O.prefill_attention)
+
+
+def test_block_accounting_golden():
+    pin_block_accounting(O.block_counts, O.sparsity_and_speedup)
+
+
+def test_prefill_mask_matches_tile_rule():
+    m = O.prefill_mask(100, 16, O.STREAMING, 1, 2)
+    for t in range(100):
+        for p in range(100):
+            a, c = t // 16, p // 16
+            assert m[t, p] == (p <= t and (c < 1 or a - c < 2))
+
+
+# ---------------------------------------------------------------------------
+# decode-level pins: full budget is dense causal attention; reuse semantics
+# ---------------------------------------------------------------------------
+
+def _rand_seq(rng, L, H_kv, D):
+    return ([rng.standard_normal((L, D)) for _ in range(H_kv)],
+            [rng.standard_normal((L, D)) for _ in range(H_kv)])
+
+
+def test_full_budget_decode_is_dense_causal():
+    rng = np.random.default_rng(7)
+    H_q, H_kv, D = 4, 2, 16
+    spec = O.DecodeSpec(H_q, H_kv, [O.RETRIEVAL, O.STREAMING], 16, 64,
+                        token_budget=64 * 8, reuse_interval=4, sink_tokens=300, local_tokens=300)
+    L0 = 400
+    keys, values = _rand_seq(rng, L0 + 6, H_kv, D)
+    sel = None
+    for i in range(6):
+        L = L0 + i + 1
+        q = rng.standard_normal((H_q, D))
+        o, sel = O.decode_step(spec, q, [k[:L] for k in keys], [v[:L] for v in values], sel, i % 4 == 0)
+        for h in range(H_q):
+            kv = h // 2
+            ref = _sdpa(q[h][None], keys[kv][:L], values[kv][:L])[0]
+            assert np.max(np.abs(o[h] - ref)) < 1e-12, (i, h)
+
+
+def test_reuse_interval_semantics():
+    """With R = 4 the selection used at step i is the one computed at step
+    4*floor(i/4) with that step's query; R = 1 reselects every step."""
+    rng = np.random.default_rng(8)
+    H_q, H_kv, D = 2, 1, 8
+    L0 = 300
+    keys, values = _rand_seq(rng, L0 + 8, H_kv, D)
+    qs = [rng.standard_normal((H_q, D)) for _ in range(8)]
+    spec4 = O.DecodeSpec(H_q, H_kv, [O.RETRIEVAL], 16, 32, 64, 4, 0, 0)
+    spec1 = O.DecodeSpec(H_q, H_kv, [O.RETRIEVAL], 16, 32, 64, 1, 0, 0)
+    sel4 = sel1 = None
+    history1 = []
+    for i in range(8):
+        L = L0 + i + 1
+        ks, vs = [keys[0][:L]], [values[0][:L]]
+        _, sel4 = O.decode_step(spec4, qs[i], ks, vs, sel4, i % 4 == 0)
+        _, sel1 = O.decode_step(spec1, qs[i], ks, vs, sel1, True)
+        history1.append(sel1.copy())
+        assert np.array_equal(sel4, history1[4 * (i // 4)])
+
+
+def test_int4_dequant_exact_and_stats_commute():
+    """(c - z) * s is exact in float32 when z is a multiple of 1/16 in [0, 15]
+    and s is an fp16 value; dequantising the code min/max equals the min/max
+    of the dequantised keys (dequantisation is increasing for s > 0)."""
+    rng = np.random.default_rng(9)
+    codes = rng.integers(0, 16, size=(16 * 4 + 3, 32)).astype(np.uint8)
+    for _ in range(20):
+        s = float(np.float16(rng.uniform(0.01, 2.0)))
+        z = float(rng.integers(0, 241)) / 16.0
+        x64 = O.dequant_int4(codes, s, z)
+        x32 = (codes.astype(np.float32) - np.float32(z)) * np.float32(s)
+        assert np.array_equal(x32.astype(np.float64), x64)
+        cmin, cmax = O.page_code_stats(codes, 16)
+        kmin, kmax = O.page_stats(x64, 16)
+        assert np.array_equal(O.dequant_int4(cmin, s, z), kmin)
+        assert np.array_equal(O.dequant_int4(cmax, s, z), kmax)
+
+
+def test_conversions_exact():
+    # bf16 bits of a few exactly known values
+    bits = np.array([0x3F80, 0xC000, 0x0000, 0x8000, 0x3EAB, 0x7F7F], dtype=np.uint16)
+    got = O.bf16_bits_to_f64(bits)
+    assert got[0] == 1.0 and got[1] == -2.0 and got[2] == 0.0
+    assert got[4] == float(torch.tensor([0x3EAB], dtype=torch.int16).view(torch.bfloat16).double()[0])
+    assert got[5] == float(torch.finfo(torch.bfloat16).max)
+    assert O.fp16_bits_to_f64(np.array([0x3C00, 0x3800], np.uint16)).tolist() == [1.0, 0.5]
+    assert O.unpack_int4(np.array([[0x21, 0xF3]], np.uint8)).tolist() == [[1, 2, 3, 15]]
+
+
+def test_pool_gather_follows_page_table():
+    rng = np.random.default_rng(10)
+    P, H, NP, D = 5, 2, 4, 3
+    k = rng.standard_normal((P, H, NP, D)).astype(np.float32)
+    v = rng.standard_normal((P, H, D, NP)).astype(np.float32)
+    pool = O.Pool("f32", k, v, NP, D)
+    table = [3, 0, 4]
+    K = pool.keys(table, 1, 10)
+    V = pool.values(table, 1, 10)
+    for p in range(10):
+        assert np.array_equal(K[p], k[table[p // NP], 1, p % NP])
+        assert np.array_equal(V[p], v[table[p // NP], 1, :, p % NP])
