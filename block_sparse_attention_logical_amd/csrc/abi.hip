@@ -1,0 +1,376 @@
+// Host side of the C ABI declared in include/lsa.h: argument validation,
+// workspace sizing, work decomposition and kernel dispatch.  Nothing here
+// allocates device memory or synchronises the host.
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <string>
+
+#include "lsa_internal.h"
+
+namespace lsa {
+namespace {
+
+thread_local std::string g_last_error;
+
+lsa_status fail(lsa_status code, const char *fmt, ...) {
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    std::vsnprintf(buf, sizeof(buf), fmt, ap);
+    va_end(ap);
+    g_last_error = buf;
+    return code;
+}
+
+lsa_status ok() {
+    g_last_error.clear();
+    return LSA_OK;
+}
+
+lsa_status from_hip(hipError_t e, const char *what) {
+    if (e == hipSuccess) return ok();
+    return fail(LSA_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+constexpr size_t kAlign = 256;
+size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+bool is_pow2(int x) { return x > 0 && (x & (x - 1)) == 0; }
+
+lsa_status check_kv(const lsa_kv *kv) {
+    if (!kv) return fail(LSA_ERR_INVALID_ARG, "kv descriptor is NULL");
+    if (kv->kv_dtype != LSA_F32 && kv->kv_dtype != LSA_BF16 && kv->kv_dtype != LSA_INT4)
+        return fail(LSA_ERR_INVALID_ARG, "kv_dtype %d is not LSA_F32, LSA_BF16 or LSA_INT4", kv->kv_dtype);
+    if (kv->reserved != 0) return fail(LSA_ERR_INVALID_ARG, "kv->reserved must be 0");
+    if (kv->num_kv_heads < 1 || kv->num_kv_heads > kMaxKvHeads)
+        return fail(LSA_ERR_UNSUPPORTED, "num_kv_heads %d outside [1, %d]", kv->num_kv_heads, kMaxKvHeads);
+    if (kv->head_dim != 64 && kv->head_dim != 128)
+        return fail(LSA_ERR_UNSUPPORTED, "head_dim %d is not 64 or 128", kv->head_dim);
+    if (kv->logical_page != 8 && kv->logical_page != 16 && kv->logical_page != 32 && kv->logical_page != 64)
+        return fail(LSA_ERR_UNSUPPORTED, "logical_page %d is not 8, 16, 32 or 64", kv->logical_page);
+    if (kv->page_size < kv->logical_page || kv->page_size % kv->logical_page != 0)
+        return fail(LSA_ERR_INVALID_ARG, "page_size %d is not a multiple of logical_page %d", kv->page_size,
+                    kv->logical_page);
+    if (kv->page_size % 32 != 0 || kv->page_size > 256 || !is_pow2(kv->page_size / kv->logical_page))
+        return fail(LSA_ERR_UNSUPPORTED, "page_size %d: need a multiple of 32, at most 256, with a power-of-two "
+                    "number of logical pages", kv->page_size);
+    if (kv->num_pages < 1) return fail(LSA_ERR_INVALID_ARG, "num_pages must be >= 1");
+    if (!kv->k || !kv->v) return fail(LSA_ERR_INVALID_ARG, "kv->k and kv->v must be non-NULL");
+    if (kv->kv_dtype == LSA_INT4) {
+        if (!kv->k_sz || !kv->v_sz) return fail(LSA_ERR_INVALID_ARG, "int4 pool needs k_sz and v_sz");
+    } else if (kv->k_sz || kv->v_sz) {
+        return fail(LSA_ERR_INVALID_ARG, "k_sz / v_sz are for int4 pools only");
+    }
+    return LSA_OK;
+}
+
+lsa_status check_seqs(const lsa_seqs *sq) {
+    if (!sq) return fail(LSA_ERR_INVALID_ARG, "seqs descriptor is NULL");
+    if (sq->batch < 0) return fail(LSA_ERR_INVALID_ARG, "batch %d < 0", sq->batch);
+    if (sq->max_pages < 1 || sq->max_pages > 65535)
+        return fail(LSA_ERR_UNSUPPORTED, "max_pages %d outside [1, 65535]", sq->max_pages);
+    if (sq->batch > 0 && (!sq->page_table || !sq->seq_lens))
+        return fail(LSA_ERR_INVALID_ARG, "page_table and seq_lens must be non-NULL");
+    return LSA_OK;
+}
+
+lsa_status check_heads(const lsa_heads *hd, const lsa_kv *kv, bool need) {
+    if (!hd) return need ? fail(LSA_ERR_INVALID_ARG, "heads descriptor is NULL") : LSA_OK;
+    if (!hd->head_kind) return fail(LSA_ERR_INVALID_ARG, "heads->head_kind is NULL");
+    if (hd->num_q_heads < 1 || hd->num_q_heads % kv->num_kv_heads != 0)
+        return fail(LSA_ERR_INVALID_ARG, "num_q_heads %d is not a positive multiple of num_kv_heads %d",
+                    hd->num_q_heads, kv->num_kv_heads);
+    if (hd->num_q_heads / kv->num_kv_heads > 16)
+        return fail(LSA_ERR_UNSUPPORTED, "GQA group size %d > 16", hd->num_q_heads / kv->num_kv_heads);
+    for (int i = 0; i < kv->num_kv_heads; ++i)
+        if (hd->head_kind[i] > 1) return fail(LSA_ERR_INVALID_ARG, "head_kind[%d] = %d is not 0 or 1", i, hd->head_kind[i]);
+    if (hd->sink_tokens < 0 || hd->local_tokens < 1)
+        return fail(LSA_ERR_INVALID_ARG, "need sink_tokens >= 0 and local_tokens >= 1");
+    if (hd->sink_blocks < 0 || hd->local_blocks < 1)
+        return fail(LSA_ERR_INVALID_ARG, "need sink_blocks >= 0 and local_blocks >= 1");
+    return LSA_OK;
+}
+
+int count_kind(const lsa_heads *hd, int h_kv, int kind) {
+    int n = 0;
+    for (int i = 0; i < h_kv; ++i) n += hd->head_kind[i] == kind;
+    return n;
+}
+
+constexpr int kPagesPerWave = 1;       // decode: pages per wavefront
+constexpr int kScorePagesPerBlock = 16;
+
+struct DecodeGeom {
+    int K, chunks_ret, chunks_str, chunks_max, rec_floats;
+};
+
+DecodeGeom decode_geometry(const lsa_kv *kv, const lsa_heads *hd, int token_budget) {
+    DecodeGeom g;
+    g.K = token_budget / kv->page_size;
+    const int per_chunk = 4 * kPagesPerWave;
+    const int NP = kv->page_size;
+    const int ret_pages = g.K + 1;
+    const int str_pages = (hd->sink_tokens + NP - 1) / NP + (hd->local_tokens - 1) / NP + 2;
+    g.chunks_ret = (ret_pages + per_chunk - 1) / per_chunk;
+    g.chunks_str = (str_pages + per_chunk - 1) / per_chunk;
+    g.chunks_max = std::max(g.chunks_ret, g.chunks_str);
+    g.rec_floats = 32 + (hd->num_q_heads / kv->num_kv_heads) * kv->head_dim;
+    return g;
+}
+
+}  // namespace
+}  // namespace lsa
+
+using namespace lsa;
+
+extern "C" {
+
+const char *lsa_last_error(void) { return g_last_error.c_str(); }
+
+const char *lsa_version(void) { return "lsa 0.1.0 gfx950"; }
+
+lsa_status lsa_page_stats_bytes(const lsa_kv *kv, size_t *bytes) {
+    if (lsa_status s = check_kv(kv)) return s;
+    if (!bytes) return fail(LSA_ERR_INVALID_ARG, "bytes is NULL");
+    const size_t g = kv->page_size / kv->logical_page;
+    const size_t per = kv->kv_dtype == LSA_INT4 ? (size_t)kv->head_dim
+                                                 : 2 * (size_t)kv->head_dim * (kv->kv_dtype == LSA_F32 ? 4 : 2);
+    *bytes = (size_t)kv->num_pages * kv->num_kv_heads * g * per;
+    return ok();
+}
+
+lsa_status lsa_build_page_stats(const lsa_kv *kv, const lsa_seqs *seqs, const lsa_heads *heads,
+                                const int32_t *first_token, int32_t max_new_tokens, void *stats,
+                                void *stream) {
+    if (lsa_status s = check_kv(kv)) return s;
+    if (lsa_status s = check_seqs(seqs)) return s;
+    if (lsa_status s = check_heads(heads, kv, false)) return s;
+    if (!stats) return fail(LSA_ERR_INVALID_ARG, "stats is NULL");
+    if (max_new_tokens < 0) return fail(LSA_ERR_INVALID_ARG, "max_new_tokens < 0");
+    StatsArgs a{};
+    a.k = kv->k;
+    a.k_sz = kv->k_sz;
+    a.stats = stats;
+    a.page_table = seqs->page_table;
+    a.seq_lens = seqs->seq_lens;
+    a.first_token = first_token;
+    a.batch = seqs->batch;
+    a.max_pages = seqs->max_pages;
+    a.num_kv_heads = kv->num_kv_heads;
+    a.head_dim = kv->head_dim;
+    a.page_size = kv->page_size;
+    a.logical_page = kv->logical_page;
+    a.dtype = kv->kv_dtype;
+    a.n_heads_sel = 0;
+    for (int i = 0; i < kv->num_kv_heads; ++i)
+        if (!heads || heads->head_kind[i] == LSA_RETRIEVAL_HEAD) a.heads_sel[a.n_heads_sel++] = (uint8_t)i;
+    const long long full = (long long)seqs->max_pages * (kv->page_size / kv->logical_page);
+    long long lp = full;
+    if (first_token) {
+        const long long span = max_new_tokens > 0 ? max_new_tokens : (long long)seqs->max_pages * kv->page_size;
+        lp = std::min(full, (span + kv->logical_page - 1) / kv->logical_page + 1);
+    }
+    a.lp_per_seq = (int32_t)lp;
+    if ((long long)a.batch * a.n_heads_sel * lp > (long long)INT32_MAX)
+        return fail(LSA_ERR_UNSUPPORTED, "statistics launch too large");
+    return from_hip(launch_stats(a, (hipStream_t)stream), "build_page_stats launch");
+}
+
+lsa_status lsa_select_pages_workspace(const lsa_kv *kv, const lsa_seqs *seqs, const lsa_heads *heads,
+                                      size_t *bytes) {
+    if (lsa_status s = check_kv(kv)) return s;
+    if (lsa_status s = check_seqs(seqs)) return s;
+    if (lsa_status s = check_heads(heads, kv, true)) return s;
+    if (!bytes) return fail(LSA_ERR_INVALID_ARG, "bytes is NULL");
+    *bytes = align_up((size_t)seqs->batch * kv->num_kv_heads * seqs->max_pages * sizeof(double));
+    return ok();
+}
+
+lsa_status lsa_select_pages(const void *q, int32_t q_dtype, const lsa_kv *kv, const void *stats,
+                            const lsa_seqs *seqs, const lsa_heads *heads, int32_t token_budget,
+                            int32_t decode_step, int32_t reuse_interval, int32_t *selected,
+                            void *workspace, size_t workspace_bytes, void *stream) {
+    if (lsa_status s = check_kv(kv)) return s;
+    if (lsa_status s = check_seqs(seqs)) return s;
+    if (lsa_status s = check_heads(heads, kv, true)) return s;
+    if (q_dtype != LSA_F32 && q_dtype != LSA_BF16)
+        return fail(LSA_ERR_INVALID_ARG, "q_dtype %d is not LSA_F32 or LSA_BF16", q_dtype);
+    if (token_budget < kv->page_size || token_budget % kv->page_size != 0)
+        return fail(LSA_ERR_INVALID_ARG, "token_budget %d is not a positive multiple of page_size %d", token_budget,
+                    kv->page_size);
+    if (reuse_interval < 1) return fail(LSA_ERR_INVALID_ARG, "reuse_interval %d < 1", reuse_interval);
+    if (decode_step < 0) return fail(LSA_ERR_INVALID_ARG, "decode_step %d < 0", decode_step);
+    if (!q || !stats || !selected) return fail(LSA_ERR_INVALID_ARG, "q, stats and selected must be non-NULL");
+    size_t need = 0;
+    lsa_select_pages_workspace(kv, seqs, heads, &need);
+    if (!workspace || workspace_bytes < need)
+        return fail(LSA_ERR_WORKSPACE, "workspace of %zu bytes, need %zu", workspace_bytes, need);
+    if (decode_step % reuse_interval != 0) return ok();     // reuse the previous selection
+    const int n_ret = count_kind(heads, kv->num_kv_heads, LSA_RETRIEVAL_HEAD);
+    if (n_ret == 0 || seqs->batch == 0) return ok();
+
+    ScoreArgs sa{};
+    sa.q = q;
+    sa.stats = stats;
+    sa.k_sz = kv->k_sz;
+    sa.page_table = seqs->page_table;
+    sa.seq_lens = seqs->seq_lens;
+    sa.phys = static_cast<double *>(workspace);
+    sa.batch = seqs->batch;
+    sa.max_pages = seqs->max_pages;
+    sa.num_q_heads = heads->num_q_heads;
+    sa.num_kv_heads = kv->num_kv_heads;
+    sa.head_dim = kv->head_dim;
+    sa.page_size = kv->page_size;
+    sa.logical_page = kv->logical_page;
+    sa.q_dtype = q_dtype;
+    sa.kv_dtype = kv->kv_dtype;
+    sa.n_ret = 0;
+    for (int i = 0; i < kv->num_kv_heads; ++i)
+        if (heads->head_kind[i] == LSA_RETRIEVAL_HEAD) sa.ret_heads[sa.n_ret++] = (uint8_t)i;
+    sa.pages_per_block = kScorePagesPerBlock;
+    sa.blocks_per_head = (seqs->max_pages + kScorePagesPerBlock - 1) / kScorePagesPerBlock;
+    if (lsa_status s = from_hip(launch_score(sa, (hipStream_t)stream), "select_pages score launch")) return s;
+
+    TopkArgs ta{};
+    ta.phys = sa.phys;
+    ta.seq_lens = seqs->seq_lens;
+    ta.selected = selected;
+    ta.batch = seqs->batch;
+    ta.max_pages = seqs->max_pages;
+    ta.num_kv_heads = kv->num_kv_heads;
+    ta.page_size = kv->page_size;
+    ta.k = token_budget / kv->page_size;
+    ta.n_ret = sa.n_ret;
+    std::memcpy(ta.ret_heads, sa.ret_heads, sizeof(ta.ret_heads));
+    return from_hip(launch_topk(ta, (hipStream_t)stream), "select_pages top-K launch");
+}
+
+lsa_status lsa_decode_workspace(const lsa_kv *kv, const lsa_seqs *seqs, const lsa_heads *heads,
+                                int32_t token_budget, size_t *bytes) {
+    if (lsa_status s = check_kv(kv)) return s;
+    if (lsa_status s = check_seqs(seqs)) return s;
+    if (lsa_status s = check_heads(heads, kv, true)) return s;
+    if (!bytes) return fail(LSA_ERR_INVALID_ARG, "bytes is NULL");
+    if (token_budget < kv->page_size || token_budget % kv->page_size != 0)
+        return fail(LSA_ERR_INVALID_ARG, "token_budget %d is not a positive multiple of page_size %d", token_budget,
+                    kv->page_size);
+    const DecodeGeom g = decode_geometry(kv, heads, token_budget);
+    *bytes = align_up((size_t)seqs->batch * kv->num_kv_heads * g.chunks_max * g.rec_floats * sizeof(float));
+    return ok();
+}
+
+lsa_status lsa_sparse_decode_attn(const void *q, int32_t q_dtype, const lsa_kv *kv, const lsa_seqs *seqs,
+                                  const lsa_heads *heads, const int32_t *selected, int32_t token_budget,
+                                  float softmax_scale, void *out, void *workspace, size_t workspace_bytes,
+                                  void *stream) {
+    if (lsa_status s = check_kv(kv)) return s;
+    if (lsa_status s = check_seqs(seqs)) return s;
+    if (lsa_status s = check_heads(heads, kv, true)) return s;
+    const bool pair_ok = (q_dtype == LSA_F32 && kv->kv_dtype == LSA_F32) ||
+                         (q_dtype == LSA_BF16 && kv->kv_dtype == LSA_BF16);
+    if (q_dtype == LSA_BF16 && kv->kv_dtype == LSA_INT4)
+        return fail(LSA_ERR_UNSUPPORTED, "int4 decode attention is not built in this library version");
+    if (!pair_ok)
+        return fail(LSA_ERR_UNSUPPORTED, "(q_dtype %d, kv_dtype %d) is not a supported pair", q_dtype, kv->kv_dtype);
+    if (!q || !out) return fail(LSA_ERR_INVALID_ARG, "q and out must be non-NULL");
+    const int n_ret = count_kind(heads, kv->num_kv_heads, LSA_RETRIEVAL_HEAD);
+    if (n_ret > 0 && !selected) return fail(LSA_ERR_INVALID_ARG, "selected is NULL but retrieval heads exist");
+    if (!(softmax_scale >= 0.f) || std::isinf(softmax_scale))
+        return fail(LSA_ERR_INVALID_ARG, "softmax_scale must be finite and >= 0");
+    size_t need = 0;
+    if (lsa_status s = lsa_decode_workspace(kv, seqs, heads, token_budget, &need)) return s;
+    if (!workspace || workspace_bytes < need)
+        return fail(LSA_ERR_WORKSPACE, "workspace of %zu bytes, need %zu", workspace_bytes, need);
+    if (seqs->batch == 0) return ok();
+
+    const DecodeGeom g = decode_geometry(kv, heads, token_budget);
+    DecodeArgs a{};
+    a.q = q;
+    a.out = out;
+    a.k = kv->k;
+    a.v = kv->v;
+    a.k_sz = kv->k_sz;
+    a.v_sz = kv->v_sz;
+    a.page_table = seqs->page_table;
+    a.seq_lens = seqs->seq_lens;
+    a.selected = selected;
+    a.part = static_cast<float *>(workspace);
+    a.batch = seqs->batch;
+    a.max_pages = seqs->max_pages;
+    a.num_q_heads = heads->num_q_heads;
+    a.num_kv_heads = kv->num_kv_heads;
+    a.group = heads->num_q_heads / kv->num_kv_heads;
+    a.head_dim = kv->head_dim;
+    a.page_size = kv->page_size;
+    a.sel_k = g.K;
+    a.sink = heads->sink_tokens;
+    a.local = heads->local_tokens;
+    a.chunks_ret = g.chunks_ret;
+    a.chunks_str = g.chunks_str;
+    a.chunks_max = g.chunks_max;
+    a.chunks_per_seq = n_ret * g.chunks_ret + (kv->num_kv_heads - n_ret) * g.chunks_str;
+    a.pages_per_wave = kPagesPerWave;
+    const float scale = softmax_scale > 0.f ? softmax_scale : 1.f / std::sqrt((float)kv->head_dim);
+    a.scale_log2 = scale * 1.4426950408889634f;
+    for (int i = 0; i < kv->num_kv_heads; ++i) a.kind[i] = heads->head_kind[i];
+    if (lsa_status s = from_hip(launch_decode(a, q_dtype, kv->kv_dtype, (hipStream_t)stream), "decode launch"))
+        return s;
+    return from_hip(launch_combine(a, q_dtype, (hipStream_t)stream), "decode combine launch");
+}
+
+lsa_status lsa_sparse_prefill_attn(const void *q, int32_t q_dtype, const lsa_kv *kv, const int32_t *page_table,
+                                   int32_t seq_len, const lsa_heads *heads, int32_t block, float softmax_scale,
+                                   void *out, int64_t *tile_counter, void *stream) {
+    if (lsa_status s = check_kv(kv)) return s;
+    if (lsa_status s = check_heads(heads, kv, true)) return s;
+    if (block != 64) return fail(LSA_ERR_UNSUPPORTED, "block %d: only 64-token tiles are built", block);
+    if (kv->page_size % 64 != 0)
+        return fail(LSA_ERR_UNSUPPORTED, "prefill needs page_size a multiple of 64 (got %d)", kv->page_size);
+    const bool pair_ok = (q_dtype == LSA_F32 && kv->kv_dtype == LSA_F32) ||
+                         (q_dtype == LSA_BF16 && kv->kv_dtype == LSA_BF16);
+    if (!pair_ok)
+        return fail(LSA_ERR_UNSUPPORTED, "(q_dtype %d, kv_dtype %d) is not a supported prefill pair", q_dtype,
+                    kv->kv_dtype);
+    if (q_dtype == LSA_F32 && kv->head_dim != 64)
+        return fail(LSA_ERR_UNSUPPORTED, "f32 prefill is built for head_dim 64 only");
+    if (seq_len < 0) return fail(LSA_ERR_INVALID_ARG, "seq_len %d < 0", seq_len);
+    if (!q || !out || (seq_len > 0 && !page_table))
+        return fail(LSA_ERR_INVALID_ARG, "q, out and page_table must be non-NULL");
+    if (!(softmax_scale >= 0.f) || std::isinf(softmax_scale))
+        return fail(LSA_ERR_INVALID_ARG, "softmax_scale must be finite and >= 0");
+    if (seq_len == 0) return ok();
+    PrefillArgs p{};
+    p.q = q;
+    p.out = out;
+    p.k = kv->k;
+    p.v = kv->v;
+    p.page_table = page_table;
+    p.tile_counter = reinterpret_cast<unsigned long long *>(tile_counter);
+    p.seq_len = seq_len;
+    p.num_q_heads = heads->num_q_heads;
+    p.num_kv_heads = kv->num_kv_heads;
+    p.group = heads->num_q_heads / kv->num_kv_heads;
+    p.head_dim = kv->head_dim;
+    p.page_size = kv->page_size;
+    p.sink_blocks = heads->sink_blocks;
+    p.local_blocks = heads->local_blocks;
+    p.n_qblocks = (seq_len + 63) / 64;
+    p.head_groups = (p.group + 3) / 4;
+    p.n_ret = 0;
+    p.n_str = 0;
+    for (int i = 0; i < kv->num_kv_heads; ++i) {
+        if (heads->head_kind[i] == LSA_RETRIEVAL_HEAD) p.ret_heads[p.n_ret++] = (uint8_t)i;
+        else p.str_heads[p.n_str++] = (uint8_t)i;
+    }
+    const long long items = (long long)kv->num_kv_heads * p.n_qblocks * p.head_groups;
+    if (items > (long long)INT32_MAX) return fail(LSA_ERR_UNSUPPORTED, "prefill launch too large");
+    p.n_items = (int32_t)items;
+    const float scale = softmax_scale > 0.f ? softmax_scale : 1.f / std::sqrt((float)kv->head_dim);
+    p.scale_log2 = scale * 1.4426950408889634f;
+    return from_hip(launch_prefill(p, q_dtype, (hipStream_t)stream), "prefill launch");
+}
+
+}  // extern "C"

@@ -1,0 +1,254 @@
+"""ctypes binding of liblsa (include/lsa.h): argument marshalling only.
+
+Every step of the attention path runs in the HIP library; this module turns
+torch tensors into the C descriptors, picks the caller's current stream and
+raises LsaError when a call returns a negative status.  There is no fallback:
+if liblsa.so is missing the first call raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass, field
+from typing import Optional, Sequence
+
+import torch
+
+F32, BF16, INT4 = 0, 1, 2
+RETRIEVAL, STREAMING = 0, 1
+
+LSA_OK = 0
+LSA_ERR_INVALID_ARG = -1
+LSA_ERR_UNSUPPORTED = -2
+LSA_ERR_WORKSPACE = -3
+LSA_ERR_HIP = -4
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "liblsa.so")
+
+# every function include/lsa.h declares
+EXPORTED = (
+    "lsa_page_stats_bytes",
+    "lsa_build_page_stats",
+    "lsa_select_pages_workspace",
+    "lsa_select_pages",
+    "lsa_decode_workspace",
+    "lsa_sparse_decode_attn",
+    "lsa_sparse_prefill_attn",
+    "lsa_last_error",
+    "lsa_version",
+)
+
+
+class LsaError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"lsa status {status}: {message}")
+        self.status = status
+
+
+class LsaKV(ctypes.Structure):
+    _fields_ = [
+        ("kv_dtype", ctypes.c_int32),
+        ("num_kv_heads", ctypes.c_int32),
+        ("head_dim", ctypes.c_int32),
+        ("page_size", ctypes.c_int32),
+        ("logical_page", ctypes.c_int32),
+        ("reserved", ctypes.c_int32),
+        ("num_pages", ctypes.c_int64),
+        ("k", ctypes.c_void_p),
+        ("v", ctypes.c_void_p),
+        ("k_sz", ctypes.c_void_p),
+        ("v_sz", ctypes.c_void_p),
+    ]
+
+
+class LsaSeqs(ctypes.Structure):
+    _fields_ = [
+        ("batch", ctypes.c_int32),
+        ("max_pages", ctypes.c_int32),
+        ("page_table", ctypes.c_void_p),
+        ("seq_lens", ctypes.c_void_p),
+    ]
+
+
+class LsaHeads(ctypes.Structure):
+    _fields_ = [
+        ("head_kind", ctypes.c_void_p),
+        ("num_q_heads", ctypes.c_int32),
+        ("sink_tokens", ctypes.c_int32),
+        ("local_tokens", ctypes.c_int32),
+        ("sink_blocks", ctypes.c_int32),
+        ("local_blocks", ctypes.c_int32),
+    ]
+
+
+_lib = None
+
+
+def load(path: str = LIB_PATH) -> ctypes.CDLL:
+    """Load liblsa.so once.  torch is imported first so that the library binds
+    to the HIP runtime torch already loaded (same soname)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} is not built; run `python -m block_sparse_attention_logical_amd.build`")
+    lib = ctypes.CDLL(path)
+    P = ctypes.POINTER
+    st = ctypes.c_int32
+    vp = ctypes.c_void_p
+    sz = P(ctypes.c_size_t)
+    lib.lsa_page_stats_bytes.argtypes = [P(LsaKV), sz]
+    lib.lsa_build_page_stats.argtypes = [P(LsaKV), P(LsaSeqs), P(LsaHeads), vp, ctypes.c_int32, vp, vp]
+    lib.lsa_select_pages_workspace.argtypes = [P(LsaKV), P(LsaSeqs), P(LsaHeads), sz]
+    lib.lsa_select_pages.argtypes = [vp, ctypes.c_int32, P(LsaKV), vp, P(LsaSeqs), P(LsaHeads), ctypes.c_int32,
+                                     ctypes.c_int32, ctypes.c_int32, vp, vp, ctypes.c_size_t, vp]
+    lib.lsa_decode_workspace.argtypes = [P(LsaKV), P(LsaSeqs), P(LsaHeads), ctypes.c_int32, sz]
+    lib.lsa_sparse_decode_attn.argtypes = [vp, ctypes.c_int32, P(LsaKV), P(LsaSeqs), P(LsaHeads), vp,
+                                           ctypes.c_int32, ctypes.c_float, vp, vp, ctypes.c_size_t, vp]
+    lib.lsa_sparse_prefill_attn.argtypes = [vp, ctypes.c_int32, P(LsaKV), vp, ctypes.c_int32, P(LsaHeads),
+                                            ctypes.c_int32, ctypes.c_float, vp, vp, vp]
+    for name in EXPORTED[:-2]:
+        getattr(lib, name).restype = st
+    lib.lsa_last_error.restype = ctypes.c_char_p
+    lib.lsa_last_error.argtypes = []
+    lib.lsa_version.restype = ctypes.c_char_p
+    lib.lsa_version.argtypes = []
+    _lib = lib
+    return lib
+
+
+def last_error() -> str:
+    return load().lsa_last_error().decode()
+
+
+def version() -> str:
+    return load().lsa_version().decode()
+
+
+def _check(status: int) -> None:
+    if status != LSA_OK:
+        raise LsaError(status, last_error())
+
+
+def _ptr(t: Optional[torch.Tensor]) -> Optional[int]:
+    if t is None:
+        return None
+    if not t.is_contiguous():
+        raise ValueError("tensors passed to liblsa must be contiguous")
+    return t.data_ptr()
+
+
+def _stream(stream) -> Optional[int]:
+    if stream is None:
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, int):
+        return stream
+    return stream.cuda_stream
+
+
+def dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.float32:
+        return F32
+    if t.dtype == torch.bfloat16:
+        return BF16
+    raise ValueError(f"unsupported query dtype {t.dtype}")
+
+
+@dataclass
+class KVPool:
+    """A caller-owned paged KV pool (layouts in include/lsa.h)."""
+    dtype: int
+    k: torch.Tensor
+    v: torch.Tensor
+    num_kv_heads: int
+    head_dim: int
+    page_size: int
+    logical_page: int
+    num_pages: int
+    k_sz: Optional[torch.Tensor] = None     # int4: [P][H_kv][2] fp16
+    v_sz: Optional[torch.Tensor] = None
+
+    def desc(self) -> LsaKV:
+        return LsaKV(self.dtype, self.num_kv_heads, self.head_dim, self.page_size, self.logical_page, 0,
+                     self.num_pages, _ptr(self.k), _ptr(self.v), _ptr(self.k_sz), _ptr(self.v_sz))
+
+
+@dataclass
+class Heads:
+    """Head classification ([host] head_kind per KV head) and Lambda sizes."""
+    head_kind: Sequence[int]
+    num_q_heads: int
+    sink_tokens: int = 0
+    local_tokens: int = 1
+    sink_blocks: int = 0
+    local_blocks: int = 1
+    _buf: object = field(default=None, repr=False)
+
+    def desc(self) -> LsaHeads:
+        self._buf = (ctypes.c_uint8 * len(self.head_kind))(*[int(x) for x in self.head_kind])
+        return LsaHeads(ctypes.cast(self._buf, ctypes.c_void_p), self.num_q_heads, self.sink_tokens,
+                        self.local_tokens, self.sink_blocks, self.local_blocks)
+
+
+def seqs_desc(page_table: torch.Tensor, seq_lens: torch.Tensor) -> LsaSeqs:
+    assert page_table.dtype == torch.int32 and seq_lens.dtype == torch.int32
+    return LsaSeqs(page_table.shape[0], page_table.shape[1], _ptr(page_table), _ptr(seq_lens))
+
+
+# ---------------------------------------------------------------------------
+# the four entry points and their size queries
+# ---------------------------------------------------------------------------
+
+def page_stats_bytes(kv: KVPool) -> int:
+    out = ctypes.c_size_t(0)
+    _check(load().lsa_page_stats_bytes(ctypes.byref(kv.desc()), ctypes.byref(out)))
+    return out.value
+
+
+def build_page_stats(kv: KVPool, page_table: torch.Tensor, seq_lens: torch.Tensor, stats: torch.Tensor,
+                     heads: Optional[Heads] = None, first_token: Optional[torch.Tensor] = None,
+                     max_new_tokens: int = 0, stream=None) -> None:
+    hd = ctypes.byref(heads.desc()) if heads is not None else None
+    _check(load().lsa_build_page_stats(ctypes.byref(kv.desc()), ctypes.byref(seqs_desc(page_table, seq_lens)),
+                                       hd, _ptr(first_token), max_new_tokens, _ptr(stats), _stream(stream)))
+
+
+def select_pages_workspace(kv: KVPool, page_table: torch.Tensor, seq_lens: torch.Tensor, heads: Heads) -> int:
+    out = ctypes.c_size_t(0)
+    _check(load().lsa_select_pages_workspace(ctypes.byref(kv.desc()), ctypes.byref(seqs_desc(page_table, seq_lens)),
+                                             ctypes.byref(heads.desc()), ctypes.byref(out)))
+    return out.value
+
+
+def select_pages(q: torch.Tensor, kv: KVPool, stats: torch.Tensor, page_table: torch.Tensor,
+                 seq_lens: torch.Tensor, heads: Heads, token_budget: int, decode_step: int,
+                 reuse_interval: int, selected: torch.Tensor, workspace: torch.Tensor, stream=None) -> None:
+    _check(load().lsa_select_pages(_ptr(q), dtype_code(q), ctypes.byref(kv.desc()), _ptr(stats),
+                                   ctypes.byref(seqs_desc(page_table, seq_lens)), ctypes.byref(heads.desc()),
+                                   token_budget, decode_step, reuse_interval, _ptr(selected), _ptr(workspace),
+                                   workspace.numel() * workspace.element_size(), _stream(stream)))
+
+
+def decode_workspace(kv: KVPool, page_table: torch.Tensor, seq_lens: torch.Tensor, heads: Heads,
+                     token_budget: int) -> int:
+    out = ctypes.c_size_t(0)
+    _check(load().lsa_decode_workspace(ctypes.byref(kv.desc()), ctypes.byref(seqs_desc(page_table, seq_lens)),
+                                       ctypes.byref(heads.desc()), token_budget, ctypes.byref(out)))
+    return out.value
+
+
+def sparse_decode_attn(q: torch.Tensor, kv: KVPool, page_table: torch.Tensor, seq_lens: torch.Tensor,
+                       heads: Heads, selected: Optional[torch.Tensor], token_budget: int, out: torch.Tensor,
+                       workspace: torch.Tensor, softmax_scale: float = 0.0, stream=None) -> None:
+    _check(load().lsa_sparse_decode_attn(_ptr(q), dtype_code(q), ctypes.byref(kv.desc()),
+                                         ctypes.byref(seqs_desc(page_table, seq_lens)), ctypes.byref(heads.desc()),
+                                         _ptr(selected), token_budget, softmax_scale, _ptr(out), _ptr(workspace),
+                                         workspace.numel() * workspace.element_size(), _stream(stream)))
+
+
+def sparse_prefill_attn(q: torch.Tensor, kv: KVPool, page_table: torch.Tensor, seq_len: int, heads: Heads,
+                        out: torch.Tensor, block: int = 64, softmax_scale: float = 0.0,
+                        tile_counter: Optional[torch.Tensor] = None, stream=None) -> None:
+    _check(load().lsa_sparse_prefill_attn(_ptr(q), dtype_code(q), ctypes.byref(kv.desc()), _ptr(page_table),
+                                          seq_len, ctypes.byref(heads.desc()), block, softmax_scale, _ptr(out),
+                                          _ptr(tile_counter), _stream(stream)))

@@ -1,0 +1,289 @@
+"""Seeded synthetic workloads shaped like the LServe evaluations.
+
+This module only makes inputs: random tensors, page tables, head classes,
+outlier channels, needle keys and the int4 storage of the KV pool.  It holds
+none of the attention method's arithmetic (no statistics, scores, selection or
+softmax), and it is the only code shared by the GPU tests and the oracle.
+
+Recipe (fixed order of random draws from one torch.Generator seeded with the
+config id, on the device the pool is built on):
+  1. head classes: exactly H_kv/2 streaming KV heads, a seeded subset
+     (config 1 is fixed: KV head 0 retrieval, KV head 1 streaming);
+  2. outlier channels: 4 per KV head, shared by the batch (keys only, x8);
+  3. context lengths (config 4: uniform in [128K, 256K]);
+  4. the page table: identity, or a seeded permutation of all pool pages;
+  5. queries of the decode window, N(0, 1);
+  6. needle positions: 8 per sequence, uniform in [0, ctx); the needle key is
+     3 * the unit vector of the sum of the group's step-0 queries;
+  7. keys, page chunk by page chunk: N(0, 1), outlier channels x8, needles
+     written over their slots, then int4 storage;
+  8. values, page chunk by page chunk: N(0, 1), then int4 storage.
+Prefill (config 3): head classes, then per-head scales U[0.5, 2] for q, k and
+v, then q, k, v ~ N(0, 1) * scale.
+
+int4 storage (KV4): per (pool page, KV head, tensor) scale s = fp16 of
+(max - min) / 15 (at least 2^-10) and zero point z = round(16 * (-min / s)) / 16
+clamped to [0, 15], so (c - z) * s is exact in fp32; codes
+c = clamp(round(x / s + z), 0, 15); keys packed two channels per byte (even
+channel in the low nibble), values two tokens per byte.
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass, field
+from typing import List, Optional
+
+import torch
+
+F32, BF16, INT4 = 0, 1, 2
+
+
+@dataclass
+class DecodeWorkload:
+    cfg: int
+    dtype: int                    # F32 | BF16 | INT4 (KV storage); q is f32 for F32, else bf16
+    batch: int
+    num_q_heads: int
+    num_kv_heads: int
+    head_dim: int
+    logical_page: int
+    page_size: int
+    token_budget: int
+    reuse_interval: int
+    sink_tokens: int
+    local_tokens: int
+    sink_blocks: int
+    local_blocks: int
+    head_kind: List[int]
+    ctx: List[int]                # cached tokens before the decode window
+    window: int                   # decode steps
+    max_pages: int
+    num_pages: int
+    page_table: torch.Tensor      # int32 [B][max_pages]
+    k: torch.Tensor
+    v: torch.Tensor
+    q: torch.Tensor               # [window][B][H_q][D]
+    k_sz: Optional[torch.Tensor] = None   # int4: [P][H_kv][2] fp16
+    v_sz: Optional[torch.Tensor] = None
+    outliers: Optional[torch.Tensor] = None
+    needles: Optional[torch.Tensor] = None   # [B][8] token positions
+
+    def seq_lens(self, step: int) -> torch.Tensor:
+        """Tokens in cache at decode step `step` (the step's token included)."""
+        return torch.tensor([c + step + 1 for c in self.ctx], dtype=torch.int32, device=self.page_table.device)
+
+
+@dataclass
+class PrefillWorkload:
+    cfg: int
+    dtype: int
+    seq_len: int
+    num_q_heads: int
+    num_kv_heads: int
+    head_dim: int
+    page_size: int
+    logical_page: int
+    sink_blocks: int
+    local_blocks: int
+    head_kind: List[int]
+    num_pages: int
+    page_table: torch.Tensor      # int32 [ceil(T / N_P)]
+    q: torch.Tensor               # [T][H_q][D]
+    k: torch.Tensor
+    v: torch.Tensor
+    scales: dict = field(default_factory=dict)
+
+
+# ---------------------------------------------------------------------------
+# config table (the five workloads)
+# ---------------------------------------------------------------------------
+
+DECODE_CONFIGS = {
+    1: dict(dtype=F32, batch=1, num_q_heads=4, num_kv_heads=2, head_dim=64, logical_page=16, page_size=64,
+            token_budget=256, reuse_interval=4, sink_tokens=16, local_tokens=128, sink_blocks=1, local_blocks=2,
+            ctx=1024, window=16, permute=True, outliers=False, needles=0),
+    2: dict(dtype=BF16, batch=8, num_q_heads=32, num_kv_heads=8, head_dim=128, logical_page=16, page_size=64,
+            token_budget=4096, reuse_interval=4, sink_tokens=64, local_tokens=1024, sink_blocks=1, local_blocks=16,
+            ctx=65536, window=4, permute=False, outliers=True, needles=8),
+    4: dict(dtype=BF16, batch=64, num_q_heads=32, num_kv_heads=8, head_dim=128, logical_page=16, page_size=128,
+            token_budget=4096, reuse_interval=4, sink_tokens=128, local_tokens=2048, sink_blocks=1, local_blocks=16,
+            ctx=(131072, 262144), window=4, permute=True, outliers=True, needles=8),
+    5: dict(dtype=INT4, batch=16, num_q_heads=32, num_kv_heads=8, head_dim=128, logical_page=16, page_size=64,
+            token_budget=4096, reuse_interval=4, sink_tokens=64, local_tokens=1024, sink_blocks=1, local_blocks=16,
+            ctx=262144, window=4, permute=False, outliers=True, needles=8),
+}
+
+PREFILL_CONFIGS = {
+    1: dict(dtype=F32, seq_len=1024, num_q_heads=4, num_kv_heads=2, head_dim=64, page_size=64, logical_page=16,
+            sink_blocks=1, local_blocks=2, permute=True, head_scales=False),
+    3: dict(dtype=BF16, seq_len=131072, num_q_heads=32, num_kv_heads=8, head_dim=128, page_size=64,
+            logical_page=16, sink_blocks=1, local_blocks=16, permute=False, head_scales=True),
+}
+
+
+def _gen(device, seed: int) -> torch.Generator:
+    g = torch.Generator(device=device)
+    g.manual_seed(seed)
+    return g
+
+
+def _head_kinds(n_kv: int, g: torch.Generator, fixed=None) -> List[int]:
+    if fixed is not None:
+        return list(fixed)
+    perm = torch.randperm(n_kv, generator=g, device=g.device).tolist()
+    kinds = [0] * n_kv
+    for h in perm[: n_kv // 2]:
+        kinds[h] = 1
+    return kinds
+
+
+def quantize_int4(x: torch.Tensor):
+    """int4 storage of x [..., A, Bd] grouped over its last two dims per leading
+    index: returns (codes packed along the last dim, [..., 2] fp16 {s, z})."""
+    lead = x.shape[:-2]
+    flat = x.reshape(*lead, -1).float()
+    lo = flat.amin(dim=-1)
+    hi = flat.amax(dim=-1)
+    s = ((hi - lo) / 15.0).clamp_min(2.0 ** -10).to(torch.float16)
+    s32 = s.float()
+    z = torch.round(16.0 * (-lo / s32)) / 16.0
+    z = z.clamp(0.0, 15.0).to(torch.float16)        # multiples of 1/16 in [0, 15] are exact in fp16
+    z32 = z.float()
+    c = torch.round(x.float() / s32[..., None, None] + z32[..., None, None]).clamp(0, 15).to(torch.uint8)
+    packed = c[..., 0::2] | (c[..., 1::2] << 4)
+    sz = torch.stack([s, z], dim=-1)
+    return packed.contiguous(), sz
+
+
+def make_decode(cfg: int, device="cpu", *, batch: Optional[int] = None, ctx=None, window: Optional[int] = None,
+                seed: Optional[int] = None, replicas: int = 1, chunk_pages: int = 2048) -> DecodeWorkload:
+    """Build a decode workload.  Overrides shrink a config for tests."""
+    c = dict(DECODE_CONFIGS[cfg])
+    B = batch if batch is not None else c["batch"]
+    W = window if window is not None else c["window"]
+    ctx_spec = ctx if ctx is not None else c["ctx"]
+    H_q, H_kv, D, NP = c["num_q_heads"], c["num_kv_heads"], c["head_dim"], c["page_size"]
+    G = H_q // H_kv
+    dt = c["dtype"]
+    g = _gen(device, cfg if seed is None else seed)
+
+    kinds = _head_kinds(H_kv, g, fixed=[0, 1] if cfg == 1 else None)
+    outl = torch.stack([torch.randperm(D, generator=g, device=device)[:4] for _ in range(H_kv)]) \
+        if c["outliers"] else None
+    if isinstance(ctx_spec, tuple):
+        lo, hi = ctx_spec
+        ctx_list = torch.randint(lo, hi + 1, (B,), generator=g, device=device).tolist()
+    elif isinstance(ctx_spec, list):
+        ctx_list = list(ctx_spec)
+    else:
+        ctx_list = [int(ctx_spec)] * B
+    pages = [-(-(cl + W) // NP) for cl in ctx_list]
+    max_pages = max(pages)
+    P = sum(pages)
+    pool_ids = torch.randperm(P, generator=g, device=device) if c["permute"] else torch.arange(P, device=device)
+    table = torch.zeros((B, max_pages), dtype=torch.int32, device=device)
+    off = 0
+    for b in range(B):
+        table[b, : pages[b]] = pool_ids[off: off + pages[b]].to(torch.int32)
+        off += pages[b]
+
+    qdt = torch.float32 if dt == F32 else torch.bfloat16
+    q = torch.randn((W, B, H_q, D), generator=g, device=device).to(qdt)
+
+    # needles: positions and key vectors
+    n_needles = c["needles"]
+    needle_pos = None
+    needle_vec = None
+    if n_needles:
+        needle_pos = torch.stack([torch.randint(0, max(1, ctx_list[b]), (n_needles,), generator=g, device=device)
+                                  for b in range(B)])
+        qs = q[0].float().reshape(B, H_kv, G, D).sum(dim=2)             # [B][H_kv][D]
+        needle_vec = 3.0 * qs / qs.norm(dim=-1, keepdim=True)
+        needle_pid = table.long().gather(1, needle_pos // NP)            # [B][n] pool pages
+        needle_slot = needle_pos % NP
+    kscale = torch.ones((H_kv, D), device=device)
+    if outl is not None:
+        kscale.scatter_(1, outl, 8.0)
+
+    # keys
+    if dt == INT4:
+        k = torch.empty((P, H_kv, NP, D // 2), dtype=torch.uint8, device=device)
+        k_sz = torch.empty((P, H_kv, 2), dtype=torch.float16, device=device)
+    else:
+        k = torch.empty((P, H_kv, NP, D), dtype=qdt, device=device)
+        k_sz = None
+    for p0 in range(0, P, chunk_pages):
+        p1 = min(P, p0 + chunk_pages)
+        x = torch.randn((p1 - p0, H_kv, NP, D), generator=g, device=device)
+        x *= kscale[None, :, None, :]
+        if n_needles:
+            bi, ni = torch.nonzero((needle_pid >= p0) & (needle_pid < p1), as_tuple=True)
+            if bi.numel():
+                x[needle_pid[bi, ni] - p0, :, needle_slot[bi, ni], :] = needle_vec[bi]
+        if dt == INT4:
+            codes, sz = quantize_int4(x)
+            k[p0:p1] = codes
+            k_sz[p0:p1] = sz
+        else:
+            k[p0:p1] = x.to(qdt)
+    # values, channel-major within a page: [P][H_kv][D][N_P]
+    if dt == INT4:
+        v = torch.empty((P, H_kv, D, NP // 2), dtype=torch.uint8, device=device)
+        v_sz = torch.empty((P, H_kv, 2), dtype=torch.float16, device=device)
+    else:
+        v = torch.empty((P, H_kv, D, NP), dtype=qdt, device=device)
+        v_sz = None
+    for p0 in range(0, P, chunk_pages):
+        p1 = min(P, p0 + chunk_pages)
+        x = torch.randn((p1 - p0, H_kv, D, NP), generator=g, device=device)
+        if dt == INT4:
+            codes, sz = quantize_int4(x)
+            v[p0:p1] = codes
+            v_sz[p0:p1] = sz
+        else:
+            v[p0:p1] = x.to(qdt)
+
+    return DecodeWorkload(
+        cfg=cfg, dtype=dt, batch=B, num_q_heads=H_q, num_kv_heads=H_kv, head_dim=D,
+        logical_page=c["logical_page"], page_size=NP, token_budget=c["token_budget"],
+        reuse_interval=c["reuse_interval"], sink_tokens=c["sink_tokens"], local_tokens=c["local_tokens"],
+        sink_blocks=c["sink_blocks"], local_blocks=c["local_blocks"], head_kind=kinds, ctx=ctx_list,
+        window=W, max_pages=max_pages, num_pages=P, page_table=table, k=k, v=v, q=q, k_sz=k_sz, v_sz=v_sz,
+        outliers=outl, needles=needle_pos)
+
+
+def make_prefill(cfg: int, device="cpu", *, seq_len: Optional[int] = None, seed: Optional[int] = None,
+                 head_kind: Optional[List[int]] = None) -> PrefillWorkload:
+    c = dict(PREFILL_CONFIGS[cfg])
+    T = seq_len if seq_len is not None else c["seq_len"]
+    H_q, H_kv, D, NP = c["num_q_heads"], c["num_kv_heads"], c["head_dim"], c["page_size"]
+    dt = c["dtype"]
+    qdt = torch.float32 if dt == F32 else torch.bfloat16
+    g = _gen(device, cfg if seed is None else seed)
+    kinds = _head_kinds(H_kv, g, fixed=[0, 1] if cfg == 1 else None)
+    if head_kind is not None:
+        kinds = list(head_kind)
+    P = -(-T // NP)
+    table = (torch.randperm(P, generator=g, device=device) if c["permute"]
+             else torch.arange(P, device=device)).to(torch.int32)
+    if c["head_scales"]:
+        sq = torch.rand(H_q, generator=g, device=device) * 1.5 + 0.5
+        sk = torch.rand(H_kv, generator=g, device=device) * 1.5 + 0.5
+        sv = torch.rand(H_kv, generator=g, device=device) * 1.5 + 0.5
+    else:
+        sq = torch.ones(H_q, device=device)
+        sk = torch.ones(H_kv, device=device)
+        sv = torch.ones(H_kv, device=device)
+    q = (torch.randn((T, H_q, D), generator=g, device=device) * sq[None, :, None]).to(qdt)
+    # pool pages are written through the page table: token p sits in page table[p // NP]
+    k = torch.empty((P, H_kv, NP, D), dtype=qdt, device=device)
+    v = torch.empty((P, H_kv, D, NP), dtype=qdt, device=device)
+    kk = torch.randn((P, H_kv, NP, D), generator=g, device=device) * sk[None, :, None, None]
+    k[table.long()] = kk.to(qdt)
+    del kk
+    vv = torch.randn((P, H_kv, D, NP), generator=g, device=device) * sv[None, :, None, None]
+    v[table.long()] = vv.to(qdt)
+    del vv
+    return PrefillWorkload(cfg=cfg, dtype=dt, seq_len=T, num_q_heads=H_q, num_kv_heads=H_kv, head_dim=D,
+                           page_size=NP, logical_page=c["logical_page"], sink_blocks=c["sink_blocks"],
+                           local_blocks=c["local_blocks"], head_kind=kinds, num_pages=P, page_table=table,
+                           q=q, k=k, v=v, scales=dict(q=sq, k=sk, v=sv))

@@ -1,0 +1,230 @@
+/*
+ * lsa.h — C ABI of the MI355X (gfx950) block-sparse attention library with
+ * hierarchical, query-aware KV page selection.
+ *
+ * Method sources (cited by page title and section):
+ *   [LS-X] "MLSys 2025論文解説: LServe — 統一疎アテンションによる長文脈LLM推論の効率化",
+ *          section 技術的詳細: 静的スパーシティ (retrieval / streaming heads,
+ *          Lambda mask of sink + local tokens), 動的スパーシティ (the page score
+ *          S^j = sum_i max(q[i] k_max^j[i], q[i] k_min^j[i])), 階層的ページング
+ *          (physical page N_P = g * N_L logical pages; physical importance is the
+ *          max of its logical pages' scores), 統一ブロックスパースアテンション
+ *          (figure: one block-sparse kernel for both head kinds and phases;
+ *          top-K physical pages at decode) and Reusable Page Selection (one
+ *          selection serves k = 4 consecutive decode tokens).
+ *   [LS-A] "LServe: Efficient Long-sequence LLM Serving with Unified Sparse
+ *          Attention" (abstract page): streaming heads in prefill and decode; a
+ *          constant number of KV pages regardless of context length.
+ *
+ * Conventions shared by every entry point
+ *   - Pointers are DEVICE pointers unless marked [host].
+ *   - Every buffer is owned by the caller; the library allocates nothing and
+ *     keeps no state between calls.  Workspaces are sized by the *_workspace
+ *     queries.
+ *   - Calls are asynchronous on `stream` (a hipStream_t; NULL = the default
+ *     stream) and never synchronise the host.
+ *   - Arguments are validated on the host before any launch.  A validation
+ *     failure returns a negative lsa_status, records a message readable with
+ *     lsa_last_error() (thread-local) and launches nothing.  A failed launch
+ *     returns LSA_ERR_HIP with the runtime's message.  No C++ exception
+ *     crosses this boundary.
+ *   - Device-side contents are trusted: page ids outside [0, num_pages),
+ *     seq_lens above max_pages * page_size or selected pages beyond the
+ *     sequence are undefined behaviour.
+ *   - Supported shapes: head_dim 64 or 128; page_size a multiple of
+ *     logical_page; logical_page in {8, 16, 32, 64}; page_size <= 256 and a
+ *     multiple of 32; num_q_heads a multiple of num_kv_heads with group size
+ *     G = num_q_heads / num_kv_heads <= 16.  Query head h uses KV head h / G.
+ *
+ * Paged KV pool layout (caller-owned, fixed):
+ *   K, f32/bf16:  [num_pages][H_kv][page_size][head_dim]   token-major in a page
+ *   V, f32/bf16:  [num_pages][H_kv][head_dim][page_size]   channel-major in a page
+ *   K, int4:      [num_pages][H_kv][page_size][head_dim/2] bytes, channel 2i in
+ *                 the low nibble of byte i
+ *   V, int4:      [num_pages][H_kv][head_dim][page_size/2] bytes, token 2j in
+ *                 the low nibble of byte j
+ *   k_sz, v_sz:   int4 only, [num_pages][H_kv][2] IEEE fp16 {scale s, zero z},
+ *                 s > 0; a stored code c means (c - z) * s.
+ *   Token p of sequence b is slot p % page_size of pool page
+ *   page_table[b * max_pages + p / page_size].
+ */
+#ifndef LSA_H
+#define LSA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef int32_t lsa_status;
+#define LSA_OK                0
+#define LSA_ERR_INVALID_ARG  (-1)
+#define LSA_ERR_UNSUPPORTED  (-2)
+#define LSA_ERR_WORKSPACE    (-3)
+#define LSA_ERR_HIP          (-4)
+
+#define LSA_F32   0
+#define LSA_BF16  1
+#define LSA_INT4  2
+
+#define LSA_RETRIEVAL_HEAD 0
+#define LSA_STREAMING_HEAD 1
+
+/* [host] descriptor of the paged KV pool (layout above). */
+typedef struct lsa_kv {
+    int32_t kv_dtype;       /* LSA_F32 | LSA_BF16 | LSA_INT4                      */
+    int32_t num_kv_heads;   /* H_kv                                               */
+    int32_t head_dim;       /* D: 64 or 128                                       */
+    int32_t page_size;      /* N_P, tokens per physical page                      */
+    int32_t logical_page;   /* N_L, tokens per logical page; N_P = g * N_L        */
+    int32_t reserved;       /* must be 0                                          */
+    int64_t num_pages;      /* pool capacity P                                    */
+    const void *k;          /* K pool                                             */
+    const void *v;          /* V pool                                             */
+    const uint16_t *k_sz;   /* int4 only, else NULL                               */
+    const uint16_t *v_sz;   /* int4 only, else NULL                               */
+} lsa_kv;
+
+/* [host] descriptor of a decode batch. */
+typedef struct lsa_seqs {
+    int32_t batch;              /* B                                              */
+    int32_t max_pages;          /* row stride of page_table                       */
+    const int32_t *page_table;  /* [B][max_pages] pool page id of sequence page m */
+    const int32_t *seq_lens;    /* [B] tokens in cache, the current one included;
+                                   each in [1, max_pages * page_size]             */
+} lsa_seqs;
+
+/* [host] head classification ([LS-X] 静的スパーシティ: a head is either a
+ * retrieval head or a streaming head; the class is fixed per KV head and known
+ * when the model is loaded). */
+typedef struct lsa_heads {
+    const uint8_t *head_kind;   /* [host] [H_kv]: LSA_RETRIEVAL_HEAD | LSA_STREAMING_HEAD */
+    int32_t num_q_heads;        /* H_q, a multiple of H_kv                        */
+    int32_t sink_tokens;        /* decode Lambda: tokens p < sink_tokens ...      */
+    int32_t local_tokens;       /* ... or t - p < local_tokens are attended       */
+    int32_t sink_blocks;        /* prefill Lambda, in tiles: tiles c < sink_blocks */
+    int32_t local_blocks;       /* ... or a - c < local_blocks (diagonal counts)  */
+} lsa_heads;
+
+/* Bytes of the logical-page statistics pool that matches `kv`:
+ *   f32/bf16: [num_pages][H_kv][g][2][head_dim] elements of kv_dtype
+ *             (index 0 = channel minimum, 1 = channel maximum), g = N_P / N_L;
+ *   int4:     [num_pages][H_kv][g][head_dim] bytes, byte = c_min | c_max << 4.
+ * Source: [LS-X] 動的スパーシティ and 階層的ページング (channel-wise k_min /
+ * k_max per logical page, kept beside each physical page). */
+lsa_status lsa_page_stats_bytes(const lsa_kv *kv, size_t *bytes /* [host] out */);
+
+/* Build the channel-wise min / max of the keys of logical pages
+ * ([LS-X] 動的スパーシティ: statistics of logical page j; 階層的ページング:
+ * N_L-token logical pages inside N_P-token physical pages).
+ *
+ * For every sequence b and KV head (only retrieval heads when `heads` is not
+ * NULL; every head when it is NULL) the logical pages j that overlap
+ * [first_token[b], seq_lens[b]) are recomputed from their valid tokens
+ * [j*N_L, min((j+1)*N_L, seq_lens[b])).  Logical pages with no valid token are
+ * left untouched.  first_token == NULL means 0 for every sequence (a full
+ * build after a prefill).  max_new_tokens [host] bounds seq_lens[b] -
+ * first_token[b] over the batch (it sizes the launch; 1 for a decode step);
+ * 0 means max_pages * page_size.  Min and max are exact (no rounding).
+ * stats: the statistics pool, layout as in lsa_page_stats_bytes.
+ * Call after the K rows of the new tokens are in the pool. */
+lsa_status lsa_build_page_stats(const lsa_kv *kv, const lsa_seqs *seqs,
+                                const lsa_heads *heads, const int32_t *first_token,
+                                int32_t max_new_tokens, void *stats, void *stream);
+
+/* Workspace of lsa_select_pages, in bytes. */
+lsa_status lsa_select_pages_workspace(const lsa_kv *kv, const lsa_seqs *seqs,
+                                      const lsa_heads *heads, size_t *bytes /* [host] out */);
+
+/* Query-aware top-K physical page selection with reuse
+ * ([LS-X] 動的スパーシティ, 階層的ページング, the figure's top-K physical pages,
+ * Reusable Page Selection; [LS-A] constant page budget).
+ *
+ * Runs only when decode_step % reuse_interval == 0; otherwise returns LSA_OK
+ * and leaves `selected` unchanged (the previous selection is reused).  For
+ * each sequence b and retrieval KV head kv, with the group's queries
+ * q_h (h = kv*G .. kv*G+G-1):
+ *   S^j  = sum_h sum_i max(q_h[i] * kmax^j[i], q_h[i] * kmin^j[i])   for every
+ *          logical page j holding a valid token (GQA heads summed);
+ *   P_m  = max over the logical pages j of physical page m (j / g == m);
+ *   selected[b][kv][0..K-1] = the K = token_budget / page_size pages m of
+ *          largest P_m, ties to the lower m, in ascending m, padded with -1
+ *          when the sequence has fewer than K pages.
+ * Products are exact and S^j, P_m are accumulated and compared in fp64.
+ * Streaming heads' rows of `selected` are not written.
+ * q: [B][H_q][head_dim] of q_dtype (LSA_F32 or LSA_BF16).
+ * stats: as built by lsa_build_page_stats for tokens < seq_lens[b].
+ * selected: [B][H_kv][K] int32.
+ * workspace: at least lsa_select_pages_workspace bytes, 256-byte aligned. */
+lsa_status lsa_select_pages(const void *q, int32_t q_dtype, const lsa_kv *kv,
+                            const void *stats, const lsa_seqs *seqs,
+                            const lsa_heads *heads, int32_t token_budget,
+                            int32_t decode_step, int32_t reuse_interval,
+                            int32_t *selected, void *workspace,
+                            size_t workspace_bytes, void *stream);
+
+/* Workspace of lsa_sparse_decode_attn, in bytes. */
+lsa_status lsa_decode_workspace(const lsa_kv *kv, const lsa_seqs *seqs,
+                                const lsa_heads *heads, int32_t token_budget,
+                                size_t *bytes /* [host] out */);
+
+/* Block-sparse paged decode attention for retrieval and streaming heads
+ * ([LS-X] 静的スパーシティ, the figure's unified block-sparse kernel;
+ * [LS-A] constant KV page count per step).
+ *
+ * For each sequence b, t = seq_lens[b] - 1, and query head h (KV head
+ * kv = h / G):
+ *   retrieval kv: attended keys A = { p <= t : p / N_P in selected[b][kv] or
+ *                 p / N_P == t / N_P }  (the current page is always read);
+ *   streaming kv: A = { p <= t : p < sink_tokens or t - p < local_tokens };
+ *   out[b][h] = sum_{p in A} softmax_p(scale * q_h . k_p) v_p.
+ * Only the pages that intersect A are read; a K/V page read serves all G
+ * query heads of its group.
+ * q, out: [B][H_q][head_dim]; supported (q_dtype, kv_dtype) pairs are
+ * (LSA_F32, LSA_F32), (LSA_BF16, LSA_BF16) and (LSA_BF16, LSA_INT4); out has
+ * q's dtype (round to nearest even).  Accumulation is fp32.
+ * selected: [B][H_kv][K] as written by lsa_select_pages (rows of streaming
+ * heads are not read; may be NULL when every head is a streaming head).
+ * softmax_scale: 0 means 1 / sqrt(head_dim).
+ * workspace: at least lsa_decode_workspace bytes, 256-byte aligned. */
+lsa_status lsa_sparse_decode_attn(const void *q, int32_t q_dtype, const lsa_kv *kv,
+                                  const lsa_seqs *seqs, const lsa_heads *heads,
+                                  const int32_t *selected, int32_t token_budget,
+                                  float softmax_scale, void *out, void *workspace,
+                                  size_t workspace_bytes, void *stream);
+
+/* Block-sparse causal prefill attention of one sequence over non-empty tiles
+ * only ([LS-X] 統一ブロックスパースアテンション: iterate the non-empty blocks;
+ * the figure's retrieval heads use a static causal pattern in prefill and
+ * streaming heads sink + local blocks; speed-up 1/(1-r)).
+ *
+ * Tiles are block x block tokens (block must be 64).  Query tile a sees key
+ * tile c when c <= a and (retrieval head, or c < sink_blocks, or
+ * a - c < local_blocks); inside a visible tile, key p is seen by query t iff
+ * p <= t.  out[t][h] = softmax over the visible keys of scale * q.k, times v.
+ * q, out: [seq_len][H_q][head_dim]; (q_dtype, kv_dtype) is (LSA_BF16, LSA_BF16)
+ * or (LSA_F32, LSA_F32) with head_dim 64 (the f32 path is the small-model
+ * path).  page_table: [ceil(seq_len / page_size)] pool page
+ * ids of the sequence; page_size must be a multiple of 64.
+ * tile_counter: NULL, or an int64 to which the number of (query head, tile)
+ * pairs computed is added (it equals the non-empty tile count of the mask).
+ * softmax_scale: 0 means 1 / sqrt(head_dim). */
+lsa_status lsa_sparse_prefill_attn(const void *q, int32_t q_dtype, const lsa_kv *kv,
+                                   const int32_t *page_table, int32_t seq_len,
+                                   const lsa_heads *heads, int32_t block,
+                                   float softmax_scale, void *out,
+                                   int64_t *tile_counter, void *stream);
+
+/* Message of the last failed call on this thread ("" if none); never NULL. */
+const char *lsa_last_error(void);
+
+/* Library version string, e.g. "lsa 0.1.0 gfx950". */
+const char *lsa_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LSA_H */

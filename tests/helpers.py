@@ -1,0 +1,62 @@
+"""Test-side glue: host copies of device tensors in the oracle's formats, and
+per-sequence gathers that keep host memory bounded on the large workloads."""
+from __future__ import annotations
+
+import numpy as np
+import torch
+
+import oracle.lsa_oracle as O
+from block_sparse_attention_logical_amd import lsa
+from block_sparse_attention_logical_amd.workloads import BF16, F32, INT4
+
+
+def bits(t: torch.Tensor) -> np.ndarray:
+    """Host numpy copy; bf16 and fp16 become their uint16 bit patterns."""
+    t = t.detach().cpu()
+    if t.dtype in (torch.bfloat16, torch.float16):
+        return t.view(torch.int16).numpy().view(np.uint16)
+    return t.numpy()
+
+
+def to_f64(t: torch.Tensor) -> np.ndarray:
+    """Exact float64 host copy of an f32 / bf16 tensor."""
+    if t.dtype == torch.bfloat16:
+        return O.bf16_bits_to_f64(bits(t))
+    return t.detach().cpu().numpy().astype(np.float64)
+
+
+DTYPE_NAME = {F32: "f32", BF16: "bf16", INT4: "int4"}
+
+
+def kv_pool(w) -> lsa.KVPool:
+    return lsa.KVPool(w.dtype, w.k, w.v, w.num_kv_heads, w.head_dim, w.page_size, w.logical_page, w.num_pages,
+                      w.k_sz, w.v_sz)
+
+
+def heads(w) -> lsa.Heads:
+    return lsa.Heads(w.head_kind, w.num_q_heads, getattr(w, "sink_tokens", 0), getattr(w, "local_tokens", 1),
+                     w.sink_blocks, w.local_blocks)
+
+
+def seq_pool(w, b: int, kv: int, length: int) -> O.Pool:
+    """An oracle Pool holding only the pages of sequence b, KV head kv (first
+    `length` tokens), with a page table 0..n-1."""
+    n = -(-length // w.page_size)
+    rows = w.page_table[b, :n].long()
+    k = w.k[rows, kv][:, None]
+    v = w.v[rows, kv][:, None]
+    ksz = bits(w.k_sz[rows, kv][:, None]) if w.k_sz is not None else None
+    vsz = bits(w.v_sz[rows, kv][:, None]) if w.v_sz is not None else None
+    return O.Pool(DTYPE_NAME[w.dtype], bits(k), bits(v), w.page_size, w.head_dim, ksz, vsz)
+
+
+def seq_kv(w, b: int, kv: int, length: int):
+    """(keys, values) float64 [length][D] of one sequence and KV head."""
+    pool = seq_pool(w, b, kv, length)
+    table = list(range(-(-length // w.page_size)))
+    return pool.keys(table, 0, length), pool.values(table, 0, length)
+
+
+def oracle_spec(w) -> O.DecodeSpec:
+    return O.DecodeSpec(w.num_q_heads, w.num_kv_heads, list(w.head_kind), w.logical_page, w.page_size,
+                        w.token_budget, w.reuse_interval, w.sink_tokens, w.local_tokens)

@@ -1,0 +1,199 @@
+"""CPU-side checks of the C ABI: the library loads, exports every function the
+header declares, sizes its buffers as documented, and rejects invalid
+arguments with the documented status before launching anything.  No call
+here reaches a kernel launch (each either fails validation or takes a
+documented no-launch path), so no GPU is needed."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+from block_sparse_attention_logical_amd import lsa
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "lsa.h")
+
+FAKE = 0x10000          # a non-NULL device address that is never dereferenced
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(lsa.LIB_PATH):
+        from block_sparse_attention_logical_amd import build
+        build.build(verbose=False)
+    return lsa.load()
+
+
+def header_functions():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^(?:lsa_status|const char \*)\s*(lsa_\w+)\s*\(", text, flags=re.M)))
+
+
+def test_header_declares_the_four_entry_points():
+    names = header_functions()
+    for n in ("lsa_build_page_stats", "lsa_select_pages", "lsa_sparse_decode_attn", "lsa_sparse_prefill_attn"):
+        assert n in names
+    assert set(names) == set(lsa.EXPORTED)
+
+
+def test_library_exports_every_declared_symbol(lib):
+    out = subprocess.run(["nm", "-D", "--defined-only", lsa.LIB_PATH], capture_output=True, text=True,
+                         check=True).stdout
+    defined = set(re.findall(r"\sT\s(lsa_\w+)$", out, flags=re.M))
+    for name in header_functions():
+        assert name in defined, name
+        assert hasattr(lib, name)
+
+
+def test_version(lib):
+    assert lsa.version().startswith("lsa ") and "gfx950" in lsa.version()
+
+
+def kv_desc(dtype=lsa.BF16, heads=8, D=128, NP=64, NL=16, P=100, sz=False):
+    k_sz = FAKE if sz else None
+    return lsa.LsaKV(dtype, heads, D, NP, NL, 0, P, FAKE, FAKE, k_sz, k_sz)
+
+
+def seqs_desc(B=2, max_pages=10):
+    return lsa.LsaSeqs(B, max_pages, FAKE, FAKE)
+
+
+def heads_desc(kinds=(0, 1, 0, 1, 0, 1, 0, 1), hq=32, sink=64, local=1024, sb=1, lb=16):
+    buf = (ctypes.c_uint8 * len(kinds))(*kinds)
+    h = lsa.LsaHeads(ctypes.cast(buf, ctypes.c_void_p), hq, sink, local, sb, lb)
+    h._keep = buf
+    return h
+
+
+def stats_bytes(lib, kv):
+    out = ctypes.c_size_t(0)
+    st = lib.lsa_page_stats_bytes(ctypes.byref(kv), ctypes.byref(out))
+    return st, out.value
+
+
+def test_stats_bytes_sizes(lib):
+    assert stats_bytes(lib, kv_desc(lsa.BF16, 8, 128, 64, 16, 100)) == (0, 100 * 8 * 4 * 2 * 128 * 2)
+    assert stats_bytes(lib, kv_desc(lsa.F32, 2, 64, 64, 16, 17)) == (0, 17 * 2 * 4 * 2 * 64 * 4)
+    assert stats_bytes(lib, kv_desc(lsa.INT4, 8, 128, 128, 16, 10, sz=True)) == (0, 10 * 8 * 8 * 128)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(D=96), lsa.LSA_ERR_UNSUPPORTED),
+    (dict(NP=48, NL=16), lsa.LSA_ERR_UNSUPPORTED),      # 3 logical pages: not a power of two
+    (dict(NP=64, NL=24), lsa.LSA_ERR_UNSUPPORTED),
+    (dict(NP=40, NL=8), lsa.LSA_ERR_UNSUPPORTED),       # not a multiple of 32
+    (dict(NP=8, NL=16), lsa.LSA_ERR_INVALID_ARG),
+    (dict(heads=0), lsa.LSA_ERR_UNSUPPORTED),
+    (dict(heads=65), lsa.LSA_ERR_UNSUPPORTED),
+    (dict(P=0), lsa.LSA_ERR_INVALID_ARG),
+    (dict(dtype=7), lsa.LSA_ERR_INVALID_ARG),
+    (dict(dtype=lsa.INT4), lsa.LSA_ERR_INVALID_ARG),    # int4 without scale / zero arrays
+    (dict(dtype=lsa.BF16, sz=True), lsa.LSA_ERR_INVALID_ARG),
+])
+def test_kv_validation(lib, kw, code):
+    st, _ = stats_bytes(lib, kv_desc(**kw))
+    assert st == code
+    assert lsa.last_error() != ""
+
+
+def test_null_descriptor_and_reserved(lib):
+    out = ctypes.c_size_t(0)
+    assert lib.lsa_page_stats_bytes(None, ctypes.byref(out)) == lsa.LSA_ERR_INVALID_ARG
+    kv = kv_desc()
+    kv.reserved = 1
+    assert stats_bytes(lib, kv)[0] == lsa.LSA_ERR_INVALID_ARG
+
+
+def select(lib, kv=None, seqs=None, heads=None, q_dtype=lsa.BF16, budget=4096, step=0, R=4, ws_bytes=1 << 30,
+           selected=FAKE, q=FAKE, stats=FAKE):
+    kv = kv or kv_desc()
+    seqs = seqs or seqs_desc()
+    heads = heads or heads_desc()
+    return lib.lsa_select_pages(q, q_dtype, ctypes.byref(kv), stats, ctypes.byref(seqs), ctypes.byref(heads),
+                                budget, step, R, selected, FAKE, ws_bytes, None)
+
+
+def test_select_validation(lib):
+    assert select(lib, budget=4000) == lsa.LSA_ERR_INVALID_ARG       # not a multiple of N_P
+    assert select(lib, budget=32) == lsa.LSA_ERR_INVALID_ARG         # below one page
+    assert select(lib, R=0) == lsa.LSA_ERR_INVALID_ARG
+    assert select(lib, step=-1) == lsa.LSA_ERR_INVALID_ARG
+    assert select(lib, q_dtype=lsa.INT4) == lsa.LSA_ERR_INVALID_ARG
+    assert select(lib, ws_bytes=16) == lsa.LSA_ERR_WORKSPACE
+    assert select(lib, selected=None) == lsa.LSA_ERR_INVALID_ARG
+    assert select(lib, heads=heads_desc(hq=30)) == lsa.LSA_ERR_INVALID_ARG
+    assert select(lib, heads=heads_desc(hq=8 * 17)) == lsa.LSA_ERR_UNSUPPORTED
+    assert select(lib, heads=heads_desc(kinds=(0, 1, 2, 1, 0, 1, 0, 1))) == lsa.LSA_ERR_INVALID_ARG
+    assert select(lib, heads=heads_desc(local=0)) == lsa.LSA_ERR_INVALID_ARG
+    assert select(lib, seqs=seqs_desc(max_pages=0)) == lsa.LSA_ERR_UNSUPPORTED
+    assert select(lib, seqs=lsa.LsaSeqs(2, 10, None, FAKE)) == lsa.LSA_ERR_INVALID_ARG
+
+
+def test_select_reuse_step_is_a_no_op(lib):
+    # steps that are not multiples of the reuse interval keep the previous
+    # selection: the call succeeds without launching anything
+    for step in (1, 2, 3, 5, 7):
+        assert select(lib, step=step, R=4) == lsa.LSA_OK
+    # no retrieval head: nothing to select
+    assert select(lib, step=0, heads=heads_desc(kinds=(1,) * 8)) == lsa.LSA_OK
+
+
+def test_select_workspace_size(lib):
+    out = ctypes.c_size_t(0)
+    st = lib.lsa_select_pages_workspace(ctypes.byref(kv_desc()), ctypes.byref(seqs_desc(8, 1025)),
+                                        ctypes.byref(heads_desc()), ctypes.byref(out))
+    assert st == 0 and out.value >= 8 * 8 * 1025 * 8 and out.value % 256 == 0
+
+
+def decode(lib, kv=None, heads=None, q_dtype=lsa.BF16, selected=FAKE, ws_bytes=1 << 30, scale=0.0, batch=2):
+    kv = kv or kv_desc()
+    heads = heads or heads_desc()
+    return lib.lsa_sparse_decode_attn(FAKE, q_dtype, ctypes.byref(kv), ctypes.byref(seqs_desc(batch)),
+                                      ctypes.byref(heads), selected, 4096, scale, FAKE, FAKE, ws_bytes, None)
+
+
+def test_decode_validation(lib):
+    assert decode(lib, q_dtype=lsa.F32) == lsa.LSA_ERR_UNSUPPORTED            # f32 q with bf16 pool
+    assert decode(lib, selected=None) == lsa.LSA_ERR_INVALID_ARG
+    assert decode(lib, ws_bytes=64) == lsa.LSA_ERR_WORKSPACE
+    assert decode(lib, scale=-1.0) == lsa.LSA_ERR_INVALID_ARG
+    assert decode(lib, scale=float("nan")) == lsa.LSA_ERR_INVALID_ARG
+    # all heads streaming: selected may be NULL; batch 0 launches nothing
+    assert decode(lib, heads=heads_desc(kinds=(1,) * 8), selected=None, batch=0) == lsa.LSA_OK
+
+
+def test_decode_workspace_size(lib):
+    out = ctypes.c_size_t(0)
+    st = lib.lsa_decode_workspace(ctypes.byref(kv_desc()), ctypes.byref(seqs_desc(8, 1025)),
+                                  ctypes.byref(heads_desc()), 4096, ctypes.byref(out))
+    assert st == 0
+    # 65 retrieval pages -> 17 chunks of 4 pages; records of 32 + G*D floats
+    assert out.value >= 8 * 8 * 17 * (32 + 4 * 128) * 4
+
+
+def prefill(lib, kv=None, q_dtype=lsa.BF16, block=64, T=1000):
+    kv = kv or kv_desc()
+    return lib.lsa_sparse_prefill_attn(FAKE, q_dtype, ctypes.byref(kv), FAKE, T, ctypes.byref(heads_desc()),
+                                       block, 0.0, FAKE, None, None)
+
+
+def test_prefill_validation(lib):
+    assert prefill(lib, block=32) == lsa.LSA_ERR_UNSUPPORTED
+    assert prefill(lib, kv=kv_desc(NP=32)) == lsa.LSA_ERR_UNSUPPORTED
+    assert prefill(lib, kv=kv_desc(dtype=lsa.F32)) == lsa.LSA_ERR_UNSUPPORTED  # f32 path is head_dim 64
+    assert prefill(lib, q_dtype=lsa.F32) == lsa.LSA_ERR_UNSUPPORTED            # mixed pair
+    assert prefill(lib, T=-1) == lsa.LSA_ERR_INVALID_ARG
+    assert prefill(lib, T=0) == lsa.LSA_OK                                     # nothing to do
+
+
+def test_stats_validation(lib):
+    kv = kv_desc()
+    seqs = seqs_desc()
+    assert lib.lsa_build_page_stats(ctypes.byref(kv), ctypes.byref(seqs), None, None, 0, None, None) == \
+        lsa.LSA_ERR_INVALID_ARG
+    assert lib.lsa_build_page_stats(ctypes.byref(kv), ctypes.byref(seqs), None, None, -1, FAKE, None) == \
+        lsa.LSA_ERR_INVALID_ARG
+    # empty batch: nothing to build
+    assert lib.lsa_build_page_stats(ctypes.byref(kv), ctypes.byref(seqs_desc(0)), None, None, 0, FAKE, None) == 0
