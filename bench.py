@@ -1,0 +1,368 @@
+#!/usr/bin/env python3
+"""Benchmark of the block-sparse attention hot path on one MI355X.
+
+Metric: sparse decode attention tokens/s and HBM GB/s at a 64K context
+(Llama-3-8B-shaped layer, bf16, batch 8), plus block-sparse prefill TFLOP/s
+at a 128K context.  One printed JSON line.
+
+Decode.  A step is one decode step of one attention layer for the whole batch:
+refresh the statistics of the current logical page, select pages (every
+R = 4 steps, reused otherwise), sparse decode attention.  Steps cycle over
+`--replicas` independent copies of the layer's KV pool (distinct layers of a
+model), so every step reads its pages from HBM rather than from the 256 MB
+last-level cache.  A cycle of replicas x R steps is captured once as a HIP
+graph and replayed; the timed region covers whole cycles.
+
+Prefill.  One call of the block-sparse prefill over 131072 tokens, 32 query
+heads, 8 KV heads (4 streaming with 1 sink + 16 local tiles).
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_HBM = 8.0e12          # MI355X HBM3E, bytes/s
+PEAK_BF16 = 2.5e15         # MI355X dense bf16 MFMA, flop/s
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=640, help="timed decode steps (rounded up to whole cycles)")
+    ap.add_argument("--warmup", type=int, default=64, help="untimed decode steps")
+    ap.add_argument("--replicas", type=int, default=8, help="KV pool replicas (layers) cycled through")
+    ap.add_argument("--prefill-reps", type=int, default=3)
+    ap.add_argument("--no-prefill", action="store_true")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0, help="budget of the oracle CPU sample")
+    ap.add_argument("--eager", action="store_true", help="time eager launches instead of graph replay")
+    ap.add_argument("--counters", action="store_true",
+                    help="counter-collection run: one 1 GiB device copy (the calibration kernel), then one eager "
+                         "decode cycle over the replicas; prints nothing else")
+    return ap.parse_args()
+
+
+def counters_run(args, torch, lsa, W):
+    """Kernels for rocprofv3 --pmc: a plain 1 GiB copy of known size, then the
+    decode steps of one cycle (each layer read once)."""
+    n = 1 << 30
+    src = torch.empty(n, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    src.fill_(1)
+    torch.cuda.synchronize()
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    del src, dst
+    torch.cuda.empty_cache()
+    args.eager = True
+    args.steps = 1
+    args.warmup = 0
+    bench_decode(args, torch, lsa, W)
+
+
+def sha_of(path):
+    with open(path, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def counters_for(kernel_tag, source_file, launch_bytes):
+    """HBM traffic of one launch from the committed rocprofv3 counter summary,
+    or None if it was taken on another version of the kernel source."""
+    path = os.path.join(ROOT, "profiles", f"{kernel_tag}_counters.txt")
+    if not os.path.exists(path):
+        return None
+    kv = {}
+    for line in open(path):
+        if "=" in line and not line.startswith("#"):
+            k, v = line.split("=", 1)
+            kv[k.strip()] = v.strip()
+    if kv.get("source_sha") != sha_of(source_file):
+        return None
+    try:
+        return float(kv["traffic_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+# ---------------------------------------------------------------------------
+# decode (config 2)
+# ---------------------------------------------------------------------------
+
+def bench_decode(args, torch, lsa, W):
+    dev = "cuda"
+    w = W.make_decode(2, dev)
+    B, Hq, Hkv, D, NP = w.batch, w.num_q_heads, w.num_kv_heads, w.head_dim, w.page_size
+    R = w.reuse_interval
+    K = w.token_budget // NP
+    hd = lsa.Heads(w.head_kind, Hq, w.sink_tokens, w.local_tokens, w.sink_blocks, w.local_blocks)
+    nrep = max(1, args.replicas)
+    layers = []
+    for r in range(nrep):
+        k = w.k if r == 0 else w.k.clone()
+        v = w.v if r == 0 else w.v.clone()
+        kv = lsa.KVPool(w.dtype, k, v, Hkv, D, NP, w.logical_page, w.num_pages)
+        stats = torch.zeros(lsa.page_stats_bytes(kv), dtype=torch.uint8, device=dev)
+        lens0 = torch.tensor(w.ctx, dtype=torch.int32, device=dev)
+        lsa.build_page_stats(kv, w.page_table, lens0, stats, heads=hd)
+        sel = torch.full((B, Hkv, K), -1, dtype=torch.int32, device=dev)
+        layers.append((kv, stats, sel))
+    lens = [w.seq_lens(s) for s in range(R)]
+    first = [x - 1 for x in lens]
+    ws_sel = torch.empty(lsa.select_pages_workspace(layers[0][0], w.page_table, lens[0], hd), dtype=torch.uint8,
+                         device=dev)
+    ws_dec = torch.zeros(lsa.decode_workspace(layers[0][0], w.page_table, lens[0], hd, w.token_budget),
+                         dtype=torch.uint8, device=dev)
+    out = torch.empty_like(w.q[0])
+    cycle = nrep * R
+
+    def step(k, timers=None):
+        l, s = k % nrep, (k // nrep) % R
+        kv, stats, sel = layers[l]
+        lsa.build_page_stats(kv, w.page_table, lens[s], stats, heads=hd, first_token=first[s], max_new_tokens=1)
+        lsa.select_pages(w.q[s], kv, stats, w.page_table, lens[s], hd, w.token_budget, s, R, sel, ws_sel)
+        if timers is not None:
+            timers[0].record()
+        lsa.sparse_decode_attn(w.q[s], kv, w.page_table, lens[s], hd, sel, w.token_budget, out, ws_dec)
+        if timers is not None:
+            timers[1].record()
+
+    # warm-up (eager): every layer selects at least once
+    for k in range(max(args.warmup, cycle)):
+        step(k)
+    torch.cuda.synchronize()
+
+    n_cycles = max(1, math.ceil(args.steps / cycle))
+    steps = n_cycles * cycle
+    timing = "eager"
+    graph = None
+    if not args.eager:
+        try:
+            s = torch.cuda.Stream()
+            s.wait_stream(torch.cuda.current_stream())
+            with torch.cuda.stream(s):
+                for k in range(cycle):            # one more eager cycle on the capture stream
+                    step(k)
+            torch.cuda.current_stream().wait_stream(s)
+            torch.cuda.synchronize()
+            graph = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(graph):
+                for k in range(cycle):
+                    step(k)
+            graph.replay()
+            torch.cuda.synchronize()
+            timing = "hip-graph replay"
+        except Exception as e:  # capture not available: time eager launches
+            print(f"# graph capture failed ({e}); timing eager launches", file=sys.stderr)
+            graph = None
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0.record()
+    if graph is not None:
+        for _ in range(n_cycles):
+            graph.replay()
+    else:
+        for k in range(steps):
+            step(k)
+    t1.record()
+    torch.cuda.synchronize()
+    elapsed = t0.elapsed_time(t1) / 1e3
+
+    # per-launch duration of the decode attention kernel, HIP events on its
+    # stream; a spin kernel holds the queue while the host enqueues the steps
+    n_kt = cycle * 4
+    timers = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n_kt)]
+    torch.cuda.synchronize()
+    torch.cuda._sleep(int(2.4e9 * 0.25))        # ~0.25 s at 2.4 GHz
+    for k in range(n_kt):
+        step(k, timers[k])
+    torch.cuda.synchronize()
+    kt = sorted(a.elapsed_time(b) / 1e3 for a, b in timers)
+    kernel_avg = sum(kt) / len(kt)
+
+    # algorithmic bytes of one attention launch: the attended keys and values
+    # of every (sequence, KV head) at the measured window steps, plus q and o
+    sel_h = [layers[0][2].cpu()]
+    att_tokens = 0
+    for s in range(R):
+        for b in range(B):
+            t = w.ctx[b] + s
+            for kvh in range(Hkv):
+                if w.head_kind[kvh] == 0:
+                    pages = set(int(m) for m in sel_h[0][b, kvh].tolist() if m >= 0)
+                    pages.add(t // NP)
+                    att_tokens += sum(min(NP, t + 1 - m * NP) for m in pages)
+                else:
+                    att_tokens += min(t + 1, w.sink_tokens + w.local_tokens)
+    att_tokens /= R
+    kv_bytes = att_tokens * D * 2 * 2
+    qo_bytes = 2 * B * Hq * D * 2
+    launch_bytes = kv_bytes + qo_bytes
+    # whole step: + statistics refresh + selection amortised over R
+    n_ret = sum(1 for x in w.head_kind if x == 0)
+    sel_bytes = B * n_ret * (w.ctx[0] + 1 + w.logical_page - 1) // w.logical_page * 2 * D * 2 / R
+    step_bytes = launch_bytes + sel_bytes
+    tok_s = B * steps / elapsed
+    src = os.path.join(ROOT, "block_sparse_attention_logical_amd", "csrc", "decode.hip")
+    return dict(
+        w=w, steps=steps, elapsed=elapsed, tok_s=tok_s, ms_per_step=elapsed / steps * 1e3,
+        step_bytes=step_bytes, launch_bytes=launch_bytes, kernel_avg=kernel_avg,
+        kernel_p50=kt[len(kt) // 2], timing=timing,
+        traffic=counters_for("decode_attn_cfg2", src, launch_bytes),
+    )
+
+
+# ---------------------------------------------------------------------------
+# prefill (config 3)
+# ---------------------------------------------------------------------------
+
+def bench_prefill(args, torch, lsa, W, O):
+    dev = "cuda"
+    p = W.make_prefill(3, dev)
+    kv = lsa.KVPool(p.dtype, p.k, p.v, p.num_kv_heads, p.head_dim, p.page_size, p.logical_page, p.num_pages)
+    hd = lsa.Heads(p.head_kind, p.num_q_heads, 0, 1, p.sink_blocks, p.local_blocks)
+    out = torch.empty_like(p.q)
+    lsa.sparse_prefill_attn(p.q, kv, p.page_table, p.seq_len, hd, out)      # warm-up
+    torch.cuda.synchronize()
+    times = []
+    for _ in range(max(1, args.prefill_reps)):
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        a.record()
+        lsa.sparse_prefill_attn(p.q, kv, p.page_table, p.seq_len, hd, out)
+        b.record()
+        torch.cuda.synchronize()
+        times.append(a.elapsed_time(b) / 1e3)
+    n = -(-p.seq_len // 64)
+    G = p.num_q_heads // p.num_kv_heads
+    tiles = sum(G * O.block_counts(n, p.head_kind[kvh], p.sink_blocks, p.local_blocks)[0]
+                for kvh in range(p.num_kv_heads))
+    dense = p.num_q_heads * n * (n + 1) // 2
+    flop = tiles * 4 * 64 * 64 * p.head_dim
+    t = sorted(times)[len(times) // 2]
+    del out, p
+    torch.cuda.empty_cache()
+    return dict(seconds=t, flop=flop, tiles=tiles, dense_tiles=dense, tflops=flop / t / 1e12)
+
+
+# ---------------------------------------------------------------------------
+# oracle CPU baseline (bounded sample)
+# ---------------------------------------------------------------------------
+
+def cpu_baseline(dec, torch, O, budget_s):
+    import numpy as np
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    except Exception:  # pragma: no cover
+        threads = 1
+    w = dec["w"]
+    G = w.num_q_heads // w.num_kv_heads
+    spec = O.DecodeSpec(w.num_q_heads, w.num_kv_heads, list(w.head_kind), w.logical_page, w.page_size,
+                        w.token_budget, w.reuse_interval, w.sink_tokens, w.local_tokens)
+    done = 0
+    t_total = 0.0
+    b = 0
+    while t_total < budget_s and b < w.batch:
+        L = w.ctx[b] + 1
+        n = -(-L // w.page_size)
+        rows = w.page_table[b, :n].long()
+        keys, vals = [], []
+        for kvh in range(w.num_kv_heads):
+            pool = O.Pool("bf16", w.k[rows, kvh][:, None].cpu().view(torch.int16).numpy().view(np.uint16),
+                          w.v[rows, kvh][:, None].cpu().view(torch.int16).numpy().view(np.uint16),
+                          w.page_size, w.head_dim)
+            keys.append(pool.keys(list(range(n)), 0, L))
+            vals.append(pool.values(list(range(n)), 0, L))
+        q = O.bf16_bits_to_f64(w.q[0, b].cpu().view(torch.int16).numpy().view(np.uint16))
+        t0 = time.perf_counter()
+        O.decode_step(spec, q, keys, vals, None, True)       # a selection step: stats, scores, top-K, attention
+        t_total += time.perf_counter() - t0
+        done += 1
+        b += 1
+    # one selection step per sequence; a window of R steps selects once, so
+    # the steady-state cost per token is below this selection-step cost
+    return dict(value=done / t_total, unit="tokens/s", cores=threads, kind="oracle",
+                sample=f"{done} sequence(s) x 1 decode step with page selection (64K context, all 8 KV heads, "
+                       f"fp64 NumPy), {t_total:.1f} s")
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build runs on one GPU; --gpus must be 1 "
+                                   "(the path shards by (sequence, KV head) with no communication, "
+                                   "but no multi-GPU run is built)"}))
+        sys.exit(2)
+    import torch
+    import oracle.lsa_oracle as O
+    from block_sparse_attention_logical_amd import lsa, workloads as W
+    torch.cuda.set_device(0)
+    lsa.load()
+
+    if args.counters:
+        counters_run(args, torch, lsa, W)
+        return
+    dec = bench_decode(args, torch, lsa, W)
+    pre = None if args.no_prefill else bench_prefill(args, torch, lsa, W, O)
+    cpu = None if args.no_cpu_baseline else cpu_baseline(dec, torch, O, args.cpu_seconds)
+
+    w = dec["w"]
+    achieved = dec["launch_bytes"] / dec["kernel_avg"]
+    line = {
+        "metric": "sparse decode attn tokens/s + HBM GB/s at 64K; prefill sparse TFLOP/s at 128K",
+        "value": round(dec["tok_s"], 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": dec["steps"],
+        "warmup": args.warmup,
+        "ms_per_step": round(dec["ms_per_step"], 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded; shapes of the LServe Llama-3-8B decode workload)",
+        "config": {
+            "workload": "decode, one Llama-3-8B-shaped attention layer: B=8, context 65536, 32 q heads / 8 KV heads "
+                        "(4 streaming: sink 64 + local 1024 tokens), D=128, N_L=16, N_P=64, token budget 4096, "
+                        "reuse interval 4; one step = stats refresh + selection (every 4th step) + attention",
+            "global_batch": w.batch, "seq_len": w.ctx[0], "parallelism": "none (1 GPU)",
+            "kv_replicas": args.replicas, "timing": dec["timing"],
+        },
+        "decode_hbm_gbps": round(dec["step_bytes"] / (dec["ms_per_step"] / 1e3) / 1e9, 1),
+        "decode_step_bytes": int(dec["step_bytes"]),
+        "roofline": {
+            "kernel": "decode_bf16_kernel (lsa_sparse_decode_attn)",
+            "bound": "hbm", "achieved": round(achieved / 1e9, 1), "peak": PEAK_HBM / 1e9, "unit": "GB/s",
+            "frac": round(achieved / PEAK_HBM, 4),
+            "traffic": dec["traffic"],
+            "bytes_per_launch": int(dec["launch_bytes"]),
+            "launch_us": round(dec["kernel_avg"] * 1e6, 2),
+        },
+        "cpu_baseline": cpu,
+    }
+    if pre is not None:
+        line["prefill"] = {
+            "workload": "prefill, 131072 tokens, 32 q heads / 8 KV heads (4 causal retrieval, 4 streaming with "
+                        "1 sink + 16 local tiles), D=128, 64x64 tiles, bf16",
+            "ms": round(pre["seconds"] * 1e3, 3),
+            "tflops": round(pre["tflops"], 1),
+            "nonempty_tile_heads": pre["tiles"],
+            "dense_causal_tile_heads": pre["dense_tiles"],
+            "theoretical_speedup": round(pre["dense_tiles"] / pre["tiles"], 4),
+            "roofline": {"bound": "mfma", "achieved": round(pre["tflops"], 1), "peak": PEAK_BF16 / 1e12,
+                         "unit": "TFLOP/s", "frac": round(pre["tflops"] * 1e12 / PEAK_BF16, 4), "traffic": None},
+        }
+    print(json.dumps(line))
+
+
+if __name__ == "__main__":
+    main()

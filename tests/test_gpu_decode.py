@@ -31,7 +31,7 @@ class Runner:
         self.selected = torch.full((w.batch, w.num_kv_heads, self.K), -1, dtype=torch.int32, device=DEV)
         self.ws_sel = torch.empty(lsa.select_pages_workspace(self.kv, w.page_table, lens0, self.hd),
                                   dtype=torch.uint8, device=DEV)
-        self.ws_dec = torch.empty(lsa.decode_workspace(self.kv, w.page_table, lens0, self.hd, w.token_budget),
+        self.ws_dec = torch.zeros(lsa.decode_workspace(self.kv, w.page_table, lens0, self.hd, w.token_budget),
                                   dtype=torch.uint8, device=DEV)
 
     def step(self, i):
