@@ -258,8 +258,7 @@ lsa_status lsa_decode_workspace(const lsa_kv *kv, const lsa_seqs *seqs, const ls
         return fail(LSA_ERR_INVALID_ARG, "token_budget %d is not a positive multiple of page_size %d", token_budget,
                     kv->page_size);
     const DecodeGeom g = decode_geometry(kv, heads, token_budget);
-    *bytes = align_up((size_t)seqs->batch * kv->num_kv_heads * sizeof(unsigned)) +
-             align_up((size_t)seqs->batch * kv->num_kv_heads * g.chunks_max * g.rec_floats * sizeof(float));
+    *bytes = align_up((size_t)seqs->batch * kv->num_kv_heads * g.chunks_max * g.rec_floats * sizeof(float));
     return ok();
 }
 
@@ -298,9 +297,7 @@ lsa_status lsa_sparse_decode_attn(const void *q, int32_t q_dtype, const lsa_kv *
     a.page_table = seqs->page_table;
     a.seq_lens = seqs->seq_lens;
     a.selected = selected;
-    a.counters = static_cast<unsigned *>(workspace);
-    a.part = reinterpret_cast<float *>(static_cast<char *>(workspace) +
-                                       align_up((size_t)seqs->batch * kv->num_kv_heads * sizeof(unsigned)));
+    a.part = static_cast<float *>(workspace);
     a.batch = seqs->batch;
     a.max_pages = seqs->max_pages;
     a.num_q_heads = heads->num_q_heads;
@@ -319,7 +316,9 @@ lsa_status lsa_sparse_decode_attn(const void *q, int32_t q_dtype, const lsa_kv *
     const float scale = softmax_scale > 0.f ? softmax_scale : 1.f / std::sqrt((float)kv->head_dim);
     a.scale_log2 = scale * 1.4426950408889634f;
     for (int i = 0; i < kv->num_kv_heads; ++i) a.kind[i] = heads->head_kind[i];
-    return from_hip(launch_decode(a, q_dtype, kv->kv_dtype, (hipStream_t)stream), "decode launch");
+    if (lsa_status s = from_hip(launch_decode(a, q_dtype, kv->kv_dtype, (hipStream_t)stream), "decode launch"))
+        return s;
+    return from_hip(launch_combine(a, q_dtype, (hipStream_t)stream), "decode combine launch");
 }
 
 lsa_status lsa_sparse_prefill_attn(const void *q, int32_t q_dtype, const lsa_kv *kv, const int32_t *page_table,

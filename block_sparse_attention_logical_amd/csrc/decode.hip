@@ -9,9 +9,9 @@
 // head) is cut into chunks of 4 * pages_per_wave pages; one workgroup of four
 // wavefronts takes a chunk, each wavefront streams its pages with an online
 // softmax, the four states are merged in LDS and one partial record
-// (max, sum, unnormalised output) is written per chunk.  The last workgroup
-// of a (sequence, KV head) to finish merges the records in chunk order, so
-// one launch does the whole call and results are deterministic.  Every K/V page read serves all G query heads of the
+// (max, sum, unnormalised output) is written per chunk.  A second, small
+// kernel merges the records of each (sequence, KV head) in chunk order, so
+// results are deterministic.  Every K/V page read serves all G query heads of the
 // group.
 //
 // bf16 path: both contractions run on v_mfma_f32_16x16x32_bf16 straight from
@@ -140,7 +140,9 @@ __device__ __forceinline__ void merge_waves_and_store(const DecodeArgs &a, const
 }
 
 // ---------------------------------------------------------------------------
-// split-KV combine, done by the last workgroup of a (sequence, KV head)
+// split-KV combine (a second kernel: the kernel boundary orders the records,
+// so no device-scope fence, which would write back and invalidate the whole
+// L2 of the XCD, is needed)
 // ---------------------------------------------------------------------------
 // Merge the chunk records of (b, kv) in chunk order (deterministic) and write
 // the normalised output in q's dtype.
@@ -153,44 +155,21 @@ __device__ __forceinline__ void combine_records(const DecodeArgs &a, int b, int 
     for (int idx = threadIdx.x; idx < G * D; idx += blockDim.x) {
         const int h = idx / D;
         float M = -__builtin_inff();
-        for (int c = 0; c < nchunks; ++c) M = fmaxf(M, __builtin_nontemporal_load(&rec0[c * rec_size + h]));
+        for (int c = 0; c < nchunks; ++c) M = fmaxf(M, rec0[c * rec_size + h]);
         float acc = 0.f, lsum = 0.f;
         for (int c = 0; c < nchunks; ++c) {
             const float *rec = rec0 + c * rec_size;
-            const float mc = __builtin_nontemporal_load(&rec[h]);
+            const float mc = rec[h];
             if (mc == -__builtin_inff()) continue;
             const float wt = exp2_fast(mc - M);
-            acc += wt * __builtin_nontemporal_load(&rec[32 + idx]);
-            lsum += wt * __builtin_nontemporal_load(&rec[16 + h]);
+            acc += wt * rec[32 + idx];
+            lsum += wt * rec[16 + h];
         }
         const float val = acc / lsum;
         const size_t o = ((size_t)b * a.num_q_heads + (size_t)kv * G) * D + idx;
         if constexpr (sizeof(OutT) == 2) static_cast<uint16_t *>(a.out)[o] = f32_to_bf16_rne(val);
         else static_cast<float *>(a.out)[o] = val;
     }
-}
-
-// After this workgroup's record is written: count it, and if it is the last
-// chunk of its (sequence, KV head) to finish, merge all chunks.  Every thread
-// fences its own record stores before the barrier so that the count is only
-// published after every record is visible device-wide; the counter is reset
-// by the last workgroup, leaving the workspace ready for the next call.
-template <typename OutT>
-__device__ __forceinline__ void finish_chunk(const DecodeArgs &a, const WorkItem &w) {
-    __shared__ int s_last;
-    __threadfence();
-    __syncthreads();
-    if (threadIdx.x == 0) {
-        const unsigned n = a.kind[w.kv] ? a.chunks_str : a.chunks_ret;
-        unsigned *ctr = a.counters + (size_t)w.b * a.num_kv_heads + w.kv;
-        const unsigned prev = atomicAdd(ctr, 1u);
-        s_last = prev == n - 1;
-        if (s_last) atomicExch(ctr, 0u);
-    }
-    __syncthreads();
-    if (!s_last) return;
-    __threadfence();
-    combine_records<OutT>(a, w.b, w.kv);
 }
 
 // ---------------------------------------------------------------------------
@@ -317,7 +296,6 @@ __global__ __launch_bounds__(256) void decode_bf16_kernel(DecodeArgs a) {
         for (int r = 0; r < 4; ++r) my[32 + h * D + 16 * dt + 4 * g4 + r] = o[dt][r];
     __syncthreads();
     merge_waves_and_store(a, w, lds, D);
-    finish_chunk<uint16_t>(a, w);
 }
 
 // ---------------------------------------------------------------------------
@@ -435,7 +413,11 @@ __global__ __launch_bounds__(256) void decode_f32_kernel(DecodeArgs a) {
     }
     __syncthreads();
     merge_waves_and_store(a, w, lds, D);
-    finish_chunk<float>(a, w);
+}
+
+template <typename OutT>
+__global__ __launch_bounds__(256) void combine_kernel(DecodeArgs a) {
+    combine_records<OutT>(a, blockIdx.x / a.num_kv_heads, blockIdx.x % a.num_kv_heads);
 }
 
 }  // namespace
@@ -461,5 +443,13 @@ hipError_t launch_decode(const DecodeArgs &a, int q_dtype, int kv_dtype, hipStre
     return hipGetLastError();
 }
 
+
+hipError_t launch_combine(const DecodeArgs &a, int q_dtype, hipStream_t s) {
+    const long long grid = (long long)a.batch * a.num_kv_heads;
+    if (grid == 0) return hipSuccess;
+    if (q_dtype == LSA_BF16) hipLaunchKernelGGL(combine_kernel<uint16_t>, dim3((unsigned)grid), dim3(256), 0, s, a);
+    else hipLaunchKernelGGL(combine_kernel<float>, dim3((unsigned)grid), dim3(256), 0, s, a);
+    return hipGetLastError();
+}
 
 }  // namespace lsa

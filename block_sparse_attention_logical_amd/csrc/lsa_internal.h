@@ -90,7 +90,6 @@ struct DecodeArgs {
     const int32_t *seq_lens;
     const int32_t *selected;
     float *part;                  // partial records
-    unsigned *counters;           // [B][H_kv] finished-chunk counts, zero between calls
     int32_t batch, max_pages, num_q_heads, num_kv_heads, group, head_dim, page_size;
     int32_t sel_k;                // K (row length of selected)
     int32_t sink, local;
@@ -128,6 +127,7 @@ hipError_t launch_stats(const StatsArgs &a, hipStream_t s);
 hipError_t launch_score(const ScoreArgs &a, hipStream_t s);
 hipError_t launch_topk(const TopkArgs &a, hipStream_t s);
 hipError_t launch_decode(const DecodeArgs &a, int q_dtype, int kv_dtype, hipStream_t s);
+hipError_t launch_combine(const DecodeArgs &a, int q_dtype, hipStream_t s);
 hipError_t launch_prefill(const PrefillArgs &a, int dtype, hipStream_t s);
 
 }  // namespace lsa

@@ -188,10 +188,10 @@ lsa_status lsa_decode_workspace(const lsa_kv *kv, const lsa_seqs *seqs,
  * selected: [B][H_kv][K] as written by lsa_select_pages (rows of streaming
  * heads are not read; may be NULL when every head is a streaming head).
  * softmax_scale: 0 means 1 / sqrt(head_dim).
- * workspace: at least lsa_decode_workspace bytes, 256-byte aligned, and
- * zero-filled before its first use; every call leaves it ready for the next
- * one (its counters back at zero).  Calls that share a workspace must not
- * overlap in time (same stream, or ordered). */
+ * workspace: at least lsa_decode_workspace bytes, 256-byte aligned; calls
+ * that share a workspace must not overlap in time (same stream, or ordered).
+ * Two kernels are launched: the split-KV pass and the merge of its partial
+ * results. */
 lsa_status lsa_sparse_decode_attn(const void *q, int32_t q_dtype, const lsa_kv *kv,
                                   const lsa_seqs *seqs, const lsa_heads *heads,
                                   const int32_t *selected, int32_t token_budget,
