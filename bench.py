@@ -6,8 +6,9 @@ Metric: sparse decode attention tokens/s and HBM GB/s at a 64K context
 at a 128K context.  One printed JSON line.
 
 Decode.  A step is one decode step of one attention layer for the whole batch:
-refresh the statistics of the current logical page, select pages (every
-R = 4 steps, reused otherwise), sparse decode attention.  Steps cycle over
+select pages (every R = 4 steps, reused otherwise; the current logical page
+is scored from its keys), then sparse decode attention, which also refreshes
+the statistics of the current logical page.  Steps cycle over
 `--replicas` independent copies of the layer's KV pool (distinct layers of a
 model), so every step reads its pages from HBM rather than from the 256 MB
 last-level cache.  A cycle of replicas x R steps is captured once as a HIP
@@ -115,7 +116,6 @@ def bench_decode(args, torch, lsa, W):
         sel = torch.full((B, Hkv, K), -1, dtype=torch.int32, device=dev)
         layers.append((kv, stats, sel))
     lens = [w.seq_lens(s) for s in range(R)]
-    first = [x - 1 for x in lens]
     ws_sel = torch.empty(lsa.select_pages_workspace(layers[0][0], w.page_table, lens[0], hd), dtype=torch.uint8,
                          device=dev)
     ws_dec = torch.zeros(lsa.decode_workspace(layers[0][0], w.page_table, lens[0], hd, w.token_budget),
@@ -126,11 +126,11 @@ def bench_decode(args, torch, lsa, W):
     def step(k, timers=None):
         l, s = k % nrep, (k // nrep) % R
         kv, stats, sel = layers[l]
-        lsa.build_page_stats(kv, w.page_table, lens[s], stats, heads=hd, first_token=first[s], max_new_tokens=1)
         lsa.select_pages(w.q[s], kv, stats, w.page_table, lens[s], hd, w.token_budget, s, R, sel, ws_sel)
         if timers is not None:
             timers[0].record()
-        lsa.sparse_decode_attn(w.q[s], kv, w.page_table, lens[s], hd, sel, w.token_budget, out, ws_dec)
+        lsa.sparse_decode_attn(w.q[s], kv, w.page_table, lens[s], hd, sel, w.token_budget, out, ws_dec,
+                               stats=stats)
         if timers is not None:
             timers[1].record()
 
@@ -334,7 +334,7 @@ def main():
         "config": {
             "workload": "decode, one Llama-3-8B-shaped attention layer: B=8, context 65536, 32 q heads / 8 KV heads "
                         "(4 streaming: sink 64 + local 1024 tokens), D=128, N_L=16, N_P=64, token budget 4096, "
-                        "reuse interval 4; one step = stats refresh + selection (every 4th step) + attention",
+                        "reuse interval 4; one step = selection (every 4th step) + attention with the stats refresh",
             "global_batch": w.batch, "seq_len": w.ctx[0], "parallelism": "none (1 GPU)",
             "kv_replicas": args.replicas, "timing": dec["timing"],
         },

@@ -100,7 +100,7 @@ int count_kind(const lsa_heads *hd, int h_kv, int kind) {
 }
 
 constexpr int kPagesPerWave = 1;       // decode: pages per wavefront
-constexpr int kScorePagesPerBlock = 16;
+constexpr int kScorePagesPerBlock = 64;
 
 struct DecodeGeom {
     int K, chunks_ret, chunks_str, chunks_max, rec_floats;
@@ -207,6 +207,9 @@ lsa_status lsa_select_pages(const void *q, int32_t q_dtype, const lsa_kv *kv, co
     lsa_select_pages_workspace(kv, seqs, heads, &need);
     if (!workspace || workspace_bytes < need)
         return fail(LSA_ERR_WORKSPACE, "workspace of %zu bytes, need %zu", workspace_bytes, need);
+    if (seqs->max_pages > topk_max_pages())
+        return fail(LSA_ERR_UNSUPPORTED, "max_pages %d: page selection handles at most %d pages per sequence",
+                    seqs->max_pages, topk_max_pages());
     if (decode_step % reuse_interval != 0) return ok();     // reuse the previous selection
     const int n_ret = count_kind(heads, kv->num_kv_heads, LSA_RETRIEVAL_HEAD);
     if (n_ret == 0 || seqs->batch == 0) return ok();
@@ -214,6 +217,7 @@ lsa_status lsa_select_pages(const void *q, int32_t q_dtype, const lsa_kv *kv, co
     ScoreArgs sa{};
     sa.q = q;
     sa.stats = stats;
+    sa.k = kv->k;
     sa.k_sz = kv->k_sz;
     sa.page_table = seqs->page_table;
     sa.seq_lens = seqs->seq_lens;
@@ -230,8 +234,8 @@ lsa_status lsa_select_pages(const void *q, int32_t q_dtype, const lsa_kv *kv, co
     sa.n_ret = 0;
     for (int i = 0; i < kv->num_kv_heads; ++i)
         if (heads->head_kind[i] == LSA_RETRIEVAL_HEAD) sa.ret_heads[sa.n_ret++] = (uint8_t)i;
-    sa.pages_per_block = kScorePagesPerBlock;
-    sa.blocks_per_head = (seqs->max_pages + kScorePagesPerBlock - 1) / kScorePagesPerBlock;
+    sa.pages_per_block = std::min(kScorePagesPerBlock, score_max_pages_per_block(kv->page_size, kv->logical_page));
+    sa.blocks_per_head = (seqs->max_pages + sa.pages_per_block - 1) / sa.pages_per_block;
     if (lsa_status s = from_hip(launch_score(sa, (hipStream_t)stream), "select_pages score launch")) return s;
 
     TopkArgs ta{};
@@ -264,15 +268,14 @@ lsa_status lsa_decode_workspace(const lsa_kv *kv, const lsa_seqs *seqs, const ls
 
 lsa_status lsa_sparse_decode_attn(const void *q, int32_t q_dtype, const lsa_kv *kv, const lsa_seqs *seqs,
                                   const lsa_heads *heads, const int32_t *selected, int32_t token_budget,
-                                  float softmax_scale, void *out, void *workspace, size_t workspace_bytes,
-                                  void *stream) {
+                                  float softmax_scale, void *out, void *stats, void *workspace,
+                                  size_t workspace_bytes, void *stream) {
     if (lsa_status s = check_kv(kv)) return s;
     if (lsa_status s = check_seqs(seqs)) return s;
     if (lsa_status s = check_heads(heads, kv, true)) return s;
     const bool pair_ok = (q_dtype == LSA_F32 && kv->kv_dtype == LSA_F32) ||
-                         (q_dtype == LSA_BF16 && kv->kv_dtype == LSA_BF16);
-    if (q_dtype == LSA_BF16 && kv->kv_dtype == LSA_INT4)
-        return fail(LSA_ERR_UNSUPPORTED, "int4 decode attention is not built in this library version");
+                         (q_dtype == LSA_BF16 && kv->kv_dtype == LSA_BF16) ||
+                         (q_dtype == LSA_BF16 && kv->kv_dtype == LSA_INT4);
     if (!pair_ok)
         return fail(LSA_ERR_UNSUPPORTED, "(q_dtype %d, kv_dtype %d) is not a supported pair", q_dtype, kv->kv_dtype);
     if (!q || !out) return fail(LSA_ERR_INVALID_ARG, "q and out must be non-NULL");
@@ -287,6 +290,9 @@ lsa_status lsa_sparse_decode_attn(const void *q, int32_t q_dtype, const lsa_kv *
     if (seqs->batch == 0) return ok();
 
     const DecodeGeom g = decode_geometry(kv, heads, token_budget);
+    if (g.chunks_max > kMaxDecodeChunks)
+        return fail(LSA_ERR_UNSUPPORTED, "token budget / Lambda window spans %d split-KV chunks (limit %d)",
+                    g.chunks_max, kMaxDecodeChunks);
     DecodeArgs a{};
     a.q = q;
     a.out = out;
@@ -298,6 +304,8 @@ lsa_status lsa_sparse_decode_attn(const void *q, int32_t q_dtype, const lsa_kv *
     a.seq_lens = seqs->seq_lens;
     a.selected = selected;
     a.part = static_cast<float *>(workspace);
+    a.stats = stats;
+    a.logical_page = kv->logical_page;
     a.batch = seqs->batch;
     a.max_pages = seqs->max_pages;
     a.num_q_heads = heads->num_q_heads;

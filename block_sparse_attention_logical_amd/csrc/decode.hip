@@ -3,7 +3,7 @@
 // and the recent tokens; 動的スパーシティ and the figure: retrieval heads read
 // only their top-K physical pages; 統一ブロックスパースアテンション: one
 // block-sparse kernel serves both head kinds; abstract page: a constant number
-// of KV pages per step).
+// of KV pages per step; the KV4 co-design pairs the sparse path with 4-bit KV).
 //
 // Work decomposition (split-KV).  The attended page list of a (sequence, KV
 // head) is cut into chunks of 4 * pages_per_wave pages; one workgroup of four
@@ -11,17 +11,26 @@
 // softmax, the four states are merged in LDS and one partial record
 // (max, sum, unnormalised output) is written per chunk.  A second, small
 // kernel merges the records of each (sequence, KV head) in chunk order, so
-// results are deterministic.  Every K/V page read serves all G query heads of the
-// group.
+// results are deterministic.  The kernel boundary orders the records; a
+// device-scope fence instead (L2 writeback + invalidate per wave) measured
+// slower than the extra launch.  Every K/V page read serves all G query heads.
 //
-// bf16 path: both contractions run on v_mfma_f32_16x16x32_bf16 straight from
-// registers.  QK^T is computed transposed (tokens in M, heads in N), so a lane
-// loads 16 contiguous bytes of one key row; the 32 keys of a block are
-// assigned to MFMA rows so that the score tile a lane receives is exactly the
-// B operand the PV product needs (8 consecutive tokens of one head), and the
-// V page is stored channel-major so the A operand of PV (one channel, 8
-// consecutive tokens) is again one 16-byte load.  Heads occupy the N
-// dimension, padded to 16 with zero queries.
+// MFMA path (bf16 and int4 pools).  Both contractions run on
+// v_mfma_f32_16x16x32_bf16 straight from registers.  QK^T is computed
+// transposed (tokens in M, heads in N): a lane loads contiguous bytes of one
+// key row; the 32 keys of a block are placed on MFMA rows so that the score
+// registers a lane receives are exactly the B operand the PV product needs
+// (8 consecutive tokens of one head); the V page is channel-major, so the A
+// operand of PV (one channel, 8 consecutive tokens) is again one load.  Heads
+// occupy the N dimension, padded to 16 with zero queries.  All K and V loads
+// of kDecodeBlocksInFlight 32-token blocks are issued before their first MFMA.
+//
+// int4 pools.  A code c (0..15) becomes the bf16 bit pattern 0x4300 | c, which
+// is exactly 128 + c, so the MFMAs see exact operands; the offset and the
+// page's zero point come off afterwards: q.k = s_k (q.(128 + c) - (128 + z_k)
+// sum(q)), and for values the probabilities are pre-multiplied by s_v and the
+// per-head term (128 + z_v) * sum(p') is subtracted at the end, with p' the
+// very bf16 weights fed to the MFMA so the offset cancels exactly.
 #include "lsa_internal.h"
 
 namespace lsa {
@@ -47,8 +56,6 @@ __device__ __forceinline__ WorkItem decode_item(const DecodeArgs &a) {
     }
     w.kv = kv;
     w.chunk = off;
-    w.L = a.seq_lens[w.b];
-    w.t = w.L - 1;
     w.streaming = a.kind[kv] != 0;
     return w;
 }
@@ -56,12 +63,9 @@ __device__ __forceinline__ WorkItem decode_item(const DecodeArgs &a) {
 // The attended physical pages of one (sequence, KV head), in ascending order.
 struct PageList {
     int n;                 // list length
-    // retrieval
-    const int32_t *sel;
+    const int32_t *sel;    // retrieval: the selection row (ascending, -1 padded)
     int n_sel, cur;
-    bool cur_in;
-    // streaming
-    int n_sink_pages, local_first;
+    int n_sink_pages, local_first;   // streaming
 
     __device__ __forceinline__ int page(int i) const {
         if (sel) return i < n_sel ? sel[i] : cur;
@@ -69,32 +73,36 @@ struct PageList {
     }
 };
 
-__device__ __forceinline__ PageList make_list(const DecodeArgs &a, const WorkItem &w) {
+// Loads seq_lens[b] and (retrieval) the selection row in parallel, then builds
+// the list.  Sets w.t and w.L.
+__device__ __forceinline__ PageList make_list(const DecodeArgs &a, WorkItem &w) {
     PageList pl;
     const int NP = a.page_size;
+    const int lane = threadIdx.x % kWave;
+    const int32_t *sel = w.streaming ? nullptr : a.selected + ((size_t)w.b * a.num_kv_heads + w.kv) * a.sel_k;
+    int m0 = -1;
+    if (sel && lane < a.sel_k) m0 = sel[lane];         // issued together with the seq_lens load
+    w.L = a.seq_lens[w.b];
+    w.t = w.L - 1;
     pl.cur = w.t / NP;
+    pl.sel = sel;
     if (w.streaming) {
-        pl.sel = nullptr;
         pl.n_sel = 0;
-        pl.cur_in = false;
-        const int sink_end = min(a.sink, w.t + 1);            // tokens [0, sink_end)
+        const int sink_end = min(a.sink, w.t + 1);     // tokens [0, sink_end)
         pl.n_sink_pages = (sink_end + NP - 1) / NP;
-        const int lf = max(0, w.t - a.local + 1) / NP;         // first local page
+        const int lf = max(0, w.t - a.local + 1) / NP;  // first local page
         pl.local_first = max(lf, pl.n_sink_pages);
         pl.n = pl.n_sink_pages + max(0, pl.cur - pl.local_first + 1);
     } else {
-        pl.sel = a.selected + ((size_t)w.b * a.num_kv_heads + w.kv) * a.sel_k;
-        const int lane = threadIdx.x % kWave;
-        int cnt = 0;
-        bool in = false;
-        for (int i0 = 0; i0 < a.sel_k; i0 += kWave) {
+        int cnt = __popcll(__ballot(m0 >= 0));
+        bool in = __ballot(m0 == pl.cur) != 0;
+        for (int i0 = kWave; i0 < a.sel_k; i0 += kWave) {
             const int i = i0 + lane;
-            const int m = i < a.sel_k ? pl.sel[i] : -1;
+            const int m = i < a.sel_k ? sel[i] : -1;
             cnt += __popcll(__ballot(m >= 0));
             in |= __ballot(m == pl.cur) != 0;
         }
         pl.n_sel = cnt;
-        pl.cur_in = in;
         pl.n_sink_pages = 0;
         pl.local_first = 0;
         pl.n = cnt + (in ? 0 : 1);
@@ -106,6 +114,62 @@ __device__ __forceinline__ bool token_visible(const DecodeArgs &a, const WorkIte
     if (p > w.t) return false;
     if (!w.streaming) return true;
     return p < a.sink || (w.t - p) < a.local;
+}
+
+// Does the 32-token block starting at tok0 hold any attended token?
+__device__ __forceinline__ bool block_needed(const DecodeArgs &a, const WorkItem &w, int tok0) {
+    if (tok0 > w.t) return false;
+    if (!w.streaming) return true;
+    const int p_last = min(tok0 + 31, w.t);
+    return tok0 < a.sink || (w.t - p_last) < a.local;
+}
+
+// Recompute the statistics of the logical page that holds token t (retrieval
+// heads keep them for later selections).  One wavefront; lanes own channels.
+__device__ __forceinline__ void refresh_current_stats(const DecodeArgs &a, const WorkItem &w, int kv_dtype) {
+    const int lane = threadIdx.x % kWave;
+    const int NL = a.logical_page, NP = a.page_size, D = a.head_dim;
+    const int g = NP / NL;
+    const int j = w.t / NL;
+    const int m = j / g, jl = j % g;
+    const int row0 = jl * NL, rows = w.t - j * NL + 1;
+    const int pool = a.page_table[(size_t)w.b * a.max_pages + m];
+    const size_t hp = (size_t)pool * a.num_kv_heads + w.kv;
+    if (kv_dtype == LSA_INT4) {
+        if (lane >= D / 2) return;
+        const uint8_t *k = static_cast<const uint8_t *>(a.k) + (hp * NP + row0) * (D / 2) + lane;
+        uint32_t lo_min = 15, lo_max = 0, hi_min = 15, hi_max = 0;
+        for (int r = 0; r < rows; ++r) {
+            const uint32_t byte = k[(size_t)r * (D / 2)];
+            lo_min = min(lo_min, byte & 15u); lo_max = max(lo_max, byte & 15u);
+            hi_min = min(hi_min, byte >> 4); hi_max = max(hi_max, byte >> 4);
+        }
+        uint8_t *st = static_cast<uint8_t *>(a.stats) + (hp * g + jl) * D + 2 * lane;
+        *reinterpret_cast<uint16_t *>(st) = uint16_t((lo_min | (lo_max << 4)) | ((hi_min | (hi_max << 4)) << 8));
+        return;
+    }
+    const int cpl = D / 64;
+    for (int c = 0; c < cpl; ++c) {
+        const int ch = lane * cpl + c;
+        float mn = __builtin_inff(), mx = -__builtin_inff();
+        for (int r = 0; r < rows; ++r) {
+            float x;
+            if (kv_dtype == LSA_BF16)
+                x = bf16_to_f32(static_cast<const uint16_t *>(a.k)[(hp * NP + row0 + r) * D + ch]);
+            else
+                x = static_cast<const float *>(a.k)[(hp * NP + row0 + r) * D + ch];
+            mn = fminf(mn, x);
+            mx = fmaxf(mx, x);
+        }
+        const size_t base = ((hp * g + jl) * 2) * D + ch;
+        if (kv_dtype == LSA_BF16) {
+            static_cast<uint16_t *>(a.stats)[base] = uint16_t(__float_as_uint(mn) >> 16);
+            static_cast<uint16_t *>(a.stats)[base + D] = uint16_t(__float_as_uint(mx) >> 16);
+        } else {
+            static_cast<float *>(a.stats)[base] = mn;
+            static_cast<float *>(a.stats)[base + D] = mx;
+        }
+    }
 }
 
 // Merge the per-wave softmax states held in LDS and write this chunk's record.
@@ -139,161 +203,229 @@ __device__ __forceinline__ void merge_waves_and_store(const DecodeArgs &a, const
     }
 }
 
-// ---------------------------------------------------------------------------
-// split-KV combine (a second kernel: the kernel boundary orders the records,
-// so no device-scope fence, which would write back and invalidate the whole
-// L2 of the XCD, is needed)
-// ---------------------------------------------------------------------------
-// Merge the chunk records of (b, kv) in chunk order (deterministic) and write
-// the normalised output in q's dtype.
-template <typename OutT>
-__device__ __forceinline__ void combine_records(const DecodeArgs &a, int b, int kv) {
-    const int G = a.group, D = a.head_dim;
-    const int nchunks = a.kind[kv] ? a.chunks_str : a.chunks_ret;
-    const size_t rec_size = 32 + (size_t)G * D;
-    const float *rec0 = a.part + ((size_t)b * a.num_kv_heads + kv) * a.chunks_max * rec_size;
-    for (int idx = threadIdx.x; idx < G * D; idx += blockDim.x) {
-        const int h = idx / D;
-        float M = -__builtin_inff();
-        for (int c = 0; c < nchunks; ++c) M = fmaxf(M, rec0[c * rec_size + h]);
-        float acc = 0.f, lsum = 0.f;
-        for (int c = 0; c < nchunks; ++c) {
-            const float *rec = rec0 + c * rec_size;
-            const float mc = rec[h];
-            if (mc == -__builtin_inff()) continue;
-            const float wt = exp2_fast(mc - M);
-            acc += wt * rec[32 + idx];
-            lsum += wt * rec[16 + h];
-        }
-        const float val = acc / lsum;
-        const size_t o = ((size_t)b * a.num_q_heads + (size_t)kv * G) * D + idx;
-        if constexpr (sizeof(OutT) == 2) static_cast<uint16_t *>(a.out)[o] = f32_to_bf16_rne(val);
-        else static_cast<float *>(a.out)[o] = val;
-    }
+// bf16 bit patterns 0x4300 | c (= 128 + c) of the two nibbles of byte k of
+// `w`, low nibble in the low half of the returned dword.
+__device__ __forceinline__ uint32_t nibble_pair_bf16(uint32_t w, int k) {
+    const uint32_t b = (w >> (8 * k)) & 0xFFu;
+    return 0x43004300u | (b & 0x0Fu) | ((b & 0xF0u) << 12);
+}
+
+__device__ __forceinline__ uint32_t pick(const uint4 &u, int i) {
+    return i == 0 ? u.x : i == 1 ? u.y : i == 2 ? u.z : u.w;
 }
 
 // ---------------------------------------------------------------------------
-// bf16 K/V, bf16 q: MFMA path
+// MFMA kernel, bf16 or int4 pool, bf16 q
 // ---------------------------------------------------------------------------
-template <int D>
-__global__ __launch_bounds__(256) void decode_bf16_kernel(DecodeArgs a) {
+template <int D, int KVT, int BIF>
+__global__ __launch_bounds__(256) void decode_mfma_kernel(DecodeArgs a) {
+    constexpr bool I4 = KVT == LSA_INT4;
+    constexpr int NS = D / 32;            // MFMA k-steps over channels
+    constexpr int NDT = D / 16;           // output channel tiles
     extern __shared__ float lds[];
-    const WorkItem w = decode_item(a);
-    const PageList pl = make_list(a, w);
+    WorkItem w = decode_item(a);
     const int lane = threadIdx.x % kWave, wave = threadIdx.x / kWave;
     const int h = lane & 15, g4 = lane >> 4;
     const int G = a.group, NP = a.page_size;
 
-    // B operand of QK^T: column h = query head, k = channel s*32 + 8*g4 + j
-    bf16x8 qb[D / 32];
+    // B operand of QK^T: column h = query head.  bf16 pools: step s holds
+    // channels 32s + 8*g4 + j; int4 pools: channels (D/4)*g4 + 8s + j, so that a
+    // lane's steps cover one contiguous run of codes of its key row.
+    bf16x8 qb[NS];
+    float qsum = 0.f;                      // int4: sum over channels of q_h
     {
         const uint16_t *q = static_cast<const uint16_t *>(a.q) +
                             ((size_t)w.b * a.num_q_heads + (size_t)w.kv * G + min(h, G - 1)) * D;
 #pragma unroll
-        for (int s = 0; s < D / 32; ++s) {
-            uint4 raw = *reinterpret_cast<const uint4 *>(q + s * 32 + 8 * g4);
+        for (int s = 0; s < NS; ++s) {
+            uint4 raw = *reinterpret_cast<const uint4 *>(q + (I4 ? (D / 4) * g4 + 8 * s : 32 * s + 8 * g4));
             if (h >= G) raw = make_uint4(0, 0, 0, 0);
+            if constexpr (I4) {
+#pragma unroll
+                for (int e = 0; e < 4; ++e) qsum += bf16_lo(pick(raw, e)) + bf16_hi(pick(raw, e));
+            }
             qb[s] = __builtin_bit_cast(bf16x8, raw);
         }
+        if constexpr (I4) {
+            qsum += __shfl_xor(qsum, 16, kWave);
+            qsum += __shfl_xor(qsum, 32, kWave);
+        }
     }
+    const PageList pl = make_list(a, w);
 
-    floatx4 o[D / 16];
+    floatx4 o[NDT];
 #pragma unroll
-    for (int i = 0; i < D / 16; ++i) o[i] = floatx4{0.f, 0.f, 0.f, 0.f};
+    for (int i = 0; i < NDT; ++i) o[i] = floatx4{0.f, 0.f, 0.f, 0.f};
     float m_run = -__builtin_inff(), l_run = 0.f;
+    float corr = 0.f;                      // int4: (128 + z_v) * sum of fed weights (per lane)
 
     const int ppw = a.pages_per_wave;
     const int i_begin = w.chunk * 4 * ppw + wave * ppw;
     const int i_end = min(i_begin + ppw, pl.n);
-    const uint16_t *kpool = static_cast<const uint16_t *>(a.k);
-    const uint16_t *vpool = static_cast<const uint16_t *>(a.v);
+    // MFMA row rho of QK tile T holds key 8*(rho/4) + 4*T + rho%4 of its 32-key block
+    const int rho = lane & 15;
+    const int key_r = 8 * (rho >> 2) + (rho & 3);
 
     for (int i = i_begin; i < i_end; ++i) {
         const int page = pl.page(i);
         const int pool = a.page_table[(size_t)w.b * a.max_pages + page];
-        const size_t head_page = (size_t)pool * a.num_kv_heads + w.kv;
-        const uint16_t *kb_ptr = kpool + head_page * NP * D;
-        const uint16_t *vb_ptr = vpool + head_page * D * NP;
+        const size_t hp = (size_t)pool * a.num_kv_heads + w.kv;
+        float sk = 1.f, zk = 0.f, sv = 1.f, zv = 0.f;
+        if constexpr (I4) {
+            const uint32_t ksz = *reinterpret_cast<const uint32_t *>(a.k_sz + hp * 2);
+            const uint32_t vsz = *reinterpret_cast<const uint32_t *>(a.v_sz + hp * 2);
+            sk = fp16_bits_to_f32(uint16_t(ksz)); zk = fp16_bits_to_f32(uint16_t(ksz >> 16));
+            sv = fp16_bits_to_f32(uint16_t(vsz)); zv = fp16_bits_to_f32(uint16_t(vsz >> 16));
+        }
         const int p0 = page * NP;
-        for (int kb = 0; kb < NP / 32; ++kb) {
-            const int tok0 = p0 + 32 * kb;
-            if (tok0 > w.t) break;
-            if (w.streaming) {
-                const int p_last = min(tok0 + 31, w.t);
-                if (!(tok0 < a.sink || (w.t - p_last) < a.local)) continue;
-            }
-            // ---- QK^T for the 32 keys of this block (two 16-row tiles)
-            // tile T, MFMA row rho -> key 8*(rho/4) + 4*T + rho%4 of the block
-            const int rho = lane & 15;
-            const int key0 = 32 * kb + 8 * (rho >> 2) + (rho & 3);
-            floatx4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
+        for (int kb0 = 0; kb0 < NP / 32; kb0 += BIF) {
+            // ---- issue every K and V load of BIF 32-token blocks
+            bool need[BIF];
+            uint4 kr[BIF][2][I4 ? 1 : NS];
+            uint4 vr[BIF][I4 ? 1 : NDT];
+            uint32_t vr4[BIF][I4 ? NDT : 1];
 #pragma unroll
-            for (int s = 0; s < D / 32; ++s) {
-                const uint4 r0 = *reinterpret_cast<const uint4 *>(kb_ptr + (size_t)key0 * D + s * 32 + 8 * g4);
-                const uint4 r1 = *reinterpret_cast<const uint4 *>(kb_ptr + (size_t)(key0 + 4) * D + s * 32 + 8 * g4);
-                s0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, r0), qb[s], s0, 0, 0, 0);
-                s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, r1), qb[s], s1, 0, 0, 0);
-            }
-            // V^T loads for this block are independent of the softmax: issue them now
-            uint4 vr[D / 16];
+            for (int e = 0; e < BIF; ++e) {
+                const int kb = kb0 + e;
+                need[e] = kb < NP / 32 && block_needed(a, w, p0 + 32 * kb);
+                if (!need[e]) continue;
+                if constexpr (I4) {
+                    const uint8_t *kp = static_cast<const uint8_t *>(a.k) + (hp * NP + 32 * kb) * (D / 2);
 #pragma unroll
-            for (int dt = 0; dt < D / 16; ++dt)
-                vr[dt] = *reinterpret_cast<const uint4 *>(vb_ptr + (size_t)(16 * dt + h) * NP + 32 * kb + 8 * g4);
-            if (tok0 + 31 > w.t) {
-                // slots after the current token may hold any bits: zero them so that
-                // a zero probability never meets a NaN in the PV product
-                const int nvalid = w.t - (tok0 + 8 * g4) + 1;
-                uint32_t keep[4];
+                    for (int T = 0; T < 2; ++T) {
+                        const uint8_t *row = kp + (size_t)(key_r + 4 * T) * (D / 2) + (D / 8) * g4;
+                        if constexpr (D == 128) {
+                            kr[e][T][0] = *reinterpret_cast<const uint4 *>(row);
+                        } else {
+                            const uint2 u = *reinterpret_cast<const uint2 *>(row);
+                            kr[e][T][0] = make_uint4(u.x, u.y, 0, 0);
+                        }
+                    }
+                    const uint8_t *vp = static_cast<const uint8_t *>(a.v) + hp * D * (NP / 2);
 #pragma unroll
-                for (int e = 0; e < 4; ++e)
-                    keep[e] = (2 * e < nvalid ? 0x0000FFFFu : 0u) | (2 * e + 1 < nvalid ? 0xFFFF0000u : 0u);
+                    for (int dt = 0; dt < NDT; ++dt)
+                        vr4[e][dt] = *reinterpret_cast<const uint32_t *>(vp + (size_t)(16 * dt + h) * (NP / 2) + 16 * kb + 4 * g4);
+                } else {
+                    const uint16_t *kp = static_cast<const uint16_t *>(a.k) + (hp * NP + 32 * kb) * D;
 #pragma unroll
-                for (int dt = 0; dt < D / 16; ++dt) {
-                    vr[dt].x &= keep[0]; vr[dt].y &= keep[1]; vr[dt].z &= keep[2]; vr[dt].w &= keep[3];
+                    for (int T = 0; T < 2; ++T)
+#pragma unroll
+                        for (int s = 0; s < NS; ++s)
+                            kr[e][T][s] = *reinterpret_cast<const uint4 *>(kp + (size_t)(key_r + 4 * T) * D + 32 * s + 8 * g4);
+                    const uint16_t *vp = static_cast<const uint16_t *>(a.v) + hp * D * NP;
+#pragma unroll
+                    for (int dt = 0; dt < NDT; ++dt)
+                        vr[e][dt] = *reinterpret_cast<const uint4 *>(vp + (size_t)(16 * dt + h) * NP + 32 * kb + 8 * g4);
                 }
             }
-            // lane holds the logits of head h for keys 8*g4 + j, j = 0..7 of the block
-            float x[8];
 #pragma unroll
-            for (int r = 0; r < 4; ++r) { x[r] = s0[r] * a.scale_log2; x[4 + r] = s1[r] * a.scale_log2; }
-            float mb = -__builtin_inff();
+            for (int e = 0; e < BIF; ++e) {
+                if (!need[e]) continue;
+                const int tok0 = p0 + 32 * (kb0 + e);
+                // ---- scores of the 32 keys (two 16-row tiles)
+                floatx4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-            for (int j = 0; j < 8; ++j) {
-                if (!token_visible(a, w, tok0 + 8 * g4 + j)) x[j] = -__builtin_inff();
-                mb = fmaxf(mb, x[j]);
-            }
-            mb = fmaxf(mb, __shfl_xor(mb, 16, kWave));
-            mb = fmaxf(mb, __shfl_xor(mb, 32, kWave));
-            const float m_new = fmaxf(m_run, mb);
-            const float alpha = exp2_fast(m_run - m_new);
-            float psum = 0.f;
-            uint32_t pk[4];
+                for (int s = 0; s < NS; ++s) {
+                    bf16x8 k0, k1;
+                    if constexpr (I4) {
+                        const uint32_t w0 = pick(kr[e][0][0], s), w1 = pick(kr[e][1][0], s);
+                        k0 = __builtin_bit_cast(bf16x8, make_uint4(nibble_pair_bf16(w0, 0), nibble_pair_bf16(w0, 1),
+                                                                   nibble_pair_bf16(w0, 2), nibble_pair_bf16(w0, 3)));
+                        k1 = __builtin_bit_cast(bf16x8, make_uint4(nibble_pair_bf16(w1, 0), nibble_pair_bf16(w1, 1),
+                                                                   nibble_pair_bf16(w1, 2), nibble_pair_bf16(w1, 3)));
+                    } else {
+                        k0 = __builtin_bit_cast(bf16x8, kr[e][0][s]);
+                        k1 = __builtin_bit_cast(bf16x8, kr[e][1][s]);
+                    }
+                    s0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k0, qb[s], s0, 0, 0, 0);
+                    s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k1, qb[s], s1, 0, 0, 0);
+                }
+                // lane holds the logits of head h for keys 8*g4 + j, j = 0..7 of the block
+                float x[8];
+                if constexpr (I4) {
+                    const float off = (128.f + zk) * qsum;
+                    const float sc = sk * a.scale_log2;
 #pragma unroll
-            for (int j = 0; j < 8; j += 2) {
-                const float pa = exp2_fast(x[j] - m_new);
-                const float pb = exp2_fast(x[j + 1] - m_new);
-                psum += pa + pb;
-                pk[j / 2] = uint32_t(f32_to_bf16_rne(pa)) | (uint32_t(f32_to_bf16_rne(pb)) << 16);
-            }
-            l_run = l_run * alpha + psum;
-            m_run = m_new;
-            const bf16x8 pbv = __builtin_bit_cast(bf16x8, make_uint4(pk[0], pk[1], pk[2], pk[3]));
+                    for (int r = 0; r < 4; ++r) { x[r] = (s0[r] - off) * sc; x[4 + r] = (s1[r] - off) * sc; }
+                } else {
 #pragma unroll
-            for (int dt = 0; dt < D / 16; ++dt) {
-                o[dt] *= alpha;
-                o[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, vr[dt]), pbv, o[dt], 0, 0, 0);
+                    for (int r = 0; r < 4; ++r) { x[r] = s0[r] * a.scale_log2; x[4 + r] = s1[r] * a.scale_log2; }
+                }
+                float mb = -__builtin_inff();
+#pragma unroll
+                for (int j = 0; j < 8; ++j) {
+                    if (!token_visible(a, w, tok0 + 8 * g4 + j)) x[j] = -__builtin_inff();
+                    mb = fmaxf(mb, x[j]);
+                }
+                mb = fmaxf(mb, __shfl_xor(mb, 16, kWave));
+                mb = fmaxf(mb, __shfl_xor(mb, 32, kWave));
+                const float m_new = fmaxf(m_run, mb);
+                const float alpha = exp2_fast(m_run - m_new);
+                float psum = 0.f, fed = 0.f;
+                uint32_t pk[4];
+#pragma unroll
+                for (int j = 0; j < 8; j += 2) {
+                    const float pa = exp2_fast(x[j] - m_new);
+                    const float pb = exp2_fast(x[j + 1] - m_new);
+                    psum += pa + pb;
+                    uint16_t ba, bb;
+                    if constexpr (I4) {
+                        ba = f32_to_bf16_rne(pa * sv);
+                        bb = f32_to_bf16_rne(pb * sv);
+                        fed += bf16_to_f32(ba) + bf16_to_f32(bb);
+                    } else {
+                        ba = f32_to_bf16_rne(pa);
+                        bb = f32_to_bf16_rne(pb);
+                    }
+                    pk[j / 2] = uint32_t(ba) | (uint32_t(bb) << 16);
+                }
+                l_run = l_run * alpha + psum;
+                if constexpr (I4) corr = corr * alpha + (128.f + zv) * fed;
+                m_run = m_new;
+                const bf16x8 pbv = __builtin_bit_cast(bf16x8, make_uint4(pk[0], pk[1], pk[2], pk[3]));
+                // slots after the current token may hold any bits: zero their values so a
+                // zero probability never meets a NaN in the PV product
+                const bool tail = tok0 + 31 > w.t;
+                const int nvalid = w.t - (tok0 + 8 * g4) + 1;
+#pragma unroll
+                for (int dt = 0; dt < NDT; ++dt) {
+                    uint4 va;
+                    if constexpr (I4) {
+                        // 4 bytes = tokens 8*g4 .. 8*g4+7 of channel 16*dt + h
+                        const uint32_t wv4 = vr4[e][dt];
+                        va = make_uint4(nibble_pair_bf16(wv4, 0), nibble_pair_bf16(wv4, 1), nibble_pair_bf16(wv4, 2),
+                                        nibble_pair_bf16(wv4, 3));
+                    } else {
+                        va = vr[e][dt];
+                    }
+                    if (tail) {
+                        uint32_t keep[4];
+#pragma unroll
+                        for (int q2 = 0; q2 < 4; ++q2)
+                            keep[q2] = (2 * q2 < nvalid ? 0x0000FFFFu : 0u) | (2 * q2 + 1 < nvalid ? 0xFFFF0000u : 0u);
+                        va.x &= keep[0]; va.y &= keep[1]; va.z &= keep[2]; va.w &= keep[3];
+                    }
+                    o[dt] *= alpha;
+                    o[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, va), pbv, o[dt], 0, 0, 0);
+                }
             }
         }
     }
     l_run += __shfl_xor(l_run, 16, kWave);
     l_run += __shfl_xor(l_run, 32, kWave);
+    if constexpr (I4) {
+        // the head's correction sums the four lane groups' tokens
+        corr += __shfl_xor(corr, 16, kWave);
+        corr += __shfl_xor(corr, 32, kWave);
+    }
 
     float *my = lds + wave * (32 + 16 * D);
     if (g4 == 0) { my[h] = m_run; my[16 + h] = l_run; }
 #pragma unroll
-    for (int dt = 0; dt < D / 16; ++dt)
+    for (int dt = 0; dt < NDT; ++dt)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) my[32 + h * D + 16 * dt + 4 * g4 + r] = o[dt][r];
+        for (int r = 0; r < 4; ++r) my[32 + h * D + 16 * dt + 4 * g4 + r] = o[dt][r] - corr;
+    if (a.stats && !w.streaming && w.chunk == 0 && wave == 0) refresh_current_stats(a, w, KVT);
     __syncthreads();
     merge_waves_and_store(a, w, lds, D);
 }
@@ -304,7 +436,7 @@ __global__ __launch_bounds__(256) void decode_bf16_kernel(DecodeArgs a) {
 template <int D>
 __global__ __launch_bounds__(256) void decode_f32_kernel(DecodeArgs a) {
     extern __shared__ float lds[];
-    const WorkItem w = decode_item(a);
+    WorkItem w = decode_item(a);
     const PageList pl = make_list(a, w);
     const int lane = threadIdx.x % kWave, wave = threadIdx.x / kWave;
     const int G = a.group, NP = a.page_size;
@@ -381,8 +513,6 @@ __global__ __launch_bounds__(256) void decode_f32_kernel(DecodeArgs a) {
                 ps[hh * 64 + lane] = pr;
             }
             __builtin_amdgcn_wave_barrier();
-            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
             const int nslots = max(0, min(min(kWave, NP - s0), w.t - (page * NP + s0) + 1));
 #pragma unroll
             for (int c = 0; c < CPL; ++c) {
@@ -411,26 +541,76 @@ __global__ __launch_bounds__(256) void decode_f32_kernel(DecodeArgs a) {
 #pragma unroll
         for (int c = 0; c < CPL; ++c) my[32 + hh * D + lane * CPL + c] = o[hh][c];
     }
+    if (a.stats && !w.streaming && w.chunk == 0 && wave == 0) refresh_current_stats(a, w, LSA_F32);
     __syncthreads();
     merge_waves_and_store(a, w, lds, D);
 }
 
+// ---------------------------------------------------------------------------
+// split-KV merge: one workgroup per (sequence, KV head).  Chunk weights are
+// formed once in LDS, then every thread sums its outputs over the chunks with
+// independent loads (fixed chunk order: deterministic).
+// ---------------------------------------------------------------------------
 template <typename OutT>
 __global__ __launch_bounds__(256) void combine_kernel(DecodeArgs a) {
-    combine_records<OutT>(a, blockIdx.x / a.num_kv_heads, blockIdx.x % a.num_kv_heads);
+    __shared__ float wt[kMaxDecodeChunks][16];
+    __shared__ float ms[kMaxDecodeChunks][16];
+    __shared__ float ls[kMaxDecodeChunks][16];
+    const int b = blockIdx.x / a.num_kv_heads, kv = blockIdx.x % a.num_kv_heads;
+    const int G = a.group, D = a.head_dim;
+    const int nchunks = a.kind[kv] ? a.chunks_str : a.chunks_ret;
+    const size_t rec_size = 32 + (size_t)G * D;
+    const float *rec0 = a.part + ((size_t)b * a.num_kv_heads + kv) * a.chunks_max * rec_size;
+    for (int i = threadIdx.x; i < nchunks * G; i += blockDim.x) {
+        const int c = i / G, hh = i % G;
+        ms[c][hh] = rec0[c * rec_size + hh];
+        ls[c][hh] = rec0[c * rec_size + 16 + hh];
+    }
+    __syncthreads();
+    if (threadIdx.x < G) {
+        const int hh = threadIdx.x;
+        float M = -__builtin_inff();
+        for (int c = 0; c < nchunks; ++c) M = fmaxf(M, ms[c][hh]);
+        float L = 0.f;
+        for (int c = 0; c < nchunks; ++c) {
+            const float e = ms[c][hh] == -__builtin_inff() ? 0.f : exp2_fast(ms[c][hh] - M);
+            wt[c][hh] = e;
+            L += e * ls[c][hh];
+        }
+        const float inv = 1.f / L;
+        for (int c = 0; c < nchunks; ++c) wt[c][hh] *= inv;
+    }
+    __syncthreads();
+    for (int idx = threadIdx.x; idx < G * D; idx += blockDim.x) {
+        const int hh = idx / D;
+        float acc = 0.f;
+#pragma unroll 8
+        for (int c = 0; c < nchunks; ++c) acc += wt[c][hh] * rec0[c * rec_size + 32 + idx];
+        const size_t o = ((size_t)b * a.num_q_heads + (size_t)kv * G) * D + idx;
+        if constexpr (sizeof(OutT) == 2) static_cast<uint16_t *>(a.out)[o] = f32_to_bf16_rne(acc);
+        else static_cast<float *>(a.out)[o] = acc;
+    }
 }
 
 }  // namespace
 
+constexpr int kDecodeBlocksInFlight = 1;
+
 hipError_t launch_decode(const DecodeArgs &a, int q_dtype, int kv_dtype, hipStream_t s) {
+    constexpr int BIF = kDecodeBlocksInFlight;
     const long long grid = (long long)a.batch * a.chunks_per_seq;
     if (grid == 0) return hipSuccess;
     const size_t lds_merge = 4 * (32 + 16 * (size_t)a.head_dim) * sizeof(float);
     if (q_dtype == LSA_BF16 && kv_dtype == LSA_BF16) {
         if (a.head_dim == 128)
-            hipLaunchKernelGGL(decode_bf16_kernel<128>, dim3((unsigned)grid), dim3(256), lds_merge, s, a);
+            hipLaunchKernelGGL((decode_mfma_kernel<128, LSA_BF16, BIF>), dim3((unsigned)grid), dim3(256), lds_merge, s, a);
         else
-            hipLaunchKernelGGL(decode_bf16_kernel<64>, dim3((unsigned)grid), dim3(256), lds_merge, s, a);
+            hipLaunchKernelGGL((decode_mfma_kernel<64, LSA_BF16, BIF>), dim3((unsigned)grid), dim3(256), lds_merge, s, a);
+    } else if (q_dtype == LSA_BF16 && kv_dtype == LSA_INT4) {
+        if (a.head_dim == 128)
+            hipLaunchKernelGGL((decode_mfma_kernel<128, LSA_INT4, BIF>), dim3((unsigned)grid), dim3(256), lds_merge, s, a);
+        else
+            hipLaunchKernelGGL((decode_mfma_kernel<64, LSA_INT4, BIF>), dim3((unsigned)grid), dim3(256), lds_merge, s, a);
     } else if (q_dtype == LSA_F32 && kv_dtype == LSA_F32) {
         const size_t lds = lds_merge + (16 * (size_t)a.head_dim + 4 * 16 * 64) * sizeof(float);
         if (a.head_dim == 128)
@@ -442,7 +622,6 @@ hipError_t launch_decode(const DecodeArgs &a, int q_dtype, int kv_dtype, hipStre
     }
     return hipGetLastError();
 }
-
 
 hipError_t launch_combine(const DecodeArgs &a, int q_dtype, hipStream_t s) {
     const long long grid = (long long)a.batch * a.num_kv_heads;

@@ -11,6 +11,7 @@ namespace lsa {
 
 constexpr int kMaxKvHeads = 64;   // H_kv limit (host-side tables live in kernel args)
 constexpr int kWave = 64;         // CDNA wavefront width
+constexpr int kMaxDecodeChunks = 128;   // split-KV chunks per (sequence, KV head)
 
 // ----------------------------------------------------------------------------
 // numeric helpers (device)
@@ -58,6 +59,7 @@ struct StatsArgs {
 struct ScoreArgs {
     const void *q;
     const void *stats;
+    const void *k;                // the key pool: the current logical page is scored from its keys
     const uint16_t *k_sz;
     const int32_t *page_table;
     const int32_t *seq_lens;
@@ -90,7 +92,8 @@ struct DecodeArgs {
     const int32_t *seq_lens;
     const int32_t *selected;
     float *part;                  // partial records
-    int32_t batch, max_pages, num_q_heads, num_kv_heads, group, head_dim, page_size;
+    void *stats;                  // may be null: refresh the current logical page's statistics
+    int32_t batch, max_pages, num_q_heads, num_kv_heads, group, head_dim, page_size, logical_page;
     int32_t sel_k;                // K (row length of selected)
     int32_t sink, local;
     int32_t chunks_ret, chunks_str;   // workgroups per (sequence, head) by kind
@@ -125,6 +128,8 @@ struct PrefillArgs {
 
 hipError_t launch_stats(const StatsArgs &a, hipStream_t s);
 hipError_t launch_score(const ScoreArgs &a, hipStream_t s);
+int score_max_pages_per_block(int page_size, int logical_page);
+int topk_max_pages();
 hipError_t launch_topk(const TopkArgs &a, hipStream_t s);
 hipError_t launch_decode(const DecodeArgs &a, int q_dtype, int kv_dtype, hipStream_t s);
 hipError_t launch_combine(const DecodeArgs &a, int q_dtype, hipStream_t s);

@@ -14,12 +14,16 @@
 // exact there), so S^j and P_m carry only fp64 rounding and the ranking is
 // decided in fp64.  For int4 keys k = (c - z) s with one (s, z) per physical
 // page and head, S^j = s * (sum_i Qp c_max + Qn c_min - z * sum_i (Qp + Qn)).
+// A group of lanes owns one logical page (one 16-byte load of its minima and
+// one of its maxima per lane); the logical page that holds the current token
+// is scored from the keys themselves.  Logical scores go to LDS and one
+// thread per physical page takes their max.
 //
-// Top-K.  Scores are mapped to order-preserving 64-bit keys; a most
-// significant digit first radix select (8-bit digits, histogram in LDS) finds
-// the K-th largest key; equal keys are taken in ascending page order (ties
-// to the lower page index); an ordered compaction writes the selected pages
-// in ascending order.
+// Top-K.  Scores are mapped to order-preserving 64-bit keys held in
+// registers; a most significant digit first radix select (8-bit digits,
+// histogram in LDS) finds the K-th largest key; equal keys are taken in
+// ascending page order (ties to the lower page index); an ordered compaction
+// writes the selected pages in ascending order.
 #include "lsa_internal.h"
 
 namespace lsa {
@@ -29,8 +33,11 @@ template <int EB, int D>
 struct ScoreShape {
     static constexpr int C = 16 / EB;        // channels per lane (one 16-byte load)
     static constexpr int LPL = D / C;        // lanes per logical page
-    static constexpr int LPP = kWave / LPL;  // logical pages per pass
+    static constexpr int LPP = kWave / LPL;  // logical pages per wavefront pass
 };
+
+constexpr int kScoreThreads = 256;
+constexpr int kMaxLogicalPerBlock = 1024;  // LDS slots for logical scores
 
 __device__ __forceinline__ double shfl_xor_d(double v, int m) { return __shfl_xor(v, m, kWave); }
 
@@ -43,42 +50,63 @@ __device__ __forceinline__ void load_q_pos_neg(const ScoreArgs &a, int b, int kv
     for (int c = 0; c < C; ++c) { qp[c] = 0.0; qn[c] = 0.0; }
     for (int h = 0; h < G; ++h) {
         const size_t row = ((size_t)b * a.num_q_heads + (size_t)kv * G + h) * a.head_dim + ch0;
+        float x[C];
+        if (a.q_dtype == LSA_BF16) {
+            const uint16_t *p = static_cast<const uint16_t *>(a.q) + row;
+#pragma unroll
+            for (int c = 0; c < C; c += 8) {
+                const uint4 u = *reinterpret_cast<const uint4 *>(p + c);
+                const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+                for (int e = 0; e < 8 && c + e < C; ++e) x[c + e] = (e & 1) ? bf16_hi(w[e / 2]) : bf16_lo(w[e / 2]);
+            }
+        } else {
+            const float *p = static_cast<const float *>(a.q) + row;
+#pragma unroll
+            for (int c = 0; c < C; c += 4) {
+                const float4 u = *reinterpret_cast<const float4 *>(p + c);
+                x[c] = u.x; x[c + 1] = u.y; x[c + 2] = u.z; x[c + 3] = u.w;
+            }
+        }
 #pragma unroll
         for (int c = 0; c < C; ++c) {
-            double x;
-            if (a.q_dtype == LSA_BF16) x = (double)bf16_to_f32(static_cast<const uint16_t *>(a.q)[row + c]);
-            else x = (double)static_cast<const float *>(a.q)[row + c];
-            qp[c] += fmax(x, 0.0);
-            qn[c] += fmin(x, 0.0);
+            const double v = (double)x[c];
+            qp[c] += fmax(v, 0.0);
+            qn[c] += fmin(v, 0.0);
         }
     }
 }
 
 // KV_DT: LSA_F32, LSA_BF16 (stats in that type) or LSA_INT4 (code stats).
 template <int KV_DT, int D>
-__global__ __launch_bounds__(256) void score_kernel(ScoreArgs a) {
+__global__ __launch_bounds__(kScoreThreads) void score_kernel(ScoreArgs a) {
     constexpr int EB = KV_DT == LSA_F32 ? 4 : (KV_DT == LSA_BF16 ? 2 : 1);
     using S = ScoreShape<EB, D>;
     constexpr int C = S::C, LPL = S::LPL, LPP = S::LPP;
+    constexpr int GROUPS = (kScoreThreads / kWave) * LPP;   // lane groups per workgroup
+    __shared__ double s_log[kMaxLogicalPerBlock];
 
     const int blk = blockIdx.x % a.blocks_per_head;
     const int rest = blockIdx.x / a.blocks_per_head;
     const int r = rest % a.n_ret;
     const int b = rest / a.n_ret;
     const int kv = a.ret_heads[r];
+    const int lane = threadIdx.x % kWave;
+    const int lg = (threadIdx.x / kWave) * LPP + lane / LPL;    // lane group in the workgroup
+    const int ch0 = (lane % LPL) * C;
+
+    double qp[C], qn[C];
+    load_q_pos_neg<C>(a, b, kv, ch0, qp, qn);
     const int L = a.seq_lens[b];
     const int n_pages = (L + a.page_size - 1) / a.page_size;
     const int m0 = blk * a.pages_per_block;
     if (m0 >= n_pages) return;
     const int m1 = min(m0 + a.pages_per_block, n_pages);
+    const int g = a.page_size / a.logical_page;
+    const int nlog = (L + a.logical_page - 1) / a.logical_page;
+    const int j0 = m0 * g, j1 = min(m1 * g, nlog);
+    const int j_cur = (L - 1) / a.logical_page;
 
-    const int lane = threadIdx.x % kWave;
-    const int wave = threadIdx.x / kWave;
-    const int lg = lane / LPL;              // lane group = logical page within a pass
-    const int ch0 = (lane % LPL) * C;
-
-    double qp[C], qn[C];
-    load_q_pos_neg<C>(a, b, kv, ch0, qp, qn);
     double qsum = 0.0;                      // int4 only: sum over all channels of Qp + Qn
     if constexpr (KV_DT == LSA_INT4) {
 #pragma unroll
@@ -86,87 +114,140 @@ __global__ __launch_bounds__(256) void score_kernel(ScoreArgs a) {
 #pragma unroll
         for (int off = 1; off < LPL; off <<= 1) qsum += shfl_xor_d(qsum, off);
     }
-
-    const int g = a.page_size / a.logical_page;
-    const int ge = min(g, LPP);             // lane groups per physical page in one pass
-    const int ppp = LPP / ge;               // physical pages per pass
-    const int npass = g / ge;               // passes per physical page
     const size_t head_stride = (size_t)g * (KV_DT == LSA_INT4 ? D : 2 * D);
+    const int NP = a.page_size;
 
-    for (int mp = m0 + wave * ppp; mp < m1; mp += 4 * ppp) {
-        const int m = mp + lg / ge;
-        const bool page_ok = m < m1;
-        int pool = 0;
+    // every lane group walks logical pages j0 + lg, j0 + lg + GROUPS, ...; the
+    // trip count is uniform so the lane-group reductions see whole wavefronts
+    const int n_iter = (j1 - j0 + GROUPS - 1) / GROUPS;
+#pragma unroll 2
+    for (int it = 0; it < n_iter; ++it) {
+        const int j = j0 + lg + it * GROUPS;
+        const bool ok = j < j1;
+        const int m = j / g, jl = j % g;
+        double acc = 0.0;
         double s_scale = 1.0, s_zero = 0.0;
-        if (page_ok) {
-            pool = a.page_table[(size_t)b * a.max_pages + m];
+        if (ok) {
+            const int pool = a.page_table[(size_t)b * a.max_pages + m];
+            const size_t hp = (size_t)pool * a.num_kv_heads + kv;
             if constexpr (KV_DT == LSA_INT4) {
-                const uint16_t *sz = a.k_sz + ((size_t)pool * a.num_kv_heads + kv) * 2;
-                s_scale = (double)fp16_bits_to_f32(sz[0]);
-                s_zero = (double)fp16_bits_to_f32(sz[1]);
+                const uint32_t sz = *reinterpret_cast<const uint32_t *>(a.k_sz + hp * 2);
+                s_scale = (double)fp16_bits_to_f32(uint16_t(sz));
+                s_zero = (double)fp16_bits_to_f32(uint16_t(sz >> 16));
             }
-        }
-        double best = -__builtin_inf();
-        for (int pass = 0; pass < npass; ++pass) {
-            const int jl = pass * ge + lg % ge;             // logical page within physical page
-            const int j = m * g + jl;
-            const bool ok = page_ok && j * a.logical_page < L;
-            double acc = 0.0;
-            if (ok) {
-                const size_t base = ((size_t)pool * a.num_kv_heads + kv) * head_stride;
-                if constexpr (KV_DT == LSA_INT4) {
-                    const uint8_t *st = static_cast<const uint8_t *>(a.stats) + base + (size_t)jl * D + ch0;
-                    const uint4 w = *reinterpret_cast<const uint4 *>(st);
-                    const uint32_t wd[4] = {w.x, w.y, w.z, w.w};
+            const bool cur = j == j_cur;
+            const int rows = L - j * a.logical_page;         // valid rows of the current logical page
+            const size_t krow0 = hp * NP + (size_t)jl * a.logical_page;
+            if constexpr (KV_DT == LSA_INT4) {
+                uint32_t cmin[C], cmax[C];
+                if (cur) {
+                    // min / max of the codes of tokens j*N_L .. t, this lane's 16 channels
+#pragma unroll
+                    for (int c = 0; c < C; ++c) { cmin[c] = 15; cmax[c] = 0; }
+                    const uint8_t *kp = static_cast<const uint8_t *>(a.k) + krow0 * (D / 2) + ch0 / 2;
+                    for (int rr = 0; rr < rows; ++rr) {
+                        const uint2 u = *reinterpret_cast<const uint2 *>(kp + (size_t)rr * (D / 2));
+#pragma unroll
+                        for (int c = 0; c < C; ++c) {
+                            const uint32_t byte = ((c < 8 ? u.x : u.y) >> (8 * ((c / 2) % 4))) & 0xFFu;
+                            const uint32_t code = (c & 1) ? (byte >> 4) : (byte & 15u);
+                            cmin[c] = min(cmin[c], code);
+                            cmax[c] = max(cmax[c], code);
+                        }
+                    }
+                } else {
+                    const uint8_t *st = static_cast<const uint8_t *>(a.stats) + hp * head_stride + (size_t)jl * D + ch0;
+                    const uint4 u = *reinterpret_cast<const uint4 *>(st);
+                    const uint32_t wd[4] = {u.x, u.y, u.z, u.w};
 #pragma unroll
                     for (int c = 0; c < C; ++c) {
                         const uint32_t byte = (wd[c / 4] >> (8 * (c % 4))) & 0xFFu;
-                        acc = fma(qp[c], (double)(byte >> 4), acc);
-                        acc = fma(qn[c], (double)(byte & 15u), acc);
+                        cmin[c] = byte & 15u;
+                        cmax[c] = byte >> 4;
+                    }
+                }
+#pragma unroll
+                for (int c = 0; c < C; ++c) {
+                    acc = fma(qp[c], (double)cmax[c], acc);
+                    acc = fma(qn[c], (double)cmin[c], acc);
+                }
+            } else {
+                float kmin[C], kmax[C];
+                if (cur) {
+#pragma unroll
+                    for (int c = 0; c < C; ++c) { kmin[c] = __builtin_inff(); kmax[c] = -__builtin_inff(); }
+                    for (int rr = 0; rr < rows; ++rr) {
+                        if constexpr (KV_DT == LSA_BF16) {
+                            const uint4 u = *reinterpret_cast<const uint4 *>(
+                                static_cast<const uint16_t *>(a.k) + (krow0 + rr) * D + ch0);
+                            const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+                            for (int c = 0; c < C; ++c) {
+                                const float x = (c & 1) ? bf16_hi(w[c / 2]) : bf16_lo(w[c / 2]);
+                                kmin[c] = fminf(kmin[c], x);
+                                kmax[c] = fmaxf(kmax[c], x);
+                            }
+                        } else {
+                            const float4 u = *reinterpret_cast<const float4 *>(
+                                static_cast<const float *>(a.k) + (krow0 + rr) * D + ch0);
+                            const float w[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+                            for (int c = 0; c < C; ++c) {
+                                kmin[c] = fminf(kmin[c], w[c]);
+                                kmax[c] = fmaxf(kmax[c], w[c]);
+                            }
+                        }
                     }
                 } else if constexpr (KV_DT == LSA_BF16) {
-                    const uint16_t *st = static_cast<const uint16_t *>(a.stats) + base + (size_t)jl * 2 * D + ch0;
+                    const uint16_t *st = static_cast<const uint16_t *>(a.stats) + hp * head_stride + (size_t)jl * 2 * D + ch0;
                     const uint4 lo = *reinterpret_cast<const uint4 *>(st);
                     const uint4 hi = *reinterpret_cast<const uint4 *>(st + D);
                     const uint32_t wl[4] = {lo.x, lo.y, lo.z, lo.w};
                     const uint32_t wh[4] = {hi.x, hi.y, hi.z, hi.w};
 #pragma unroll
                     for (int c = 0; c < C; ++c) {
-                        const float kmin = (c & 1) ? bf16_hi(wl[c / 2]) : bf16_lo(wl[c / 2]);
-                        const float kmax = (c & 1) ? bf16_hi(wh[c / 2]) : bf16_lo(wh[c / 2]);
-                        acc = fma(qp[c], (double)kmax, acc);
-                        acc = fma(qn[c], (double)kmin, acc);
+                        kmin[c] = (c & 1) ? bf16_hi(wl[c / 2]) : bf16_lo(wl[c / 2]);
+                        kmax[c] = (c & 1) ? bf16_hi(wh[c / 2]) : bf16_lo(wh[c / 2]);
                     }
                 } else {
-                    const float *st = static_cast<const float *>(a.stats) + base + (size_t)jl * 2 * D + ch0;
+                    const float *st = static_cast<const float *>(a.stats) + hp * head_stride + (size_t)jl * 2 * D + ch0;
                     const float4 lo = *reinterpret_cast<const float4 *>(st);
                     const float4 hi = *reinterpret_cast<const float4 *>(st + D);
                     const float vl[4] = {lo.x, lo.y, lo.z, lo.w};
                     const float vh[4] = {hi.x, hi.y, hi.z, hi.w};
 #pragma unroll
-                    for (int c = 0; c < C; ++c) {
-                        acc = fma(qp[c], (double)vh[c], acc);
-                        acc = fma(qn[c], (double)vl[c], acc);
-                    }
+                    for (int c = 0; c < C; ++c) { kmin[c] = vl[c]; kmax[c] = vh[c]; }
+                }
+#pragma unroll
+                for (int c = 0; c < C; ++c) {
+                    acc = fma(qp[c], (double)kmax[c], acc);
+                    acc = fma(qn[c], (double)kmin[c], acc);
                 }
             }
+        }
 #pragma unroll
-            for (int off = 1; off < LPL; off <<= 1) acc += shfl_xor_d(acc, off);
+        for (int off = 1; off < LPL; off <<= 1) acc += shfl_xor_d(acc, off);
+        if (ok && lane % LPL == 0) {
             double sj = acc;
             if constexpr (KV_DT == LSA_INT4) sj = s_scale * (acc - s_zero * qsum);
-            if (!ok) sj = -__builtin_inf();
-            // max over the lane groups that hold logical pages of the same physical page
-            for (int off = LPL; off < ge * LPL; off <<= 1) sj = fmax(sj, shfl_xor_d(sj, off));
-            best = fmax(best, sj);
+            s_log[j - j0] = sj;
         }
-        if (page_ok && (lane % (ge * LPL)) == 0)
-            a.phys[((size_t)b * a.num_kv_heads + kv) * a.max_pages + m] = best + 0.0;
+    }
+    __syncthreads();
+    // P_m = max over the logical pages of physical page m
+    for (int m = m0 + threadIdx.x; m < m1; m += blockDim.x) {
+        const int ja = m * g - j0, jb = min((m + 1) * g, j1) - j0;
+        double best = s_log[ja];
+        for (int jj = ja + 1; jj < jb; ++jj) best = fmax(best, s_log[jj]);
+        a.phys[((size_t)b * a.num_kv_heads + kv) * a.max_pages + m] = best + 0.0;
     }
 }
 
 // ---------------------------------------------------------------------------
-// top-K: one workgroup of 256 threads per (sequence, retrieval head)
+// top-K: one workgroup of 1024 threads per (sequence, retrieval head)
 // ---------------------------------------------------------------------------
+constexpr int kTopkThreads = 1024;
+constexpr int kTopkPerThread = 16;        // pages per thread: up to 16384 pages
 
 __device__ __forceinline__ unsigned long long order_key(double x) {
     x = x + 0.0;                                  // -0 -> +0
@@ -174,26 +255,26 @@ __device__ __forceinline__ unsigned long long order_key(double x) {
     return (u >> 63) ? ~u : (u | 0x8000000000000000ull);
 }
 
-// inclusive prefix sum over the 256 threads of a 32-bit packed counter
-__device__ __forceinline__ uint32_t block_inclusive_scan(uint32_t v, uint32_t *wave_tot) {
+// exclusive prefix sum over the workgroup of a 32-bit packed counter
+__device__ __forceinline__ uint32_t block_exclusive_scan(uint32_t v, uint32_t *wave_tot) {
     const int lane = threadIdx.x % kWave, wave = threadIdx.x / kWave;
+    uint32_t incl = v;
 #pragma unroll
     for (int off = 1; off < kWave; off <<= 1) {
-        const uint32_t n = __shfl_up(v, off, kWave);
-        if (lane >= off) v += n;
+        const uint32_t n = __shfl_up(incl, off, kWave);
+        if (lane >= off) incl += n;
     }
-    if (lane == kWave - 1) wave_tot[wave] = v;
+    if (lane == kWave - 1) wave_tot[wave] = incl;
     __syncthreads();
     uint32_t add = 0;
     for (int w = 0; w < wave; ++w) add += wave_tot[w];
-    __syncthreads();
-    return v + add;
+    return incl - v + add;
 }
 
-__global__ __launch_bounds__(256) void topk_kernel(TopkArgs a) {
+__global__ __launch_bounds__(kTopkThreads) void topk_kernel(TopkArgs a) {
     __shared__ uint32_t hist[256];
     __shared__ uint32_t sh_digit, sh_above;
-    __shared__ uint32_t wave_tot[4];
+    __shared__ uint32_t wave_tot[kTopkThreads / kWave];
 
     const int r = blockIdx.x % a.n_ret;
     const int b = blockIdx.x / a.n_ret;
@@ -210,15 +291,22 @@ __global__ __launch_bounds__(256) void topk_kernel(TopkArgs a) {
         return;
     }
 
+    // thread t owns the contiguous pages [t*seg, t*seg + cnt)
+    const int seg = (n + kTopkThreads - 1) / kTopkThreads;
+    const int i0 = min(n, tid * seg);
+    const int cnt = min(n, i0 + seg) - i0;
+    unsigned long long key[kTopkPerThread];
+#pragma unroll
+    for (int e = 0; e < kTopkPerThread; ++e) key[e] = e < cnt ? order_key(P[i0 + e]) : 0ull;
+
     unsigned long long prefix = 0, mask = 0;
     uint32_t need = (uint32_t)K;
     for (int shift = 56; shift >= 0; shift -= 8) {
-        hist[tid] = 0;
+        if (tid < 256) hist[tid] = 0;
         __syncthreads();
-        for (int i = tid; i < n; i += blockDim.x) {
-            const unsigned long long key = order_key(P[i]);
-            if ((key & mask) == prefix) atomicAdd(&hist[(key >> shift) & 0xFFu], 1u);
-        }
+#pragma unroll
+        for (int e = 0; e < kTopkPerThread; ++e)
+            if (e < cnt && (key[e] & mask) == prefix) atomicAdd(&hist[(key[e] >> shift) & 0xFFu], 1u);
         __syncthreads();
         if (tid < kWave) {
             // lane l owns bins 4l..4l+3; suffix sums from the top bin down
@@ -232,12 +320,12 @@ __global__ __launch_bounds__(256) void topk_kernel(TopkArgs a) {
             }
             uint32_t above = suf - mine;          // elements in bins of higher lanes
             const uint32_t cs[4] = {c0, c1, c2, c3};
-            for (int q = 3; q >= 0; --q) {
-                if (above < need && above + cs[q] >= need) {
-                    sh_digit = 4 * tid + q;
+            for (int qd = 3; qd >= 0; --qd) {
+                if (above < need && above + cs[qd] >= need) {
+                    sh_digit = 4 * tid + qd;
                     sh_above = above;
                 }
-                above += cs[q];
+                above += cs[qd];
             }
         }
         __syncthreads();
@@ -250,24 +338,26 @@ __global__ __launch_bounds__(256) void topk_kernel(TopkArgs a) {
         if (done) break;
     }
 
-    // ordered compaction: thread t owns the contiguous segment [t*seg, (t+1)*seg)
-    const int seg = (n + blockDim.x - 1) / blockDim.x;
-    const int i0 = min(n, tid * seg), i1 = min(n, i0 + seg);
-    uint32_t cnt = 0;                             // low 16 bits: greater, high 16 bits: equal
-    for (int i = i0; i < i1; ++i) {
-        const unsigned long long km = order_key(P[i]) & mask;
-        cnt += km > prefix ? 1u : (km == prefix ? 0x10000u : 0u);
+    // ordered compaction
+    uint32_t c = 0;                               // low 16 bits: greater, high 16 bits: equal
+#pragma unroll
+    for (int e = 0; e < kTopkPerThread; ++e) {
+        if (e >= cnt) continue;
+        const unsigned long long km = key[e] & mask;
+        c += km > prefix ? 1u : (km == prefix ? 0x10000u : 0u);
     }
-    const uint32_t incl = block_inclusive_scan(cnt, wave_tot);
-    uint32_t gt_before = (incl - cnt) & 0xFFFFu;
-    uint32_t eq_before = (incl - cnt) >> 16;
-    for (int i = i0; i < i1; ++i) {
-        const unsigned long long km = order_key(P[i]) & mask;
+    const uint32_t excl = block_exclusive_scan(c, wave_tot);
+    uint32_t gt_before = excl & 0xFFFFu;
+    uint32_t eq_before = excl >> 16;
+#pragma unroll
+    for (int e = 0; e < kTopkPerThread; ++e) {
+        if (e >= cnt) continue;
+        const unsigned long long km = key[e] & mask;
         if (km > prefix) {
-            out[gt_before + min(eq_before, need)] = i;
+            out[gt_before + min(eq_before, need)] = i0 + e;
             ++gt_before;
         } else if (km == prefix) {
-            if (eq_before < need) out[gt_before + eq_before] = i;
+            if (eq_before < need) out[gt_before + eq_before] = i0 + e;
             ++eq_before;
         }
     }
@@ -275,12 +365,18 @@ __global__ __launch_bounds__(256) void topk_kernel(TopkArgs a) {
 
 template <int KV_DT>
 hipError_t launch_score_dt(const ScoreArgs &a, unsigned grid, hipStream_t s) {
-    if (a.head_dim == 128) hipLaunchKernelGGL((score_kernel<KV_DT, 128>), dim3(grid), dim3(256), 0, s, a);
-    else hipLaunchKernelGGL((score_kernel<KV_DT, 64>), dim3(grid), dim3(256), 0, s, a);
+    if (a.head_dim == 128) hipLaunchKernelGGL((score_kernel<KV_DT, 128>), dim3(grid), dim3(kScoreThreads), 0, s, a);
+    else hipLaunchKernelGGL((score_kernel<KV_DT, 64>), dim3(grid), dim3(kScoreThreads), 0, s, a);
     return hipGetLastError();
 }
 
 }  // namespace
+
+int score_max_pages_per_block(int page_size, int logical_page) {
+    return kMaxLogicalPerBlock / (page_size / logical_page);
+}
+
+int topk_max_pages() { return kTopkThreads * kTopkPerThread; }
 
 hipError_t launch_score(const ScoreArgs &a, hipStream_t s) {
     const long long grid = (long long)a.batch * a.n_ret * a.blocks_per_head;
@@ -293,7 +389,7 @@ hipError_t launch_score(const ScoreArgs &a, hipStream_t s) {
 hipError_t launch_topk(const TopkArgs &a, hipStream_t s) {
     const long long grid = (long long)a.batch * a.n_ret;
     if (grid == 0) return hipSuccess;
-    hipLaunchKernelGGL(topk_kernel, dim3((unsigned)grid), dim3(256), 0, s, a);
+    hipLaunchKernelGGL(topk_kernel, dim3((unsigned)grid), dim3(kTopkThreads), 0, s, a);
     return hipGetLastError();
 }
 

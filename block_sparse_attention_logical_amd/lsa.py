@@ -104,7 +104,7 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
                                      ctypes.c_int32, ctypes.c_int32, vp, vp, ctypes.c_size_t, vp]
     lib.lsa_decode_workspace.argtypes = [P(LsaKV), P(LsaSeqs), P(LsaHeads), ctypes.c_int32, sz]
     lib.lsa_sparse_decode_attn.argtypes = [vp, ctypes.c_int32, P(LsaKV), P(LsaSeqs), P(LsaHeads), vp,
-                                           ctypes.c_int32, ctypes.c_float, vp, vp, ctypes.c_size_t, vp]
+                                           ctypes.c_int32, ctypes.c_float, vp, vp, vp, ctypes.c_size_t, vp]
     lib.lsa_sparse_prefill_attn.argtypes = [vp, ctypes.c_int32, P(LsaKV), vp, ctypes.c_int32, P(LsaHeads),
                                             ctypes.c_int32, ctypes.c_float, vp, vp, vp]
     for name in EXPORTED[:-2]:
@@ -239,11 +239,13 @@ def decode_workspace(kv: KVPool, page_table: torch.Tensor, seq_lens: torch.Tenso
 
 def sparse_decode_attn(q: torch.Tensor, kv: KVPool, page_table: torch.Tensor, seq_lens: torch.Tensor,
                        heads: Heads, selected: Optional[torch.Tensor], token_budget: int, out: torch.Tensor,
-                       workspace: torch.Tensor, softmax_scale: float = 0.0, stream=None) -> None:
+                       workspace: torch.Tensor, softmax_scale: float = 0.0, stats: Optional[torch.Tensor] = None,
+                       stream=None) -> None:
     _check(load().lsa_sparse_decode_attn(_ptr(q), dtype_code(q), ctypes.byref(kv.desc()),
                                          ctypes.byref(seqs_desc(page_table, seq_lens)), ctypes.byref(heads.desc()),
-                                         _ptr(selected), token_budget, softmax_scale, _ptr(out), _ptr(workspace),
-                                         workspace.numel() * workspace.element_size(), _stream(stream)))
+                                         _ptr(selected), token_budget, softmax_scale, _ptr(out), _ptr(stats),
+                                         _ptr(workspace), workspace.numel() * workspace.element_size(),
+                                         _stream(stream)))
 
 
 def sparse_prefill_attn(q: torch.Tensor, kv: KVPool, page_table: torch.Tensor, seq_len: int, heads: Heads,

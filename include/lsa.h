@@ -153,6 +153,10 @@ lsa_status lsa_select_pages_workspace(const lsa_kv *kv, const lsa_seqs *seqs,
  *          largest P_m, ties to the lower m, in ascending m, padded with -1
  *          when the sequence has fewer than K pages.
  * Products are exact and S^j, P_m are accumulated and compared in fp64.
+ * The logical page that holds the current token t = seq_lens[b] - 1 is scored
+ * from its keys in the pool (min / max of tokens j*N_L .. t taken on the fly),
+ * so its entry in `stats` may be stale; every earlier logical page is read
+ * from `stats`.
  * Streaming heads' rows of `selected` are not written.
  * q: [B][H_q][head_dim] of q_dtype (LSA_F32 or LSA_BF16).
  * stats: as built by lsa_build_page_stats for tokens < seq_lens[b].
@@ -188,6 +192,10 @@ lsa_status lsa_decode_workspace(const lsa_kv *kv, const lsa_seqs *seqs,
  * selected: [B][H_kv][K] as written by lsa_select_pages (rows of streaming
  * heads are not read; may be NULL when every head is a streaming head).
  * softmax_scale: 0 means 1 / sqrt(head_dim).
+ * stats: NULL, or the statistics pool of lsa_build_page_stats: the call then
+ * also refreshes, for every retrieval head, the statistics of the logical page
+ * that holds token t (what lsa_build_page_stats does with first_token = t), so
+ * a decode step needs no separate statistics launch.
  * workspace: at least lsa_decode_workspace bytes, 256-byte aligned; calls
  * that share a workspace must not overlap in time (same stream, or ordered).
  * Two kernels are launched: the split-KV pass and the merge of its partial
@@ -195,8 +203,8 @@ lsa_status lsa_decode_workspace(const lsa_kv *kv, const lsa_seqs *seqs,
 lsa_status lsa_sparse_decode_attn(const void *q, int32_t q_dtype, const lsa_kv *kv,
                                   const lsa_seqs *seqs, const lsa_heads *heads,
                                   const int32_t *selected, int32_t token_budget,
-                                  float softmax_scale, void *out, void *workspace,
-                                  size_t workspace_bytes, void *stream);
+                                  float softmax_scale, void *out, void *stats,
+                                  void *workspace, size_t workspace_bytes, void *stream);
 
 /* Block-sparse causal prefill attention of one sequence over non-empty tiles
  * only ([LS-X] 統一ブロックスパースアテンション: iterate the non-empty blocks;

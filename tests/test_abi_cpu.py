@@ -151,7 +151,7 @@ def decode(lib, kv=None, heads=None, q_dtype=lsa.BF16, selected=FAKE, ws_bytes=1
     kv = kv or kv_desc()
     heads = heads or heads_desc()
     return lib.lsa_sparse_decode_attn(FAKE, q_dtype, ctypes.byref(kv), ctypes.byref(seqs_desc(batch)),
-                                      ctypes.byref(heads), selected, 4096, scale, FAKE, FAKE, ws_bytes, None)
+                                      ctypes.byref(heads), selected, 4096, scale, FAKE, None, FAKE, ws_bytes, None)
 
 
 def test_decode_validation(lib):

@@ -35,16 +35,16 @@ class Runner:
                                   dtype=torch.uint8, device=DEV)
 
     def step(self, i):
+        """One decode step: select (every R steps; the current logical page is
+        scored from its keys), then attend; the attention call also refreshes
+        the statistics of the current logical page."""
         w = self.w
         lens = w.seq_lens(i)
-        first = lens - 1
-        lsa.build_page_stats(self.kv, w.page_table, lens, self.stats, heads=self.hd, first_token=first,
-                             max_new_tokens=1)
         lsa.select_pages(w.q[i], self.kv, self.stats, w.page_table, lens, self.hd, w.token_budget, i,
                          w.reuse_interval, self.selected, self.ws_sel)
         out = torch.empty_like(w.q[i])
         lsa.sparse_decode_attn(w.q[i], self.kv, w.page_table, lens, self.hd, self.selected, w.token_budget,
-                               out, self.ws_dec)
+                               out, self.ws_dec, stats=self.stats)
         torch.cuda.synchronize()
         return out
 
@@ -109,6 +109,27 @@ def test_decode_cfg1_full_window():
 def test_decode_cfg2_small(ctx):
     w = W.make_decode(2, DEV, batch=len(ctx), ctx=ctx)
     print("max abs err", check_window(w))
+
+
+@pytest.mark.parametrize("ctx", [[1000, 2500], [127, 4096 + 17]])
+def test_decode_cfg5_int4_small(ctx):
+    """KV4 pool: dequantisation fused into scoring and attention."""
+    w = W.make_decode(5, DEV, batch=len(ctx), ctx=ctx)
+    print("max abs err", check_window(w))
+
+
+def test_decode_refreshes_statistics():
+    """After a window of fused steps the statistics pool equals a full build
+    at the final length (every logical page the window touched refreshed)."""
+    import tests.test_gpu_stats_select as S
+    for cfg, kw in ((2, dict(batch=2, ctx=[1000, 2000], window=20)), (5, dict(batch=2, ctx=[700, 1500], window=20)),
+                    (1, dict(window=16))):
+        w = W.make_decode(cfg, DEV, **kw)
+        r = Runner(w)
+        for i in range(w.window):
+            r.step(i)
+        lens = [c + w.window for c in w.ctx]
+        S.check_stats(w, r.stats, lens, kinds=w.head_kind)
 
 
 def test_decode_cfg4_small_np128_permuted():

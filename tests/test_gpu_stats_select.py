@@ -201,6 +201,19 @@ def test_select_ties_go_to_lower_page():
     check_selection(w, 0, lens, sel)
 
 
+def test_select_scores_current_page_from_keys():
+    """Statistics built only up to the previous token: the logical page that
+    holds the current token is scored from its keys, so the selection still
+    matches the oracle (which sees every token)."""
+    for cfg, kw in ((2, dict(batch=3, ctx=[1000, 2047, 5000])), (5, dict(batch=2, ctx=[777, 3000])),
+                    (4, dict(batch=2, ctx=(3000, 6000))), (1, {})):
+        w = W.make_decode(cfg, DEV, **kw)
+        stats = build_stats(w, list(w.ctx))          # tokens < ctx only
+        lens = [c + 1 for c in w.ctx]
+        sel = run_select(w, 0, lens, stats=stats)
+        check_selection(w, 0, lens, sel)
+
+
 def test_select_full_size_cfg2():
     """Config 2 at full size (B = 8, 64K context): every retrieval head."""
     w = W.make_decode(2, DEV)
