@@ -100,7 +100,6 @@ int count_kind(const lsa_heads *hd, int h_kv, int kind) {
 }
 
 constexpr int kPagesPerWave = 1;       // decode: pages per wavefront
-constexpr int kScorePagesPerBlock = 64;
 
 struct DecodeGeom {
     int K, chunks_ret, chunks_str, chunks_max, rec_floats;
@@ -234,7 +233,7 @@ lsa_status lsa_select_pages(const void *q, int32_t q_dtype, const lsa_kv *kv, co
     sa.n_ret = 0;
     for (int i = 0; i < kv->num_kv_heads; ++i)
         if (heads->head_kind[i] == LSA_RETRIEVAL_HEAD) sa.ret_heads[sa.n_ret++] = (uint8_t)i;
-    sa.pages_per_block = std::min(kScorePagesPerBlock, score_max_pages_per_block(kv->page_size, kv->logical_page));
+    sa.pages_per_block = score_pages_per_block(kv->kv_dtype, kv->head_dim, kv->page_size, kv->logical_page);
     sa.blocks_per_head = (seqs->max_pages + sa.pages_per_block - 1) / sa.pages_per_block;
     if (lsa_status s = from_hip(launch_score(sa, (hipStream_t)stream), "select_pages score launch")) return s;
 

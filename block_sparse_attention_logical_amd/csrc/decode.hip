@@ -547,48 +547,34 @@ __global__ __launch_bounds__(256) void decode_f32_kernel(DecodeArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-// split-KV merge: one workgroup per (sequence, KV head).  Chunk weights are
-// formed once in LDS, then every thread sums its outputs over the chunks with
-// independent loads (fixed chunk order: deterministic).
+// split-KV merge: one workgroup per (sequence, query head), one thread per
+// output channel.  Each thread forms the chunk weights of its head itself (no
+// barrier) and sums its channel over the chunks with independent loads, in
+// chunk order (deterministic).
 // ---------------------------------------------------------------------------
 template <typename OutT>
-__global__ __launch_bounds__(256) void combine_kernel(DecodeArgs a) {
-    __shared__ float wt[kMaxDecodeChunks][16];
-    __shared__ float ms[kMaxDecodeChunks][16];
-    __shared__ float ls[kMaxDecodeChunks][16];
-    const int b = blockIdx.x / a.num_kv_heads, kv = blockIdx.x % a.num_kv_heads;
+__global__ __launch_bounds__(128) void combine_kernel(DecodeArgs a) {
+    const int b = blockIdx.x / a.num_q_heads, hq = blockIdx.x % a.num_q_heads;
     const int G = a.group, D = a.head_dim;
+    const int kv = hq / G, hh = hq % G;
     const int nchunks = a.kind[kv] ? a.chunks_str : a.chunks_ret;
     const size_t rec_size = 32 + (size_t)G * D;
     const float *rec0 = a.part + ((size_t)b * a.num_kv_heads + kv) * a.chunks_max * rec_size;
-    for (int i = threadIdx.x; i < nchunks * G; i += blockDim.x) {
-        const int c = i / G, hh = i % G;
-        ms[c][hh] = rec0[c * rec_size + hh];
-        ls[c][hh] = rec0[c * rec_size + 16 + hh];
-    }
-    __syncthreads();
-    if (threadIdx.x < G) {
-        const int hh = threadIdx.x;
+    for (int d = threadIdx.x; d < D; d += blockDim.x) {
         float M = -__builtin_inff();
-        for (int c = 0; c < nchunks; ++c) M = fmaxf(M, ms[c][hh]);
-        float L = 0.f;
+        for (int c = 0; c < nchunks; ++c) M = fmaxf(M, rec0[c * rec_size + hh]);
+        float acc = 0.f, L = 0.f;
+#pragma unroll 4
         for (int c = 0; c < nchunks; ++c) {
-            const float e = ms[c][hh] == -__builtin_inff() ? 0.f : exp2_fast(ms[c][hh] - M);
-            wt[c][hh] = e;
-            L += e * ls[c][hh];
+            const float *rec = rec0 + c * rec_size;
+            const float mc = rec[hh];
+            const float e = mc == -__builtin_inff() ? 0.f : exp2_fast(mc - M);
+            L += e * rec[16 + hh];
+            acc += e * rec[32 + hh * D + d];
         }
-        const float inv = 1.f / L;
-        for (int c = 0; c < nchunks; ++c) wt[c][hh] *= inv;
-    }
-    __syncthreads();
-    for (int idx = threadIdx.x; idx < G * D; idx += blockDim.x) {
-        const int hh = idx / D;
-        float acc = 0.f;
-#pragma unroll 8
-        for (int c = 0; c < nchunks; ++c) acc += wt[c][hh] * rec0[c * rec_size + 32 + idx];
-        const size_t o = ((size_t)b * a.num_q_heads + (size_t)kv * G) * D + idx;
-        if constexpr (sizeof(OutT) == 2) static_cast<uint16_t *>(a.out)[o] = f32_to_bf16_rne(acc);
-        else static_cast<float *>(a.out)[o] = acc;
+        const size_t o = ((size_t)b * a.num_q_heads + hq) * D + d;
+        if constexpr (sizeof(OutT) == 2) static_cast<uint16_t *>(a.out)[o] = f32_to_bf16_rne(acc / L);
+        else static_cast<float *>(a.out)[o] = acc / L;
     }
 }
 
@@ -624,10 +610,10 @@ hipError_t launch_decode(const DecodeArgs &a, int q_dtype, int kv_dtype, hipStre
 }
 
 hipError_t launch_combine(const DecodeArgs &a, int q_dtype, hipStream_t s) {
-    const long long grid = (long long)a.batch * a.num_kv_heads;
+    const long long grid = (long long)a.batch * a.num_q_heads;
     if (grid == 0) return hipSuccess;
-    if (q_dtype == LSA_BF16) hipLaunchKernelGGL(combine_kernel<uint16_t>, dim3((unsigned)grid), dim3(256), 0, s, a);
-    else hipLaunchKernelGGL(combine_kernel<float>, dim3((unsigned)grid), dim3(256), 0, s, a);
+    if (q_dtype == LSA_BF16) hipLaunchKernelGGL(combine_kernel<uint16_t>, dim3((unsigned)grid), dim3(128), 0, s, a);
+    else hipLaunchKernelGGL(combine_kernel<float>, dim3((unsigned)grid), dim3(128), 0, s, a);
     return hipGetLastError();
 }
 

@@ -128,7 +128,7 @@ struct PrefillArgs {
 
 hipError_t launch_stats(const StatsArgs &a, hipStream_t s);
 hipError_t launch_score(const ScoreArgs &a, hipStream_t s);
-int score_max_pages_per_block(int page_size, int logical_page);
+int score_pages_per_block(int kv_dtype, int head_dim, int page_size, int logical_page);
 int topk_max_pages();
 hipError_t launch_topk(const TopkArgs &a, hipStream_t s);
 hipError_t launch_decode(const DecodeArgs &a, int q_dtype, int kv_dtype, hipStream_t s);

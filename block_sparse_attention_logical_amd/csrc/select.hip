@@ -37,6 +37,7 @@ struct ScoreShape {
 };
 
 constexpr int kScoreThreads = 256;
+constexpr int kScoreMaxIter = 8;           // logical pages per lane group and workgroup
 constexpr int kMaxLogicalPerBlock = 1024;  // LDS slots for logical scores
 
 __device__ __forceinline__ double shfl_xor_d(double v, int m) { return __shfl_xor(v, m, kWave); }
@@ -118,18 +119,43 @@ __global__ __launch_bounds__(kScoreThreads) void score_kernel(ScoreArgs a) {
     const int NP = a.page_size;
 
     // every lane group walks logical pages j0 + lg, j0 + lg + GROUPS, ...; the
-    // trip count is uniform so the lane-group reductions see whole wavefronts
+    // trip count is uniform so the lane-group reductions see whole wavefronts.
+    // The page-table entries of all iterations are loaded first, then every
+    // iteration's statistics, so no load waits on another.
     const int n_iter = (j1 - j0 + GROUPS - 1) / GROUPS;
-#pragma unroll 2
-    for (int it = 0; it < n_iter; ++it) {
+    int pools[kScoreMaxIter];
+#pragma unroll
+    for (int it = 0; it < kScoreMaxIter; ++it) {
+        const int j = j0 + lg + it * GROUPS;
+        pools[it] = (it < n_iter && j < j1) ? a.page_table[(size_t)b * a.max_pages + j / g] : 0;
+    }
+    uint4 st_lo[kScoreMaxIter], st_hi[kScoreMaxIter];
+#pragma unroll
+    for (int it = 0; it < kScoreMaxIter; ++it) {
+        const int j = j0 + lg + it * GROUPS;
+        if (it < n_iter && j < j1 && j != j_cur) {
+            const size_t hp = (size_t)pools[it] * a.num_kv_heads + kv;
+            const int jl = j % g;
+            if constexpr (KV_DT == LSA_INT4) {
+                st_lo[it] = *reinterpret_cast<const uint4 *>(static_cast<const uint8_t *>(a.stats) + hp * head_stride +
+                                                             (size_t)jl * D + ch0);
+            } else {
+                const char *st = static_cast<const char *>(a.stats) + (hp * head_stride + (size_t)jl * 2 * D + ch0) * EB;
+                st_lo[it] = *reinterpret_cast<const uint4 *>(st);
+                st_hi[it] = *reinterpret_cast<const uint4 *>(st + (size_t)D * EB);
+            }
+        }
+    }
+#pragma unroll
+    for (int it = 0; it < kScoreMaxIter; ++it) {
+        if (it >= n_iter) break;
         const int j = j0 + lg + it * GROUPS;
         const bool ok = j < j1;
-        const int m = j / g, jl = j % g;
+        const int jl = j % g;
         double acc = 0.0;
         double s_scale = 1.0, s_zero = 0.0;
         if (ok) {
-            const int pool = a.page_table[(size_t)b * a.max_pages + m];
-            const size_t hp = (size_t)pool * a.num_kv_heads + kv;
+            const size_t hp = (size_t)pools[it] * a.num_kv_heads + kv;
             if constexpr (KV_DT == LSA_INT4) {
                 const uint32_t sz = *reinterpret_cast<const uint32_t *>(a.k_sz + hp * 2);
                 s_scale = (double)fp16_bits_to_f32(uint16_t(sz));
@@ -156,9 +182,7 @@ __global__ __launch_bounds__(kScoreThreads) void score_kernel(ScoreArgs a) {
                         }
                     }
                 } else {
-                    const uint8_t *st = static_cast<const uint8_t *>(a.stats) + hp * head_stride + (size_t)jl * D + ch0;
-                    const uint4 u = *reinterpret_cast<const uint4 *>(st);
-                    const uint32_t wd[4] = {u.x, u.y, u.z, u.w};
+                    const uint32_t wd[4] = {st_lo[it].x, st_lo[it].y, st_lo[it].z, st_lo[it].w};
 #pragma unroll
                     for (int c = 0; c < C; ++c) {
                         const uint32_t byte = (wd[c / 4] >> (8 * (c % 4))) & 0xFFu;
@@ -199,22 +223,18 @@ __global__ __launch_bounds__(kScoreThreads) void score_kernel(ScoreArgs a) {
                         }
                     }
                 } else if constexpr (KV_DT == LSA_BF16) {
-                    const uint16_t *st = static_cast<const uint16_t *>(a.stats) + hp * head_stride + (size_t)jl * 2 * D + ch0;
-                    const uint4 lo = *reinterpret_cast<const uint4 *>(st);
-                    const uint4 hi = *reinterpret_cast<const uint4 *>(st + D);
-                    const uint32_t wl[4] = {lo.x, lo.y, lo.z, lo.w};
-                    const uint32_t wh[4] = {hi.x, hi.y, hi.z, hi.w};
+                    const uint32_t wl[4] = {st_lo[it].x, st_lo[it].y, st_lo[it].z, st_lo[it].w};
+                    const uint32_t wh[4] = {st_hi[it].x, st_hi[it].y, st_hi[it].z, st_hi[it].w};
 #pragma unroll
                     for (int c = 0; c < C; ++c) {
                         kmin[c] = (c & 1) ? bf16_hi(wl[c / 2]) : bf16_lo(wl[c / 2]);
                         kmax[c] = (c & 1) ? bf16_hi(wh[c / 2]) : bf16_lo(wh[c / 2]);
                     }
                 } else {
-                    const float *st = static_cast<const float *>(a.stats) + hp * head_stride + (size_t)jl * 2 * D + ch0;
-                    const float4 lo = *reinterpret_cast<const float4 *>(st);
-                    const float4 hi = *reinterpret_cast<const float4 *>(st + D);
-                    const float vl[4] = {lo.x, lo.y, lo.z, lo.w};
-                    const float vh[4] = {hi.x, hi.y, hi.z, hi.w};
+                    const float vl[4] = {__uint_as_float(st_lo[it].x), __uint_as_float(st_lo[it].y),
+                                         __uint_as_float(st_lo[it].z), __uint_as_float(st_lo[it].w)};
+                    const float vh[4] = {__uint_as_float(st_hi[it].x), __uint_as_float(st_hi[it].y),
+                                         __uint_as_float(st_hi[it].z), __uint_as_float(st_hi[it].w)};
 #pragma unroll
                     for (int c = 0; c < C; ++c) { kmin[c] = vl[c]; kmax[c] = vh[c]; }
                 }
@@ -299,9 +319,33 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(TopkArgs a) {
 #pragma unroll
     for (int e = 0; e < kTopkPerThread; ++e) key[e] = e < cnt ? order_key(P[i0 + e]) : 0ull;
 
-    unsigned long long prefix = 0, mask = 0;
+    // the leading bits shared by every key decide nothing: find the highest
+    // differing bit (block-wide and / or of the keys) and start the radix
+    // passes at its digit, taking the shared bits as the prefix
+    __shared__ unsigned long long sh_and[kTopkThreads / kWave], sh_or[kTopkThreads / kWave];
+    unsigned long long k_and = ~0ull, k_or = 0ull;
+#pragma unroll
+    for (int e = 0; e < kTopkPerThread; ++e)
+        if (e < cnt) { k_and &= key[e]; k_or |= key[e]; }
+#pragma unroll
+    for (int off = 1; off < kWave; off <<= 1) {
+        k_and &= __shfl_xor(k_and, off, kWave);
+        k_or |= __shfl_xor(k_or, off, kWave);
+    }
+    if (tid % kWave == 0) { sh_and[tid / kWave] = k_and; sh_or[tid / kWave] = k_or; }
+    __syncthreads();
+    k_and = ~0ull; k_or = 0ull;
+    for (int w2 = 0; w2 < kTopkThreads / kWave; ++w2) { k_and &= sh_and[w2]; k_or |= sh_or[w2]; }
+    const unsigned long long differ = k_and ^ k_or;      // bits that are not the same in every key
+    int start = 56;
+    if (differ != 0ull) {
+        const int top = 63 - __clzll((long long)differ);  // highest differing bit
+        start = (top / 8) * 8;
+    }
+    const unsigned long long common_mask = start >= 56 ? 0ull : (~0ull << (start + 8));
+    unsigned long long prefix = k_and & common_mask, mask = common_mask;
     uint32_t need = (uint32_t)K;
-    for (int shift = 56; shift >= 0; shift -= 8) {
+    for (int shift = start; shift >= 0; shift -= 8) {
         if (tid < 256) hist[tid] = 0;
         __syncthreads();
 #pragma unroll
@@ -372,8 +416,15 @@ hipError_t launch_score_dt(const ScoreArgs &a, unsigned grid, hipStream_t s) {
 
 }  // namespace
 
-int score_max_pages_per_block(int page_size, int logical_page) {
-    return kMaxLogicalPerBlock / (page_size / logical_page);
+int score_pages_per_block(int kv_dtype, int head_dim, int page_size, int logical_page) {
+    // lane groups per workgroup x iterations, in logical pages, over g
+    const int eb = kv_dtype == LSA_F32 ? 4 : (kv_dtype == LSA_BF16 ? 2 : 1);
+    const int lpl = head_dim / (16 / eb);
+    const int groups = (kScoreThreads / kWave) * (kWave / lpl);
+    const int g = page_size / logical_page;
+    int ppb = groups * kScoreMaxIter / g;
+    ppb = ppb < 1 ? 1 : ppb;
+    return ppb * g > kMaxLogicalPerBlock ? kMaxLogicalPerBlock / g : ppb;
 }
 
 int topk_max_pages() { return kTopkThreads * kTopkPerThread; }
