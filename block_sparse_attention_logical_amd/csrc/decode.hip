@@ -218,7 +218,7 @@ __device__ __forceinline__ uint32_t pick(const uint4 &u, int i) {
 // MFMA kernel, bf16 or int4 pool, bf16 q
 // ---------------------------------------------------------------------------
 template <int D, int KVT, int BIF>
-__global__ __launch_bounds__(256) void decode_mfma_kernel(DecodeArgs a) {
+__global__ __launch_bounds__(256, 3) void decode_mfma_kernel(DecodeArgs a) {
     constexpr bool I4 = KVT == LSA_INT4;
     constexpr int NS = D / 32;            // MFMA k-steps over channels
     constexpr int NDT = D / 16;           // output channel tiles
@@ -548,12 +548,14 @@ __global__ __launch_bounds__(256) void decode_f32_kernel(DecodeArgs a) {
 
 // ---------------------------------------------------------------------------
 // split-KV merge: one workgroup per (sequence, query head), one thread per
-// output channel.  Each thread forms the chunk weights of its head itself (no
-// barrier) and sums its channel over the chunks with independent loads, in
-// chunk order (deterministic).
+// output channel.  Each thread loads the records of up to 32 chunks in one
+// batch (one memory round trip), forms the chunk weights of its head itself
+// (no barrier) and sums its channel over the chunks in chunk order
+// (deterministic).
 // ---------------------------------------------------------------------------
 template <typename OutT>
 __global__ __launch_bounds__(128) void combine_kernel(DecodeArgs a) {
+    constexpr int CB = 32;                 // chunks whose records are loaded in one batch
     const int b = blockIdx.x / a.num_q_heads, hq = blockIdx.x % a.num_q_heads;
     const int G = a.group, D = a.head_dim;
     const int kv = hq / G, hh = hq % G;
@@ -561,16 +563,30 @@ __global__ __launch_bounds__(128) void combine_kernel(DecodeArgs a) {
     const size_t rec_size = 32 + (size_t)G * D;
     const float *rec0 = a.part + ((size_t)b * a.num_kv_heads + kv) * a.chunks_max * rec_size;
     for (int d = threadIdx.x; d < D; d += blockDim.x) {
-        float M = -__builtin_inff();
-        for (int c = 0; c < nchunks; ++c) M = fmaxf(M, rec0[c * rec_size + hh]);
-        float acc = 0.f, L = 0.f;
-#pragma unroll 4
-        for (int c = 0; c < nchunks; ++c) {
-            const float *rec = rec0 + c * rec_size;
-            const float mc = rec[hh];
-            const float e = mc == -__builtin_inff() ? 0.f : exp2_fast(mc - M);
-            L += e * rec[16 + hh];
-            acc += e * rec[32 + hh * D + d];
+        float M = -__builtin_inff(), acc = 0.f, L = 0.f;
+        for (int c0 = 0; c0 < nchunks; c0 += CB) {
+            float mv[CB], lv[CB], ov[CB];
+#pragma unroll
+            for (int c = 0; c < CB; ++c) {
+                const bool in = c0 + c < nchunks;
+                const float *rec = rec0 + (size_t)(c0 + c) * rec_size;
+                mv[c] = in ? rec[hh] : -__builtin_inff();
+                lv[c] = in ? rec[16 + hh] : 0.f;
+                ov[c] = in ? rec[32 + hh * D + d] : 0.f;
+            }
+            float Mb = M;
+#pragma unroll
+            for (int c = 0; c < CB; ++c) Mb = fmaxf(Mb, mv[c]);
+            const float sc = M == -__builtin_inff() ? 0.f : exp2_fast(M - Mb);
+            acc *= sc;
+            L *= sc;
+#pragma unroll
+            for (int c = 0; c < CB; ++c) {
+                const float e = mv[c] == -__builtin_inff() ? 0.f : exp2_fast(mv[c] - Mb);
+                L += e * lv[c];
+                acc += e * ov[c];
+            }
+            M = Mb;
         }
         const size_t o = ((size_t)b * a.num_q_heads + hq) * D + d;
         if constexpr (sizeof(OutT) == 2) static_cast<uint16_t *>(a.out)[o] = f32_to_bf16_rne(acc / L);

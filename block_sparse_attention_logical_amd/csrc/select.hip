@@ -96,16 +96,25 @@ __global__ __launch_bounds__(kScoreThreads) void score_kernel(ScoreArgs a) {
     const int lg = (threadIdx.x / kWave) * LPP + lane / LPL;    // lane group in the workgroup
     const int ch0 = (lane % LPL) * C;
 
+    const int g = a.page_size / a.logical_page;
+    const int m0 = blk * a.pages_per_block;
+    const int j0 = m0 * g;
+    // page-table entries of this lane group's logical pages, loaded together
+    // with seq_lens and q (nothing here waits on another load)
+    int pools[kScoreMaxIter];
+#pragma unroll
+    for (int it = 0; it < kScoreMaxIter; ++it) {
+        const int m = (j0 + lg + it * GROUPS) / g;
+        pools[it] = m < a.max_pages ? a.page_table[(size_t)b * a.max_pages + m] : 0;
+    }
+    const int L = a.seq_lens[b];
     double qp[C], qn[C];
     load_q_pos_neg<C>(a, b, kv, ch0, qp, qn);
-    const int L = a.seq_lens[b];
     const int n_pages = (L + a.page_size - 1) / a.page_size;
-    const int m0 = blk * a.pages_per_block;
     if (m0 >= n_pages) return;
     const int m1 = min(m0 + a.pages_per_block, n_pages);
-    const int g = a.page_size / a.logical_page;
     const int nlog = (L + a.logical_page - 1) / a.logical_page;
-    const int j0 = m0 * g, j1 = min(m1 * g, nlog);
+    const int j1 = min(m1 * g, nlog);
     const int j_cur = (L - 1) / a.logical_page;
 
     double qsum = 0.0;                      // int4 only: sum over all channels of Qp + Qn
@@ -123,12 +132,6 @@ __global__ __launch_bounds__(kScoreThreads) void score_kernel(ScoreArgs a) {
     // The page-table entries of all iterations are loaded first, then every
     // iteration's statistics, so no load waits on another.
     const int n_iter = (j1 - j0 + GROUPS - 1) / GROUPS;
-    int pools[kScoreMaxIter];
-#pragma unroll
-    for (int it = 0; it < kScoreMaxIter; ++it) {
-        const int j = j0 + lg + it * GROUPS;
-        pools[it] = (it < n_iter && j < j1) ? a.page_table[(size_t)b * a.max_pages + j / g] : 0;
-    }
     uint4 st_lo[kScoreMaxIter], st_hi[kScoreMaxIter];
 #pragma unroll
     for (int it = 0; it < kScoreMaxIter; ++it) {
@@ -299,25 +302,29 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(TopkArgs a) {
     const int r = blockIdx.x % a.n_ret;
     const int b = blockIdx.x / a.n_ret;
     const int kv = a.ret_heads[r];
-    const int L = a.seq_lens[b];
-    const int n = (L + a.page_size - 1) / a.page_size;
     const int K = a.k;
     int32_t *out = a.selected + ((size_t)b * a.num_kv_heads + kv) * K;
     const double *P = a.phys + ((size_t)b * a.num_kv_heads + kv) * a.max_pages;
     const int tid = threadIdx.x;
 
+    // thread t owns the contiguous pages [t*seg, t*seg + cnt); the scores are
+    // loaded for every row slot at once, together with seq_lens, and the
+    // entries past the sequence's last page are dropped afterwards
+    const int seg = (a.max_pages + kTopkThreads - 1) / kTopkThreads;
+    const int i0 = min(a.max_pages, tid * seg);
+    double pv[kTopkPerThread];
+#pragma unroll
+    for (int e = 0; e < kTopkPerThread; ++e) pv[e] = e < seg && i0 + e < a.max_pages ? P[i0 + e] : 0.0;
+    const int L = a.seq_lens[b];
+    const int n = (L + a.page_size - 1) / a.page_size;
     if (n <= K) {                                 // every page, ascending, padded with -1
         for (int i = tid; i < K; i += blockDim.x) out[i] = i < n ? i : -1;
         return;
     }
-
-    // thread t owns the contiguous pages [t*seg, t*seg + cnt)
-    const int seg = (n + kTopkThreads - 1) / kTopkThreads;
-    const int i0 = min(n, tid * seg);
-    const int cnt = min(n, i0 + seg) - i0;
+    const int cnt = max(0, min(n, i0 + seg) - i0);
     unsigned long long key[kTopkPerThread];
 #pragma unroll
-    for (int e = 0; e < kTopkPerThread; ++e) key[e] = e < cnt ? order_key(P[i0 + e]) : 0ull;
+    for (int e = 0; e < kTopkPerThread; ++e) key[e] = e < cnt ? order_key(pv[e]) : 0ull;
 
     // the leading bits shared by every key decide nothing: find the highest
     // differing bit (block-wide and / or of the keys) and start the radix
