@@ -42,6 +42,7 @@ def parse():
     ap.add_argument("--replicas", type=int, default=8, help="KV pool replicas (layers) cycled through")
     ap.add_argument("--prefill-reps", type=int, default=3)
     ap.add_argument("--no-prefill", action="store_true")
+    ap.add_argument("--prefill-only", action="store_true", help="time only the prefill leg (profiling runs)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="budget of the oracle CPU sample")
     ap.add_argument("--eager", action="store_true", help="time eager launches instead of graph replay")
@@ -311,6 +312,10 @@ def main():
 
     if args.counters:
         counters_run(args, torch, lsa, W)
+        return
+    if args.prefill_only:
+        pre = bench_prefill(args, torch, lsa, W, O)
+        print(json.dumps({"prefill_ms": round(pre["seconds"] * 1e3, 3), "tflops": round(pre["tflops"], 1)}))
         return
     dec = bench_decode(args, torch, lsa, W)
     pre = None if args.no_prefill else bench_prefill(args, torch, lsa, W, O)

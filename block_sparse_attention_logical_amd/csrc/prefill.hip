@@ -68,14 +68,26 @@ __device__ __forceinline__ void tile_ranges(const PrefillArgs &p, const PItem &i
 }
 
 // ---------------------------------------------------------------------------
-// bf16 MFMA kernel, head_dim D
+// bf16 MFMA kernel, head_dim D.  Eight wavefronts: wave w takes query head
+// hg*4 + w/2 and query rows 32*(w%2) .. +31 of the tile, so with GQA group 4
+// one workgroup covers the tile's four heads and reads each K/V tile once.
+// K/V tiles are double-buffered in LDS: the global loads of tile i+1 are in
+// flight while tile i is computed, one barrier per tile.  In LDS, key rows are
+// stored in MFMA-row order (the order the QK A operand reads them), so the
+// eight lanes of a 128-byte LDS read touch eight consecutive padded rows.
 // ---------------------------------------------------------------------------
 template <int D>
-__global__ __launch_bounds__(256) void prefill_bf16_kernel(PrefillArgs p) {
-    constexpr int KS = D + 8;          // LDS row stride of K (elements), padded
-    constexpr int VS = kTile + 8;      // LDS row stride of V^T (elements), padded
-    __shared__ __attribute__((aligned(16))) uint16_t k_lds[kTile * KS];
-    __shared__ __attribute__((aligned(16))) uint16_t v_lds[D * VS];
+__global__ __launch_bounds__(512, 2) void prefill_bf16_kernel(PrefillArgs p) {
+    typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+    typedef float floatx2 __attribute__((ext_vector_type(2)));
+    constexpr int KS = D + 8;          // LDS row stride of K (elements), padded 16 bytes
+    constexpr int VS = kTile + 8;      // LDS row stride of V^T (elements), padded 16 bytes
+    constexpr int KCH = kTile * D / 8; // 16-byte chunks of a K tile
+    constexpr int VCH = D * kTile / 8; // 16-byte chunks of a V^T tile
+    constexpr int NT = 512;
+    constexpr int KPT = KCH / NT, VPT = VCH / NT;   // chunks per thread
+    __shared__ __attribute__((aligned(16))) uint16_t k_lds[2][kTile * KS];
+    __shared__ __attribute__((aligned(16))) uint16_t v_lds[2][D * VS];
 
     const PItem it = prefill_item(p);
     int e0, s1;
@@ -83,151 +95,160 @@ __global__ __launch_bounds__(256) void prefill_bf16_kernel(PrefillArgs p) {
 
     const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
     const int T = p.seq_len, G = p.group, HQ = p.num_q_heads, NP = p.page_size;
-    const int hq_local = it.hg * 4 + wave;          // query head within the group
+    const int hq_local = it.hg * 4 + (wave >> 1);
     const bool head_ok = hq_local < G;
     const int hq = it.kv * G + min(hq_local, G - 1);
+    const int q0 = it.a * kTile + 32 * (wave & 1);  // first query row of this wave
     const int col = lane & 31, lg = lane >> 5;      // MFMA column / lane group
 
-    // Q^T as B operand: query 32*qt + col, channels 16*s + 8*lg + j
-    bf16x8 qb[2][D / 16];
-#pragma unroll
-    for (int qt = 0; qt < 2; ++qt) {
-        const int row = min(it.a * kTile + 32 * qt + col, T - 1);
+    // Q^T as B operand: query q0 + col, channels 16*s + 8*lg + j
+    bf16x8 qb[D / 16];
+    {
+        const int row = min(q0 + col, T - 1);
         const uint16_t *qrow = static_cast<const uint16_t *>(p.q) + ((size_t)row * HQ + hq) * D;
 #pragma unroll
         for (int s = 0; s < D / 16; ++s)
-            qb[qt][s] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4 *>(qrow + 16 * s + 8 * lg));
+            qb[s] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4 *>(qrow + 16 * s + 8 * lg));
     }
 
-    floatx16 o[D / 32][2];
+    floatx16 o[D / 32];
 #pragma unroll
     for (int dt = 0; dt < D / 32; ++dt)
 #pragma unroll
-        for (int qt = 0; qt < 2; ++qt)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) o[dt][qt][r] = 0.f;
-    float m_run[2] = {-__builtin_inff(), -__builtin_inff()};
-    float l_run[2] = {0.f, 0.f};
-
-    // MFMA row rho = 8*ra + 4*rg + rc of a 32-key tile holds key 16*(ra/2) + 8*rg + 4*(ra%2) + rc
-    const int rho = lane & 31;
-    const int key_of_row = 16 * ((rho >> 3) >> 1) + 8 * ((rho >> 2) & 1) + 4 * ((rho >> 3) & 1) + (rho & 3);
+        for (int r = 0; r < 16; ++r) o[dt][r] = 0.f;
+    float m_run = -__builtin_inff();   // running max of the raw scores of query q0 + col
+    float l_run = 0.f;                 // this lane's part of the running sum
 
     const uint16_t *kpool = static_cast<const uint16_t *>(p.k);
     const uint16_t *vpool = static_cast<const uint16_t *>(p.v);
     const int n_iter = e0 + (it.a - s1 + 1);
-    for (int ii = 0; ii < n_iter; ++ii) {
+
+    // global -> registers for tile ii (zero keys >= T); registers -> LDS buffer
+    uint4 kreg[KPT], vreg[VPT];
+    auto fetch = [&](int ii) {
         const int c = ii < e0 ? ii : s1 + (ii - e0);
-        // ---- stage K tile [64][D] and V^T tile [D][64] in LDS (zero keys >= T)
         const int key0 = c * kTile;
         const int pool = p.page_table[key0 / NP];
         const int slot0 = key0 % NP;
         const size_t hp = (size_t)pool * p.num_kv_heads + it.kv;
-        __syncthreads();
-        {
-            constexpr int KCH = kTile * D / 8;      // 16-byte chunks of the K tile
-            for (int ch = tid; ch < KCH; ch += 256) {
-                const int r = ch / (D / 8), cc = ch % (D / 8);
-                uint4 val = make_uint4(0, 0, 0, 0);
-                if (key0 + r < T) val = *reinterpret_cast<const uint4 *>(kpool + (hp * NP + slot0 + r) * D + cc * 8);
-                *reinterpret_cast<uint4 *>(&k_lds[r * KS + cc * 8]) = val;
-            }
-            constexpr int VCH = D * kTile / 8;
-            for (int ch = tid; ch < VCH; ch += 256) {
-                const int d = ch / (kTile / 8), cc = ch % (kTile / 8);
-                uint4 val = *reinterpret_cast<const uint4 *>(vpool + (hp * D + d) * NP + slot0 + cc * 8);
-                const int kbase = key0 + cc * 8;
-                if (kbase + 8 > T) {
-                    uint16_t e[8];
-                    __builtin_memcpy(e, &val, 16);
 #pragma unroll
-                    for (int j = 0; j < 8; ++j) if (kbase + j >= T) e[j] = 0;
-                    __builtin_memcpy(&val, e, 16);
-                }
-                *reinterpret_cast<uint4 *>(&v_lds[d * VS + cc * 8]) = val;
-            }
+        for (int e = 0; e < KPT; ++e) {
+            const int ch = tid + e * NT;
+            const int r = ch / (D / 8), cc = ch % (D / 8);
+            kreg[e] = key0 + r < T ? *reinterpret_cast<const uint4 *>(kpool + (hp * NP + slot0 + r) * D + cc * 8)
+                                   : make_uint4(0, 0, 0, 0);
         }
-        __syncthreads();
-        if (!head_ok) continue;
+#pragma unroll
+        for (int e = 0; e < VPT; ++e) {
+            const int ch = tid + e * NT;
+            const int d = ch / (kTile / 8), cc = ch % (kTile / 8);
+            uint4 val = *reinterpret_cast<const uint4 *>(vpool + (hp * D + d) * NP + slot0 + cc * 8);
+            const int kbase = key0 + cc * 8;
+            if (kbase + 8 > T) {
+                const int nv = T - kbase;          // valid keys in this chunk (<= 7)
+                uint32_t w[4] = {val.x, val.y, val.z, val.w};
+#pragma unroll
+                for (int q2 = 0; q2 < 4; ++q2)
+                    w[q2] &= (2 * q2 < nv ? 0x0000FFFFu : 0u) | (2 * q2 + 1 < nv ? 0xFFFF0000u : 0u);
+                val = make_uint4(w[0], w[1], w[2], w[3]);
+            }
+            vreg[e] = val;
+        }
+    };
+    auto stash = [&](int buf) {
+#pragma unroll
+        for (int e = 0; e < KPT; ++e) {
+            const int ch = tid + e * NT;
+            const int key = ch / (D / 8), cc = ch % (D / 8);
+            // key k of a 32-key half is stored at the LDS row of the MFMA row that reads it
+            const int kk = key & 31;
+            const int rho = 8 * (2 * (kk >> 4) + ((kk >> 2) & 1)) + 4 * ((kk >> 3) & 1) + (kk & 3);
+            *reinterpret_cast<uint4 *>(&k_lds[buf][((key & 32) + rho) * KS + cc * 8]) = kreg[e];
+        }
+#pragma unroll
+        for (int e = 0; e < VPT; ++e) {
+            const int ch = tid + e * NT;
+            const int d = ch / (kTile / 8), cc = ch % (kTile / 8);
+            *reinterpret_cast<uint4 *>(&v_lds[buf][d * VS + cc * 8]) = vreg[e];
+        }
+    };
 
-        // ---- S^T = K Q^T : [kt][qt] 32x32 tiles
-        floatx16 s[2][2];
+    fetch(0);
+    stash(0);
+    __syncthreads();
+    const float sc = p.scale_log2;
+    for (int ii = 0; ii < n_iter; ++ii) {
+        const int buf = ii & 1;
+        if (ii + 1 < n_iter) fetch(ii + 1);            // in flight during this tile's MFMAs
+        const int c = ii < e0 ? ii : s1 + (ii - e0);
+        if (head_ok) {
+            // ---- S^T = K Q^T : two 32-key tiles, lane holds keys 16*(r/8) + 8*lg + r%8 of tile kt
+            floatx16 s[2];
 #pragma unroll
-        for (int kt = 0; kt < 2; ++kt)
+            for (int kt = 0; kt < 2; ++kt) {
 #pragma unroll
-            for (int qt = 0; qt < 2; ++qt)
+                for (int r = 0; r < 16; ++r) s[kt][r] = 0.f;
+                const uint16_t *krow = &k_lds[buf][(32 * kt + col) * KS + 8 * lg];
 #pragma unroll
-                for (int r = 0; r < 16; ++r) s[kt][qt][r] = 0.f;
-#pragma unroll
-        for (int kt = 0; kt < 2; ++kt) {
-            const uint16_t *krow = &k_lds[(32 * kt + key_of_row) * KS + 8 * lg];
-#pragma unroll
-            for (int st = 0; st < D / 16; ++st) {
-                const bf16x8 ka = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4 *>(krow + 16 * st));
-#pragma unroll
-                for (int qt = 0; qt < 2; ++qt)
-                    s[kt][qt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qb[qt][st], s[kt][qt], 0, 0, 0);
+                for (int st = 0; st < D / 16; ++st) {
+                    const bf16x8 ka = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4 *>(krow + 16 * st));
+                    s[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qb[st], s[kt], 0, 0, 0);
+                }
             }
-        }
-        // ---- online softmax per query column; lane holds keys 16*(r/8) + 8*lg + (r%8) of tile kt
-        const bool diag = c == it.a;
+            // ---- online softmax of column q0 + col (raw scores; scale folded into exp2)
+            if (c == it.a) {                           // diagonal tile: causal mask
+                const int qrow = q0 + col;
 #pragma unroll
-        for (int qt = 0; qt < 2; ++qt) {
-            const int qrow = it.a * kTile + 32 * qt + col;
+                for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r)
+                        if (c * kTile + 32 * kt + 16 * (r >> 3) + 8 * lg + (r & 7) > qrow) s[kt][r] = -__builtin_inff();
+            }
             float mx = -__builtin_inff();
 #pragma unroll
             for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    float x = s[kt][qt][r] * p.scale_log2;
-                    if (diag) {
-                        const int key = key0 + 32 * kt + 16 * (r >> 3) + 8 * lg + (r & 7);
-                        if (key > qrow) x = -__builtin_inff();
-                    }
-                    s[kt][qt][r] = x;
-                    mx = fmaxf(mx, x);
-                }
+                for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kt][r]);
             mx = fmaxf(mx, __shfl_xor(mx, 32, kWave));
-            const float m_new = fmaxf(m_run[qt], mx);
-            const float alpha = exp2_fast(m_run[qt] - m_new);
-            float ps = 0.f;
+            const float m_new = fmaxf(m_run, mx);
+            if (__ballot(m_new > m_run) != 0) {        // rescale only when some column's max moved
+                const float alpha = exp2_fast((m_run - m_new) * sc);
+                l_run *= alpha;
+#pragma unroll
+                for (int dt = 0; dt < D / 32; ++dt) o[dt] *= alpha;
+                m_run = m_new;
+            }
+            const float mb = m_run * sc;
+            bf16x8 pb[2][2];
 #pragma unroll
             for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    const float e = exp2_fast(s[kt][qt][r] - m_new);
-                    s[kt][qt][r] = e;
-                    ps += e;
-                }
-            l_run[qt] = l_run[qt] * alpha + ps;
-            m_run[qt] = m_new;
-#pragma unroll
-            for (int dt = 0; dt < D / 32; ++dt) o[dt][qt] *= alpha;
-        }
-        // ---- O^T += V^T P^T ; k-step (kt, st): keys 32*kt + 16*st + 8*lg + j
-#pragma unroll
-        for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-            for (int st = 0; st < 2; ++st) {
-                bf16x8 pb[2];
-#pragma unroll
-                for (int qt = 0; qt < 2; ++qt) {
+                for (int st = 0; st < 2; ++st) {
                     uint32_t pk[4];
 #pragma unroll
-                    for (int j = 0; j < 8; j += 2)
-                        pk[j / 2] = uint32_t(f32_to_bf16_rne(s[kt][qt][8 * st + j])) |
-                                    (uint32_t(f32_to_bf16_rne(s[kt][qt][8 * st + j + 1])) << 16);
-                    pb[qt] = __builtin_bit_cast(bf16x8, make_uint4(pk[0], pk[1], pk[2], pk[3]));
+                    for (int j = 0; j < 8; j += 2) {
+                        const float e0v = exp2_fast(fmaf(s[kt][8 * st + j], sc, -mb));
+                        const float e1v = exp2_fast(fmaf(s[kt][8 * st + j + 1], sc, -mb));
+                        l_run += e0v + e1v;
+                        const bf16x2 h2 = __builtin_convertvector(floatx2{e0v, e1v}, bf16x2);
+                        pk[j / 2] = __builtin_bit_cast(uint32_t, h2);
+                    }
+                    pb[kt][st] = __builtin_bit_cast(bf16x8, make_uint4(pk[0], pk[1], pk[2], pk[3]));
                 }
+            // ---- O^T += V^T P^T ; k-step (kt, st): keys 32*kt + 16*st + 8*lg + j
 #pragma unroll
-                for (int dt = 0; dt < D / 32; ++dt) {
-                    const bf16x8 va = __builtin_bit_cast(
-                        bf16x8, *reinterpret_cast<const uint4 *>(&v_lds[(32 * dt + col) * VS + 32 * kt + 16 * st + 8 * lg]));
+            for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
-                    for (int qt = 0; qt < 2; ++qt)
-                        o[dt][qt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pb[qt], o[dt][qt], 0, 0, 0);
-                }
-            }
+                for (int st = 0; st < 2; ++st)
+#pragma unroll
+                    for (int dt = 0; dt < D / 32; ++dt) {
+                        const bf16x8 va = __builtin_bit_cast(
+                            bf16x8, *reinterpret_cast<const uint4 *>(&v_lds[buf][(32 * dt + col) * VS + 32 * kt + 16 * st + 8 * lg]));
+                        o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pb[kt][st], o[dt], 0, 0, 0);
+                    }
+        }
+        if (ii + 1 < n_iter) stash(buf ^ 1);
+        __syncthreads();
     }
 
     if (p.tile_counter && tid == 0) {
@@ -235,27 +256,24 @@ __global__ __launch_bounds__(256) void prefill_bf16_kernel(PrefillArgs p) {
         atomicAdd(p.tile_counter, (unsigned long long)n_iter * heads_here);
     }
     if (!head_ok) return;
-    // ---- normalise and store: lane holds query 32*qt + col, channels 32*dt + 8*(r/4) + 4*lg + r%4
+    // ---- normalise and store: lane holds query q0 + col, channels 32*dt + 8*(r/4) + 4*lg + r%4
+    const float lt = l_run + __shfl_xor(l_run, 32, kWave);
+    const float inv = 1.f / lt;
+    const int row = q0 + col;
+    if (row >= T) return;
+    uint16_t *orow = static_cast<uint16_t *>(p.out) + ((size_t)row * HQ + hq) * D;
 #pragma unroll
-    for (int qt = 0; qt < 2; ++qt) {
-        const float lt = l_run[qt] + __shfl_xor(l_run[qt], 32, kWave);
-        const float inv = 1.f / lt;
-        const int row = it.a * kTile + 32 * qt + col;
-        if (row >= T) continue;
-        uint16_t *orow = static_cast<uint16_t *>(p.out) + ((size_t)row * HQ + hq) * D;
+    for (int dt = 0; dt < D / 32; ++dt)
 #pragma unroll
-        for (int dt = 0; dt < D / 32; ++dt)
-#pragma unroll
-            for (int rb = 0; rb < 4; ++rb) {
-                const int d0 = 32 * dt + 8 * rb + 4 * lg;
-                uint2 pk;
-                pk.x = uint32_t(f32_to_bf16_rne(o[dt][qt][4 * rb] * inv)) |
-                       (uint32_t(f32_to_bf16_rne(o[dt][qt][4 * rb + 1] * inv)) << 16);
-                pk.y = uint32_t(f32_to_bf16_rne(o[dt][qt][4 * rb + 2] * inv)) |
-                       (uint32_t(f32_to_bf16_rne(o[dt][qt][4 * rb + 3] * inv)) << 16);
-                *reinterpret_cast<uint2 *>(orow + d0) = pk;
-            }
-    }
+        for (int rb = 0; rb < 4; ++rb) {
+            const int d0 = 32 * dt + 8 * rb + 4 * lg;
+            const bf16x2 a01 = __builtin_convertvector(floatx2{o[dt][4 * rb] * inv, o[dt][4 * rb + 1] * inv}, bf16x2);
+            const bf16x2 a23 = __builtin_convertvector(floatx2{o[dt][4 * rb + 2] * inv, o[dt][4 * rb + 3] * inv}, bf16x2);
+            uint2 pk;
+            pk.x = __builtin_bit_cast(uint32_t, a01);
+            pk.y = __builtin_bit_cast(uint32_t, a23);
+            *reinterpret_cast<uint2 *>(orow + d0) = pk;
+        }
 }
 
 // ---------------------------------------------------------------------------
@@ -347,8 +365,8 @@ hipError_t launch_prefill(const PrefillArgs &p, int dtype, hipStream_t s) {
     if (p.n_items == 0) return hipSuccess;
     const dim3 grid((unsigned)p.n_items), block(256);
     if (dtype == LSA_BF16) {
-        if (p.head_dim == 128) hipLaunchKernelGGL(prefill_bf16_kernel<128>, grid, block, 0, s, p);
-        else hipLaunchKernelGGL(prefill_bf16_kernel<64>, grid, block, 0, s, p);
+        if (p.head_dim == 128) hipLaunchKernelGGL(prefill_bf16_kernel<128>, grid, dim3(512), 0, s, p);
+        else hipLaunchKernelGGL(prefill_bf16_kernel<64>, grid, dim3(512), 0, s, p);
     } else {
         // f32 is the small-model path: head_dim 64 only (validated by the caller)
         const size_t lds = 2 * (size_t)kTile * 64 * sizeof(float);
