@@ -22,6 +22,8 @@
 // bf16 path: v_mfma_f32_32x32x16_bf16 for S^T = K Q^T (keys in M, queries in
 // N) and O^T = V^T P^T.  Keys are placed on MFMA rows so that the S^T
 // registers of a lane are directly the B operand of the PV product.
+#include <type_traits>
+
 #include "lsa_internal.h"
 
 namespace lsa {
@@ -71,10 +73,15 @@ __device__ __forceinline__ void tile_ranges(const PrefillArgs &p, const PItem &i
 // bf16 MFMA kernel, head_dim D.  Eight wavefronts: wave w takes query head
 // hg*4 + w/2 and query rows 32*(w%2) .. +31 of the tile, so with GQA group 4
 // one workgroup covers the tile's four heads and reads each K/V tile once.
-// K/V tiles are double-buffered in LDS: the global loads of tile i+1 are in
-// flight while tile i is computed, one barrier per tile.  In LDS, key rows are
-// stored in MFMA-row order (the order the QK A operand reads them), so the
-// eight lanes of a 128-byte LDS read touch eight consecutive padded rows.
+// Software pipeline: iteration t issues the QK^T MFMAs of key tile t, then
+// runs the softmax and PV of tile t-1, whose VALU work overlaps the QK
+// MFMAs in flight.  K tiles and V tiles are double-buffered in LDS separately
+// (V lags K by one tile); the global loads of the next tiles are in flight
+// during the compute, one barrier per tile.  The last tile is the diagonal
+// one: its causal mask is applied in the pipeline's epilogue only.  In LDS,
+// key rows are stored in MFMA-row order (the order the QK A operand reads
+// them), so the eight lanes of a 128-byte LDS read touch eight consecutive
+// padded rows.
 // ---------------------------------------------------------------------------
 template <int D>
 __global__ __launch_bounds__(512, 2) void prefill_bf16_kernel(PrefillArgs p) {
@@ -122,28 +129,37 @@ __global__ __launch_bounds__(512, 2) void prefill_bf16_kernel(PrefillArgs p) {
     const uint16_t *kpool = static_cast<const uint16_t *>(p.k);
     const uint16_t *vpool = static_cast<const uint16_t *>(p.v);
     const int n_iter = e0 + (it.a - s1 + 1);
-
-    // global -> registers for tile ii (zero keys >= T); registers -> LDS buffer
-    uint4 kreg[KPT], vreg[VPT];
-    auto fetch = [&](int ii) {
-        const int c = ii < e0 ? ii : s1 + (ii - e0);
+    auto tile_of = [&](int ii) { return ii < e0 ? ii : s1 + (ii - e0); };
+    auto head_page = [&](int c, int &slot0) {
         const int key0 = c * kTile;
-        const int pool = p.page_table[key0 / NP];
-        const int slot0 = key0 % NP;
-        const size_t hp = (size_t)pool * p.num_kv_heads + it.kv;
+        slot0 = key0 % NP;
+        return (size_t)p.page_table[key0 / NP] * p.num_kv_heads + it.kv;
+    };
+
+    // global -> registers (keys >= T read as zero); registers -> LDS
+    uint4 kreg[KPT], vreg[VPT];
+    auto fetch_k = [&](int ii) {
+        const int c = tile_of(ii);
+        int slot0;
+        const size_t hp = head_page(c, slot0);
 #pragma unroll
         for (int e = 0; e < KPT; ++e) {
             const int ch = tid + e * NT;
             const int r = ch / (D / 8), cc = ch % (D / 8);
-            kreg[e] = key0 + r < T ? *reinterpret_cast<const uint4 *>(kpool + (hp * NP + slot0 + r) * D + cc * 8)
-                                   : make_uint4(0, 0, 0, 0);
+            kreg[e] = c * kTile + r < T ? *reinterpret_cast<const uint4 *>(kpool + (hp * NP + slot0 + r) * D + cc * 8)
+                                        : make_uint4(0, 0, 0, 0);
         }
+    };
+    auto fetch_v = [&](int ii) {
+        const int c = tile_of(ii);
+        int slot0;
+        const size_t hp = head_page(c, slot0);
 #pragma unroll
         for (int e = 0; e < VPT; ++e) {
             const int ch = tid + e * NT;
             const int d = ch / (kTile / 8), cc = ch % (kTile / 8);
             uint4 val = *reinterpret_cast<const uint4 *>(vpool + (hp * D + d) * NP + slot0 + cc * 8);
-            const int kbase = key0 + cc * 8;
+            const int kbase = c * kTile + cc * 8;
             if (kbase + 8 > T) {
                 const int nv = T - kbase;          // valid keys in this chunk (<= 7)
                 uint32_t w[4] = {val.x, val.y, val.z, val.w};
@@ -155,7 +171,7 @@ __global__ __launch_bounds__(512, 2) void prefill_bf16_kernel(PrefillArgs p) {
             vreg[e] = val;
         }
     };
-    auto stash = [&](int buf) {
+    auto stash_k = [&](int buf) {
 #pragma unroll
         for (int e = 0; e < KPT; ++e) {
             const int ch = tid + e * NT;
@@ -165,6 +181,8 @@ __global__ __launch_bounds__(512, 2) void prefill_bf16_kernel(PrefillArgs p) {
             const int rho = 8 * (2 * (kk >> 4) + ((kk >> 2) & 1)) + 4 * ((kk >> 3) & 1) + (kk & 3);
             *reinterpret_cast<uint4 *>(&k_lds[buf][((key & 32) + rho) * KS + cc * 8]) = kreg[e];
         }
+    };
+    auto stash_v = [&](int buf) {
 #pragma unroll
         for (int e = 0; e < VPT; ++e) {
             const int ch = tid + e * NT;
@@ -173,82 +191,97 @@ __global__ __launch_bounds__(512, 2) void prefill_bf16_kernel(PrefillArgs p) {
         }
     };
 
-    fetch(0);
-    stash(0);
-    __syncthreads();
     const float sc = p.scale_log2;
-    for (int ii = 0; ii < n_iter; ++ii) {
-        const int buf = ii & 1;
-        if (ii + 1 < n_iter) fetch(ii + 1);            // in flight during this tile's MFMAs
-        const int c = ii < e0 ? ii : s1 + (ii - e0);
-        if (head_ok) {
-            // ---- S^T = K Q^T : two 32-key tiles, lane holds keys 16*(r/8) + 8*lg + r%8 of tile kt
-            floatx16 s[2];
+    // S^T = K Q^T of the tile in K buffer kb: lane holds keys 32*kt + 16*(r/8) + 8*lg + r%8, query q0 + col
+    auto qk = [&](int kb, floatx16 (&s)[2]) {
 #pragma unroll
-            for (int kt = 0; kt < 2; ++kt) {
+        for (int kt = 0; kt < 2; ++kt) {
+            const uint16_t *krow = &k_lds[kb][(32 * kt + col) * KS + 8 * lg];
+            s[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4 *>(krow)), qb[0], floatx16{}, 0, 0, 0);
 #pragma unroll
-                for (int r = 0; r < 16; ++r) s[kt][r] = 0.f;
-                const uint16_t *krow = &k_lds[buf][(32 * kt + col) * KS + 8 * lg];
-#pragma unroll
-                for (int st = 0; st < D / 16; ++st) {
-                    const bf16x8 ka = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4 *>(krow + 16 * st));
-                    s[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qb[st], s[kt], 0, 0, 0);
-                }
+            for (int st = 1; st < D / 16; ++st) {
+                const bf16x8 ka = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4 *>(krow + 16 * st));
+                s[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qb[st], s[kt], 0, 0, 0);
             }
-            // ---- online softmax of column q0 + col (raw scores; scale folded into exp2)
-            if (c == it.a) {                           // diagonal tile: causal mask
-                const int qrow = q0 + col;
-#pragma unroll
-                for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-                    for (int r = 0; r < 16; ++r)
-                        if (c * kTile + 32 * kt + 16 * (r >> 3) + 8 * lg + (r & 7) > qrow) s[kt][r] = -__builtin_inff();
-            }
-            float mx = -__builtin_inff();
-#pragma unroll
-            for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-                for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kt][r]);
-            mx = fmaxf(mx, __shfl_xor(mx, 32, kWave));
-            const float m_new = fmaxf(m_run, mx);
-            if (__ballot(m_new > m_run) != 0) {        // rescale only when some column's max moved
-                const float alpha = exp2_fast((m_run - m_new) * sc);
-                l_run *= alpha;
-#pragma unroll
-                for (int dt = 0; dt < D / 32; ++dt) o[dt] *= alpha;
-                m_run = m_new;
-            }
-            const float mb = m_run * sc;
-            bf16x8 pb[2][2];
-#pragma unroll
-            for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-                for (int st = 0; st < 2; ++st) {
-                    uint32_t pk[4];
-#pragma unroll
-                    for (int j = 0; j < 8; j += 2) {
-                        const float e0v = exp2_fast(fmaf(s[kt][8 * st + j], sc, -mb));
-                        const float e1v = exp2_fast(fmaf(s[kt][8 * st + j + 1], sc, -mb));
-                        l_run += e0v + e1v;
-                        const bf16x2 h2 = __builtin_convertvector(floatx2{e0v, e1v}, bf16x2);
-                        pk[j / 2] = __builtin_bit_cast(uint32_t, h2);
-                    }
-                    pb[kt][st] = __builtin_bit_cast(bf16x8, make_uint4(pk[0], pk[1], pk[2], pk[3]));
-                }
-            // ---- O^T += V^T P^T ; k-step (kt, st): keys 32*kt + 16*st + 8*lg + j
-#pragma unroll
-            for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-                for (int st = 0; st < 2; ++st)
-#pragma unroll
-                    for (int dt = 0; dt < D / 32; ++dt) {
-                        const bf16x8 va = __builtin_bit_cast(
-                            bf16x8, *reinterpret_cast<const uint4 *>(&v_lds[buf][(32 * dt + col) * VS + 32 * kt + 16 * st + 8 * lg]));
-                        o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pb[kt][st], o[dt], 0, 0, 0);
-                    }
         }
-        if (ii + 1 < n_iter) stash(buf ^ 1);
+    };
+    // online softmax of the scores s (DIAG: causal mask against key0), then O^T += V^T P^T
+    auto softmax_pv = [&](floatx16 (&s)[2], int vb, int key0, auto diag_tag) {
+        constexpr bool DIAG = decltype(diag_tag)::value;
+        if constexpr (DIAG) {
+            const int qrow = q0 + col;
+#pragma unroll
+            for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+                for (int r = 0; r < 16; ++r)
+                    if (key0 + 32 * kt + 16 * (r >> 3) + 8 * lg + (r & 7) > qrow) s[kt][r] = -__builtin_inff();
+        }
+        float mx = s[0][0];
+#pragma unroll
+        for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kt][r]);
+        mx = fmaxf(mx, __shfl_xor(mx, 32, kWave));
+        const float m_new = fmaxf(m_run, mx);
+        if (__ballot(m_new > m_run) != 0) {            // rescale only when some column's max moved
+            const float alpha = exp2_fast((m_run - m_new) * sc);
+            l_run *= alpha;
+#pragma unroll
+            for (int dt = 0; dt < D / 32; ++dt) o[dt] *= alpha;
+            m_run = m_new;
+        }
+        const float mb = m_run * sc;
+#pragma unroll
+        for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+            for (int st = 0; st < 2; ++st) {
+                uint32_t pk[4];
+#pragma unroll
+                for (int j = 0; j < 8; j += 2) {
+                    const float e0v = exp2_fast(fmaf(s[kt][8 * st + j], sc, -mb));
+                    const float e1v = exp2_fast(fmaf(s[kt][8 * st + j + 1], sc, -mb));
+                    l_run += e0v + e1v;
+                    pk[j / 2] = __builtin_bit_cast(uint32_t, __builtin_convertvector(floatx2{e0v, e1v}, bf16x2));
+                }
+                const bf16x8 pb = __builtin_bit_cast(bf16x8, make_uint4(pk[0], pk[1], pk[2], pk[3]));
+                // k-step (kt, st): keys 32*kt + 16*st + 8*lg + j
+#pragma unroll
+                for (int dt = 0; dt < D / 32; ++dt) {
+                    const bf16x8 va = __builtin_bit_cast(
+                        bf16x8, *reinterpret_cast<const uint4 *>(&v_lds[vb][(32 * dt + col) * VS + 32 * kt + 16 * st + 8 * lg]));
+                    o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pb, o[dt], 0, 0, 0);
+                }
+            }
+    };
+
+    // prologue: K(0) in LDS
+    fetch_k(0);
+    stash_k(0);
+    __syncthreads();
+    floatx16 sa[2], sb[2];                           // scores of even / odd tiles
+    auto step = [&](int ii, floatx16 (&s_cur)[2], floatx16 (&s_prev)[2]) {
+        // in flight during the compute: K(ii+1) and V(ii)
+        if (ii + 1 < n_iter) fetch_k(ii + 1);
+        fetch_v(ii);
+        if (head_ok) {
+            qk(ii & 1, s_cur);
+            if (ii > 0) softmax_pv(s_prev, (ii - 1) & 1, tile_of(ii - 1) * kTile, std::false_type{});
+        }
+        if (ii + 1 < n_iter) stash_k((ii + 1) & 1);
+        stash_v(ii & 1);
         __syncthreads();
+    };
+    int ii = 0;
+    for (; ii + 1 < n_iter; ii += 2) {
+        step(ii, sa, sb);
+        step(ii + 1, sb, sa);
+    }
+    if (ii < n_iter) step(ii, sa, sb);
+    // epilogue: the last tile (the diagonal one)
+    if (head_ok) {
+        if ((n_iter - 1) & 1) softmax_pv(sb, (n_iter - 1) & 1, tile_of(n_iter - 1) * kTile, std::true_type{});
+        else softmax_pv(sa, (n_iter - 1) & 1, tile_of(n_iter - 1) * kTile, std::true_type{});
     }
 
     if (p.tile_counter && tid == 0) {
