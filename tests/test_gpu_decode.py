@@ -178,3 +178,70 @@ def test_decode_full_size_cfg2_sampled():
     ret = [kv for kv in range(w.num_kv_heads) if w.head_kind[kv] == 0][:2]
     st = [kv for kv in range(w.num_kv_heads) if w.head_kind[kv] == 1][:2]
     print("max abs err", check_window(w, kv_heads=ret + st, batches=[0, 7]))
+
+
+def test_decode_full_size_cfg4_sampled():
+    """Config 4 at full size (B = 64, contexts 128K-256K, N_P = 128, permuted
+    pool of about 48 GiB): the whole batch runs on the GPU; the oracle
+    recomputes one retrieval and one streaming KV head of three sequences for
+    the 4-step window, selections included."""
+    w = W.make_decode(4, DEV)
+    ret = [kv for kv in range(w.num_kv_heads) if w.head_kind[kv] == 0][:1]
+    st = [kv for kv in range(w.num_kv_heads) if w.head_kind[kv] == 1][:1]
+    batches = [0, int(np.argmax(w.ctx)), int(np.argmin(w.ctx))]
+    print("max abs err", check_window(w, kv_heads=ret + st, batches=batches))
+    del w
+    torch.cuda.empty_cache()
+
+
+def test_decode_full_size_cfg5_int4_sampled():
+    """Config 5 at full size (KV4, B = 16, 256K context)."""
+    w = W.make_decode(5, DEV)
+    ret = [kv for kv in range(w.num_kv_heads) if w.head_kind[kv] == 0][:2]
+    st = [kv for kv in range(w.num_kv_heads) if w.head_kind[kv] == 1][:1]
+    print("max abs err", check_window(w, kv_heads=ret + st, batches=[0, 15]))
+    del w
+    torch.cuda.empty_cache()
+
+
+def test_decode_window_in_hip_graph_matches_eager():
+    """A whole decode window (selection every R steps, attention with the
+    statistics refresh) captured as a HIP graph and replayed three times, with
+    eager work in between, gives bitwise the eager outputs on every replay."""
+    w = W.make_decode(2, DEV, batch=3, ctx=[3000, 4500, 6000])
+    r = Runner(w)
+    stats0 = r.stats.clone()
+    eager = []
+    for i in range(w.window):
+        eager.append(r.step(i).clone())
+    outs = [torch.empty_like(w.q[i]) for i in range(w.window)]
+    lens = [w.seq_lens(i) for i in range(w.window)]
+
+    def window():
+        for i in range(w.window):
+            lsa.select_pages(w.q[i], r.kv, r.stats, w.page_table, lens[i], r.hd, w.token_budget, i,
+                             w.reuse_interval, r.selected, r.ws_sel)
+            lsa.sparse_decode_attn(w.q[i], r.kv, w.page_table, lens[i], r.hd, r.selected, w.token_budget,
+                                   outs[i], r.ws_dec, stats=r.stats)
+
+    r.stats.copy_(stats0)
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        window()                                   # warm-up on the capture stream
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        window()
+    for rep in range(3):
+        r.stats.copy_(stats0)
+        junk = torch.randn(1 << 20, device=DEV).sum()    # eager work between replays
+        torch.cuda.synchronize()
+        for o in outs:
+            o.fill_(float("nan"))
+        g.replay()
+        torch.cuda.synchronize()
+        for i in range(w.window):
+            assert torch.equal(outs[i].view(torch.int16), eager[i].view(torch.int16)), (rep, i)
+        del junk
