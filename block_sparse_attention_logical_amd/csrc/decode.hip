@@ -247,8 +247,7 @@ __global__ __launch_bounds__(256, 3) void decode_mfma_kernel(DecodeArgs a) {
             qb[s] = __builtin_bit_cast(bf16x8, raw);
         }
         if constexpr (I4) {
-            qsum += __shfl_xor(qsum, 16, kWave);
-            qsum += __shfl_xor(qsum, 32, kWave);
+            qsum = sum_xor32(sum_xor16(qsum));
         }
     }
     const PageList pl = make_list(a, w);
@@ -357,8 +356,7 @@ __global__ __launch_bounds__(256, 3) void decode_mfma_kernel(DecodeArgs a) {
                     if (!token_visible(a, w, tok0 + 8 * g4 + j)) x[j] = -__builtin_inff();
                     mb = fmaxf(mb, x[j]);
                 }
-                mb = fmaxf(mb, __shfl_xor(mb, 16, kWave));
-                mb = fmaxf(mb, __shfl_xor(mb, 32, kWave));
+                mb = max_xor32(max_xor16(mb));
                 const float m_new = fmaxf(m_run, mb);
                 const float alpha = exp2_fast(m_run - m_new);
                 float psum = 0.f, fed = 0.f;
@@ -411,12 +409,10 @@ __global__ __launch_bounds__(256, 3) void decode_mfma_kernel(DecodeArgs a) {
             }
         }
     }
-    l_run += __shfl_xor(l_run, 16, kWave);
-    l_run += __shfl_xor(l_run, 32, kWave);
+    l_run = sum_xor32(sum_xor16(l_run));
     if constexpr (I4) {
         // the head's correction sums the four lane groups' tokens
-        corr += __shfl_xor(corr, 16, kWave);
-        corr += __shfl_xor(corr, 32, kWave);
+        corr = sum_xor32(sum_xor16(corr));
     }
 
     float *my = lds + wave * (32 + 16 * D);
@@ -498,16 +494,12 @@ __global__ __launch_bounds__(256) void decode_f32_kernel(DecodeArgs a) {
             for (int hh = 0; hh < 16; ++hh) {
                 if (hh >= G) { alpha[hh] = 1.f; continue; }
                 const float x = vis ? sc[hh] * a.scale_log2 : -__builtin_inff();
-                float mb = x;
-#pragma unroll
-                for (int off = 1; off < kWave; off <<= 1) mb = fmaxf(mb, __shfl_xor(mb, off, kWave));
+                const float mb = wave_max(x);
                 if (mb == -__builtin_inff()) { alpha[hh] = 1.f; ps[hh * 64 + lane] = 0.f; continue; }
                 const float m_new = fmaxf(m_run[hh], mb);
                 alpha[hh] = exp2_fast(m_run[hh] - m_new);
                 const float pr = vis ? exp2_fast(x - m_new) : 0.f;
-                float psum = pr;
-#pragma unroll
-                for (int off = 1; off < kWave; off <<= 1) psum += __shfl_xor(psum, off, kWave);
+                const float psum = wave_sum(pr);
                 l_run[hh] = l_run[hh] * alpha[hh] + psum;
                 m_run[hh] = m_new;
                 ps[hh * 64 + lane] = pr;

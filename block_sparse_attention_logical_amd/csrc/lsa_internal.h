@@ -39,6 +39,133 @@ __device__ __forceinline__ float fp16_bits_to_f32(uint16_t h) {
 __device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
 
 // ----------------------------------------------------------------------------
+// cross-lane primitives on the VALU (DPP and gfx950 permlane swaps).  A
+// ds_bpermute (what __shfl_* lowers to) goes through the LDS crossbar and
+// costs a long round trip; chains of them dominated the small kernels.
+// ----------------------------------------------------------------------------
+
+// {x[l], x[l ^ 32]} in some order, in every lane l
+__device__ __forceinline__ void pair32(uint32_t x, uint32_t &a, uint32_t &b) {
+    const auto r = __builtin_amdgcn_permlane32_swap(x, x, false, false);
+    a = r[0];
+    b = r[1];
+}
+// {x[l], x[l ^ 16]} in some order, in every lane l
+__device__ __forceinline__ void pair16(uint32_t x, uint32_t &a, uint32_t &b) {
+    const auto r = __builtin_amdgcn_permlane16_swap(x, x, false, false);
+    a = r[0];
+    b = r[1];
+}
+__device__ __forceinline__ float max_xor32(float x) {
+    uint32_t a, b;
+    pair32(__float_as_uint(x), a, b);
+    return fmaxf(__uint_as_float(a), __uint_as_float(b));
+}
+__device__ __forceinline__ float max_xor16(float x) {
+    uint32_t a, b;
+    pair16(__float_as_uint(x), a, b);
+    return fmaxf(__uint_as_float(a), __uint_as_float(b));
+}
+__device__ __forceinline__ float sum_xor32(float x) {
+    uint32_t a, b;
+    pair32(__float_as_uint(x), a, b);
+    return __uint_as_float(a) + __uint_as_float(b);
+}
+__device__ __forceinline__ float sum_xor16(float x) {
+    uint32_t a, b;
+    pair16(__float_as_uint(x), a, b);
+    return __uint_as_float(a) + __uint_as_float(b);
+}
+
+// DPP controls
+constexpr int kDppQuadSwap1 = 0xB1;    // quad_perm [1,0,3,2]
+constexpr int kDppQuadSwap2 = 0x4E;    // quad_perm [2,3,0,1]
+constexpr int kDppHalfMirror = 0x141;  // row_half_mirror
+constexpr int kDppMirror = 0x140;      // row_mirror
+constexpr int kDppRowRor4 = 0x124;     // row_ror:4
+constexpr int kDppRowRor8 = 0x128;     // row_ror:8
+
+template <int CTRL>
+__device__ __forceinline__ double dpp_d(double v) {
+    const unsigned long long u = __double_as_longlong(v);
+    const uint32_t lo = __builtin_amdgcn_mov_dpp((int)(uint32_t)u, CTRL, 0xf, 0xf, false);
+    const uint32_t hi = __builtin_amdgcn_mov_dpp((int)(uint32_t)(u >> 32), CTRL, 0xf, 0xf, false);
+    return __longlong_as_double((long long)(((unsigned long long)hi << 32) | lo));
+}
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp_u(uint32_t v) {
+    return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, CTRL, 0xf, 0xf, false);
+}
+
+// Sum of v over aligned groups of N lanes (N = 1, 2, 4, 8, 16, 32), result in every lane of the group.
+template <int N>
+__device__ __forceinline__ double group_sum_d(double v) {
+    if constexpr (N >= 2) v += dpp_d<kDppQuadSwap1>(v);
+    if constexpr (N >= 4) v += dpp_d<kDppQuadSwap2>(v);
+    if constexpr (N >= 8) v += dpp_d<kDppHalfMirror>(v);
+    if constexpr (N >= 16) v += dpp_d<kDppMirror>(v);
+    if constexpr (N >= 32) {
+        const unsigned long long u = __double_as_longlong(v);
+        uint32_t l0, l1, h0, h1;
+        pair16((uint32_t)u, l0, l1);
+        pair16((uint32_t)(u >> 32), h0, h1);
+        v = __longlong_as_double((long long)(((unsigned long long)h0 << 32) | l0)) +
+            __longlong_as_double((long long)(((unsigned long long)h1 << 32) | l1));
+    }
+    return v;
+}
+
+// max / sum over all 64 lanes of a wavefront, result in every lane
+__device__ __forceinline__ float wave_max(float v) {
+    v = fmaxf(v, __uint_as_float(dpp_u<kDppQuadSwap1>(__float_as_uint(v))));
+    v = fmaxf(v, __uint_as_float(dpp_u<kDppQuadSwap2>(__float_as_uint(v))));
+    v = fmaxf(v, __uint_as_float(dpp_u<kDppHalfMirror>(__float_as_uint(v))));
+    v = fmaxf(v, __uint_as_float(dpp_u<kDppMirror>(__float_as_uint(v))));
+    return max_xor32(max_xor16(v));
+}
+__device__ __forceinline__ float wave_sum(float v) {
+    v += __uint_as_float(dpp_u<kDppQuadSwap1>(__float_as_uint(v)));
+    v += __uint_as_float(dpp_u<kDppQuadSwap2>(__float_as_uint(v)));
+    v += __uint_as_float(dpp_u<kDppHalfMirror>(__float_as_uint(v)));
+    v += __uint_as_float(dpp_u<kDppMirror>(__float_as_uint(v)));
+    return sum_xor32(sum_xor16(v));
+}
+
+// Inclusive prefix sum over the 64 lanes of a wavefront.
+__device__ __forceinline__ uint32_t wave_inclusive_scan(uint32_t v) {
+    v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x111, 0xf, 0xf, false);   // row_shr:1
+    v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x112, 0xf, 0xf, false);   // row_shr:2
+    v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x114, 0xf, 0xf, false);   // row_shr:4
+    v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x118, 0xf, 0xf, false);   // row_shr:8
+    v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x142, 0xa, 0xf, false);   // row_bcast:15
+    v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x143, 0xc, 0xf, false);   // row_bcast:31
+    return v;
+}
+
+// Bitwise and / or of a 64-bit value over the wavefront (every lane gets it).
+__device__ __forceinline__ void wave_and_or(unsigned long long &a, unsigned long long &o) {
+    uint32_t al = (uint32_t)a, ah = (uint32_t)(a >> 32), ol = (uint32_t)o, oh = (uint32_t)(o >> 32);
+#define LSA_AO_STEP(C)                                                                  \
+    al &= dpp_u<C>(al); ah &= dpp_u<C>(ah); ol |= dpp_u<C>(ol); oh |= dpp_u<C>(oh);
+    LSA_AO_STEP(kDppQuadSwap1)
+    LSA_AO_STEP(kDppQuadSwap2)
+    LSA_AO_STEP(kDppHalfMirror)
+    LSA_AO_STEP(kDppMirror)
+#undef LSA_AO_STEP
+    uint32_t x, y;
+    pair16(al, x, y); al = x & y;
+    pair16(ah, x, y); ah = x & y;
+    pair16(ol, x, y); ol = x | y;
+    pair16(oh, x, y); oh = x | y;
+    pair32(al, x, y); al = x & y;
+    pair32(ah, x, y); ah = x & y;
+    pair32(ol, x, y); ol = x | y;
+    pair32(oh, x, y); oh = x | y;
+    a = ((unsigned long long)ah << 32) | al;
+    o = ((unsigned long long)oh << 32) | ol;
+}
+
+// ----------------------------------------------------------------------------
 // launch arguments
 // ----------------------------------------------------------------------------
 

@@ -222,7 +222,7 @@ __global__ __launch_bounds__(512, 2) void prefill_bf16_kernel(PrefillArgs p) {
         for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
             for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kt][r]);
-        mx = fmaxf(mx, __shfl_xor(mx, 32, kWave));
+        mx = max_xor32(mx);
         const float m_new = fmaxf(m_run, mx);
         if (__ballot(m_new > m_run) != 0) {            // rescale only when some column's max moved
             const float alpha = exp2_fast((m_run - m_new) * sc);
@@ -290,7 +290,7 @@ __global__ __launch_bounds__(512, 2) void prefill_bf16_kernel(PrefillArgs p) {
     }
     if (!head_ok) return;
     // ---- normalise and store: lane holds query q0 + col, channels 32*dt + 8*(r/4) + 4*lg + r%4
-    const float lt = l_run + __shfl_xor(l_run, 32, kWave);
+    const float lt = sum_xor32(l_run);
     const float inv = 1.f / lt;
     const int row = q0 + col;
     if (row >= T) return;

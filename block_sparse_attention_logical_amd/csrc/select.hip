@@ -40,8 +40,6 @@ constexpr int kScoreThreads = 256;
 constexpr int kScoreMaxIter = 8;           // logical pages per lane group and workgroup
 constexpr int kMaxLogicalPerBlock = 1024;  // LDS slots for logical scores
 
-__device__ __forceinline__ double shfl_xor_d(double v, int m) { return __shfl_xor(v, m, kWave); }
-
 // Qp / Qn of this lane's channels, fp64.
 template <int C>
 __device__ __forceinline__ void load_q_pos_neg(const ScoreArgs &a, int b, int kv, int ch0,
@@ -78,6 +76,82 @@ __device__ __forceinline__ void load_q_pos_neg(const ScoreArgs &a, int b, int kv
     }
 }
 
+// min / max of this lane's C channels over the current logical page's rows
+// held by the wavefront (lane group q of the LPP groups takes rows q, q + LPP,
+// ...), combined over the groups so every lane ends with all rows.  Float
+// channels for f32 / bf16 pools, 4-bit codes (as floats) for int4 pools.
+template <int KV_DT, int D, int C, int LPL, int LPP>
+__device__ __forceinline__ void current_page_minmax(const ScoreArgs &a, size_t krow0, int rows, int q, int ch0,
+                                                    float (&kmin)[C], float (&kmax)[C]) {
+#pragma unroll
+    for (int c = 0; c < C; ++c) { kmin[c] = __builtin_inff(); kmax[c] = -__builtin_inff(); }
+    constexpr int RB = 4;                       // rows per lane and batch, loaded together
+    for (int r0 = 0; r0 < rows; r0 += RB * LPP) {
+        if constexpr (KV_DT == LSA_INT4) {
+            uint2 u[RB];
+#pragma unroll
+            for (int i = 0; i < RB; ++i) {
+                const int rr = r0 + q + i * LPP;
+                u[i] = rr < rows ? *reinterpret_cast<const uint2 *>(static_cast<const uint8_t *>(a.k) +
+                                                                    (krow0 + rr) * (D / 2) + ch0 / 2)
+                                 : make_uint2(0xFFFFFFFFu, 0xFFFFFFFFu);
+            }
+#pragma unroll
+            for (int i = 0; i < RB; ++i) {
+                if (r0 + q + i * LPP >= rows) continue;
+#pragma unroll
+                for (int c = 0; c < C; ++c) {
+                    const uint32_t byte = ((c < 8 ? u[i].x : u[i].y) >> (8 * ((c / 2) % 4))) & 0xFFu;
+                    const float code = (float)((c & 1) ? (byte >> 4) : (byte & 15u));
+                    kmin[c] = fminf(kmin[c], code);
+                    kmax[c] = fmaxf(kmax[c], code);
+                }
+            }
+        } else {
+            uint4 u[RB];
+#pragma unroll
+            for (int i = 0; i < RB; ++i) {
+                const int rr = r0 + q + i * LPP;
+                u[i] = rr < rows ? *reinterpret_cast<const uint4 *>(static_cast<const char *>(a.k) +
+                                                                    ((krow0 + rr) * D + ch0) * (KV_DT == LSA_F32 ? 4 : 2))
+                                 : make_uint4(0, 0, 0, 0);
+            }
+#pragma unroll
+            for (int i = 0; i < RB; ++i) {
+                if (r0 + q + i * LPP >= rows) continue;
+                const uint32_t w[4] = {u[i].x, u[i].y, u[i].z, u[i].w};
+#pragma unroll
+                for (int c = 0; c < C; ++c) {
+                    float x;
+                    if constexpr (KV_DT == LSA_BF16) x = (c & 1) ? bf16_hi(w[c / 2]) : bf16_lo(w[c / 2]);
+                    else x = __uint_as_float(w[c]);
+                    kmin[c] = fminf(kmin[c], x);
+                    kmax[c] = fmaxf(kmax[c], x);
+                }
+            }
+        }
+    }
+    // combine the lane groups that share this lane's channels (the lanes
+    // with the same lane % LPL): rotations inside a row of 16, then swaps
+#pragma unroll
+    for (int c = 0; c < C; ++c) {
+        if constexpr (LPL <= 4) {
+            kmin[c] = fminf(kmin[c], __uint_as_float(dpp_u<kDppRowRor4>(__float_as_uint(kmin[c]))));
+            kmax[c] = fmaxf(kmax[c], __uint_as_float(dpp_u<kDppRowRor4>(__float_as_uint(kmax[c]))));
+        }
+        if constexpr (LPL <= 8) {
+            kmin[c] = fminf(kmin[c], __uint_as_float(dpp_u<kDppRowRor8>(__float_as_uint(kmin[c]))));
+            kmax[c] = fmaxf(kmax[c], __uint_as_float(dpp_u<kDppRowRor8>(__float_as_uint(kmax[c]))));
+        }
+        if constexpr (LPL <= 16) {
+            kmin[c] = -max_xor16(-kmin[c]);
+            kmax[c] = max_xor16(kmax[c]);
+        }
+        kmin[c] = -max_xor32(-kmin[c]);
+        kmax[c] = max_xor32(kmax[c]);
+    }
+}
+
 // KV_DT: LSA_F32, LSA_BF16 (stats in that type) or LSA_INT4 (code stats).
 template <int KV_DT, int D>
 __global__ __launch_bounds__(kScoreThreads) void score_kernel(ScoreArgs a) {
@@ -85,6 +159,7 @@ __global__ __launch_bounds__(kScoreThreads) void score_kernel(ScoreArgs a) {
     using S = ScoreShape<EB, D>;
     constexpr int C = S::C, LPL = S::LPL, LPP = S::LPP;
     constexpr int GROUPS = (kScoreThreads / kWave) * LPP;   // lane groups per workgroup
+    constexpr int IT = kScoreMaxIter;
     __shared__ double s_log[kMaxLogicalPerBlock];
 
     const int blk = blockIdx.x % a.blocks_per_head;
@@ -93,7 +168,8 @@ __global__ __launch_bounds__(kScoreThreads) void score_kernel(ScoreArgs a) {
     const int b = rest / a.n_ret;
     const int kv = a.ret_heads[r];
     const int lane = threadIdx.x % kWave;
-    const int lg = (threadIdx.x / kWave) * LPP + lane / LPL;    // lane group in the workgroup
+    const int wave = threadIdx.x / kWave;
+    const int lg = wave * LPP + lane / LPL;       // lane group in the workgroup
     const int ch0 = (lane % LPL) * C;
 
     const int g = a.page_size / a.logical_page;
@@ -101,9 +177,9 @@ __global__ __launch_bounds__(kScoreThreads) void score_kernel(ScoreArgs a) {
     const int j0 = m0 * g;
     // page-table entries of this lane group's logical pages, loaded together
     // with seq_lens and q (nothing here waits on another load)
-    int pools[kScoreMaxIter];
+    int pools[IT];
 #pragma unroll
-    for (int it = 0; it < kScoreMaxIter; ++it) {
+    for (int it = 0; it < IT; ++it) {
         const int m = (j0 + lg + it * GROUPS) / g;
         pools[it] = m < a.max_pages ? a.page_table[(size_t)b * a.max_pages + m] : 0;
     }
@@ -115,33 +191,25 @@ __global__ __launch_bounds__(kScoreThreads) void score_kernel(ScoreArgs a) {
     const int m1 = min(m0 + a.pages_per_block, n_pages);
     const int nlog = (L + a.logical_page - 1) / a.logical_page;
     const int j1 = min(m1 * g, nlog);
-    const int j_cur = (L - 1) / a.logical_page;
-
-    double qsum = 0.0;                      // int4 only: sum over all channels of Qp + Qn
-    if constexpr (KV_DT == LSA_INT4) {
-#pragma unroll
-        for (int c = 0; c < C; ++c) qsum += qp[c] + qn[c];
-#pragma unroll
-        for (int off = 1; off < LPL; off <<= 1) qsum += shfl_xor_d(qsum, off);
-    }
+    const int j_cur = (L - 1) / a.logical_page;   // the logical page that holds the current token
     const size_t head_stride = (size_t)g * (KV_DT == LSA_INT4 ? D : 2 * D);
-    const int NP = a.page_size;
 
-    // every lane group walks logical pages j0 + lg, j0 + lg + GROUPS, ...; the
-    // trip count is uniform so the lane-group reductions see whole wavefronts.
-    // The page-table entries of all iterations are loaded first, then every
-    // iteration's statistics, so no load waits on another.
-    const int n_iter = (j1 - j0 + GROUPS - 1) / GROUPS;
-    uint4 st_lo[kScoreMaxIter], st_hi[kScoreMaxIter];
+    // every statistics load of the workgroup is issued before any product
+    uint4 st_lo[IT], st_hi[IT];
+    uint32_t szw[IT];                             // int4: the page's fp16 scale | zero << 16
 #pragma unroll
-    for (int it = 0; it < kScoreMaxIter; ++it) {
+    for (int it = 0; it < IT; ++it) {
         const int j = j0 + lg + it * GROUPS;
-        if (it < n_iter && j < j1 && j != j_cur) {
+        st_lo[it] = make_uint4(0, 0, 0, 0);
+        st_hi[it] = make_uint4(0, 0, 0, 0);
+        szw[it] = 0;
+        if (j < j1 && j != j_cur) {
             const size_t hp = (size_t)pools[it] * a.num_kv_heads + kv;
             const int jl = j % g;
             if constexpr (KV_DT == LSA_INT4) {
                 st_lo[it] = *reinterpret_cast<const uint4 *>(static_cast<const uint8_t *>(a.stats) + hp * head_stride +
                                                              (size_t)jl * D + ch0);
+                szw[it] = *reinterpret_cast<const uint32_t *>(a.k_sz + hp * 2);
             } else {
                 const char *st = static_cast<const char *>(a.stats) + (hp * head_stride + (size_t)jl * 2 * D + ch0) * EB;
                 st_lo[it] = *reinterpret_cast<const uint4 *>(st);
@@ -149,110 +217,78 @@ __global__ __launch_bounds__(kScoreThreads) void score_kernel(ScoreArgs a) {
             }
         }
     }
+
+    double qsum = 0.0;                            // int4 only: sum over all channels of Qp + Qn
+    if constexpr (KV_DT == LSA_INT4) {
 #pragma unroll
-    for (int it = 0; it < kScoreMaxIter; ++it) {
-        if (it >= n_iter) break;
-        const int j = j0 + lg + it * GROUPS;
-        const bool ok = j < j1;
-        const int jl = j % g;
-        double acc = 0.0;
-        double s_scale = 1.0, s_zero = 0.0;
-        if (ok) {
-            const size_t hp = (size_t)pools[it] * a.num_kv_heads + kv;
-            if constexpr (KV_DT == LSA_INT4) {
-                const uint32_t sz = *reinterpret_cast<const uint32_t *>(a.k_sz + hp * 2);
-                s_scale = (double)fp16_bits_to_f32(uint16_t(sz));
-                s_zero = (double)fp16_bits_to_f32(uint16_t(sz >> 16));
+        for (int c = 0; c < C; ++c) qsum += qp[c] + qn[c];
+        qsum = group_sum_d<LPL>(qsum);
+    }
+
+    // the current logical page, scored from its keys by one whole wavefront
+    if (j_cur >= j0 && j_cur < j1 && wave == ((j_cur - j0) % GROUPS) / LPP) {
+        const int m = j_cur / g;
+        const int pool = a.page_table[(size_t)b * a.max_pages + m];
+        const size_t hp = (size_t)pool * a.num_kv_heads + kv;
+        const size_t krow0 = hp * a.page_size + (size_t)(j_cur % g) * a.logical_page;
+        float kmin[C], kmax[C];
+        current_page_minmax<KV_DT, D, C, LPL, LPP>(a, krow0, L - j_cur * a.logical_page, lane / LPL, ch0, kmin, kmax);
+        double c0 = 0.0, c1 = 0.0;
+#pragma unroll
+        for (int c = 0; c < C; ++c) {
+            c0 = fma(qp[c], (double)kmax[c], c0);
+            c1 = fma(qn[c], (double)kmin[c], c1);
+        }
+        double sj = group_sum_d<LPL>(c0 + c1);
+        if constexpr (KV_DT == LSA_INT4) {
+            const uint32_t sz = *reinterpret_cast<const uint32_t *>(a.k_sz + hp * 2);
+            sj = (double)fp16_bits_to_f32(uint16_t(sz)) * (sj - (double)fp16_bits_to_f32(uint16_t(sz >> 16)) * qsum);
+        }
+        if (lane == 0) s_log[j_cur - j0] = sj;
+    }
+
+    // S^j of every other logical page: one independent product chain per slot
+    double acc[IT];
+#pragma unroll
+    for (int it = 0; it < IT; ++it) {
+        double c0 = 0.0, c1 = 0.0;
+        if constexpr (KV_DT == LSA_INT4) {
+            const uint32_t wd[4] = {st_lo[it].x, st_lo[it].y, st_lo[it].z, st_lo[it].w};
+#pragma unroll
+            for (int c = 0; c < C; ++c) {
+                const uint32_t byte = (wd[c / 4] >> (8 * (c % 4))) & 0xFFu;
+                c0 = fma(qp[c], (double)(byte >> 4), c0);
+                c1 = fma(qn[c], (double)(byte & 15u), c1);
             }
-            const bool cur = j == j_cur;
-            const int rows = L - j * a.logical_page;         // valid rows of the current logical page
-            const size_t krow0 = hp * NP + (size_t)jl * a.logical_page;
-            if constexpr (KV_DT == LSA_INT4) {
-                uint32_t cmin[C], cmax[C];
-                if (cur) {
-                    // min / max of the codes of tokens j*N_L .. t, this lane's 16 channels
+        } else {
+            const uint32_t wl[4] = {st_lo[it].x, st_lo[it].y, st_lo[it].z, st_lo[it].w};
+            const uint32_t wh[4] = {st_hi[it].x, st_hi[it].y, st_hi[it].z, st_hi[it].w};
 #pragma unroll
-                    for (int c = 0; c < C; ++c) { cmin[c] = 15; cmax[c] = 0; }
-                    const uint8_t *kp = static_cast<const uint8_t *>(a.k) + krow0 * (D / 2) + ch0 / 2;
-                    for (int rr = 0; rr < rows; ++rr) {
-                        const uint2 u = *reinterpret_cast<const uint2 *>(kp + (size_t)rr * (D / 2));
-#pragma unroll
-                        for (int c = 0; c < C; ++c) {
-                            const uint32_t byte = ((c < 8 ? u.x : u.y) >> (8 * ((c / 2) % 4))) & 0xFFu;
-                            const uint32_t code = (c & 1) ? (byte >> 4) : (byte & 15u);
-                            cmin[c] = min(cmin[c], code);
-                            cmax[c] = max(cmax[c], code);
-                        }
-                    }
+            for (int c = 0; c < C; ++c) {
+                float kmin, kmax;
+                if constexpr (KV_DT == LSA_BF16) {
+                    kmin = (c & 1) ? bf16_hi(wl[c / 2]) : bf16_lo(wl[c / 2]);
+                    kmax = (c & 1) ? bf16_hi(wh[c / 2]) : bf16_lo(wh[c / 2]);
                 } else {
-                    const uint32_t wd[4] = {st_lo[it].x, st_lo[it].y, st_lo[it].z, st_lo[it].w};
-#pragma unroll
-                    for (int c = 0; c < C; ++c) {
-                        const uint32_t byte = (wd[c / 4] >> (8 * (c % 4))) & 0xFFu;
-                        cmin[c] = byte & 15u;
-                        cmax[c] = byte >> 4;
-                    }
+                    kmin = __uint_as_float(wl[c]);
+                    kmax = __uint_as_float(wh[c]);
                 }
-#pragma unroll
-                for (int c = 0; c < C; ++c) {
-                    acc = fma(qp[c], (double)cmax[c], acc);
-                    acc = fma(qn[c], (double)cmin[c], acc);
-                }
-            } else {
-                float kmin[C], kmax[C];
-                if (cur) {
-#pragma unroll
-                    for (int c = 0; c < C; ++c) { kmin[c] = __builtin_inff(); kmax[c] = -__builtin_inff(); }
-                    for (int rr = 0; rr < rows; ++rr) {
-                        if constexpr (KV_DT == LSA_BF16) {
-                            const uint4 u = *reinterpret_cast<const uint4 *>(
-                                static_cast<const uint16_t *>(a.k) + (krow0 + rr) * D + ch0);
-                            const uint32_t w[4] = {u.x, u.y, u.z, u.w};
-#pragma unroll
-                            for (int c = 0; c < C; ++c) {
-                                const float x = (c & 1) ? bf16_hi(w[c / 2]) : bf16_lo(w[c / 2]);
-                                kmin[c] = fminf(kmin[c], x);
-                                kmax[c] = fmaxf(kmax[c], x);
-                            }
-                        } else {
-                            const float4 u = *reinterpret_cast<const float4 *>(
-                                static_cast<const float *>(a.k) + (krow0 + rr) * D + ch0);
-                            const float w[4] = {u.x, u.y, u.z, u.w};
-#pragma unroll
-                            for (int c = 0; c < C; ++c) {
-                                kmin[c] = fminf(kmin[c], w[c]);
-                                kmax[c] = fmaxf(kmax[c], w[c]);
-                            }
-                        }
-                    }
-                } else if constexpr (KV_DT == LSA_BF16) {
-                    const uint32_t wl[4] = {st_lo[it].x, st_lo[it].y, st_lo[it].z, st_lo[it].w};
-                    const uint32_t wh[4] = {st_hi[it].x, st_hi[it].y, st_hi[it].z, st_hi[it].w};
-#pragma unroll
-                    for (int c = 0; c < C; ++c) {
-                        kmin[c] = (c & 1) ? bf16_hi(wl[c / 2]) : bf16_lo(wl[c / 2]);
-                        kmax[c] = (c & 1) ? bf16_hi(wh[c / 2]) : bf16_lo(wh[c / 2]);
-                    }
-                } else {
-                    const float vl[4] = {__uint_as_float(st_lo[it].x), __uint_as_float(st_lo[it].y),
-                                         __uint_as_float(st_lo[it].z), __uint_as_float(st_lo[it].w)};
-                    const float vh[4] = {__uint_as_float(st_hi[it].x), __uint_as_float(st_hi[it].y),
-                                         __uint_as_float(st_hi[it].z), __uint_as_float(st_hi[it].w)};
-#pragma unroll
-                    for (int c = 0; c < C; ++c) { kmin[c] = vl[c]; kmax[c] = vh[c]; }
-                }
-#pragma unroll
-                for (int c = 0; c < C; ++c) {
-                    acc = fma(qp[c], (double)kmax[c], acc);
-                    acc = fma(qn[c], (double)kmin[c], acc);
-                }
+                c0 = fma(qp[c], (double)kmax, c0);
+                c1 = fma(qn[c], (double)kmin, c1);
             }
         }
+        acc[it] = c0 + c1;
+    }
 #pragma unroll
-        for (int off = 1; off < LPL; off <<= 1) acc += shfl_xor_d(acc, off);
-        if (ok && lane % LPL == 0) {
-            double sj = acc;
-            if constexpr (KV_DT == LSA_INT4) sj = s_scale * (acc - s_zero * qsum);
+    for (int it = 0; it < IT; ++it) acc[it] = group_sum_d<LPL>(acc[it]);
+#pragma unroll
+    for (int it = 0; it < IT; ++it) {
+        const int j = j0 + lg + it * GROUPS;
+        if (j < j1 && j != j_cur && lane % LPL == 0) {
+            double sj = acc[it];
+            if constexpr (KV_DT == LSA_INT4)
+                sj = (double)fp16_bits_to_f32(uint16_t(szw[it])) *
+                     (sj - (double)fp16_bits_to_f32(uint16_t(szw[it] >> 16)) * qsum);
             s_log[j - j0] = sj;
         }
     }
@@ -281,12 +317,7 @@ __device__ __forceinline__ unsigned long long order_key(double x) {
 // exclusive prefix sum over the workgroup of a 32-bit packed counter
 __device__ __forceinline__ uint32_t block_exclusive_scan(uint32_t v, uint32_t *wave_tot) {
     const int lane = threadIdx.x % kWave, wave = threadIdx.x / kWave;
-    uint32_t incl = v;
-#pragma unroll
-    for (int off = 1; off < kWave; off <<= 1) {
-        const uint32_t n = __shfl_up(incl, off, kWave);
-        if (lane >= off) incl += n;
-    }
+    const uint32_t incl = wave_inclusive_scan(v);
     if (lane == kWave - 1) wave_tot[wave] = incl;
     __syncthreads();
     uint32_t add = 0;
@@ -334,11 +365,7 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(TopkArgs a) {
 #pragma unroll
     for (int e = 0; e < kTopkPerThread; ++e)
         if (e < cnt) { k_and &= key[e]; k_or |= key[e]; }
-#pragma unroll
-    for (int off = 1; off < kWave; off <<= 1) {
-        k_and &= __shfl_xor(k_and, off, kWave);
-        k_or |= __shfl_xor(k_or, off, kWave);
-    }
+    wave_and_or(k_and, k_or);
     if (tid % kWave == 0) { sh_and[tid / kWave] = k_and; sh_or[tid / kWave] = k_or; }
     __syncthreads();
     k_and = ~0ull; k_or = 0ull;
@@ -363,13 +390,9 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(TopkArgs a) {
             // lane l owns bins 4l..4l+3; suffix sums from the top bin down
             const uint32_t c0 = hist[4 * tid], c1 = hist[4 * tid + 1], c2 = hist[4 * tid + 2], c3 = hist[4 * tid + 3];
             const uint32_t mine = c0 + c1 + c2 + c3;
-            uint32_t suf = mine;                  // inclusive suffix sum over lanes >= tid
-#pragma unroll
-            for (int off = 1; off < kWave; off <<= 1) {
-                const uint32_t nb = __shfl_down(suf, off, kWave);
-                if (tid + off < kWave) suf += nb;
-            }
-            uint32_t above = suf - mine;          // elements in bins of higher lanes
+            const uint32_t incl = wave_inclusive_scan(mine);
+            const uint32_t total = (uint32_t)__builtin_amdgcn_readlane((int)incl, kWave - 1);
+            uint32_t above = total - incl;        // elements in bins of higher lanes
             const uint32_t cs[4] = {c0, c1, c2, c3};
             for (int qd = 3; qd >= 0; --qd) {
                 if (above < need && above + cs[qd] >= need) {
