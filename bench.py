@@ -346,7 +346,7 @@ def main():
         "decode_hbm_gbps": round(dec["step_bytes"] / (dec["ms_per_step"] / 1e3) / 1e9, 1),
         "decode_step_bytes": int(dec["step_bytes"]),
         "roofline": {
-            "kernel": "lsa_sparse_decode_attn: decode_bf16_kernel + combine_kernel",
+            "kernel": "lsa_sparse_decode_attn: decode_mfma_kernel (split-KV pass with the merge in its last workgroup per head)",
             "bound": "hbm", "achieved": round(achieved / 1e9, 1), "peak": PEAK_HBM / 1e9, "unit": "GB/s",
             "frac": round(achieved / PEAK_HBM, 4),
             "traffic": dec["traffic"],

@@ -105,6 +105,9 @@ struct DecodeGeom {
     int K, chunks_ret, chunks_str, chunks_max, rec_floats;
 };
 
+// arrival counters at the start of the decode workspace: one int32 per (sequence, KV head)
+size_t decode_counter_bytes(int batch, int num_kv_heads) { return align_up((size_t)batch * num_kv_heads * 4); }
+
 DecodeGeom decode_geometry(const lsa_kv *kv, const lsa_heads *hd, int token_budget) {
     DecodeGeom g;
     g.K = token_budget / kv->page_size;
@@ -261,7 +264,8 @@ lsa_status lsa_decode_workspace(const lsa_kv *kv, const lsa_seqs *seqs, const ls
         return fail(LSA_ERR_INVALID_ARG, "token_budget %d is not a positive multiple of page_size %d", token_budget,
                     kv->page_size);
     const DecodeGeom g = decode_geometry(kv, heads, token_budget);
-    *bytes = align_up((size_t)seqs->batch * kv->num_kv_heads * g.chunks_max * g.rec_floats * sizeof(float));
+    *bytes = decode_counter_bytes(seqs->batch, kv->num_kv_heads) +
+             align_up((size_t)seqs->batch * kv->num_kv_heads * g.chunks_max * g.rec_floats * sizeof(float));
     return ok();
 }
 
@@ -302,7 +306,9 @@ lsa_status lsa_sparse_decode_attn(const void *q, int32_t q_dtype, const lsa_kv *
     a.page_table = seqs->page_table;
     a.seq_lens = seqs->seq_lens;
     a.selected = selected;
-    a.part = static_cast<float *>(workspace);
+    a.counters = static_cast<int32_t *>(workspace);
+    a.part = reinterpret_cast<float *>(static_cast<char *>(workspace) +
+                                       decode_counter_bytes(seqs->batch, kv->num_kv_heads));
     a.stats = stats;
     a.logical_page = kv->logical_page;
     a.batch = seqs->batch;
@@ -323,9 +329,7 @@ lsa_status lsa_sparse_decode_attn(const void *q, int32_t q_dtype, const lsa_kv *
     const float scale = softmax_scale > 0.f ? softmax_scale : 1.f / std::sqrt((float)kv->head_dim);
     a.scale_log2 = scale * 1.4426950408889634f;
     for (int i = 0; i < kv->num_kv_heads; ++i) a.kind[i] = heads->head_kind[i];
-    if (lsa_status s = from_hip(launch_decode(a, q_dtype, kv->kv_dtype, (hipStream_t)stream), "decode launch"))
-        return s;
-    return from_hip(launch_combine(a, q_dtype, (hipStream_t)stream), "decode combine launch");
+    return from_hip(launch_decode(a, q_dtype, kv->kv_dtype, (hipStream_t)stream), "decode launch");
 }
 
 lsa_status lsa_sparse_prefill_attn(const void *q, int32_t q_dtype, const lsa_kv *kv, const int32_t *page_table,

@@ -9,11 +9,15 @@
 // head) is cut into chunks of 4 * pages_per_wave pages; one workgroup of four
 // wavefronts takes a chunk, each wavefront streams its pages with an online
 // softmax, the four states are merged in LDS and one partial record
-// (max, sum, unnormalised output) is written per chunk.  A second, small
-// kernel merges the records of each (sequence, KV head) in chunk order, so
-// results are deterministic.  The kernel boundary orders the records; a
-// device-scope fence instead (L2 writeback + invalidate per wave) measured
-// slower than the extra launch.  Every K/V page read serves all G query heads.
+// (max, sum, unnormalised output) is written per chunk.  The last workgroup of
+// a (sequence, KV head) to finish merges every record in chunk order (so the
+// result does not depend on arrival order) and writes the output.  The
+// hand-off avoids a device-scope fence (an L2 writeback on this part): the
+// records are written and read with agent-scope stores and loads, which go to
+// the coherence point past the per-XCD L2s, and a workgroup counts its arrival
+// only after its record stores have completed (s_waitcnt vmcnt(0)).  The
+// arrival counter is an agent-scope atomic; the last arrival resets it to
+// zero.  Every K/V page read serves all G query heads.
 //
 // MFMA path (bf16 and int4 pools).  Both contractions run on
 // v_mfma_f32_16x16x32_bf16 straight from registers.  QK^T is computed
@@ -172,33 +176,114 @@ __device__ __forceinline__ void refresh_current_stats(const DecodeArgs &a, const
     }
 }
 
-// Merge the per-wave softmax states held in LDS and write this chunk's record.
-// LDS layout per wave: m[16], l[16], o[16][D].
+__device__ __forceinline__ void store_agent(float *p, float v) {
+    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void store_agent2(float *p, float x, float y) {
+    const unsigned long long u = (unsigned long long)__float_as_uint(x) | ((unsigned long long)__float_as_uint(y) << 32);
+    __hip_atomic_store(reinterpret_cast<unsigned long long *>(p), u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float load_agent(const float *p) {
+    return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float2 load_agent2(const float *p) {
+    const unsigned long long u =
+        __hip_atomic_load(reinterpret_cast<const unsigned long long *>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    return make_float2(__uint_as_float(uint32_t(u)), __uint_as_float(uint32_t(u >> 32)));
+}
+
+// Merge the per-wave softmax states held in LDS and write this chunk's record
+// (m[16], l[16], o[G][D]) with agent-scope stores.  LDS layout per wave:
+// m[16], l[16], o[16][D].
 __device__ __forceinline__ void merge_waves_and_store(const DecodeArgs &a, const WorkItem &w,
                                                       const float *lds, int D) {
     const int G = a.group;
     const int wave_stride = 32 + 16 * D;
     const size_t rec_size = 32 + (size_t)G * D;
     float *rec = a.part + (((size_t)w.b * a.num_kv_heads + w.kv) * a.chunks_max + w.chunk) * rec_size;
-    for (int idx = threadIdx.x; idx < G * D; idx += blockDim.x) {
-        const int h = idx / D, d = idx % D;
+    for (int pi = threadIdx.x; pi < G * D / 2; pi += blockDim.x) {
+        const int h = (2 * pi) / D, d = 2 * pi - h * D;
         float M = -__builtin_inff();
 #pragma unroll
         for (int wv = 0; wv < 4; ++wv) M = fmaxf(M, lds[wv * wave_stride + h]);
-        float acc = 0.f, lsum = 0.f;
+        float acc0 = 0.f, acc1 = 0.f, lsum = 0.f;
         if (M != -__builtin_inff()) {
 #pragma unroll
             for (int wv = 0; wv < 4; ++wv) {
                 const float mw = lds[wv * wave_stride + h];
                 const float wt = mw == -__builtin_inff() ? 0.f : exp2_fast(mw - M);
-                acc += wt * lds[wv * wave_stride + 32 + h * D + d];
+                acc0 += wt * lds[wv * wave_stride + 32 + h * D + d];
+                acc1 += wt * lds[wv * wave_stride + 32 + h * D + d + 1];
                 lsum += wt * lds[wv * wave_stride + 16 + h];
             }
         }
-        rec[32 + idx] = acc;
+        store_agent2(rec + 32 + 2 * pi, acc0, acc1);
         if (d == 0) {
-            rec[h] = M;
-            rec[16 + h] = lsum;
+            store_agent(rec + h, M);
+            store_agent(rec + 16 + h, lsum);
+        }
+    }
+}
+
+// Count this chunk's arrival; the last workgroup of the (sequence, KV head)
+// merges the records of all its chunks, in chunk order, into out.
+template <typename OutT>
+__device__ __forceinline__ void finish_head(const DecodeArgs &a, const WorkItem &w, int D) {
+    __shared__ int s_last;
+    // this wavefront's record stores have reached the coherence point
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+    const int nchunks = w.streaming ? a.chunks_str : a.chunks_ret;
+    if (threadIdx.x == 0) {
+        int32_t *cnt = a.counters + (size_t)w.b * a.num_kv_heads + w.kv;
+        const int old = __hip_atomic_fetch_add(cnt, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        const int last = old == nchunks - 1;
+        if (last) __hip_atomic_store(cnt, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        s_last = last;
+    }
+    __syncthreads();
+    if (!s_last) return;
+
+    constexpr int CB = 16;                 // chunks whose records are loaded in one batch
+    const int G = a.group;
+    const size_t rec_size = 32 + (size_t)G * D;
+    const float *rec0 = a.part + ((size_t)w.b * a.num_kv_heads + w.kv) * a.chunks_max * rec_size;
+    for (int pi = threadIdx.x; pi < G * D / 2; pi += blockDim.x) {
+        const int hh = (2 * pi) / D, d = 2 * pi - hh * D;
+        float M = -__builtin_inff(), acc0 = 0.f, acc1 = 0.f, L = 0.f;
+        for (int c0 = 0; c0 < nchunks; c0 += CB) {
+            float mv[CB], lv[CB];
+            float2 ov[CB];
+#pragma unroll
+            for (int c = 0; c < CB; ++c) {
+                const float *rec = rec0 + (size_t)(c0 + c) * rec_size;
+                const bool in = c0 + c < nchunks;
+                mv[c] = in ? load_agent(rec + hh) : -__builtin_inff();
+                lv[c] = in ? load_agent(rec + 16 + hh) : 0.f;
+                ov[c] = in ? load_agent2(rec + 32 + 2 * pi) : make_float2(0.f, 0.f);
+            }
+            float Mb = M;
+#pragma unroll
+            for (int c = 0; c < CB; ++c) Mb = fmaxf(Mb, mv[c]);
+            const float sc = M == -__builtin_inff() ? 0.f : exp2_fast(M - Mb);
+            acc0 *= sc;
+            acc1 *= sc;
+            L *= sc;
+#pragma unroll
+            for (int c = 0; c < CB; ++c) {
+                const float e = mv[c] == -__builtin_inff() ? 0.f : exp2_fast(mv[c] - Mb);
+                L += e * lv[c];
+                acc0 += e * ov[c].x;
+                acc1 += e * ov[c].y;
+            }
+            M = Mb;
+        }
+        const size_t o = ((size_t)w.b * a.num_q_heads + (size_t)w.kv * G + hh) * D + d;
+        if constexpr (sizeof(OutT) == 2) {
+            static_cast<uint32_t *>(a.out)[o / 2] =
+                uint32_t(f32_to_bf16_rne(acc0 / L)) | (uint32_t(f32_to_bf16_rne(acc1 / L)) << 16);
+        } else {
+            *reinterpret_cast<float2 *>(static_cast<float *>(a.out) + o) = make_float2(acc0 / L, acc1 / L);
         }
     }
 }
@@ -424,6 +509,7 @@ __global__ __launch_bounds__(256, 3) void decode_mfma_kernel(DecodeArgs a) {
     if (a.stats && !w.streaming && w.chunk == 0 && wave == 0) refresh_current_stats(a, w, KVT);
     __syncthreads();
     merge_waves_and_store(a, w, lds, D);
+    finish_head<uint16_t>(a, w, D);
 }
 
 // ---------------------------------------------------------------------------
@@ -536,54 +622,7 @@ __global__ __launch_bounds__(256) void decode_f32_kernel(DecodeArgs a) {
     if (a.stats && !w.streaming && w.chunk == 0 && wave == 0) refresh_current_stats(a, w, LSA_F32);
     __syncthreads();
     merge_waves_and_store(a, w, lds, D);
-}
-
-// ---------------------------------------------------------------------------
-// split-KV merge: one workgroup per (sequence, query head), one thread per
-// output channel.  Each thread loads the records of up to 32 chunks in one
-// batch (one memory round trip), forms the chunk weights of its head itself
-// (no barrier) and sums its channel over the chunks in chunk order
-// (deterministic).
-// ---------------------------------------------------------------------------
-template <typename OutT>
-__global__ __launch_bounds__(128) void combine_kernel(DecodeArgs a) {
-    constexpr int CB = 32;                 // chunks whose records are loaded in one batch
-    const int b = blockIdx.x / a.num_q_heads, hq = blockIdx.x % a.num_q_heads;
-    const int G = a.group, D = a.head_dim;
-    const int kv = hq / G, hh = hq % G;
-    const int nchunks = a.kind[kv] ? a.chunks_str : a.chunks_ret;
-    const size_t rec_size = 32 + (size_t)G * D;
-    const float *rec0 = a.part + ((size_t)b * a.num_kv_heads + kv) * a.chunks_max * rec_size;
-    for (int d = threadIdx.x; d < D; d += blockDim.x) {
-        float M = -__builtin_inff(), acc = 0.f, L = 0.f;
-        for (int c0 = 0; c0 < nchunks; c0 += CB) {
-            float mv[CB], lv[CB], ov[CB];
-#pragma unroll
-            for (int c = 0; c < CB; ++c) {
-                const bool in = c0 + c < nchunks;
-                const float *rec = rec0 + (size_t)(c0 + c) * rec_size;
-                mv[c] = in ? rec[hh] : -__builtin_inff();
-                lv[c] = in ? rec[16 + hh] : 0.f;
-                ov[c] = in ? rec[32 + hh * D + d] : 0.f;
-            }
-            float Mb = M;
-#pragma unroll
-            for (int c = 0; c < CB; ++c) Mb = fmaxf(Mb, mv[c]);
-            const float sc = M == -__builtin_inff() ? 0.f : exp2_fast(M - Mb);
-            acc *= sc;
-            L *= sc;
-#pragma unroll
-            for (int c = 0; c < CB; ++c) {
-                const float e = mv[c] == -__builtin_inff() ? 0.f : exp2_fast(mv[c] - Mb);
-                L += e * lv[c];
-                acc += e * ov[c];
-            }
-            M = Mb;
-        }
-        const size_t o = ((size_t)b * a.num_q_heads + hq) * D + d;
-        if constexpr (sizeof(OutT) == 2) static_cast<uint16_t *>(a.out)[o] = f32_to_bf16_rne(acc / L);
-        else static_cast<float *>(a.out)[o] = acc / L;
-    }
+    finish_head<float>(a, w, D);
 }
 
 }  // namespace
@@ -614,14 +653,6 @@ hipError_t launch_decode(const DecodeArgs &a, int q_dtype, int kv_dtype, hipStre
     } else {
         return hipErrorInvalidValue;
     }
-    return hipGetLastError();
-}
-
-hipError_t launch_combine(const DecodeArgs &a, int q_dtype, hipStream_t s) {
-    const long long grid = (long long)a.batch * a.num_q_heads;
-    if (grid == 0) return hipSuccess;
-    if (q_dtype == LSA_BF16) hipLaunchKernelGGL(combine_kernel<uint16_t>, dim3((unsigned)grid), dim3(128), 0, s, a);
-    else hipLaunchKernelGGL(combine_kernel<float>, dim3((unsigned)grid), dim3(128), 0, s, a);
     return hipGetLastError();
 }
 

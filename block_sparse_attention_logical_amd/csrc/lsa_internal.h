@@ -219,6 +219,7 @@ struct DecodeArgs {
     const int32_t *seq_lens;
     const int32_t *selected;
     float *part;                  // partial records
+    int32_t *counters;            // [B][H_kv] arrivals per (sequence, KV head); zero between calls
     void *stats;                  // may be null: refresh the current logical page's statistics
     int32_t batch, max_pages, num_q_heads, num_kv_heads, group, head_dim, page_size, logical_page;
     int32_t sel_k;                // K (row length of selected)
@@ -259,7 +260,6 @@ int score_pages_per_block(int kv_dtype, int head_dim, int page_size, int logical
 int topk_max_pages();
 hipError_t launch_topk(const TopkArgs &a, hipStream_t s);
 hipError_t launch_decode(const DecodeArgs &a, int q_dtype, int kv_dtype, hipStream_t s);
-hipError_t launch_combine(const DecodeArgs &a, int q_dtype, hipStream_t s);
 hipError_t launch_prefill(const PrefillArgs &a, int dtype, hipStream_t s);
 
 }  // namespace lsa

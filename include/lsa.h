@@ -19,8 +19,10 @@
  * Conventions shared by every entry point
  *   - Pointers are DEVICE pointers unless marked [host].
  *   - Every buffer is owned by the caller; the library allocates nothing and
- *     keeps no state between calls.  Workspaces are sized by the *_workspace
- *     queries.
+ *     keeps no state of its own between calls.  Workspaces are sized by the
+ *     *_workspace queries.  The decode workspace holds arrival counters that
+ *     must be zero when a call starts; every completed call leaves them zero,
+ *     so zero-filling the buffer once, before its first use, is enough.
  *   - Calls are asynchronous on `stream` (a hipStream_t; NULL = the default
  *     stream) and never synchronise the host.
  *   - Arguments are validated on the host before any launch.  A validation
@@ -196,10 +198,12 @@ lsa_status lsa_decode_workspace(const lsa_kv *kv, const lsa_seqs *seqs,
  * also refreshes, for every retrieval head, the statistics of the logical page
  * that holds token t (what lsa_build_page_stats does with first_token = t), so
  * a decode step needs no separate statistics launch.
- * workspace: at least lsa_decode_workspace bytes, 256-byte aligned; calls
- * that share a workspace must not overlap in time (same stream, or ordered).
- * Two kernels are launched: the split-KV pass and the merge of its partial
- * results. */
+ * workspace: at least lsa_decode_workspace bytes, 256-byte aligned, zero-filled
+ * before its first use (its leading B * H_kv int32 arrival counters must be
+ * zero when a call starts; each completed call leaves them zero); calls that
+ * share a workspace must not overlap in time (same stream, or ordered).
+ * One kernel is launched: the split-KV pass, whose last workgroup per
+ * (sequence, KV head) merges the partial results in chunk order. */
 lsa_status lsa_sparse_decode_attn(const void *q, int32_t q_dtype, const lsa_kv *kv,
                                   const lsa_seqs *seqs, const lsa_heads *heads,
                                   const int32_t *selected, int32_t token_budget,

@@ -170,6 +170,22 @@ def test_decode_deterministic():
     assert torch.equal(a.view(torch.int16), b.view(torch.int16))
 
 
+@pytest.mark.parametrize("cfg", [1, 2, 5])
+def test_decode_workspace_counters_return_to_zero(cfg):
+    """The split-KV pass counts arrivals per (sequence, KV head) in the head of
+    the workspace; the last arrival merges and resets its counter, so repeated
+    calls on one workspace see zero counters and give identical outputs."""
+    w = W.make_decode(cfg, DEV, batch=3, ctx=[700, 2100, 1500]) if cfg != 1 else W.make_decode(1, DEV)
+    r = Runner(w)
+    n = w.batch * w.num_kv_heads
+    outs = []
+    for _ in range(3):
+        outs.append(r.step(0))
+        assert int(r.ws_dec[:4 * n].view(torch.int32).abs().sum()) == 0
+    for o in outs[1:]:
+        assert torch.equal(o.view(torch.int16), outs[0].view(torch.int16))
+
+
 def test_decode_full_size_cfg2_sampled():
     """Config 2 at full size (B = 8, 64K context, all heads on the GPU); the
     oracle recomputes two retrieval and two streaming KV heads of sequences 0
