@@ -20,8 +20,10 @@
 // thread per physical page takes their max.
 //
 // Top-K.  Scores are mapped to order-preserving 64-bit keys held in
-// registers; a most significant digit first radix select (8-bit digits,
-// histogram in LDS) finds the K-th largest key; equal keys are taken in
+// registers; a most significant digit first radix select finds the K-th
+// largest key.  The passes start at the highest bit in which the keys differ
+// (the bits above it are common to all keys) and take the next 8 bits each;
+// the histogram is in LDS, double-buffered so a pass needs two barriers.  Equal keys are taken in
 // ascending page order (ties to the lower page index); an ordered compaction
 // writes the selected pages in ascending order.
 #include "lsa_internal.h"
@@ -306,7 +308,7 @@ __global__ __launch_bounds__(kScoreThreads) void score_kernel(ScoreArgs a) {
 // top-K: one workgroup of 1024 threads per (sequence, retrieval head)
 // ---------------------------------------------------------------------------
 constexpr int kTopkThreads = 1024;
-constexpr int kTopkPerThread = 16;        // pages per thread: up to 16384 pages
+constexpr int kTopkPerThread = 16;        // pages per thread at most: up to 16384 pages
 
 __device__ __forceinline__ unsigned long long order_key(double x) {
     x = x + 0.0;                                  // -0 -> +0
@@ -325,10 +327,14 @@ __device__ __forceinline__ uint32_t block_exclusive_scan(uint32_t v, uint32_t *w
     return incl - v + add;
 }
 
+// PT: pages per thread, the smallest power of two with kTopkThreads * PT >=
+// max_pages (every per-page loop below is unrolled over PT slots).
+template <int PT>
 __global__ __launch_bounds__(kTopkThreads) void topk_kernel(TopkArgs a) {
-    __shared__ uint32_t hist[256];
-    __shared__ uint32_t sh_digit, sh_above;
+    __shared__ uint32_t hist[2][256];
+    __shared__ uint32_t sh_digit, sh_above, sh_done;
     __shared__ uint32_t wave_tot[kTopkThreads / kWave];
+    __shared__ unsigned long long sh_and[kTopkThreads / kWave], sh_or[kTopkThreads / kWave];
 
     const int r = blockIdx.x % a.n_ret;
     const int b = blockIdx.x / a.n_ret;
@@ -341,11 +347,11 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(TopkArgs a) {
     // thread t owns the contiguous pages [t*seg, t*seg + cnt); the scores are
     // loaded for every row slot at once, together with seq_lens, and the
     // entries past the sequence's last page are dropped afterwards
-    const int seg = (a.max_pages + kTopkThreads - 1) / kTopkThreads;
+    constexpr int seg = PT;
     const int i0 = min(a.max_pages, tid * seg);
-    double pv[kTopkPerThread];
+    double pv[PT];
 #pragma unroll
-    for (int e = 0; e < kTopkPerThread; ++e) pv[e] = e < seg && i0 + e < a.max_pages ? P[i0 + e] : 0.0;
+    for (int e = 0; e < PT; ++e) pv[e] = i0 + e < a.max_pages ? P[i0 + e] : 0.0;
     const int L = a.seq_lens[b];
     const int n = (L + a.page_size - 1) / a.page_size;
     if (n <= K) {                                 // every page, ascending, padded with -1
@@ -353,42 +359,41 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(TopkArgs a) {
         return;
     }
     const int cnt = max(0, min(n, i0 + seg) - i0);
-    unsigned long long key[kTopkPerThread];
+    unsigned long long key[PT];
 #pragma unroll
-    for (int e = 0; e < kTopkPerThread; ++e) key[e] = e < cnt ? order_key(pv[e]) : 0ull;
+    for (int e = 0; e < PT; ++e) key[e] = e < cnt ? order_key(pv[e]) : 0ull;
 
-    // the leading bits shared by every key decide nothing: find the highest
-    // differing bit (block-wide and / or of the keys) and start the radix
-    // passes at its digit, taking the shared bits as the prefix
-    __shared__ unsigned long long sh_and[kTopkThreads / kWave], sh_or[kTopkThreads / kWave];
+    // The bits above the highest one that differs between keys are shared by
+    // every key and decide nothing: the radix passes start there, each pass
+    // resolving the next (up to) 8 bits of the K-th largest key.
     unsigned long long k_and = ~0ull, k_or = 0ull;
 #pragma unroll
-    for (int e = 0; e < kTopkPerThread; ++e)
+    for (int e = 0; e < PT; ++e)
         if (e < cnt) { k_and &= key[e]; k_or |= key[e]; }
     wave_and_or(k_and, k_or);
     if (tid % kWave == 0) { sh_and[tid / kWave] = k_and; sh_or[tid / kWave] = k_or; }
+    if (tid < 256) hist[0][tid] = 0;
     __syncthreads();
     k_and = ~0ull; k_or = 0ull;
     for (int w2 = 0; w2 < kTopkThreads / kWave; ++w2) { k_and &= sh_and[w2]; k_or |= sh_or[w2]; }
     const unsigned long long differ = k_and ^ k_or;      // bits that are not the same in every key
-    int start = 56;
-    if (differ != 0ull) {
-        const int top = 63 - __clzll((long long)differ);  // highest differing bit
-        start = (top / 8) * 8;
-    }
-    const unsigned long long common_mask = start >= 56 ? 0ull : (~0ull << (start + 8));
-    unsigned long long prefix = k_and & common_mask, mask = common_mask;
+    int hi = differ ? 64 - __clzll((long long)differ) : 0;   // one past the highest differing bit
+    unsigned long long mask = hi >= 64 ? 0ull : (~0ull << hi);
+    unsigned long long prefix = k_and & mask;
     uint32_t need = (uint32_t)K;
-    for (int shift = start; shift >= 0; shift -= 8) {
-        if (tid < 256) hist[tid] = 0;
-        __syncthreads();
+    int buf = 0;
+    while (hi > 0) {
+        const int lo = max(0, hi - 8);
+        const uint32_t dmask = (1u << (hi - lo)) - 1u;
 #pragma unroll
-        for (int e = 0; e < kTopkPerThread; ++e)
-            if (e < cnt && (key[e] & mask) == prefix) atomicAdd(&hist[(key[e] >> shift) & 0xFFu], 1u);
+        for (int e = 0; e < PT; ++e)
+            if (e < cnt && (key[e] & mask) == prefix) atomicAdd(&hist[buf][uint32_t(key[e] >> lo) & dmask], 1u);
+        if (tid < 256) hist[buf ^ 1][tid] = 0;    // the next pass's histogram
         __syncthreads();
         if (tid < kWave) {
-            // lane l owns bins 4l..4l+3; suffix sums from the top bin down
-            const uint32_t c0 = hist[4 * tid], c1 = hist[4 * tid + 1], c2 = hist[4 * tid + 2], c3 = hist[4 * tid + 3];
+            // lane l owns bins 4l..4l+3; count the elements in higher bins
+            const uint32_t *hb = hist[buf];
+            const uint32_t c0 = hb[4 * tid], c1 = hb[4 * tid + 1], c2 = hb[4 * tid + 2], c3 = hb[4 * tid + 3];
             const uint32_t mine = c0 + c1 + c2 + c3;
             const uint32_t incl = wave_inclusive_scan(mine);
             const uint32_t total = (uint32_t)__builtin_amdgcn_readlane((int)incl, kWave - 1);
@@ -398,24 +403,24 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(TopkArgs a) {
                 if (above < need && above + cs[qd] >= need) {
                     sh_digit = 4 * tid + qd;
                     sh_above = above;
+                    sh_done = above + cs[qd] == need;   // the whole bin is taken
                 }
                 above += cs[qd];
             }
         }
         __syncthreads();
-        const uint32_t d = sh_digit;
         need -= sh_above;
-        prefix |= (unsigned long long)d << shift;
-        mask |= 0xFFull << shift;
-        const bool done = hist[d] == need;        // the whole bin is taken
-        __syncthreads();
-        if (done) break;
+        prefix |= (unsigned long long)sh_digit << lo;
+        mask |= (unsigned long long)dmask << lo;
+        hi = lo;
+        if (sh_done) break;
+        buf ^= 1;
     }
 
     // ordered compaction
     uint32_t c = 0;                               // low 16 bits: greater, high 16 bits: equal
 #pragma unroll
-    for (int e = 0; e < kTopkPerThread; ++e) {
+    for (int e = 0; e < PT; ++e) {
         if (e >= cnt) continue;
         const unsigned long long km = key[e] & mask;
         c += km > prefix ? 1u : (km == prefix ? 0x10000u : 0u);
@@ -424,7 +429,7 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(TopkArgs a) {
     uint32_t gt_before = excl & 0xFFFFu;
     uint32_t eq_before = excl >> 16;
 #pragma unroll
-    for (int e = 0; e < kTopkPerThread; ++e) {
+    for (int e = 0; e < PT; ++e) {
         if (e >= cnt) continue;
         const unsigned long long km = key[e] & mask;
         if (km > prefix) {
@@ -470,7 +475,13 @@ hipError_t launch_score(const ScoreArgs &a, hipStream_t s) {
 hipError_t launch_topk(const TopkArgs &a, hipStream_t s) {
     const long long grid = (long long)a.batch * a.n_ret;
     if (grid == 0) return hipSuccess;
-    hipLaunchKernelGGL(topk_kernel, dim3((unsigned)grid), dim3(kTopkThreads), 0, s, a);
+    const int per = (a.max_pages + kTopkThreads - 1) / kTopkThreads;
+    const dim3 g((unsigned)grid), blk(kTopkThreads);
+    if (per <= 1) hipLaunchKernelGGL(topk_kernel<1>, g, blk, 0, s, a);
+    else if (per <= 2) hipLaunchKernelGGL(topk_kernel<2>, g, blk, 0, s, a);
+    else if (per <= 4) hipLaunchKernelGGL(topk_kernel<4>, g, blk, 0, s, a);
+    else if (per <= 8) hipLaunchKernelGGL(topk_kernel<8>, g, blk, 0, s, a);
+    else hipLaunchKernelGGL(topk_kernel<kTopkPerThread>, g, blk, 0, s, a);
     return hipGetLastError();
 }
 
