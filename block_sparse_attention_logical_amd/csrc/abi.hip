@@ -99,7 +99,7 @@ int count_kind(const lsa_heads *hd, int h_kv, int kind) {
     return n;
 }
 
-constexpr int kPagesPerWave = 1;       // decode: pages per wavefront
+constexpr int kDecodeChunkPages = 4;   // decode: pages per workgroup (one per wavefront)
 
 struct DecodeGeom {
     int K, chunks_ret, chunks_str, chunks_max, rec_floats;
@@ -111,7 +111,7 @@ size_t decode_counter_bytes(int batch, int num_kv_heads) { return align_up((size
 DecodeGeom decode_geometry(const lsa_kv *kv, const lsa_heads *hd, int token_budget) {
     DecodeGeom g;
     g.K = token_budget / kv->page_size;
-    const int per_chunk = 4 * kPagesPerWave;
+    const int per_chunk = kDecodeChunkPages;
     const int NP = kv->page_size;
     const int ret_pages = g.K + 1;
     const int str_pages = (hd->sink_tokens + NP - 1) / NP + (hd->local_tokens - 1) / NP + 2;
@@ -325,7 +325,6 @@ lsa_status lsa_sparse_decode_attn(const void *q, int32_t q_dtype, const lsa_kv *
     a.chunks_str = g.chunks_str;
     a.chunks_max = g.chunks_max;
     a.chunks_per_seq = n_ret * g.chunks_ret + (kv->num_kv_heads - n_ret) * g.chunks_str;
-    a.pages_per_wave = kPagesPerWave;
     const float scale = softmax_scale > 0.f ? softmax_scale : 1.f / std::sqrt((float)kv->head_dim);
     a.scale_log2 = scale * 1.4426950408889634f;
     for (int i = 0; i < kv->num_kv_heads; ++i) a.kind[i] = heads->head_kind[i];

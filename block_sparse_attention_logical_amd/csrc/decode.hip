@@ -6,10 +6,10 @@
 // of KV pages per step; the KV4 co-design pairs the sparse path with 4-bit KV).
 //
 // Work decomposition (split-KV).  The attended page list of a (sequence, KV
-// head) is cut into chunks of 4 * pages_per_wave pages; one workgroup of four
-// wavefronts takes a chunk, each wavefront streams its pages with an online
-// softmax, the four states are merged in LDS and one partial record
-// (max, sum, unnormalised output) is written per chunk.  The last workgroup of
+// head) is cut into chunks of 4 pages; one workgroup of four wavefronts takes
+// a chunk (wavefront 0 resolves the four pool pages into LDS), each wavefront
+// streams its page with an online softmax, the four states are merged in LDS
+// and one partial record (max, sum, unnormalised output) is written per chunk.  The last workgroup of
 // a (sequence, KV head) to finish merges every record in chunk order (so the
 // result does not depend on arrival order) and writes the output.  The
 // hand-off avoids a device-scope fence (an L2 writeback on this part): the
@@ -21,13 +21,14 @@
 //
 // MFMA path (bf16 and int4 pools).  Both contractions run on
 // v_mfma_f32_16x16x32_bf16 straight from registers.  QK^T is computed
-// transposed (tokens in M, heads in N): a lane loads contiguous bytes of one
-// key row; the 32 keys of a block are placed on MFMA rows so that the score
-// registers a lane receives are exactly the B operand the PV product needs
-// (8 consecutive tokens of one head); the V page is channel-major, so the A
-// operand of PV (one channel, 8 consecutive tokens) is again one load.  Heads
-// occupy the N dimension, padded to 16 with zero queries.  All K and V loads
-// of kDecodeBlocksInFlight 32-token blocks are issued before their first MFMA.
+// transposed (tokens in M, heads in N) as two 16-token tiles per 32-token
+// block; with the pool's key tiles every channel step of a tile is one
+// contiguous 1 KiB read.  A lane's scores (4 tokens of each tile) are
+// regrouped with two permlane swaps into 8 consecutive tokens of one head, the
+// B operand of PV; the A operand of PV (one channel, 8 consecutive tokens of
+// the value rows) is again a contiguous read.  Heads occupy the N dimension,
+// padded to 16 with zero queries.  All K and V loads of kDecodeBlocksInFlight
+// 32-token blocks are issued before their first MFMA.
 //
 // int4 pools.  A code c (0..15) becomes the bf16 bit pattern 0x4300 | c, which
 // is exactly 128 + c, so the MFMAs see exact operands; the offset and the
@@ -64,54 +65,51 @@ __device__ __forceinline__ WorkItem decode_item(const DecodeArgs &a) {
     return w;
 }
 
-// The attended physical pages of one (sequence, KV head), in ascending order.
-struct PageList {
-    int n;                 // list length
-    const int32_t *sel;    // retrieval: the selection row (ascending, -1 padded)
-    int n_sel, cur;
-    int n_sink_pages, local_first;   // streaming
+// Slots of the per-workgroup page list in LDS: t, L, then the sequence page
+// and the pool page of each of the four wavefronts (-1: no page).
+constexpr int kListSlots = 10;
 
-    __device__ __forceinline__ int page(int i) const {
-        if (sel) return i < n_sel ? sel[i] : cur;
-        return i < n_sink_pages ? i : local_first + (i - n_sink_pages);
-    }
-};
-
-// Loads seq_lens[b] and (retrieval) the selection row in parallel, then builds
-// the list.  Sets w.t and w.L.
-__device__ __forceinline__ PageList make_list(const DecodeArgs &a, WorkItem &w) {
-    PageList pl;
-    const int NP = a.page_size;
+// Wavefront 0 of a workgroup resolves the pages of its chunk: the attended
+// pages of a (sequence, KV head) in ascending order are the selection row
+// (valid entries first, then -1) followed by the current page when the row
+// lacks it (retrieval heads), or the sink pages followed by the local window
+// (streaming heads); the chunk takes list entries 4 * chunk .. 4 * chunk + 3.
+// seq_lens and the selection entries are loaded together, then the four
+// page-table entries: two dependent loads in all.
+__device__ __forceinline__ void wg_pages(const DecodeArgs &a, const WorkItem &w, int *list) {
     const int lane = threadIdx.x % kWave;
+    const int NP = a.page_size;
+    const int i = w.chunk * 4 + (lane & 3);            // list index of this lane's page (lanes 0..3)
     const int32_t *sel = w.streaming ? nullptr : a.selected + ((size_t)w.b * a.num_kv_heads + w.kv) * a.sel_k;
-    int m0 = -1;
-    if (sel && lane < a.sel_k) m0 = sel[lane];         // issued together with the seq_lens load
-    w.L = a.seq_lens[w.b];
-    w.t = w.L - 1;
-    pl.cur = w.t / NP;
-    pl.sel = sel;
-    if (w.streaming) {
-        pl.n_sel = 0;
-        const int sink_end = min(a.sink, w.t + 1);     // tokens [0, sink_end)
-        pl.n_sink_pages = (sink_end + NP - 1) / NP;
-        const int lf = max(0, w.t - a.local + 1) / NP;  // first local page
-        pl.local_first = max(lf, pl.n_sink_pages);
-        pl.n = pl.n_sink_pages + max(0, pl.cur - pl.local_first + 1);
-    } else {
-        int cnt = __popcll(__ballot(m0 >= 0));
-        bool in = __ballot(m0 == pl.cur) != 0;
-        for (int i0 = kWave; i0 < a.sel_k; i0 += kWave) {
-            const int i = i0 + lane;
-            const int m = i < a.sel_k ? sel[i] : -1;
-            cnt += __popcll(__ballot(m >= 0));
-            in |= __ballot(m == pl.cur) != 0;
-        }
-        pl.n_sel = cnt;
-        pl.n_sink_pages = 0;
-        pl.local_first = 0;
-        pl.n = cnt + (in ? 0 : 1);
+    int m_row = -1, m_i = -1;
+    if (sel) {
+        if (lane < a.sel_k) m_row = sel[lane];
+        if (lane < 4 && i < a.sel_k) m_i = sel[i];
     }
-    return pl;
+    const int L = a.seq_lens[w.b];
+    const int t = L - 1, cur = t / NP;
+    int page = -1;
+    if (w.streaming) {
+        const int sink_end = min(a.sink, t + 1);          // tokens [0, sink_end)
+        const int n_sink = (sink_end + NP - 1) / NP;
+        const int local_first = max(max(0, t - a.local + 1) / NP, n_sink);
+        const int n = n_sink + max(0, cur - local_first + 1);
+        if (i < n) page = i < n_sink ? i : local_first + (i - n_sink);
+    } else {
+        int cnt = __popcll(__ballot(m_row >= 0));
+        bool in = __ballot(m_row == cur) != 0;
+        for (int j0 = kWave; j0 < a.sel_k; j0 += kWave) {
+            const int m = j0 + lane < a.sel_k ? sel[j0 + lane] : -1;
+            cnt += __popcll(__ballot(m >= 0));
+            in |= __ballot(m == cur) != 0;
+        }
+        const int n = cnt + (in ? 0 : 1);
+        if (i < n) page = i < cnt ? m_i : cur;
+    }
+    int pool = -1;
+    if (lane < 4 && page >= 0) pool = a.page_table[(size_t)w.b * a.max_pages + page];
+    if (lane == 0) { list[0] = t; list[1] = L; }
+    if (lane < 4) { list[2 + lane] = page; list[6 + lane] = pool; }
 }
 
 __device__ __forceinline__ bool token_visible(const DecodeArgs &a, const WorkItem &w, int p) {
@@ -139,12 +137,13 @@ __device__ __forceinline__ void refresh_current_stats(const DecodeArgs &a, const
     const int row0 = jl * NL, rows = w.t - j * NL + 1;
     const int pool = a.page_table[(size_t)w.b * a.max_pages + m];
     const size_t hp = (size_t)pool * a.num_kv_heads + w.kv;
+    const size_t page_base = hp * NP * D;
     if (kv_dtype == LSA_INT4) {
         if (lane >= D / 2) return;
-        const uint8_t *k = static_cast<const uint8_t *>(a.k) + (hp * NP + row0) * (D / 2) + lane;
+        const uint8_t *k = static_cast<const uint8_t *>(a.k);
         uint32_t lo_min = 15, lo_max = 0, hi_min = 15, hi_max = 0;
         for (int r = 0; r < rows; ++r) {
-            const uint32_t byte = k[(size_t)r * (D / 2)];
+            const uint32_t byte = k[(page_base + key_offset(row0 + r, 2 * lane, D)) / 2];
             lo_min = min(lo_min, byte & 15u); lo_max = max(lo_max, byte & 15u);
             hi_min = min(hi_min, byte >> 4); hi_max = max(hi_max, byte >> 4);
         }
@@ -158,10 +157,11 @@ __device__ __forceinline__ void refresh_current_stats(const DecodeArgs &a, const
         float mn = __builtin_inff(), mx = -__builtin_inff();
         for (int r = 0; r < rows; ++r) {
             float x;
+            const size_t off = page_base + key_offset(row0 + r, ch, D);
             if (kv_dtype == LSA_BF16)
-                x = bf16_to_f32(static_cast<const uint16_t *>(a.k)[(hp * NP + row0 + r) * D + ch]);
+                x = bf16_to_f32(static_cast<const uint16_t *>(a.k)[off]);
             else
-                x = static_cast<const float *>(a.k)[(hp * NP + row0 + r) * D + ch];
+                x = static_cast<const float *>(a.k)[off];
             mn = fminf(mn, x);
             mx = fmaxf(mx, x);
         }
@@ -335,7 +335,12 @@ __global__ __launch_bounds__(256, 3) void decode_mfma_kernel(DecodeArgs a) {
             qsum = sum_xor32(sum_xor16(qsum));
         }
     }
-    const PageList pl = make_list(a, w);
+    __shared__ int s_list[kListSlots];
+    if (wave == 0) wg_pages(a, w, s_list);
+    __syncthreads();
+    w.t = s_list[0];
+    w.L = s_list[1];
+    const int my_page = s_list[2 + wave], my_pool = s_list[6 + wave];
 
     floatx4 o[NDT];
 #pragma unroll
@@ -343,17 +348,14 @@ __global__ __launch_bounds__(256, 3) void decode_mfma_kernel(DecodeArgs a) {
     float m_run = -__builtin_inff(), l_run = 0.f;
     float corr = 0.f;                      // int4: (128 + z_v) * sum of fed weights (per lane)
 
-    const int ppw = a.pages_per_wave;
-    const int i_begin = w.chunk * 4 * ppw + wave * ppw;
-    const int i_end = min(i_begin + ppw, pl.n);
-    // MFMA row rho of QK tile T holds key 8*(rho/4) + 4*T + rho%4 of its 32-key block
+    // QK^T tile T of a 32-token block holds tokens 16T .. 16T + 15 on MFMA
+    // rows (row rho = token 16T + rho, one contiguous 1 KiB key-tile read per
+    // channel step); a lane's result registers hold tokens 16T + 4*g4 + r.
     const int rho = lane & 15;
-    const int key_r = 8 * (rho >> 2) + (rho & 3);
 
-    for (int i = i_begin; i < i_end; ++i) {
-        const int page = pl.page(i);
-        const int pool = a.page_table[(size_t)w.b * a.max_pages + page];
-        const size_t hp = (size_t)pool * a.num_kv_heads + w.kv;
+    if (my_page >= 0) {
+        const int page = my_page;
+        const size_t hp = (size_t)my_pool * a.num_kv_heads + w.kv;
         float sk = 1.f, zk = 0.f, sv = 1.f, zv = 0.f;
         if constexpr (I4) {
             const uint32_t ksz = *reinterpret_cast<const uint32_t *>(a.k_sz + hp * 2);
@@ -374,10 +376,10 @@ __global__ __launch_bounds__(256, 3) void decode_mfma_kernel(DecodeArgs a) {
                 need[e] = kb < NP / 32 && block_needed(a, w, p0 + 32 * kb);
                 if (!need[e]) continue;
                 if constexpr (I4) {
-                    const uint8_t *kp = static_cast<const uint8_t *>(a.k) + (hp * NP + 32 * kb) * (D / 2);
+                    const uint8_t *k8 = static_cast<const uint8_t *>(a.k);
 #pragma unroll
                     for (int T = 0; T < 2; ++T) {
-                        const uint8_t *row = kp + (size_t)(key_r + 4 * T) * (D / 2) + (D / 8) * g4;
+                        const uint8_t *row = k8 + (hp * NP * D + key_offset(32 * kb + 16 * T + rho, (D / 4) * g4, D)) / 2;
                         if constexpr (D == 128) {
                             kr[e][T][0] = *reinterpret_cast<const uint4 *>(row);
                         } else {
@@ -385,21 +387,23 @@ __global__ __launch_bounds__(256, 3) void decode_mfma_kernel(DecodeArgs a) {
                             kr[e][T][0] = make_uint4(u.x, u.y, 0, 0);
                         }
                     }
-                    const uint8_t *vp = static_cast<const uint8_t *>(a.v) + hp * D * (NP / 2);
+                    const uint8_t *v8 = static_cast<const uint8_t *>(a.v);
 #pragma unroll
                     for (int dt = 0; dt < NDT; ++dt)
-                        vr4[e][dt] = *reinterpret_cast<const uint32_t *>(vp + (size_t)(16 * dt + h) * (NP / 2) + 16 * kb + 4 * g4);
+                        vr4[e][dt] = *reinterpret_cast<const uint32_t *>(
+                            v8 + (hp * NP * D + value_offset(32 * kb + 8 * g4, 16 * dt + h, D)) / 2);
                 } else {
-                    const uint16_t *kp = static_cast<const uint16_t *>(a.k) + (hp * NP + 32 * kb) * D;
+                    const uint16_t *kp = static_cast<const uint16_t *>(a.k) + hp * NP * D;
 #pragma unroll
                     for (int T = 0; T < 2; ++T)
 #pragma unroll
                         for (int s = 0; s < NS; ++s)
-                            kr[e][T][s] = *reinterpret_cast<const uint4 *>(kp + (size_t)(key_r + 4 * T) * D + 32 * s + 8 * g4);
-                    const uint16_t *vp = static_cast<const uint16_t *>(a.v) + hp * D * NP;
+                            kr[e][T][s] = *reinterpret_cast<const uint4 *>(
+                                kp + key_offset(32 * kb + 16 * T + rho, 32 * s + 8 * g4, D));
+                    const uint16_t *vp = static_cast<const uint16_t *>(a.v) + hp * NP * D;
 #pragma unroll
                     for (int dt = 0; dt < NDT; ++dt)
-                        vr[e][dt] = *reinterpret_cast<const uint4 *>(vp + (size_t)(16 * dt + h) * NP + 32 * kb + 8 * g4);
+                        vr[e][dt] = *reinterpret_cast<const uint4 *>(vp + value_offset(32 * kb + 8 * g4, 16 * dt + h, D));
                 }
             }
 #pragma unroll
@@ -424,7 +428,8 @@ __global__ __launch_bounds__(256, 3) void decode_mfma_kernel(DecodeArgs a) {
                     s0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k0, qb[s], s0, 0, 0, 0);
                     s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k1, qb[s], s1, 0, 0, 0);
                 }
-                // lane holds the logits of head h for keys 8*g4 + j, j = 0..7 of the block
+                // lane holds the logits of head h for tokens 4*g4 + r (x[r]) and
+                // 16 + 4*g4 + r (x[4 + r]) of the block, r = 0..3
                 float x[8];
                 if constexpr (I4) {
                     const float off = (128.f + zk) * qsum;
@@ -438,7 +443,7 @@ __global__ __launch_bounds__(256, 3) void decode_mfma_kernel(DecodeArgs a) {
                 float mb = -__builtin_inff();
 #pragma unroll
                 for (int j = 0; j < 8; ++j) {
-                    if (!token_visible(a, w, tok0 + 8 * g4 + j)) x[j] = -__builtin_inff();
+                    if (!token_visible(a, w, tok0 + 4 * g4 + (j & 3) + 16 * (j >> 2))) x[j] = -__builtin_inff();
                     mb = fmaxf(mb, x[j]);
                 }
                 mb = max_xor32(max_xor16(mb));
@@ -465,7 +470,20 @@ __global__ __launch_bounds__(256, 3) void decode_mfma_kernel(DecodeArgs a) {
                 l_run = l_run * alpha + psum;
                 if constexpr (I4) corr = corr * alpha + (128.f + zv) * fed;
                 m_run = m_new;
-                const bf16x8 pbv = __builtin_bit_cast(bf16x8, make_uint4(pk[0], pk[1], pk[2], pk[3]));
+                // The PV operand of lane (h, g4) wants tokens 8*g4 .. 8*g4 + 7.  Swapping
+                // the upper 32 lanes of pk[0..1] (tokens 4*g4 + r) with the lower 32
+                // lanes of pk[2..3] (tokens 16 + 4*g4 + r), then the odd 16-lane rows
+                // of the first result with the even rows of the second, regroups the
+                // four 4-token runs of every head into that order.
+                uint32_t pv[4];
+#pragma unroll
+                for (int d = 0; d < 2; ++d) {
+                    const auto r32 = __builtin_amdgcn_permlane32_swap(pk[d], pk[2 + d], false, false);
+                    const auto r16 = __builtin_amdgcn_permlane16_swap(r32[0], r32[1], false, false);
+                    pv[d] = r16[0];
+                    pv[2 + d] = r16[1];
+                }
+                const bf16x8 pbv = __builtin_bit_cast(bf16x8, make_uint4(pv[0], pv[1], pv[2], pv[3]));
                 // slots after the current token may hold any bits: zero their values so a
                 // zero probability never meets a NaN in the PV product
                 const bool tail = tok0 + 31 > w.t;
@@ -519,16 +537,20 @@ template <int D>
 __global__ __launch_bounds__(256) void decode_f32_kernel(DecodeArgs a) {
     extern __shared__ float lds[];
     WorkItem w = decode_item(a);
-    const PageList pl = make_list(a, w);
     const int lane = threadIdx.x % kWave, wave = threadIdx.x / kWave;
     const int G = a.group, NP = a.page_size;
     constexpr int CPL = D / 64;                   // channels per lane in PV
+    __shared__ int s_list[kListSlots];
+    if (wave == 0) wg_pages(a, w, s_list);
 
     float *qs = lds + 4 * (32 + 16 * D);          // [G][D]
     float *ps = qs + 16 * D + wave * 16 * 64;     // this wave's [16][64] probabilities
     for (int idx = threadIdx.x; idx < G * D; idx += blockDim.x)
         qs[idx] = static_cast<const float *>(a.q)[((size_t)w.b * a.num_q_heads + (size_t)w.kv * G) * D + idx];
     __syncthreads();
+    w.t = s_list[0];
+    w.L = s_list[1];
+    const int my_page = s_list[2 + wave], my_pool = s_list[6 + wave];
 
     float o[16][CPL];
     float m_run[16], l_run[16];
@@ -540,18 +562,14 @@ __global__ __launch_bounds__(256) void decode_f32_kernel(DecodeArgs a) {
         for (int c = 0; c < CPL; ++c) o[hh][c] = 0.f;
     }
 
-    const int ppw = a.pages_per_wave;
-    const int i_begin = w.chunk * 4 * ppw + wave * ppw;
-    const int i_end = min(i_begin + ppw, pl.n);
     const float *kpool = static_cast<const float *>(a.k);
     const float *vpool = static_cast<const float *>(a.v);
 
-    for (int i = i_begin; i < i_end; ++i) {
-        const int page = pl.page(i);
-        const int pool = a.page_table[(size_t)w.b * a.max_pages + page];
-        const size_t head_page = (size_t)pool * a.num_kv_heads + w.kv;
+    if (my_page >= 0) {
+        const int page = my_page;
+        const size_t head_page = (size_t)my_pool * a.num_kv_heads + w.kv;
         const float *kp = kpool + head_page * NP * D;
-        const float *vp = vpool + head_page * D * NP;
+        const float *vp = vpool + head_page * NP * D;
         for (int s0 = 0; s0 < NP; s0 += kWave) {
             const int slot = s0 + lane;
             const int p = page * NP + slot;
@@ -560,9 +578,8 @@ __global__ __launch_bounds__(256) void decode_f32_kernel(DecodeArgs a) {
 #pragma unroll
             for (int hh = 0; hh < 16; ++hh) sc[hh] = 0.f;
             if (slot < NP) {
-                const float *krow = kp + (size_t)slot * D;
                 for (int d = 0; d < D; d += 4) {
-                    const float4 kv4 = *reinterpret_cast<const float4 *>(krow + d);
+                    const float4 kv4 = *reinterpret_cast<const float4 *>(kp + key_offset(slot, d, D));
 #pragma unroll
                     for (int hh = 0; hh < 16; ++hh) {
                         if (hh < G) {
@@ -595,12 +612,12 @@ __global__ __launch_bounds__(256) void decode_f32_kernel(DecodeArgs a) {
 #pragma unroll
             for (int c = 0; c < CPL; ++c) {
                 const int d = lane * CPL + c;
-                const float *vrow = vp + (size_t)d * NP + s0;
+
                 float acc[16];
 #pragma unroll
                 for (int hh = 0; hh < 16; ++hh) acc[hh] = o[hh][c] * alpha[hh];
                 for (int sl = 0; sl < nslots; ++sl) {
-                    const float vv = vrow[sl];
+                    const float vv = vp[value_offset(s0 + sl, d, D)];
 #pragma unroll
                     for (int hh = 0; hh < 16; ++hh)
                         if (hh < G) acc[hh] = fmaf(ps[hh * 64 + sl], vv, acc[hh]);

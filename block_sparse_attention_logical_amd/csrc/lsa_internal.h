@@ -39,6 +39,19 @@ __device__ __forceinline__ float fp16_bits_to_f32(uint16_t h) {
 __device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
 
 // ----------------------------------------------------------------------------
+// page layout: a page of N_P tokens of one KV head is N_P/32 blocks of 32
+// tokens; keys are [block][D/32][32 tokens][32 channels] tiles, values are
+// [block][D][32 tokens] rows.  Offsets are in elements (int4: halve for the
+// byte of an even channel / token).
+// ----------------------------------------------------------------------------
+__device__ __forceinline__ size_t key_offset(int s, int c, int D) {
+    return ((size_t)(s >> 5) * (D >> 5) + (c >> 5)) * 1024 + (size_t)(s & 31) * 32 + (c & 31);
+}
+__device__ __forceinline__ size_t value_offset(int s, int c, int D) {
+    return (size_t)(s >> 5) * D * 32 + (size_t)c * 32 + (s & 31);
+}
+
+// ----------------------------------------------------------------------------
 // cross-lane primitives on the VALU (DPP and gfx950 permlane swaps).  A
 // ds_bpermute (what __shfl_* lowers to) goes through the LDS crossbar and
 // costs a long round trip; chains of them dominated the small kernels.
@@ -227,7 +240,6 @@ struct DecodeArgs {
     int32_t chunks_ret, chunks_str;   // workgroups per (sequence, head) by kind
     int32_t chunks_max;               // record slots per (sequence, head)
     int32_t chunks_per_seq;           // workgroups per sequence
-    int32_t pages_per_wave;
     float scale_log2;                 // softmax scale * log2(e)
     uint8_t kind[kMaxKvHeads];
 };

@@ -130,35 +130,49 @@ __global__ __launch_bounds__(512, 2) void prefill_bf16_kernel(PrefillArgs p) {
     const uint16_t *vpool = static_cast<const uint16_t *>(p.v);
     const int n_iter = e0 + (it.a - s1 + 1);
     auto tile_of = [&](int ii) { return ii < e0 ? ii : s1 + (ii - e0); };
-    auto head_page = [&](int c, int &slot0) {
+    // A 64-key tile is two whole 32-token blocks of its page, so its keys (and
+    // its values) are one contiguous run of 64 * D elements: 16-byte chunk ch of
+    // the run is read by consecutive threads, and the chunk's (key, channel
+    // group) or (channel, key group) follows from the pool layout.
+    auto tile_base = [&](int c) {
         const int key0 = c * kTile;
-        slot0 = key0 % NP;
-        return (size_t)p.page_table[key0 / NP] * p.num_kv_heads + it.kv;
+        const size_t hp = (size_t)p.page_table[key0 / NP] * p.num_kv_heads + it.kv;
+        return hp * NP * D + key_offset(key0 % NP, 0, D);       // == value_offset(key0 % NP, 0, D)
+    };
+    // key chunk ch: tile row r (key), channels 8 * cc .. 8 * cc + 7
+    auto k_chunk = [&](int ch, int &r, int &cc) {
+        const int rest = ch >> 7;                                // block * (D / 32) + channel slice
+        r = 32 * (rest / (D / 32)) + ((ch >> 2) & 31);
+        cc = 4 * (rest % (D / 32)) + (ch & 3);
+    };
+    // value chunk ch: channel d, keys 8 * cc .. 8 * cc + 7 of the tile
+    auto v_chunk = [&](int ch, int &d, int &cc) {
+        d = (ch >> 2) % D;
+        cc = 4 * (ch / (4 * D)) + (ch & 3);
     };
 
     // global -> registers (keys >= T read as zero); registers -> LDS
     uint4 kreg[KPT], vreg[VPT];
     auto fetch_k = [&](int ii) {
         const int c = tile_of(ii);
-        int slot0;
-        const size_t hp = head_page(c, slot0);
+        const uint16_t *src = kpool + tile_base(c);
 #pragma unroll
         for (int e = 0; e < KPT; ++e) {
             const int ch = tid + e * NT;
-            const int r = ch / (D / 8), cc = ch % (D / 8);
-            kreg[e] = c * kTile + r < T ? *reinterpret_cast<const uint4 *>(kpool + (hp * NP + slot0 + r) * D + cc * 8)
-                                        : make_uint4(0, 0, 0, 0);
+            int r, cc;
+            k_chunk(ch, r, cc);
+            kreg[e] = c * kTile + r < T ? *reinterpret_cast<const uint4 *>(src + (size_t)ch * 8) : make_uint4(0, 0, 0, 0);
         }
     };
     auto fetch_v = [&](int ii) {
         const int c = tile_of(ii);
-        int slot0;
-        const size_t hp = head_page(c, slot0);
+        const uint16_t *src = vpool + tile_base(c);
 #pragma unroll
         for (int e = 0; e < VPT; ++e) {
             const int ch = tid + e * NT;
-            const int d = ch / (kTile / 8), cc = ch % (kTile / 8);
-            uint4 val = *reinterpret_cast<const uint4 *>(vpool + (hp * D + d) * NP + slot0 + cc * 8);
+            int d, cc;
+            v_chunk(ch, d, cc);
+            uint4 val = *reinterpret_cast<const uint4 *>(src + (size_t)ch * 8);
             const int kbase = c * kTile + cc * 8;
             if (kbase + 8 > T) {
                 const int nv = T - kbase;          // valid keys in this chunk (<= 7)
@@ -175,7 +189,8 @@ __global__ __launch_bounds__(512, 2) void prefill_bf16_kernel(PrefillArgs p) {
 #pragma unroll
         for (int e = 0; e < KPT; ++e) {
             const int ch = tid + e * NT;
-            const int key = ch / (D / 8), cc = ch % (D / 8);
+            int key, cc;
+            k_chunk(ch, key, cc);
             // key k of a 32-key half is stored at the LDS row of the MFMA row that reads it
             const int kk = key & 31;
             const int rho = 8 * (2 * (kk >> 4) + ((kk >> 2) & 1)) + 4 * ((kk >> 3) & 1) + (kk & 3);
@@ -186,7 +201,8 @@ __global__ __launch_bounds__(512, 2) void prefill_bf16_kernel(PrefillArgs p) {
 #pragma unroll
         for (int e = 0; e < VPT; ++e) {
             const int ch = tid + e * NT;
-            const int d = ch / (kTile / 8), cc = ch % (kTile / 8);
+            int d, cc;
+            v_chunk(ch, d, cc);
             *reinterpret_cast<uint4 *>(&v_lds[buf][d * VS + cc * 8]) = vreg[e];
         }
     };
@@ -348,9 +364,9 @@ __global__ __launch_bounds__(256) void prefill_f32_kernel(PrefillArgs p) {
         __syncthreads();
         for (int e = tid; e < kTile * D; e += 256) {
             const int r = e / D, d = e % D;
-            k_lds[e] = key0 + r < T ? kpool[(hp * NP + slot0 + r) * D + d] : 0.f;
+            k_lds[e] = key0 + r < T ? kpool[hp * NP * D + key_offset(slot0 + r, d, D)] : 0.f;
             const int dv = e / kTile, rv = e % kTile;
-            v_lds[e] = key0 + rv < T ? vpool[(hp * D + dv) * NP + slot0 + rv] : 0.f;
+            v_lds[e] = key0 + rv < T ? vpool[hp * NP * D + value_offset(slot0 + rv, dv, D)] : 0.f;
         }
         __syncthreads();
         if (!head_ok) continue;

@@ -83,8 +83,8 @@ __device__ __forceinline__ void load_q_pos_neg(const ScoreArgs &a, int b, int kv
 // ...), combined over the groups so every lane ends with all rows.  Float
 // channels for f32 / bf16 pools, 4-bit codes (as floats) for int4 pools.
 template <int KV_DT, int D, int C, int LPL, int LPP>
-__device__ __forceinline__ void current_page_minmax(const ScoreArgs &a, size_t krow0, int rows, int q, int ch0,
-                                                    float (&kmin)[C], float (&kmax)[C]) {
+__device__ __forceinline__ void current_page_minmax(const ScoreArgs &a, size_t page_base, int row0, int rows, int q,
+                                                    int ch0, float (&kmin)[C], float (&kmax)[C]) {
 #pragma unroll
     for (int c = 0; c < C; ++c) { kmin[c] = __builtin_inff(); kmax[c] = -__builtin_inff(); }
     constexpr int RB = 4;                       // rows per lane and batch, loaded together
@@ -95,7 +95,7 @@ __device__ __forceinline__ void current_page_minmax(const ScoreArgs &a, size_t k
             for (int i = 0; i < RB; ++i) {
                 const int rr = r0 + q + i * LPP;
                 u[i] = rr < rows ? *reinterpret_cast<const uint2 *>(static_cast<const uint8_t *>(a.k) +
-                                                                    (krow0 + rr) * (D / 2) + ch0 / 2)
+                                                                    (page_base + key_offset(row0 + rr, ch0, D)) / 2)
                                  : make_uint2(0xFFFFFFFFu, 0xFFFFFFFFu);
             }
 #pragma unroll
@@ -115,7 +115,8 @@ __device__ __forceinline__ void current_page_minmax(const ScoreArgs &a, size_t k
             for (int i = 0; i < RB; ++i) {
                 const int rr = r0 + q + i * LPP;
                 u[i] = rr < rows ? *reinterpret_cast<const uint4 *>(static_cast<const char *>(a.k) +
-                                                                    ((krow0 + rr) * D + ch0) * (KV_DT == LSA_F32 ? 4 : 2))
+                                                                    (page_base + key_offset(row0 + rr, ch0, D)) *
+                                                                        (KV_DT == LSA_F32 ? 4 : 2))
                                  : make_uint4(0, 0, 0, 0);
             }
 #pragma unroll
@@ -232,9 +233,9 @@ __global__ __launch_bounds__(kScoreThreads) void score_kernel(ScoreArgs a) {
         const int m = j_cur / g;
         const int pool = a.page_table[(size_t)b * a.max_pages + m];
         const size_t hp = (size_t)pool * a.num_kv_heads + kv;
-        const size_t krow0 = hp * a.page_size + (size_t)(j_cur % g) * a.logical_page;
         float kmin[C], kmax[C];
-        current_page_minmax<KV_DT, D, C, LPL, LPP>(a, krow0, L - j_cur * a.logical_page, lane / LPL, ch0, kmin, kmax);
+        current_page_minmax<KV_DT, D, C, LPL, LPP>(a, hp * a.page_size * D, (j_cur % g) * a.logical_page,
+                                                   L - j_cur * a.logical_page, lane / LPL, ch0, kmin, kmax);
         double c0 = 0.0, c1 = 0.0;
 #pragma unroll
         for (int c = 0; c < C; ++c) {

@@ -4,9 +4,10 @@
 // N_P-token physical pages, kept beside the physical page).
 //
 // One wavefront per (sequence, KV head, logical page).  Each lane owns one or
-// two adjacent channels and walks the page's valid rows, so every row read is
-// one contiguous, coalesced segment of the page.  Min / max select one of the
-// inputs, so the results are exact in the storage type.
+// two adjacent channels and walks the page's valid rows (a row of the key
+// tiles is 32 channels, so a wavefront's read of one token is D/32 runs of 32
+// channels).  Min / max select one of the inputs, so the results are exact in
+// the storage type.
 #include "lsa_internal.h"
 
 namespace lsa {
@@ -50,13 +51,13 @@ __global__ __launch_bounds__(256) void stats_float_kernel(StatsArgs a) {
     const int lane = threadIdx.x % kWave;
     const int D = a.head_dim;
     const int g = a.page_size / a.logical_page;
-    const size_t page_base = ((size_t)it.pool * a.num_kv_heads + it.kv) * a.page_size;
+    const size_t page_base = ((size_t)it.pool * a.num_kv_heads + it.kv) * a.page_size * D;
     const Elem *k = static_cast<const Elem *>(a.k);
     float mn[CPL], mx[CPL];
 #pragma unroll
     for (int c = 0; c < CPL; ++c) { mn[c] = __builtin_inff(); mx[c] = -__builtin_inff(); }
     for (int r = 0; r < it.rows; ++r) {
-        const Elem *row = k + (page_base + it.row0 + r) * D + lane * CPL;
+        const Elem *row = k + page_base + key_offset(it.row0 + r, lane * CPL, D);
 #pragma unroll
         for (int c = 0; c < CPL; ++c) {
             float x;
@@ -80,7 +81,7 @@ __global__ __launch_bounds__(256) void stats_float_kernel(StatsArgs a) {
     }
 }
 
-// int4 keys: byte i of a row holds channels 2i (low nibble) and 2i+1.
+// int4 keys: a tile row's byte i holds channels 2i (low nibble) and 2i+1.
 // Output byte per channel: c_min | c_max << 4.
 __global__ __launch_bounds__(256) void stats_int4_kernel(StatsArgs a) {
     const Item it = locate(a);
@@ -90,11 +91,11 @@ __global__ __launch_bounds__(256) void stats_int4_kernel(StatsArgs a) {
     const int row_bytes = D / 2;
     if (lane >= row_bytes) return;
     const int g = a.page_size / a.logical_page;
-    const size_t page_base = ((size_t)it.pool * a.num_kv_heads + it.kv) * a.page_size;
+    const size_t page_base = ((size_t)it.pool * a.num_kv_heads + it.kv) * a.page_size * D;
     const uint8_t *k = static_cast<const uint8_t *>(a.k);
     uint32_t lo_min = 15, lo_max = 0, hi_min = 15, hi_max = 0;
     for (int r = 0; r < it.rows; ++r) {
-        const uint32_t byte = k[(page_base + it.row0 + r) * row_bytes + lane];
+        const uint32_t byte = k[(page_base + key_offset(it.row0 + r, 2 * lane, D)) / 2];
         const uint32_t lo = byte & 15u, hi = byte >> 4;
         lo_min = min(lo_min, lo); lo_max = max(lo_max, lo);
         hi_min = min(hi_min, hi); hi_max = max(hi_max, hi);

@@ -26,6 +26,10 @@ int4 storage (KV4): per (pool page, KV head, tensor) scale s = fp16 of
 clamped to [0, 15], so (c - z) * s is exact in fp32; codes
 c = clamp(round(x / s + z), 0, 15); keys packed two channels per byte (even
 channel in the low nibble), values two tokens per byte.
+
+Every pool is written in the library's page layout: keys as 32 x 32 tiles
+[P][H_kv][N_P/32][D/32][32][32], values as rows [P][H_kv][N_P/32][D][32]
+(int4: the same with code pairs packed into bytes).
 """
 from __future__ import annotations
 
@@ -137,8 +141,8 @@ def _head_kinds(n_kv: int, g: torch.Generator, fixed=None) -> List[int]:
 
 
 def quantize_int4(x: torch.Tensor):
-    """int4 storage of x [..., A, Bd] grouped over its last two dims per leading
-    index: returns (codes packed along the last dim, [..., 2] fp16 {s, z})."""
+    """int4 codes of x [..., A, Bd], one (s, z) per leading index over its last
+    two dims: returns (codes uint8 [..., A, Bd], [..., 2] fp16 {s, z})."""
     lead = x.shape[:-2]
     flat = x.reshape(*lead, -1).float()
     lo = flat.amin(dim=-1)
@@ -149,9 +153,25 @@ def quantize_int4(x: torch.Tensor):
     z = z.clamp(0.0, 15.0).to(torch.float16)        # multiples of 1/16 in [0, 15] are exact in fp16
     z32 = z.float()
     c = torch.round(x.float() / s32[..., None, None] + z32[..., None, None]).clamp(0, 15).to(torch.uint8)
-    packed = c[..., 0::2] | (c[..., 1::2] << 4)
     sz = torch.stack([s, z], dim=-1)
-    return packed.contiguous(), sz
+    return c, sz
+
+
+def pack_int4(c: torch.Tensor) -> torch.Tensor:
+    """Pairs of 4-bit codes along the last dim into bytes (even element low)."""
+    return (c[..., 0::2] | (c[..., 1::2] << 4)).contiguous()
+
+
+def tile_keys(x: torch.Tensor) -> torch.Tensor:
+    """Keys [..., N_P, D] of pages -> the pool's key tiles [..., N_P/32, D/32, 32, 32]."""
+    *lead, NP, D = x.shape
+    return x.reshape(*lead, NP // 32, 32, D // 32, 32).transpose(-3, -2).contiguous()
+
+
+def tile_values(x: torch.Tensor) -> torch.Tensor:
+    """Values [..., D, N_P] (channel-major) of pages -> the pool's value rows [..., N_P/32, D, 32]."""
+    *lead, D, NP = x.shape
+    return x.reshape(*lead, D, NP // 32, 32).transpose(-3, -2).contiguous()
 
 
 def make_decode(cfg: int, device="cpu", *, batch: Optional[int] = None, ctx=None, window: Optional[int] = None,
@@ -204,12 +224,12 @@ def make_decode(cfg: int, device="cpu", *, batch: Optional[int] = None, ctx=None
     if outl is not None:
         kscale.scatter_(1, outl, 8.0)
 
-    # keys
+    # keys, as tiles [P][H_kv][N_P/32][D/32][32][32] (int4: codes packed in pairs)
     if dt == INT4:
-        k = torch.empty((P, H_kv, NP, D // 2), dtype=torch.uint8, device=device)
+        k = torch.empty((P, H_kv, NP // 32, D // 32, 32, 16), dtype=torch.uint8, device=device)
         k_sz = torch.empty((P, H_kv, 2), dtype=torch.float16, device=device)
     else:
-        k = torch.empty((P, H_kv, NP, D), dtype=qdt, device=device)
+        k = torch.empty((P, H_kv, NP // 32, D // 32, 32, 32), dtype=qdt, device=device)
         k_sz = None
     for p0 in range(0, P, chunk_pages):
         p1 = min(P, p0 + chunk_pages)
@@ -221,26 +241,27 @@ def make_decode(cfg: int, device="cpu", *, batch: Optional[int] = None, ctx=None
                 x[needle_pid[bi, ni] - p0, :, needle_slot[bi, ni], :] = needle_vec[bi]
         if dt == INT4:
             codes, sz = quantize_int4(x)
-            k[p0:p1] = codes
+            k[p0:p1] = pack_int4(tile_keys(codes))
             k_sz[p0:p1] = sz
         else:
-            k[p0:p1] = x.to(qdt)
-    # values, channel-major within a page: [P][H_kv][D][N_P]
+            k[p0:p1] = tile_keys(x.to(qdt))
+    # values, drawn channel-major per page ([D][N_P]) and stored as rows
+    # [P][H_kv][N_P/32][D][32] (int4: token codes packed in pairs)
     if dt == INT4:
-        v = torch.empty((P, H_kv, D, NP // 2), dtype=torch.uint8, device=device)
+        v = torch.empty((P, H_kv, NP // 32, D, 16), dtype=torch.uint8, device=device)
         v_sz = torch.empty((P, H_kv, 2), dtype=torch.float16, device=device)
     else:
-        v = torch.empty((P, H_kv, D, NP), dtype=qdt, device=device)
+        v = torch.empty((P, H_kv, NP // 32, D, 32), dtype=qdt, device=device)
         v_sz = None
     for p0 in range(0, P, chunk_pages):
         p1 = min(P, p0 + chunk_pages)
         x = torch.randn((p1 - p0, H_kv, D, NP), generator=g, device=device)
         if dt == INT4:
             codes, sz = quantize_int4(x)
-            v[p0:p1] = codes
+            v[p0:p1] = pack_int4(tile_values(codes))
             v_sz[p0:p1] = sz
         else:
-            v[p0:p1] = x.to(qdt)
+            v[p0:p1] = tile_values(x.to(qdt))
 
     return DecodeWorkload(
         cfg=cfg, dtype=dt, batch=B, num_q_heads=H_q, num_kv_heads=H_kv, head_dim=D,
@@ -275,13 +296,13 @@ def make_prefill(cfg: int, device="cpu", *, seq_len: Optional[int] = None, seed:
         sv = torch.ones(H_kv, device=device)
     q = (torch.randn((T, H_q, D), generator=g, device=device) * sq[None, :, None]).to(qdt)
     # pool pages are written through the page table: token p sits in page table[p // NP]
-    k = torch.empty((P, H_kv, NP, D), dtype=qdt, device=device)
-    v = torch.empty((P, H_kv, D, NP), dtype=qdt, device=device)
+    k = torch.empty((P, H_kv, NP // 32, D // 32, 32, 32), dtype=qdt, device=device)
+    v = torch.empty((P, H_kv, NP // 32, D, 32), dtype=qdt, device=device)
     kk = torch.randn((P, H_kv, NP, D), generator=g, device=device) * sk[None, :, None, None]
-    k[table.long()] = kk.to(qdt)
+    k[table.long()] = tile_keys(kk.to(qdt))
     del kk
     vv = torch.randn((P, H_kv, D, NP), generator=g, device=device) * sv[None, :, None, None]
-    v[table.long()] = vv.to(qdt)
+    v[table.long()] = tile_values(vv.to(qdt))
     del vv
     return PrefillWorkload(cfg=cfg, dtype=dt, seq_len=T, num_q_heads=H_q, num_kv_heads=H_kv, head_dim=D,
                            page_size=NP, logical_page=c["logical_page"], sink_blocks=c["sink_blocks"],

@@ -38,15 +38,25 @@
  *     multiple of 32; num_q_heads a multiple of num_kv_heads with group size
  *     G = num_q_heads / num_kv_heads <= 16.  Query head h uses KV head h / G.
  *
- * Paged KV pool layout (caller-owned, fixed):
- *   K, f32/bf16:  [num_pages][H_kv][page_size][head_dim]   token-major in a page
- *   V, f32/bf16:  [num_pages][H_kv][head_dim][page_size]   channel-major in a page
- *   K, int4:      [num_pages][H_kv][page_size][head_dim/2] bytes, channel 2i in
- *                 the low nibble of byte i
- *   V, int4:      [num_pages][H_kv][head_dim][page_size/2] bytes, token 2j in
- *                 the low nibble of byte j
+ * Paged KV pool layout (caller-owned, fixed).  A page holds page_size tokens
+ * of one KV head as page_size/32 blocks of 32 consecutive tokens; inside a
+ * block, keys are tiles of 32 tokens x 32 channels and values are
+ * channel-major rows of 32 tokens:
+ *   K, f32/bf16:  [num_pages][H_kv][page_size/32][head_dim/32][32][32]
+ *                 key (token p, channel c) of a page at
+ *                 [p/32][c/32][p%32][c%32]
+ *   V, f32/bf16:  [num_pages][H_kv][page_size/32][head_dim][32]
+ *                 value (p, c) at [p/32][c][p%32]
+ *   K, int4:      [num_pages][H_kv][page_size/32][head_dim/32][32][16] bytes:
+ *                 the K tile with channels 2i, 2i+1 of a tile row packed in
+ *                 byte i (2i in the low nibble)
+ *   V, int4:      [num_pages][H_kv][page_size/32][head_dim][16] bytes: the V
+ *                 rows with tokens 2j, 2j+1 packed in byte j (2j low nibble)
  *   k_sz, v_sz:   int4 only, [num_pages][H_kv][2] IEEE fp16 {scale s, zero z},
  *                 s > 0; a stored code c means (c - z) * s.
+ *   Every 16-byte group a kernel loads is a run of one tile row, so the
+ *   matrix-core operands of a 16-token group of keys or values are single
+ *   contiguous 1 KiB reads.
  *   Token p of sequence b is slot p % page_size of pool page
  *   page_table[b * max_pages + p / page_size].
  */

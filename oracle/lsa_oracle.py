@@ -22,11 +22,16 @@ Where the pages leave a step open, the reading taken is stated at the function
 that takes it (readings Z1..Z23, listed together in the design notes of the
 repository).
 
-Data conventions (the layout of the caller-owned paged KV pool):
-  * K  (f32 / bf16): [P][H_kv][N_P][D]        token-major within a page
-  * V  (f32 / bf16): [P][H_kv][D][N_P]        channel-major within a page
-  * K  (int4):       [P][H_kv][N_P][D/2] u8   channel 2i in the low nibble
-  * V  (int4):       [P][H_kv][D][N_P/2] u8   token 2j in the low nibble
+Data conventions (the layout of the caller-owned paged KV pool; a page is
+N_P/32 blocks of 32 consecutive tokens):
+  * K  (f32 / bf16): [P][H_kv][N_P/32][D/32][32][32]   key (p, c) of a page at
+                     [p // 32][c // 32][p % 32][c % 32]
+  * V  (f32 / bf16): [P][H_kv][N_P/32][D][32]          value (p, c) at
+                     [p // 32][c][p % 32]
+  * K  (int4):       [P][H_kv][N_P/32][D/32][32][16] u8, the K tiles with
+                     channels 2i, 2i+1 of a row in byte i (2i in the low nibble)
+  * V  (int4):       [P][H_kv][N_P/32][D][16] u8, the V rows with tokens 2j,
+                     2j+1 in byte j (2j in the low nibble)
   * k_sz, v_sz:      [P][H_kv][2] fp16 bits   (scale s, zero z); x = (c - z) * s
   * bf16 arrays are passed as uint16 bit patterns, fp16 as uint16 bit patterns.
 Token p of sequence b lives in pool page page_table[b][p // N_P], slot p % N_P.
@@ -92,32 +97,45 @@ class Pool:
     k_sz: Optional[np.ndarray] = None   # [P][H_kv][2] uint16 (fp16 bits)
     v_sz: Optional[np.ndarray] = None
 
+    def _untile_k(self, a: np.ndarray) -> np.ndarray:
+        """[N_P/32][D/32][32][32] key tiles of one page -> [N_P][D]."""
+        a = np.asarray(a).reshape(self.page_size // 32, self.head_dim // 32, 32, 32)
+        return a.transpose(0, 2, 1, 3).reshape(self.page_size, self.head_dim)
+
+    def _untile_v(self, a: np.ndarray) -> np.ndarray:
+        """[N_P/32][D][32] value rows of one page -> [N_P][D]."""
+        a = np.asarray(a).reshape(self.page_size // 32, self.head_dim, 32)
+        return a.transpose(0, 2, 1).reshape(self.page_size, self.head_dim)
+
+    def _page_codes_k(self, page: int, kv: int) -> np.ndarray:
+        """INT4: the key codes of one (pool page, KV head) as [N_P][D] uint8."""
+        return self._untile_k(unpack_int4(self.k[page, kv]))
+
     def _page_rows_k(self, page: int, kv: int) -> np.ndarray:
         """All N_P keys of one (pool page, KV head) as [N_P][D] float64."""
         if self.dtype == "f32":
-            return np.asarray(self.k[page, kv], dtype=np.float64)
+            return self._untile_k(np.asarray(self.k[page, kv], dtype=np.float64))
         if self.dtype == "bf16":
-            return bf16_bits_to_f64(self.k[page, kv])
-        codes = unpack_int4(self.k[page, kv])                      # [N_P][D]
+            return self._untile_k(bf16_bits_to_f64(self.k[page, kv]))
         s, z = fp16_bits_to_f64(self.k_sz[page, kv])
-        return dequant_int4(codes, s, z)
+        return dequant_int4(self._page_codes_k(page, kv), s, z)
 
     def _page_rows_v(self, page: int, kv: int) -> np.ndarray:
         """All N_P values of one (pool page, KV head) as [N_P][D] float64."""
         if self.dtype == "f32":
-            return np.asarray(self.v[page, kv], dtype=np.float64).T
+            return self._untile_v(np.asarray(self.v[page, kv], dtype=np.float64))
         if self.dtype == "bf16":
-            return bf16_bits_to_f64(self.v[page, kv]).T
-        codes = unpack_int4(self.v[page, kv])                      # [D][N_P]
+            return self._untile_v(bf16_bits_to_f64(self.v[page, kv]))
+        codes = self._untile_v(unpack_int4(self.v[page, kv]))     # [N_P][D]
         s, z = fp16_bits_to_f64(self.v_sz[page, kv])
-        return dequant_int4(codes, s, z).T
+        return dequant_int4(codes, s, z)
 
     def k_codes(self, page_table_row: Sequence[int], kv: int, length: int) -> np.ndarray:
         """INT4 only: the raw key codes of tokens 0..length-1, [length][D] uint8."""
         assert self.dtype == "int4"
         rows = []
         for m in range(-(-length // self.page_size)):
-            rows.append(unpack_int4(self.k[int(page_table_row[m]), kv]))
+            rows.append(self._page_codes_k(int(page_table_row[m]), kv))
         return np.concatenate(rows, axis=0)[:length] if rows else np.zeros((0, self.head_dim), np.uint8)
 
     def keys(self, page_table_row: Sequence[int], kv: int, length: int) -> np.ndarray:

@@ -348,14 +348,43 @@ def test_conversions_exact():
 
 
 def test_pool_gather_follows_page_table():
+    """Token p, channel c of a sequence sits in pool page table[p // N_P] at
+    key tile [s // 32][c // 32][s % 32][c % 32] and value row [s // 32][c][s % 32]
+    with s = p % N_P (the header's layout statement), element by element."""
     rng = np.random.default_rng(10)
-    P, H, NP, D = 5, 2, 4, 3
-    k = rng.standard_normal((P, H, NP, D)).astype(np.float32)
-    v = rng.standard_normal((P, H, D, NP)).astype(np.float32)
+    P, H, NP, D = 5, 2, 64, 64
+    k = rng.standard_normal((P, H, NP // 32, D // 32, 32, 32)).astype(np.float32)
+    v = rng.standard_normal((P, H, NP // 32, D, 32)).astype(np.float32)
     pool = O.Pool("f32", k, v, NP, D)
     table = [3, 0, 4]
-    K = pool.keys(table, 1, 10)
-    V = pool.values(table, 1, 10)
-    for p in range(10):
-        assert np.array_equal(K[p], k[table[p // NP], 1, p % NP])
-        assert np.array_equal(V[p], v[table[p // NP], 1, :, p % NP])
+    L = 150
+    K = pool.keys(table, 1, L)
+    V = pool.values(table, 1, L)
+    assert K.shape == (L, D) and V.shape == (L, D)
+    for p in range(L):
+        pg, sl = table[p // NP], p % NP
+        for c in range(D):
+            assert K[p, c] == k[pg, 1, sl // 32, c // 32, sl % 32, c % 32]
+            assert V[p, c] == v[pg, 1, sl // 32, c, sl % 32]
+
+
+def test_pool_int4_codes_follow_layout():
+    """int4 pools: code pairs packed low nibble first inside the same tiles."""
+    rng = np.random.default_rng(11)
+    P, H, NP, D = 2, 1, 32, 64
+    kc = rng.integers(0, 16, (P, H, NP // 32, D // 32, 32, 32), dtype=np.uint8)
+    vc = rng.integers(0, 16, (P, H, NP // 32, D, 32), dtype=np.uint8)
+    kb = (kc[..., 0::2] | (kc[..., 1::2] << 4)).astype(np.uint8)
+    vb = (vc[..., 0::2] | (vc[..., 1::2] << 4)).astype(np.uint8)
+    one = np.array([[0x3C00, 0x0000]] * (P * H), np.uint16).reshape(P, H, 2)   # s = 1, z = 0
+    pool = O.Pool("int4", kb, vb, NP, D, one, one)
+    table = [1, 0]
+    codes = pool.k_codes(table, 0, 64)
+    K = pool.keys(table, 0, 64)
+    V = pool.values(table, 0, 64)
+    for p in range(64):
+        pg, sl = table[p // NP], p % NP
+        for c in range(D):
+            assert codes[p, c] == kc[pg, 0, sl // 32, c // 32, sl % 32, c % 32]
+            assert K[p, c] == kc[pg, 0, sl // 32, c // 32, sl % 32, c % 32]
+            assert V[p, c] == vc[pg, 0, sl // 32, c, sl % 32]
