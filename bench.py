@@ -43,6 +43,8 @@ def parse():
     ap.add_argument("--prefill-reps", type=int, default=3)
     ap.add_argument("--no-prefill", action="store_true")
     ap.add_argument("--prefill-only", action="store_true", help="time only the prefill leg (profiling runs)")
+    ap.add_argument("--no-causal", action="store_true",
+                    help="skip the all-causal prefill reference run (profiling runs of the sparse kernel)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="budget of the oracle CPU sample")
     ap.add_argument("--eager", action="store_true", help="time eager launches instead of graph replay")
@@ -249,9 +251,24 @@ def bench_prefill(args, torch, lsa, W, O):
     dense = p.num_q_heads * n * (n + 1) // 2
     flop = tiles * 4 * 64 * 64 * p.head_dim
     t = sorted(times)[len(times) // 2]
+    # the same kernel with every head causal (the dense-causal reference the
+    # block-sparse speed-up 1 / (1 - r) is measured against)
+    causal = lsa.Heads([0] * p.num_kv_heads, p.num_q_heads, 0, 1, p.sink_blocks, p.local_blocks)
+    tc = []
+    for _ in range(0 if args.no_causal else max(1, min(2, args.prefill_reps))):
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        a.record()
+        lsa.sparse_prefill_attn(p.q, kv, p.page_table, p.seq_len, causal, out)
+        b.record()
+        torch.cuda.synchronize()
+        tc.append(a.elapsed_time(b) / 1e3)
+    t_causal = min(tc) if tc else float("nan")
+    causal_flop = dense * 4 * 64 * 64 * p.head_dim
     del out, p
     torch.cuda.empty_cache()
-    return dict(seconds=t, flop=flop, tiles=tiles, dense_tiles=dense, tflops=flop / t / 1e12)
+    return dict(seconds=t, flop=flop, tiles=tiles, dense_tiles=dense, tflops=flop / t / 1e12,
+                causal_seconds=t_causal, causal_tflops=causal_flop / t_causal / 1e12)
 
 
 # ---------------------------------------------------------------------------
@@ -315,7 +332,9 @@ def main():
         return
     if args.prefill_only:
         pre = bench_prefill(args, torch, lsa, W, O)
-        print(json.dumps({"prefill_ms": round(pre["seconds"] * 1e3, 3), "tflops": round(pre["tflops"], 1)}))
+        print(json.dumps({"prefill_ms": round(pre["seconds"] * 1e3, 3), "tflops": round(pre["tflops"], 1),
+                          "all_causal_ms": round(pre["causal_seconds"] * 1e3, 3),
+                          "measured_speedup": round(pre["causal_seconds"] / pre["seconds"], 4)}))
         return
     dec = bench_decode(args, torch, lsa, W)
     pre = None if args.no_prefill else bench_prefill(args, torch, lsa, W, O)
@@ -364,6 +383,9 @@ def main():
             "nonempty_tile_heads": pre["tiles"],
             "dense_causal_tile_heads": pre["dense_tiles"],
             "theoretical_speedup": round(pre["dense_tiles"] / pre["tiles"], 4),
+            "all_causal_ms": round(pre["causal_seconds"] * 1e3, 3),
+            "all_causal_tflops": round(pre["causal_tflops"], 1),
+            "measured_speedup": round(pre["causal_seconds"] / pre["seconds"], 4),
             "roofline": {"bound": "mfma", "achieved": round(pre["tflops"], 1), "peak": PEAK_BF16 / 1e12,
                          "unit": "TFLOP/s", "frac": round(pre["tflops"] * 1e12 / PEAK_BF16, 4), "traffic": None},
         }

@@ -151,6 +151,18 @@ __global__ __launch_bounds__(512, 2) void prefill_bf16_kernel(PrefillArgs p) {
         cc = 4 * (ch / (4 * D)) + (ch & 3);
     };
 
+    // Chunk handled by this thread in round e: the wavefront's 64 chunks are
+    // one contiguous 1 KiB (16 rows x 4 chunks).  Lane l takes chunk column
+    // l / 16 of row l % 16 (values) or of the key row that lands on LDS row
+    // l % 16 (keys: the MFMA-order row permutation swaps bits 2 and 3 of the
+    // key), so consecutive lanes store to consecutive padded LDS rows and a
+    // write phase touches distinct banks.
+    const int r16 = lane & 15;
+    const int k_lane_chunk = 4 * ((r16 & 3) | ((r16 & 4) << 1) | ((r16 & 8) >> 1)) + (lane >> 4);
+    const int v_lane_chunk = 4 * r16 + (lane >> 4);
+    auto chunk_k = [&](int e) { return (wave + e * (NT / kWave)) * kWave + k_lane_chunk; };
+    auto chunk_v = [&](int e) { return (wave + e * (NT / kWave)) * kWave + v_lane_chunk; };
+
     // global -> registers (keys >= T read as zero); registers -> LDS
     uint4 kreg[KPT], vreg[VPT];
     auto fetch_k = [&](int ii) {
@@ -158,7 +170,7 @@ __global__ __launch_bounds__(512, 2) void prefill_bf16_kernel(PrefillArgs p) {
         const uint16_t *src = kpool + tile_base(c);
 #pragma unroll
         for (int e = 0; e < KPT; ++e) {
-            const int ch = tid + e * NT;
+            const int ch = chunk_k(e);
             int r, cc;
             k_chunk(ch, r, cc);
             kreg[e] = c * kTile + r < T ? *reinterpret_cast<const uint4 *>(src + (size_t)ch * 8) : make_uint4(0, 0, 0, 0);
@@ -169,7 +181,7 @@ __global__ __launch_bounds__(512, 2) void prefill_bf16_kernel(PrefillArgs p) {
         const uint16_t *src = vpool + tile_base(c);
 #pragma unroll
         for (int e = 0; e < VPT; ++e) {
-            const int ch = tid + e * NT;
+            const int ch = chunk_v(e);
             int d, cc;
             v_chunk(ch, d, cc);
             uint4 val = *reinterpret_cast<const uint4 *>(src + (size_t)ch * 8);
@@ -188,7 +200,7 @@ __global__ __launch_bounds__(512, 2) void prefill_bf16_kernel(PrefillArgs p) {
     auto stash_k = [&](int buf) {
 #pragma unroll
         for (int e = 0; e < KPT; ++e) {
-            const int ch = tid + e * NT;
+            const int ch = chunk_k(e);
             int key, cc;
             k_chunk(ch, key, cc);
             // key k of a 32-key half is stored at the LDS row of the MFMA row that reads it
@@ -200,7 +212,7 @@ __global__ __launch_bounds__(512, 2) void prefill_bf16_kernel(PrefillArgs p) {
     auto stash_v = [&](int buf) {
 #pragma unroll
         for (int e = 0; e < VPT; ++e) {
-            const int ch = tid + e * NT;
+            const int ch = chunk_v(e);
             int d, cc;
             v_chunk(ch, d, cc);
             *reinterpret_cast<uint4 *>(&v_lds[buf][d * VS + cc * 8]) = vreg[e];
