@@ -244,7 +244,10 @@ __device__ __forceinline__ void finish_head(const DecodeArgs &a, const WorkItem 
     __syncthreads();
     if (!s_last) return;
 
-    constexpr int CB = 16;                 // chunks whose records are loaded in one batch
+    // chunks whose records are loaded in one batch: 17 covers a 4096-token
+    // budget at N_P = 64 (64 selected pages and the current one, 4 per chunk)
+    // in a single memory round trip without spilling
+    constexpr int CB = 17;
     const int G = a.group;
     const size_t rec_size = 32 + (size_t)G * D;
     const float *rec0 = a.part + ((size_t)w.b * a.num_kv_heads + w.kv) * a.chunks_max * rec_size;
