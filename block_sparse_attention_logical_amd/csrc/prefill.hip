@@ -76,25 +76,24 @@ __device__ __forceinline__ void tile_ranges(const PrefillArgs &p, const PItem &i
 // Software pipeline: iteration t issues the QK^T MFMAs of key tile t, then
 // runs the softmax and PV of tile t-1, whose VALU work overlaps the QK
 // MFMAs in flight.  K tiles and V tiles are double-buffered in LDS separately
-// (V lags K by one tile); the global loads of the next tiles are in flight
-// during the compute, one barrier per tile.  The last tile is the diagonal
-// one: its causal mask is applied in the pipeline's epilogue only.  In LDS,
-// key rows are stored in MFMA-row order (the order the QK A operand reads
-// them), so the eight lanes of a 128-byte LDS read touch eight consecutive
-// padded rows.
+// (V lags K by one tile) and loaded from global memory straight into LDS
+// (global_load_lds_dwordx4: no registers, no LDS store instructions) while
+// the compute runs, one barrier per tile.  The last tile is the diagonal one:
+// its causal mask is applied in the pipeline's epilogue only.
 // ---------------------------------------------------------------------------
 template <int D>
 __global__ __launch_bounds__(512, 2) void prefill_bf16_kernel(PrefillArgs p) {
     typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
     typedef float floatx2 __attribute__((ext_vector_type(2)));
-    constexpr int KS = D + 8;          // LDS row stride of K (elements), padded 16 bytes
-    constexpr int VS = kTile + 8;      // LDS row stride of V^T (elements), padded 16 bytes
-    constexpr int KCH = kTile * D / 8; // 16-byte chunks of a K tile
-    constexpr int VCH = D * kTile / 8; // 16-byte chunks of a V^T tile
     constexpr int NT = 512;
-    constexpr int KPT = KCH / NT, VPT = VCH / NT;   // chunks per thread
-    __shared__ __attribute__((aligned(16))) uint16_t k_lds[2][kTile * KS];
-    __shared__ __attribute__((aligned(16))) uint16_t v_lds[2][D * VS];
+    constexpr int NS = D / 32;                        // 32-channel slices of a key row
+    constexpr int KPT = kTile * D / 8 / NT;           // 16-byte chunks per thread and tile
+    // LDS tiles mirror the pool's blocks: K as [2 blocks][D/32 slices][32 rows][32 channels],
+    // V as [2 blocks][D channels][32 tokens]; 16-byte chunk c of a 64-byte row r sits at
+    // position c ^ ((r >> 2) & 3) of its row (row = key for K, channel for V), which keeps
+    // the MFMA operand reads free of bank conflicts.
+    __shared__ __attribute__((aligned(16))) uint16_t k_lds[2][kTile * D];
+    __shared__ __attribute__((aligned(16))) uint16_t v_lds[2][kTile * D];
 
     const PItem it = prefill_item(p);
     int e0, s1;
@@ -130,108 +129,59 @@ __global__ __launch_bounds__(512, 2) void prefill_bf16_kernel(PrefillArgs p) {
     const uint16_t *vpool = static_cast<const uint16_t *>(p.v);
     const int n_iter = e0 + (it.a - s1 + 1);
     auto tile_of = [&](int ii) { return ii < e0 ? ii : s1 + (ii - e0); };
-    // A 64-key tile is two whole 32-token blocks of its page, so its keys (and
-    // its values) are one contiguous run of 64 * D elements: 16-byte chunk ch of
-    // the run is read by consecutive threads, and the chunk's (key, channel
-    // group) or (channel, key group) follows from the pool layout.
+    // A 64-key tile is two whole 32-token blocks of its page: its keys (and its
+    // values) are one contiguous run of 64 * D elements laid out like the LDS tile.
     auto tile_base = [&](int c) {
         const int key0 = c * kTile;
         const size_t hp = (size_t)p.page_table[key0 / NP] * p.num_kv_heads + it.kv;
         return hp * NP * D + key_offset(key0 % NP, 0, D);       // == value_offset(key0 % NP, 0, D)
     };
-    // key chunk ch: tile row r (key), channels 8 * cc .. 8 * cc + 7
-    auto k_chunk = [&](int ch, int &r, int &cc) {
-        const int rest = ch >> 7;                                // block * (D / 32) + channel slice
-        r = 32 * (rest / (D / 32)) + ((ch >> 2) & 31);
-        cc = 4 * (rest % (D / 32)) + (ch & 3);
-    };
-    // value chunk ch: channel d, keys 8 * cc .. 8 * cc + 7 of the tile
-    auto v_chunk = [&](int ch, int &d, int &cc) {
-        d = (ch >> 2) % D;
-        cc = 4 * (ch / (4 * D)) + (ch & 3);
-    };
+    auto swz = [](int r) { return (r >> 2) & 3; };
 
-    // Chunk handled by this thread in round e: the wavefront's 64 chunks are
-    // one contiguous 1 KiB (16 rows x 4 chunks).  Lane l takes chunk column
-    // l / 16 of row l % 16 (values) or of the key row that lands on LDS row
-    // l % 16 (keys: the MFMA-order row permutation swaps bits 2 and 3 of the
-    // key), so consecutive lanes store to consecutive padded LDS rows and a
-    // write phase touches distinct banks.
-    const int r16 = lane & 15;
-    const int k_lane_chunk = 4 * ((r16 & 3) | ((r16 & 4) << 1) | ((r16 & 8) >> 1)) + (lane >> 4);
-    const int v_lane_chunk = 4 * r16 + (lane >> 4);
-    auto chunk_k = [&](int e) { return (wave + e * (NT / kWave)) * kWave + k_lane_chunk; };
-    auto chunk_v = [&](int e) { return (wave + e * (NT / kWave)) * kWave + v_lane_chunk; };
-
-    // global -> registers (keys >= T read as zero); registers -> LDS
-    uint4 kreg[KPT], vreg[VPT];
-    auto fetch_k = [&](int ii) {
-        const int c = tile_of(ii);
-        const uint16_t *src = kpool + tile_base(c);
+    // global -> LDS without registers: wavefront instruction j fills LDS chunks
+    // 64j .. 64j+63 (16 rows of 4 chunks); lane l writes position l, i.e. row
+    // 16j + l/4, position l%4, and so reads the row's logical chunk
+    // (l%4) ^ swz(row) from the pool: one contiguous 1 KiB per instruction.
+    auto fetch = [&](const uint16_t *pool, uint16_t *lds, int ii) {
+        const uint16_t *src = pool + tile_base(tile_of(ii));
 #pragma unroll
         for (int e = 0; e < KPT; ++e) {
-            const int ch = chunk_k(e);
-            int r, cc;
-            k_chunk(ch, r, cc);
-            kreg[e] = c * kTile + r < T ? *reinterpret_cast<const uint4 *>(src + (size_t)ch * 8) : make_uint4(0, 0, 0, 0);
+            const int j = wave + e * (NT / kWave);
+            const int row = 16 * j + (lane >> 2);                // (block, slice, key) or (block, channel) row
+            const int c = (lane & 3) ^ swz(row);                 // swz(row) = swz(row % 32) = swz(channel)
+            __builtin_amdgcn_global_load_lds(
+                (const void __attribute__((address_space(1))) *)(src + (size_t)row * 32 + c * 8),
+                (void __attribute__((address_space(3))) *)(lds + (size_t)j * 512), 16, 0, 0);
         }
     };
-    auto fetch_v = [&](int ii) {
-        const int c = tile_of(ii);
-        const uint16_t *src = vpool + tile_base(c);
-#pragma unroll
-        for (int e = 0; e < VPT; ++e) {
-            const int ch = chunk_v(e);
-            int d, cc;
-            v_chunk(ch, d, cc);
-            uint4 val = *reinterpret_cast<const uint4 *>(src + (size_t)ch * 8);
-            const int kbase = c * kTile + cc * 8;
-            if (kbase + 8 > T) {
-                const int nv = T - kbase;          // valid keys in this chunk (<= 7)
-                uint32_t w[4] = {val.x, val.y, val.z, val.w};
-#pragma unroll
-                for (int q2 = 0; q2 < 4; ++q2)
-                    w[q2] &= (2 * q2 < nv ? 0x0000FFFFu : 0u) | (2 * q2 + 1 < nv ? 0xFFFF0000u : 0u);
-                val = make_uint4(w[0], w[1], w[2], w[3]);
-            }
-            vreg[e] = val;
+    // values of keys >= T (only in the sequence's last tile) may hold any bits:
+    // zero them once they have landed, so a zero probability never meets a NaN
+    auto zero_v_tail = [&](int vb, int ii) {
+        const int key0 = tile_of(ii) * kTile;
+        if (key0 + kTile <= T) return;
+        for (int e = tid; e < 2 * D * 32; e += NT) {
+            const int blk = e / (D * 32), ch = (e / 32) % D, t = e % 32;
+            if (key0 + 32 * blk + t >= T)
+                v_lds[vb][(blk * D + ch) * 32 + (((t >> 3) ^ swz(ch)) << 3) + (t & 7)] = 0;
         }
     };
-    auto stash_k = [&](int buf) {
-#pragma unroll
-        for (int e = 0; e < KPT; ++e) {
-            const int ch = chunk_k(e);
-            int key, cc;
-            k_chunk(ch, key, cc);
-            // key k of a 32-key half is stored at the LDS row of the MFMA row that reads it
-            const int kk = key & 31;
-            const int rho = 8 * (2 * (kk >> 4) + ((kk >> 2) & 1)) + 4 * ((kk >> 3) & 1) + (kk & 3);
-            *reinterpret_cast<uint4 *>(&k_lds[buf][((key & 32) + rho) * KS + cc * 8]) = kreg[e];
-        }
-    };
-    auto stash_v = [&](int buf) {
-#pragma unroll
-        for (int e = 0; e < VPT; ++e) {
-            const int ch = chunk_v(e);
-            int d, cc;
-            v_chunk(ch, d, cc);
-            *reinterpret_cast<uint4 *>(&v_lds[buf][d * VS + cc * 8]) = vreg[e];
-        }
-    };
-
     const float sc = p.scale_log2;
     // S^T = K Q^T of the tile in K buffer kb: lane holds keys 32*kt + 16*(r/8) + 8*lg + r%8, query q0 + col
+    // MFMA row col of tile kt reads key 32*kt + rho(col), rho swapping bits 2 and 3,
+    // so the score registers come out in the order the PV B operand needs.
+    const int krho = (col & 19) | ((col & 4) << 1) | ((col & 8) >> 1);
+    auto k_at = [&](int kb, int kt, int st) {
+        const int slice = st >> 1, c = 2 * (st & 1) + lg;
+        return __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4 *>(
+            &k_lds[kb][((kt * NS + slice) * 32 + krho) * 32 + ((c ^ swz(krho)) << 3)]));
+    };
     auto qk = [&](int kb, floatx16 (&s)[2]) {
 #pragma unroll
         for (int kt = 0; kt < 2; ++kt) {
-            const uint16_t *krow = &k_lds[kb][(32 * kt + col) * KS + 8 * lg];
-            s[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-                __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4 *>(krow)), qb[0], floatx16{}, 0, 0, 0);
+            s[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k_at(kb, kt, 0), qb[0], floatx16{}, 0, 0, 0);
 #pragma unroll
-            for (int st = 1; st < D / 16; ++st) {
-                const bf16x8 ka = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4 *>(krow + 16 * st));
-                s[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qb[st], s[kt], 0, 0, 0);
-            }
+            for (int st = 1; st < D / 16; ++st)
+                s[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k_at(kb, kt, st), qb[st], s[kt], 0, 0, 0);
         }
     };
     // online softmax of the scores s (DIAG: causal mask against key0), then O^T += V^T P^T
@@ -276,28 +226,33 @@ __global__ __launch_bounds__(512, 2) void prefill_bf16_kernel(PrefillArgs p) {
                 // k-step (kt, st): keys 32*kt + 16*st + 8*lg + j
 #pragma unroll
                 for (int dt = 0; dt < D / 32; ++dt) {
-                    const bf16x8 va = __builtin_bit_cast(
-                        bf16x8, *reinterpret_cast<const uint4 *>(&v_lds[vb][(32 * dt + col) * VS + 32 * kt + 16 * st + 8 * lg]));
+                    const int ch = 32 * dt + col, c = 2 * st + lg;
+                    const bf16x8 va = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4 *>(
+                        &v_lds[vb][(kt * D + ch) * 32 + ((c ^ swz(ch)) << 3)]));
                     o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pb, o[dt], 0, 0, 0);
                 }
             }
     };
 
     // prologue: K(0) in LDS
-    fetch_k(0);
-    stash_k(0);
+    fetch(kpool, k_lds[0], 0);
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
     floatx16 sa[2], sb[2];                           // scores of even / odd tiles
     auto step = [&](int ii, floatx16 (&s_cur)[2], floatx16 (&s_prev)[2]) {
-        // in flight during the compute: K(ii+1) and V(ii)
-        if (ii + 1 < n_iter) fetch_k(ii + 1);
-        fetch_v(ii);
+        // landing in LDS during the compute: K(ii+1) and V(ii), in the buffers
+        // last read before the previous barrier
+        if (ii + 1 < n_iter) fetch(kpool, k_lds[(ii + 1) & 1], ii + 1);
+        fetch(vpool, v_lds[ii & 1], ii);
         if (head_ok) {
             qk(ii & 1, s_cur);
             if (ii > 0) softmax_pv(s_prev, (ii - 1) & 1, tile_of(ii - 1) * kTile, std::false_type{});
         }
-        if (ii + 1 < n_iter) stash_k((ii + 1) & 1);
-        stash_v(ii & 1);
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        if (ii == n_iter - 1) {                       // the last tile may reach past T
+            __syncthreads();
+            zero_v_tail(ii & 1, ii);
+        }
         __syncthreads();
     };
     int ii = 0;
