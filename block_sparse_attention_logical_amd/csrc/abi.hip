@@ -90,6 +90,9 @@ lsa_status check_heads(const lsa_heads *hd, const lsa_kv *kv, bool need) {
         return fail(LSA_ERR_INVALID_ARG, "need sink_tokens >= 0 and local_tokens >= 1");
     if (hd->sink_blocks < 0 || hd->local_blocks < 1)
         return fail(LSA_ERR_INVALID_ARG, "need sink_blocks >= 0 and local_blocks >= 1");
+    if (hd->score_aggregation != LSA_AGG_SUM && hd->score_aggregation != LSA_AGG_MAX)
+        return fail(LSA_ERR_INVALID_ARG, "score_aggregation %d is not LSA_AGG_SUM or LSA_AGG_MAX",
+                    hd->score_aggregation);
     return LSA_OK;
 }
 
@@ -233,6 +236,7 @@ lsa_status lsa_select_pages(const void *q, int32_t q_dtype, const lsa_kv *kv, co
     sa.logical_page = kv->logical_page;
     sa.q_dtype = q_dtype;
     sa.kv_dtype = kv->kv_dtype;
+    sa.aggregation = heads->score_aggregation;
     sa.n_ret = 0;
     for (int i = 0; i < kv->num_kv_heads; ++i)
         if (heads->head_kind[i] == LSA_RETRIEVAL_HEAD) sa.ret_heads[sa.n_ret++] = (uint8_t)i;

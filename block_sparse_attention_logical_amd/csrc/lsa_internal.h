@@ -206,6 +206,7 @@ struct ScoreArgs {
     double *phys;                 // [B][H_kv][max_pages]
     int32_t batch, max_pages, num_q_heads, num_kv_heads, head_dim, page_size, logical_page;
     int32_t q_dtype, kv_dtype;
+    int32_t aggregation;          // LSA_AGG_SUM | LSA_AGG_MAX
     int32_t n_ret;                // number of retrieval heads
     int32_t pages_per_block;      // physical pages per workgroup
     int32_t blocks_per_head;      // workgroups per (sequence, retrieval head)

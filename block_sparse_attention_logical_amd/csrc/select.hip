@@ -42,14 +42,14 @@ constexpr int kScoreThreads = 256;
 constexpr int kScoreMaxIter = 8;           // logical pages per lane group and workgroup
 constexpr int kMaxLogicalPerBlock = 1024;  // LDS slots for logical scores
 
-// Qp / Qn of this lane's channels, fp64.
+// Qp / Qn of this lane's channels over the group's query heads h0 .. h1-1, fp64.
 template <int C>
-__device__ __forceinline__ void load_q_pos_neg(const ScoreArgs &a, int b, int kv, int ch0,
+__device__ __forceinline__ void load_q_pos_neg(const ScoreArgs &a, int b, int kv, int ch0, int h0, int h1,
                                                 double (&qp)[C], double (&qn)[C]) {
     const int G = a.num_q_heads / a.num_kv_heads;
 #pragma unroll
     for (int c = 0; c < C; ++c) { qp[c] = 0.0; qn[c] = 0.0; }
-    for (int h = 0; h < G; ++h) {
+    for (int h = h0; h < h1; ++h) {
         const size_t row = ((size_t)b * a.num_q_heads + (size_t)kv * G + h) * a.head_dim + ch0;
         float x[C];
         if (a.q_dtype == LSA_BF16) {
@@ -156,7 +156,9 @@ __device__ __forceinline__ void current_page_minmax(const ScoreArgs &a, size_t p
 }
 
 // KV_DT: LSA_F32, LSA_BF16 (stats in that type) or LSA_INT4 (code stats).
-template <int KV_DT, int D>
+// AGG_MAX: the group's heads are scored one by one and their scores combined
+// by max; otherwise their sum is formed with one folded (Qp, Qn) pass.
+template <int KV_DT, int D, bool AGG_MAX>
 __global__ __launch_bounds__(kScoreThreads) void score_kernel(ScoreArgs a) {
     constexpr int EB = KV_DT == LSA_F32 ? 4 : (KV_DT == LSA_BF16 ? 2 : 1);
     using S = ScoreShape<EB, D>;
@@ -187,8 +189,7 @@ __global__ __launch_bounds__(kScoreThreads) void score_kernel(ScoreArgs a) {
         pools[it] = m < a.max_pages ? a.page_table[(size_t)b * a.max_pages + m] : 0;
     }
     const int L = a.seq_lens[b];
-    double qp[C], qn[C];
-    load_q_pos_neg<C>(a, b, kv, ch0, qp, qn);
+    const int G = a.num_q_heads / a.num_kv_heads;
     const int n_pages = (L + a.page_size - 1) / a.page_size;
     if (m0 >= n_pages) return;
     const int m1 = min(m0 + a.pages_per_block, n_pages);
@@ -221,79 +222,90 @@ __global__ __launch_bounds__(kScoreThreads) void score_kernel(ScoreArgs a) {
         }
     }
 
-    double qsum = 0.0;                            // int4 only: sum over all channels of Qp + Qn
-    if constexpr (KV_DT == LSA_INT4) {
-#pragma unroll
-        for (int c = 0; c < C; ++c) qsum += qp[c] + qn[c];
-        qsum = group_sum_d<LPL>(qsum);
-    }
-
-    // the current logical page, scored from its keys by one whole wavefront
-    if (j_cur >= j0 && j_cur < j1 && wave == ((j_cur - j0) % GROUPS) / LPP) {
-        const int m = j_cur / g;
-        const int pool = a.page_table[(size_t)b * a.max_pages + m];
+    // the current logical page's min / max, from its keys, by one whole wavefront
+    const bool own_cur = j_cur >= j0 && j_cur < j1 && wave == ((j_cur - j0) % GROUPS) / LPP;
+    float cmin[C], cmax[C];
+    uint32_t sz_cur = 0;
+    if (own_cur) {
+        const int pool = a.page_table[(size_t)b * a.max_pages + j_cur / g];
         const size_t hp = (size_t)pool * a.num_kv_heads + kv;
-        float kmin[C], kmax[C];
+        if constexpr (KV_DT == LSA_INT4) sz_cur = *reinterpret_cast<const uint32_t *>(a.k_sz + hp * 2);
         current_page_minmax<KV_DT, D, C, LPL, LPP>(a, hp * a.page_size * D, (j_cur % g) * a.logical_page,
-                                                   L - j_cur * a.logical_page, lane / LPL, ch0, kmin, kmax);
-        double c0 = 0.0, c1 = 0.0;
-#pragma unroll
-        for (int c = 0; c < C; ++c) {
-            c0 = fma(qp[c], (double)kmax[c], c0);
-            c1 = fma(qn[c], (double)kmin[c], c1);
-        }
-        double sj = group_sum_d<LPL>(c0 + c1);
-        if constexpr (KV_DT == LSA_INT4) {
-            const uint32_t sz = *reinterpret_cast<const uint32_t *>(a.k_sz + hp * 2);
-            sj = (double)fp16_bits_to_f32(uint16_t(sz)) * (sj - (double)fp16_bits_to_f32(uint16_t(sz >> 16)) * qsum);
-        }
-        if (lane == 0) s_log[j_cur - j0] = sj;
+                                                   L - j_cur * a.logical_page, lane / LPL, ch0, cmin, cmax);
     }
 
-    // S^j of every other logical page: one independent product chain per slot
-    double acc[IT];
-#pragma unroll
-    for (int it = 0; it < IT; ++it) {
-        double c0 = 0.0, c1 = 0.0;
+    // int4: S = s * (sum_i Qp c_max + Qn c_min - z * sum_i (Qp + Qn))
+    auto finish = [&](double dot, uint32_t sz, double qsum) {
+        if constexpr (KV_DT == LSA_INT4)
+            return (double)fp16_bits_to_f32(uint16_t(sz)) * (dot - (double)fp16_bits_to_f32(uint16_t(sz >> 16)) * qsum);
+        return dot;
+    };
+
+    // S^j of every logical page: one pass with the folded group (sum), or one
+    // pass per query head combined by max; each slot has its own product chains
+    double best[IT], best_cur = 0.0;
+    const int n_pass = AGG_MAX ? G : 1;
+    for (int hv = 0; hv < n_pass; ++hv) {
+        double qp[C], qn[C];
+        load_q_pos_neg<C>(a, b, kv, ch0, AGG_MAX ? hv : 0, AGG_MAX ? hv + 1 : G, qp, qn);
+        double qsum = 0.0;                        // int4 only: sum over all channels of Qp + Qn
         if constexpr (KV_DT == LSA_INT4) {
-            const uint32_t wd[4] = {st_lo[it].x, st_lo[it].y, st_lo[it].z, st_lo[it].w};
 #pragma unroll
-            for (int c = 0; c < C; ++c) {
-                const uint32_t byte = (wd[c / 4] >> (8 * (c % 4))) & 0xFFu;
-                c0 = fma(qp[c], (double)(byte >> 4), c0);
-                c1 = fma(qn[c], (double)(byte & 15u), c1);
-            }
-        } else {
-            const uint32_t wl[4] = {st_lo[it].x, st_lo[it].y, st_lo[it].z, st_lo[it].w};
-            const uint32_t wh[4] = {st_hi[it].x, st_hi[it].y, st_hi[it].z, st_hi[it].w};
-#pragma unroll
-            for (int c = 0; c < C; ++c) {
-                float kmin, kmax;
-                if constexpr (KV_DT == LSA_BF16) {
-                    kmin = (c & 1) ? bf16_hi(wl[c / 2]) : bf16_lo(wl[c / 2]);
-                    kmax = (c & 1) ? bf16_hi(wh[c / 2]) : bf16_lo(wh[c / 2]);
-                } else {
-                    kmin = __uint_as_float(wl[c]);
-                    kmax = __uint_as_float(wh[c]);
-                }
-                c0 = fma(qp[c], (double)kmax, c0);
-                c1 = fma(qn[c], (double)kmin, c1);
-            }
+            for (int c = 0; c < C; ++c) qsum += qp[c] + qn[c];
+            qsum = group_sum_d<LPL>(qsum);
         }
-        acc[it] = c0 + c1;
-    }
+        if (own_cur) {
+            double c0 = 0.0, c1 = 0.0;
 #pragma unroll
-    for (int it = 0; it < IT; ++it) acc[it] = group_sum_d<LPL>(acc[it]);
+            for (int c = 0; c < C; ++c) {
+                c0 = fma(qp[c], (double)cmax[c], c0);
+                c1 = fma(qn[c], (double)cmin[c], c1);
+            }
+            const double sj = finish(group_sum_d<LPL>(c0 + c1), sz_cur, qsum);
+            best_cur = hv == 0 ? sj : fmax(best_cur, sj);
+        }
+        double acc[IT];
+#pragma unroll
+        for (int it = 0; it < IT; ++it) {
+            double c0 = 0.0, c1 = 0.0;
+            if constexpr (KV_DT == LSA_INT4) {
+                const uint32_t wd[4] = {st_lo[it].x, st_lo[it].y, st_lo[it].z, st_lo[it].w};
+#pragma unroll
+                for (int c = 0; c < C; ++c) {
+                    const uint32_t byte = (wd[c / 4] >> (8 * (c % 4))) & 0xFFu;
+                    c0 = fma(qp[c], (double)(byte >> 4), c0);
+                    c1 = fma(qn[c], (double)(byte & 15u), c1);
+                }
+            } else {
+                const uint32_t wl[4] = {st_lo[it].x, st_lo[it].y, st_lo[it].z, st_lo[it].w};
+                const uint32_t wh[4] = {st_hi[it].x, st_hi[it].y, st_hi[it].z, st_hi[it].w};
+#pragma unroll
+                for (int c = 0; c < C; ++c) {
+                    float kmin, kmax;
+                    if constexpr (KV_DT == LSA_BF16) {
+                        kmin = (c & 1) ? bf16_hi(wl[c / 2]) : bf16_lo(wl[c / 2]);
+                        kmax = (c & 1) ? bf16_hi(wh[c / 2]) : bf16_lo(wh[c / 2]);
+                    } else {
+                        kmin = __uint_as_float(wl[c]);
+                        kmax = __uint_as_float(wh[c]);
+                    }
+                    c0 = fma(qp[c], (double)kmax, c0);
+                    c1 = fma(qn[c], (double)kmin, c1);
+                }
+            }
+            acc[it] = c0 + c1;
+        }
+#pragma unroll
+        for (int it = 0; it < IT; ++it) {
+            const double sj = finish(group_sum_d<LPL>(acc[it]), szw[it], qsum);
+            best[it] = hv == 0 ? sj : fmax(best[it], sj);
+        }
+    }
+    if (own_cur && lane == 0) s_log[j_cur - j0] = best_cur;
 #pragma unroll
     for (int it = 0; it < IT; ++it) {
         const int j = j0 + lg + it * GROUPS;
-        if (j < j1 && j != j_cur && lane % LPL == 0) {
-            double sj = acc[it];
-            if constexpr (KV_DT == LSA_INT4)
-                sj = (double)fp16_bits_to_f32(uint16_t(szw[it])) *
-                     (sj - (double)fp16_bits_to_f32(uint16_t(szw[it] >> 16)) * qsum);
-            s_log[j - j0] = sj;
-        }
+        if (j < j1 && j != j_cur && lane % LPL == 0) s_log[j - j0] = best[it];
     }
     __syncthreads();
     // P_m = max over the logical pages of physical page m
@@ -443,11 +455,17 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(TopkArgs a) {
     }
 }
 
+template <int KV_DT, bool AGG_MAX>
+hipError_t launch_score_agg(const ScoreArgs &a, unsigned grid, hipStream_t s) {
+    if (a.head_dim == 128) hipLaunchKernelGGL((score_kernel<KV_DT, 128, AGG_MAX>), dim3(grid), dim3(kScoreThreads), 0, s, a);
+    else hipLaunchKernelGGL((score_kernel<KV_DT, 64, AGG_MAX>), dim3(grid), dim3(kScoreThreads), 0, s, a);
+    return hipGetLastError();
+}
+
 template <int KV_DT>
 hipError_t launch_score_dt(const ScoreArgs &a, unsigned grid, hipStream_t s) {
-    if (a.head_dim == 128) hipLaunchKernelGGL((score_kernel<KV_DT, 128>), dim3(grid), dim3(kScoreThreads), 0, s, a);
-    else hipLaunchKernelGGL((score_kernel<KV_DT, 64>), dim3(grid), dim3(kScoreThreads), 0, s, a);
-    return hipGetLastError();
+    return a.aggregation == LSA_AGG_MAX ? launch_score_agg<KV_DT, true>(a, grid, s)
+                                        : launch_score_agg<KV_DT, false>(a, grid, s);
 }
 
 }  // namespace

@@ -16,6 +16,7 @@ import torch
 
 F32, BF16, INT4 = 0, 1, 2
 RETRIEVAL, STREAMING = 0, 1
+AGG_SUM, AGG_MAX = 0, 1
 
 LSA_OK = 0
 LSA_ERR_INVALID_ARG = -1
@@ -78,6 +79,7 @@ class LsaHeads(ctypes.Structure):
         ("local_tokens", ctypes.c_int32),
         ("sink_blocks", ctypes.c_int32),
         ("local_blocks", ctypes.c_int32),
+        ("score_aggregation", ctypes.c_int32),
     ]
 
 
@@ -182,12 +184,13 @@ class Heads:
     local_tokens: int = 1
     sink_blocks: int = 0
     local_blocks: int = 1
+    score_aggregation: int = AGG_SUM
     _buf: object = field(default=None, repr=False)
 
     def desc(self) -> LsaHeads:
         self._buf = (ctypes.c_uint8 * len(self.head_kind))(*[int(x) for x in self.head_kind])
         return LsaHeads(ctypes.cast(self._buf, ctypes.c_void_p), self.num_q_heads, self.sink_tokens,
-                        self.local_tokens, self.sink_blocks, self.local_blocks)
+                        self.local_tokens, self.sink_blocks, self.local_blocks, self.score_aggregation)
 
 
 def seqs_desc(page_table: torch.Tensor, seq_lens: torch.Tensor) -> LsaSeqs:

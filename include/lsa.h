@@ -84,6 +84,11 @@ typedef int32_t lsa_status;
 #define LSA_RETRIEVAL_HEAD 0
 #define LSA_STREAMING_HEAD 1
 
+/* How the page scores of the query heads that share one KV head combine
+ * (lsa_heads.score_aggregation): their sum (the default), or their maximum. */
+#define LSA_AGG_SUM 0
+#define LSA_AGG_MAX 1
+
 /* [host] descriptor of the paged KV pool (layout above). */
 typedef struct lsa_kv {
     int32_t kv_dtype;       /* LSA_F32 | LSA_BF16 | LSA_INT4                      */
@@ -118,6 +123,8 @@ typedef struct lsa_heads {
     int32_t local_tokens;       /* ... or t - p < local_tokens are attended       */
     int32_t sink_blocks;        /* prefill Lambda, in tiles: tiles c < sink_blocks */
     int32_t local_blocks;       /* ... or a - c < local_blocks (diagonal counts)  */
+    int32_t score_aggregation;  /* LSA_AGG_SUM (0) or LSA_AGG_MAX: how the G heads'
+                                   page scores combine in lsa_select_pages        */
 } lsa_heads;
 
 /* Bytes of the logical-page statistics pool that matches `kv`:
@@ -158,8 +165,10 @@ lsa_status lsa_select_pages_workspace(const lsa_kv *kv, const lsa_seqs *seqs,
  * and leaves `selected` unchanged (the previous selection is reused).  For
  * each sequence b and retrieval KV head kv, with the group's queries
  * q_h (h = kv*G .. kv*G+G-1):
- *   S^j  = sum_h sum_i max(q_h[i] * kmax^j[i], q_h[i] * kmin^j[i])   for every
- *          logical page j holding a valid token (GQA heads summed);
+ *   S_h^j = sum_i max(q_h[i] * kmax^j[i], q_h[i] * kmin^j[i])   for every
+ *          logical page j holding a valid token;
+ *   S^j  = sum_h S_h^j (heads->score_aggregation == LSA_AGG_SUM, the default)
+ *          or max_h S_h^j (LSA_AGG_MAX);
  *   P_m  = max over the logical pages j of physical page m (j / g == m);
  *   selected[b][kv][0..K-1] = the K = token_budget / page_size pages m of
  *          largest P_m, ties to the lower m, in ascending m, padded with -1

@@ -201,22 +201,33 @@ def page_code_stats(codes: np.ndarray, logical_page: int):
 # O3: query-aware logical-page score       ([LS-X] 動的スパーシティ, the S^j equation)
 # ---------------------------------------------------------------------------
 
-def logical_scores(q_group: np.ndarray, kmin: np.ndarray, kmax: np.ndarray) -> np.ndarray:
-    """S^j = sum over the group's query heads h and channels i of
-    max(q_h[i] * kmax^j[i], q_h[i] * kmin^j[i]).
+SUM, MAX = "sum", "max"
 
-    q_group: [G][D] float64, the query heads that share one KV head.  With
-    G = 1 this is the equation of [LS-X] as printed; for GQA the per-head
-    scores are summed (reading Z1).  kmin, kmax: [n][D].  Returns [n] float64.
+
+def logical_scores(q_group: np.ndarray, kmin: np.ndarray, kmax: np.ndarray, aggregation: str = SUM) -> np.ndarray:
+    """S^j of every logical page for one GQA group.
+
+    For one query head h the score is the equation of [LS-X] as printed,
+    S_h^j = sum over channels i of max(q_h[i] * kmax^j[i], q_h[i] * kmin^j[i]).
+    The heads of a group share one selection; their scores are combined by
+    `aggregation`: "sum" adds them (reading Z1, the default), "max" takes the
+    largest.  With G = 1 both are the printed equation.
+
+    q_group: [G][D] float64, the query heads that share one KV head.
+    kmin, kmax: [n][D].  Returns [n] float64.
     """
     q = np.asarray(q_group, dtype=np.float64)
     n = kmin.shape[0]
-    out = np.zeros(n)
+    per_head = np.zeros((q.shape[0], n))
     for h in range(q.shape[0]):
         a = q[h][None, :] * kmax          # [n][D]
         b = q[h][None, :] * kmin
-        out += np.sum(np.maximum(a, b), axis=1)
-    return out
+        per_head[h] = np.sum(np.maximum(a, b), axis=1)
+    if aggregation == SUM:
+        return per_head.sum(axis=0)
+    if aggregation == MAX:
+        return per_head.max(axis=0)
+    raise ValueError(f"unknown aggregation {aggregation!r}")
 
 
 # ---------------------------------------------------------------------------
@@ -250,9 +261,9 @@ def topk_pages(phys: np.ndarray, k: int) -> np.ndarray:
     return out
 
 
-def select_pages(q_group, kmin, kmax, g: int, k: int) -> np.ndarray:
+def select_pages(q_group, kmin, kmax, g: int, k: int, aggregation: str = SUM) -> np.ndarray:
     """O3 -> O4 -> O5 for one (sequence, retrieval KV head)."""
-    return topk_pages(physical_scores(logical_scores(q_group, kmin, kmax), g), k)
+    return topk_pages(physical_scores(logical_scores(q_group, kmin, kmax, aggregation), g), k)
 
 
 # ---------------------------------------------------------------------------
@@ -306,6 +317,7 @@ class DecodeSpec:
     sink_tokens: int
     local_tokens: int
     scale: Optional[float] = None   # softmax scale; None -> 1/sqrt(D)
+    aggregation: str = SUM          # how a GQA group's per-head page scores combine
 
 
 def decode_step(spec: DecodeSpec, q: np.ndarray, keys: Sequence[np.ndarray],
@@ -336,7 +348,7 @@ def decode_step(spec: DecodeSpec, q: np.ndarray, keys: Sequence[np.ndarray],
         if spec.head_kind[kv] == RETRIEVAL:
             if reselect:
                 kmin, kmax = page_stats(keys[kv], spec.logical_page)
-                sel[kv] = select_pages(group, kmin, kmax, g, K)
+                sel[kv] = select_pages(group, kmin, kmax, g, K, spec.aggregation)
             mask = attended_retrieval(t, sel[kv], spec.page_size)
         else:
             mask = attended_streaming(t, spec.sink_tokens, spec.local_tokens)

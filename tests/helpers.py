@@ -33,9 +33,9 @@ def kv_pool(w) -> lsa.KVPool:
                       w.k_sz, w.v_sz)
 
 
-def heads(w) -> lsa.Heads:
+def heads(w, aggregation: int = lsa.AGG_SUM) -> lsa.Heads:
     return lsa.Heads(w.head_kind, w.num_q_heads, getattr(w, "sink_tokens", 0), getattr(w, "local_tokens", 1),
-                     w.sink_blocks, w.local_blocks)
+                     w.sink_blocks, w.local_blocks, aggregation)
 
 
 def seq_pool(w, b: int, kv: int, length: int) -> O.Pool:
@@ -57,6 +57,10 @@ def seq_kv(w, b: int, kv: int, length: int):
     return pool.keys(table, 0, length), pool.values(table, 0, length)
 
 
-def oracle_spec(w) -> O.DecodeSpec:
+AGG_NAME = {lsa.AGG_SUM: O.SUM, lsa.AGG_MAX: O.MAX}
+
+
+def oracle_spec(w, aggregation: int = lsa.AGG_SUM) -> O.DecodeSpec:
     return O.DecodeSpec(w.num_q_heads, w.num_kv_heads, list(w.head_kind), w.logical_page, w.page_size,
-                        w.token_budget, w.reuse_interval, w.sink_tokens, w.local_tokens)
+                        w.token_budget, w.reuse_interval, w.sink_tokens, w.local_tokens,
+                        aggregation=AGG_NAME[aggregation])

@@ -127,6 +127,9 @@ def test_select_validation(lib):
     assert select(lib, heads=heads_desc(hq=8 * 17)) == lsa.LSA_ERR_UNSUPPORTED
     assert select(lib, heads=heads_desc(kinds=(0, 1, 2, 1, 0, 1, 0, 1))) == lsa.LSA_ERR_INVALID_ARG
     assert select(lib, heads=heads_desc(local=0)) == lsa.LSA_ERR_INVALID_ARG
+    bad_agg = heads_desc()
+    bad_agg.score_aggregation = 2
+    assert select(lib, heads=bad_agg) == lsa.LSA_ERR_INVALID_ARG
     assert select(lib, seqs=seqs_desc(max_pages=0)) == lsa.LSA_ERR_UNSUPPORTED
     assert select(lib, seqs=lsa.LsaSeqs(2, 10, None, FAKE)) == lsa.LSA_ERR_INVALID_ARG
 

@@ -20,10 +20,10 @@ def tol(w):
 class Runner:
     """Drives the decode window through the C ABI the way a serving loop does."""
 
-    def __init__(self, w):
+    def __init__(self, w, agg=lsa.AGG_SUM):
         self.w = w
         self.kv = H.kv_pool(w)
-        self.hd = H.heads(w)
+        self.hd = H.heads(w, agg)
         self.K = w.token_budget // w.page_size
         lens0 = torch.tensor(w.ctx, dtype=torch.int32, device=DEV)
         self.stats = torch.zeros(lsa.page_stats_bytes(self.kv), dtype=torch.uint8, device=DEV)
@@ -49,10 +49,10 @@ class Runner:
         return out
 
 
-def oracle_window(w, b, kv_heads=None):
+def oracle_window(w, b, kv_heads=None, agg=lsa.AGG_SUM):
     """Outputs of every decode step of sequence b from the oracle, following
     the step order of the reusable selection."""
-    spec = H.oracle_spec(w)
+    spec = H.oracle_spec(w, agg)
     G = w.num_q_heads // w.num_kv_heads
     Lmax = w.ctx[b] + w.window
     kvs = range(w.num_kv_heads) if kv_heads is None else kv_heads
@@ -72,7 +72,7 @@ def oracle_window(w, b, kv_heads=None):
             if spec.head_kind[kv] == O.RETRIEVAL:
                 if i % w.reuse_interval == 0:
                     kmin, kmax = O.page_stats(keys[kv][:L], w.logical_page)
-                    sel[kv] = O.select_pages(group, kmin, kmax, w.page_size // w.logical_page, K)
+                    sel[kv] = O.select_pages(group, kmin, kmax, w.page_size // w.logical_page, K, spec.aggregation)
                 mask = O.attended_retrieval(t, sel[kv], w.page_size)
             else:
                 mask = O.attended_streaming(t, w.sink_tokens, w.local_tokens)
@@ -83,12 +83,12 @@ def oracle_window(w, b, kv_heads=None):
     return outs
 
 
-def check_window(w, kv_heads=None, batches=None):
-    r = Runner(w)
+def check_window(w, kv_heads=None, batches=None, agg=lsa.AGG_SUM):
+    r = Runner(w, agg)
     gpu = [H.to_f64(r.step(i)) for i in range(w.window)]
     worst = 0.0
     for b in (range(w.batch) if batches is None else batches):
-        ref = oracle_window(w, b, kv_heads)
+        ref = oracle_window(w, b, kv_heads, agg)
         for i in range(w.window):
             G = w.num_q_heads // w.num_kv_heads
             heads = range(w.num_q_heads) if kv_heads is None else [kv * G + h for kv in kv_heads for h in range(G)]
@@ -161,6 +161,14 @@ def test_decode_budget_covers_everything_is_dense():
 def test_decode_single_token_sequence():
     w = W.make_decode(2, DEV, batch=2, ctx=[0, 0], window=2)
     check_window(w)
+
+
+@pytest.mark.parametrize("cfg", [1, 2, 5])
+def test_decode_window_max_aggregation(cfg):
+    """The decode window with page scores combined by max over the GQA group."""
+    # 6000 and 9000 tokens span 94 and 141 pages, above the 64-page budget.
+    w = W.make_decode(cfg, DEV) if cfg == 1 else W.make_decode(cfg, DEV, batch=2, ctx=[6000, 9000])
+    check_window(w, agg=lsa.AGG_MAX)
 
 
 def test_decode_deterministic():

@@ -107,9 +107,9 @@ def test_stats_retrieval_heads_only():
 # selection
 # ---------------------------------------------------------------------------
 
-def run_select(w, step, lens, stats=None, selected=None, decode_step=0):
+def run_select(w, step, lens, stats=None, selected=None, decode_step=0, agg=lsa.AGG_SUM):
     kv = H.kv_pool(w)
-    hd = H.heads(w)
+    hd = H.heads(w, agg)
     seq_lens = torch.tensor(lens, dtype=torch.int32, device=DEV)
     if stats is None:
         stats = build_stats(w, lens)
@@ -123,25 +123,25 @@ def run_select(w, step, lens, stats=None, selected=None, decode_step=0):
     return selected
 
 
-def oracle_selection(w, step, b, kv, L):
+def oracle_selection(w, step, b, kv, L, agg=lsa.AGG_SUM):
     G = w.num_q_heads // w.num_kv_heads
     keys, _ = H.seq_kv(w, b, kv, L)
     kmin, kmax = O.page_stats(keys, w.logical_page)
     q = H.to_f64(w.q[step, b, kv * G:(kv + 1) * G])
-    S = O.logical_scores(q, kmin, kmax)
+    S = O.logical_scores(q, kmin, kmax, H.AGG_NAME[agg])
     P = O.physical_scores(S, w.page_size // w.logical_page)
     K = w.token_budget // w.page_size
     return O.topk_pages(P, K), P
 
 
-def check_selection(w, step, lens, selected, pairs=None, report=None):
+def check_selection(w, step, lens, selected, pairs=None, report=None, agg=lsa.AGG_SUM):
     K = w.token_budget // w.page_size
     sel = selected.cpu().numpy()
     for b, L in enumerate(lens):
         for kv in range(w.num_kv_heads):
             if w.head_kind[kv] != 0 or (pairs is not None and (b, kv) not in pairs):
                 continue
-            expect, P = oracle_selection(w, step, b, kv, L)
+            expect, P = oracle_selection(w, step, b, kv, L, agg)
             if report is not None and len(P) > K:
                 s = np.sort(P)[::-1]
                 report.append(abs(s[K - 1] - s[K]) / max(1.0, abs(s[K - 1])))
@@ -159,6 +159,27 @@ def test_select_matches_oracle(name, make):
         for kv in range(w.num_kv_heads):
             if w.head_kind[kv]:
                 assert bool((sel[:, kv] == -7).all())
+
+
+@pytest.mark.parametrize("name,make", CASES, ids=[c[0] for c in CASES])
+def test_select_max_aggregation_matches_oracle(name, make):
+    """score_aggregation = LSA_AGG_MAX: the group's per-head page scores are
+    combined by max; the selection still matches the oracle bit for bit."""
+    w = make()
+    lens = [c + 1 for c in w.ctx]
+    sel = run_select(w, 0, lens, agg=lsa.AGG_MAX)
+    check_selection(w, 0, lens, sel, agg=lsa.AGG_MAX)
+
+
+def test_select_max_and_sum_aggregation_differ():
+    """The two aggregations are different rankings on the bf16 workload (so the
+    max-aggregation parity test above is not the sum test in disguise)."""
+    w = W.make_decode(2, DEV, batch=2, ctx=[20000, 30000])      # 313 and 469 pages for K = 64
+    lens = [c + 1 for c in w.ctx]
+    a = run_select(w, 0, lens, agg=lsa.AGG_SUM).cpu().numpy()
+    m = run_select(w, 0, lens, agg=lsa.AGG_MAX).cpu().numpy()
+    ret = [kv for kv in range(w.num_kv_heads) if w.head_kind[kv] == 0]
+    assert any(not np.array_equal(a[b, kv], m[b, kv]) for b in range(w.batch) for kv in ret)
 
 
 def test_select_reuse_keeps_previous_selection():

@@ -56,6 +56,28 @@ def test_score_mutants_caught(mutant):
     assert caught
 
 
+def _agg(per_head_fn):
+    """A logical_scores stand-in whose "max" path is per_head_fn (the "sum"
+    path is the oracle's)."""
+    def f(q, kmin, kmax, aggregation="sum"):
+        if aggregation == "sum":
+            return O.logical_scores(q, kmin, kmax)
+        q = np.asarray(q, float)
+        per = np.array([np.sum(np.maximum(q[h] * kmax, q[h] * kmin), axis=1) for h in range(q.shape[0])])
+        return per_head_fn(per)
+    return f
+
+
+@pytest.mark.parametrize("mutant", [
+    _agg(lambda per: per.sum(axis=0)),            # sums although max was asked for
+    _agg(lambda per: per.mean(axis=0)),           # mean of the heads
+    _agg(lambda per: per[0]),                     # first head only
+    _agg(lambda per: per.min(axis=0)),            # min for max
+])
+def test_score_max_aggregation_mutants_caught(mutant):
+    assert _fails(P.pin_score_max_aggregation, mutant, O.page_stats)
+
+
 # --- stats -----------------------------------------------------------------
 
 def stats_shifted(keys, n_l):

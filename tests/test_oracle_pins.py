@@ -73,6 +73,37 @@ def pin_score_special_cases(logical_scores):
     assert logical_scores(q2, kmin2, kmax2)[0] == 4.0 + 1.75
 
 
+def pin_score_max_aggregation(logical_scores, page_stats, seed=21):
+    """aggregation="max": the score is the largest over the group's heads of
+    each head's box support (enumeration of the box corners at D <= 8); it
+    upper-bounds every head's q_h . k for every key of its page (so each head
+    still attends to a page whose bound covers it); with one head it is the
+    printed equation (equal to the sum); a hand example with G = 2."""
+    rng = np.random.default_rng(seed)
+    for D, G, n_tok in [(5, 2, 7), (8, 3, 16), (6, 4, 2)]:
+        keys = rng.standard_normal((n_tok, D))
+        q = rng.standard_normal((G, D))
+        kmin, kmax = keys.min(0, keepdims=True), keys.max(0, keepdims=True)
+        corners = np.array(list(itertools.product(*[(kmin[0, i], kmax[0, i]) for i in range(D)])))
+        expect = max(np.max(corners @ q[h]) for h in range(G))
+        got = logical_scores(q, kmin, kmax, "max")[0]
+        assert abs(got - expect) <= 1e-12 * max(1.0, abs(expect)), (D, G, got, expect)
+    keys = rng.standard_normal((16 * 5 + 3, 20)) * rng.uniform(0.5, 3, size=20)
+    q = rng.standard_normal((4, 20))
+    kmin, kmax = page_stats(keys, 16)
+    S = logical_scores(q, kmin, kmax, "max")
+    for p in range(keys.shape[0]):
+        for h in range(4):
+            assert S[p // 16] >= float(q[h] @ keys[p]) - 1e-9, (p, h)
+    q1 = rng.standard_normal((1, 20))
+    assert np.array_equal(logical_scores(q1, kmin, kmax, "max"), logical_scores(q1, kmin, kmax, "sum"))
+    kmin2 = np.array([[-1.0, 2.0]])
+    kmax2 = np.array([[3.0, 5.0]])
+    q2 = np.array([[2.0, -1.0], [-0.5, 0.25]])
+    # head 0: 6 - 2 = 4 ; head 1: 0.5 + 1.25 = 1.75 -> max 4
+    assert logical_scores(q2, kmin2, kmax2, "max")[0] == 4.0
+
+
 def pin_stats_brute_force(page_stats):
     """Channel min/max per 16-token logical page equal a scalar loop; every
     key lies inside its page's box; the ragged tail covers only valid tokens."""
@@ -228,6 +259,10 @@ def test_score_upper_bound():
 
 def test_score_special_cases():
     pin_score_special_cases(O.logical_scores)
+
+
+def test_score_max_aggregation():
+    pin_score_max_aggregation(O.logical_scores, O.page_stats)
 
 
 def test_stats_brute_force():
