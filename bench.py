@@ -16,6 +16,11 @@ graph and replayed; the timed region covers whole cycles.
 
 Prefill.  One call of the block-sparse prefill over 131072 tokens, 32 query
 heads, 8 KV heads (4 streaming with 1 sink + 16 local tiles).
+
+Variants (the default run is the Llama-3-8B-shaped layer with R = 4 and the
+group's page scores summed): --workload llama2-7b-mha runs the multi-head
+layer (32 KV heads, group size 1) in both legs, --reuse R sets the selection
+interval, --aggregation max combines the group's per-head page scores by max.
 """
 from __future__ import annotations
 
@@ -33,10 +38,20 @@ sys.path.insert(0, ROOT)
 PEAK_HBM = 8.0e12          # MI355X HBM3E, bytes/s
 PEAK_BF16 = 2.5e15         # MI355X dense bf16 MFMA, flop/s
 
+# workload name -> (decode config, prefill config, model shape)
+WORKLOADS = {
+    "llama3-8b": (2, 3, "Llama-3-8B-shaped attention layer"),
+    "llama2-7b-mha": (6, 7, "Llama-2-7B-shaped (multi-head) attention layer"),
+}
+
 
 def parse():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--workload", choices=sorted(WORKLOADS), default="llama3-8b")
+    ap.add_argument("--reuse", type=int, default=None, help="selection reuse interval R (default: 4)")
+    ap.add_argument("--aggregation", choices=["sum", "max"], default="sum",
+                    help="how a KV head's query group combines its page scores")
     ap.add_argument("--steps", type=int, default=640, help="timed decode steps (rounded up to whole cycles)")
     ap.add_argument("--warmup", type=int, default=64, help="untimed decode steps")
     ap.add_argument("--replicas", type=int, default=8, help="KV pool replicas (layers) cycled through")
@@ -102,11 +117,14 @@ def counters_for(kernel_tag, source_file, launch_bytes):
 
 def bench_decode(args, torch, lsa, W):
     dev = "cuda"
-    w = W.make_decode(2, dev)
+    cfg = WORKLOADS[args.workload][0]
+    R = args.reuse or W.DECODE_CONFIGS[cfg]["reuse_interval"]
+    w = W.make_decode(cfg, dev, window=max(R, W.DECODE_CONFIGS[cfg]["window"]))
+    w.reuse_interval = R
     B, Hq, Hkv, D, NP = w.batch, w.num_q_heads, w.num_kv_heads, w.head_dim, w.page_size
-    R = w.reuse_interval
     K = w.token_budget // NP
-    hd = lsa.Heads(w.head_kind, Hq, w.sink_tokens, w.local_tokens, w.sink_blocks, w.local_blocks)
+    agg = lsa.AGG_MAX if args.aggregation == "max" else lsa.AGG_SUM
+    hd = lsa.Heads(w.head_kind, Hq, w.sink_tokens, w.local_tokens, w.sink_blocks, w.local_blocks, agg)
     nrep = max(1, args.replicas)
     layers = []
     for r in range(nrep):
@@ -246,11 +264,12 @@ def bench_decode(args, torch, lsa, W):
     step_bytes = launch_bytes + sel_bytes
     tok_s = B * steps / elapsed
     src = os.path.join(ROOT, "block_sparse_attention_logical_amd", "csrc", "decode.hip")
+    default = args.workload == "llama3-8b" and R == 4      # the workload the counter summary covers
     return dict(
-        w=w, steps=steps, elapsed=elapsed, tok_s=tok_s, ms_per_step=elapsed / steps * 1e3,
+        w=w, agg=args.aggregation, steps=steps, elapsed=elapsed, tok_s=tok_s, ms_per_step=elapsed / steps * 1e3,
         step_bytes=step_bytes, launch_bytes=launch_bytes, kernel_avg=kernel_avg,
         kernel_p50=kt[len(kt) // 2], timing=timing,
-        traffic=counters_for("decode_attn_cfg2", src, launch_bytes),
+        traffic=counters_for("decode_attn_cfg2", src, launch_bytes) if default else None,
     )
 
 
@@ -260,7 +279,7 @@ def bench_decode(args, torch, lsa, W):
 
 def bench_prefill(args, torch, lsa, W, O):
     dev = "cuda"
-    p = W.make_prefill(3, dev)
+    p = W.make_prefill(WORKLOADS[args.workload][1], dev)
     kv = lsa.KVPool(p.dtype, p.k, p.v, p.num_kv_heads, p.head_dim, p.page_size, p.logical_page, p.num_pages)
     hd = lsa.Heads(p.head_kind, p.num_q_heads, 0, 1, p.sink_blocks, p.local_blocks)
     out = torch.empty_like(p.q)
@@ -296,10 +315,12 @@ def bench_prefill(args, torch, lsa, W, O):
         tc.append(a.elapsed_time(b) / 1e3)
     t_causal = min(tc) if tc else float("nan")
     causal_flop = dense * 4 * 64 * 64 * p.head_dim
+    shape = dict(T=p.seq_len, Hq=p.num_q_heads, Hkv=p.num_kv_heads, D=p.head_dim,
+                 n_str=sum(1 for x in p.head_kind if x == 1), sink=p.sink_blocks, local=p.local_blocks)
     del out, p
     torch.cuda.empty_cache()
     return dict(seconds=t, flop=flop, tiles=tiles, dense_tiles=dense, tflops=flop / t / 1e12,
-                causal_seconds=t_causal, causal_tflops=causal_flop / t_causal / 1e12)
+                causal_seconds=t_causal, causal_tflops=causal_flop / t_causal / 1e12, **shape)
 
 
 # ---------------------------------------------------------------------------
@@ -316,7 +337,8 @@ def cpu_baseline(dec, torch, O, budget_s):
     w = dec["w"]
     G = w.num_q_heads // w.num_kv_heads
     spec = O.DecodeSpec(w.num_q_heads, w.num_kv_heads, list(w.head_kind), w.logical_page, w.page_size,
-                        w.token_budget, w.reuse_interval, w.sink_tokens, w.local_tokens)
+                        w.token_budget, w.reuse_interval, w.sink_tokens, w.local_tokens,
+                        aggregation=O.MAX if dec["agg"] == "max" else O.SUM)
     done = 0
     t_total = 0.0
     i = 0
@@ -341,8 +363,8 @@ def cpu_baseline(dec, torch, O, budget_s):
     # one selection step per sequence; a window of R steps selects once, so
     # the steady-state cost per token is below this selection-step cost
     return dict(value=done / t_total, unit="tokens/s", cores=threads, kind="oracle",
-                sample=f"{done} decode steps with page selection, one sequence each (64K context, all 8 KV heads, "
-                       f"fp64 NumPy), {t_total:.1f} s")
+                sample=f"{done} decode steps with page selection, one sequence each ({w.ctx[0] // 1024}K context, "
+                       f"all {w.num_kv_heads} KV heads, fp64 NumPy), {t_total:.1f} s")
 
 
 def main():
@@ -373,6 +395,9 @@ def main():
 
     w = dec["w"]
     achieved = dec["launch_bytes"] / dec["kernel_avg"]
+    model = WORKLOADS[args.workload][2]
+    n_str = sum(1 for x in w.head_kind if x == 1)
+    G = w.num_q_heads // w.num_kv_heads
     line = {
         "metric": "sparse decode attn tokens/s + HBM GB/s at 64K; prefill sparse TFLOP/s at 128K",
         "value": round(dec["tok_s"], 1),
@@ -385,11 +410,14 @@ def main():
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "bf16",
-        "data": "synthetic (seeded; shapes of the LServe Llama-3-8B decode workload)",
+        "data": f"synthetic (seeded; shapes of the LServe {model.split('-shaped')[0]} decode workload)",
         "config": {
-            "workload": "decode, one Llama-3-8B-shaped attention layer: B=8, context 65536, 32 q heads / 8 KV heads "
-                        "(4 streaming: sink 64 + local 1024 tokens), D=128, N_L=16, N_P=64, token budget 4096, "
-                        "reuse interval 4; one step = selection (every 4th step) + attention with the stats refresh",
+            "workload": f"decode, one {model}: B={w.batch}, context {w.ctx[0]}, {w.num_q_heads} q heads / "
+                        f"{w.num_kv_heads} KV heads ({n_str} streaming: sink {w.sink_tokens} + local "
+                        f"{w.local_tokens} tokens), D={w.head_dim}, N_L={w.logical_page}, N_P={w.page_size}, "
+                        f"token budget {w.token_budget}, reuse interval {w.reuse_interval}, group page scores "
+                        f"combined by {args.aggregation}; one step = selection (every {w.reuse_interval}th step) "
+                        f"+ attention with the stats refresh",
             "global_batch": w.batch, "seq_len": w.ctx[0], "parallelism": "none (1 GPU)",
             "kv_replicas": args.replicas, "timing": dec["timing"],
         },
@@ -407,8 +435,9 @@ def main():
     }
     if pre is not None:
         line["prefill"] = {
-            "workload": "prefill, 131072 tokens, 32 q heads / 8 KV heads (4 causal retrieval, 4 streaming with "
-                        "1 sink + 16 local tiles), D=128, 64x64 tiles, bf16",
+            "workload": f"prefill, {pre['T']} tokens, {pre['Hq']} q heads / {pre['Hkv']} KV heads "
+                        f"({pre['Hkv'] - pre['n_str']} causal retrieval, {pre['n_str']} streaming with "
+                        f"{pre['sink']} sink + {pre['local']} local tiles), D={pre['D']}, 64x64 tiles, bf16",
             "ms": round(pre["seconds"] * 1e3, 3),
             "tflops": round(pre["tflops"], 1),
             "nonempty_tile_heads": pre["tiles"],

@@ -18,8 +18,10 @@ config id, on the device the pool is built on):
   7. keys, page chunk by page chunk: N(0, 1), outlier channels x8, needles
      written over their slots, then int4 storage;
   8. values, page chunk by page chunk: N(0, 1), then int4 storage.
-Prefill (config 3): head classes, then per-head scales U[0.5, 2] for q, k and
-v, then q, k, v ~ N(0, 1) * scale.
+Prefill (configs 3 and 7): head classes, then per-head scales U[0.5, 2] for
+q, k and v, then q, k, v ~ N(0, 1) * scale.
+Configs 6 (decode) and 7 (prefill) are multi-head attention (32 query heads,
+32 KV heads, group size 1) with the other settings of configs 2 and 3.
 
 int4 storage (KV4): per (pool page, KV head, tensor) scale s = fp16 of
 (max - min) / 15 (at least 2^-10) and zero point z = round(16 * (-min / s)) / 16
@@ -98,7 +100,7 @@ class PrefillWorkload:
 
 
 # ---------------------------------------------------------------------------
-# config table (the five workloads)
+# config table
 # ---------------------------------------------------------------------------
 
 DECODE_CONFIGS = {
@@ -114,12 +116,19 @@ DECODE_CONFIGS = {
     5: dict(dtype=INT4, batch=16, num_q_heads=32, num_kv_heads=8, head_dim=128, logical_page=16, page_size=64,
             token_budget=4096, reuse_interval=4, sink_tokens=64, local_tokens=1024, sink_blocks=1, local_blocks=16,
             ctx=262144, window=4, permute=False, outliers=True, needles=8),
+    # multi-head attention (Llama-2-7B-shaped layer: 32 query heads, each its own KV head)
+    6: dict(dtype=BF16, batch=8, num_q_heads=32, num_kv_heads=32, head_dim=128, logical_page=16, page_size=64,
+            token_budget=4096, reuse_interval=4, sink_tokens=64, local_tokens=1024, sink_blocks=1, local_blocks=16,
+            ctx=65536, window=4, permute=False, outliers=True, needles=8),
 }
 
 PREFILL_CONFIGS = {
     1: dict(dtype=F32, seq_len=1024, num_q_heads=4, num_kv_heads=2, head_dim=64, page_size=64, logical_page=16,
             sink_blocks=1, local_blocks=2, permute=True, head_scales=False),
     3: dict(dtype=BF16, seq_len=131072, num_q_heads=32, num_kv_heads=8, head_dim=128, page_size=64,
+            logical_page=16, sink_blocks=1, local_blocks=16, permute=False, head_scales=True),
+    # multi-head attention (Llama-2-7B-shaped layer)
+    7: dict(dtype=BF16, seq_len=131072, num_q_heads=32, num_kv_heads=32, head_dim=128, page_size=64,
             logical_page=16, sink_blocks=1, local_blocks=16, permute=False, head_scales=True),
 }
 

@@ -228,6 +228,36 @@ def test_decode_full_size_cfg5_int4_sampled():
     torch.cuda.empty_cache()
 
 
+@pytest.mark.parametrize("R", [1, 2, 8])
+def test_decode_reuse_interval(R):
+    """An 8-step window with the selection made every R steps (R = 1 selects
+    on every step, R = 8 once); the oracle follows the same schedule."""
+    w = W.make_decode(2, DEV, batch=2, ctx=[6000, 9000], window=8)
+    w.reuse_interval = R
+    ret = [kv for kv in range(w.num_kv_heads) if w.head_kind[kv] == 0]
+    st = [kv for kv in range(w.num_kv_heads) if w.head_kind[kv] == 1][:1]
+    print("max abs err", check_window(w, kv_heads=ret + st))
+
+
+@pytest.mark.parametrize("ctx", [[6000, 9000], [63, 4096 + 17]])
+def test_decode_cfg6_mha_small(ctx):
+    """Multi-head attention (32 KV heads, group size 1)."""
+    w = W.make_decode(6, DEV, batch=len(ctx), ctx=ctx)
+    ret = [kv for kv in range(w.num_kv_heads) if w.head_kind[kv] == 0][:3]
+    st = [kv for kv in range(w.num_kv_heads) if w.head_kind[kv] == 1][:2]
+    print("max abs err", check_window(w, kv_heads=ret + st))
+
+
+def test_decode_full_size_cfg6_mha_sampled():
+    """Config 6 at full size (B = 8, 64K context, 32 KV heads)."""
+    w = W.make_decode(6, DEV)
+    ret = [kv for kv in range(w.num_kv_heads) if w.head_kind[kv] == 0][:2]
+    st = [kv for kv in range(w.num_kv_heads) if w.head_kind[kv] == 1][:1]
+    print("max abs err", check_window(w, kv_heads=ret + st, batches=[0, 7]))
+    del w
+    torch.cuda.empty_cache()
+
+
 def test_decode_window_in_hip_graph_matches_eager():
     """A whole decode window (selection every R steps, attention with the
     statistics refresh) captured as a HIP graph and replayed three times, with

@@ -104,3 +104,29 @@ def test_prefill_full_size_cfg3_sampled():
     st = [kv for kv in range(8) if p.head_kind[kv] == 1][0]
     rows = [0, 1, 63, 64, 1000, 1023, 1024, 1087, 65536, 100000, 131071]
     print("max abs err", check(p, out, rows=rows, heads=[ret * 4 + 1, st * 4 + 2]))
+
+
+@pytest.mark.parametrize("T", [777, 1088])
+def test_prefill_cfg7_mha_small(T):
+    """Multi-head attention (32 KV heads, group size 1)."""
+    p = W.make_prefill(7, DEV, seq_len=T)
+    out, cnt = run_prefill(p)
+    assert cnt == expected_tiles(p)
+    print("max abs err", check(p, out, heads=[0, 1, 7, 18, 31]))
+
+
+def test_prefill_full_size_cfg7_mha_sampled():
+    """Config 7 at full size (T = 131072, 32 query and 32 KV heads, 16 of them
+    streaming): the same 34,125,696 non-empty (head, tile) pairs as the
+    grouped layer, no NaN left, sampled rows of one retrieval and one
+    streaming head against the oracle."""
+    p = W.make_prefill(7, DEV)
+    out, cnt = run_prefill(p)
+    assert cnt == expected_tiles(p) == 34125696
+    assert not bool(torch.isnan(out).any())
+    ret = [kv for kv in range(32) if p.head_kind[kv] == 0][0]
+    st = [kv for kv in range(32) if p.head_kind[kv] == 1][0]
+    rows = [0, 63, 64, 1087, 65536, 131071]
+    print("max abs err", check(p, out, rows=rows, heads=[ret, st]))
+    del out, p
+    torch.cuda.empty_cache()
