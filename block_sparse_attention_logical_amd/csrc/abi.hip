@@ -102,8 +102,6 @@ int count_kind(const lsa_heads *hd, int h_kv, int kind) {
     return n;
 }
 
-constexpr int kDecodeChunkPages = 4;   // decode: pages per workgroup (one per wavefront)
-
 struct DecodeGeom {
     int K, chunks_ret, chunks_str, chunks_max, rec_floats;
 };
@@ -114,7 +112,7 @@ size_t decode_counter_bytes(int batch, int num_kv_heads) { return align_up((size
 DecodeGeom decode_geometry(const lsa_kv *kv, const lsa_heads *hd, int token_budget) {
     DecodeGeom g;
     g.K = token_budget / kv->page_size;
-    const int per_chunk = kDecodeChunkPages;
+    const int per_chunk = decode_chunk_pages(kv->kv_dtype, kv->page_size);
     const int NP = kv->page_size;
     const int ret_pages = g.K + 1;
     const int str_pages = (hd->sink_tokens + NP - 1) / NP + (hd->local_tokens - 1) / NP + 2;

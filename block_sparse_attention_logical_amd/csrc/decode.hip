@@ -6,11 +6,13 @@
 // of KV pages per step; the KV4 co-design pairs the sparse path with 4-bit KV).
 //
 // Work decomposition (split-KV).  The attended page list of a (sequence, KV
-// head) is cut into chunks of 4 pages; one workgroup of four wavefronts takes
-// a chunk (wavefront 0 resolves the four pool pages into LDS), each wavefront
-// streams its page with an online softmax, the four states are merged in LDS
-// and one partial record (max, sum, unnormalised output) is written per chunk.  The last workgroup of
-// a (sequence, KV head) to finish merges every record in chunk order (so the
+// head) is cut into chunks; one workgroup takes a chunk (wavefront 0 resolves
+// the chunk's pool pages into LDS), each wavefront streams its share with an
+// online softmax, the wavefronts' states are merged in LDS and one partial
+// record (max, sum, unnormalised output) is written per chunk.  The MFMA path
+// runs four wavefronts of 128 tokens each (eight pages of 64 tokens per chunk);
+// the f32 path four wavefronts of one page.  The last workgroup of a
+// (sequence, KV head) to finish merges every record in chunk order (so the
 // result does not depend on arrival order) and writes the output.  The
 // hand-off avoids a device-scope fence (an L2 writeback on this part): the
 // records are written and read with agent-scope stores and loads, which go to
@@ -27,8 +29,13 @@
 // regrouped with two permlane swaps into 8 consecutive tokens of one head, the
 // B operand of PV; the A operand of PV (one channel, 8 consecutive tokens of
 // the value rows) is again a contiguous read.  Heads occupy the N dimension,
-// padded to 16 with zero queries.  All K and V loads of kDecodeBlocksInFlight
-// 32-token blocks are issued before their first MFMA.
+// padded to 16 with zero queries.  A wavefront walks its 32-token blocks
+// through a ring of register buffers: the loads of the next blocks (one more
+// for bf16, three more for int4) are in flight while a block is computed, so
+// the wavefront's memory stream never drains between blocks.  Every slot of
+// the ring is always loaded (a block that needs no keys re-reads the
+// wavefront's first needed block, which is already on its way to the caches),
+// so the wait before each block counts exactly the loads issued after it.
 //
 // int4 pools.  A code c (0..15) becomes the bf16 bit pattern 0x4300 | c, which
 // is exactly 128 + c, so the MFMAs see exact operands; the offset and the
@@ -65,26 +72,28 @@ __device__ __forceinline__ WorkItem decode_item(const DecodeArgs &a) {
     return w;
 }
 
-// Slots of the per-workgroup page list in LDS: t, L, then the sequence page
-// and the pool page of each of the four wavefronts (-1: no page).
-constexpr int kListSlots = 10;
+// Slots of the per-workgroup page list in LDS: t, L, then the sequence pages
+// of the chunk, then their pool pages (-1: no page).
+constexpr int kListSlots = 2 + 2 * kMaxChunkPages;
 
-// Wavefront 0 of a workgroup resolves the pages of its chunk: the attended
+// Wavefront 0 of a workgroup resolves the CP pages of its chunk: the attended
 // pages of a (sequence, KV head) in ascending order are the selection row
 // (valid entries first, then -1) followed by the current page when the row
 // lacks it (retrieval heads), or the sink pages followed by the local window
-// (streaming heads); the chunk takes list entries 4 * chunk .. 4 * chunk + 3.
-// seq_lens and the selection entries are loaded together, then the four
+// (streaming heads); the chunk takes list entries CP * chunk .. CP * chunk + CP - 1.
+// seq_lens and the selection entries are loaded together, then the CP
 // page-table entries: two dependent loads in all.
+template <int CP>
 __device__ __forceinline__ void wg_pages(const DecodeArgs &a, const WorkItem &w, int *list) {
+    static_assert(CP <= kMaxChunkPages && (CP & (CP - 1)) == 0, "chunk pages");
     const int lane = threadIdx.x % kWave;
     const int NP = a.page_size;
-    const int i = w.chunk * 4 + (lane & 3);            // list index of this lane's page (lanes 0..3)
+    const int i = w.chunk * CP + (lane & (CP - 1));    // list index of this lane's page (lanes 0..CP-1)
     const int32_t *sel = w.streaming ? nullptr : a.selected + ((size_t)w.b * a.num_kv_heads + w.kv) * a.sel_k;
     int m_row = -1, m_i = -1;
     if (sel) {
         if (lane < a.sel_k) m_row = sel[lane];
-        if (lane < 4 && i < a.sel_k) m_i = sel[i];
+        if (lane < CP && i < a.sel_k) m_i = sel[i];
     }
     const int L = a.seq_lens[w.b];
     const int t = L - 1, cur = t / NP;
@@ -107,15 +116,14 @@ __device__ __forceinline__ void wg_pages(const DecodeArgs &a, const WorkItem &w,
         if (i < n) page = i < cnt ? m_i : cur;
     }
     int pool = -1;
-    if (lane < 4 && page >= 0) pool = a.page_table[(size_t)w.b * a.max_pages + page];
+    if (lane < CP && page >= 0) pool = a.page_table[(size_t)w.b * a.max_pages + page];
     if (lane == 0) { list[0] = t; list[1] = L; }
-    if (lane < 4) { list[2 + lane] = page; list[6 + lane] = pool; }
+    if (lane < CP) { list[2 + lane] = page; list[2 + CP + lane] = pool; }
 }
 
 __device__ __forceinline__ bool token_visible(const DecodeArgs &a, const WorkItem &w, int p) {
-    if (p > w.t) return false;
-    if (!w.streaming) return true;
-    return p < a.sink || (w.t - p) < a.local;
+    // bitwise, not short-circuit: no branch inside the block compute
+    return (p <= w.t) & (!w.streaming | (p < a.sink) | ((w.t - p) < a.local));
 }
 
 // Does the 32-token block starting at tok0 hold any attended token?
@@ -192,9 +200,10 @@ __device__ __forceinline__ float2 load_agent2(const float *p) {
     return make_float2(__uint_as_float(uint32_t(u)), __uint_as_float(uint32_t(u >> 32)));
 }
 
-// Merge the per-wave softmax states held in LDS and write this chunk's record
-// (m[16], l[16], o[G][D]) with agent-scope stores.  LDS layout per wave:
-// m[16], l[16], o[16][D].
+// Merge the softmax states of the NW wavefronts held in LDS and write this
+// chunk's record (m[16], l[16], o[G][D]) with agent-scope stores.  LDS layout
+// per wave: m[16], l[16], o[16][D].
+template <int NW>
 __device__ __forceinline__ void merge_waves_and_store(const DecodeArgs &a, const WorkItem &w,
                                                       const float *lds, int D) {
     const int G = a.group;
@@ -205,11 +214,11 @@ __device__ __forceinline__ void merge_waves_and_store(const DecodeArgs &a, const
         const int h = (2 * pi) / D, d = 2 * pi - h * D;
         float M = -__builtin_inff();
 #pragma unroll
-        for (int wv = 0; wv < 4; ++wv) M = fmaxf(M, lds[wv * wave_stride + h]);
+        for (int wv = 0; wv < NW; ++wv) M = fmaxf(M, lds[wv * wave_stride + h]);
         float acc0 = 0.f, acc1 = 0.f, lsum = 0.f;
         if (M != -__builtin_inff()) {
 #pragma unroll
-            for (int wv = 0; wv < 4; ++wv) {
+            for (int wv = 0; wv < NW; ++wv) {
                 const float mw = lds[wv * wave_stride + h];
                 const float wt = mw == -__builtin_inff() ? 0.f : exp2_fast(mw - M);
                 acc0 += wt * lds[wv * wave_stride + 32 + h * D + d];
@@ -226,8 +235,9 @@ __device__ __forceinline__ void merge_waves_and_store(const DecodeArgs &a, const
 }
 
 // Count this chunk's arrival; the last workgroup of the (sequence, KV head)
-// merges the records of all its chunks, in chunk order, into out.
-template <typename OutT>
+// merges the records of all its chunks, in chunk order, into out, loading CB
+// chunks' records per memory round trip.
+template <typename OutT, int CB>
 __device__ __forceinline__ void finish_head(const DecodeArgs &a, const WorkItem &w, int D) {
     __shared__ int s_last;
     // this wavefront's record stores have reached the coherence point
@@ -244,49 +254,53 @@ __device__ __forceinline__ void finish_head(const DecodeArgs &a, const WorkItem 
     __syncthreads();
     if (!s_last) return;
 
-    // chunks whose records are loaded in one batch: 17 covers a 4096-token
-    // budget at N_P = 64 (64 selected pages and the current one, 4 per chunk)
-    // in a single memory round trip without spilling
-    constexpr int CB = 17;
+    // a thread merges four channels
     const int G = a.group;
     const size_t rec_size = 32 + (size_t)G * D;
     const float *rec0 = a.part + ((size_t)w.b * a.num_kv_heads + w.kv) * a.chunks_max * rec_size;
-    for (int pi = threadIdx.x; pi < G * D / 2; pi += blockDim.x) {
-        const int hh = (2 * pi) / D, d = 2 * pi - hh * D;
-        float M = -__builtin_inff(), acc0 = 0.f, acc1 = 0.f, L = 0.f;
+    for (int qi = threadIdx.x; qi < G * D / 4; qi += blockDim.x) {
+        const int hh = (4 * qi) / D, d = 4 * qi - hh * D;
+        float M = -__builtin_inff(), L = 0.f;
+        float acc[4] = {0.f, 0.f, 0.f, 0.f};
         for (int c0 = 0; c0 < nchunks; c0 += CB) {
             float mv[CB], lv[CB];
-            float2 ov[CB];
+            float2 ov[CB][2];
 #pragma unroll
             for (int c = 0; c < CB; ++c) {
                 const float *rec = rec0 + (size_t)(c0 + c) * rec_size;
                 const bool in = c0 + c < nchunks;
                 mv[c] = in ? load_agent(rec + hh) : -__builtin_inff();
                 lv[c] = in ? load_agent(rec + 16 + hh) : 0.f;
-                ov[c] = in ? load_agent2(rec + 32 + 2 * pi) : make_float2(0.f, 0.f);
+                ov[c][0] = in ? load_agent2(rec + 32 + 4 * qi) : make_float2(0.f, 0.f);
+                ov[c][1] = in ? load_agent2(rec + 32 + 4 * qi + 2) : make_float2(0.f, 0.f);
             }
             float Mb = M;
 #pragma unroll
             for (int c = 0; c < CB; ++c) Mb = fmaxf(Mb, mv[c]);
             const float sc = M == -__builtin_inff() ? 0.f : exp2_fast(M - Mb);
-            acc0 *= sc;
-            acc1 *= sc;
             L *= sc;
+#pragma unroll
+            for (int k = 0; k < 4; ++k) acc[k] *= sc;
 #pragma unroll
             for (int c = 0; c < CB; ++c) {
                 const float e = mv[c] == -__builtin_inff() ? 0.f : exp2_fast(mv[c] - Mb);
                 L += e * lv[c];
-                acc0 += e * ov[c].x;
-                acc1 += e * ov[c].y;
+                acc[0] += e * ov[c][0].x;
+                acc[1] += e * ov[c][0].y;
+                acc[2] += e * ov[c][1].x;
+                acc[3] += e * ov[c][1].y;
             }
             M = Mb;
         }
         const size_t o = ((size_t)w.b * a.num_q_heads + (size_t)w.kv * G + hh) * D + d;
         if constexpr (sizeof(OutT) == 2) {
-            static_cast<uint32_t *>(a.out)[o / 2] =
-                uint32_t(f32_to_bf16_rne(acc0 / L)) | (uint32_t(f32_to_bf16_rne(acc1 / L)) << 16);
+            uint2 pk;
+            pk.x = uint32_t(f32_to_bf16_rne(acc[0] / L)) | (uint32_t(f32_to_bf16_rne(acc[1] / L)) << 16);
+            pk.y = uint32_t(f32_to_bf16_rne(acc[2] / L)) | (uint32_t(f32_to_bf16_rne(acc[3] / L)) << 16);
+            *reinterpret_cast<uint2 *>(static_cast<uint16_t *>(a.out) + o) = pk;
         } else {
-            *reinterpret_cast<float2 *>(static_cast<float *>(a.out) + o) = make_float2(acc0 / L, acc1 / L);
+            *reinterpret_cast<float4 *>(static_cast<float *>(a.out) + o) =
+                make_float4(acc[0] / L, acc[1] / L, acc[2] / L, acc[3] / L);
         }
     }
 }
@@ -305,16 +319,21 @@ __device__ __forceinline__ uint32_t pick(const uint4 &u, int i) {
 // ---------------------------------------------------------------------------
 // MFMA kernel, bf16 or int4 pool, bf16 q
 // ---------------------------------------------------------------------------
-template <int D, int KVT, int BIF>
-__global__ __launch_bounds__(256, 3) void decode_mfma_kernel(DecodeArgs a) {
+template <int D, int KVT, int NB>
+__global__ __launch_bounds__(kDecodeWaves * kWave, 2) void decode_mfma_kernel(DecodeArgs a) {
     constexpr bool I4 = KVT == LSA_INT4;
     constexpr int NS = D / 32;            // MFMA k-steps over channels
     constexpr int NDT = D / 16;           // output channel tiles
+    constexpr int NP = 32 * NB;           // page size
+    constexpr int PPW = decode_pages_per_wave(KVT, NP);
+    constexpr int NBW = PPW * NB;         // 32-token blocks per wavefront
+    constexpr int CP = kDecodeWaves * PPW;
+    constexpr int BIF = I4 ? (NBW < 4 ? NBW : 4) : 2;   // blocks in flight (ring size)
     extern __shared__ float lds[];
     WorkItem w = decode_item(a);
     const int lane = threadIdx.x % kWave, wave = threadIdx.x / kWave;
     const int h = lane & 15, g4 = lane >> 4;
-    const int G = a.group, NP = a.page_size;
+    const int G = a.group;
 
     // B operand of QK^T: column h = query head.  bf16 pools: step s holds
     // channels 32s + 8*g4 + j; int4 pools: channels (D/4)*g4 + 8s + j, so that a
@@ -339,11 +358,28 @@ __global__ __launch_bounds__(256, 3) void decode_mfma_kernel(DecodeArgs a) {
         }
     }
     __shared__ int s_list[kListSlots];
-    if (wave == 0) wg_pages(a, w, s_list);
+    if (wave == 0) wg_pages<CP>(a, w, s_list);
     __syncthreads();
-    w.t = s_list[0];
-    w.L = s_list[1];
-    const int my_page = s_list[2 + wave], my_pool = s_list[6 + wave];
+    w.t = __builtin_amdgcn_readfirstlane(s_list[0]);
+    w.L = __builtin_amdgcn_readfirstlane(s_list[1]);
+
+    // this wavefront's pages: chunk slots PPW*wave .. PPW*wave + PPW - 1
+    int pg[PPW];
+    size_t hp[PPW];
+#pragma unroll
+    for (int j = 0; j < PPW; ++j) {
+        pg[j] = __builtin_amdgcn_readfirstlane(s_list[2 + PPW * wave + j]);
+        const int pool = __builtin_amdgcn_readfirstlane(s_list[2 + CP + PPW * wave + j]);
+        hp[j] = (size_t)max(pool, 0) * a.num_kv_heads + w.kv;
+    }
+    // block i of the wavefront: page slot i / NB, 32-token block i % NB of that page
+    bool need[NBW];
+    bool any = false;
+#pragma unroll
+    for (int i = 0; i < NBW; ++i) {
+        need[i] = pg[i / NB] >= 0 && block_needed(a, w, pg[i / NB] * NP + 32 * (i % NB));
+        any |= need[i];
+    }
 
     floatx4 o[NDT];
 #pragma unroll
@@ -356,163 +392,194 @@ __global__ __launch_bounds__(256, 3) void decode_mfma_kernel(DecodeArgs a) {
     // channel step); a lane's result registers hold tokens 16T + 4*g4 + r.
     const int rho = lane & 15;
 
-    if (my_page >= 0) {
-        const int page = my_page;
-        const size_t hp = (size_t)my_pool * a.num_kv_heads + w.kv;
-        float sk = 1.f, zk = 0.f, sv = 1.f, zv = 0.f;
-        if constexpr (I4) {
-            const uint32_t ksz = *reinterpret_cast<const uint32_t *>(a.k_sz + hp * 2);
-            const uint32_t vsz = *reinterpret_cast<const uint32_t *>(a.v_sz + hp * 2);
-            sk = fp16_bits_to_f32(uint16_t(ksz)); zk = fp16_bits_to_f32(uint16_t(ksz >> 16));
-            sv = fp16_bits_to_f32(uint16_t(vsz)); zv = fp16_bits_to_f32(uint16_t(vsz >> 16));
+    if (any) {
+        float sk[PPW], zk[PPW], sv[PPW], zv[PPW];
+#pragma unroll
+        for (int j = 0; j < PPW; ++j) {
+            sk[j] = 1.f; zk[j] = 0.f; sv[j] = 1.f; zv[j] = 0.f;
+            if constexpr (I4) {
+                if (pg[j] >= 0) {
+                    const uint32_t ksz = *reinterpret_cast<const uint32_t *>(a.k_sz + hp[j] * 2);
+                    const uint32_t vsz = *reinterpret_cast<const uint32_t *>(a.v_sz + hp[j] * 2);
+                    sk[j] = fp16_bits_to_f32(uint16_t(ksz)); zk[j] = fp16_bits_to_f32(uint16_t(ksz >> 16));
+                    sv[j] = fp16_bits_to_f32(uint16_t(vsz)); zv[j] = fp16_bits_to_f32(uint16_t(vsz >> 16));
+                }
+            }
         }
-        const int p0 = page * NP;
-        for (int kb0 = 0; kb0 < NP / 32; kb0 += BIF) {
-            // ---- issue every K and V load of BIF 32-token blocks
-            bool need[BIF];
-            uint4 kr[BIF][2][I4 ? 1 : NS];
-            uint4 vr[BIF][I4 ? 1 : NDT];
-            uint32_t vr4[BIF][I4 ? NDT : 1];
+        // source of each ring load: the block itself, or the first needed block
+        size_t src_hp[NBW];
+        int src_kb[NBW];
+        {
+            size_t f_hp = 0;
+            int f_kb = 0;
+            bool found = false;
 #pragma unroll
-            for (int e = 0; e < BIF; ++e) {
-                const int kb = kb0 + e;
-                need[e] = kb < NP / 32 && block_needed(a, w, p0 + 32 * kb);
-                if (!need[e]) continue;
-                if constexpr (I4) {
-                    const uint8_t *k8 = static_cast<const uint8_t *>(a.k);
+            for (int i = 0; i < NBW; ++i)
+                if (need[i] && !found) { f_hp = hp[i / NB]; f_kb = i % NB; found = true; }
 #pragma unroll
-                    for (int T = 0; T < 2; ++T) {
-                        const uint8_t *row = k8 + (hp * NP * D + key_offset(32 * kb + 16 * T + rho, (D / 4) * g4, D)) / 2;
-                        if constexpr (D == 128) {
-                            kr[e][T][0] = *reinterpret_cast<const uint4 *>(row);
-                        } else {
-                            const uint2 u = *reinterpret_cast<const uint2 *>(row);
-                            kr[e][T][0] = make_uint4(u.x, u.y, 0, 0);
-                        }
-                    }
-                    const uint8_t *v8 = static_cast<const uint8_t *>(a.v);
-#pragma unroll
-                    for (int dt = 0; dt < NDT; ++dt)
-                        vr4[e][dt] = *reinterpret_cast<const uint32_t *>(
-                            v8 + (hp * NP * D + value_offset(32 * kb + 8 * g4, 16 * dt + h, D)) / 2);
-                } else {
-                    const uint16_t *kp = static_cast<const uint16_t *>(a.k) + hp * NP * D;
-#pragma unroll
-                    for (int T = 0; T < 2; ++T)
-#pragma unroll
-                        for (int s = 0; s < NS; ++s)
-                            kr[e][T][s] = *reinterpret_cast<const uint4 *>(
-                                kp + key_offset(32 * kb + 16 * T + rho, 32 * s + 8 * g4, D));
-                    const uint16_t *vp = static_cast<const uint16_t *>(a.v) + hp * NP * D;
-#pragma unroll
-                    for (int dt = 0; dt < NDT; ++dt)
-                        vr[e][dt] = *reinterpret_cast<const uint4 *>(vp + value_offset(32 * kb + 8 * g4, 16 * dt + h, D));
-                }
+            for (int i = 0; i < NBW; ++i) {
+                src_hp[i] = need[i] ? hp[i / NB] : f_hp;
+                src_kb[i] = need[i] ? i % NB : f_kb;
             }
+        }
+
+        uint4 kr[BIF][2][I4 ? 1 : NS];
+        uint4 vr[BIF][I4 ? 1 : NDT];
+        uint32_t vr4[BIF][I4 ? NDT : 1];
+        // ---- issue every K and V load of block i into ring slot e
+        auto issue = [&](int e, int i) {
+            const size_t base = src_hp[i] * NP * D;
+            const int kb = src_kb[i];
+            if constexpr (I4) {
+                const uint8_t *k8 = static_cast<const uint8_t *>(a.k);
 #pragma unroll
-            for (int e = 0; e < BIF; ++e) {
-                if (!need[e]) continue;
-                const int tok0 = p0 + 32 * (kb0 + e);
-                // ---- scores of the 32 keys (two 16-row tiles)
-                floatx4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-                for (int s = 0; s < NS; ++s) {
-                    bf16x8 k0, k1;
-                    if constexpr (I4) {
-                        const uint32_t w0 = pick(kr[e][0][0], s), w1 = pick(kr[e][1][0], s);
-                        k0 = __builtin_bit_cast(bf16x8, make_uint4(nibble_pair_bf16(w0, 0), nibble_pair_bf16(w0, 1),
-                                                                   nibble_pair_bf16(w0, 2), nibble_pair_bf16(w0, 3)));
-                        k1 = __builtin_bit_cast(bf16x8, make_uint4(nibble_pair_bf16(w1, 0), nibble_pair_bf16(w1, 1),
-                                                                   nibble_pair_bf16(w1, 2), nibble_pair_bf16(w1, 3)));
+                for (int T = 0; T < 2; ++T) {
+                    const uint8_t *row = k8 + (base + key_offset(32 * kb + 16 * T + rho, (D / 4) * g4, D)) / 2;
+                    if constexpr (D == 128) {
+                        kr[e][T][0] = *reinterpret_cast<const uint4 *>(row);
                     } else {
-                        k0 = __builtin_bit_cast(bf16x8, kr[e][0][s]);
-                        k1 = __builtin_bit_cast(bf16x8, kr[e][1][s]);
+                        const uint2 u = *reinterpret_cast<const uint2 *>(row);
+                        kr[e][T][0] = make_uint4(u.x, u.y, 0, 0);
                     }
-                    s0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k0, qb[s], s0, 0, 0, 0);
-                    s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k1, qb[s], s1, 0, 0, 0);
                 }
-                // lane holds the logits of head h for tokens 4*g4 + r (x[r]) and
-                // 16 + 4*g4 + r (x[4 + r]) of the block, r = 0..3
-                float x[8];
-                if constexpr (I4) {
-                    const float off = (128.f + zk) * qsum;
-                    const float sc = sk * a.scale_log2;
+                const uint8_t *v8 = static_cast<const uint8_t *>(a.v);
 #pragma unroll
-                    for (int r = 0; r < 4; ++r) { x[r] = (s0[r] - off) * sc; x[4 + r] = (s1[r] - off) * sc; }
-                } else {
+                for (int dt = 0; dt < NDT; ++dt)
+                    vr4[e][dt] = *reinterpret_cast<const uint32_t *>(
+                        v8 + (base + value_offset(32 * kb + 8 * g4, 16 * dt + h, D)) / 2);
+            } else {
+                const uint16_t *kp = static_cast<const uint16_t *>(a.k) + base;
 #pragma unroll
-                    for (int r = 0; r < 4; ++r) { x[r] = s0[r] * a.scale_log2; x[4 + r] = s1[r] * a.scale_log2; }
-                }
-                float mb = -__builtin_inff();
+                for (int T = 0; T < 2; ++T)
 #pragma unroll
-                for (int j = 0; j < 8; ++j) {
-                    if (!token_visible(a, w, tok0 + 4 * g4 + (j & 3) + 16 * (j >> 2))) x[j] = -__builtin_inff();
-                    mb = fmaxf(mb, x[j]);
-                }
-                mb = max_xor32(max_xor16(mb));
-                const float m_new = fmaxf(m_run, mb);
-                const float alpha = exp2_fast(m_run - m_new);
-                float psum = 0.f, fed = 0.f;
-                uint32_t pk[4];
+                    for (int s = 0; s < NS; ++s)
+                        kr[e][T][s] = *reinterpret_cast<const uint4 *>(
+                            kp + key_offset(32 * kb + 16 * T + rho, 32 * s + 8 * g4, D));
+                const uint16_t *vp = static_cast<const uint16_t *>(a.v) + base;
 #pragma unroll
-                for (int j = 0; j < 8; j += 2) {
-                    const float pa = exp2_fast(x[j] - m_new);
-                    const float pb = exp2_fast(x[j + 1] - m_new);
-                    psum += pa + pb;
-                    uint16_t ba, bb;
-                    if constexpr (I4) {
-                        ba = f32_to_bf16_rne(pa * sv);
-                        bb = f32_to_bf16_rne(pb * sv);
-                        fed += bf16_to_f32(ba) + bf16_to_f32(bb);
-                    } else {
-                        ba = f32_to_bf16_rne(pa);
-                        bb = f32_to_bf16_rne(pb);
-                    }
-                    pk[j / 2] = uint32_t(ba) | (uint32_t(bb) << 16);
-                }
-                l_run = l_run * alpha + psum;
-                if constexpr (I4) corr = corr * alpha + (128.f + zv) * fed;
-                m_run = m_new;
-                // The PV operand of lane (h, g4) wants tokens 8*g4 .. 8*g4 + 7.  Swapping
-                // the upper 32 lanes of pk[0..1] (tokens 4*g4 + r) with the lower 32
-                // lanes of pk[2..3] (tokens 16 + 4*g4 + r), then the odd 16-lane rows
-                // of the first result with the even rows of the second, regroups the
-                // four 4-token runs of every head into that order.
-                uint32_t pv[4];
-#pragma unroll
-                for (int d = 0; d < 2; ++d) {
-                    const auto r32 = __builtin_amdgcn_permlane32_swap(pk[d], pk[2 + d], false, false);
-                    const auto r16 = __builtin_amdgcn_permlane16_swap(r32[0], r32[1], false, false);
-                    pv[d] = r16[0];
-                    pv[2 + d] = r16[1];
-                }
-                const bf16x8 pbv = __builtin_bit_cast(bf16x8, make_uint4(pv[0], pv[1], pv[2], pv[3]));
-                // slots after the current token may hold any bits: zero their values so a
-                // zero probability never meets a NaN in the PV product
-                const bool tail = tok0 + 31 > w.t;
-                const int nvalid = w.t - (tok0 + 8 * g4) + 1;
-#pragma unroll
-                for (int dt = 0; dt < NDT; ++dt) {
-                    uint4 va;
-                    if constexpr (I4) {
-                        // 4 bytes = tokens 8*g4 .. 8*g4+7 of channel 16*dt + h
-                        const uint32_t wv4 = vr4[e][dt];
-                        va = make_uint4(nibble_pair_bf16(wv4, 0), nibble_pair_bf16(wv4, 1), nibble_pair_bf16(wv4, 2),
-                                        nibble_pair_bf16(wv4, 3));
-                    } else {
-                        va = vr[e][dt];
-                    }
-                    if (tail) {
-                        uint32_t keep[4];
-#pragma unroll
-                        for (int q2 = 0; q2 < 4; ++q2)
-                            keep[q2] = (2 * q2 < nvalid ? 0x0000FFFFu : 0u) | (2 * q2 + 1 < nvalid ? 0xFFFF0000u : 0u);
-                        va.x &= keep[0]; va.y &= keep[1]; va.z &= keep[2]; va.w &= keep[3];
-                    }
-                    o[dt] *= alpha;
-                    o[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, va), pbv, o[dt], 0, 0, 0);
-                }
+                for (int dt = 0; dt < NDT; ++dt)
+                    vr[e][dt] = *reinterpret_cast<const uint4 *>(vp + value_offset(32 * kb + 8 * g4, 16 * dt + h, D));
             }
+            // keep the block's loads ahead of the compute that follows them
+            __builtin_amdgcn_sched_barrier(0);
+        };
+        // ---- online softmax and PV of block i from ring slot e.  A block that
+        // needs no keys is computed fully masked with its values zeroed (its slot
+        // holds another block's data); there is no branch around it, so the
+        // compiler keeps every ring load where it is issued.
+        auto consume = [&](int e, int i) {
+            const bool blk = need[i];
+            const int j = i / NB;
+            const int tok0 = pg[j] * NP + 32 * (i % NB);
+            // scores of the 32 keys (two 16-row tiles)
+            floatx4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int s = 0; s < NS; ++s) {
+                bf16x8 k0, k1;
+                if constexpr (I4) {
+                    const uint32_t w0 = pick(kr[e][0][0], s), w1 = pick(kr[e][1][0], s);
+                    k0 = __builtin_bit_cast(bf16x8, make_uint4(nibble_pair_bf16(w0, 0), nibble_pair_bf16(w0, 1),
+                                                               nibble_pair_bf16(w0, 2), nibble_pair_bf16(w0, 3)));
+                    k1 = __builtin_bit_cast(bf16x8, make_uint4(nibble_pair_bf16(w1, 0), nibble_pair_bf16(w1, 1),
+                                                               nibble_pair_bf16(w1, 2), nibble_pair_bf16(w1, 3)));
+                } else {
+                    k0 = __builtin_bit_cast(bf16x8, kr[e][0][s]);
+                    k1 = __builtin_bit_cast(bf16x8, kr[e][1][s]);
+                }
+                s0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k0, qb[s], s0, 0, 0, 0);
+                s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k1, qb[s], s1, 0, 0, 0);
+            }
+            // lane holds the logits of head h for tokens 4*g4 + r (x[r]) and
+            // 16 + 4*g4 + r (x[4 + r]) of the block, r = 0..3
+            float x[8];
+            if constexpr (I4) {
+                const float off = (128.f + zk[j]) * qsum;
+                const float sc = sk[j] * a.scale_log2;
+#pragma unroll
+                for (int r = 0; r < 4; ++r) { x[r] = (s0[r] - off) * sc; x[4 + r] = (s1[r] - off) * sc; }
+            } else {
+#pragma unroll
+                for (int r = 0; r < 4; ++r) { x[r] = s0[r] * a.scale_log2; x[4 + r] = s1[r] * a.scale_log2; }
+            }
+            float mb = -__builtin_inff();
+#pragma unroll
+            for (int jj = 0; jj < 8; ++jj) {
+                if (!blk || !token_visible(a, w, tok0 + 4 * g4 + (jj & 3) + 16 * (jj >> 2))) x[jj] = -__builtin_inff();
+                mb = fmaxf(mb, x[jj]);
+            }
+            mb = max_xor32(max_xor16(mb));
+            const float m_new = fmaxf(m_run, mb);
+            // reference of the exponentials: any finite value while nothing is visible yet
+            const float m_ref = m_new == -__builtin_inff() ? 0.f : m_new;
+            const float alpha = exp2_fast(m_run - m_ref);
+            float psum = 0.f, fed = 0.f;
+            uint32_t pk[4];
+#pragma unroll
+            for (int jj = 0; jj < 8; jj += 2) {
+                const float pa = exp2_fast(x[jj] - m_ref);
+                const float pb = exp2_fast(x[jj + 1] - m_ref);
+                psum += pa + pb;
+                uint16_t ba, bb;
+                if constexpr (I4) {
+                    ba = f32_to_bf16_rne(pa * sv[j]);
+                    bb = f32_to_bf16_rne(pb * sv[j]);
+                    fed += bf16_to_f32(ba) + bf16_to_f32(bb);
+                } else {
+                    ba = f32_to_bf16_rne(pa);
+                    bb = f32_to_bf16_rne(pb);
+                }
+                pk[jj / 2] = uint32_t(ba) | (uint32_t(bb) << 16);
+            }
+            l_run = l_run * alpha + psum;
+            if constexpr (I4) corr = corr * alpha + (128.f + zv[j]) * fed;
+            m_run = m_new;
+            // The PV operand of lane (h, g4) wants tokens 8*g4 .. 8*g4 + 7.  Swapping
+            // the upper 32 lanes of pk[0..1] (tokens 4*g4 + r) with the lower 32
+            // lanes of pk[2..3] (tokens 16 + 4*g4 + r), then the odd 16-lane rows
+            // of the first result with the even rows of the second, regroups the
+            // four 4-token runs of every head into that order.
+            uint32_t pv[4];
+#pragma unroll
+            for (int d = 0; d < 2; ++d) {
+                const auto r32 = __builtin_amdgcn_permlane32_swap(pk[d], pk[2 + d], false, false);
+                const auto r16 = __builtin_amdgcn_permlane16_swap(r32[0], r32[1], false, false);
+                pv[d] = r16[0];
+                pv[2 + d] = r16[1];
+            }
+            const bf16x8 pbv = __builtin_bit_cast(bf16x8, make_uint4(pv[0], pv[1], pv[2], pv[3]));
+            // slots after the current token may hold any bits: zero their values so a
+            // zero probability never meets a NaN in the PV product
+            const bool tail = !blk || tok0 + 31 > w.t;
+            const int nvalid = blk ? w.t - (tok0 + 8 * g4) + 1 : 0;
+#pragma unroll
+            for (int dt = 0; dt < NDT; ++dt) {
+                uint4 va;
+                if constexpr (I4) {
+                    // 4 bytes = tokens 8*g4 .. 8*g4+7 of channel 16*dt + h
+                    const uint32_t wv4 = vr4[e][dt];
+                    va = make_uint4(nibble_pair_bf16(wv4, 0), nibble_pair_bf16(wv4, 1), nibble_pair_bf16(wv4, 2),
+                                    nibble_pair_bf16(wv4, 3));
+                } else {
+                    va = vr[e][dt];
+                }
+                if (tail) {
+                    uint32_t keep[4];
+#pragma unroll
+                    for (int q2 = 0; q2 < 4; ++q2)
+                        keep[q2] = (2 * q2 < nvalid ? 0x0000FFFFu : 0u) | (2 * q2 + 1 < nvalid ? 0xFFFF0000u : 0u);
+                    va.x &= keep[0]; va.y &= keep[1]; va.z &= keep[2]; va.w &= keep[3];
+                }
+                o[dt] *= alpha;
+                o[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, va), pbv, o[dt], 0, 0, 0);
+            }
+        };
+        // ---- the ring: BIF blocks in flight
+#pragma unroll
+        for (int i = 0; i < BIF; ++i) issue(i, i);
+#pragma unroll
+        for (int i = 0; i < NBW; ++i) {
+            consume(i % BIF, i);
+            if (i + BIF < NBW) issue(i % BIF, i + BIF);
         }
     }
     l_run = sum_xor32(sum_xor16(l_run));
@@ -529,8 +596,10 @@ __global__ __launch_bounds__(256, 3) void decode_mfma_kernel(DecodeArgs a) {
         for (int r = 0; r < 4; ++r) my[32 + h * D + 16 * dt + 4 * g4 + r] = o[dt][r] - corr;
     if (a.stats && !w.streaming && w.chunk == 0 && wave == 0) refresh_current_stats(a, w, KVT);
     __syncthreads();
-    merge_waves_and_store(a, w, lds, D);
-    finish_head<uint16_t>(a, w, D);
+    merge_waves_and_store<kDecodeWaves>(a, w, lds, D);
+    // one batch of records covers a 4096-token budget (its pages plus the current one)
+    constexpr int CB = (4096 / NP + CP) / CP < 17 ? (4096 / NP + CP) / CP : 17;
+    finish_head<uint16_t, CB>(a, w, D);
 }
 
 // ---------------------------------------------------------------------------
@@ -544,7 +613,7 @@ __global__ __launch_bounds__(256) void decode_f32_kernel(DecodeArgs a) {
     const int G = a.group, NP = a.page_size;
     constexpr int CPL = D / 64;                   // channels per lane in PV
     __shared__ int s_list[kListSlots];
-    if (wave == 0) wg_pages(a, w, s_list);
+    if (wave == 0) wg_pages<4>(a, w, s_list);
 
     float *qs = lds + 4 * (32 + 16 * D);          // [G][D]
     float *ps = qs + 16 * D + wave * 16 * 64;     // this wave's [16][64] probabilities
@@ -641,31 +710,42 @@ __global__ __launch_bounds__(256) void decode_f32_kernel(DecodeArgs a) {
     }
     if (a.stats && !w.streaming && w.chunk == 0 && wave == 0) refresh_current_stats(a, w, LSA_F32);
     __syncthreads();
-    merge_waves_and_store(a, w, lds, D);
-    finish_head<float>(a, w, D);
+    merge_waves_and_store<4>(a, w, lds, D);
+    finish_head<float, 17>(a, w, D);
 }
 
 }  // namespace
 
-constexpr int kDecodeBlocksInFlight = 1;
+namespace {
+
+template <int D, int KVT>
+hipError_t launch_mfma(const DecodeArgs &a, unsigned grid, hipStream_t s) {
+    const size_t lds = kDecodeWaves * (32 + 16 * (size_t)D) * sizeof(float);
+    const dim3 block(kDecodeWaves * kWave);
+    switch (a.page_size) {
+        case 32: hipLaunchKernelGGL((decode_mfma_kernel<D, KVT, 1>), dim3(grid), block, lds, s, a); break;
+        case 64: hipLaunchKernelGGL((decode_mfma_kernel<D, KVT, 2>), dim3(grid), block, lds, s, a); break;
+        case 128: hipLaunchKernelGGL((decode_mfma_kernel<D, KVT, 4>), dim3(grid), block, lds, s, a); break;
+        case 256: hipLaunchKernelGGL((decode_mfma_kernel<D, KVT, 8>), dim3(grid), block, lds, s, a); break;
+        default: return hipErrorInvalidValue;
+    }
+    return hipSuccess;
+}
+
+}  // namespace
 
 hipError_t launch_decode(const DecodeArgs &a, int q_dtype, int kv_dtype, hipStream_t s) {
-    constexpr int BIF = kDecodeBlocksInFlight;
     const long long grid = (long long)a.batch * a.chunks_per_seq;
     if (grid == 0) return hipSuccess;
-    const size_t lds_merge = 4 * (32 + 16 * (size_t)a.head_dim) * sizeof(float);
+    hipError_t e = hipSuccess;
     if (q_dtype == LSA_BF16 && kv_dtype == LSA_BF16) {
-        if (a.head_dim == 128)
-            hipLaunchKernelGGL((decode_mfma_kernel<128, LSA_BF16, BIF>), dim3((unsigned)grid), dim3(256), lds_merge, s, a);
-        else
-            hipLaunchKernelGGL((decode_mfma_kernel<64, LSA_BF16, BIF>), dim3((unsigned)grid), dim3(256), lds_merge, s, a);
+        e = a.head_dim == 128 ? launch_mfma<128, LSA_BF16>(a, (unsigned)grid, s)
+                              : launch_mfma<64, LSA_BF16>(a, (unsigned)grid, s);
     } else if (q_dtype == LSA_BF16 && kv_dtype == LSA_INT4) {
-        if (a.head_dim == 128)
-            hipLaunchKernelGGL((decode_mfma_kernel<128, LSA_INT4, BIF>), dim3((unsigned)grid), dim3(256), lds_merge, s, a);
-        else
-            hipLaunchKernelGGL((decode_mfma_kernel<64, LSA_INT4, BIF>), dim3((unsigned)grid), dim3(256), lds_merge, s, a);
+        e = a.head_dim == 128 ? launch_mfma<128, LSA_INT4>(a, (unsigned)grid, s)
+                              : launch_mfma<64, LSA_INT4>(a, (unsigned)grid, s);
     } else if (q_dtype == LSA_F32 && kv_dtype == LSA_F32) {
-        const size_t lds = lds_merge + (16 * (size_t)a.head_dim + 4 * 16 * 64) * sizeof(float);
+        const size_t lds = (4 * (32 + 16 * (size_t)a.head_dim) + 16 * (size_t)a.head_dim + 4 * 16 * 64) * sizeof(float);
         if (a.head_dim == 128)
             hipLaunchKernelGGL(decode_f32_kernel<128>, dim3((unsigned)grid), dim3(256), lds, s, a);
         else
@@ -673,6 +753,7 @@ hipError_t launch_decode(const DecodeArgs &a, int q_dtype, int kv_dtype, hipStre
     } else {
         return hipErrorInvalidValue;
     }
+    if (e != hipSuccess) return e;
     return hipGetLastError();
 }
 

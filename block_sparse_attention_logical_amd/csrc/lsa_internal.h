@@ -13,6 +13,21 @@ constexpr int kMaxKvHeads = 64;   // H_kv limit (host-side tables live in kernel
 constexpr int kWave = 64;         // CDNA wavefront width
 constexpr int kMaxDecodeChunks = 128;   // split-KV chunks per (sequence, KV head)
 
+// Split-KV geometry of decode attention.  The MFMA path runs kDecodeWaves
+// wavefronts per workgroup, each streaming 128 tokens (one page when pages are
+// longer); the f32 path runs four wavefronts of one page each.  A workgroup
+// takes one chunk of the attended page list.
+constexpr int kDecodeWaves = 4;
+constexpr int kMaxChunkPages = 16;
+__host__ __device__ constexpr int decode_wave_tokens(int) { return 128; }
+__host__ __device__ constexpr int decode_pages_per_wave(int kv_dtype, int page_size) {
+    return kv_dtype == LSA_F32 || page_size >= decode_wave_tokens(kv_dtype) ? 1
+                                                                             : decode_wave_tokens(kv_dtype) / page_size;
+}
+__host__ __device__ constexpr int decode_chunk_pages(int kv_dtype, int page_size) {
+    return kv_dtype == LSA_F32 ? 4 : kDecodeWaves * decode_pages_per_wave(kv_dtype, page_size);
+}
+
 // ----------------------------------------------------------------------------
 // numeric helpers (device)
 // ----------------------------------------------------------------------------

@@ -172,8 +172,9 @@ def test_decode_workspace_size(lib):
     st = lib.lsa_decode_workspace(ctypes.byref(kv_desc()), ctypes.byref(seqs_desc(8, 1025)),
                                   ctypes.byref(heads_desc()), 4096, ctypes.byref(out))
     assert st == 0
-    # 65 retrieval pages -> 17 chunks of 4 pages; records of 32 + G*D floats
-    assert out.value >= 8 * 8 * 17 * (32 + 4 * 128) * 4
+    # 65 retrieval pages -> 9 chunks of 8 pages (four wavefronts of 128 tokens);
+    # records of 32 + G*D floats per chunk, after one int32 counter per (sequence, KV head)
+    assert out.value == 256 + 8 * 8 * 9 * (32 + 4 * 128) * 4
 
 
 def prefill(lib, kv=None, q_dtype=lsa.BF16, block=64, T=1000):
