@@ -19,7 +19,7 @@ Sources (cited by page title and section):
          constant number of KV pages suffices regardless of context length.
 
 Where the pages leave a step open, the reading taken is stated at the function
-that takes it (readings Z1..Z23, listed together in the design notes of the
+that takes it (readings Z1..Z25, listed together in the design notes of the
 repository).
 
 Data conventions (the layout of the caller-owned paged KV pool; a page is
@@ -406,6 +406,39 @@ def prefill_attention(q: np.ndarray, keys: np.ndarray, values: np.ndarray, kind:
         w = np.exp(logits - m)
         out[r_i] = (w @ values[idx]) / np.sum(w)
     return out
+
+
+def block_mask_attention(q: np.ndarray, keys: np.ndarray, values: np.ndarray, tile_mask: np.ndarray,
+                         block: int, scale: float, rows: Optional[Sequence[int]] = None) -> np.ndarray:
+    """Softmax attention of one query head under an arbitrary static tile
+    mask ([LS-X] 統一ブロックスパースアテンション: the kernel visits the
+    non-empty tiles of a block-sparse pattern; reading Z24: any pattern of
+    tiles at or below the diagonal, with the token-level causal rule p <= t
+    kept inside every tile).
+
+    tile_mask: [n][n] bool, n = ceil(T / block); query t sees key p iff
+    tile_mask[t // block][p // block] and p <= t.  A query that sees no key
+    gets the zero vector (reading Z25).  Returns [len(rows)][D].
+    """
+    T, D = q.shape
+    rows = range(T) if rows is None else rows
+    out = np.zeros((len(rows), D))
+    for r_i, t in enumerate(rows):
+        a = t // block
+        idx = np.array([p for p in range(t + 1) if tile_mask[a, p // block]], dtype=np.int64)
+        if idx.size == 0:
+            continue
+        logits = scale * (keys[idx] @ q[t])
+        m = np.max(logits)
+        w = np.exp(logits - m)
+        out[r_i] = (w @ values[idx]) / np.sum(w)
+    return out
+
+
+def kind_tile_mask(n_blocks: int, kind: int, sink_blocks: int, local_blocks: int) -> np.ndarray:
+    """The tile mask [n][n] of a head kind (the figure's causal and Lambda patterns)."""
+    return np.array([[tile_visible(a, c, kind, sink_blocks, local_blocks) for c in range(n_blocks)]
+                     for a in range(n_blocks)], dtype=bool)
 
 
 # ---------------------------------------------------------------------------

@@ -223,6 +223,53 @@ def test_prefill_mutants_caught(mutant):
     assert _fails(P.pin_prefill, mutant)
 
 
+def mask_transposed(q, k, v, m, B, sc, rows=None):
+    return O.block_mask_attention(q, k, v, m.T, B, sc, rows)
+
+
+def mask_no_token_causal(q, k, v, m, B, sc, rows=None):
+    T, D = q.shape
+    rows = range(T) if rows is None else rows
+    out = np.zeros((len(rows), D))
+    for i, t in enumerate(rows):
+        idx = np.array([p for p in range(T) if m[t // B, p // B]], dtype=np.int64)
+        if idx.size:
+            lg = sc * (k[idx] @ q[t])
+            w = np.exp(lg - lg.max())
+            out[i] = (w @ v[idx]) / w.sum()
+    return out
+
+
+def mask_tile_index_shifted(q, k, v, m, B, sc, rows=None):
+    T, D = q.shape
+    rows = range(T) if rows is None else rows
+    out = np.zeros((len(rows), D))
+    for i, t in enumerate(rows):
+        idx = np.array([p for p in range(t + 1) if m[t // B, (p + 1) // B if (p + 1) // B < m.shape[1] else p // B]],
+                       dtype=np.int64)
+        if idx.size:
+            lg = sc * (k[idx] @ q[t])
+            w = np.exp(lg - lg.max())
+            out[i] = (w @ v[idx]) / w.sum()
+    return out
+
+
+def mask_empty_row_uniform(q, k, v, m, B, sc, rows=None):
+    out = O.block_mask_attention(q, k, v, m, B, sc, rows)
+    T = q.shape[0]
+    rows = list(range(T)) if rows is None else list(rows)
+    for i, t in enumerate(rows):
+        if not m[t // B].any():
+            out[i] = v[: t + 1].mean(axis=0)
+    return out
+
+
+@pytest.mark.parametrize("mutant", [mask_transposed, mask_no_token_causal, mask_tile_index_shifted,
+                                    mask_empty_row_uniform])
+def test_block_mask_mutants_caught(mutant):
+    assert _fails(P.pin_block_mask, mutant)
+
+
 def counts_square(n, kind, sb, lb):
     nnz, _ = O.block_counts(n, kind, sb, lb)
     return nnz, n * n

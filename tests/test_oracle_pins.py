@@ -230,6 +230,49 @@ def pin_prefill(prefill_attention, seed=6):
     assert np.max(np.abs(got - _sdpa(q, k, v, mask=mask))) < 1e-12
 
 
+def pin_block_mask(block_mask_attention, seed=11):
+    """Arbitrary static tile masks: the full causal grid and the diagonal-only
+    grid reduce to library attention; the pages' 10-of-21 grid and a random
+    grid match library attention under the token mask they define; a query
+    tile without tiles gives zeros."""
+    rng = np.random.default_rng(seed)
+    T, D, B = 200, 8, 16          # 13 tiles, ragged last tile
+    n = -(-T // B)
+    q = rng.standard_normal((T, D))
+    k = rng.standard_normal((T, D)) * 1.5
+    v = rng.standard_normal((T, D))
+    sc = 1 / np.sqrt(D)
+    full = np.tril(np.ones((n, n), dtype=bool))
+    assert np.max(np.abs(block_mask_attention(q, k, v, full, B, sc) - _sdpa(q, k, v, causal=True))) < 1e-12
+    eye = np.eye(n, dtype=bool)
+    got = block_mask_attention(q, k, v, eye, B, sc)
+    for a in range(n):
+        r = slice(a * B, min((a + 1) * B, T))
+        assert np.max(np.abs(got[r] - _sdpa(q[r], k[r], v[r], causal=True))) < 1e-12
+    tq, tk = np.arange(T)[:, None], np.arange(T)[None, :]
+    with open(os.path.join(GOLDEN, "block_mask_10_of_21.json")) as f:
+        g = json.load(f)
+    gm = np.zeros((g["n_blocks"], g["n_blocks"]), dtype=bool)
+    for a, c in g["nonempty"]:
+        gm[a, c] = True
+    T6 = g["n_blocks"] * B
+    tok6 = (tk[:, :T6] <= tq[:T6]) & gm[tq[:T6] // B, tk[:, :T6] // B]
+    got = block_mask_attention(q[:T6], k[:T6], v[:T6], gm, B, sc)
+    assert np.max(np.abs(got - _sdpa(q[:T6], k[:T6], v[:T6], mask=tok6))) < 1e-12
+    m = np.tril(rng.random((n, n)) < 0.4) | eye
+    tok = (tk <= tq) & m[tq // B, tk // B]
+    ref = _sdpa(q, k, v, mask=tok)
+    assert np.max(np.abs(block_mask_attention(q, k, v, m, B, sc) - ref)) < 1e-12
+    rows = [0, 5, 17, 150, 199]
+    assert np.max(np.abs(block_mask_attention(q, k, v, m, B, sc, rows=rows) - ref[rows])) < 1e-12
+    m2 = m.copy()
+    m2[3, :] = False
+    got = block_mask_attention(q, k, v, m2, B, sc)
+    assert np.all(got[3 * B:4 * B] == 0)
+    keep = np.r_[0:3 * B, 4 * B:T]
+    assert np.max(np.abs(got[keep] - ref[keep])) < 1e-12
+
+
 def pin_block_accounting(block_counts, sparsity_and_speedup):
     with open(os.path.join(GOLDEN, "block_mask_10_of_21.json")) as f:
         g = json.load(f)
@@ -295,6 +338,23 @@ def test_prefill_vs_sdpa():
 
 def test_block_accounting_golden():
     pin_block_accounting(O.block_counts, O.sparsity_and_speedup)
+
+
+def test_block_mask_attention():
+    pin_block_mask(O.block_mask_attention)
+
+
+def test_kind_tile_mask_matches_prefill():
+    rng = np.random.default_rng(12)
+    T, D, B = 150, 8, 16
+    q, k, v = (rng.standard_normal((T, D)) for _ in range(3))
+    n = -(-T // B)
+    for kind, sb, lb in ((O.RETRIEVAL, 1, 2), (O.STREAMING, 1, 3), (O.STREAMING, 0, 2)):
+        m = O.kind_tile_mask(n, kind, sb, lb)
+        assert O.mask_sparsity(m) == O.sparsity_and_speedup(*O.block_counts(n, kind, sb, lb))
+        a = O.block_mask_attention(q, k, v, m, B, 0.3)
+        b = O.prefill_attention(q, k, v, kind, B, sb, lb, 0.3)
+        assert np.max(np.abs(a - b)) < 1e-12
 
 
 def test_prefill_mask_matches_tile_rule():
