@@ -15,7 +15,9 @@ last-level cache.  A cycle of replicas x R steps is captured once as a HIP
 graph and replayed; the timed region covers whole cycles.
 
 Prefill.  One call of the block-sparse prefill over 131072 tokens, 32 query
-heads, 8 KV heads (4 streaming with 1 sink + 16 local tiles).
+heads, 8 KV heads (4 streaming with 1 sink + 16 local tiles); the same
+kernel with every head causal (the dense-causal reference of the speed-up);
+and the same patterns given as static block masks (CSR lists of key tiles).
 
 Variants (the default run is the Llama-3-8B-shaped layer with R = 4 and the
 group's page scores summed): --workload llama2-7b-mha runs the multi-head
@@ -60,6 +62,8 @@ def parse():
     ap.add_argument("--prefill-only", action="store_true", help="time only the prefill leg (profiling runs)")
     ap.add_argument("--no-causal", action="store_true",
                     help="skip the all-causal prefill reference run (profiling runs of the sparse kernel)")
+    ap.add_argument("--no-csr", action="store_true",
+                    help="skip the prefill run with the same patterns given as static block masks (CSR)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="budget of the oracle CPU sample")
     ap.add_argument("--eager", action="store_true", help="time eager launches instead of graph replay")
@@ -315,12 +319,39 @@ def bench_prefill(args, torch, lsa, W, O):
         tc.append(a.elapsed_time(b) / 1e3)
     t_causal = min(tc) if tc else float("nan")
     causal_flop = dense * 4 * 64 * 64 * p.head_dim
+    # the same patterns given as static block masks (CSR lists): the general
+    # iterator against the analytic one
+    t_csr = float("nan")
+    if not args.no_csr:
+        a_idx = torch.arange(n)[:, None]
+        c_idx = torch.arange(n)[None, :]
+        masks = torch.stack([(c_idx <= a_idx) & ((p.head_kind[h] == 0) | (c_idx < p.sink_blocks) |
+                                                 (a_idx - c_idx < p.local_blocks)) for h in range(p.num_kv_heads)])
+        row_ptr, col_idx = W.csr_from_tile_masks(masks)
+        del masks
+        order = lsa.block_mask_schedule(row_ptr, p.num_kv_heads, p.num_q_heads, p.seq_len).to(dev)
+        row_ptr, col_idx = row_ptr.to(dev), col_idx.to(dev)
+        lsa.sparse_prefill_attn_csr(p.q, kv, p.page_table, p.seq_len, p.num_q_heads, row_ptr, col_idx, out,
+                                    order=order)
+        torch.cuda.synchronize()
+        tcs = []
+        for _ in range(max(1, min(2, args.prefill_reps))):
+            a = torch.cuda.Event(enable_timing=True)
+            b = torch.cuda.Event(enable_timing=True)
+            a.record()
+            lsa.sparse_prefill_attn_csr(p.q, kv, p.page_table, p.seq_len, p.num_q_heads, row_ptr, col_idx, out,
+                                        order=order)
+            b.record()
+            torch.cuda.synchronize()
+            tcs.append(a.elapsed_time(b) / 1e3)
+        t_csr = min(tcs)
+        del row_ptr, col_idx, order
     shape = dict(T=p.seq_len, Hq=p.num_q_heads, Hkv=p.num_kv_heads, D=p.head_dim,
                  n_str=sum(1 for x in p.head_kind if x == 1), sink=p.sink_blocks, local=p.local_blocks)
     del out, p
     torch.cuda.empty_cache()
     return dict(seconds=t, flop=flop, tiles=tiles, dense_tiles=dense, tflops=flop / t / 1e12,
-                causal_seconds=t_causal, causal_tflops=causal_flop / t_causal / 1e12, **shape)
+                causal_seconds=t_causal, causal_tflops=causal_flop / t_causal / 1e12, csr_seconds=t_csr, **shape)
 
 
 # ---------------------------------------------------------------------------
@@ -387,6 +418,7 @@ def main():
         pre = bench_prefill(args, torch, lsa, W, O)
         print(json.dumps({"prefill_ms": round(pre["seconds"] * 1e3, 3), "tflops": round(pre["tflops"], 1),
                           "all_causal_ms": round(pre["causal_seconds"] * 1e3, 3),
+                          "csr_mask_ms": round(pre["csr_seconds"] * 1e3, 3),
                           "measured_speedup": round(pre["causal_seconds"] / pre["seconds"], 4)}))
         return
     dec = bench_decode(args, torch, lsa, W)
@@ -446,6 +478,7 @@ def main():
             "all_causal_ms": round(pre["causal_seconds"] * 1e3, 3),
             "all_causal_tflops": round(pre["causal_tflops"], 1),
             "measured_speedup": round(pre["causal_seconds"] / pre["seconds"], 4),
+            "csr_mask_ms": round(pre["csr_seconds"] * 1e3, 3),
             "roofline": {"bound": "mfma", "achieved": round(pre["tflops"], 1), "peak": PEAK_BF16 / 1e12,
                          "unit": "TFLOP/s", "frac": round(pre["tflops"] * 1e12 / PEAK_BF16, 4), "traffic": None},
         }

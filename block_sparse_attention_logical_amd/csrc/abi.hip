@@ -1,7 +1,10 @@
 // Host side of the C ABI declared in include/lsa.h: argument validation,
 // workspace sizing, work decomposition and kernel dispatch.  Nothing here
 // allocates device memory or synchronises the host.
+#include <algorithm>
 #include <cmath>
+#include <utility>
+#include <vector>
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
@@ -121,6 +124,50 @@ DecodeGeom decode_geometry(const lsa_kv *kv, const lsa_heads *hd, int token_budg
     g.chunks_max = std::max(g.chunks_ret, g.chunks_str);
     g.rec_floats = 32 + (hd->num_q_heads / kv->num_kv_heads) * kv->head_dim;
     return g;
+}
+
+// Validation and the shared fields of a prefill launch (both mask kinds).
+lsa_status prefill_setup(PrefillArgs &p, const void *q, int32_t q_dtype, const lsa_kv *kv, const int32_t *page_table,
+                         int32_t seq_len, int32_t num_q_heads, int32_t block, float softmax_scale, void *out,
+                         int64_t *tile_counter, bool &empty) {
+    if (block != 64) return fail(LSA_ERR_UNSUPPORTED, "block %d: only 64-token tiles are built", block);
+    if (kv->page_size % 64 != 0)
+        return fail(LSA_ERR_UNSUPPORTED, "prefill needs page_size a multiple of 64 (got %d)", kv->page_size);
+    const bool pair_ok = (q_dtype == LSA_F32 && kv->kv_dtype == LSA_F32) ||
+                         (q_dtype == LSA_BF16 && kv->kv_dtype == LSA_BF16);
+    if (!pair_ok)
+        return fail(LSA_ERR_UNSUPPORTED, "(q_dtype %d, kv_dtype %d) is not a supported prefill pair", q_dtype,
+                    kv->kv_dtype);
+    if (q_dtype == LSA_F32 && kv->head_dim != 64)
+        return fail(LSA_ERR_UNSUPPORTED, "f32 prefill is built for head_dim 64 only");
+    if (seq_len < 0) return fail(LSA_ERR_INVALID_ARG, "seq_len %d < 0", seq_len);
+    if (!q || !out || (seq_len > 0 && !page_table))
+        return fail(LSA_ERR_INVALID_ARG, "q, out and page_table must be non-NULL");
+    if (!(softmax_scale >= 0.f) || std::isinf(softmax_scale))
+        return fail(LSA_ERR_INVALID_ARG, "softmax_scale must be finite and >= 0");
+    empty = seq_len == 0;
+    p.q = q;
+    p.out = out;
+    p.k = kv->k;
+    p.v = kv->v;
+    p.page_table = page_table;
+    p.tile_counter = reinterpret_cast<unsigned long long *>(tile_counter);
+    p.seq_len = seq_len;
+    p.num_q_heads = num_q_heads;
+    p.num_kv_heads = kv->num_kv_heads;
+    p.group = num_q_heads / kv->num_kv_heads;
+    p.head_dim = kv->head_dim;
+    p.page_size = kv->page_size;
+    p.n_qblocks = (seq_len + 63) / 64;
+    p.head_groups = (p.group + 3) / 4;
+    p.n_ret = 0;
+    p.n_str = 0;
+    const long long items = (long long)kv->num_kv_heads * p.n_qblocks * p.head_groups;
+    if (items > (long long)INT32_MAX) return fail(LSA_ERR_UNSUPPORTED, "prefill launch too large");
+    p.n_items = (int32_t)items;
+    const float scale = softmax_scale > 0.f ? softmax_scale : 1.f / std::sqrt((float)kv->head_dim);
+    p.scale_log2 = scale * 1.4426950408889634f;
+    return LSA_OK;
 }
 
 }  // namespace
@@ -338,51 +385,101 @@ lsa_status lsa_sparse_prefill_attn(const void *q, int32_t q_dtype, const lsa_kv 
                                    void *out, int64_t *tile_counter, void *stream) {
     if (lsa_status s = check_kv(kv)) return s;
     if (lsa_status s = check_heads(heads, kv, true)) return s;
-    if (block != 64) return fail(LSA_ERR_UNSUPPORTED, "block %d: only 64-token tiles are built", block);
-    if (kv->page_size % 64 != 0)
-        return fail(LSA_ERR_UNSUPPORTED, "prefill needs page_size a multiple of 64 (got %d)", kv->page_size);
-    const bool pair_ok = (q_dtype == LSA_F32 && kv->kv_dtype == LSA_F32) ||
-                         (q_dtype == LSA_BF16 && kv->kv_dtype == LSA_BF16);
-    if (!pair_ok)
-        return fail(LSA_ERR_UNSUPPORTED, "(q_dtype %d, kv_dtype %d) is not a supported prefill pair", q_dtype,
-                    kv->kv_dtype);
-    if (q_dtype == LSA_F32 && kv->head_dim != 64)
-        return fail(LSA_ERR_UNSUPPORTED, "f32 prefill is built for head_dim 64 only");
-    if (seq_len < 0) return fail(LSA_ERR_INVALID_ARG, "seq_len %d < 0", seq_len);
-    if (!q || !out || (seq_len > 0 && !page_table))
-        return fail(LSA_ERR_INVALID_ARG, "q, out and page_table must be non-NULL");
-    if (!(softmax_scale >= 0.f) || std::isinf(softmax_scale))
-        return fail(LSA_ERR_INVALID_ARG, "softmax_scale must be finite and >= 0");
-    if (seq_len == 0) return ok();
     PrefillArgs p{};
-    p.q = q;
-    p.out = out;
-    p.k = kv->k;
-    p.v = kv->v;
-    p.page_table = page_table;
-    p.tile_counter = reinterpret_cast<unsigned long long *>(tile_counter);
-    p.seq_len = seq_len;
-    p.num_q_heads = heads->num_q_heads;
-    p.num_kv_heads = kv->num_kv_heads;
-    p.group = heads->num_q_heads / kv->num_kv_heads;
-    p.head_dim = kv->head_dim;
-    p.page_size = kv->page_size;
+    bool empty = false;
+    if (lsa_status s = prefill_setup(p, q, q_dtype, kv, page_table, seq_len, heads->num_q_heads, block,
+                                     softmax_scale, out, tile_counter, empty))
+        return s;
+    if (empty) return ok();
     p.sink_blocks = heads->sink_blocks;
     p.local_blocks = heads->local_blocks;
-    p.n_qblocks = (seq_len + 63) / 64;
-    p.head_groups = (p.group + 3) / 4;
-    p.n_ret = 0;
-    p.n_str = 0;
     for (int i = 0; i < kv->num_kv_heads; ++i) {
         if (heads->head_kind[i] == LSA_RETRIEVAL_HEAD) p.ret_heads[p.n_ret++] = (uint8_t)i;
         else p.str_heads[p.n_str++] = (uint8_t)i;
     }
-    const long long items = (long long)kv->num_kv_heads * p.n_qblocks * p.head_groups;
-    if (items > (long long)INT32_MAX) return fail(LSA_ERR_UNSUPPORTED, "prefill launch too large");
-    p.n_items = (int32_t)items;
-    const float scale = softmax_scale > 0.f ? softmax_scale : 1.f / std::sqrt((float)kv->head_dim);
-    p.scale_log2 = scale * 1.4426950408889634f;
     return from_hip(launch_prefill(p, q_dtype, (hipStream_t)stream), "prefill launch");
+}
+
+lsa_status lsa_sparse_prefill_attn_csr(const void *q, int32_t q_dtype, const lsa_kv *kv,
+                                       const int32_t *page_table, int32_t seq_len, int32_t num_q_heads,
+                                       int32_t block, const int32_t *row_ptr, const int32_t *col_idx,
+                                       int32_t nnz, const int32_t *order, float softmax_scale, void *out,
+                                       int64_t *tile_counter, void *stream) {
+    if (lsa_status s = check_kv(kv)) return s;
+    if (num_q_heads < 1 || num_q_heads % kv->num_kv_heads != 0)
+        return fail(LSA_ERR_INVALID_ARG, "num_q_heads %d is not a positive multiple of num_kv_heads %d",
+                    num_q_heads, kv->num_kv_heads);
+    if (num_q_heads / kv->num_kv_heads > 16)
+        return fail(LSA_ERR_UNSUPPORTED, "GQA group size %d > 16", num_q_heads / kv->num_kv_heads);
+    if (nnz < 0) return fail(LSA_ERR_INVALID_ARG, "nnz %d < 0", nnz);
+    if (!row_ptr || (nnz > 0 && !col_idx)) return fail(LSA_ERR_INVALID_ARG, "row_ptr and col_idx must be non-NULL");
+    PrefillArgs p{};
+    bool empty = false;
+    if (lsa_status s = prefill_setup(p, q, q_dtype, kv, page_table, seq_len, num_q_heads, block, softmax_scale, out,
+                                     tile_counter, empty))
+        return s;
+    if (empty) return ok();
+    // every KV head follows its own rows of the mask; work items are ordered like retrieval heads
+    for (int i = 0; i < kv->num_kv_heads; ++i) p.ret_heads[p.n_ret++] = (uint8_t)i;
+    p.row_ptr = row_ptr;
+    p.col_idx = col_idx;
+    p.nnz = nnz;
+    p.order = order;
+    return from_hip(launch_prefill(p, q_dtype, (hipStream_t)stream), "prefill launch");
+}
+
+lsa_status lsa_block_mask_schedule(const int32_t *row_ptr, int32_t num_kv_heads, int32_t num_q_heads,
+                                   int32_t seq_len, int32_t block, int32_t *order) {
+    if (block != 64) return fail(LSA_ERR_UNSUPPORTED, "block %d: only 64-token tiles are built", block);
+    if (num_kv_heads < 1 || num_q_heads < 1 || num_q_heads % num_kv_heads != 0 || seq_len < 0)
+        return fail(LSA_ERR_INVALID_ARG, "num_kv_heads %d, num_q_heads %d, seq_len %d", num_kv_heads, num_q_heads,
+                    seq_len);
+    if (!row_ptr || !order) return fail(LSA_ERR_INVALID_ARG, "row_ptr and order must be non-NULL");
+    const int n = (seq_len + 63) / 64;
+    const int hg = (num_q_heads / num_kv_heads + 3) / 4;
+    std::vector<std::pair<long long, int>> items;       // (sort key, item code)
+    items.reserve((size_t)num_kv_heads * n * hg);
+    for (int h = 0; h < num_kv_heads; ++h)
+        for (int a = 0; a < n; ++a) {
+            const long long len = (long long)row_ptr[(size_t)h * (n + 1) + a + 1] - row_ptr[(size_t)h * (n + 1) + a];
+            for (int g = 0; g < hg; ++g) {
+                const int code = (h * n + a) * hg + g;
+                // longest rows first; among equal lengths, later query tiles first, then the code
+                items.push_back({-(len * ((long long)n + 1) + a), code});
+            }
+        }
+    std::stable_sort(items.begin(), items.end(),
+                     [](const std::pair<long long, int> &x, const std::pair<long long, int> &y) {
+                         return x.first < y.first;
+                     });
+    for (size_t i = 0; i < items.size(); ++i) order[i] = items[i].second;
+    return ok();
+}
+
+lsa_status lsa_check_block_mask(const int32_t *row_ptr, const int32_t *col_idx, int32_t num_kv_heads,
+                                int32_t seq_len, int32_t block, int32_t nnz) {
+    if (block != 64) return fail(LSA_ERR_UNSUPPORTED, "block %d: only 64-token tiles are built", block);
+    if (num_kv_heads < 1 || seq_len < 0 || nnz < 0)
+        return fail(LSA_ERR_INVALID_ARG, "num_kv_heads %d, seq_len %d, nnz %d", num_kv_heads, seq_len, nnz);
+    if (!row_ptr || (nnz > 0 && !col_idx)) return fail(LSA_ERR_INVALID_ARG, "row_ptr and col_idx must be non-NULL");
+    const int n = (seq_len + 63) / 64;
+    for (int h = 0; h < num_kv_heads; ++h) {
+        const int32_t *rp = row_ptr + (size_t)h * (n + 1);
+        if (rp[0] < 0) return fail(LSA_ERR_INVALID_ARG, "head %d: row_ptr[0] = %d < 0", h, rp[0]);
+        for (int a = 0; a < n; ++a) {
+            if (rp[a + 1] < rp[a] || rp[a + 1] > nnz)
+                return fail(LSA_ERR_INVALID_ARG, "head %d, query tile %d: row_ptr %d -> %d outside [.., %d]", h, a,
+                            rp[a], rp[a + 1], nnz);
+            for (int e = rp[a]; e < rp[a + 1]; ++e) {
+                const int c = col_idx[e];
+                if (c < 0 || c > a)
+                    return fail(LSA_ERR_INVALID_ARG, "head %d, query tile %d: key tile %d outside [0, %d]", h, a, c, a);
+                if (e > rp[a] && c <= col_idx[e - 1])
+                    return fail(LSA_ERR_INVALID_ARG, "head %d, query tile %d: key tiles not strictly ascending", h, a);
+            }
+        }
+    }
+    return ok();
 }
 
 }  // extern "C"

@@ -276,6 +276,13 @@ struct PrefillArgs {
     int32_t n_ret, n_str;         // retrieval / streaming KV heads
     uint8_t ret_heads[kMaxKvHeads];
     uint8_t str_heads[kMaxKvHeads];
+    // static block mask (CSR): per KV head, row_ptr[h * (n_qblocks + 1) + a]
+    // .. [.. + a + 1] index col_idx, the key tiles of query tile a
+    const int32_t *row_ptr;
+    const int32_t *col_idx;
+    int32_t nnz;
+    // optional work order of a static mask: order[blockIdx] = (kv * n_qblocks + a) * head_groups + hg
+    const int32_t *order;
 };
 
 // ----------------------------------------------------------------------------

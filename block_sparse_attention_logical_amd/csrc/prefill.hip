@@ -39,15 +39,30 @@ struct PItem {
     bool streaming;
 };
 
-// blockIdx -> (kv head, query tile, head group), longest rows first
+// blockIdx -> (kv head, query tile, head group), longest rows first.
+// Workgroups are handed to the XCDs in number order, round robin, so each
+// round of consecutive numbers should hold rows of equal length: a round that
+// mixes long and short rows leaves the XCDs of the short ones waiting for the
+// others.  Head-kind patterns order rows by a and kind.  A static block mask
+// comes with its own order (rows sorted by length, computed once per mask);
+// without one, the head of consecutive workgroups rotates every round.
+template <bool CSR>
 __device__ __forceinline__ PItem prefill_item(const PrefillArgs &p) {
     PItem it;
     const int nq = p.n_qblocks, HG = p.head_groups;
     int i = blockIdx.x;
+    if (CSR && p.order) {
+        const int code = min(max(p.order[i], 0), p.n_items - 1);
+        it.hg = code % HG;
+        it.a = (code / HG) % nq;
+        it.kv = code / (HG * nq);
+        it.streaming = false;
+        return it;
+    }
     const int n_ret_items = p.n_ret * nq * HG;
     if (i < n_ret_items) {
-        it.kv = p.ret_heads[i % p.n_ret];
         const int j = i / p.n_ret;
+        it.kv = p.ret_heads[CSR ? (i + j) % p.n_ret : i % p.n_ret];
         it.hg = j % HG;
         it.a = nq - 1 - j / HG;
         it.streaming = false;
@@ -62,11 +77,37 @@ __device__ __forceinline__ PItem prefill_item(const PrefillArgs &p) {
     return it;
 }
 
-// visible key tiles of query tile a, ascending: [0, e0) U [s1, a]
-__device__ __forceinline__ void tile_ranges(const PrefillArgs &p, const PItem &it, int &e0, int &s1) {
-    if (!it.streaming) { e0 = 0; s1 = 0; return; }
-    e0 = min(p.sink_blocks, it.a + 1);
-    s1 = max(it.a - p.local_blocks + 1, e0);
+// The key tiles a work item visits, ascending.  Head-kind patterns: [0, e0)
+// U [s1, a].  Static block masks: entries rp0 .. rp0 + n - 1 of col_idx; the
+// row offsets are clamped to [0, nnz] and the tiles to [0, a], so a malformed
+// mask cannot make the kernel read outside the arrays or the sequence.
+struct TileRow {
+    int e0, s1, rp0, n;
+};
+
+template <bool CSR>
+__device__ __forceinline__ TileRow tile_row(const PrefillArgs &p, const PItem &it) {
+    TileRow r{0, 0, 0, 0};
+    if constexpr (CSR) {
+        const int32_t *rp = p.row_ptr + (size_t)it.kv * (p.n_qblocks + 1) + it.a;
+        const int b0 = min(max(rp[0], 0), p.nnz);
+        const int b1 = min(max(rp[1], b0), p.nnz);
+        r.rp0 = b0;
+        r.n = b1 - b0;
+    } else {
+        if (it.streaming) {
+            r.e0 = min(p.sink_blocks, it.a + 1);
+            r.s1 = max(it.a - p.local_blocks + 1, r.e0);
+        }
+        r.n = r.e0 + (it.a - r.s1 + 1);
+    }
+    return r;
+}
+
+template <bool CSR>
+__device__ __forceinline__ int row_tile(const PrefillArgs &p, const PItem &it, const TileRow &r, int ii) {
+    if constexpr (CSR) return min(max(p.col_idx[r.rp0 + ii], 0), it.a);
+    else return ii < r.e0 ? ii : r.s1 + (ii - r.e0);
 }
 
 // ---------------------------------------------------------------------------
@@ -81,7 +122,7 @@ __device__ __forceinline__ void tile_ranges(const PrefillArgs &p, const PItem &i
 // the compute runs, one barrier per tile.  The last tile is the diagonal one:
 // its causal mask is applied in the pipeline's epilogue only.
 // ---------------------------------------------------------------------------
-template <int D>
+template <int D, bool CSR>
 __global__ __launch_bounds__(512, 2) void prefill_bf16_kernel(PrefillArgs p) {
     typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
     typedef float floatx2 __attribute__((ext_vector_type(2)));
@@ -95,9 +136,8 @@ __global__ __launch_bounds__(512, 2) void prefill_bf16_kernel(PrefillArgs p) {
     __shared__ __attribute__((aligned(16))) uint16_t k_lds[2][kTile * D];
     __shared__ __attribute__((aligned(16))) uint16_t v_lds[2][kTile * D];
 
-    const PItem it = prefill_item(p);
-    int e0, s1;
-    tile_ranges(p, it, e0, s1);
+    const PItem it = prefill_item<CSR>(p);
+    const TileRow trow = tile_row<CSR>(p, it);
 
     const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
     const int T = p.seq_len, G = p.group, HQ = p.num_q_heads, NP = p.page_size;
@@ -106,6 +146,17 @@ __global__ __launch_bounds__(512, 2) void prefill_bf16_kernel(PrefillArgs p) {
     const int hq = it.kv * G + min(hq_local, G - 1);
     const int q0 = it.a * kTile + 32 * (wave & 1);  // first query row of this wave
     const int col = lane & 31, lg = lane >> 5;      // MFMA column / lane group
+    const int n_iter = trow.n;
+    if (n_iter == 0) {                              // a query tile without key tiles: zero output
+        const int row = q0 + col;
+        if (!head_ok || row >= T) return;
+        uint16_t *orow = static_cast<uint16_t *>(p.out) + ((size_t)row * HQ + hq) * D;
+#pragma unroll
+        for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+            for (int rb = 0; rb < 4; ++rb) *reinterpret_cast<uint2 *>(orow + 32 * dt + 8 * rb + 4 * lg) = make_uint2(0, 0);
+        return;
+    }
 
     // Q^T as B operand: query q0 + col, channels 16*s + 8*lg + j
     bf16x8 qb[D / 16];
@@ -127,8 +178,28 @@ __global__ __launch_bounds__(512, 2) void prefill_bf16_kernel(PrefillArgs p) {
 
     const uint16_t *kpool = static_cast<const uint16_t *>(p.k);
     const uint16_t *vpool = static_cast<const uint16_t *>(p.v);
-    const int n_iter = e0 + (it.a - s1 + 1);
-    auto tile_of = [&](int ii) { return ii < e0 ? ii : s1 + (ii - e0); };
+    // Static masks: the row's key tiles stream through two 64-entry register
+    // windows (entries w0 .. w0 + 127 of the row, one per lane), read with
+    // readlane; a window is refilled about 60 steps before it is needed, so
+    // no step waits on an index load.
+    int win_lo = 0, win_hi = 0, w0 = 0;
+    auto load_win = [&](int base) {
+        const int e = base + lane;
+        return e < n_iter ? p.col_idx[trow.rp0 + e] : 0;
+    };
+    if constexpr (CSR) {
+        win_lo = load_win(0);
+        win_hi = load_win(kWave);
+    }
+    auto tile_of = [&](int ii) {
+        if constexpr (CSR) {
+            const int j = ii - w0;
+            const int c = j < kWave ? __builtin_amdgcn_readlane(win_lo, j) : __builtin_amdgcn_readlane(win_hi, j - kWave);
+            return min(max(c, 0), it.a);
+        } else {
+            return row_tile<false>(p, it, trow, ii);
+        }
+    };
     // A 64-key tile is two whole 32-token blocks of its page: its keys (and its
     // values) are one contiguous run of 64 * D elements laid out like the LDS tile.
     auto tile_base = [&](int c) {
@@ -254,6 +325,14 @@ __global__ __launch_bounds__(512, 2) void prefill_bf16_kernel(PrefillArgs p) {
             zero_v_tail(ii & 1, ii);
         }
         __syncthreads();
+        if constexpr (CSR) {
+            // the next step reads entries ii .. ii + 2: slide the windows once ii leaves the low one
+            if (ii >= w0 + kWave) {
+                w0 += kWave;
+                win_lo = win_hi;
+                win_hi = load_win(w0 + kWave);
+            }
+        }
     };
     int ii = 0;
     for (; ii + 1 < n_iter; ii += 2) {
@@ -295,15 +374,14 @@ __global__ __launch_bounds__(512, 2) void prefill_bf16_kernel(PrefillArgs p) {
 // ---------------------------------------------------------------------------
 // f32 VALU kernel: lane = query row, wave = query head; K/V tiles in LDS
 // ---------------------------------------------------------------------------
-template <int D>
+template <int D, bool CSR>
 __global__ __launch_bounds__(256) void prefill_f32_kernel(PrefillArgs p) {
     extern __shared__ float sm[];
     float *k_lds = sm;                 // [64][D]
     float *v_lds = sm + kTile * D;     // [D][64]
 
-    const PItem it = prefill_item(p);
-    int e0, s1;
-    tile_ranges(p, it, e0, s1);
+    const PItem it = prefill_item<CSR>(p);
+    const TileRow trow = tile_row<CSR>(p, it);
 
     const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
     const int T = p.seq_len, G = p.group, HQ = p.num_q_heads, NP = p.page_size;
@@ -321,9 +399,9 @@ __global__ __launch_bounds__(256) void prefill_f32_kernel(PrefillArgs p) {
 
     const float *kpool = static_cast<const float *>(p.k);
     const float *vpool = static_cast<const float *>(p.v);
-    const int n_iter = e0 + (it.a - s1 + 1);
+    const int n_iter = trow.n;
     for (int ii = 0; ii < n_iter; ++ii) {
-        const int c = ii < e0 ? ii : s1 + (ii - e0);
+        const int c = row_tile<CSR>(p, it, trow, ii);
         const int key0 = c * kTile;
         const int pool = p.page_table[key0 / NP];
         const int slot0 = key0 % NP;
@@ -370,24 +448,30 @@ __global__ __launch_bounds__(256) void prefill_f32_kernel(PrefillArgs p) {
     }
     if (!head_ok || qrow >= T) return;
     float *orow = static_cast<float *>(p.out) + ((size_t)qrow * HQ + hq) * D;
-    const float inv = 1.f / l_run;
+    const float inv = l_run > 0.f ? 1.f / l_run : 0.f;      // no visible key: zero output
 #pragma unroll
     for (int d = 0; d < D; ++d) orow[d] = o[d] * inv;
 }
 
 }  // namespace
 
-hipError_t launch_prefill(const PrefillArgs &p, int dtype, hipStream_t s) {
-    if (p.n_items == 0) return hipSuccess;
-    const dim3 grid((unsigned)p.n_items), block(256);
+template <bool CSR>
+void launch_prefill_kernels(const PrefillArgs &p, int dtype, hipStream_t s) {
+    const dim3 grid((unsigned)p.n_items);
     if (dtype == LSA_BF16) {
-        if (p.head_dim == 128) hipLaunchKernelGGL(prefill_bf16_kernel<128>, grid, dim3(512), 0, s, p);
-        else hipLaunchKernelGGL(prefill_bf16_kernel<64>, grid, dim3(512), 0, s, p);
+        if (p.head_dim == 128) hipLaunchKernelGGL((prefill_bf16_kernel<128, CSR>), grid, dim3(512), 0, s, p);
+        else hipLaunchKernelGGL((prefill_bf16_kernel<64, CSR>), grid, dim3(512), 0, s, p);
     } else {
         // f32 is the small-model path: head_dim 64 only (validated by the caller)
         const size_t lds = 2 * (size_t)kTile * 64 * sizeof(float);
-        hipLaunchKernelGGL(prefill_f32_kernel<64>, grid, block, lds, s, p);
+        hipLaunchKernelGGL((prefill_f32_kernel<64, CSR>), grid, dim3(256), lds, s, p);
     }
+}
+
+hipError_t launch_prefill(const PrefillArgs &p, int dtype, hipStream_t s) {
+    if (p.n_items == 0) return hipSuccess;
+    if (p.row_ptr) launch_prefill_kernels<true>(p, dtype, s);
+    else launch_prefill_kernels<false>(p, dtype, s);
     return hipGetLastError();
 }
 

@@ -35,6 +35,9 @@ EXPORTED = (
     "lsa_decode_workspace",
     "lsa_sparse_decode_attn",
     "lsa_sparse_prefill_attn",
+    "lsa_sparse_prefill_attn_csr",
+    "lsa_block_mask_schedule",
+    "lsa_check_block_mask",
     "lsa_last_error",
     "lsa_version",
 )
@@ -109,6 +112,11 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
                                            ctypes.c_int32, ctypes.c_float, vp, vp, vp, ctypes.c_size_t, vp]
     lib.lsa_sparse_prefill_attn.argtypes = [vp, ctypes.c_int32, P(LsaKV), vp, ctypes.c_int32, P(LsaHeads),
                                             ctypes.c_int32, ctypes.c_float, vp, vp, vp]
+    lib.lsa_sparse_prefill_attn_csr.argtypes = [vp, ctypes.c_int32, P(LsaKV), vp, ctypes.c_int32, ctypes.c_int32,
+                                                ctypes.c_int32, vp, vp, ctypes.c_int32, vp, ctypes.c_float, vp, vp,
+                                                vp]
+    lib.lsa_block_mask_schedule.argtypes = [vp, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, vp]
+    lib.lsa_check_block_mask.argtypes = [vp, vp, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32]
     for name in EXPORTED[:-2]:
         getattr(lib, name).restype = st
     lib.lsa_last_error.restype = ctypes.c_char_p
@@ -257,3 +265,41 @@ def sparse_prefill_attn(q: torch.Tensor, kv: KVPool, page_table: torch.Tensor, s
     _check(load().lsa_sparse_prefill_attn(_ptr(q), dtype_code(q), ctypes.byref(kv.desc()), _ptr(page_table),
                                           seq_len, ctypes.byref(heads.desc()), block, softmax_scale, _ptr(out),
                                           _ptr(tile_counter), _stream(stream)))
+
+
+def sparse_prefill_attn_csr(q: torch.Tensor, kv: KVPool, page_table: torch.Tensor, seq_len: int, num_q_heads: int,
+                            row_ptr: torch.Tensor, col_idx: torch.Tensor, out: torch.Tensor,
+                            order: Optional[torch.Tensor] = None, block: int = 64, softmax_scale: float = 0.0,
+                            tile_counter: Optional[torch.Tensor] = None, stream=None) -> None:
+    """Prefill under a static block mask: row_ptr [H_kv][n + 1], col_idx [nnz]
+    and the optional work order of block_mask_schedule, int32 device tensors
+    (layout in include/lsa.h)."""
+    assert row_ptr.dtype == torch.int32 and col_idx.dtype == torch.int32
+    assert order is None or order.dtype == torch.int32
+    _check(load().lsa_sparse_prefill_attn_csr(_ptr(q), dtype_code(q), ctypes.byref(kv.desc()), _ptr(page_table),
+                                              seq_len, num_q_heads, block, _ptr(row_ptr), _ptr(col_idx),
+                                              col_idx.numel(), _ptr(order), softmax_scale, _ptr(out),
+                                              _ptr(tile_counter), _stream(stream)))
+
+
+def block_mask_schedule(row_ptr: torch.Tensor, num_kv_heads: int, num_q_heads: int, seq_len: int,
+                        block: int = 64) -> torch.Tensor:
+    """Work order of a static block mask (host row_ptr in, host int32 order out)."""
+    assert row_ptr.device.type == "cpu"
+    rp = row_ptr.to(torch.int32).contiguous()
+    n = -(-seq_len // block)
+    hg = -(-(num_q_heads // num_kv_heads) // 4)
+    order = torch.empty(num_kv_heads * n * hg, dtype=torch.int32)
+    _check(load().lsa_block_mask_schedule(rp.data_ptr(), num_kv_heads, num_q_heads, seq_len, block,
+                                          order.data_ptr()))
+    return order
+
+
+def check_block_mask(row_ptr: torch.Tensor, col_idx: torch.Tensor, num_kv_heads: int, seq_len: int,
+                     block: int = 64) -> None:
+    """Validate a block mask held in host memory; raises LsaError if malformed."""
+    assert row_ptr.device.type == "cpu" and col_idx.device.type == "cpu"
+    rp = row_ptr.to(torch.int32).contiguous()
+    ci = col_idx.to(torch.int32).contiguous()
+    _check(load().lsa_check_block_mask(rp.data_ptr(), ci.data_ptr() if ci.numel() else None, num_kv_heads,
+                                       seq_len, block, ci.numel()))

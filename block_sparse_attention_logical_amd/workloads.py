@@ -317,3 +317,32 @@ def make_prefill(cfg: int, device="cpu", *, seq_len: Optional[int] = None, seed:
                            page_size=NP, logical_page=c["logical_page"], sink_blocks=c["sink_blocks"],
                            local_blocks=c["local_blocks"], head_kind=kinds, num_pages=P, page_table=table,
                            q=q, k=k, v=v, scales=dict(q=sq, k=sk, v=sv))
+
+
+# ---------------------------------------------------------------------------
+# static block masks (inputs of the CSR prefill)
+# ---------------------------------------------------------------------------
+
+def csr_from_tile_masks(masks) -> "tuple[torch.Tensor, torch.Tensor]":
+    """Per-KV-head tile masks [H][n][n] (bool; row = query tile, column = key
+    tile) -> row_ptr [H][n + 1] (offsets into one shared col_idx) and col_idx
+    [nnz], int32 tensors on the CPU, key tiles ascending within a row."""
+    m = torch.as_tensor(masks).bool().cpu()
+    H, n, _ = m.shape
+    offs = torch.zeros(H * n + 1, dtype=torch.int64)
+    offs[1:] = torch.cumsum(m.sum(dim=2).reshape(-1), 0)
+    row_ptr = torch.stack([offs[h * n: h * n + n + 1] for h in range(H)]).to(torch.int32)
+    col_idx = m.nonzero()[:, 2].to(torch.int32).contiguous()     # (h, a, c) in lexicographic order
+    return row_ptr.contiguous(), col_idx
+
+
+def random_tile_masks(num_kv_heads: int, n_blocks: int, density: float, seed: int,
+                      diagonal: bool = True) -> torch.Tensor:
+    """Seeded random tile masks [H][n][n]: each tile below the diagonal kept
+    with probability `density`, the diagonal tiles kept when `diagonal`."""
+    g = torch.Generator().manual_seed(seed)
+    m = torch.rand((num_kv_heads, n_blocks, n_blocks), generator=g) < density
+    m = torch.tril(m, diagonal=-1)
+    if diagonal:
+        m |= torch.eye(n_blocks, dtype=torch.bool)[None]
+    return m

@@ -251,6 +251,52 @@ lsa_status lsa_sparse_prefill_attn(const void *q, int32_t q_dtype, const lsa_kv 
                                    float softmax_scale, void *out,
                                    int64_t *tile_counter, void *stream);
 
+/* Block-sparse causal prefill attention of one sequence under an arbitrary
+ * static block mask given as per-KV-head CSR lists of key tiles ([LS-X]
+ * 統一ブロックスパースアテンション: an iterator over the non-empty blocks of a
+ * static pattern, cost falling as 1/(1-r); 主要な貢献: iterator-based
+ * block-sparse kernels).
+ *
+ * Tiles are block x block tokens (block must be 64); n = ceil(seq_len / 64).
+ * row_ptr: [device] int32 [num_kv_heads][n + 1]; the key tiles of query tile a
+ * for KV head kv are col_idx[row_ptr[kv][a] .. row_ptr[kv][a + 1]), offsets
+ * into col_idx of nnz int32 entries ([device]).  A valid mask has
+ * 0 <= row_ptr[kv][0] <= ... <= row_ptr[kv][n] <= nnz and, within a row, key
+ * tiles strictly ascending in [0, a]; lsa_check_block_mask validates a host
+ * copy.  The kernels clamp offsets to [0, nnz] and tiles to [0, a], so a
+ * malformed mask gives unspecified outputs but no access outside the arrays.
+ * Inside a listed tile, key p is seen by query t iff p <= t; a query tile
+ * with an empty row gets zero output.  The query heads of a KV head share its
+ * rows.  q, out, page_table, dtypes, softmax_scale and tile_counter are as for
+ * lsa_sparse_prefill_attn (the counter adds (row length) x G per row).
+ * order: NULL, or [device] int32 [num_kv_heads * n * ceil(G / 4)], the work
+ * order written by lsa_block_mask_schedule for this mask (entries are clamped
+ * to the item range).  Workgroups start in this order, round robin over the
+ * XCDs, so rows of equal length side by side keep every XCD busy; a mask whose
+ * rows differ in length runs up to twice as fast with it. */
+lsa_status lsa_sparse_prefill_attn_csr(const void *q, int32_t q_dtype, const lsa_kv *kv,
+                                       const int32_t *page_table, int32_t seq_len,
+                                       int32_t num_q_heads, int32_t block,
+                                       const int32_t *row_ptr, const int32_t *col_idx,
+                                       int32_t nnz, const int32_t *order, float softmax_scale,
+                                       void *out, int64_t *tile_counter, void *stream);
+
+/* Work order of a static block mask for lsa_sparse_prefill_attn_csr, computed
+ * once per mask on the host: row_ptr is a [host] copy ([num_kv_heads][n + 1]);
+ * order ([host] out, num_kv_heads * n * ceil(G / 4) int32) receives every work
+ * item (kv * n + a) * ceil(G / 4) + g once, longest rows first, then later
+ * query tiles first. */
+lsa_status lsa_block_mask_schedule(const int32_t *row_ptr, int32_t num_kv_heads,
+                                   int32_t num_q_heads, int32_t seq_len, int32_t block,
+                                   int32_t *order);
+
+/* Host-side check of a block mask for lsa_sparse_prefill_attn_csr: row_ptr
+ * and col_idx are [host] copies with the layout above.  Returns LSA_OK, or
+ * LSA_ERR_INVALID_ARG naming the first bad head / query tile. */
+lsa_status lsa_check_block_mask(const int32_t *row_ptr, const int32_t *col_idx,
+                                int32_t num_kv_heads, int32_t seq_len, int32_t block,
+                                int32_t nnz);
+
 /* Message of the last failed call on this thread ("" if none); never NULL. */
 const char *lsa_last_error(void);
 

@@ -10,7 +10,7 @@ import subprocess
 
 import pytest
 
-from block_sparse_attention_logical_amd import lsa
+from block_sparse_attention_logical_amd import lsa, workloads as W
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "lsa.h")
@@ -190,6 +190,70 @@ def test_prefill_validation(lib):
     assert prefill(lib, q_dtype=lsa.F32) == lsa.LSA_ERR_UNSUPPORTED            # mixed pair
     assert prefill(lib, T=-1) == lsa.LSA_ERR_INVALID_ARG
     assert prefill(lib, T=0) == lsa.LSA_OK                                     # nothing to do
+
+
+def prefill_csr(lib, kv=None, block=64, T=1000, rp=FAKE, ci=FAKE, nnz=10, hq=32):
+    kv = kv or kv_desc()
+    return lib.lsa_sparse_prefill_attn_csr(FAKE, lsa.BF16, ctypes.byref(kv), FAKE, T, hq, block, rp, ci, nnz,
+                                           None, 0.0, FAKE, None, None)
+
+
+def test_prefill_csr_validation(lib):
+    assert prefill_csr(lib, block=128) == lsa.LSA_ERR_UNSUPPORTED
+    assert prefill_csr(lib, rp=None) == lsa.LSA_ERR_INVALID_ARG
+    assert prefill_csr(lib, ci=None) == lsa.LSA_ERR_INVALID_ARG
+    assert prefill_csr(lib, nnz=-1) == lsa.LSA_ERR_INVALID_ARG
+    assert prefill_csr(lib, hq=12) == lsa.LSA_ERR_INVALID_ARG                 # not a multiple of 8 KV heads
+    assert prefill_csr(lib, hq=8 * 32) == lsa.LSA_ERR_UNSUPPORTED             # group of 32
+    assert prefill_csr(lib, T=0) == lsa.LSA_OK                                # nothing to do
+    assert prefill_csr(lib, T=0, ci=None, nnz=0) == lsa.LSA_OK
+
+
+def test_check_block_mask():
+    """The host-side mask checker accepts CSR lists built from tile masks and
+    names the first malformed row."""
+    m = W.random_tile_masks(2, 9, 0.4, 3)
+    rp, ci = W.csr_from_tile_masks(m)
+    lsa.check_block_mask(rp, ci, 2, 9 * 64)
+    lsa.check_block_mask(rp, ci, 2, 8 * 64 + 1)                 # ragged last tile
+    empty_rows = m.clone()
+    empty_rows[1, 4] = False
+    lsa.check_block_mask(*W.csr_from_tile_masks(empty_rows), 2, 9 * 64)   # empty rows are allowed
+    bad = ci.clone()
+    bad[int(rp[0, 5])] = 6                                       # tile above the diagonal
+    with pytest.raises(lsa.LsaError, match="query tile 5"):
+        lsa.check_block_mask(rp, bad, 2, 9 * 64)
+    r2 = int(rp[1, 6])
+    assert int(rp[1, 7]) - r2 >= 2
+    bad = ci.clone()
+    bad[r2], bad[r2 + 1] = ci[r2 + 1], ci[r2]                    # descending within a row
+    with pytest.raises(lsa.LsaError, match="ascending"):
+        lsa.check_block_mask(rp, bad, 2, 9 * 64)
+    bad_rp = rp.clone()
+    bad_rp[0, 3] = bad_rp[0, 2] - 1                              # offsets decrease
+    with pytest.raises(lsa.LsaError, match="head 0"):
+        lsa.check_block_mask(bad_rp, ci, 2, 9 * 64)
+    bad_rp = rp.clone()
+    bad_rp[1, 9] = ci.numel() + 1                                # past nnz
+    with pytest.raises(lsa.LsaError, match="head 1"):
+        lsa.check_block_mask(bad_rp, ci, 2, 9 * 64)
+
+
+def test_block_mask_schedule():
+    """The work order of a mask lists every (KV head, query tile, head group)
+    item once, rows in non-increasing length."""
+    for H, G, n in ((8, 4, 13), (4, 8, 9), (32, 1, 5)):
+        m = W.random_tile_masks(H, n, 0.35, seed=H * n)
+        m[0, 2] = False                                          # an empty row
+        rp, _ = W.csr_from_tile_masks(m)
+        order = lsa.block_mask_schedule(rp, H, H * G, n * 64 - 3)
+        hg = -(-G // 4)
+        assert sorted(order.tolist()) == list(range(H * n * hg))
+        lens = (rp[:, 1:] - rp[:, :-1]).reshape(-1)             # [H * n], row (kv, a) at kv * n + a
+        row_len = [int(lens[int(c) // hg]) for c in order]
+        assert all(x >= y for x, y in zip(row_len, row_len[1:]))
+    with pytest.raises(lsa.LsaError):
+        lsa.block_mask_schedule(rp, 32, 31, 5 * 64)
 
 
 def test_stats_validation(lib):

@@ -1,5 +1,8 @@
 """GPU parity of block-sparse prefill attention against the fp64 oracle, and
 the tile counter against the oracle's block accounting."""
+import json
+import os
+
 import numpy as np
 import pytest
 import torch
@@ -129,4 +132,108 @@ def test_prefill_full_size_cfg7_mha_sampled():
     rows = [0, 63, 64, 1087, 65536, 131071]
     print("max abs err", check(p, out, rows=rows, heads=[ret, st]))
     del out, p
+    torch.cuda.empty_cache()
+
+
+# ---------------------------------------------------------------------------
+# static block masks (CSR)
+# ---------------------------------------------------------------------------
+
+def run_prefill_csr(p, masks, scheduled=True):
+    """masks: [H_kv][n][n] bool tile masks; returns (out, tile counter).  The
+    work order of the mask is used unless scheduled is False."""
+    kv = lsa.KVPool(p.dtype, p.k, p.v, p.num_kv_heads, p.head_dim, p.page_size, p.logical_page, p.num_pages)
+    row_ptr, col_idx = W.csr_from_tile_masks(masks)
+    lsa.check_block_mask(row_ptr, col_idx, p.num_kv_heads, p.seq_len)
+    order = lsa.block_mask_schedule(row_ptr, p.num_kv_heads, p.num_q_heads, p.seq_len).to(DEV) if scheduled else None
+    out = torch.full_like(p.q, float("nan"))
+    cnt = torch.zeros(1, dtype=torch.int64, device=DEV)
+    lsa.sparse_prefill_attn_csr(p.q, kv, p.page_table, p.seq_len, p.num_q_heads, row_ptr.to(DEV),
+                                col_idx.to(DEV), out, order=order, tile_counter=cnt)
+    torch.cuda.synchronize()
+    return out, int(cnt.item())
+
+
+def check_mask(p, out, masks, heads=None, rows=None, tol=2e-2):
+    G = p.num_q_heads // p.num_kv_heads
+    got = H.to_f64(out)
+    worst = 0.0
+    for kv in range(p.num_kv_heads):
+        hs = [kv * G + h for h in range(G) if heads is None or kv * G + h in heads]
+        if not hs:
+            continue
+        keys, values = seq_kv(p, kv)
+        m = np.asarray(masks[kv], dtype=bool)
+        for h in hs:
+            ref = O.block_mask_attention(H.to_f64(p.q[:, h]), keys, values, m, 64, 1 / np.sqrt(p.head_dim), rows=rows)
+            g = got[:, h] if rows is None else got[rows, h]
+            err = np.max(np.abs(g - ref))
+            worst = max(worst, err)
+            assert err <= tol, (kv, h, err)
+    return worst
+
+
+@pytest.mark.parametrize("cfg,T,heads,scheduled", [(1, 1024, None, True), (3, 777, [0, 5, 13, 22, 31], True),
+                                                   (3, 1088, [2, 9, 27], False), (7, 777, [0, 1, 14, 31], True)])
+def test_prefill_csr_random_masks(cfg, T, heads, scheduled):
+    """Random static masks (30% of the tiles below the diagonal, the diagonal
+    kept except in one head, so some query tiles have no key tiles), with and
+    without the mask's work order."""
+    p = W.make_prefill(cfg, DEV, seq_len=T)
+    n = -(-T // 64)
+    masks = W.random_tile_masks(p.num_kv_heads, n, 0.3, seed=cfg * 1000 + T)
+    masks[-1] = W.random_tile_masks(1, n, 0.3, seed=T, diagonal=False)[0]
+    out, cnt = run_prefill_csr(p, masks, scheduled)
+    G = p.num_q_heads // p.num_kv_heads
+    assert cnt == G * int(masks.sum())
+    tol = 1e-5 if p.dtype == W.F32 else 2e-2
+    print("max abs err", check_mask(p, out, masks, heads=heads, tol=tol))
+
+
+def test_prefill_csr_golden_10_of_21():
+    """The pages' worked example on the GPU: a 6 x 6 tile grid with 10 of its 21
+    causal tiles kept, for every KV head; the tile counter counts 10 tiles per
+    query head and the outputs match the oracle."""
+    with open(os.path.join(os.path.dirname(__file__), "golden", "block_mask_10_of_21.json")) as f:
+        g = json.load(f)
+    n = g["n_blocks"]
+    gm = torch.zeros((n, n), dtype=torch.bool)
+    for a, c in g["nonempty"]:
+        gm[a, c] = True
+    p = W.make_prefill(3, DEV, seq_len=n * 64)
+    masks = gm[None].expand(p.num_kv_heads, n, n).clone()
+    out, cnt = run_prefill_csr(p, masks)
+    assert cnt == g["expected_nonempty"] * p.num_q_heads
+    print("max abs err", check_mask(p, out, masks))
+
+
+def test_prefill_csr_kind_masks_equal_analytic():
+    """The causal and Lambda patterns given as CSR lists give bitwise the
+    outputs and the tile count of the head-kind call."""
+    for cfg, T in ((3, 1500), (7, 1100), (1, 1024)):
+        p = W.make_prefill(cfg, DEV, seq_len=T)
+        n = -(-T // 64)
+        masks = torch.stack([torch.from_numpy(O.kind_tile_mask(n, p.head_kind[kv], p.sink_blocks, p.local_blocks))
+                             for kv in range(p.num_kv_heads)])
+        a, ca = run_prefill(p)
+        b, cb = run_prefill_csr(p, masks)
+        assert ca == cb == expected_tiles(p)
+        assert torch.equal(a.view(torch.int16) if a.dtype == torch.bfloat16 else a.view(torch.int32),
+                           b.view(torch.int16) if b.dtype == torch.bfloat16 else b.view(torch.int32)), cfg
+
+
+def test_prefill_csr_full_size_cfg3():
+    """Config 3 at full size with its head-kind patterns given as CSR lists
+    (2.1 million tiles per causal head): the counter gives 34,125,696, and the
+    outputs equal the head-kind call bitwise."""
+    p = W.make_prefill(3, DEV)
+    n = -(-p.seq_len // 64)
+    masks = torch.stack([torch.from_numpy(O.kind_tile_mask(n, p.head_kind[kv], p.sink_blocks, p.local_blocks))
+                         for kv in range(p.num_kv_heads)])
+    b, cb = run_prefill_csr(p, masks)
+    del masks
+    assert cb == 34125696
+    a, ca = run_prefill(p)
+    assert torch.equal(a.view(torch.int16), b.view(torch.int16))
+    del a, b, p
     torch.cuda.empty_cache()
