@@ -22,7 +22,8 @@ and the same patterns given as static block masks (CSR lists of key tiles).
 Variants (the default run is the Llama-3-8B-shaped layer with R = 4 and the
 group's page scores summed): --workload llama2-7b-mha runs the multi-head
 layer (32 KV heads, group size 1) in both legs, --reuse R sets the selection
-interval, --aggregation max combines the group's per-head page scores by max.
+interval, --aggregation max combines the group's per-head page scores by max,
+--page-size / --logical-page change the page geometry of the decode pool.
 """
 from __future__ import annotations
 
@@ -54,6 +55,8 @@ def parse():
     ap.add_argument("--reuse", type=int, default=None, help="selection reuse interval R (default: 4)")
     ap.add_argument("--aggregation", choices=["sum", "max"], default="sum",
                     help="how a KV head's query group combines its page scores")
+    ap.add_argument("--page-size", type=int, default=None, help="physical page size N_P of the decode pool")
+    ap.add_argument("--logical-page", type=int, default=None, help="logical page size N_L of the statistics")
     ap.add_argument("--steps", type=int, default=640, help="timed decode steps (rounded up to whole cycles)")
     ap.add_argument("--warmup", type=int, default=64, help="untimed decode steps")
     ap.add_argument("--replicas", type=int, default=8, help="KV pool replicas (layers) cycled through")
@@ -123,7 +126,8 @@ def bench_decode(args, torch, lsa, W):
     dev = "cuda"
     cfg = WORKLOADS[args.workload][0]
     R = args.reuse or W.DECODE_CONFIGS[cfg]["reuse_interval"]
-    w = W.make_decode(cfg, dev, window=max(R, W.DECODE_CONFIGS[cfg]["window"]))
+    w = W.make_decode(cfg, dev, window=max(R, W.DECODE_CONFIGS[cfg]["window"]), page_size=args.page_size,
+                      logical_page=args.logical_page)
     w.reuse_interval = R
     B, Hq, Hkv, D, NP = w.batch, w.num_q_heads, w.num_kv_heads, w.head_dim, w.page_size
     K = w.token_budget // NP
@@ -268,7 +272,9 @@ def bench_decode(args, torch, lsa, W):
     step_bytes = launch_bytes + sel_bytes
     tok_s = B * steps / elapsed
     src = os.path.join(ROOT, "block_sparse_attention_logical_amd", "csrc", "decode.hip")
-    default = args.workload == "llama3-8b" and R == 4      # the workload the counter summary covers
+    # the workload the counter summary covers
+    default = args.workload == "llama3-8b" and R == 4 and args.page_size in (None, 64) and \
+        args.logical_page in (None, 16)
     return dict(
         w=w, agg=args.aggregation, steps=steps, elapsed=elapsed, tok_s=tok_s, ms_per_step=elapsed / steps * 1e3,
         step_bytes=step_bytes, launch_bytes=launch_bytes, kernel_avg=kernel_avg,

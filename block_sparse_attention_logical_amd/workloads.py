@@ -184,9 +184,15 @@ def tile_values(x: torch.Tensor) -> torch.Tensor:
 
 
 def make_decode(cfg: int, device="cpu", *, batch: Optional[int] = None, ctx=None, window: Optional[int] = None,
-                seed: Optional[int] = None, replicas: int = 1, chunk_pages: int = 2048) -> DecodeWorkload:
-    """Build a decode workload.  Overrides shrink a config for tests."""
+                seed: Optional[int] = None, replicas: int = 1, chunk_pages: int = 2048,
+                page_size: Optional[int] = None, logical_page: Optional[int] = None) -> DecodeWorkload:
+    """Build a decode workload.  Overrides shrink a config for tests or change
+    its page geometry (physical page size N_P, logical page size N_L)."""
     c = dict(DECODE_CONFIGS[cfg])
+    if page_size is not None:
+        c["page_size"] = page_size
+    if logical_page is not None:
+        c["logical_page"] = logical_page
     B = batch if batch is not None else c["batch"]
     W = window if window is not None else c["window"]
     ctx_spec = ctx if ctx is not None else c["ctx"]

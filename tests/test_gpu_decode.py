@@ -239,6 +239,23 @@ def test_decode_reuse_interval(R):
     print("max abs err", check_window(w, kv_heads=ret + st))
 
 
+@pytest.mark.parametrize("NP,NL", [(32, 16), (32, 32), (128, 16), (128, 64), (256, 32), (256, 16)])
+def test_decode_page_geometry(NP, NL):
+    """The config 2 layer with other physical / logical page sizes (g = N_P /
+    N_L from 1 to 16; the same 4096-token budget): the window's outputs match
+    the oracle and the statistics refreshed by the decode calls equal a full
+    build."""
+    import tests.test_gpu_stats_select as S
+    w = W.make_decode(2, DEV, batch=2, ctx=[6000, 9000], page_size=NP, logical_page=NL)
+    ret = [kv for kv in range(w.num_kv_heads) if w.head_kind[kv] == 0][:2]
+    st = [kv for kv in range(w.num_kv_heads) if w.head_kind[kv] == 1][:1]
+    print("max abs err", check_window(w, kv_heads=ret + st))
+    r = Runner(w)
+    for i in range(w.window):
+        r.step(i)
+    S.check_stats(w, r.stats, [c + w.window for c in w.ctx], kinds=w.head_kind)
+
+
 @pytest.mark.parametrize("ctx", [[6000, 9000], [63, 4096 + 17]])
 def test_decode_cfg6_mha_small(ctx):
     """Multi-head attention (32 KV heads, group size 1)."""
