@@ -160,6 +160,8 @@ lsa_status prefill_setup(PrefillArgs &p, const void *q, int32_t q_dtype, const l
     p.page_size = kv->page_size;
     p.n_qblocks = (seq_len + 63) / 64;
     p.head_groups = (p.group + 3) / 4;
+    p.q_tiles = 1;
+    p.n_qgroups = p.n_qblocks;
     p.n_ret = 0;
     p.n_str = 0;
     const long long items = (long long)kv->num_kv_heads * p.n_qblocks * p.head_groups;
@@ -396,6 +398,12 @@ lsa_status lsa_sparse_prefill_attn(const void *q, int32_t q_dtype, const lsa_kv 
     for (int i = 0; i < kv->num_kv_heads; ++i) {
         if (heads->head_kind[i] == LSA_RETRIEVAL_HEAD) p.ret_heads[p.n_ret++] = (uint8_t)i;
         else p.str_heads[p.n_str++] = (uint8_t)i;
+    }
+    // bf16 with one or two query heads per KV head: a work item takes 4 / G query tiles
+    if (q_dtype == LSA_BF16 && (p.group == 1 || p.group == 2)) {
+        p.q_tiles = 4 / p.group;
+        p.n_qgroups = (p.n_qblocks + p.q_tiles - 1) / p.q_tiles;
+        p.n_items = kv->num_kv_heads * p.n_qgroups * p.head_groups;
     }
     return from_hip(launch_prefill(p, q_dtype, (hipStream_t)stream), "prefill launch");
 }

@@ -270,8 +270,10 @@ struct PrefillArgs {
     int32_t seq_len, num_q_heads, num_kv_heads, group, head_dim, page_size;
     int32_t sink_blocks, local_blocks;
     int32_t n_qblocks;
-    int32_t n_items;              // work items (kv head, query tile, head group)
+    int32_t n_items;              // work items (kv head, query tile group, head group)
     int32_t head_groups;          // query-head groups of 4 per KV head
+    int32_t q_tiles;              // query tiles per work item (4 / G when G < 4, else 1)
+    int32_t n_qgroups;            // ceil(n_qblocks / q_tiles)
     float scale_log2;
     int32_t n_ret, n_str;         // retrieval / streaming KV heads
     uint8_t ret_heads[kMaxKvHeads];

@@ -10,8 +10,11 @@
 // tile a (retrieval: c = 0..a; streaming: c < sink_blocks or
 // a - c < local_blocks); no dense mask is ever tested.  Each K/V tile is
 // staged once in LDS and used by the four query heads of the group (one
-// wavefront each), so GQA heads share every K/V read.  The causal mask is
-// applied only on the diagonal tile.
+// wavefront pair each), so GQA heads share every K/V read.  The causal mask is
+// applied only on the diagonal tile.  With fewer than four query heads per KV
+// head (G = 1 or 2) a workgroup takes 4 / G consecutive query tiles of its KV
+// head instead, walks the union of their key tiles, and each wavefront pair
+// computes only the tiles its own query tile sees, so no wavefront idles.
 //
 // Work order.  Workgroups are numbered longest row first (retrieval rows by
 // descending a, then the short streaming rows), and consecutive numbers go to
@@ -22,8 +25,6 @@
 // bf16 path: v_mfma_f32_32x32x16_bf16 for S^T = K Q^T (keys in M, queries in
 // N) and O^T = V^T P^T.  Keys are placed on MFMA rows so that the S^T
 // registers of a lane are directly the B operand of the PV product.
-#include <type_traits>
-
 #include "lsa_internal.h"
 
 namespace lsa {
@@ -46,10 +47,10 @@ struct PItem {
 // others.  Head-kind patterns order rows by a and kind.  A static block mask
 // comes with its own order (rows sorted by length, computed once per mask);
 // without one, the head of consecutive workgroups rotates every round.
-template <bool CSR>
+template <bool CSR, int QT>
 __device__ __forceinline__ PItem prefill_item(const PrefillArgs &p) {
     PItem it;
-    const int nq = p.n_qblocks, HG = p.head_groups;
+    const int nq = p.n_qblocks, HG = p.head_groups, NG = p.n_qgroups;
     int i = blockIdx.x;
     if (CSR && p.order) {
         const int code = min(max(p.order[i], 0), p.n_items - 1);
@@ -59,19 +60,20 @@ __device__ __forceinline__ PItem prefill_item(const PrefillArgs &p) {
         it.streaming = false;
         return it;
     }
-    const int n_ret_items = p.n_ret * nq * HG;
+    // it.a is the highest query tile of the item (its QT tiles are it.a - QT + 1 .. it.a)
+    const int n_ret_items = p.n_ret * NG * HG;
     if (i < n_ret_items) {
         const int j = i / p.n_ret;
         it.kv = p.ret_heads[CSR ? (i + j) % p.n_ret : i % p.n_ret];
         it.hg = j % HG;
-        it.a = nq - 1 - j / HG;
+        it.a = nq - 1 - (j / HG) * QT;
         it.streaming = false;
     } else {
         i -= n_ret_items;
         it.kv = p.str_heads[i % p.n_str];
         const int j = i / p.n_str;
         it.hg = j % HG;
-        it.a = nq - 1 - j / HG;
+        it.a = nq - 1 - (j / HG) * QT;
         it.streaming = true;
     }
     return it;
@@ -85,7 +87,7 @@ struct TileRow {
     int e0, s1, rp0, n;
 };
 
-template <bool CSR>
+template <bool CSR, int QT>
 __device__ __forceinline__ TileRow tile_row(const PrefillArgs &p, const PItem &it) {
     TileRow r{0, 0, 0, 0};
     if constexpr (CSR) {
@@ -95,9 +97,9 @@ __device__ __forceinline__ TileRow tile_row(const PrefillArgs &p, const PItem &i
         r.rp0 = b0;
         r.n = b1 - b0;
     } else {
-        if (it.streaming) {
+        if (it.streaming) {                       // the union over the item's query tiles
             r.e0 = min(p.sink_blocks, it.a + 1);
-            r.s1 = max(it.a - p.local_blocks + 1, r.e0);
+            r.s1 = max(max(it.a - QT + 1, 0) - p.local_blocks + 1, r.e0);
         }
         r.n = r.e0 + (it.a - r.s1 + 1);
     }
@@ -122,7 +124,7 @@ __device__ __forceinline__ int row_tile(const PrefillArgs &p, const PItem &it, c
 // the compute runs, one barrier per tile.  The last tile is the diagonal one:
 // its causal mask is applied in the pipeline's epilogue only.
 // ---------------------------------------------------------------------------
-template <int D, bool CSR>
+template <int D, bool CSR, int QT>
 __global__ __launch_bounds__(512, 2) void prefill_bf16_kernel(PrefillArgs p) {
     typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
     typedef float floatx2 __attribute__((ext_vector_type(2)));
@@ -136,15 +138,23 @@ __global__ __launch_bounds__(512, 2) void prefill_bf16_kernel(PrefillArgs p) {
     __shared__ __attribute__((aligned(16))) uint16_t k_lds[2][kTile * D];
     __shared__ __attribute__((aligned(16))) uint16_t v_lds[2][kTile * D];
 
-    const PItem it = prefill_item<CSR>(p);
-    const TileRow trow = tile_row<CSR>(p, it);
+    const PItem it = prefill_item<CSR, QT>(p);
+    const TileRow trow = tile_row<CSR, QT>(p, it);
 
     const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
     const int T = p.seq_len, G = p.group, HQ = p.num_q_heads, NP = p.page_size;
-    const int hq_local = it.hg * 4 + (wave >> 1);
-    const bool head_ok = hq_local < G;
+    // wavefront pair `slot`: query head and query tile; with QT > 1 the group is G = 4 / QT
+    const int slot = wave >> 1;
+    constexpr int GQ = QT > 1 ? 4 / QT : 1;
+    const int hq_local = QT == 1 ? it.hg * 4 + slot : slot % GQ;
+    const int a_s = QT == 1 ? it.a : it.a - slot / GQ;        // this pair's query tile
+    const bool head_ok = QT == 1 ? hq_local < G : a_s >= 0;
     const int hq = it.kv * G + min(hq_local, G - 1);
-    const int q0 = it.a * kTile + 32 * (wave & 1);  // first query row of this wave
+    const int q0 = max(a_s, 0) * kTile + 32 * (wave & 1);   // first query row of this wave
+    // does this pair's query tile see key tile c (QT > 1: the item walks a union)
+    auto sees = [&](int c) {
+        return c <= a_s && (!it.streaming || c < p.sink_blocks || a_s - c < p.local_blocks);
+    };
     const int col = lane & 31, lg = lane >> 5;      // MFMA column / lane group
     const int n_iter = trow.n;
     if (n_iter == 0) {                              // a query tile without key tiles: zero output
@@ -255,10 +265,9 @@ __global__ __launch_bounds__(512, 2) void prefill_bf16_kernel(PrefillArgs p) {
                 s[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k_at(kb, kt, st), qb[st], s[kt], 0, 0, 0);
         }
     };
-    // online softmax of the scores s (DIAG: causal mask against key0), then O^T += V^T P^T
-    auto softmax_pv = [&](floatx16 (&s)[2], int vb, int key0, auto diag_tag) {
-        constexpr bool DIAG = decltype(diag_tag)::value;
-        if constexpr (DIAG) {
+    // online softmax of the scores s (diag: causal mask against key0), then O^T += V^T P^T
+    auto softmax_pv = [&](floatx16 (&s)[2], int vb, int key0, bool diag) {
+        if (diag) {
             const int qrow = q0 + col;
 #pragma unroll
             for (int kt = 0; kt < 2; ++kt)
@@ -316,8 +325,16 @@ __global__ __launch_bounds__(512, 2) void prefill_bf16_kernel(PrefillArgs p) {
         if (ii + 1 < n_iter) fetch(kpool, k_lds[(ii + 1) & 1], ii + 1);
         fetch(vpool, v_lds[ii & 1], ii);
         if (head_ok) {
-            qk(ii & 1, s_cur);
-            if (ii > 0) softmax_pv(s_prev, (ii - 1) & 1, tile_of(ii - 1) * kTile, std::false_type{});
+            if constexpr (QT == 1) {
+                qk(ii & 1, s_cur);
+                if (ii > 0) softmax_pv(s_prev, (ii - 1) & 1, tile_of(ii - 1) * kTile, false);
+            } else {
+                if (sees(tile_of(ii))) qk(ii & 1, s_cur);
+                if (ii > 0) {
+                    const int c = tile_of(ii - 1);
+                    if (sees(c)) softmax_pv(s_prev, (ii - 1) & 1, c * kTile, c == a_s);
+                }
+            }
         }
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
         if (ii == n_iter - 1) {                       // the last tile may reach past T
@@ -340,15 +357,26 @@ __global__ __launch_bounds__(512, 2) void prefill_bf16_kernel(PrefillArgs p) {
         step(ii + 1, sb, sa);
     }
     if (ii < n_iter) step(ii, sa, sb);
-    // epilogue: the last tile (the diagonal one)
-    if (head_ok) {
-        if ((n_iter - 1) & 1) softmax_pv(sb, (n_iter - 1) & 1, tile_of(n_iter - 1) * kTile, std::true_type{});
-        else softmax_pv(sa, (n_iter - 1) & 1, tile_of(n_iter - 1) * kTile, std::true_type{});
+    // epilogue: the last tile (the diagonal one of the highest query tile)
+    const int c_last = tile_of(n_iter - 1);
+    if (head_ok && (QT == 1 || sees(c_last))) {
+        const bool diag = QT == 1 || c_last == a_s;
+        if ((n_iter - 1) & 1) softmax_pv(sb, (n_iter - 1) & 1, c_last * kTile, diag);
+        else softmax_pv(sa, (n_iter - 1) & 1, c_last * kTile, diag);
     }
 
-    if (p.tile_counter && tid == 0) {
-        const int heads_here = min(4, G - it.hg * 4);
-        atomicAdd(p.tile_counter, (unsigned long long)n_iter * heads_here);
+    if (p.tile_counter) {
+        if constexpr (QT == 1) {
+            if (tid == 0) {
+                const int heads_here = min(4, G - it.hg * 4);
+                atomicAdd(p.tile_counter, (unsigned long long)n_iter * heads_here);
+            }
+        } else if (head_ok && (wave & 1) == 0 && lane == 0) {
+            // the tiles this pair's query tile sees
+            const int e0s = it.streaming ? min(p.sink_blocks, a_s + 1) : 0;
+            const int s1s = it.streaming ? max(a_s - p.local_blocks + 1, e0s) : 0;
+            atomicAdd(p.tile_counter, (unsigned long long)(e0s + (a_s - s1s + 1)));
+        }
     }
     if (!head_ok) return;
     // ---- normalise and store: lane holds query q0 + col, channels 32*dt + 8*(r/4) + 4*lg + r%4
@@ -380,8 +408,8 @@ __global__ __launch_bounds__(256) void prefill_f32_kernel(PrefillArgs p) {
     float *k_lds = sm;                 // [64][D]
     float *v_lds = sm + kTile * D;     // [D][64]
 
-    const PItem it = prefill_item<CSR>(p);
-    const TileRow trow = tile_row<CSR>(p, it);
+    const PItem it = prefill_item<CSR, 1>(p);
+    const TileRow trow = tile_row<CSR, 1>(p, it);
 
     const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
     const int T = p.seq_len, G = p.group, HQ = p.num_q_heads, NP = p.page_size;
@@ -455,12 +483,19 @@ __global__ __launch_bounds__(256) void prefill_f32_kernel(PrefillArgs p) {
 
 }  // namespace
 
+template <int D, bool CSR>
+void launch_bf16(const PrefillArgs &p, dim3 grid, hipStream_t s) {
+    if (CSR || p.q_tiles == 1) hipLaunchKernelGGL((prefill_bf16_kernel<D, CSR, 1>), grid, dim3(512), 0, s, p);
+    else if (p.q_tiles == 2) hipLaunchKernelGGL((prefill_bf16_kernel<D, false, 2>), grid, dim3(512), 0, s, p);
+    else hipLaunchKernelGGL((prefill_bf16_kernel<D, false, 4>), grid, dim3(512), 0, s, p);
+}
+
 template <bool CSR>
 void launch_prefill_kernels(const PrefillArgs &p, int dtype, hipStream_t s) {
     const dim3 grid((unsigned)p.n_items);
     if (dtype == LSA_BF16) {
-        if (p.head_dim == 128) hipLaunchKernelGGL((prefill_bf16_kernel<128, CSR>), grid, dim3(512), 0, s, p);
-        else hipLaunchKernelGGL((prefill_bf16_kernel<64, CSR>), grid, dim3(512), 0, s, p);
+        if (p.head_dim == 128) launch_bf16<128, CSR>(p, grid, s);
+        else launch_bf16<64, CSR>(p, grid, s);
     } else {
         // f32 is the small-model path: head_dim 64 only (validated by the caller)
         const size_t lds = 2 * (size_t)kTile * 64 * sizeof(float);

@@ -109,13 +109,22 @@ def test_prefill_full_size_cfg3_sampled():
     print("max abs err", check(p, out, rows=rows, heads=[ret * 4 + 1, st * 4 + 2]))
 
 
-@pytest.mark.parametrize("T", [777, 1088])
+@pytest.mark.parametrize("T", [777, 1088, 64, 200])
 def test_prefill_cfg7_mha_small(T):
     """Multi-head attention (32 KV heads, group size 1)."""
     p = W.make_prefill(7, DEV, seq_len=T)
     out, cnt = run_prefill(p)
     assert cnt == expected_tiles(p)
     print("max abs err", check(p, out, heads=[0, 1, 7, 18, 31]))
+
+
+@pytest.mark.parametrize("T", [777, 1088, 64, 130])
+def test_prefill_group2_small(T):
+    """Two query heads per KV head (32 / 16 heads): a workgroup takes two query tiles."""
+    p = W.make_prefill(3, DEV, seq_len=T, num_kv_heads=16)
+    out, cnt = run_prefill(p)
+    assert cnt == expected_tiles(p)
+    print("max abs err", check(p, out, heads=[0, 1, 6, 17, 30, 31]))
 
 
 def test_prefill_full_size_cfg7_mha_sampled():
