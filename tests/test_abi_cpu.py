@@ -131,6 +131,7 @@ def test_select_validation(lib):
     bad_agg.score_aggregation = 2
     assert select(lib, heads=bad_agg) == lsa.LSA_ERR_INVALID_ARG
     assert select(lib, seqs=seqs_desc(max_pages=0)) == lsa.LSA_ERR_UNSUPPORTED
+    assert select(lib, seqs=seqs_desc(max_pages=16385)) == lsa.LSA_ERR_UNSUPPORTED   # above the top-K limit
     assert select(lib, seqs=lsa.LsaSeqs(2, 10, None, FAKE)) == lsa.LSA_ERR_INVALID_ARG
 
 

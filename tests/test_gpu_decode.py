@@ -256,6 +256,30 @@ def test_decode_page_geometry(NP, NL):
     S.check_stats(w, r.stats, [c + w.window for c in w.ctx], kinds=w.head_kind)
 
 
+@pytest.mark.parametrize("cfg", [2, 5])
+def test_decode_large_budget_multi_batch_merge(cfg):
+    """A 16384-token budget (256 selected pages: 33 chunks per retrieval
+    head), so the last workgroup of a head merges the chunk records in four
+    batches."""
+    w = W.make_decode(cfg, DEV, batch=2, ctx=[30000, 41000])
+    w.token_budget = 16384
+    ret = [kv for kv in range(w.num_kv_heads) if w.head_kind[kv] == 0][:2]
+    print("max abs err", check_window(w, kv_heads=ret))
+
+
+def test_select_and_decode_at_page_limit():
+    """One sequence of 16384 pages (1,048,572 cached tokens plus the window at
+    N_P = 64), the most pages the selection takes: the window matches the
+    oracle for one retrieval and one streaming KV head."""
+    w = W.make_decode(2, DEV, batch=1, ctx=[16384 * 64 - 4])
+    assert w.max_pages == 16384
+    ret = [kv for kv in range(w.num_kv_heads) if w.head_kind[kv] == 0][:1]
+    st = [kv for kv in range(w.num_kv_heads) if w.head_kind[kv] == 1][:1]
+    print("max abs err", check_window(w, kv_heads=ret + st))
+    del w
+    torch.cuda.empty_cache()
+
+
 @pytest.mark.parametrize("ctx", [[6000, 9000], [63, 4096 + 17]])
 def test_decode_cfg6_mha_small(ctx):
     """Multi-head attention (32 KV heads, group size 1)."""
