@@ -19,10 +19,9 @@ constexpr int kMaxDecodeChunks = 128;   // split-KV chunks per (sequence, KV hea
 // takes one chunk of the attended page list.
 constexpr int kDecodeWaves = 4;
 constexpr int kMaxChunkPages = 16;
-__host__ __device__ constexpr int decode_wave_tokens(int) { return 128; }
+constexpr int kDecodeWaveTokens = 128;
 __host__ __device__ constexpr int decode_pages_per_wave(int kv_dtype, int page_size) {
-    return kv_dtype == LSA_F32 || page_size >= decode_wave_tokens(kv_dtype) ? 1
-                                                                             : decode_wave_tokens(kv_dtype) / page_size;
+    return kv_dtype == LSA_F32 || page_size >= kDecodeWaveTokens ? 1 : kDecodeWaveTokens / page_size;
 }
 __host__ __device__ constexpr int decode_chunk_pages(int kv_dtype, int page_size) {
     return kv_dtype == LSA_F32 ? 4 : kDecodeWaves * decode_pages_per_wave(kv_dtype, page_size);
