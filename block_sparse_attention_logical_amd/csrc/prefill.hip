@@ -212,9 +212,16 @@ __global__ __launch_bounds__(512, 2) void prefill_bf16_kernel(PrefillArgs p) {
     };
     // A 64-key tile is two whole 32-token blocks of its page: its keys (and its
     // values) are one contiguous run of 64 * D elements laid out like the LDS tile.
+    // The page table is read through the constant address space: a scalar
+    // load, counted apart from the vector loads, so the lookup does not wait
+    // for the tile fetches in flight (a vector load here made every step wait
+    // for the K tile it had just requested).  Nothing writes the table while
+    // the kernel runs.
+    const int32_t __attribute__((address_space(4))) *ptab =
+        (const int32_t __attribute__((address_space(4))) *)p.page_table;
     auto tile_base = [&](int c) {
         const int key0 = c * kTile;
-        const size_t hp = (size_t)p.page_table[key0 / NP] * p.num_kv_heads + it.kv;
+        const size_t hp = (size_t)ptab[key0 / NP] * p.num_kv_heads + it.kv;
         return hp * NP * D + key_offset(key0 % NP, 0, D);       // == value_offset(key0 % NP, 0, D)
     };
     auto swz = [](int r) { return (r >> 2) & 3; };
