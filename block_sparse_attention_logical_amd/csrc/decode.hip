@@ -504,7 +504,8 @@ __global__ __launch_bounds__(kDecodeWaves * kWave, 2) void decode_mfma_kernel(De
             float mb = -__builtin_inff();
 #pragma unroll
             for (int jj = 0; jj < 8; ++jj) {
-                if (!blk || !token_visible(a, w, tok0 + 4 * g4 + (jj & 3) + 16 * (jj >> 2))) x[jj] = -__builtin_inff();
+                const bool vis = blk & token_visible(a, w, tok0 + 4 * g4 + (jj & 3) + 16 * (jj >> 2));
+                x[jj] = vis ? x[jj] : -__builtin_inff();        // a select, not a branch
                 mb = fmaxf(mb, x[jj]);
             }
             mb = max_xor32(max_xor16(mb));
