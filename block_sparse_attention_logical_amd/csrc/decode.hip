@@ -552,6 +552,12 @@ __global__ __launch_bounds__(kDecodeWaves * kWave, 2) void decode_mfma_kernel(De
             // zero probability never meets a NaN in the PV product
             const bool tail = !blk || tok0 + 31 > w.t;
             const int nvalid = blk ? w.t - (tok0 + 8 * g4) + 1 : 0;
+            uint32_t keep[4] = {~0u, ~0u, ~0u, ~0u};
+            if (tail) {
+#pragma unroll
+                for (int q2 = 0; q2 < 4; ++q2)
+                    keep[q2] = (2 * q2 < nvalid ? 0x0000FFFFu : 0u) | (2 * q2 + 1 < nvalid ? 0xFFFF0000u : 0u);
+            }
 #pragma unroll
             for (int dt = 0; dt < NDT; ++dt) {
                 uint4 va;
@@ -564,10 +570,6 @@ __global__ __launch_bounds__(kDecodeWaves * kWave, 2) void decode_mfma_kernel(De
                     va = vr[e][dt];
                 }
                 if (tail) {
-                    uint32_t keep[4];
-#pragma unroll
-                    for (int q2 = 0; q2 < 4; ++q2)
-                        keep[q2] = (2 * q2 < nvalid ? 0x0000FFFFu : 0u) | (2 * q2 + 1 < nvalid ? 0xFFFF0000u : 0u);
                     va.x &= keep[0]; va.y &= keep[1]; va.z &= keep[2]; va.w &= keep[3];
                 }
                 o[dt] *= alpha;
