@@ -145,7 +145,7 @@ def bench_decode(args, torch, lsa, W):
         sel = torch.full((B, Hkv, K), -1, dtype=torch.int32, device=dev)
         layers.append((kv, stats, sel))
     lens = [w.seq_lens(s) for s in range(R)]
-    ws_sel = torch.empty(lsa.select_pages_workspace(layers[0][0], w.page_table, lens[0], hd), dtype=torch.uint8,
+    ws_sel = torch.zeros(lsa.select_pages_workspace(layers[0][0], w.page_table, lens[0], hd), dtype=torch.uint8,
                          device=dev)
     ws_dec = torch.zeros(lsa.decode_workspace(layers[0][0], w.page_table, lens[0], hd, w.token_budget),
                          dtype=torch.uint8, device=dev)

@@ -236,7 +236,9 @@ lsa_status lsa_select_pages_workspace(const lsa_kv *kv, const lsa_seqs *seqs, co
     if (lsa_status s = check_seqs(seqs)) return s;
     if (lsa_status s = check_heads(heads, kv, true)) return s;
     if (!bytes) return fail(LSA_ERR_INVALID_ARG, "bytes is NULL");
-    *bytes = align_up((size_t)seqs->batch * kv->num_kv_heads * seqs->max_pages * sizeof(double));
+    // arrival counters of the fused top-K, then the physical page scores
+    *bytes = decode_counter_bytes(seqs->batch, kv->num_kv_heads) +
+             align_up((size_t)seqs->batch * kv->num_kv_heads * seqs->max_pages * sizeof(double));
     return ok();
 }
 
@@ -273,7 +275,12 @@ lsa_status lsa_select_pages(const void *q, int32_t q_dtype, const lsa_kv *kv, co
     sa.k_sz = kv->k_sz;
     sa.page_table = seqs->page_table;
     sa.seq_lens = seqs->seq_lens;
-    sa.phys = static_cast<double *>(workspace);
+    sa.counters = static_cast<int32_t *>(workspace);
+    sa.phys = reinterpret_cast<double *>(static_cast<char *>(workspace) +
+                                         decode_counter_bytes(seqs->batch, kv->num_kv_heads));
+    sa.selected = selected;
+    sa.k_pages = token_budget / kv->page_size;
+    sa.fused_pt = score_fused_pt(seqs->max_pages);
     sa.batch = seqs->batch;
     sa.max_pages = seqs->max_pages;
     sa.num_q_heads = heads->num_q_heads;
@@ -290,6 +297,7 @@ lsa_status lsa_select_pages(const void *q, int32_t q_dtype, const lsa_kv *kv, co
     sa.pages_per_block = score_pages_per_block(kv->kv_dtype, kv->head_dim, kv->page_size, kv->logical_page);
     sa.blocks_per_head = (seqs->max_pages + sa.pages_per_block - 1) / sa.pages_per_block;
     if (lsa_status s = from_hip(launch_score(sa, (hipStream_t)stream), "select_pages score launch")) return s;
+    if (sa.fused_pt > 0) return ok();              // the score kernel's last workgroups have selected
 
     TopkArgs ta{};
     ta.phys = sa.phys;

@@ -225,6 +225,13 @@ struct ScoreArgs {
     int32_t pages_per_block;      // physical pages per workgroup
     int32_t blocks_per_head;      // workgroups per (sequence, retrieval head)
     uint8_t ret_heads[kMaxKvHeads];
+    // fused top-K: the last score workgroup of a (sequence, head) selects its
+    // pages; arrival counters [B][H_kv] head the workspace.  fused_pt is the
+    // top-K's pages per thread (4, 8 or 16), 0 for a separate top-K launch.
+    int32_t *counters;
+    int32_t *selected;            // [B][H_kv][K]
+    int32_t k_pages;              // K
+    int32_t fused_pt;
 };
 
 struct TopkArgs {
@@ -294,6 +301,7 @@ hipError_t launch_stats(const StatsArgs &a, hipStream_t s);
 hipError_t launch_score(const ScoreArgs &a, hipStream_t s);
 int score_pages_per_block(int kv_dtype, int head_dim, int page_size, int logical_page);
 int topk_max_pages();
+int score_fused_pt(int max_pages);   // top-K pages per thread inside the score kernel, 0: a separate launch
 hipError_t launch_topk(const TopkArgs &a, hipStream_t s);
 hipError_t launch_decode(const DecodeArgs &a, int q_dtype, int kv_dtype, hipStream_t s);
 hipError_t launch_prefill(const PrefillArgs &a, int dtype, hipStream_t s);

@@ -155,10 +155,172 @@ __device__ __forceinline__ void current_page_minmax(const ScoreArgs &a, size_t p
     }
 }
 
+// ---------------------------------------------------------------------------
+// top-K of one (sequence, retrieval head): by a 1024-thread workgroup of its
+// own, or by the last score workgroup of the head (256 threads)
+// ---------------------------------------------------------------------------
+constexpr int kTopkThreads = 1024;
+constexpr int kTopkPerThread = 16;        // pages per thread at most: up to 16384 pages
+
+__device__ __forceinline__ unsigned long long order_key(double x) {
+    x = x + 0.0;                                  // -0 -> +0
+    const unsigned long long u = __double_as_longlong(x);
+    return (u >> 63) ? ~u : (u | 0x8000000000000000ull);
+}
+
+__device__ __forceinline__ void store_agent_d(double *p, double v) {
+    __hip_atomic_store(reinterpret_cast<unsigned long long *>(p), (unsigned long long)__double_as_longlong(v),
+                       __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ double load_agent_d(const double *p) {
+    return __longlong_as_double((long long)__hip_atomic_load(reinterpret_cast<const unsigned long long *>(p),
+                                                             __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+}
+
+// exclusive prefix sum over the NT threads of a 32-bit packed counter
+template <int NT>
+__device__ __forceinline__ uint32_t block_exclusive_scan(uint32_t v, uint32_t *wave_tot) {
+    const int lane = threadIdx.x % kWave, wave = threadIdx.x / kWave;
+    const uint32_t incl = wave_inclusive_scan(v);
+    if (lane == kWave - 1) wave_tot[wave] = incl;
+    __syncthreads();
+    uint32_t add = 0;
+    for (int w = 0; w < wave; ++w) add += wave_tot[w];
+    return incl - v + add;
+}
+
+// The K largest of the n = ceil(L / N_P) scores P[0..n) into out, ascending by
+// page, ties to the lower page, -1 padded; NT threads, PT pages per thread
+// (NT * PT >= max_pages).  AGENT: P was written by other workgroups of this
+// launch and is read with agent-scope loads.
+template <int NT, int PT, bool AGENT>
+__device__ __forceinline__ void topk_rows(const double *P, int L, int page_size, int max_pages, int K,
+                                          int32_t *out) {
+    __shared__ uint32_t hist[2][256];
+    __shared__ uint32_t sh_digit, sh_above, sh_done;
+    __shared__ uint32_t wave_tot[NT / kWave];
+    __shared__ unsigned long long sh_and[NT / kWave], sh_or[NT / kWave];
+    const int tid = threadIdx.x;
+
+    // thread t owns the contiguous pages [t*seg, t*seg + cnt); the scores are
+    // loaded for every row slot at once, and the entries past the sequence's
+    // last page are dropped afterwards
+    constexpr int seg = PT;
+    const int i0 = min(max_pages, tid * seg);
+    double pv[PT];
+#pragma unroll
+    for (int e = 0; e < PT; ++e) {
+        if constexpr (AGENT) pv[e] = i0 + e < max_pages ? load_agent_d(P + i0 + e) : 0.0;
+        else pv[e] = i0 + e < max_pages ? P[i0 + e] : 0.0;
+    }
+    const int n = (L + page_size - 1) / page_size;
+    if (n <= K) {                                 // every page, ascending, padded with -1
+        for (int i = tid; i < K; i += NT) out[i] = i < n ? i : -1;
+        return;
+    }
+    const int cnt = max(0, min(n, i0 + seg) - i0);
+    unsigned long long key[PT];
+#pragma unroll
+    for (int e = 0; e < PT; ++e) key[e] = e < cnt ? order_key(pv[e]) : 0ull;
+
+    // The bits above the highest one that differs between keys are shared by
+    // every key and decide nothing: the radix passes start there, each pass
+    // resolving the next (up to) 8 bits of the K-th largest key.
+    unsigned long long k_and = ~0ull, k_or = 0ull;
+#pragma unroll
+    for (int e = 0; e < PT; ++e)
+        if (e < cnt) { k_and &= key[e]; k_or |= key[e]; }
+    wave_and_or(k_and, k_or);
+    if (tid % kWave == 0) { sh_and[tid / kWave] = k_and; sh_or[tid / kWave] = k_or; }
+    for (int i = tid; i < 256; i += NT) hist[0][i] = 0;
+    __syncthreads();
+    k_and = ~0ull; k_or = 0ull;
+    for (int w2 = 0; w2 < NT / kWave; ++w2) { k_and &= sh_and[w2]; k_or |= sh_or[w2]; }
+    const unsigned long long differ = k_and ^ k_or;      // bits that are not the same in every key
+    int hi = differ ? 64 - __clzll((long long)differ) : 0;   // one past the highest differing bit
+    unsigned long long mask = hi >= 64 ? 0ull : (~0ull << hi);
+    unsigned long long prefix = k_and & mask;
+    uint32_t need = (uint32_t)K;
+    int buf = 0;
+    while (hi > 0) {
+        const int lo = max(0, hi - 8);
+        const uint32_t dmask = (1u << (hi - lo)) - 1u;
+#pragma unroll
+        for (int e = 0; e < PT; ++e)
+            if (e < cnt && (key[e] & mask) == prefix) atomicAdd(&hist[buf][uint32_t(key[e] >> lo) & dmask], 1u);
+        for (int i = tid; i < 256; i += NT) hist[buf ^ 1][i] = 0;    // the next pass's histogram
+        __syncthreads();
+        if (tid < kWave) {
+            // lane l owns bins 4l..4l+3; count the elements in higher bins
+            const uint32_t *hb = hist[buf];
+            const uint32_t c0 = hb[4 * tid], c1 = hb[4 * tid + 1], c2 = hb[4 * tid + 2], c3 = hb[4 * tid + 3];
+            const uint32_t mine = c0 + c1 + c2 + c3;
+            const uint32_t incl = wave_inclusive_scan(mine);
+            const uint32_t total = (uint32_t)__builtin_amdgcn_readlane((int)incl, kWave - 1);
+            uint32_t above = total - incl;        // elements in bins of higher lanes
+            const uint32_t cs[4] = {c0, c1, c2, c3};
+            for (int qd = 3; qd >= 0; --qd) {
+                if (above < need && above + cs[qd] >= need) {
+                    sh_digit = 4 * tid + qd;
+                    sh_above = above;
+                    sh_done = above + cs[qd] == need;   // the whole bin is taken
+                }
+                above += cs[qd];
+            }
+        }
+        __syncthreads();
+        need -= sh_above;
+        prefix |= (unsigned long long)sh_digit << lo;
+        mask |= (unsigned long long)dmask << lo;
+        hi = lo;
+        if (sh_done) break;
+        buf ^= 1;
+    }
+
+    // ordered compaction
+    uint32_t c = 0;                               // low 16 bits: greater, high 16 bits: equal
+#pragma unroll
+    for (int e = 0; e < PT; ++e) {
+        if (e >= cnt) continue;
+        const unsigned long long km = key[e] & mask;
+        c += km > prefix ? 1u : (km == prefix ? 0x10000u : 0u);
+    }
+    const uint32_t excl = block_exclusive_scan<NT>(c, wave_tot);
+    uint32_t gt_before = excl & 0xFFFFu;
+    uint32_t eq_before = excl >> 16;
+#pragma unroll
+    for (int e = 0; e < PT; ++e) {
+        if (e >= cnt) continue;
+        const unsigned long long km = key[e] & mask;
+        if (km > prefix) {
+            out[gt_before + min(eq_before, need)] = i0 + e;
+            ++gt_before;
+        } else if (km == prefix) {
+            if (eq_before < need) out[gt_before + eq_before] = i0 + e;
+            ++eq_before;
+        }
+    }
+}
+
+// PT: pages per thread, the smallest power of two with kTopkThreads * PT >=
+// max_pages (every per-page loop is unrolled over PT slots).
+template <int PT>
+__global__ __launch_bounds__(kTopkThreads) void topk_kernel(TopkArgs a) {
+    const int r = blockIdx.x % a.n_ret;
+    const int b = blockIdx.x / a.n_ret;
+    const int kv = a.ret_heads[r];
+    topk_rows<kTopkThreads, PT, false>(a.phys + ((size_t)b * a.num_kv_heads + kv) * a.max_pages, a.seq_lens[b],
+                                       a.page_size, a.max_pages, a.k,
+                                       a.selected + ((size_t)b * a.num_kv_heads + kv) * a.k);
+}
+
 // KV_DT: LSA_F32, LSA_BF16 (stats in that type) or LSA_INT4 (code stats).
 // AGG_MAX: the group's heads are scored one by one and their scores combined
 // by max; otherwise their sum is formed with one folded (Qp, Qn) pass.
-template <int KV_DT, int D, bool AGG_MAX>
+// FPT > 0: the physical scores go out with agent-scope stores and the last
+// workgroup of a (sequence, head) to finish runs the head's top-K with FPT
+// pages per thread (the hand-off of the decode kernel's split-KV merge).
+template <int KV_DT, int D, bool AGG_MAX, int FPT>
 __global__ __launch_bounds__(kScoreThreads) void score_kernel(ScoreArgs a) {
     constexpr int EB = KV_DT == LSA_F32 ? 4 : (KV_DT == LSA_BF16 ? 2 : 1);
     using S = ScoreShape<EB, D>;
@@ -191,7 +353,7 @@ __global__ __launch_bounds__(kScoreThreads) void score_kernel(ScoreArgs a) {
     const int L = a.seq_lens[b];
     const int G = a.num_q_heads / a.num_kv_heads;
     const int n_pages = (L + a.page_size - 1) / a.page_size;
-    if (m0 >= n_pages) return;
+    if (m0 < n_pages) {                           // (uniform: a workgroup past the last page only arrives)
     const int m1 = min(m0 + a.pages_per_block, n_pages);
     const int nlog = (L + a.logical_page - 1) / a.logical_page;
     const int j1 = min(m1 * g, nlog);
@@ -313,152 +475,46 @@ __global__ __launch_bounds__(kScoreThreads) void score_kernel(ScoreArgs a) {
         const int ja = m * g - j0, jb = min((m + 1) * g, j1) - j0;
         double best = s_log[ja];
         for (int jj = ja + 1; jj < jb; ++jj) best = fmax(best, s_log[jj]);
-        a.phys[((size_t)b * a.num_kv_heads + kv) * a.max_pages + m] = best + 0.0;
+        double *dst = a.phys + ((size_t)b * a.num_kv_heads + kv) * a.max_pages + m;
+        if constexpr (FPT > 0) store_agent_d(dst, best + 0.0);
+        else *dst = best + 0.0;
     }
-}
-
-// ---------------------------------------------------------------------------
-// top-K: one workgroup of 1024 threads per (sequence, retrieval head)
-// ---------------------------------------------------------------------------
-constexpr int kTopkThreads = 1024;
-constexpr int kTopkPerThread = 16;        // pages per thread at most: up to 16384 pages
-
-__device__ __forceinline__ unsigned long long order_key(double x) {
-    x = x + 0.0;                                  // -0 -> +0
-    const unsigned long long u = __double_as_longlong(x);
-    return (u >> 63) ? ~u : (u | 0x8000000000000000ull);
-}
-
-// exclusive prefix sum over the workgroup of a 32-bit packed counter
-__device__ __forceinline__ uint32_t block_exclusive_scan(uint32_t v, uint32_t *wave_tot) {
-    const int lane = threadIdx.x % kWave, wave = threadIdx.x / kWave;
-    const uint32_t incl = wave_inclusive_scan(v);
-    if (lane == kWave - 1) wave_tot[wave] = incl;
-    __syncthreads();
-    uint32_t add = 0;
-    for (int w = 0; w < wave; ++w) add += wave_tot[w];
-    return incl - v + add;
-}
-
-// PT: pages per thread, the smallest power of two with kTopkThreads * PT >=
-// max_pages (every per-page loop below is unrolled over PT slots).
-template <int PT>
-__global__ __launch_bounds__(kTopkThreads) void topk_kernel(TopkArgs a) {
-    __shared__ uint32_t hist[2][256];
-    __shared__ uint32_t sh_digit, sh_above, sh_done;
-    __shared__ uint32_t wave_tot[kTopkThreads / kWave];
-    __shared__ unsigned long long sh_and[kTopkThreads / kWave], sh_or[kTopkThreads / kWave];
-
-    const int r = blockIdx.x % a.n_ret;
-    const int b = blockIdx.x / a.n_ret;
-    const int kv = a.ret_heads[r];
-    const int K = a.k;
-    int32_t *out = a.selected + ((size_t)b * a.num_kv_heads + kv) * K;
-    const double *P = a.phys + ((size_t)b * a.num_kv_heads + kv) * a.max_pages;
-    const int tid = threadIdx.x;
-
-    // thread t owns the contiguous pages [t*seg, t*seg + cnt); the scores are
-    // loaded for every row slot at once, together with seq_lens, and the
-    // entries past the sequence's last page are dropped afterwards
-    constexpr int seg = PT;
-    const int i0 = min(a.max_pages, tid * seg);
-    double pv[PT];
-#pragma unroll
-    for (int e = 0; e < PT; ++e) pv[e] = i0 + e < a.max_pages ? P[i0 + e] : 0.0;
-    const int L = a.seq_lens[b];
-    const int n = (L + a.page_size - 1) / a.page_size;
-    if (n <= K) {                                 // every page, ascending, padded with -1
-        for (int i = tid; i < K; i += blockDim.x) out[i] = i < n ? i : -1;
-        return;
     }
-    const int cnt = max(0, min(n, i0 + seg) - i0);
-    unsigned long long key[PT];
-#pragma unroll
-    for (int e = 0; e < PT; ++e) key[e] = e < cnt ? order_key(pv[e]) : 0ull;
-
-    // The bits above the highest one that differs between keys are shared by
-    // every key and decide nothing: the radix passes start there, each pass
-    // resolving the next (up to) 8 bits of the K-th largest key.
-    unsigned long long k_and = ~0ull, k_or = 0ull;
-#pragma unroll
-    for (int e = 0; e < PT; ++e)
-        if (e < cnt) { k_and &= key[e]; k_or |= key[e]; }
-    wave_and_or(k_and, k_or);
-    if (tid % kWave == 0) { sh_and[tid / kWave] = k_and; sh_or[tid / kWave] = k_or; }
-    if (tid < 256) hist[0][tid] = 0;
-    __syncthreads();
-    k_and = ~0ull; k_or = 0ull;
-    for (int w2 = 0; w2 < kTopkThreads / kWave; ++w2) { k_and &= sh_and[w2]; k_or |= sh_or[w2]; }
-    const unsigned long long differ = k_and ^ k_or;      // bits that are not the same in every key
-    int hi = differ ? 64 - __clzll((long long)differ) : 0;   // one past the highest differing bit
-    unsigned long long mask = hi >= 64 ? 0ull : (~0ull << hi);
-    unsigned long long prefix = k_and & mask;
-    uint32_t need = (uint32_t)K;
-    int buf = 0;
-    while (hi > 0) {
-        const int lo = max(0, hi - 8);
-        const uint32_t dmask = (1u << (hi - lo)) - 1u;
-#pragma unroll
-        for (int e = 0; e < PT; ++e)
-            if (e < cnt && (key[e] & mask) == prefix) atomicAdd(&hist[buf][uint32_t(key[e] >> lo) & dmask], 1u);
-        if (tid < 256) hist[buf ^ 1][tid] = 0;    // the next pass's histogram
+    if constexpr (FPT > 0) {
+        __shared__ int s_last;
+        // this wavefront's score stores have reached the coherence point
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
         __syncthreads();
-        if (tid < kWave) {
-            // lane l owns bins 4l..4l+3; count the elements in higher bins
-            const uint32_t *hb = hist[buf];
-            const uint32_t c0 = hb[4 * tid], c1 = hb[4 * tid + 1], c2 = hb[4 * tid + 2], c3 = hb[4 * tid + 3];
-            const uint32_t mine = c0 + c1 + c2 + c3;
-            const uint32_t incl = wave_inclusive_scan(mine);
-            const uint32_t total = (uint32_t)__builtin_amdgcn_readlane((int)incl, kWave - 1);
-            uint32_t above = total - incl;        // elements in bins of higher lanes
-            const uint32_t cs[4] = {c0, c1, c2, c3};
-            for (int qd = 3; qd >= 0; --qd) {
-                if (above < need && above + cs[qd] >= need) {
-                    sh_digit = 4 * tid + qd;
-                    sh_above = above;
-                    sh_done = above + cs[qd] == need;   // the whole bin is taken
-                }
-                above += cs[qd];
-            }
+        if (threadIdx.x == 0) {
+            int32_t *cnt = a.counters + (size_t)b * a.num_kv_heads + kv;
+            const int old = __hip_atomic_fetch_add(cnt, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            const int last = old == a.blocks_per_head - 1;
+            if (last) __hip_atomic_store(cnt, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            s_last = last;
         }
         __syncthreads();
-        need -= sh_above;
-        prefix |= (unsigned long long)sh_digit << lo;
-        mask |= (unsigned long long)dmask << lo;
-        hi = lo;
-        if (sh_done) break;
-        buf ^= 1;
+        if (s_last)
+            topk_rows<kScoreThreads, (FPT > 0 ? FPT : 1), true>(
+                a.phys + ((size_t)b * a.num_kv_heads + kv) * a.max_pages, L, a.page_size, a.max_pages, a.k_pages,
+                a.selected + ((size_t)b * a.num_kv_heads + kv) * a.k_pages);
     }
+}
 
-    // ordered compaction
-    uint32_t c = 0;                               // low 16 bits: greater, high 16 bits: equal
-#pragma unroll
-    for (int e = 0; e < PT; ++e) {
-        if (e >= cnt) continue;
-        const unsigned long long km = key[e] & mask;
-        c += km > prefix ? 1u : (km == prefix ? 0x10000u : 0u);
-    }
-    const uint32_t excl = block_exclusive_scan(c, wave_tot);
-    uint32_t gt_before = excl & 0xFFFFu;
-    uint32_t eq_before = excl >> 16;
-#pragma unroll
-    for (int e = 0; e < PT; ++e) {
-        if (e >= cnt) continue;
-        const unsigned long long km = key[e] & mask;
-        if (km > prefix) {
-            out[gt_before + min(eq_before, need)] = i0 + e;
-            ++gt_before;
-        } else if (km == prefix) {
-            if (eq_before < need) out[gt_before + eq_before] = i0 + e;
-            ++eq_before;
-        }
-    }
+template <int KV_DT, bool AGG_MAX, int FPT>
+void launch_score_fpt(const ScoreArgs &a, unsigned grid, hipStream_t s) {
+    if (a.head_dim == 128) hipLaunchKernelGGL((score_kernel<KV_DT, 128, AGG_MAX, FPT>), dim3(grid), dim3(kScoreThreads), 0, s, a);
+    else hipLaunchKernelGGL((score_kernel<KV_DT, 64, AGG_MAX, FPT>), dim3(grid), dim3(kScoreThreads), 0, s, a);
 }
 
 template <int KV_DT, bool AGG_MAX>
 hipError_t launch_score_agg(const ScoreArgs &a, unsigned grid, hipStream_t s) {
-    if (a.head_dim == 128) hipLaunchKernelGGL((score_kernel<KV_DT, 128, AGG_MAX>), dim3(grid), dim3(kScoreThreads), 0, s, a);
-    else hipLaunchKernelGGL((score_kernel<KV_DT, 64, AGG_MAX>), dim3(grid), dim3(kScoreThreads), 0, s, a);
+    switch (a.fused_pt) {
+        case 0: launch_score_fpt<KV_DT, AGG_MAX, 0>(a, grid, s); break;
+        case 4: launch_score_fpt<KV_DT, AGG_MAX, 4>(a, grid, s); break;
+        case 8: launch_score_fpt<KV_DT, AGG_MAX, 8>(a, grid, s); break;
+        case 16: launch_score_fpt<KV_DT, AGG_MAX, 16>(a, grid, s); break;
+        default: return hipErrorInvalidValue;
+    }
     return hipGetLastError();
 }
 
@@ -482,6 +538,11 @@ int score_pages_per_block(int kv_dtype, int head_dim, int page_size, int logical
 }
 
 int topk_max_pages() { return kTopkThreads * kTopkPerThread; }
+
+int score_fused_pt(int max_pages) {
+    const int per = (max_pages + kScoreThreads - 1) / kScoreThreads;
+    return per <= 4 ? 4 : per <= 8 ? 8 : per <= 16 ? 16 : 0;
+}
 
 hipError_t launch_score(const ScoreArgs &a, hipStream_t s) {
     const long long grid = (long long)a.batch * a.n_ret * a.blocks_per_head;

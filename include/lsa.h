@@ -20,9 +20,10 @@
  *   - Pointers are DEVICE pointers unless marked [host].
  *   - Every buffer is owned by the caller; the library allocates nothing and
  *     keeps no state of its own between calls.  Workspaces are sized by the
- *     *_workspace queries.  The decode workspace holds arrival counters that
- *     must be zero when a call starts; every completed call leaves them zero,
- *     so zero-filling the buffer once, before its first use, is enough.
+ *     *_workspace queries.  The selection and decode workspaces hold arrival
+ *     counters that must be zero when a call starts; every completed call
+ *     leaves them zero, so zero-filling a workspace once, before its first
+ *     use, is enough.
  *   - Calls are asynchronous on `stream` (a hipStream_t; NULL = the default
  *     stream) and never synchronise the host.
  *   - Arguments are validated on the host before any launch.  A validation
@@ -182,7 +183,13 @@ lsa_status lsa_select_pages_workspace(const lsa_kv *kv, const lsa_seqs *seqs,
  * q: [B][H_q][head_dim] of q_dtype (LSA_F32 or LSA_BF16).
  * stats: as built by lsa_build_page_stats for tokens < seq_lens[b].
  * selected: [B][H_kv][K] int32.
- * workspace: at least lsa_select_pages_workspace bytes, 256-byte aligned. */
+ * workspace: at least lsa_select_pages_workspace bytes, 256-byte aligned,
+ * zero-filled before its first use: its leading B * H_kv int32 arrival
+ * counters must be zero when a call starts, and each completed call leaves
+ * them zero; calls that share a workspace must not overlap in time.
+ * Up to 4096 pages per sequence one kernel is launched (the last score
+ * workgroup of a (sequence, head) runs its top-K); above that a second,
+ * top-K kernel follows. */
 lsa_status lsa_select_pages(const void *q, int32_t q_dtype, const lsa_kv *kv,
                             const void *stats, const lsa_seqs *seqs,
                             const lsa_heads *heads, int32_t token_budget,

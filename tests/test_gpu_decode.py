@@ -29,7 +29,7 @@ class Runner:
         self.stats = torch.zeros(lsa.page_stats_bytes(self.kv), dtype=torch.uint8, device=DEV)
         lsa.build_page_stats(self.kv, w.page_table, lens0, self.stats, heads=self.hd)
         self.selected = torch.full((w.batch, w.num_kv_heads, self.K), -1, dtype=torch.int32, device=DEV)
-        self.ws_sel = torch.empty(lsa.select_pages_workspace(self.kv, w.page_table, lens0, self.hd),
+        self.ws_sel = torch.zeros(lsa.select_pages_workspace(self.kv, w.page_table, lens0, self.hd),
                                   dtype=torch.uint8, device=DEV)
         self.ws_dec = torch.zeros(lsa.decode_workspace(self.kv, w.page_table, lens0, self.hd, w.token_budget),
                                   dtype=torch.uint8, device=DEV)

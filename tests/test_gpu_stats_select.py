@@ -116,7 +116,7 @@ def run_select(w, step, lens, stats=None, selected=None, decode_step=0, agg=lsa.
     K = w.token_budget // w.page_size
     if selected is None:
         selected = torch.full((w.batch, w.num_kv_heads, K), -7, dtype=torch.int32, device=DEV)
-    ws = torch.empty(lsa.select_pages_workspace(kv, w.page_table, seq_lens, hd), dtype=torch.uint8, device=DEV)
+    ws = torch.zeros(lsa.select_pages_workspace(kv, w.page_table, seq_lens, hd), dtype=torch.uint8, device=DEV)
     lsa.select_pages(w.q[step], kv, stats, w.page_table, seq_lens, hd, w.token_budget, decode_step,
                      w.reuse_interval, selected, ws)
     torch.cuda.synchronize()
@@ -243,3 +243,19 @@ def test_select_full_size_cfg2():
     gaps = []
     check_selection(w, 0, lens, sel, report=gaps)
     print(f"smallest relative gap between the K-th and (K+1)-th page scores: {min(gaps):.3e}")
+
+
+@pytest.mark.parametrize("pages", [4096, 4097])
+def test_select_either_side_of_one_kernel_limit(pages):
+    """Up to 4096 pages per sequence the last score workgroup of a (sequence,
+    head) runs its top-K; from 4097 pages a separate top-K kernel does.  Both
+    sides of that limit, with a shorter second sequence in the batch."""
+    w = W.make_decode(2, DEV, batch=2, ctx=[pages * 64 - 4, 3000])      # + 4 window tokens
+    assert w.max_pages == pages
+    lens = [c + 1 for c in w.ctx]
+    sel = run_select(w, 0, lens)
+    ret = [kv for kv in range(w.num_kv_heads) if w.head_kind[kv] == 0]
+    check_selection(w, 0, lens, sel, pairs={(0, ret[0]), (0, ret[-1]), (1, ret[0])})
+    del w
+    torch.cuda.empty_cache()
+
