@@ -27,6 +27,8 @@
 // registers of a lane are directly the B operand of the PV product.
 #include "lsa_internal.h"
 
+#include <type_traits>
+
 namespace lsa {
 namespace {
 
@@ -135,8 +137,29 @@ __global__ __launch_bounds__(512, 2) void prefill_bf16_kernel(PrefillArgs p) {
     // V as [2 blocks][D channels][32 tokens]; 16-byte chunk c of a 64-byte row r sits at
     // position c ^ ((r >> 2) & 3) of its row (row = key for K, channel for V), which keeps
     // the MFMA operand reads free of bank conflicts.
-    __shared__ __attribute__((aligned(16))) uint16_t k_lds[2][kTile * D];
-    __shared__ __attribute__((aligned(16))) uint16_t v_lds[2][kTile * D];
+    // A ring of four K and four V tiles: step ii computes on K(ii) and V(ii-1)
+    // while K(ii+2) and V(ii+1) land, so a fetch has two steps to arrive.  Each
+    // buffer is an LDS object of its own and the steps are unrolled by four, so
+    // the compiler can tell that the tile being read is not one that a fetch
+    // in flight writes (else it waits for every fetch before each read).
+    __shared__ __attribute__((aligned(16))) uint16_t k_lds0[kTile * D], k_lds1[kTile * D], k_lds2[kTile * D],
+        k_lds3[kTile * D];
+    __shared__ __attribute__((aligned(16))) uint16_t v_lds0[kTile * D], v_lds1[kTile * D], v_lds2[kTile * D],
+        v_lds3[kTile * D];
+    auto kbuf = [&](auto b) -> uint16_t * {
+        constexpr int i = decltype(b)::value & 3;
+        if constexpr (i == 0) return k_lds0;
+        else if constexpr (i == 1) return k_lds1;
+        else if constexpr (i == 2) return k_lds2;
+        else return k_lds3;
+    };
+    auto vbuf = [&](auto b) -> uint16_t * {
+        constexpr int i = decltype(b)::value & 3;
+        if constexpr (i == 0) return v_lds0;
+        else if constexpr (i == 1) return v_lds1;
+        else if constexpr (i == 2) return v_lds2;
+        else return v_lds3;
+    };
 
     const PItem it = prefill_item<CSR, QT>(p);
     const TileRow trow = tile_row<CSR, QT>(p, it);
@@ -188,24 +211,14 @@ __global__ __launch_bounds__(512, 2) void prefill_bf16_kernel(PrefillArgs p) {
 
     const uint16_t *kpool = static_cast<const uint16_t *>(p.k);
     const uint16_t *vpool = static_cast<const uint16_t *>(p.v);
-    // Static masks: the row's key tiles stream through two 64-entry register
-    // windows (entries w0 .. w0 + 127 of the row, one per lane), read with
-    // readlane; a window is refilled about 60 steps before it is needed, so
-    // no step waits on an index load.
-    int win_lo = 0, win_hi = 0, w0 = 0;
-    auto load_win = [&](int base) {
-        const int e = base + lane;
-        return e < n_iter ? p.col_idx[trow.rp0 + e] : 0;
-    };
-    if constexpr (CSR) {
-        win_lo = load_win(0);
-        win_hi = load_win(kWave);
-    }
+    // Static masks: the row's column indices are read with scalar loads
+    // (constant address space, like the page table below), which the tile
+    // fetches in flight do not delay; ii < n_iter always.
+    const int32_t __attribute__((address_space(4))) *cidx =
+        (const int32_t __attribute__((address_space(4))) *)p.col_idx + trow.rp0;
     auto tile_of = [&](int ii) {
         if constexpr (CSR) {
-            const int j = ii - w0;
-            const int c = j < kWave ? __builtin_amdgcn_readlane(win_lo, j) : __builtin_amdgcn_readlane(win_hi, j - kWave);
-            return min(max(c, 0), it.a);
+            return min(max((int)cidx[ii], 0), it.a);
         } else {
             return row_tile<false>(p, it, trow, ii);
         }
@@ -230,8 +243,8 @@ __global__ __launch_bounds__(512, 2) void prefill_bf16_kernel(PrefillArgs p) {
     // 64j .. 64j+63 (16 rows of 4 chunks); lane l writes position l, i.e. row
     // 16j + l/4, position l%4, and so reads the row's logical chunk
     // (l%4) ^ swz(row) from the pool: one contiguous 1 KiB per instruction.
-    auto fetch = [&](const uint16_t *pool, uint16_t *lds, int ii) {
-        const uint16_t *src = pool + tile_base(tile_of(ii));
+    auto fetch = [&](const uint16_t *pool, uint16_t *lds, size_t base) {
+        const uint16_t *src = pool + base;
 #pragma unroll
         for (int e = 0; e < KPT; ++e) {
             const int j = wave + e * (NT / kWave);
@@ -244,36 +257,37 @@ __global__ __launch_bounds__(512, 2) void prefill_bf16_kernel(PrefillArgs p) {
     };
     // values of keys >= T (only in the sequence's last tile) may hold any bits:
     // zero them once they have landed, so a zero probability never meets a NaN
-    auto zero_v_tail = [&](int vb, int ii) {
-        const int key0 = tile_of(ii) * kTile;
+    auto zero_v_tail = [&](uint16_t *vl, int key0) {
         if (key0 + kTile <= T) return;
         for (int e = tid; e < 2 * D * 32; e += NT) {
             const int blk = e / (D * 32), ch = (e / 32) % D, t = e % 32;
             if (key0 + 32 * blk + t >= T)
-                v_lds[vb][(blk * D + ch) * 32 + (((t >> 3) ^ swz(ch)) << 3) + (t & 7)] = 0;
+                vl[(blk * D + ch) * 32 + (((t >> 3) ^ swz(ch)) << 3) + (t & 7)] = 0;
         }
     };
     const float sc = p.scale_log2;
-    // S^T = K Q^T of the tile in K buffer kb: lane holds keys 32*kt + 16*(r/8) + 8*lg + r%8, query q0 + col
+    // S^T = K Q^T of the tile in K buffer kl: lane holds keys 32*kt + 16*(r/8) + 8*lg + r%8, query q0 + col
     // MFMA row col of tile kt reads key 32*kt + rho(col), rho swapping bits 2 and 3,
     // so the score registers come out in the order the PV B operand needs.
     const int krho = (col & 19) | ((col & 4) << 1) | ((col & 8) >> 1);
-    auto k_at = [&](int kb, int kt, int st) {
+    auto k_at = [&](const uint16_t *kl, int kt, int st) {
         const int slice = st >> 1, c = 2 * (st & 1) + lg;
         return __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4 *>(
-            &k_lds[kb][((kt * NS + slice) * 32 + krho) * 32 + ((c ^ swz(krho)) << 3)]));
+            &kl[((kt * NS + slice) * 32 + krho) * 32 + ((c ^ swz(krho)) << 3)]));
     };
-    auto qk = [&](int kb, floatx16 (&s)[2]) {
+    auto qk = [&](const uint16_t *kl, floatx16 (&s)[2]) {
 #pragma unroll
         for (int kt = 0; kt < 2; ++kt) {
-            s[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k_at(kb, kt, 0), qb[0], floatx16{}, 0, 0, 0);
+            s[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k_at(kl, kt, 0), qb[0], floatx16{}, 0, 0, 0);
 #pragma unroll
             for (int st = 1; st < D / 16; ++st)
-                s[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k_at(kb, kt, st), qb[st], s[kt], 0, 0, 0);
+                s[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k_at(kl, kt, st), qb[st], s[kt], 0, 0, 0);
         }
     };
-    // online softmax of the scores s (diag: causal mask against key0), then O^T += V^T P^T
-    auto softmax_pv = [&](floatx16 (&s)[2], int vb, int key0, bool diag) {
+    // online softmax of the scores s (diag: causal mask against key0): rescale
+    // O and l when the running max moves, and pack P = exp2(s * sc - m) as the
+    // bf16 B operands of the four k-steps of O^T += V^T P^T
+    auto softmax_p = [&](floatx16 (&s)[2], int key0, bool diag, bf16x8 (&pb)[4]) {
         if (diag) {
             const int qrow = q0 + col;
 #pragma unroll
@@ -309,67 +323,121 @@ __global__ __launch_bounds__(512, 2) void prefill_bf16_kernel(PrefillArgs p) {
                     l_run += e0v + e1v;
                     pk[j / 2] = __builtin_bit_cast(uint32_t, __builtin_convertvector(floatx2{e0v, e1v}, bf16x2));
                 }
-                const bf16x8 pb = __builtin_bit_cast(bf16x8, make_uint4(pk[0], pk[1], pk[2], pk[3]));
-                // k-step (kt, st): keys 32*kt + 16*st + 8*lg + j
+                pb[2 * kt + st] = __builtin_bit_cast(bf16x8, make_uint4(pk[0], pk[1], pk[2], pk[3]));
+            }
+    };
+    // O^T += V^T P^T over the tile in V buffer vl; k-step (kt, st) covers keys 32*kt + 16*st + 8*lg + j
+    auto pv = [&](const uint16_t *vl, const bf16x8 (&pb)[4]) {
+#pragma unroll
+        for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+            for (int st = 0; st < 2; ++st)
 #pragma unroll
                 for (int dt = 0; dt < D / 32; ++dt) {
                     const int ch = 32 * dt + col, c = 2 * st + lg;
                     const bf16x8 va = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4 *>(
-                        &v_lds[vb][(kt * D + ch) * 32 + ((c ^ swz(ch)) << 3)]));
-                    o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pb, o[dt], 0, 0, 0);
+                        &vl[(kt * D + ch) * 32 + ((c ^ swz(ch)) << 3)]));
+                    o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pb[2 * kt + st], o[dt], 0, 0, 0);
                 }
-            }
     };
 
-    // prologue: K(0) in LDS
-    fetch(kpool, k_lds[0], 0);
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    // s_waitcnt immediates (vmcnt in bits 3:0 and 15:14, expcnt 6:4, lgkmcnt
+    // 11:8), issued through the builtin so the compiler knows what has landed
+    constexpr int kWaitVm0 = 0x0F70;                  // vmcnt(0)
+    constexpr int kWaitStep = 0x0070 | (2 * KPT);     // vmcnt(2 KPT) lgkmcnt(0): one step's fetches may stay in flight
+    using I0 = std::integral_constant<int, 0>;
+    using I1 = std::integral_constant<int, 1>;
+    using I2 = std::integral_constant<int, 2>;
+    using I3 = std::integral_constant<int, 3>;
+
+    // Every step issues the same two fetches, so the count of loads in flight
+    // is the same on every path (the compiler then knows which tiles have
+    // landed); past the row's end a step fetches the row's last tile again
+    // into a buffer that is not read again.
+    auto clamp_tile = [&](int ii) { return tile_of(min(ii, n_iter - 1)); };
+    // prologue: K(0), V(0) and K(1) in LDS.  The key tiles of steps ii - 1,
+    // ii and ii + 1 travel from step to step: a step looks up only tile ii + 2.
+    int c_prev = tile_of(0), c_cur = c_prev, c_n1 = clamp_tile(1);
+    size_t base_next = tile_base(c_cur);             // pool offset of the tile whose V is fetched next
+    fetch(kpool, k_lds0, base_next);
+    fetch(vpool, v_lds0, base_next);
+    base_next = tile_base(c_n1);
+    fetch(kpool, k_lds1, base_next);
+    __builtin_amdgcn_s_waitcnt(kWaitVm0);
     __syncthreads();
     floatx16 sa[2], sb[2];                           // scores of even / odd tiles
-    auto step = [&](int ii, floatx16 (&s_cur)[2], floatx16 (&s_prev)[2]) {
-        // landing in LDS during the compute: K(ii+1) and V(ii), in the buffers
-        // last read before the previous barrier
-        if (ii + 1 < n_iter) fetch(kpool, k_lds[(ii + 1) & 1], ii + 1);
-        fetch(vpool, v_lds[ii & 1], ii);
-        if (head_ok) {
-            if constexpr (QT == 1) {
-                qk(ii & 1, s_cur);
-                if (ii > 0) softmax_pv(s_prev, (ii - 1) & 1, tile_of(ii - 1) * kTile, false);
-            } else {
-                if (sees(tile_of(ii))) qk(ii & 1, s_cur);
-                if (ii > 0) {
-                    const int c = tile_of(ii - 1);
-                    if (sees(c)) softmax_pv(s_prev, (ii - 1) & 1, c * kTile, c == a_s);
-                }
-            }
-        }
-        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-        if (ii == n_iter - 1) {                       // the last tile may reach past T
-            __syncthreads();
-            zero_v_tail(ii & 1, ii);
-        }
-        __syncthreads();
-        if constexpr (CSR) {
-            // the next step reads entries ii .. ii + 2: slide the windows once ii leaves the low one
-            if (ii >= w0 + kWave) {
-                w0 += kWave;
-                win_lo = win_hi;
-                win_hi = load_win(w0 + kWave);
-            }
-        }
+    auto bar = [] {                                  // a plain barrier, kept in place by the compiler
+        asm volatile("" ::: "memory");
+        __builtin_amdgcn_s_barrier();
+        asm volatile("" ::: "memory");
     };
-    int ii = 0;
-    for (; ii + 1 < n_iter; ii += 2) {
-        step(ii, sa, sb);
-        step(ii + 1, sb, sa);
+    // Ping-pong.  A step is a VALU phase (the previous tile's softmax) and an
+    // MFMA phase (its PV product, then this tile's QK^T), each closed by a
+    // barrier.  Waves 4-7 pass one extra barrier first and so run one phase
+    // behind waves 0-3: the two wavefronts of a SIMD (w and w + 4) alternate,
+    // one computing exponentials while the other feeds the matrix core.  The
+    // ring keeps this safe: a fetch writes a buffer three tiles away from any
+    // the other group reads, and every tile has been waited for by both
+    // groups before the barrier that opens a phase reading it.
+    const bool lag = wave >= 4;
+    if (lag) bar();
+    auto step = [&](auto b, int ii, floatx16 (&s_cur)[2], floatx16 (&s_prev)[2]) {
+        constexpr int B = decltype(b)::value;        // == ii % 4
+        using Next2 = std::integral_constant<int, B + 2>;
+        using Next1 = std::integral_constant<int, B + 1>;
+        using Prev = std::integral_constant<int, B + 3>;
+        // K(ii+2) and V(ii+1) land during the step, in buffers last read two
+        // steps ago; the V tile's pool offset is the one its K fetch used
+        const int c_n2 = clamp_tile(ii + 2);
+        const size_t base_k = tile_base(c_n2);
+        fetch(kpool, kbuf(Next2{}), base_k);
+        fetch(vpool, vbuf(Next1{}), base_next);
+        base_next = base_k;
+        // With QT == 1 every pair has a head (head_ok is false only past the
+        // group's last head); with QT > 1 sees() is false for a pair without a
+        // query tile.  ii > 0 is known in three of the four unrolled steps.
+        const bool prev_ok = (B != 0 || ii > 0) && (QT == 1 ? head_ok : sees(c_prev));
+        const bool cur_ok = QT == 1 ? head_ok : sees(c_cur);
+        bf16x8 pb[4];
+        if (prev_ok) softmax_p(s_prev, c_prev * kTile, QT > 1 && c_prev == a_s, pb);
+        bar();
+        if (prev_ok) pv(vbuf(Prev{}), pb);
+        if (cur_ok) qk(kbuf(b), s_cur);
+        // K(ii+1) and V(ii) have landed and this wavefront's LDS reads are
+        // done; this step's own fetches may still be in flight
+        __builtin_amdgcn_s_waitcnt(kWaitStep);
+        bar();
+        c_prev = c_cur;
+        c_cur = c_n1;
+        c_n1 = c_n2;
+    };
+    for (int ii = 0;; ii += 4) {
+        step(I0{}, ii, sa, sb);
+        if (ii + 1 >= n_iter) break;
+        step(I1{}, ii + 1, sb, sa);
+        if (ii + 2 >= n_iter) break;
+        step(I2{}, ii + 2, sa, sb);
+        if (ii + 3 >= n_iter) break;
+        step(I3{}, ii + 3, sb, sa);
+        if (ii + 4 >= n_iter) break;
     }
-    if (ii < n_iter) step(ii, sa, sb);
-    // epilogue: the last tile (the diagonal one of the highest query tile)
-    const int c_last = tile_of(n_iter - 1);
+    if (!lag) bar();                                 // the groups meet again
+    // epilogue: the last tile (the diagonal one of the highest query tile);
+    // its values past T may hold any bits: zero them, so a zero probability
+    // never meets a NaN
+    const int c_last = c_prev;                       // tile n_iter - 1
+    const int lb = (n_iter - 1) & 3;
+    uint16_t *vl_last = lb == 0 ? v_lds0 : lb == 1 ? v_lds1 : lb == 2 ? v_lds2 : v_lds3;
+    __builtin_amdgcn_s_waitcnt(kWaitVm0);            // no fetch lands after this point
+    __syncthreads();
+    zero_v_tail(vl_last, c_last * kTile);
+    __syncthreads();
     if (head_ok && (QT == 1 || sees(c_last))) {
         const bool diag = QT == 1 || c_last == a_s;
-        if ((n_iter - 1) & 1) softmax_pv(sb, (n_iter - 1) & 1, c_last * kTile, diag);
-        else softmax_pv(sa, (n_iter - 1) & 1, c_last * kTile, diag);
+        bf16x8 pb[4];
+        if ((n_iter - 1) & 1) softmax_p(sb, c_last * kTile, diag, pb);
+        else softmax_p(sa, c_last * kTile, diag, pb);
+        pv(vl_last, pb);
     }
 
     if (p.tile_counter) {

@@ -288,10 +288,15 @@ def make_decode(cfg: int, device="cpu", *, batch: Optional[int] = None, ctx=None
 
 
 def make_prefill(cfg: int, device="cpu", *, seq_len: Optional[int] = None, seed: Optional[int] = None,
-                 head_kind: Optional[List[int]] = None, num_kv_heads: Optional[int] = None) -> PrefillWorkload:
+                 head_kind: Optional[List[int]] = None, num_kv_heads: Optional[int] = None,
+                 head_dim: Optional[int] = None, page_size: Optional[int] = None) -> PrefillWorkload:
     c = dict(PREFILL_CONFIGS[cfg])
     if num_kv_heads is not None:
         c["num_kv_heads"] = num_kv_heads
+    if head_dim is not None:
+        c["head_dim"] = head_dim
+    if page_size is not None:
+        c["page_size"] = page_size
     T = seq_len if seq_len is not None else c["seq_len"]
     H_q, H_kv, D, NP = c["num_q_heads"], c["num_kv_heads"], c["head_dim"], c["page_size"]
     dt = c["dtype"]

@@ -127,6 +127,18 @@ def test_prefill_group2_small(T):
     print("max abs err", check(p, out, heads=[0, 1, 6, 17, 30, 31]))
 
 
+@pytest.mark.parametrize("D,NP,H_kv,T", [(64, 64, 8, 777), (64, 128, 8, 1088), (64, 64, 32, 700),
+                                         (64, 256, 16, 1300), (128, 256, 8, 1000), (128, 128, 32, 900)])
+def test_prefill_head_dim_and_page_size(D, NP, H_kv, T):
+    """head_dim 64 and 128 with pages of 1 to 4 tiles, for one, two and four
+    query tiles per workgroup (group sizes 4, 2 and 1)."""
+    p = W.make_prefill(3, DEV, seq_len=T, head_dim=D, page_size=NP, num_kv_heads=H_kv)
+    out, cnt = run_prefill(p)
+    assert cnt == expected_tiles(p)
+    G = p.num_q_heads // p.num_kv_heads
+    print("max abs err", check(p, out, heads=[0, G - 1, 13, 31]))
+
+
 def test_prefill_full_size_cfg7_mha_sampled():
     """Config 7 at full size (T = 131072, 32 query and 32 KV heads, 16 of them
     streaming): the same 34,125,696 non-empty (head, tile) pairs as the
