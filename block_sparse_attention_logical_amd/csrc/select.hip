@@ -408,6 +408,20 @@ __global__ __launch_bounds__(kScoreThreads) void score_kernel(ScoreArgs a) {
     double best[IT], best_cur = 0.0;
     const int n_pass = AGG_MAX ? G : 1;
     for (int hv = 0; hv < n_pass; ++hv) {
+        if constexpr (AGG_MAX) {
+            // keep the statistics packed across passes: without this the
+            // compiler converts every slot to fp64 once, before the loop, which
+            // needs four times the registers and leaves one wavefront per SIMD
+#pragma unroll
+            for (int it = 0; it < IT; ++it) {
+                if constexpr (KV_DT == LSA_INT4)
+                    asm volatile("" : "+v"(st_lo[it].x), "+v"(st_lo[it].y), "+v"(st_lo[it].z), "+v"(st_lo[it].w),
+                                 "+v"(szw[it]));
+                else
+                    asm volatile("" : "+v"(st_lo[it].x), "+v"(st_lo[it].y), "+v"(st_lo[it].z), "+v"(st_lo[it].w),
+                                 "+v"(st_hi[it].x), "+v"(st_hi[it].y), "+v"(st_hi[it].z), "+v"(st_hi[it].w));
+            }
+        }
         double qp[C], qn[C];
         load_q_pos_neg<C>(a, b, kv, ch0, AGG_MAX ? hv : 0, AGG_MAX ? hv + 1 : G, qp, qn);
         double qsum = 0.0;                        // int4 only: sum over all channels of Qp + Qn
