@@ -185,14 +185,17 @@ def tile_values(x: torch.Tensor) -> torch.Tensor:
 
 def make_decode(cfg: int, device="cpu", *, batch: Optional[int] = None, ctx=None, window: Optional[int] = None,
                 seed: Optional[int] = None, replicas: int = 1, chunk_pages: int = 2048,
-                page_size: Optional[int] = None, logical_page: Optional[int] = None) -> DecodeWorkload:
+                page_size: Optional[int] = None, logical_page: Optional[int] = None,
+                head_dim: Optional[int] = None, num_q_heads: Optional[int] = None,
+                num_kv_heads: Optional[int] = None) -> DecodeWorkload:
     """Build a decode workload.  Overrides shrink a config for tests or change
-    its page geometry (physical page size N_P, logical page size N_L)."""
+    its page geometry (physical page size N_P, logical page size N_L) or its
+    head shape."""
     c = dict(DECODE_CONFIGS[cfg])
-    if page_size is not None:
-        c["page_size"] = page_size
-    if logical_page is not None:
-        c["logical_page"] = logical_page
+    for key, val in (("page_size", page_size), ("logical_page", logical_page), ("head_dim", head_dim),
+                     ("num_q_heads", num_q_heads), ("num_kv_heads", num_kv_heads)):
+        if val is not None:
+            c[key] = val
     B = batch if batch is not None else c["batch"]
     W = window if window is not None else c["window"]
     ctx_spec = ctx if ctx is not None else c["ctx"]
@@ -289,14 +292,13 @@ def make_decode(cfg: int, device="cpu", *, batch: Optional[int] = None, ctx=None
 
 def make_prefill(cfg: int, device="cpu", *, seq_len: Optional[int] = None, seed: Optional[int] = None,
                  head_kind: Optional[List[int]] = None, num_kv_heads: Optional[int] = None,
-                 head_dim: Optional[int] = None, page_size: Optional[int] = None) -> PrefillWorkload:
+                 head_dim: Optional[int] = None, page_size: Optional[int] = None,
+                 num_q_heads: Optional[int] = None) -> PrefillWorkload:
     c = dict(PREFILL_CONFIGS[cfg])
-    if num_kv_heads is not None:
-        c["num_kv_heads"] = num_kv_heads
-    if head_dim is not None:
-        c["head_dim"] = head_dim
-    if page_size is not None:
-        c["page_size"] = page_size
+    for key, val in (("num_kv_heads", num_kv_heads), ("head_dim", head_dim), ("page_size", page_size),
+                     ("num_q_heads", num_q_heads)):
+        if val is not None:
+            c[key] = val
     T = seq_len if seq_len is not None else c["seq_len"]
     H_q, H_kv, D, NP = c["num_q_heads"], c["num_kv_heads"], c["head_dim"], c["page_size"]
     dt = c["dtype"]

@@ -118,6 +118,20 @@ def test_decode_cfg5_int4_small(ctx):
     print("max abs err", check_window(w))
 
 
+@pytest.mark.parametrize("cfg,D,H_q,H_kv,ctx", [(2, 64, 32, 8, [3000, 7000]), (5, 64, 32, 8, [2100, 5000]),
+                                                 (2, 128, 32, 2, [3000, 6000]), (5, 128, 32, 2, [3000]),
+                                                 (2, 128, 24, 8, [2500, 700]), (2, 128, 64, 8, [2000, 4500]),
+                                                 (2, 64, 16, 16, [1500])])
+def test_decode_head_shapes(cfg, D, H_q, H_kv, ctx):
+    """head_dim 64 and 128, bf16 and int4 pools, group sizes 1, 3, 4, 8 and 16
+    (the largest the matrix-core mapping takes), through selection and
+    attention over the whole window."""
+    w = W.make_decode(cfg, DEV, batch=len(ctx), ctx=ctx, head_dim=D, num_q_heads=H_q, num_kv_heads=H_kv)
+    ret = [kv for kv in range(w.num_kv_heads) if w.head_kind[kv] == 0][:2]
+    st = [kv for kv in range(w.num_kv_heads) if w.head_kind[kv] == 1][:1]
+    print("max abs err", check_window(w, kv_heads=ret + st))
+
+
 def test_decode_refreshes_statistics():
     """After a window of fused steps the statistics pool equals a full build
     at the final length (every logical page the window touched refreshed)."""

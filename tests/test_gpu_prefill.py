@@ -139,6 +139,17 @@ def test_prefill_head_dim_and_page_size(D, NP, H_kv, T):
     print("max abs err", check(p, out, heads=[0, G - 1, 13, 31]))
 
 
+@pytest.mark.parametrize("H_q,H_kv,T", [(24, 8, 777), (40, 8, 1088), (64, 8, 700), (32, 2, 900)])
+def test_prefill_group_sizes(H_q, H_kv, T):
+    """Group sizes 3, 5, 8 and 16: several workgroups per (KV head, query
+    tile), the last one with fewer than four heads."""
+    p = W.make_prefill(3, DEV, seq_len=T, num_q_heads=H_q, num_kv_heads=H_kv)
+    out, cnt = run_prefill(p)
+    assert cnt == expected_tiles(p)
+    G = H_q // H_kv
+    print("max abs err", check(p, out, heads=sorted({0, 3, G - 1, G, H_q - 1})))
+
+
 def test_prefill_full_size_cfg7_mha_sampled():
     """Config 7 at full size (T = 131072, 32 query and 32 KV heads, 16 of them
     streaming): the same 34,125,696 non-empty (head, tile) pairs as the
