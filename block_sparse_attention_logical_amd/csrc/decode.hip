@@ -436,29 +436,27 @@ __global__ __launch_bounds__(kDecodeWaves * kWave, 2) void decode_mfma_kernel(De
                 for (int T = 0; T < 2; ++T) {
                     const uint8_t *row = k8 + (base + key_offset(32 * kb + 16 * T + rho, (D / 4) * g4, D)) / 2;
                     if constexpr (D == 128) {
-                        kr[e][T][0] = *reinterpret_cast<const uint4 *>(row);
+                        kr[e][T][0] = load_stream16(row);
                     } else {
-                        const uint2 u = *reinterpret_cast<const uint2 *>(row);
+                        const uint2 u = load_stream8(row);
                         kr[e][T][0] = make_uint4(u.x, u.y, 0, 0);
                     }
                 }
                 const uint8_t *v8 = static_cast<const uint8_t *>(a.v);
 #pragma unroll
                 for (int dt = 0; dt < NDT; ++dt)
-                    vr4[e][dt] = *reinterpret_cast<const uint32_t *>(
-                        v8 + (base + value_offset(32 * kb + 8 * g4, 16 * dt + h, D)) / 2);
+                    vr4[e][dt] = load_stream4(v8 + (base + value_offset(32 * kb + 8 * g4, 16 * dt + h, D)) / 2);
             } else {
                 const uint16_t *kp = static_cast<const uint16_t *>(a.k) + base;
 #pragma unroll
                 for (int T = 0; T < 2; ++T)
 #pragma unroll
                     for (int s = 0; s < NS; ++s)
-                        kr[e][T][s] = *reinterpret_cast<const uint4 *>(
-                            kp + key_offset(32 * kb + 16 * T + rho, 32 * s + 8 * g4, D));
+                        kr[e][T][s] = load_stream16(kp + key_offset(32 * kb + 16 * T + rho, 32 * s + 8 * g4, D));
                 const uint16_t *vp = static_cast<const uint16_t *>(a.v) + base;
 #pragma unroll
                 for (int dt = 0; dt < NDT; ++dt)
-                    vr[e][dt] = *reinterpret_cast<const uint4 *>(vp + value_offset(32 * kb + 8 * g4, 16 * dt + h, D));
+                    vr[e][dt] = load_stream16(vp + value_offset(32 * kb + 8 * g4, 16 * dt + h, D));
             }
             // keep the block's loads ahead of the compute that follows them
             __builtin_amdgcn_sched_barrier(0);

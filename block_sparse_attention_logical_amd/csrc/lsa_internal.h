@@ -52,6 +52,21 @@ __device__ __forceinline__ float fp16_bits_to_f32(uint16_t h) {
 // 2^x on the hardware exponential unit
 __device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// Loads of data read once per launch (decode K/V blocks, page statistics in
+// scoring) carry the non-temporal hint, so the stream does not displace lines
+// the rest of the launch still uses.
+__device__ __forceinline__ uint4 load_stream16(const void *p) {
+    typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+    return __builtin_bit_cast(uint4, __builtin_nontemporal_load(static_cast<const u32x4 *>(p)));
+}
+__device__ __forceinline__ uint2 load_stream8(const void *p) {
+    typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+    return __builtin_bit_cast(uint2, __builtin_nontemporal_load(static_cast<const u32x2 *>(p)));
+}
+__device__ __forceinline__ uint32_t load_stream4(const void *p) {
+    return __builtin_nontemporal_load(static_cast<const uint32_t *>(p));
+}
+
 // ----------------------------------------------------------------------------
 // page layout: a page of N_P tokens of one KV head is N_P/32 blocks of 32
 // tokens; keys are [block][D/32][32 tokens][32 channels] tiles, values are

@@ -373,13 +373,12 @@ __global__ __launch_bounds__(kScoreThreads) void score_kernel(ScoreArgs a) {
             const size_t hp = (size_t)pools[it] * a.num_kv_heads + kv;
             const int jl = j % g;
             if constexpr (KV_DT == LSA_INT4) {
-                st_lo[it] = *reinterpret_cast<const uint4 *>(static_cast<const uint8_t *>(a.stats) + hp * head_stride +
-                                                             (size_t)jl * D + ch0);
-                szw[it] = *reinterpret_cast<const uint32_t *>(a.k_sz + hp * 2);
+                st_lo[it] = load_stream16(static_cast<const uint8_t *>(a.stats) + hp * head_stride + (size_t)jl * D + ch0);
+                szw[it] = load_stream4(a.k_sz + hp * 2);
             } else {
                 const char *st = static_cast<const char *>(a.stats) + (hp * head_stride + (size_t)jl * 2 * D + ch0) * EB;
-                st_lo[it] = *reinterpret_cast<const uint4 *>(st);
-                st_hi[it] = *reinterpret_cast<const uint4 *>(st + (size_t)D * EB);
+                st_lo[it] = load_stream16(st);
+                st_hi[it] = load_stream16(st + (size_t)D * EB);
             }
         }
     }
