@@ -118,13 +118,14 @@ __device__ __forceinline__ int row_tile(const PrefillArgs &p, const PItem &it, c
 // bf16 MFMA kernel, head_dim D.  Eight wavefronts: wave w takes query head
 // hg*4 + w/2 and query rows 32*(w%2) .. +31 of the tile, so with GQA group 4
 // one workgroup covers the tile's four heads and reads each K/V tile once.
-// Software pipeline: iteration t issues the QK^T MFMAs of key tile t, then
-// runs the softmax and PV of tile t-1, whose VALU work overlaps the QK
-// MFMAs in flight.  K tiles and V tiles are double-buffered in LDS separately
-// (V lags K by one tile) and loaded from global memory straight into LDS
-// (global_load_lds_dwordx4: no registers, no LDS store instructions) while
-// the compute runs, one barrier per tile.  The last tile is the diagonal one:
-// its causal mask is applied in the pipeline's epilogue only.
+// Step t runs the softmax of key tile t-1 (VALU phase), then its PV product
+// and the QK^T MFMAs of tile t (MFMA phase); waves 4-7 run one phase behind
+// waves 0-3, so the two wavefronts of each SIMD alternate between the
+// phases.  K and V tiles sit in a four-deep LDS ring, loaded from global
+// memory straight into LDS (global_load_lds_dwordx4: no registers, no LDS
+// store instructions) two tiles (K) and one tile (V) ahead of their use.
+// The last tile is the diagonal one: its causal mask is applied in the
+// epilogue only.
 // ---------------------------------------------------------------------------
 template <int D, bool CSR, int QT>
 __global__ __launch_bounds__(512, 2) void prefill_bf16_kernel(PrefillArgs p) {
