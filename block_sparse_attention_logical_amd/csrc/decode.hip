@@ -36,6 +36,8 @@
 // the ring is always loaded (a block that needs no keys re-reads the
 // wavefront's first needed block, which is already on its way to the caches),
 // so the wait before each block counts exactly the loads issued after it.
+// The block loads carry the non-temporal hint: each K/V byte is read once per
+// launch, and the stream should not displace the lines the launch reuses.
 //
 // int4 pools.  A code c (0..15) becomes the bf16 bit pattern 0x4300 | c, which
 // is exactly 128 + c, so the MFMAs see exact operands; the offset and the

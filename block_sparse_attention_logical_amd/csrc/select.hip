@@ -23,9 +23,14 @@
 // registers; a most significant digit first radix select finds the K-th
 // largest key.  The passes start at the highest bit in which the keys differ
 // (the bits above it are common to all keys) and take the next 8 bits each;
-// the histogram is in LDS, double-buffered so a pass needs two barriers.  Equal keys are taken in
-// ascending page order (ties to the lower page index); an ordered compaction
-// writes the selected pages in ascending order.
+// the histogram is in LDS, double-buffered so a pass needs two barriers.
+// Equal keys are taken in ascending page order (ties to the lower page
+// index); an ordered compaction writes the selected pages in ascending order.
+// Up to 4096 pages per sequence the ranking runs inside the score kernel: the
+// last score workgroup of a (sequence, head) to finish, counted with an
+// arrival counter, ranks that head; above that a separate top-K kernel does.
+// The page statistics are read once per launch and carry the non-temporal
+// hint.
 #include "lsa_internal.h"
 
 namespace lsa {
