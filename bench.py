@@ -73,7 +73,33 @@ def parse():
     ap.add_argument("--counters", action="store_true",
                     help="counter-collection run: one 1 GiB device copy (the calibration kernel), then one eager "
                          "decode cycle over the replicas; prints nothing else")
+    ap.add_argument("--gemm-reference", action="store_true",
+                    help="time a plain 16384x16384x8192 bf16 torch.matmul (the vendor GEMM library) as the "
+                         "practical matrix-core reference for the prefill figure, and print one JSON line")
     return ap.parse_args()
+
+
+def gemm_reference(torch):
+    """A large bf16 GEMM through torch (hipBLASLt): what the matrix cores
+    sustain on this part in a plain contraction, to set the prefill kernel's
+    MFMA fraction against something reachable."""
+    m, n, k = 16384, 16384, 8192
+    a = torch.randn(m, k, dtype=torch.bfloat16, device="cuda")
+    b = torch.randn(k, n, dtype=torch.bfloat16, device="cuda")
+    for _ in range(3):
+        c = a @ b
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    reps = 20
+    e0.record()
+    for _ in range(reps):
+        c = a @ b
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / reps
+    del c
+    return {"gemm": f"bf16 {m}x{n}x{k} torch.matmul", "ms": round(ms, 4),
+            "tflops": round(2 * m * n * k / ms / 1e9, 1), "frac_of_2500": round(2 * m * n * k / ms / 1e9 / 2500, 4)}
 
 
 def counters_run(args, torch, lsa, W):
@@ -419,6 +445,9 @@ def main():
 
     if args.counters:
         counters_run(args, torch, lsa, W)
+        return
+    if args.gemm_reference:
+        print(json.dumps(gemm_reference(torch)))
         return
     if args.prefill_only:
         pre = bench_prefill(args, torch, lsa, W, O)
