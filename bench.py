@@ -76,7 +76,34 @@ def parse():
     ap.add_argument("--gemm-reference", action="store_true",
                     help="time a plain 16384x16384x8192 bf16 torch.matmul (the vendor GEMM library) as the "
                          "practical matrix-core reference for the prefill figure, and print one JSON line")
+    ap.add_argument("--hbm-reference", action="store_true",
+                    help="time a plain 4 GiB device copy and a 4 GiB reduction (torch) as the reachable HBM "
+                         "bandwidth reference for the decode figure, and print one JSON line")
     return ap.parse_args()
+
+
+def hbm_reference(torch):
+    """Large plain streams through torch: the HBM bandwidth a read+write copy
+    and a read-only reduction sustain on this part."""
+    n = 1 << 30                                   # 4 GiB of fp32
+    a = torch.ones(n, dtype=torch.float32, device="cuda")
+    b = torch.empty_like(a)
+    out = {}
+    for name, fn, nbytes in (("copy", lambda: b.copy_(a), 2 * 4 * n), ("sum", lambda: a.sum(), 4 * n)):
+        for _ in range(3):
+            fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        reps = 10
+        e0.record()
+        for _ in range(reps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / reps
+        out[name] = {"ms": round(ms, 4), "gbps": round(nbytes / ms / 1e6, 1), "frac_of_8000": round(nbytes / ms / 1e6 / 8000, 4)}
+    del a, b
+    return {"hbm": "4 GiB fp32 streams through torch", **out}
 
 
 def gemm_reference(torch):
@@ -448,6 +475,9 @@ def main():
         return
     if args.gemm_reference:
         print(json.dumps(gemm_reference(torch)))
+        return
+    if args.hbm_reference:
+        print(json.dumps(hbm_reference(torch)))
         return
     if args.prefill_only:
         pre = bench_prefill(args, torch, lsa, W, O)
