@@ -42,9 +42,14 @@ PEAK_HBM = 8.0e12          # MI355X HBM3E, bytes/s
 PEAK_BF16 = 2.5e15         # MI355X dense bf16 MFMA, flop/s
 
 # workload name -> (decode config, prefill config, model shape)
+# name: (decode config, prefill config, layer, KV replicas by default)
 WORKLOADS = {
-    "llama3-8b": (2, 3, "Llama-3-8B-shaped attention layer"),
-    "llama2-7b-mha": (6, 7, "Llama-2-7B-shaped (multi-head) attention layer"),
+    "llama3-8b": (2, 3, "Llama-3-8B-shaped attention layer", 8),
+    "llama2-7b-mha": (6, 7, "Llama-2-7B-shaped (multi-head) attention layer", 8),
+    # config 4: 64 sequences of 128K-256K tokens (about 51 GB of bf16 KV per replica)
+    "llama3-8b-b64-long": (4, 3, "Llama-3-8B-shaped attention layer at batch 64, 128K-256K context", 2),
+    # config 5: a 4-bit KV pool at 256K context
+    "llama3-8b-kv4": (5, 3, "Llama-3-8B-shaped attention layer with a 4-bit KV pool", 8),
 }
 
 
@@ -59,7 +64,8 @@ def parse():
     ap.add_argument("--logical-page", type=int, default=None, help="logical page size N_L of the statistics")
     ap.add_argument("--steps", type=int, default=640, help="timed decode steps (rounded up to whole cycles)")
     ap.add_argument("--warmup", type=int, default=64, help="untimed decode steps")
-    ap.add_argument("--replicas", type=int, default=8, help="KV pool replicas (layers) cycled through")
+    ap.add_argument("--replicas", type=int, default=None,
+                    help="KV pool replicas (layers) cycled through (default: 8; 2 for the batch-64 workload)")
     ap.add_argument("--prefill-reps", type=int, default=3)
     ap.add_argument("--no-prefill", action="store_true")
     ap.add_argument("--prefill-only", action="store_true", help="time only the prefill leg (profiling runs)")
@@ -191,7 +197,9 @@ def bench_decode(args, torch, lsa, W):
     for r in range(nrep):
         k = w.k if r == 0 else w.k.clone()
         v = w.v if r == 0 else w.v.clone()
-        kv = lsa.KVPool(w.dtype, k, v, Hkv, D, NP, w.logical_page, w.num_pages)
+        k_sz = w.k_sz if (r == 0 or w.k_sz is None) else w.k_sz.clone()
+        v_sz = w.v_sz if (r == 0 or w.v_sz is None) else w.v_sz.clone()
+        kv = lsa.KVPool(w.dtype, k, v, Hkv, D, NP, w.logical_page, w.num_pages, k_sz=k_sz, v_sz=v_sz)
         stats = torch.zeros(lsa.page_stats_bytes(kv), dtype=torch.uint8, device=dev)
         lens0 = torch.tensor(w.ctx, dtype=torch.int32, device=dev)
         lsa.build_page_stats(kv, w.page_table, lens0, stats, heads=hd)
@@ -303,8 +311,11 @@ def bench_decode(args, torch, lsa, W):
 
     # algorithmic bytes of one attention launch: the attended keys and values
     # of every (sequence, KV head) at the measured window steps, plus q and o
+    # (bytes per K or V element: 2 for bf16, 4 for f32, half a byte for int4
+    # codes, whose pages also carry one fp16 (scale, zero) pair each for K and V)
+    eb = {W.F32: 4, W.BF16: 2, W.INT4: 0.5}[w.dtype]
     sel_h = [layers[0][2].cpu()]
-    att_tokens = 0
+    att_tokens = att_pages = 0
     for s in range(R):
         for b in range(B):
             t = w.ctx[b] + s
@@ -313,15 +324,23 @@ def bench_decode(args, torch, lsa, W):
                     pages = set(int(m) for m in sel_h[0][b, kvh].tolist() if m >= 0)
                     pages.add(t // NP)
                     att_tokens += sum(min(NP, t + 1 - m * NP) for m in pages)
+                    att_pages += len(pages)
                 else:
+                    lo = max(0, t + 1 - w.local_tokens)
                     att_tokens += min(t + 1, w.sink_tokens + w.local_tokens)
+                    att_pages += len({p // NP for p in range(min(w.sink_tokens, t + 1))} |
+                                     set(range(lo // NP, t // NP + 1)))
     att_tokens /= R
-    kv_bytes = att_tokens * D * 2 * 2
+    att_pages /= R
+    kv_bytes = att_tokens * D * eb * 2 + (att_pages * 2 * 4 if w.dtype == W.INT4 else 0)
     qo_bytes = 2 * B * Hq * D * 2
     launch_bytes = kv_bytes + qo_bytes
-    # whole step: + statistics refresh + selection amortised over R
+    # whole step: + statistics refresh + selection amortised over R (the
+    # statistics of every logical page of each retrieval head; int4 codes are
+    # one byte per channel plus the page's (scale, zero))
     n_ret = sum(1 for x in w.head_kind if x == 0)
-    sel_bytes = B * n_ret * (w.ctx[0] + 1 + w.logical_page - 1) // w.logical_page * 2 * D * 2 / R
+    lp_bytes = D + 4 / (NP // w.logical_page) if w.dtype == W.INT4 else 2 * D * eb
+    sel_bytes = n_ret * sum(-(-(c + 1) // w.logical_page) for c in w.ctx) * lp_bytes / R
     step_bytes = launch_bytes + sel_bytes
     tok_s = B * steps / elapsed
     src = os.path.join(ROOT, "block_sparse_attention_logical_amd", "csrc", "decode.hip")
@@ -469,6 +488,8 @@ def main():
     from block_sparse_attention_logical_amd import lsa, workloads as W
     torch.cuda.set_device(0)
     lsa.load()
+    if args.replicas is None:
+        args.replicas = WORKLOADS[args.workload][3]
 
     if args.counters:
         counters_run(args, torch, lsa, W)
@@ -509,13 +530,15 @@ def main():
         "dtype": "bf16",
         "data": f"synthetic (seeded; shapes of the LServe {model.split('-shaped')[0]} decode workload)",
         "config": {
-            "workload": f"decode, one {model}: B={w.batch}, context {w.ctx[0]}, {w.num_q_heads} q heads / "
+            "workload": f"decode, one {model}: B={w.batch}, context "
+                        f"{w.ctx[0] if min(w.ctx) == max(w.ctx) else f'{min(w.ctx)}-{max(w.ctx)}'}, "
+                        f"{'int4 KV, ' if w.dtype == W.INT4 else ''}{w.num_q_heads} q heads / "
                         f"{w.num_kv_heads} KV heads ({n_str} streaming: sink {w.sink_tokens} + local "
                         f"{w.local_tokens} tokens), D={w.head_dim}, N_L={w.logical_page}, N_P={w.page_size}, "
                         f"token budget {w.token_budget}, reuse interval {w.reuse_interval}, group page scores "
                         f"combined by {args.aggregation}; one step = selection (every {w.reuse_interval}th step) "
                         f"+ attention with the stats refresh",
-            "global_batch": w.batch, "seq_len": w.ctx[0], "parallelism": "none (1 GPU)",
+            "global_batch": w.batch, "seq_len": max(w.ctx), "parallelism": "none (1 GPU)",
             "kv_replicas": args.replicas, "timing": dec["timing"],
         },
         "decode_hbm_gbps": round(dec["step_bytes"] / (dec["ms_per_step"] / 1e3) / 1e9, 1),
