@@ -44,7 +44,12 @@ struct ScoreShape {
 };
 
 constexpr int kScoreThreads = 256;
-constexpr int kScoreMaxIter = 8;           // logical pages per lane group and workgroup
+// logical pages per lane group and workgroup.  An int4 lane holds 16
+// channels of fp64 query terms; six pages in flight instead of eight leave
+// room for a third wavefront per SIMD (162 against 174 VGPRs), which hides the
+// statistics loads behind another wavefront's arithmetic (config 5: 102 ->
+// 90 us per score launch; four pages gave no further gain)
+constexpr int score_iters(int kv_dtype) { return kv_dtype == LSA_INT4 ? 6 : 8; }
 constexpr int kMaxLogicalPerBlock = 1024;  // LDS slots for logical scores
 
 // Qp / Qn of this lane's channels over the group's query heads h0 .. h1-1, fp64.
@@ -331,7 +336,7 @@ __global__ __launch_bounds__(kScoreThreads) void score_kernel(ScoreArgs a) {
     using S = ScoreShape<EB, D>;
     constexpr int C = S::C, LPL = S::LPL, LPP = S::LPP;
     constexpr int GROUPS = (kScoreThreads / kWave) * LPP;   // lane groups per workgroup
-    constexpr int IT = kScoreMaxIter;
+    constexpr int IT = score_iters(KV_DT);
     __shared__ double s_log[kMaxLogicalPerBlock];
 
     const int blk = blockIdx.x % a.blocks_per_head;
@@ -550,7 +555,7 @@ int score_pages_per_block(int kv_dtype, int head_dim, int page_size, int logical
     const int lpl = head_dim / (16 / eb);
     const int groups = (kScoreThreads / kWave) * (kWave / lpl);
     const int g = page_size / logical_page;
-    int ppb = groups * kScoreMaxIter / g;
+    int ppb = groups * score_iters(kv_dtype) / g;
     ppb = ppb < 1 ? 1 : ppb;
     return ppb * g > kMaxLogicalPerBlock ? kMaxLogicalPerBlock / g : ppb;
 }
