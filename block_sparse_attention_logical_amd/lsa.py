@@ -225,6 +225,7 @@ def build_page_stats(kv: KVPool, page_table: torch.Tensor, seq_lens: torch.Tenso
 
 
 def select_pages_workspace(kv: KVPool, page_table: torch.Tensor, seq_lens: torch.Tensor, heads: Heads) -> int:
+    """Bytes of the select_pages workspace (lsa_select_pages_workspace)."""
     out = ctypes.c_size_t(0)
     _check(load().lsa_select_pages_workspace(ctypes.byref(kv.desc()), ctypes.byref(seqs_desc(page_table, seq_lens)),
                                              ctypes.byref(heads.desc()), ctypes.byref(out)))
@@ -234,6 +235,10 @@ def select_pages_workspace(kv: KVPool, page_table: torch.Tensor, seq_lens: torch
 def select_pages(q: torch.Tensor, kv: KVPool, stats: torch.Tensor, page_table: torch.Tensor,
                  seq_lens: torch.Tensor, heads: Heads, token_budget: int, decode_step: int,
                  reuse_interval: int, selected: torch.Tensor, workspace: torch.Tensor, stream=None) -> None:
+    """lsa_select_pages: writes selected[B][H_kv][K] when decode_step % reuse_interval == 0.
+    The workspace (uint8, select_pages_workspace bytes) must be zero-filled before its first use
+    (it starts with arrival counters that every completed call leaves at zero); calls that share
+    a workspace must not overlap."""
     _check(load().lsa_select_pages(_ptr(q), dtype_code(q), ctypes.byref(kv.desc()), _ptr(stats),
                                    ctypes.byref(seqs_desc(page_table, seq_lens)), ctypes.byref(heads.desc()),
                                    token_budget, decode_step, reuse_interval, _ptr(selected), _ptr(workspace),
@@ -242,6 +247,7 @@ def select_pages(q: torch.Tensor, kv: KVPool, stats: torch.Tensor, page_table: t
 
 def decode_workspace(kv: KVPool, page_table: torch.Tensor, seq_lens: torch.Tensor, heads: Heads,
                      token_budget: int) -> int:
+    """Bytes of the sparse_decode_attn workspace (lsa_decode_workspace)."""
     out = ctypes.c_size_t(0)
     _check(load().lsa_decode_workspace(ctypes.byref(kv.desc()), ctypes.byref(seqs_desc(page_table, seq_lens)),
                                        ctypes.byref(heads.desc()), token_budget, ctypes.byref(out)))
@@ -252,6 +258,11 @@ def sparse_decode_attn(q: torch.Tensor, kv: KVPool, page_table: torch.Tensor, se
                        heads: Heads, selected: Optional[torch.Tensor], token_budget: int, out: torch.Tensor,
                        workspace: torch.Tensor, softmax_scale: float = 0.0, stats: Optional[torch.Tensor] = None,
                        stream=None) -> None:
+    """lsa_sparse_decode_attn: out[B][H_q][D] for the current token of every sequence.  The
+    workspace (uint8, decode_workspace bytes) must be zero-filled before its first use (arrival
+    counters, left at zero by every completed call); calls that share it must not overlap.
+    With stats given, the statistics of the logical page holding the current token are
+    refreshed in the same launch."""
     _check(load().lsa_sparse_decode_attn(_ptr(q), dtype_code(q), ctypes.byref(kv.desc()),
                                          ctypes.byref(seqs_desc(page_table, seq_lens)), ctypes.byref(heads.desc()),
                                          _ptr(selected), token_budget, softmax_scale, _ptr(out), _ptr(stats),
