@@ -48,8 +48,10 @@ constexpr int kScoreThreads = 256;
 // channels of fp64 query terms; six pages in flight instead of eight leave
 // room for a third wavefront per SIMD (162 against 174 VGPRs), which hides the
 // statistics loads behind another wavefront's arithmetic (config 5: 102 ->
-// 90 us per score launch; four pages gave no further gain)
-constexpr int score_iters(int kv_dtype) { return kv_dtype == LSA_INT4 ? 6 : 8; }
+// 90 us per score launch; four pages gave no further gain).  bf16 takes ten
+// (160 VGPRs, still three wavefronts per SIMD): fewer, fuller workgroups
+// (config 2: 29.1 -> 28.4 us per score launch).
+constexpr int score_iters(int kv_dtype) { return kv_dtype == LSA_INT4 ? 6 : kv_dtype == LSA_BF16 ? 10 : 8; }
 constexpr int kMaxLogicalPerBlock = 1024;  // LDS slots for logical scores
 
 // Qp / Qn of this lane's channels over the group's query heads h0 .. h1-1, fp64.
