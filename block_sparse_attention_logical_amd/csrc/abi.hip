@@ -437,6 +437,15 @@ lsa_status lsa_sparse_prefill_attn_csr(const void *q, int32_t q_dtype, const lsa
     if (empty) return ok();
     // every KV head follows its own rows of the mask; work items are ordered like retrieval heads
     for (int i = 0; i < kv->num_kv_heads; ++i) p.ret_heads[p.n_ret++] = (uint8_t)i;
+    // bf16 with one or two query heads per KV head: a work item takes 4 / G
+    // query tiles and walks the union of their rows.  A work order then
+    // starts with one code per group of query tiles (block_mask_schedule puts
+    // them first), and only those leading entries are read.
+    if (q_dtype == LSA_BF16 && mask_q_tiles(p.group, p.n_qblocks) > 1) {
+        p.q_tiles = mask_q_tiles(p.group, p.n_qblocks);
+        p.n_qgroups = (p.n_qblocks + p.q_tiles - 1) / p.q_tiles;
+        p.n_items = kv->num_kv_heads * p.n_qgroups * p.head_groups;
+    }
     p.row_ptr = row_ptr;
     p.col_idx = col_idx;
     p.nnz = nnz;
@@ -452,23 +461,38 @@ lsa_status lsa_block_mask_schedule(const int32_t *row_ptr, int32_t num_kv_heads,
                     seq_len);
     if (!row_ptr || !order) return fail(LSA_ERR_INVALID_ARG, "row_ptr and order must be non-NULL");
     const int n = (seq_len + 63) / 64;
-    const int hg = (num_q_heads / num_kv_heads + 3) / 4;
-    std::vector<std::pair<long long, int>> items;       // (sort key, item code)
-    items.reserve((size_t)num_kv_heads * n * hg);
-    for (int h = 0; h < num_kv_heads; ++h)
+    const int G = num_q_heads / num_kv_heads;
+    const int hg = (G + 3) / 4;
+    // With query-tile groups (bf16, G <= 2) a work item covers QT tiles
+    // n-1-QT*j-QT+1 .. n-1-QT*j; its cost follows the longest row of the
+    // group.  The group's highest tile leads: leaders come first, then the
+    // other codes, each part longest first, so a kernel that reads one code
+    // per group and one that reads every code both find a balanced order.
+    const int QT = mask_q_tiles(G, n);
+    std::vector<std::pair<long long, int>> lead, rest;  // (sort key, item code)
+    lead.reserve((size_t)num_kv_heads * n * hg);
+    for (int h = 0; h < num_kv_heads; ++h) {
+        const int32_t *rp = row_ptr + (size_t)h * (n + 1);
         for (int a = 0; a < n; ++a) {
-            const long long len = (long long)row_ptr[(size_t)h * (n + 1) + a + 1] - row_ptr[(size_t)h * (n + 1) + a];
+            const bool leader = (n - 1 - a) % QT == 0;
+            long long len = (long long)rp[a + 1] - rp[a];
+            if (leader)
+                for (int s = 1; s < QT && a - s >= 0; ++s) len = std::max(len, (long long)rp[a - s + 1] - rp[a - s]);
             for (int g = 0; g < hg; ++g) {
                 const int code = (h * n + a) * hg + g;
-                // longest rows first; among equal lengths, later query tiles first, then the code
-                items.push_back({-(len * ((long long)n + 1) + a), code});
+                // longest first; among equal lengths, later query tiles first, then the code
+                (leader ? lead : rest).push_back({-(len * ((long long)n + 1) + a), code});
             }
         }
-    std::stable_sort(items.begin(), items.end(),
-                     [](const std::pair<long long, int> &x, const std::pair<long long, int> &y) {
-                         return x.first < y.first;
-                     });
-    for (size_t i = 0; i < items.size(); ++i) order[i] = items[i].second;
+    }
+    const auto by_key = [](const std::pair<long long, int> &x, const std::pair<long long, int> &y) {
+        return x.first < y.first;
+    };
+    std::stable_sort(lead.begin(), lead.end(), by_key);
+    std::stable_sort(rest.begin(), rest.end(), by_key);
+    size_t i = 0;
+    for (const auto &e : lead) order[i++] = e.second;
+    for (const auto &e : rest) order[i++] = e.second;
     return ok();
 }
 

@@ -20,6 +20,14 @@ constexpr int kMaxDecodeChunks = 128;   // split-KV chunks per (sequence, KV hea
 constexpr int kDecodeWaves = 4;
 constexpr int kMaxChunkPages = 16;
 constexpr int kDecodeWaveTokens = 128;
+// Static-mask prefill with several query tiles per workgroup builds the union
+// of their rows in LDS: rows of up to this many 64-token tiles
+constexpr int kPrefillMaxUnionTiles = 4096;
+// Query tiles per static-mask work item in the bf16 kernel: four wavefront
+// pairs cover G query heads x (4 / G) query tiles when G is 1 or 2.
+__host__ __device__ constexpr int mask_q_tiles(int group, int n_qblocks) {
+    return group <= 2 && n_qblocks <= kPrefillMaxUnionTiles ? 4 / group : 1;
+}
 __host__ __device__ constexpr int decode_pages_per_wave(int kv_dtype, int page_size) {
     return kv_dtype == LSA_F32 || page_size >= kDecodeWaveTokens ? 1 : kDecodeWaveTokens / page_size;
 }

@@ -55,11 +55,16 @@ __device__ __forceinline__ PItem prefill_item(const PrefillArgs &p) {
     const int nq = p.n_qblocks, HG = p.head_groups, NG = p.n_qgroups;
     int i = blockIdx.x;
     if (CSR && p.order) {
-        const int code = min(max(p.order[i], 0), p.n_items - 1);
+        // one code per (KV head, query tile, head group); with QT > 1 a code
+        // stands for the group of QT query tiles that holds its tile, and the
+        // grid reads only the leading entries, which the schedule fills with
+        // one code per group
+        const int code = min(max(p.order[i], 0), p.n_ret * nq * HG - 1);
         it.hg = code % HG;
         it.a = (code / HG) % nq;
         it.kv = code / (HG * nq);
         it.streaming = false;
+        if (QT > 1) it.a = nq - 1 - ((nq - 1 - it.a) / QT) * QT;
         return it;
     }
     // it.a is the highest query tile of the item (its QT tiles are it.a - QT + 1 .. it.a)
@@ -92,7 +97,9 @@ struct TileRow {
 template <bool CSR, int QT>
 __device__ __forceinline__ TileRow tile_row(const PrefillArgs &p, const PItem &it) {
     TileRow r{0, 0, 0, 0};
-    if constexpr (CSR) {
+    if constexpr (CSR && QT > 1) {
+        return r;                                 // the union of the item's rows is built in LDS
+    } else if constexpr (CSR) {
         const int32_t *rp = p.row_ptr + (size_t)it.kv * (p.n_qblocks + 1) + it.a;
         const int b0 = min(max(rp[0], 0), p.nnz);
         const int b1 = min(max(rp[1], b0), p.nnz);
@@ -175,12 +182,69 @@ __global__ __launch_bounds__(512, 2) void prefill_bf16_kernel(PrefillArgs p) {
     const bool head_ok = QT == 1 ? hq_local < G : a_s >= 0;
     const int hq = it.kv * G + min(hq_local, G - 1);
     const int q0 = max(a_s, 0) * kTile + 32 * (wave & 1);   // first query row of this wave
-    // does this pair's query tile see key tile c (QT > 1: the item walks a union)
-    auto sees = [&](int c) {
-        return c <= a_s && (!it.streaming || c < p.sink_blocks || a_s - c < p.local_blocks);
+    // A static mask with QT > 1: the item walks the union of its query tiles'
+    // rows.  Each row marks its tiles in a bitmap of its own; the union is
+    // then compacted in ascending order into u_list, each entry the tile in
+    // bits 0..23 and, in bits 24..27, which of the QT query tiles list it.
+    // Elsewhere an entry is just the tile.
+    constexpr bool kUnion = CSR && QT > 1;
+    int n_union = 0;
+    int *u_list = nullptr;
+    if constexpr (kUnion) {
+        __shared__ int u_entries[kPrefillMaxUnionTiles];
+        __shared__ uint32_t u_bits[QT][kPrefillMaxUnionTiles / 32];
+        __shared__ uint32_t u_wtot[NT / kWave];
+        u_list = u_entries;
+        const int words = (it.a + 32) / 32;                  // tiles 0 .. it.a
+        for (int e = tid; e < QT * words; e += NT) u_bits[e / words][e % words] = 0;
+        __syncthreads();
+#pragma unroll
+        for (int si = 0; si < QT; ++si) {
+            const int ar = it.a - si;
+            if (ar < 0) break;
+            const int32_t *rp = p.row_ptr + (size_t)it.kv * (p.n_qblocks + 1) + ar;
+            const int b0 = min(max(rp[0], 0), p.nnz);
+            const int b1 = min(max(rp[1], b0), p.nnz);
+            for (int e = b0 + tid; e < b1; e += NT) {
+                const int c = min(max(p.col_idx[e], 0), ar);
+                atomicOr(&u_bits[si][c >> 5], 1u << (c & 31));
+            }
+        }
+        __syncthreads();
+        uint32_t uw = 0, cnt = 0;
+        if (tid < words) {
+#pragma unroll
+            for (int si = 0; si < QT; ++si) uw |= u_bits[si][tid];
+            cnt = __popc(uw);
+        }
+        const uint32_t incl = wave_inclusive_scan(cnt);
+        if (lane == kWave - 1) u_wtot[wave] = incl;
+        __syncthreads();
+        uint32_t off = incl - cnt, total = 0;
+#pragma unroll
+        for (int w2 = 0; w2 < NT / kWave; ++w2) {
+            off += w2 < wave ? u_wtot[w2] : 0;
+            total += u_wtot[w2];
+        }
+        while (uw) {
+            const int bit = __builtin_ctz(uw);
+            uw &= uw - 1;
+            uint32_t mem = 0;
+#pragma unroll
+            for (int si = 0; si < QT; ++si) mem |= ((u_bits[si][tid] >> bit) & 1u) << si;
+            u_list[off++] = (32 * tid + bit) | (int)(mem << 24);
+        }
+        n_union = (int)total;
+        __syncthreads();
+    }
+    auto tile_id = [&](int v) { return kUnion ? (v & 0xFFFFFF) : v; };
+    // does this pair's query tile see key tile entry v (QT > 1: the item walks a union)
+    auto sees = [&](int v) {
+        if constexpr (kUnion) return ((v >> (24 + slot / GQ)) & 1) != 0;
+        return v <= a_s && (!it.streaming || v < p.sink_blocks || a_s - v < p.local_blocks);
     };
     const int col = lane & 31, lg = lane >> 5;      // MFMA column / lane group
-    const int n_iter = trow.n;
+    const int n_iter = kUnion ? n_union : trow.n;
     if (n_iter == 0) {                              // a query tile without key tiles: zero output
         const int row = q0 + col;
         if (!head_ok || row >= T) return;
@@ -218,7 +282,9 @@ __global__ __launch_bounds__(512, 2) void prefill_bf16_kernel(PrefillArgs p) {
     const int32_t __attribute__((address_space(4))) *cidx =
         (const int32_t __attribute__((address_space(4))) *)p.col_idx + trow.rp0;
     auto tile_of = [&](int ii) {
-        if constexpr (CSR) {
+        if constexpr (kUnion) {
+            return __builtin_amdgcn_readfirstlane(u_list[ii]);
+        } else if constexpr (CSR) {
             return min(max((int)cidx[ii], 0), it.a);
         } else {
             return row_tile<false>(p, it, trow, ii);
@@ -359,10 +425,10 @@ __global__ __launch_bounds__(512, 2) void prefill_bf16_kernel(PrefillArgs p) {
     // prologue: K(0), V(0) and K(1) in LDS.  The key tiles of steps ii - 1,
     // ii and ii + 1 travel from step to step: a step looks up only tile ii + 2.
     int c_prev = tile_of(0), c_cur = c_prev, c_n1 = clamp_tile(1);
-    size_t base_next = tile_base(c_cur);             // pool offset of the tile whose V is fetched next
+    size_t base_next = tile_base(tile_id(c_cur));    // pool offset of the tile whose V is fetched next
     fetch(kpool, k_lds0, base_next);
     fetch(vpool, v_lds0, base_next);
-    base_next = tile_base(c_n1);
+    base_next = tile_base(tile_id(c_n1));
     fetch(kpool, k_lds1, base_next);
     __builtin_amdgcn_s_waitcnt(kWaitVm0);
     __syncthreads();
@@ -390,7 +456,7 @@ __global__ __launch_bounds__(512, 2) void prefill_bf16_kernel(PrefillArgs p) {
         // K(ii+2) and V(ii+1) land during the step, in buffers last read two
         // steps ago; the V tile's pool offset is the one its K fetch used
         const int c_n2 = clamp_tile(ii + 2);
-        const size_t base_k = tile_base(c_n2);
+        const size_t base_k = tile_base(tile_id(c_n2));
         fetch(kpool, kbuf(Next2{}), base_k);
         fetch(vpool, vbuf(Next1{}), base_next);
         base_next = base_k;
@@ -400,7 +466,7 @@ __global__ __launch_bounds__(512, 2) void prefill_bf16_kernel(PrefillArgs p) {
         const bool prev_ok = (B != 0 || ii > 0) && (QT == 1 ? head_ok : sees(c_prev));
         const bool cur_ok = QT == 1 ? head_ok : sees(c_cur);
         bf16x8 pb[4];
-        if (prev_ok) softmax_p(s_prev, c_prev * kTile, QT > 1 && c_prev == a_s, pb);
+        if (prev_ok) softmax_p(s_prev, tile_id(c_prev) * kTile, QT > 1 && tile_id(c_prev) == a_s, pb);
         bar();
         if (prev_ok) pv(vbuf(Prev{}), pb);
         if (cur_ok) qk(kbuf(b), s_cur);
@@ -431,13 +497,13 @@ __global__ __launch_bounds__(512, 2) void prefill_bf16_kernel(PrefillArgs p) {
     uint16_t *vl_last = lb == 0 ? v_lds0 : lb == 1 ? v_lds1 : lb == 2 ? v_lds2 : v_lds3;
     __builtin_amdgcn_s_waitcnt(kWaitVm0);            // no fetch lands after this point
     __syncthreads();
-    zero_v_tail(vl_last, c_last * kTile);
+    zero_v_tail(vl_last, tile_id(c_last) * kTile);
     __syncthreads();
     if (head_ok && (QT == 1 || sees(c_last))) {
-        const bool diag = QT == 1 || c_last == a_s;
+        const bool diag = QT == 1 || tile_id(c_last) == a_s;
         bf16x8 pb[4];
-        if ((n_iter - 1) & 1) softmax_p(sb, c_last * kTile, diag, pb);
-        else softmax_p(sa, c_last * kTile, diag, pb);
+        if ((n_iter - 1) & 1) softmax_p(sb, tile_id(c_last) * kTile, diag, pb);
+        else softmax_p(sa, tile_id(c_last) * kTile, diag, pb);
         pv(vl_last, pb);
     }
 
@@ -449,15 +515,21 @@ __global__ __launch_bounds__(512, 2) void prefill_bf16_kernel(PrefillArgs p) {
             }
         } else if (head_ok && (wave & 1) == 0 && lane == 0) {
             // the tiles this pair's query tile sees
-            const int e0s = it.streaming ? min(p.sink_blocks, a_s + 1) : 0;
-            const int s1s = it.streaming ? max(a_s - p.local_blocks + 1, e0s) : 0;
-            atomicAdd(p.tile_counter, (unsigned long long)(e0s + (a_s - s1s + 1)));
+            if constexpr (kUnion) {
+                const int32_t *rp = p.row_ptr + (size_t)it.kv * (p.n_qblocks + 1) + a_s;
+                const int b0 = min(max(rp[0], 0), p.nnz);
+                atomicAdd(p.tile_counter, (unsigned long long)(min(max(rp[1], b0), p.nnz) - b0));
+            } else {
+                const int e0s = it.streaming ? min(p.sink_blocks, a_s + 1) : 0;
+                const int s1s = it.streaming ? max(a_s - p.local_blocks + 1, e0s) : 0;
+                atomicAdd(p.tile_counter, (unsigned long long)(e0s + (a_s - s1s + 1)));
+            }
         }
     }
     if (!head_ok) return;
     // ---- normalise and store: lane holds query q0 + col, channels 32*dt + 8*(r/4) + 4*lg + r%4
     const float lt = sum_xor32(l_run);
-    const float inv = 1.f / lt;
+    const float inv = lt > 0.f ? 1.f / lt : 0.f;    // a query tile whose own row is empty: zero output
     const int row = q0 + col;
     if (row >= T) return;
     uint16_t *orow = static_cast<uint16_t *>(p.out) + ((size_t)row * HQ + hq) * D;
@@ -561,9 +633,9 @@ __global__ __launch_bounds__(256) void prefill_f32_kernel(PrefillArgs p) {
 
 template <int D, bool CSR>
 void launch_bf16(const PrefillArgs &p, dim3 grid, hipStream_t s) {
-    if (CSR || p.q_tiles == 1) hipLaunchKernelGGL((prefill_bf16_kernel<D, CSR, 1>), grid, dim3(512), 0, s, p);
-    else if (p.q_tiles == 2) hipLaunchKernelGGL((prefill_bf16_kernel<D, false, 2>), grid, dim3(512), 0, s, p);
-    else hipLaunchKernelGGL((prefill_bf16_kernel<D, false, 4>), grid, dim3(512), 0, s, p);
+    if (p.q_tiles == 1) hipLaunchKernelGGL((prefill_bf16_kernel<D, CSR, 1>), grid, dim3(512), 0, s, p);
+    else if (p.q_tiles == 2) hipLaunchKernelGGL((prefill_bf16_kernel<D, CSR, 2>), grid, dim3(512), 0, s, p);
+    else hipLaunchKernelGGL((prefill_bf16_kernel<D, CSR, 4>), grid, dim3(512), 0, s, p);
 }
 
 template <bool CSR>

@@ -276,11 +276,16 @@ lsa_status lsa_sparse_prefill_attn(const void *q, int32_t q_dtype, const lsa_kv 
  * with an empty row gets zero output.  The query heads of a KV head share its
  * rows.  q, out, page_table, dtypes, softmax_scale and tile_counter are as for
  * lsa_sparse_prefill_attn (the counter adds (row length) x G per row).
+ * With bf16 q and G <= 2 (and n <= 4096) one workgroup takes QT = 4 / G
+ * query tiles n-1-QT*j-QT+1 .. n-1-QT*j and walks the union of their rows.
  * order: NULL, or [device] int32 [num_kv_heads * n * ceil(G / 4)], the work
- * order written by lsa_block_mask_schedule for this mask (entries are clamped
- * to the item range).  Workgroups start in this order, round robin over the
- * XCDs, so rows of equal length side by side keep every XCD busy; a mask whose
- * rows differ in length runs up to twice as fast with it. */
+ * order written by lsa_block_mask_schedule for this mask and these head
+ * counts (entries are clamped to the item range).  Workgroups start in this
+ * order, round robin over the XCDs, so rows of equal length side by side keep
+ * every XCD busy; a mask whose rows differ in length runs up to twice as fast
+ * with it.  Where QT > 1 only the first num_kv_heads * ceil(n / QT) entries
+ * are read, each standing for the group of query tiles that holds its tile;
+ * another permutation than the schedule's may then leave groups out. */
 lsa_status lsa_sparse_prefill_attn_csr(const void *q, int32_t q_dtype, const lsa_kv *kv,
                                        const int32_t *page_table, int32_t seq_len,
                                        int32_t num_q_heads, int32_t block,
@@ -292,7 +297,10 @@ lsa_status lsa_sparse_prefill_attn_csr(const void *q, int32_t q_dtype, const lsa
  * once per mask on the host: row_ptr is a [host] copy ([num_kv_heads][n + 1]);
  * order ([host] out, num_kv_heads * n * ceil(G / 4) int32) receives every work
  * item (kv * n + a) * ceil(G / 4) + g once, longest rows first, then later
- * query tiles first. */
+ * query tiles first.  At G <= 2 (n <= 4096) the codes of each query-tile
+ * group's highest tile come first, ranked by the longest row of the group,
+ * then the other codes, so the same order serves the bf16 kernel (which
+ * reads one code per group) and the f32 kernel (which reads them all). */
 lsa_status lsa_block_mask_schedule(const int32_t *row_ptr, int32_t num_kv_heads,
                                    int32_t num_q_heads, int32_t seq_len, int32_t block,
                                    int32_t *order);

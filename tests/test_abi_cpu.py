@@ -244,8 +244,11 @@ def test_check_block_mask():
 
 def test_block_mask_schedule():
     """The work order of a mask lists every (KV head, query tile, head group)
-    item once, rows in non-increasing length."""
-    for H, G, n in ((8, 4, 13), (4, 8, 9), (32, 1, 5)):
+    item once.  At group sizes above 2 rows come in non-increasing length; at
+    1 and 2, where a bf16 work item takes 4 / G query tiles
+    n-1-QT*j-QT+1 .. n-1-QT*j, each group's highest tile comes first, ordered
+    by the longest row of its group, then every other code by its own row."""
+    for H, G, n in ((8, 4, 13), (4, 8, 9), (32, 1, 5), (4, 1, 11), (8, 2, 7)):
         m = W.random_tile_masks(H, n, 0.35, seed=H * n)
         m[0, 2] = False                                          # an empty row
         rp, _ = W.csr_from_tile_masks(m)
@@ -253,8 +256,17 @@ def test_block_mask_schedule():
         hg = -(-G // 4)
         assert sorted(order.tolist()) == list(range(H * n * hg))
         lens = (rp[:, 1:] - rp[:, :-1]).reshape(-1)             # [H * n], row (kv, a) at kv * n + a
-        row_len = [int(lens[int(c) // hg]) for c in order]
-        assert all(x >= y for x, y in zip(row_len, row_len[1:]))
+        qt = 4 // G if G <= 2 else 1
+        is_lead = [(n - 1 - (int(c) // hg) % n) % qt == 0 for c in order]
+        n_lead = H * (-(-n // qt)) * hg
+        assert all(is_lead[:n_lead]) and not any(is_lead[n_lead:])
+
+        def group_len(c):
+            kv, a = divmod(int(c) // hg, n)
+            return max(int(lens[kv * n + a - s]) for s in range(qt) if a - s >= 0)
+        key = [group_len(c) for c in order[:n_lead]] + [int(lens[int(c) // hg]) for c in order[n_lead:]]
+        for part in (key[:n_lead], key[n_lead:]):
+            assert all(x >= y for x, y in zip(part, part[1:]))
     with pytest.raises(lsa.LsaError):
         lsa.block_mask_schedule(rp, 32, 31, 5 * 64)
 

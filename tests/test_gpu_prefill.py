@@ -205,13 +205,18 @@ def check_mask(p, out, masks, heads=None, rows=None, tol=2e-2):
     return worst
 
 
-@pytest.mark.parametrize("cfg,T,heads,scheduled", [(1, 1024, None, True), (3, 777, [0, 5, 13, 22, 31], True),
-                                                   (3, 1088, [2, 9, 27], False), (7, 777, [0, 1, 14, 31], True)])
-def test_prefill_csr_random_masks(cfg, T, heads, scheduled):
+@pytest.mark.parametrize("cfg,T,heads,scheduled,H_kv", [(1, 1024, None, True, None), (3, 777, [0, 5, 13, 22, 31], True, None),
+                                                        (3, 1088, [2, 9, 27], False, None),
+                                                        (7, 777, [0, 1, 14, 31], True, None),
+                                                        (7, 1088, [0, 3, 30, 31], False, None),
+                                                        (3, 900, [0, 1, 6, 29, 30, 31], True, 16),
+                                                        (3, 700, [0, 1, 17, 31], False, 16)])
+def test_prefill_csr_random_masks(cfg, T, heads, scheduled, H_kv):
     """Random static masks (30% of the tiles below the diagonal, the diagonal
     kept except in one head, so some query tiles have no key tiles), with and
-    without the mask's work order."""
-    p = W.make_prefill(cfg, DEV, seq_len=T)
+    without the mask's work order; at group sizes 1 and 2 a workgroup walks the
+    union of 4 / G query tiles' rows."""
+    p = W.make_prefill(cfg, DEV, seq_len=T, num_kv_heads=H_kv)
     n = -(-T // 64)
     masks = W.random_tile_masks(p.num_kv_heads, n, 0.3, seed=cfg * 1000 + T)
     masks[-1] = W.random_tile_masks(1, n, 0.3, seed=T, diagonal=False)[0]
@@ -254,18 +259,21 @@ def test_prefill_csr_kind_masks_equal_analytic():
                            b.view(torch.int16) if b.dtype == torch.bfloat16 else b.view(torch.int32)), cfg
 
 
-def test_prefill_csr_full_size_cfg3():
-    """Config 3 at full size with its head-kind patterns given as CSR lists
-    (2.1 million tiles per causal head): the counter gives 34,125,696, and the
-    outputs equal the head-kind call bitwise."""
-    p = W.make_prefill(3, DEV)
+@pytest.mark.parametrize("cfg", [3, 7])
+def test_prefill_csr_full_size(cfg):
+    """Full-size prefill (T = 131072) with its head-kind patterns given as CSR
+    lists and the mask's work order (config 3: GQA 4; config 7: MHA, where a
+    workgroup walks the union of four query tiles' rows): the counter gives
+    34,125,696 as for the head-kind call, and the outputs equal that call's
+    bitwise."""
+    p = W.make_prefill(cfg, DEV)
     n = -(-p.seq_len // 64)
     masks = torch.stack([torch.from_numpy(O.kind_tile_mask(n, p.head_kind[kv], p.sink_blocks, p.local_blocks))
                          for kv in range(p.num_kv_heads)])
     b, cb = run_prefill_csr(p, masks)
     del masks
-    assert cb == 34125696
     a, ca = run_prefill(p)
+    assert cb == ca == 34125696
     assert torch.equal(a.view(torch.int16), b.view(torch.int16))
     del a, b, p
     torch.cuda.empty_cache()
