@@ -259,6 +259,28 @@ def test_prefill_csr_kind_masks_equal_analytic():
                            b.view(torch.int16) if b.dtype == torch.bfloat16 else b.view(torch.int32)), cfg
 
 
+@pytest.mark.parametrize("n,H_q", [(4096, 4), (4097, 4), (4096, 8)])
+def test_prefill_csr_either_side_of_union_limit(n, H_q):
+    """At group sizes 1 and 2 a bf16 workgroup walks the union of 4 / G query
+    tiles' rows for up to 4096 tiles (the LDS tile list full at n = 4096) and
+    takes one query tile past it (n = 4097).  With causal and Lambda heads
+    given as CSR lists and the mask's work order, the counter and the outputs
+    equal the head-kind call's bitwise, and sampled rows of a causal head
+    match the oracle."""
+    T = 64 * n - 5
+    p = W.make_prefill(7, DEV, seq_len=T, num_q_heads=H_q, num_kv_heads=4, head_kind=[0, 1, 1, 0])
+    masks = torch.stack([torch.from_numpy(O.kind_tile_mask(n, p.head_kind[kv], p.sink_blocks, p.local_blocks))
+                         for kv in range(p.num_kv_heads)])
+    b, cb = run_prefill_csr(p, masks)
+    del masks
+    a, ca = run_prefill(p)
+    assert cb == ca == expected_tiles(p)
+    assert torch.equal(a.view(torch.int16), b.view(torch.int16))
+    print("max abs err", check(p, b, rows=[0, 64 * 4095 + 3, T - 1], heads=[H_q - 1]))
+    del a, b, p
+    torch.cuda.empty_cache()
+
+
 @pytest.mark.parametrize("cfg", [3, 7])
 def test_prefill_csr_full_size(cfg):
     """Full-size prefill (T = 131072) with its head-kind patterns given as CSR
