@@ -48,10 +48,16 @@ constexpr int kScoreThreads = 256;
 // channels of fp64 query terms; six pages in flight instead of eight leave
 // room for a third wavefront per SIMD (162 against 174 VGPRs), which hides the
 // statistics loads behind another wavefront's arithmetic (config 5: 102 ->
-// 90 us per score launch; four pages gave no further gain).  bf16 takes ten
-// (160 VGPRs, still three wavefronts per SIMD): fewer, fuller workgroups
-// (config 2: 29.1 -> 28.4 us per score launch).
-constexpr int score_iters(int kv_dtype) { return kv_dtype == LSA_INT4 ? 6 : kv_dtype == LSA_BF16 ? 10 : 8; }
+// 90 us per score launch; four pages gave no further gain).  bf16 takes
+// eleven (168 VGPRs, the most that keeps three wavefronts per SIMD): fewer,
+// fuller workgroups, and 44 physical pages per workgroup put a 1025-page
+// selection of 8 sequences x 4 heads in 768 workgroups, one per slot of the
+// chip (config 2: 29.1 us per score launch at eight, 28.4 at ten, 26.8 at
+// eleven).  With the 16-pages-per-thread top-K fused in, eleven would need
+// 172 VGPRs, so that instance keeps ten.
+constexpr int score_iters(int kv_dtype, int fused_pt) {
+    return kv_dtype == LSA_INT4 ? 6 : kv_dtype == LSA_BF16 ? (fused_pt == 16 ? 10 : 11) : 8;
+}
 constexpr int kMaxLogicalPerBlock = 1024;  // LDS slots for logical scores
 
 // Qp / Qn of this lane's channels over the group's query heads h0 .. h1-1, fp64.
@@ -338,7 +344,7 @@ __global__ __launch_bounds__(kScoreThreads) void score_kernel(ScoreArgs a) {
     using S = ScoreShape<EB, D>;
     constexpr int C = S::C, LPL = S::LPL, LPP = S::LPP;
     constexpr int GROUPS = (kScoreThreads / kWave) * LPP;   // lane groups per workgroup
-    constexpr int IT = score_iters(KV_DT);
+    constexpr int IT = score_iters(KV_DT, FPT);
     __shared__ double s_log[kMaxLogicalPerBlock];
 
     const int blk = blockIdx.x % a.blocks_per_head;
@@ -551,13 +557,13 @@ hipError_t launch_score_dt(const ScoreArgs &a, unsigned grid, hipStream_t s) {
 
 }  // namespace
 
-int score_pages_per_block(int kv_dtype, int head_dim, int page_size, int logical_page) {
+int score_pages_per_block(int kv_dtype, int head_dim, int page_size, int logical_page, int fused_pt) {
     // lane groups per workgroup x iterations, in logical pages, over g
     const int eb = kv_dtype == LSA_F32 ? 4 : (kv_dtype == LSA_BF16 ? 2 : 1);
     const int lpl = head_dim / (16 / eb);
     const int groups = (kScoreThreads / kWave) * (kWave / lpl);
     const int g = page_size / logical_page;
-    int ppb = groups * score_iters(kv_dtype) / g;
+    int ppb = groups * score_iters(kv_dtype, fused_pt) / g;
     ppb = ppb < 1 ? 1 : ppb;
     return ppb * g > kMaxLogicalPerBlock ? kMaxLogicalPerBlock / g : ppb;
 }
