@@ -322,7 +322,7 @@ struct PrefillArgs {
 
 hipError_t launch_stats(const StatsArgs &a, hipStream_t s);
 hipError_t launch_score(const ScoreArgs &a, hipStream_t s);
-int score_pages_per_block(int kv_dtype, int head_dim, int page_size, int logical_page, int fused_pt);
+int score_pages_per_block(int kv_dtype, int head_dim, int page_size, int logical_page, int fused_pt, bool agg_max);
 int topk_max_pages();
 int score_fused_pt(int max_pages);   // top-K pages per thread inside the score kernel, 0: a separate launch
 hipError_t launch_topk(const TopkArgs &a, hipStream_t s);

@@ -44,19 +44,27 @@ struct ScoreShape {
 };
 
 constexpr int kScoreThreads = 256;
-// logical pages per lane group and workgroup.  An int4 lane holds 16
-// channels of fp64 query terms; six pages in flight instead of eight leave
-// room for a third wavefront per SIMD (162 against 174 VGPRs), which hides the
-// statistics loads behind another wavefront's arithmetic (config 5: 102 ->
-// 90 us per score launch; four pages gave no further gain).  bf16 takes
-// eleven (168 VGPRs, the most that keeps three wavefronts per SIMD): fewer,
-// fuller workgroups, and 44 physical pages per workgroup put a 1025-page
-// selection of 8 sequences x 4 heads in 768 workgroups, one per slot of the
-// chip (config 2: 29.1 us per score launch at eight, 28.4 at ten, 26.8 at
-// eleven).  With the 16-pages-per-thread top-K fused in, eleven would need
-// 172 VGPRs, so that instance keeps ten.
-constexpr int score_iters(int kv_dtype, int fused_pt) {
-    return kv_dtype == LSA_INT4 ? 6 : kv_dtype == LSA_BF16 ? (fused_pt == 16 ? 10 : 11) : 8;
+// logical pages per lane group and workgroup, chosen per instance so that
+// three wavefronts fit per SIMD (at most 168 VGPRs), which hides one
+// wavefront's statistics loads behind another's arithmetic:
+// - int4 (a lane holds 16 channels of fp64 query terms): seven pages
+//   (config 5: 102 us per score launch at eight pages and two wavefronts per
+//   SIMD, 90 at six, 87 at seven);
+// - bf16: eleven, fewer and fuller workgroups; 44 physical pages per
+//   workgroup put a 1025-page selection of 8 sequences x 4 heads in 768
+//   workgroups, one per slot of the chip (config 2: 29.1 us per score launch
+//   at eight, 28.4 at ten, 26.8 at eleven);
+// - with the 16-pages-per-thread top-K fused in, one page fewer each (one
+//   more would cross 168 VGPRs);
+// - max aggregation keeps the packed statistics across one pass per query
+//   head: bf16 fits three wavefronts per SIMD at six pages (160 VGPRs;
+//   config 2: 42.9 us per selection against 46.8 at ten and 45.0 at nine,
+//   both at two wavefronts per SIMD); int4 needs over 200 VGPRs at any
+//   count and keeps six.
+constexpr int score_iters(int kv_dtype, int fused_pt, bool agg_max) {
+    if (kv_dtype == LSA_INT4) return agg_max || fused_pt == 16 ? 6 : 7;
+    if (kv_dtype == LSA_BF16) return agg_max ? 6 : fused_pt == 16 ? 10 : 11;
+    return 8;
 }
 constexpr int kMaxLogicalPerBlock = 1024;  // LDS slots for logical scores
 
@@ -344,7 +352,7 @@ __global__ __launch_bounds__(kScoreThreads) void score_kernel(ScoreArgs a) {
     using S = ScoreShape<EB, D>;
     constexpr int C = S::C, LPL = S::LPL, LPP = S::LPP;
     constexpr int GROUPS = (kScoreThreads / kWave) * LPP;   // lane groups per workgroup
-    constexpr int IT = score_iters(KV_DT, FPT);
+    constexpr int IT = score_iters(KV_DT, FPT, AGG_MAX);
     __shared__ double s_log[kMaxLogicalPerBlock];
 
     const int blk = blockIdx.x % a.blocks_per_head;
@@ -557,13 +565,13 @@ hipError_t launch_score_dt(const ScoreArgs &a, unsigned grid, hipStream_t s) {
 
 }  // namespace
 
-int score_pages_per_block(int kv_dtype, int head_dim, int page_size, int logical_page, int fused_pt) {
+int score_pages_per_block(int kv_dtype, int head_dim, int page_size, int logical_page, int fused_pt, bool agg_max) {
     // lane groups per workgroup x iterations, in logical pages, over g
     const int eb = kv_dtype == LSA_F32 ? 4 : (kv_dtype == LSA_BF16 ? 2 : 1);
     const int lpl = head_dim / (16 / eb);
     const int groups = (kScoreThreads / kWave) * (kWave / lpl);
     const int g = page_size / logical_page;
-    int ppb = groups * score_iters(kv_dtype, fused_pt) / g;
+    int ppb = groups * score_iters(kv_dtype, fused_pt, agg_max) / g;
     ppb = ppb < 1 ? 1 : ppb;
     return ppb * g > kMaxLogicalPerBlock ? kMaxLogicalPerBlock / g : ppb;
 }
