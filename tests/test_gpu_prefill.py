@@ -205,18 +205,21 @@ def check_mask(p, out, masks, heads=None, rows=None, tol=2e-2):
     return worst
 
 
-@pytest.mark.parametrize("cfg,T,heads,scheduled,H_kv", [(1, 1024, None, True, None), (3, 777, [0, 5, 13, 22, 31], True, None),
-                                                        (3, 1088, [2, 9, 27], False, None),
-                                                        (7, 777, [0, 1, 14, 31], True, None),
-                                                        (7, 1088, [0, 3, 30, 31], False, None),
-                                                        (3, 900, [0, 1, 6, 29, 30, 31], True, 16),
-                                                        (3, 700, [0, 1, 17, 31], False, 16)])
-def test_prefill_csr_random_masks(cfg, T, heads, scheduled, H_kv):
+@pytest.mark.parametrize("cfg,T,heads,scheduled,H_kv,D", [(1, 1024, None, True, None, None),
+                                                          (3, 777, [0, 5, 13, 22, 31], True, None, None),
+                                                          (3, 1088, [2, 9, 27], False, None, None),
+                                                          (7, 777, [0, 1, 14, 31], True, None, None),
+                                                          (7, 1088, [0, 3, 30, 31], False, None, None),
+                                                          (3, 900, [0, 1, 6, 29, 30, 31], True, 16, None),
+                                                          (3, 700, [0, 1, 17, 31], False, 16, None),
+                                                          (7, 1000, [0, 2, 29, 31], True, None, 64),
+                                                          (3, 830, [0, 1, 14, 31], True, 16, 64)])
+def test_prefill_csr_random_masks(cfg, T, heads, scheduled, H_kv, D):
     """Random static masks (30% of the tiles below the diagonal, the diagonal
     kept except in one head, so some query tiles have no key tiles), with and
-    without the mask's work order; at group sizes 1 and 2 a workgroup walks the
-    union of 4 / G query tiles' rows."""
-    p = W.make_prefill(cfg, DEV, seq_len=T, num_kv_heads=H_kv)
+    without the mask's work order, at head_dim 128 and 64; at group sizes 1
+    and 2 a workgroup walks the union of 4 / G query tiles' rows."""
+    p = W.make_prefill(cfg, DEV, seq_len=T, num_kv_heads=H_kv, head_dim=D)
     n = -(-T // 64)
     masks = W.random_tile_masks(p.num_kv_heads, n, 0.3, seed=cfg * 1000 + T)
     masks[-1] = W.random_tile_masks(1, n, 0.3, seed=T, diagonal=False)[0]
