@@ -20,6 +20,8 @@ constexpr int kMaxDecodeChunks = 128;   // split-KV chunks per (sequence, KV hea
 constexpr int kDecodeWaves = 4;
 constexpr int kMaxChunkPages = 16;
 constexpr int kDecodeWaveTokens = 128;
+// XCDs of the part; workgroups are handed to them round robin in number order
+constexpr int kXcds = 8;
 // Static-mask prefill with several query tiles per workgroup builds the union
 // of their rows in LDS: rows of up to this many 64-token tiles
 constexpr int kPrefillMaxUnionTiles = 4096;
