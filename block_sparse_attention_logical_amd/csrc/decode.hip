@@ -307,11 +307,19 @@ __device__ __forceinline__ void finish_head(const DecodeArgs &a, const WorkItem 
     }
 }
 
-// bf16 bit patterns 0x4300 | c (= 128 + c) of the two nibbles of byte k of
-// `w`, low nibble in the low half of the returned dword.
-__device__ __forceinline__ uint32_t nibble_pair_bf16(uint32_t w, int k) {
-    const uint32_t b = (w >> (8 * k)) & 0xFFu;
-    return 0x43004300u | (b & 0x0Fu) | ((b & 0xF0u) << 12);
+// The eight codes of `w` as bf16 bit patterns 0x4300 | c (= 128 + c): dword
+// k holds the low nibble of byte k in its low half and the high nibble in its
+// high half.  The low and high nibbles are masked out once; one byte permute
+// per dword then places byte k of each in bytes 0 and 2 (bytes 1 and 3 zero,
+// selector 12), and one OR sets the exponent bytes.
+__device__ __forceinline__ uint4 nibbles_bf16x8(uint32_t w) {
+    const uint32_t lo = w & 0x0F0F0F0Fu, hi = (w >> 4) & 0x0F0F0F0Fu;
+    // v_perm_b32 selector bytes: 0..3 pick bytes of the second operand (lo),
+    // 4..7 bytes of the first (hi), 12 gives 0x00
+    return make_uint4(__builtin_amdgcn_perm(hi, lo, 0x0C040C00u) | 0x43004300u,
+                      __builtin_amdgcn_perm(hi, lo, 0x0C050C01u) | 0x43004300u,
+                      __builtin_amdgcn_perm(hi, lo, 0x0C060C02u) | 0x43004300u,
+                      __builtin_amdgcn_perm(hi, lo, 0x0C070C03u) | 0x43004300u);
 }
 
 __device__ __forceinline__ uint32_t pick(const uint4 &u, int i) {
@@ -478,10 +486,8 @@ __global__ __launch_bounds__(kDecodeWaves * kWave, 2) void decode_mfma_kernel(De
                 bf16x8 k0, k1;
                 if constexpr (I4) {
                     const uint32_t w0 = pick(kr[e][0][0], s), w1 = pick(kr[e][1][0], s);
-                    k0 = __builtin_bit_cast(bf16x8, make_uint4(nibble_pair_bf16(w0, 0), nibble_pair_bf16(w0, 1),
-                                                               nibble_pair_bf16(w0, 2), nibble_pair_bf16(w0, 3)));
-                    k1 = __builtin_bit_cast(bf16x8, make_uint4(nibble_pair_bf16(w1, 0), nibble_pair_bf16(w1, 1),
-                                                               nibble_pair_bf16(w1, 2), nibble_pair_bf16(w1, 3)));
+                    k0 = __builtin_bit_cast(bf16x8, nibbles_bf16x8(w0));
+                    k1 = __builtin_bit_cast(bf16x8, nibbles_bf16x8(w1));
                 } else {
                     k0 = __builtin_bit_cast(bf16x8, kr[e][0][s]);
                     k1 = __builtin_bit_cast(bf16x8, kr[e][1][s]);
@@ -564,8 +570,7 @@ __global__ __launch_bounds__(kDecodeWaves * kWave, 2) void decode_mfma_kernel(De
                 if constexpr (I4) {
                     // 4 bytes = tokens 8*g4 .. 8*g4+7 of channel 16*dt + h
                     const uint32_t wv4 = vr4[e][dt];
-                    va = make_uint4(nibble_pair_bf16(wv4, 0), nibble_pair_bf16(wv4, 1), nibble_pair_bf16(wv4, 2),
-                                    nibble_pair_bf16(wv4, 3));
+                    va = nibbles_bf16x8(wv4);
                 } else {
                     va = vr[e][dt];
                 }
