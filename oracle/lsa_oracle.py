@@ -19,7 +19,7 @@ Sources (cited by page title and section):
          constant number of KV pages suffices regardless of context length.
 
 Where the pages leave a step open, the reading taken is stated at the function
-that takes it (readings Z1..Z25, listed together in the design notes of the
+that takes it (readings Z1..Z27, listed together in the design notes of the
 repository).
 
 Data conventions (the layout of the caller-owned paged KV pool; a page is
@@ -412,13 +412,13 @@ def block_mask_attention(q: np.ndarray, keys: np.ndarray, values: np.ndarray, ti
                          block: int, scale: float, rows: Optional[Sequence[int]] = None) -> np.ndarray:
     """Softmax attention of one query head under an arbitrary static tile
     mask ([LS-X] 統一ブロックスパースアテンション: the kernel visits the
-    non-empty tiles of a block-sparse pattern; reading Z24: any pattern of
+    non-empty tiles of a block-sparse pattern; reading Z26: any pattern of
     tiles at or below the diagonal, with the token-level causal rule p <= t
     kept inside every tile).
 
     tile_mask: [n][n] bool, n = ceil(T / block); query t sees key p iff
     tile_mask[t // block][p // block] and p <= t.  A query that sees no key
-    gets the zero vector (reading Z25).  Returns [len(rows)][D].
+    gets the zero vector (reading Z27).  Returns [len(rows)][D].
     """
     T, D = q.shape
     rows = range(T) if rows is None else rows

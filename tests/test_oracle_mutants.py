@@ -283,3 +283,67 @@ def speedup_inverted(nnz, dense):
 def test_accounting_mutants_caught():
     assert _fails(P.pin_block_accounting, counts_square, O.sparsity_and_speedup)
     assert _fails(P.pin_block_accounting, O.block_counts, speedup_inverted)
+
+
+# --- KV4 dequantisation ----------------------------------------------------
+
+def dequant_scale_then_zero(codes, s, z):
+    return np.asarray(codes, np.float64) * s - z
+
+
+def dequant_plus_zero(codes, s, z):
+    return (np.asarray(codes, np.float64) + z) * s
+
+
+def dequant_divides_by_scale(codes, s, z):
+    return (np.asarray(codes, np.float64) - z) / s
+
+
+@pytest.mark.parametrize("mutant", [dequant_scale_then_zero, dequant_plus_zero, dequant_divides_by_scale])
+def test_dequant_mutants_caught(mutant):
+    assert _fails(P.pin_dequant_int4, mutant)
+
+
+# --- the decode step's reselect path -----------------------------------------
+
+def decode_step_stats_before_current(spec, q, keys, values, selected, reselect, key_codes=None):
+    """Builds the selection statistics from keys[:t], leaving out the current token."""
+    orig = O.page_stats
+    O.page_stats = lambda k, n_l: orig(k[:-1], n_l)
+    try:
+        return O.decode_step(spec, q, keys, values, selected, reselect)
+    finally:
+        O.page_stats = orig
+
+
+def decode_step_always_reselects(spec, q, keys, values, selected, reselect, key_codes=None):
+    return O.decode_step(spec, q, keys, values, selected, True)
+
+
+def decode_step_drops_current_page(spec, q, keys, values, selected, reselect, key_codes=None):
+    """Attends the selected pages only, not the page of the current token."""
+    orig = O.attended_retrieval
+
+    def no_current(t, sel, n_p):
+        pages = set(int(m) for m in sel if m >= 0)
+        return np.array([(p // n_p) in pages for p in range(t + 1)], dtype=bool)
+    O.attended_retrieval = no_current
+    try:
+        return O.decode_step(spec, q, keys, values, selected, reselect)
+    finally:
+        O.attended_retrieval = orig
+
+
+def decode_step_scores_first_head_only(spec, q, keys, values, selected, reselect, key_codes=None):
+    orig = O.select_pages
+    O.select_pages = lambda qg, kmin, kmax, g, k, agg=O.SUM: orig(qg[:1], kmin, kmax, g, k, agg)
+    try:
+        return O.decode_step(spec, q, keys, values, selected, reselect)
+    finally:
+        O.select_pages = orig
+
+
+@pytest.mark.parametrize("mutant", [decode_step_stats_before_current, decode_step_always_reselects,
+                                    decode_step_drops_current_page, decode_step_scores_first_head_only])
+def test_decode_step_mutants_caught(mutant):
+    assert _fails(P.pin_decode_step_partial_budget, mutant)

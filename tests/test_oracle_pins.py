@@ -483,3 +483,125 @@ def test_pool_int4_codes_follow_layout():
             assert codes[p, c] == kc[pg, 0, sl // 32, c // 32, sl % 32, c % 32]
             assert K[p, c] == kc[pg, 0, sl // 32, c // 32, sl % 32, c % 32]
             assert V[p, c] == vc[pg, 0, sl // 32, c, sl % 32]
+
+
+# ---------------------------------------------------------------------------
+# KV4 dequantisation x = (c - z) * s (reading Z17) with s != 1 and z != 0
+# ---------------------------------------------------------------------------
+
+def pin_dequant_int4(dequant_int4, seed=13):
+    """Hand-worked values of the affine code map, then the round trip through
+    the input generator's quantiser (nearest code on the grid (c - z) * s):
+    on data whose range holds 0, every value comes back within half a step,
+    |dequant(quant(x)) - x| <= s / 2."""
+    # (3 - 1.5) * 0.25 = 0.375;  (1 - 2.5) * 0.5 = -0.75;  (15 - 0.0625) * 2 = 29.875;  (0 - 7) * 0.125 = -0.875
+    for c, s, z, x in ((3, 0.25, 1.5, 0.375), (1, 0.5, 2.5, -0.75), (15, 2.0, 0.0625, 29.875),
+                       (0, 0.125, 7.0, -0.875)):
+        got = dequant_int4(np.array([c], dtype=np.uint8), s, z)
+        assert got.dtype == np.float64 and got.tolist() == [x], (c, s, z, got)
+    from block_sparse_attention_logical_amd.workloads import quantize_int4
+    g = torch.Generator().manual_seed(seed)
+    x = torch.randn((6, 2, 64, 32), generator=g) * torch.tensor([0.3, 5.0])[None, :, None, None]
+    codes, sz = quantize_int4(x)
+    sz_bits = sz.view(torch.int16).numpy().view(np.uint16)
+    for p in range(x.shape[0]):
+        for h in range(x.shape[1]):
+            s, z = O.fp16_bits_to_f64(sz_bits[p, h])
+            assert s != 1.0 and z != 0.0
+            back = dequant_int4(codes[p, h].numpy(), s, z)
+            err = np.abs(back - x[p, h].double().numpy())
+            assert np.max(err) <= s * (0.5 + 1e-5), (p, h, np.max(err) / s)
+
+
+def test_dequant_int4_hand_values_and_round_trip():
+    pin_dequant_int4(O.dequant_int4)
+
+
+def test_pool_int4_applies_each_pages_scale_and_zero():
+    """An int4 pool whose pages hold one code each under different (s, z) for
+    K and V: every key and value of a page is that page's hand-worked value,
+    so a scale taken from another page or the other tensor shows."""
+    P, H, NP, D = 2, 1, 32, 64
+    kc = np.zeros((P, H, NP // 32, D // 32, 32, 32), np.uint8)
+    vc = np.zeros((P, H, NP // 32, D, 32), np.uint8)
+    kc[0], kc[1], vc[0], vc[1] = 3, 1, 15, 0
+    pack = lambda c: (c[..., 0::2] | (c[..., 1::2] << 4)).astype(np.uint8)   # noqa: E731
+    fp16 = lambda a: np.array(a, np.float16).view(np.uint16)                  # noqa: E731
+    k_sz = fp16([[[0.25, 1.5]], [[0.5, 2.5]]])         # page 0: (3 - 1.5) * 0.25; page 1: (1 - 2.5) * 0.5
+    v_sz = fp16([[[2.0, 0.0625]], [[0.125, 7.0]]])     # page 0: (15 - 0.0625) * 2; page 1: (0 - 7) * 0.125
+    pool = O.Pool("int4", pack(kc), pack(vc), NP, D, k_sz, v_sz)
+    K = pool.keys([1, 0], 0, 64)
+    V = pool.values([1, 0], 0, 64)
+    assert np.all(K[:32] == -0.75) and np.all(K[32:] == 0.375)
+    assert np.all(V[:32] == -0.875) and np.all(V[32:] == 29.875)
+
+
+# ---------------------------------------------------------------------------
+# decode_step with a budget below the sequence: the reselect path
+# ---------------------------------------------------------------------------
+
+def _box_support_scores(keys, qg, NL):
+    """Per logical page j of the valid keys: sum over the group's heads of the
+    largest q_h . x over the 2^D corners x of the page's bounding box, the
+    box taken with Python's min / max over the page's tokens."""
+    L, D = keys.shape
+    corners = list(itertools.product((0, 1), repeat=D))
+    out = []
+    for j in range(-(-L // NL)):
+        rows = [list(keys[p]) for p in range(j * NL, min((j + 1) * NL, L))]
+        lo = [min(r[i] for r in rows) for i in range(D)]
+        hi = [max(r[i] for r in rows) for i in range(D)]
+        out.append(sum(max(sum(qh[i] * (hi[i] if c[i] else lo[i]) for i in range(D)) for c in corners)
+                       for qh in qg))
+    return out
+
+
+def pin_decode_step_partial_budget(decode_step, seed=12):
+    """Windows of six decode steps of a retrieval and a streaming KV head (G =
+    2) with a budget of 3 of 10-11 pages.  At each selection step (i % R == 0,
+    Z9) the kept pages are the 3 best physical pages by a brute-force rank
+    (descending score, then ascending page; Z5) of physical scores that are the
+    max over their logical pages of explicitly enumerated box supports over
+    tokens 0..t, the current token included (Z14, Z7); between selections the
+    earlier selection stays.  The first window token opens a page and is a key
+    along (first window) or against (second window) the group's step-0
+    queries: its page ranks first only when the current token is scored, and
+    in the second window it ranks last, so it is read only as the current page.
+    Every output equals torch SDPA in fp64 under the explicit attended mask:
+    the kept pages plus the current page (Z10), or the sink + local window
+    (Z11)."""
+    H_q, H_kv, D, G = 4, 2, 5, 2
+    NL, NP, K, R, sink, local = 4, 8, 3, 4, 3, 10
+    spec = O.DecodeSpec(H_q, H_kv, [O.RETRIEVAL, O.STREAMING], NL, NP, K * NP, R, sink, local)
+    L0, steps = 10 * NP, 6
+    for sign in (1.0, -1.0):
+        rng = np.random.default_rng(seed)
+        keys = [rng.standard_normal((L0 + steps, D)) for _ in range(H_kv)]
+        values = [rng.standard_normal((L0 + steps, D)) for _ in range(H_kv)]
+        qs = [rng.standard_normal((H_q, D)) for _ in range(steps)]
+        d0 = qs[0][0] + qs[0][1]
+        keys[0][L0] = sign * 6.0 * d0 / np.linalg.norm(d0)
+        sel, kept = None, None
+        for i in range(steps):
+            L = L0 + i + 1
+            t = L - 1
+            o, sel = decode_step(spec, qs[i], [k[:L] for k in keys], [v[:L] for v in values], sel, i % R == 0)
+            if i % R == 0:
+                S = _box_support_scores(keys[0][:L], qs[i][:G], NL)
+                g = NP // NL
+                Pm = [max(S[m * g:(m + 1) * g]) for m in range(-(-L // NP))]
+                kept = sorted(sorted(range(len(Pm)), key=lambda m: (-Pm[m], m))[:K])
+                if i == 0:                      # the page the current token opened
+                    assert (L0 // NP in kept) == (sign > 0)
+            assert list(sel[0]) == kept, (sign, i, list(sel[0]), kept)
+            pages = set(kept) | {t // NP}
+            p = np.arange(L)
+            masks = [np.array([(x // NP) in pages for x in p]), (p < sink) | (t - p < local)]
+            for h in range(H_q):
+                kv = h // G
+                ref = _sdpa(qs[i][h][None], keys[kv][:L], values[kv][:L], mask=masks[kv][None])[0]
+                assert np.max(np.abs(o[h] - ref)) < 1e-12, (sign, i, h)
+
+
+def test_decode_step_partial_budget_reselect_path():
+    pin_decode_step_partial_budget(O.decode_step)
