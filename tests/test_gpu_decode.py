@@ -33,6 +33,7 @@ class Runner:
                                   dtype=torch.uint8, device=DEV)
         self.ws_dec = torch.zeros(lsa.decode_workspace(self.kv, w.page_table, lens0, self.hd, w.token_budget),
                                   dtype=torch.uint8, device=DEV)
+        self.history = []            # host copy of the selection after every step
 
     def step(self, i):
         """One decode step: select (every R steps; the current logical page is
@@ -46,12 +47,16 @@ class Runner:
         lsa.sparse_decode_attn(w.q[i], self.kv, w.page_table, lens, self.hd, self.selected, w.token_budget,
                                out, self.ws_dec, stats=self.stats)
         torch.cuda.synchronize()
+        self.history.append(self.selected.cpu().numpy().copy())
         return out
 
 
-def oracle_window(w, b, kv_heads=None, agg=lsa.AGG_SUM):
+def oracle_window(w, b, kv_heads=None, agg=lsa.AGG_SUM, selections=None, gaps=None):
     """Outputs of every decode step of sequence b from the oracle, following
-    the step order of the reusable selection."""
+    the step order of the reusable selection.  With `selections` (a dict) the
+    oracle's selection of every retrieval head is recorded per step under
+    (step, kv); with `gaps` (a list) the relative gap between the K-th and
+    (K+1)-th physical page scores of every selection is appended."""
     spec = H.oracle_spec(w, agg)
     G = w.num_q_heads // w.num_kv_heads
     Lmax = w.ctx[b] + w.window
@@ -72,7 +77,14 @@ def oracle_window(w, b, kv_heads=None, agg=lsa.AGG_SUM):
             if spec.head_kind[kv] == O.RETRIEVAL:
                 if i % w.reuse_interval == 0:
                     kmin, kmax = O.page_stats(keys[kv][:L], w.logical_page)
-                    sel[kv] = O.select_pages(group, kmin, kmax, w.page_size // w.logical_page, K, spec.aggregation)
+                    P = O.physical_scores(O.logical_scores(group, kmin, kmax, spec.aggregation),
+                                          w.page_size // w.logical_page)
+                    sel[kv] = O.topk_pages(P, K)
+                    if gaps is not None and len(P) > K:
+                        srt = np.sort(P)[::-1]
+                        gaps.append(abs(srt[K - 1] - srt[K]) / max(1.0, abs(srt[K - 1])))
+                if selections is not None:
+                    selections[(i, kv)] = sel[kv].copy()
                 mask = O.attended_retrieval(t, sel[kv], w.page_size)
             else:
                 mask = O.attended_streaming(t, w.sink_tokens, w.local_tokens)
@@ -84,11 +96,18 @@ def oracle_window(w, b, kv_heads=None, agg=lsa.AGG_SUM):
 
 
 def check_window(w, kv_heads=None, batches=None, agg=lsa.AGG_SUM):
+    """Run the window on the GPU and compare, for the sampled sequences and
+    KV heads, the selection after every step (bit for bit, ties to the lower
+    page) and the outputs (within the tolerance) with the oracle."""
     r = Runner(w, agg)
     gpu = [H.to_f64(r.step(i)) for i in range(w.window)]
     worst = 0.0
+    gaps = []
     for b in (range(w.batch) if batches is None else batches):
-        ref = oracle_window(w, b, kv_heads, agg)
+        oracle_sel = {}
+        ref = oracle_window(w, b, kv_heads, agg, selections=oracle_sel, gaps=gaps)
+        for (i, kv), expect in oracle_sel.items():
+            assert np.array_equal(r.history[i][b, kv], expect), (b, i, kv, r.history[i][b, kv], expect)
         for i in range(w.window):
             G = w.num_q_heads // w.num_kv_heads
             heads = range(w.num_q_heads) if kv_heads is None else [kv * G + h for kv in kv_heads for h in range(G)]
@@ -96,6 +115,9 @@ def check_window(w, kv_heads=None, batches=None, agg=lsa.AGG_SUM):
                 err = np.max(np.abs(gpu[i][b, h] - ref[i][h]))
                 worst = max(worst, err)
                 assert err <= tol(w), (b, i, h, err)
+    if gaps:
+        print(f"selections checked bit for bit; smallest relative gap between the K-th and (K+1)-th page "
+              f"scores: {min(gaps):.3e}")
     return worst
 
 
@@ -221,10 +243,11 @@ def test_decode_full_size_cfg2_sampled():
 def test_decode_full_size_cfg4_sampled():
     """Config 4 at full size (B = 64, contexts 128K-256K, N_P = 128, permuted
     pool of about 48 GiB): the whole batch runs on the GPU; the oracle
-    recomputes one retrieval and one streaming KV head of three sequences for
-    the 4-step window, selections included."""
+    recomputes every retrieval KV head and one streaming KV head of three
+    sequences (the first, the longest and the shortest) for the 4-step window:
+    selections bit for bit, outputs within the tolerance."""
     w = W.make_decode(4, DEV)
-    ret = [kv for kv in range(w.num_kv_heads) if w.head_kind[kv] == 0][:1]
+    ret = [kv for kv in range(w.num_kv_heads) if w.head_kind[kv] == 0]
     st = [kv for kv in range(w.num_kv_heads) if w.head_kind[kv] == 1][:1]
     batches = [0, int(np.argmax(w.ctx)), int(np.argmin(w.ctx))]
     print("max abs err", check_window(w, kv_heads=ret + st, batches=batches))
@@ -233,11 +256,14 @@ def test_decode_full_size_cfg4_sampled():
 
 
 def test_decode_full_size_cfg5_int4_sampled():
-    """Config 5 at full size (KV4, B = 16, 256K context)."""
+    """Config 5 at full size (KV4, B = 16, 256K context: 4097 pages per
+    sequence, so the selection runs its separate top-K): every retrieval KV
+    head and one streaming KV head of three sequences, selections bit for bit."""
     w = W.make_decode(5, DEV)
-    ret = [kv for kv in range(w.num_kv_heads) if w.head_kind[kv] == 0][:2]
+    assert w.max_pages == 4097
+    ret = [kv for kv in range(w.num_kv_heads) if w.head_kind[kv] == 0]
     st = [kv for kv in range(w.num_kv_heads) if w.head_kind[kv] == 1][:1]
-    print("max abs err", check_window(w, kv_heads=ret + st, batches=[0, 15]))
+    print("max abs err", check_window(w, kv_heads=ret + st, batches=[0, 7, 15]))
     del w
     torch.cuda.empty_cache()
 
@@ -354,3 +380,43 @@ def test_decode_window_in_hip_graph_matches_eager():
         for i in range(w.window):
             assert torch.equal(outs[i].view(torch.int16), eager[i].view(torch.int16)), (rep, i)
         del junk
+
+
+@pytest.mark.parametrize("H_q,H_kv", [(16, 2), (6, 2)])
+def test_decode_f32_head_dim_128_groups(H_q, H_kv):
+    """The f32 path (config 1's dtype) at head_dim 128 with group sizes 8 and
+    3: the 16-step window's selections bit for bit and outputs within 1e-5,
+    and the statistics the decode calls refreshed equal a full build."""
+    import tests.test_gpu_stats_select as S
+    w = W.make_decode(1, DEV, head_dim=128, num_q_heads=H_q, num_kv_heads=H_kv)
+    print("max abs err", check_window(w))
+    r = Runner(w)
+    for i in range(w.window):
+        r.step(i)
+    S.check_stats(w, r.stats, [c + w.window for c in w.ctx], kinds=w.head_kind)
+
+
+@pytest.mark.parametrize("cfg", [1, 2])
+def test_decode_ignores_values_past_the_current_token(cfg):
+    """Pool slots after the current token hold NaN (bf16 0x7FC0, or an f32
+    NaN) in K and V: the statistics refresh, the selection and the attention
+    read none of them, so the outputs have no NaN and match the oracle."""
+    w = W.make_decode(cfg, DEV, batch=2, ctx=[1000, 2500], window=1) if cfg != 1 else \
+        W.make_decode(1, DEV, window=1)
+    for b, c in enumerate(w.ctx):
+        t = c                                   # the one window step's token
+        pool = int(w.page_table[b, t // w.page_size])
+        for s_ in range(t % w.page_size + 1, w.page_size):
+            blk, r = s_ // 32, s_ % 32          # key tiles [blk][D/32][32][32], value rows [blk][D][32]
+            w.k[pool, :, blk, :, r, :] = float("nan")
+            w.v[pool, :, blk, :, r] = float("nan")
+    r = Runner(w)
+    out = r.step(0)
+    assert not torch.isnan(out.float()).any()
+    gpu = H.to_f64(out)
+    sel = {}
+    for b in range(w.batch):
+        ref = oracle_window(w, b, selections=sel)
+        for (i, kv), expect in sel.items():
+            assert np.array_equal(r.history[i][b, kv], expect)
+        assert np.max(np.abs(gpu[b] - ref[0])) <= tol(w)

@@ -302,3 +302,21 @@ def test_prefill_csr_full_size(cfg):
     assert torch.equal(a.view(torch.int16), b.view(torch.int16))
     del a, b, p
     torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("cfg", [1, 3])
+def test_prefill_ignores_slots_past_the_sequence(cfg):
+    """The last page's slots past the sequence (tokens 1000..1023) hold NaN in
+    K and V (f32 NaN, or bf16 0x7FC0): no query reads them, so the outputs have
+    no NaN and match the oracle, including the rows of the ragged last tile."""
+    p = W.make_prefill(cfg, DEV, seq_len=1000)
+    last = int(p.page_table[-1])
+    for s_ in range(p.seq_len % p.page_size, p.page_size):
+        blk, r = s_ // 32, s_ % 32              # key tiles [blk][D/32][32][32], value rows [blk][D][32]
+        p.k[last, :, blk, :, r, :] = float("nan")
+        p.v[last, :, blk, :, r] = float("nan")
+    out, cnt = run_prefill(p)
+    assert cnt == expected_tiles(p)
+    assert not torch.isnan(out.float()).any()
+    heads = None if cfg == 1 else {0, 5, 17, 31}
+    print("max abs err", check(p, out, heads=heads, tol=1e-5 if cfg == 1 else 2e-2))

@@ -245,17 +245,20 @@ def test_select_full_size_cfg2():
     print(f"smallest relative gap between the K-th and (K+1)-th page scores: {min(gaps):.3e}")
 
 
-@pytest.mark.parametrize("pages", [4096, 4097])
-def test_select_either_side_of_one_kernel_limit(pages):
+@pytest.mark.parametrize("cfg,pages", [(2, 4096), (2, 4097), (5, 4096), (5, 4097)])
+def test_select_either_side_of_one_kernel_limit(cfg, pages):
     """Up to 4096 pages per sequence the last score workgroup of a (sequence,
     head) runs its top-K; from 4097 pages a separate top-K kernel does.  Both
-    sides of that limit, with a shorter second sequence in the batch."""
-    w = W.make_decode(2, DEV, batch=2, ctx=[pages * 64 - 4, 3000])      # + 4 window tokens
+    sides of that limit, for the bf16 pool (config 2) and the int4 pool
+    (config 5, whose 256K context has 4097 pages), with a shorter second
+    sequence in the batch; every retrieval head, bit for bit."""
+    w = W.make_decode(cfg, DEV, batch=2, ctx=[pages * 64 - 4, 3000])      # + 4 window tokens
     assert w.max_pages == pages
     lens = [c + 1 for c in w.ctx]
     sel = run_select(w, 0, lens)
-    ret = [kv for kv in range(w.num_kv_heads) if w.head_kind[kv] == 0]
-    check_selection(w, 0, lens, sel, pairs={(0, ret[0]), (0, ret[-1]), (1, ret[0])})
+    gaps = []
+    check_selection(w, 0, lens, sel, report=gaps)
+    print(f"smallest relative gap between the K-th and (K+1)-th page scores: {min(gaps):.3e}")
     del w
     torch.cuda.empty_cache()
 
