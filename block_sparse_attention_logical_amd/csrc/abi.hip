@@ -8,6 +8,7 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 #include <string>
 
 #include "lsa_internal.h"
@@ -172,6 +173,49 @@ lsa_status prefill_setup(PrefillArgs &p, const void *q, int32_t q_dtype, const l
     return LSA_OK;
 }
 
+// ---------------------------------------------------------------------------
+// Static scratch of lsa_sparse_decode_attn_noalloc: the decode workspace
+// (arrival counters, then the split-KV partial records) in a file-scope device
+// array, for callers that cannot allocate.  Each GPU the library runs on holds
+// its own copy until the process ends; every call on that GPU shares it.
+// Host code addresses it only through the pointer hipGetSymbolAddress returns
+// for the current device (the array's name is a host-side stand-in).
+// ---------------------------------------------------------------------------
+constexpr size_t kStaticScratchBytes = (size_t)16 << 20;
+constexpr int kMaxDevices = 64;
+
+static __device__ __align__(256) unsigned char scratch[kStaticScratchBytes];
+
+std::mutex g_scratch_mu;
+void *g_scratch_ptr[kMaxDevices] = {};
+
+// The address of the current device's copy of the scratch array, looked up
+// once per device (with that device current) and kept.
+lsa_status static_scratch(void **out) {
+    int dev = -1;
+    if (hipError_t e = hipGetDevice(&dev)) return from_hip(e, "hipGetDevice");
+    if (dev < 0 || dev >= kMaxDevices) return fail(LSA_ERR_UNSUPPORTED, "device %d beyond %d", dev, kMaxDevices);
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void *p = nullptr;
+        if (hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch))) return from_hip(e, "hipGetSymbolAddress");
+        if (!p) return fail(LSA_ERR_HIP, "hipGetSymbolAddress returned NULL for the scratch array");
+        g_scratch_ptr[dev] = p;
+    }
+    *out = g_scratch_ptr[dev];
+    return LSA_OK;
+}
+
+__global__ void zero_i32_kernel(int32_t *p, int n) {
+    const int i = blockIdx.x * blockDim.x + threadIdx.x;
+    if (i < n) p[i] = 0;
+}
+
+lsa_status decode_attn_impl(const void *q, int32_t q_dtype, const lsa_kv *kv, const lsa_seqs *seqs,
+                            const lsa_heads *heads, const int32_t *selected, int32_t token_budget,
+                            float softmax_scale, void *out, void *stats, void *workspace, size_t workspace_bytes,
+                            bool clear_counters, hipStream_t stream);
+
 }  // namespace
 }  // namespace lsa
 
@@ -334,6 +378,26 @@ lsa_status lsa_sparse_decode_attn(const void *q, int32_t q_dtype, const lsa_kv *
                                   const lsa_heads *heads, const int32_t *selected, int32_t token_budget,
                                   float softmax_scale, void *out, void *stats, void *workspace,
                                   size_t workspace_bytes, void *stream) {
+    return decode_attn_impl(q, q_dtype, kv, seqs, heads, selected, token_budget, softmax_scale, out, stats,
+                            workspace, workspace_bytes, false, (hipStream_t)stream);
+}
+
+lsa_status lsa_sparse_decode_attn_noalloc(const void *q, int32_t q_dtype, const lsa_kv *kv, const lsa_seqs *seqs,
+                                          const lsa_heads *heads, const int32_t *selected, int32_t token_budget,
+                                          float softmax_scale, void *out, void *stats, void *stream) {
+    return decode_attn_impl(q, q_dtype, kv, seqs, heads, selected, token_budget, softmax_scale, out, stats,
+                            nullptr, 0, true, (hipStream_t)stream);
+}
+
+}  // extern "C"
+
+namespace lsa {
+namespace {
+
+lsa_status decode_attn_impl(const void *q, int32_t q_dtype, const lsa_kv *kv, const lsa_seqs *seqs,
+                            const lsa_heads *heads, const int32_t *selected, int32_t token_budget,
+                            float softmax_scale, void *out, void *stats, void *workspace, size_t workspace_bytes,
+                            bool use_static, hipStream_t stream) {
     if (lsa_status s = check_kv(kv)) return s;
     if (lsa_status s = check_seqs(seqs)) return s;
     if (lsa_status s = check_heads(heads, kv, true)) return s;
@@ -349,14 +413,20 @@ lsa_status lsa_sparse_decode_attn(const void *q, int32_t q_dtype, const lsa_kv *
         return fail(LSA_ERR_INVALID_ARG, "softmax_scale must be finite and >= 0");
     size_t need = 0;
     if (lsa_status s = lsa_decode_workspace(kv, seqs, heads, token_budget, &need)) return s;
-    if (!workspace || workspace_bytes < need)
+    if (use_static && need > kStaticScratchBytes)
+        return fail(LSA_ERR_UNSUPPORTED,
+                    "lsa_sparse_decode_attn_noalloc: this batch needs %zu bytes of scratch, above the %zu-byte "
+                    "static scratch array; use lsa_sparse_decode_attn with a caller workspace",
+                    need, kStaticScratchBytes);
+    if (!use_static && (!workspace || workspace_bytes < need))
         return fail(LSA_ERR_WORKSPACE, "workspace of %zu bytes, need %zu", workspace_bytes, need);
-    if (seqs->batch == 0) return ok();
-
     const DecodeGeom g = decode_geometry(kv, heads, token_budget);
     if (g.chunks_max > kMaxDecodeChunks)
         return fail(LSA_ERR_UNSUPPORTED, "token budget / Lambda window spans %d split-KV chunks (limit %d)",
                     g.chunks_max, kMaxDecodeChunks);
+    if (seqs->batch == 0) return ok();
+    if (use_static)                       // every argument is valid: now touch the device
+        if (lsa_status s = static_scratch(&workspace)) return s;
     DecodeArgs a{};
     a.q = q;
     a.out = out;
@@ -389,8 +459,20 @@ lsa_status lsa_sparse_decode_attn(const void *q, int32_t q_dtype, const lsa_kv *
     const float scale = softmax_scale > 0.f ? softmax_scale : 1.f / std::sqrt((float)kv->head_dim);
     a.scale_log2 = scale * 1.4426950408889634f;
     for (int i = 0; i < kv->num_kv_heads; ++i) a.kind[i] = heads->head_kind[i];
-    return from_hip(launch_decode(a, q_dtype, kv->kv_dtype, (hipStream_t)stream), "decode launch");
+    if (use_static) {
+        // the static scratch keeps whatever the previous call left: zero the
+        // arrival counters with a fill kernel (no memset node in a captured graph)
+        const int n = seqs->batch * kv->num_kv_heads;
+        hipLaunchKernelGGL(zero_i32_kernel, dim3((n + 255) / 256), dim3(256), 0, stream, a.counters, n);
+        if (lsa_status s = from_hip(hipGetLastError(), "decode counter clear launch")) return s;
+    }
+    return from_hip(launch_decode(a, q_dtype, kv->kv_dtype, stream), "decode launch");
 }
+
+}  // namespace
+}  // namespace lsa
+
+extern "C" {
 
 lsa_status lsa_sparse_prefill_attn(const void *q, int32_t q_dtype, const lsa_kv *kv, const int32_t *page_table,
                                    int32_t seq_len, const lsa_heads *heads, int32_t block, float softmax_scale,

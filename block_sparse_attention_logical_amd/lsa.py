@@ -34,6 +34,7 @@ EXPORTED = (
     "lsa_select_pages",
     "lsa_decode_workspace",
     "lsa_sparse_decode_attn",
+    "lsa_sparse_decode_attn_noalloc",
     "lsa_sparse_prefill_attn",
     "lsa_sparse_prefill_attn_csr",
     "lsa_block_mask_schedule",
@@ -110,6 +111,8 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.lsa_decode_workspace.argtypes = [P(LsaKV), P(LsaSeqs), P(LsaHeads), ctypes.c_int32, sz]
     lib.lsa_sparse_decode_attn.argtypes = [vp, ctypes.c_int32, P(LsaKV), P(LsaSeqs), P(LsaHeads), vp,
                                            ctypes.c_int32, ctypes.c_float, vp, vp, vp, ctypes.c_size_t, vp]
+    lib.lsa_sparse_decode_attn_noalloc.argtypes = [vp, ctypes.c_int32, P(LsaKV), P(LsaSeqs), P(LsaHeads), vp,
+                                                   ctypes.c_int32, ctypes.c_float, vp, vp, vp]
     lib.lsa_sparse_prefill_attn.argtypes = [vp, ctypes.c_int32, P(LsaKV), vp, ctypes.c_int32, P(LsaHeads),
                                             ctypes.c_int32, ctypes.c_float, vp, vp, vp]
     lib.lsa_sparse_prefill_attn_csr.argtypes = [vp, ctypes.c_int32, P(LsaKV), vp, ctypes.c_int32, ctypes.c_int32,
@@ -268,6 +271,18 @@ def sparse_decode_attn(q: torch.Tensor, kv: KVPool, page_table: torch.Tensor, se
                                          _ptr(selected), token_budget, softmax_scale, _ptr(out), _ptr(stats),
                                          _ptr(workspace), workspace.numel() * workspace.element_size(),
                                          _stream(stream)))
+
+
+def sparse_decode_attn_noalloc(q: torch.Tensor, kv: KVPool, page_table: torch.Tensor, seq_lens: torch.Tensor,
+                               heads: Heads, selected: Optional[torch.Tensor], token_budget: int, out: torch.Tensor,
+                               softmax_scale: float = 0.0, stats: Optional[torch.Tensor] = None,
+                               stream=None) -> None:
+    """lsa_sparse_decode_attn_noalloc: sparse_decode_attn with its scratch in the library's
+    static per-GPU array (16 MiB) instead of a caller workspace; calls that overlap on one GPU race."""
+    _check(load().lsa_sparse_decode_attn_noalloc(_ptr(q), dtype_code(q), ctypes.byref(kv.desc()),
+                                                 ctypes.byref(seqs_desc(page_table, seq_lens)),
+                                                 ctypes.byref(heads.desc()), _ptr(selected), token_budget,
+                                                 softmax_scale, _ptr(out), _ptr(stats), _stream(stream)))
 
 
 def sparse_prefill_attn(q: torch.Tensor, kv: KVPool, page_table: torch.Tensor, seq_len: int, heads: Heads,

@@ -19,7 +19,8 @@
  * Conventions shared by every entry point
  *   - Pointers are DEVICE pointers unless marked [host].
  *   - Every buffer is owned by the caller; the library allocates nothing and
- *     keeps no state of its own between calls.  Workspaces are sized by the
+ *     keeps no state of its own between calls (the one exception is the
+ *     static scratch of lsa_sparse_decode_attn_noalloc).  Workspaces are sized by the
  *     *_workspace queries.  The selection and decode workspaces hold arrival
  *     counters that must be zero when a call starts; every completed call
  *     leaves them zero, so zero-filling a workspace once, before its first
@@ -235,6 +236,28 @@ lsa_status lsa_sparse_decode_attn(const void *q, int32_t q_dtype, const lsa_kv *
                                   const int32_t *selected, int32_t token_budget,
                                   float softmax_scale, void *out, void *stats,
                                   void *workspace, size_t workspace_bytes, void *stream);
+
+/* lsa_sparse_decode_attn without a workspace argument, for callers that
+ * cannot allocate device memory (code under HIP graph capture, tight serving
+ * loops, harnesses that forbid allocation).  It computes exactly what
+ * lsa_sparse_decode_attn computes, with the same kernels, and allocates
+ * nothing: its scratch (the arrival counters and the split-KV partial
+ * records that lsa_decode_workspace sizes) is a 16 MiB (16777216-byte)
+ * static device array inside the library, one copy per GPU, held until the
+ * process ends.  The copy of the current device (hipGetDevice) is used; its
+ * address is looked up on the first call on that device.  A batch whose
+ * lsa_decode_workspace size exceeds 16 MiB is rejected with
+ * LSA_ERR_UNSUPPORTED and nothing is launched (config-2-shaped layers, 8 x 8
+ * heads at a 4096-token budget, need 1.25 MB; 64 x 8 heads at N_P = 128 need
+ * 10 MB).  Each call first clears the counters with a small fill kernel on
+ * `stream`, then launches the decode kernel.  Every call on a GPU shares that
+ * GPU's array: calls that overlap in time on one GPU (other streams, other
+ * threads) race and give undefined results; order them on one stream.
+ * Arguments and errors are otherwise those of lsa_sparse_decode_attn. */
+lsa_status lsa_sparse_decode_attn_noalloc(const void *q, int32_t q_dtype, const lsa_kv *kv,
+                                          const lsa_seqs *seqs, const lsa_heads *heads,
+                                          const int32_t *selected, int32_t token_budget,
+                                          float softmax_scale, void *out, void *stats, void *stream);
 
 /* Block-sparse causal prefill attention of one sequence over non-empty tiles
  * only ([LS-X] 統一ブロックスパースアテンション: iterate the non-empty blocks;

@@ -280,3 +280,20 @@ def test_stats_validation(lib):
         lsa.LSA_ERR_INVALID_ARG
     # empty batch: nothing to build
     assert lib.lsa_build_page_stats(ctypes.byref(kv), ctypes.byref(seqs_desc(0)), None, None, 0, FAKE, None) == 0
+
+
+def test_decode_noalloc_validation(lib):
+    """The static-scratch decode call validates like lsa_sparse_decode_attn and
+    rejects a batch whose scratch exceeds its 16 MiB array before touching the
+    device."""
+    def call(B=2, q_dtype=lsa.BF16, selected=FAKE, budget=4096, heads=None):
+        return lib.lsa_sparse_decode_attn_noalloc(FAKE, q_dtype, ctypes.byref(kv_desc()),
+                                                  ctypes.byref(seqs_desc(B, 1025)),
+                                                  ctypes.byref(heads or heads_desc()), selected, budget, 0.0,
+                                                  FAKE, None, None)
+    assert call(q_dtype=lsa.F32) == lsa.LSA_ERR_UNSUPPORTED
+    assert call(selected=None) == lsa.LSA_ERR_INVALID_ARG
+    # 8 x 8 heads at a 4096-token budget need 1.25 MB; 128 sequences need 20 MB
+    assert call(B=128) == lsa.LSA_ERR_UNSUPPORTED
+    assert "16777216-byte static scratch" in lsa.last_error()
+    assert call(B=0) == lsa.LSA_OK                      # an empty batch launches nothing
