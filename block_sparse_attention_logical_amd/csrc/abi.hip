@@ -57,9 +57,8 @@ lsa_status check_kv(const lsa_kv *kv) {
     if (kv->page_size < kv->logical_page || kv->page_size % kv->logical_page != 0)
         return fail(LSA_ERR_INVALID_ARG, "page_size %d is not a multiple of logical_page %d", kv->page_size,
                     kv->logical_page);
-    if (kv->page_size % 32 != 0 || kv->page_size > 256 || !is_pow2(kv->page_size / kv->logical_page))
-        return fail(LSA_ERR_UNSUPPORTED, "page_size %d: need a multiple of 32, at most 256, with a power-of-two "
-                    "number of logical pages", kv->page_size);
+    if (kv->page_size < 16 || kv->page_size > 256 || !is_pow2(kv->page_size))
+        return fail(LSA_ERR_UNSUPPORTED, "page_size %d: need 16, 32, 64, 128 or 256", kv->page_size);
     if (kv->num_pages < 1) return fail(LSA_ERR_INVALID_ARG, "num_pages must be >= 1");
     if (!kv->k || !kv->v) return fail(LSA_ERR_INVALID_ARG, "kv->k and kv->v must be non-NULL");
     if (kv->kv_dtype == LSA_INT4) {

@@ -128,11 +128,11 @@ __device__ __forceinline__ bool token_visible(const DecodeArgs &a, const WorkIte
     return (p <= w.t) & (!w.streaming | (p < a.sink) | ((w.t - p) < a.local));
 }
 
-// Does the 32-token block starting at tok0 hold any attended token?
-__device__ __forceinline__ bool block_needed(const DecodeArgs &a, const WorkItem &w, int tok0) {
+// Does the run of n tokens starting at tok0 hold any attended token?
+__device__ __forceinline__ bool block_needed(const DecodeArgs &a, const WorkItem &w, int tok0, int n) {
     if (tok0 > w.t) return false;
     if (!w.streaming) return true;
-    const int p_last = min(tok0 + 31, w.t);
+    const int p_last = min(tok0 + n - 1, w.t);
     return tok0 < a.sink || (w.t - p_last) < a.local;
 }
 
@@ -153,7 +153,7 @@ __device__ __forceinline__ void refresh_current_stats(const DecodeArgs &a, const
         const uint8_t *k = static_cast<const uint8_t *>(a.k);
         uint32_t lo_min = 15, lo_max = 0, hi_min = 15, hi_max = 0;
         for (int r = 0; r < rows; ++r) {
-            const uint32_t byte = k[(page_base + key_offset(row0 + r, 2 * lane, D)) / 2];
+            const uint32_t byte = k[(page_base + key_offset(row0 + r, 2 * lane, D, block_shift(NP))) / 2];
             lo_min = min(lo_min, byte & 15u); lo_max = max(lo_max, byte & 15u);
             hi_min = min(hi_min, byte >> 4); hi_max = max(hi_max, byte >> 4);
         }
@@ -167,7 +167,7 @@ __device__ __forceinline__ void refresh_current_stats(const DecodeArgs &a, const
         float mn = __builtin_inff(), mx = -__builtin_inff();
         for (int r = 0; r < rows; ++r) {
             float x;
-            const size_t off = page_base + key_offset(row0 + r, ch, D);
+            const size_t off = page_base + key_offset(row0 + r, ch, D, block_shift(NP));
             if (kv_dtype == LSA_BF16)
                 x = bf16_to_f32(static_cast<const uint16_t *>(a.k)[off]);
             else
@@ -329,14 +329,18 @@ __device__ __forceinline__ uint32_t pick(const uint4 &u, int i) {
 // ---------------------------------------------------------------------------
 // MFMA kernel, bf16 or int4 pool, bf16 q
 // ---------------------------------------------------------------------------
-template <int D, int KVT, int NB>
+template <int D, int KVT, int NP>
 __global__ __launch_bounds__(kDecodeWaves * kWave, 2) void decode_mfma_kernel(DecodeArgs a) {
     constexpr bool I4 = KVT == LSA_INT4;
+    // 16-token pages: a 32-token block is two pages, QK^T tile T (and the
+    // value rows of lanes with g4 / 2 == T) coming from page 2i + T of block i
+    constexpr bool HALF = NP == 16;
+    constexpr int BS = block_shift(NP);   // log2 of the tokens per layout block
     constexpr int NS = D / 32;            // MFMA k-steps over channels
     constexpr int NDT = D / 16;           // output channel tiles
-    constexpr int NP = 32 * NB;           // page size
+    constexpr int NB = HALF ? 1 : NP / 32;   // 32-token blocks per page
     constexpr int PPW = decode_pages_per_wave(KVT, NP);
-    constexpr int NBW = PPW * NB;         // 32-token blocks per wavefront
+    constexpr int NBW = HALF ? PPW / 2 : PPW * NB;   // 32-token blocks per wavefront
     constexpr int CP = kDecodeWaves * PPW;
     constexpr int BIF = I4 ? (NBW < 4 ? NBW : 4) : 2;   // blocks in flight (ring size)
     extern __shared__ float lds[];
@@ -382,12 +386,30 @@ __global__ __launch_bounds__(kDecodeWaves * kWave, 2) void decode_mfma_kernel(De
         const int pool = __builtin_amdgcn_readfirstlane(s_list[2 + CP + PPW * wave + j]);
         hp[j] = (size_t)max(pool, 0) * a.num_kv_heads + w.kv;
     }
-    // block i of the wavefront: page slot i / NB, 32-token block i % NB of that page
+    // block i of the wavefront: page slot i / NB, 32-token block i % NB of that
+    // page; with 16-token pages, tile T of block i is page slot 2i + T.  For
+    // every (block, tile): whether it holds an attended token, and its first
+    // token position.
+    bool need_t[NBW][2];
+    int tok_t[NBW][2];
     bool need[NBW];
     bool any = false;
 #pragma unroll
     for (int i = 0; i < NBW; ++i) {
-        need[i] = pg[i / NB] >= 0 && block_needed(a, w, pg[i / NB] * NP + 32 * (i % NB));
+        if constexpr (HALF) {
+#pragma unroll
+            for (int T = 0; T < 2; ++T) {
+                tok_t[i][T] = pg[2 * i + T] * NP;
+                need_t[i][T] = pg[2 * i + T] >= 0 && block_needed(a, w, tok_t[i][T], NP);
+            }
+        } else {
+            const int tok0 = pg[i / NB] * NP + 32 * (i % NB);
+            const bool nd = pg[i / NB] >= 0 && block_needed(a, w, tok0, 32);
+            need_t[i][0] = need_t[i][1] = nd;
+            tok_t[i][0] = tok0;
+            tok_t[i][1] = tok0 + 16;
+        }
+        need[i] = need_t[i][0] | need_t[i][1];
         any |= need[i];
     }
 
@@ -416,8 +438,8 @@ __global__ __launch_bounds__(kDecodeWaves * kWave, 2) void decode_mfma_kernel(De
                 }
             }
         }
-        // source of each ring load: the block itself, or the first needed block
-        size_t src_hp[NBW];
+        // source of each ring load: the block (tile) itself, or the first needed one
+        size_t src_hp[NBW][2];
         int src_kb[NBW];
         {
             size_t f_hp = 0;
@@ -425,11 +447,18 @@ __global__ __launch_bounds__(kDecodeWaves * kWave, 2) void decode_mfma_kernel(De
             bool found = false;
 #pragma unroll
             for (int i = 0; i < NBW; ++i)
-                if (need[i] && !found) { f_hp = hp[i / NB]; f_kb = i % NB; found = true; }
+#pragma unroll
+                for (int T = 0; T < 2; ++T)
+                    if (need_t[i][T] && !found) {
+                        f_hp = hp[HALF ? 2 * i + T : i / NB];
+                        f_kb = HALF ? 0 : i % NB;
+                        found = true;
+                    }
 #pragma unroll
             for (int i = 0; i < NBW; ++i) {
-                src_hp[i] = need[i] ? hp[i / NB] : f_hp;
-                src_kb[i] = need[i] ? i % NB : f_kb;
+#pragma unroll
+                for (int T = 0; T < 2; ++T) src_hp[i][T] = need_t[i][T] ? hp[HALF ? 2 * i + T : i / NB] : f_hp;
+                src_kb[i] = need[i] ? (HALF ? 0 : i % NB) : f_kb;
             }
         }
 
@@ -438,13 +467,18 @@ __global__ __launch_bounds__(kDecodeWaves * kWave, 2) void decode_mfma_kernel(De
         uint32_t vr4[BIF][I4 ? NDT : 1];
         // ---- issue every K and V load of block i into ring slot e
         auto issue = [&](int e, int i) {
-            const size_t base = src_hp[i] * NP * D;
             const int kb = src_kb[i];
+            // key rows of tile T; the value rows this lane reads (tokens 8*g4 ..
+            // 8*g4 + 7 of the block: page 2i + g4/2, tokens 8*(g4%2).. with 16-token pages)
+            const size_t kbase[2] = {src_hp[i][0] * NP * D, src_hp[i][1] * NP * D};
+            const size_t vbase = HALF ? (g4 < 2 ? kbase[0] : kbase[1]) : kbase[0];
+            const int vtok = HALF ? 8 * (g4 & 1) : 32 * kb + 8 * g4;
             if constexpr (I4) {
                 const uint8_t *k8 = static_cast<const uint8_t *>(a.k);
 #pragma unroll
                 for (int T = 0; T < 2; ++T) {
-                    const uint8_t *row = k8 + (base + key_offset(32 * kb + 16 * T + rho, (D / 4) * g4, D)) / 2;
+                    const int row_tok = HALF ? rho : 32 * kb + 16 * T + rho;
+                    const uint8_t *row = k8 + (kbase[T] + key_offset(row_tok, (D / 4) * g4, D, BS)) / 2;
                     if constexpr (D == 128) {
                         kr[e][T][0] = load_stream16(row);
                     } else {
@@ -455,18 +489,20 @@ __global__ __launch_bounds__(kDecodeWaves * kWave, 2) void decode_mfma_kernel(De
                 const uint8_t *v8 = static_cast<const uint8_t *>(a.v);
 #pragma unroll
                 for (int dt = 0; dt < NDT; ++dt)
-                    vr4[e][dt] = load_stream4(v8 + (base + value_offset(32 * kb + 8 * g4, 16 * dt + h, D)) / 2);
+                    vr4[e][dt] = load_stream4(v8 + (vbase + value_offset(vtok, 16 * dt + h, D, BS)) / 2);
             } else {
-                const uint16_t *kp = static_cast<const uint16_t *>(a.k) + base;
+                const uint16_t *kp = static_cast<const uint16_t *>(a.k);
 #pragma unroll
-                for (int T = 0; T < 2; ++T)
+                for (int T = 0; T < 2; ++T) {
+                    const int row_tok = HALF ? rho : 32 * kb + 16 * T + rho;
 #pragma unroll
                     for (int s = 0; s < NS; ++s)
-                        kr[e][T][s] = load_stream16(kp + key_offset(32 * kb + 16 * T + rho, 32 * s + 8 * g4, D));
-                const uint16_t *vp = static_cast<const uint16_t *>(a.v) + base;
+                        kr[e][T][s] = load_stream16(kp + kbase[T] + key_offset(row_tok, 32 * s + 8 * g4, D, BS));
+                }
+                const uint16_t *vp = static_cast<const uint16_t *>(a.v) + vbase;
 #pragma unroll
                 for (int dt = 0; dt < NDT; ++dt)
-                    vr[e][dt] = load_stream16(vp + value_offset(32 * kb + 8 * g4, 16 * dt + h, D));
+                    vr[e][dt] = load_stream16(vp + value_offset(vtok, 16 * dt + h, D, BS));
             }
             // keep the block's loads ahead of the compute that follows them
             __builtin_amdgcn_sched_barrier(0);
@@ -476,9 +512,8 @@ __global__ __launch_bounds__(kDecodeWaves * kWave, 2) void decode_mfma_kernel(De
         // holds another block's data); there is no branch around it, so the
         // compiler keeps every ring load where it is issued.
         auto consume = [&](int e, int i) {
-            const bool blk = need[i];
-            const int j = i / NB;
-            const int tok0 = pg[j] * NP + 32 * (i % NB);
+            // the page slot of each tile (for the int4 scale and zero point)
+            const int jt[2] = {HALF ? 2 * i : i / NB, HALF ? 2 * i + 1 : i / NB};
             // scores of the 32 keys (two 16-row tiles)
             floatx4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -499,10 +534,10 @@ __global__ __launch_bounds__(kDecodeWaves * kWave, 2) void decode_mfma_kernel(De
             // 16 + 4*g4 + r (x[4 + r]) of the block, r = 0..3
             float x[8];
             if constexpr (I4) {
-                const float off = (128.f + zk[j]) * qsum;
-                const float sc = sk[j] * a.scale_log2;
+                const float off0 = (128.f + zk[jt[0]]) * qsum, off1 = (128.f + zk[jt[1]]) * qsum;
+                const float sc0 = sk[jt[0]] * a.scale_log2, sc1 = sk[jt[1]] * a.scale_log2;
 #pragma unroll
-                for (int r = 0; r < 4; ++r) { x[r] = (s0[r] - off) * sc; x[4 + r] = (s1[r] - off) * sc; }
+                for (int r = 0; r < 4; ++r) { x[r] = (s0[r] - off0) * sc0; x[4 + r] = (s1[r] - off1) * sc1; }
             } else {
 #pragma unroll
                 for (int r = 0; r < 4; ++r) { x[r] = s0[r] * a.scale_log2; x[4 + r] = s1[r] * a.scale_log2; }
@@ -510,7 +545,8 @@ __global__ __launch_bounds__(kDecodeWaves * kWave, 2) void decode_mfma_kernel(De
             float mb = -__builtin_inff();
 #pragma unroll
             for (int jj = 0; jj < 8; ++jj) {
-                const bool vis = blk & token_visible(a, w, tok0 + 4 * g4 + (jj & 3) + 16 * (jj >> 2));
+                const int T = jj >> 2;
+                const bool vis = need_t[i][T] & token_visible(a, w, tok_t[i][T] + 4 * g4 + (jj & 3));
                 x[jj] = vis ? x[jj] : -__builtin_inff();        // a select, not a branch
                 mb = fmaxf(mb, x[jj]);
             }
@@ -519,7 +555,7 @@ __global__ __launch_bounds__(kDecodeWaves * kWave, 2) void decode_mfma_kernel(De
             // reference of the exponentials: any finite value while nothing is visible yet
             const float m_ref = m_new == -__builtin_inff() ? 0.f : m_new;
             const float alpha = exp2_fast(m_run - m_ref);
-            float psum = 0.f, fed = 0.f;
+            float psum = 0.f, fed[2] = {0.f, 0.f};
             uint32_t pk[4];
 #pragma unroll
             for (int jj = 0; jj < 8; jj += 2) {
@@ -528,9 +564,10 @@ __global__ __launch_bounds__(kDecodeWaves * kWave, 2) void decode_mfma_kernel(De
                 psum += pa + pb;
                 uint16_t ba, bb;
                 if constexpr (I4) {
-                    ba = f32_to_bf16_rne(pa * sv[j]);
-                    bb = f32_to_bf16_rne(pb * sv[j]);
-                    fed += bf16_to_f32(ba) + bf16_to_f32(bb);
+                    const float svt = sv[jt[jj >> 2]];
+                    ba = f32_to_bf16_rne(pa * svt);
+                    bb = f32_to_bf16_rne(pb * svt);
+                    fed[jj >> 2] += bf16_to_f32(ba) + bf16_to_f32(bb);
                 } else {
                     ba = f32_to_bf16_rne(pa);
                     bb = f32_to_bf16_rne(pb);
@@ -538,7 +575,7 @@ __global__ __launch_bounds__(kDecodeWaves * kWave, 2) void decode_mfma_kernel(De
                 pk[jj / 2] = uint32_t(ba) | (uint32_t(bb) << 16);
             }
             l_run = l_run * alpha + psum;
-            if constexpr (I4) corr = corr * alpha + (128.f + zv[j]) * fed;
+            if constexpr (I4) corr = corr * alpha + (128.f + zv[jt[0]]) * fed[0] + (128.f + zv[jt[1]]) * fed[1];
             m_run = m_new;
             // The PV operand of lane (h, g4) wants tokens 8*g4 .. 8*g4 + 7.  Swapping
             // the upper 32 lanes of pk[0..1] (tokens 4*g4 + r) with the lower 32
@@ -556,8 +593,9 @@ __global__ __launch_bounds__(kDecodeWaves * kWave, 2) void decode_mfma_kernel(De
             const bf16x8 pbv = __builtin_bit_cast(bf16x8, make_uint4(pv[0], pv[1], pv[2], pv[3]));
             // slots after the current token may hold any bits: zero their values so a
             // zero probability never meets a NaN in the PV product
-            const bool tail = !blk || tok0 + 31 > w.t;
-            const int nvalid = blk ? w.t - (tok0 + 8 * g4) + 1 : 0;
+            const bool tail = !(need_t[i][0] & need_t[i][1]) || max(tok_t[i][0], tok_t[i][1]) + 15 > w.t;
+            const int vt = HALF ? g4 >> 1 : 0;       // the tile whose tokens this lane's value rows hold
+            const int nvalid = need_t[i][vt] ? w.t - (tok_t[i][vt] + (HALF ? 8 * (g4 & 1) : 8 * g4)) + 1 : 0;
             uint32_t keep[4] = {~0u, ~0u, ~0u, ~0u};
             if (tail) {
 #pragma unroll
@@ -644,6 +682,7 @@ __global__ __launch_bounds__(256) void decode_f32_kernel(DecodeArgs a) {
 
     const float *kpool = static_cast<const float *>(a.k);
     const float *vpool = static_cast<const float *>(a.v);
+    const int bs = block_shift(NP);
 
     if (my_page >= 0) {
         const int page = my_page;
@@ -659,7 +698,7 @@ __global__ __launch_bounds__(256) void decode_f32_kernel(DecodeArgs a) {
             for (int hh = 0; hh < 16; ++hh) sc[hh] = 0.f;
             if (slot < NP) {
                 for (int d = 0; d < D; d += 4) {
-                    const float4 kv4 = *reinterpret_cast<const float4 *>(kp + key_offset(slot, d, D));
+                    const float4 kv4 = *reinterpret_cast<const float4 *>(kp + key_offset(slot, d, D, bs));
 #pragma unroll
                     for (int hh = 0; hh < 16; ++hh) {
                         if (hh < G) {
@@ -697,7 +736,7 @@ __global__ __launch_bounds__(256) void decode_f32_kernel(DecodeArgs a) {
 #pragma unroll
                 for (int hh = 0; hh < 16; ++hh) acc[hh] = o[hh][c] * alpha[hh];
                 for (int sl = 0; sl < nslots; ++sl) {
-                    const float vv = vp[value_offset(s0 + sl, d, D)];
+                    const float vv = vp[value_offset(s0 + sl, d, D, bs)];
 #pragma unroll
                     for (int hh = 0; hh < 16; ++hh)
                         if (hh < G) acc[hh] = fmaf(ps[hh * 64 + sl], vv, acc[hh]);
@@ -731,10 +770,11 @@ hipError_t launch_mfma(const DecodeArgs &a, unsigned grid, hipStream_t s) {
     const size_t lds = kDecodeWaves * (32 + 16 * (size_t)D) * sizeof(float);
     const dim3 block(kDecodeWaves * kWave);
     switch (a.page_size) {
-        case 32: hipLaunchKernelGGL((decode_mfma_kernel<D, KVT, 1>), dim3(grid), block, lds, s, a); break;
-        case 64: hipLaunchKernelGGL((decode_mfma_kernel<D, KVT, 2>), dim3(grid), block, lds, s, a); break;
-        case 128: hipLaunchKernelGGL((decode_mfma_kernel<D, KVT, 4>), dim3(grid), block, lds, s, a); break;
-        case 256: hipLaunchKernelGGL((decode_mfma_kernel<D, KVT, 8>), dim3(grid), block, lds, s, a); break;
+        case 16: hipLaunchKernelGGL((decode_mfma_kernel<D, KVT, 16>), dim3(grid), block, lds, s, a); break;
+        case 32: hipLaunchKernelGGL((decode_mfma_kernel<D, KVT, 32>), dim3(grid), block, lds, s, a); break;
+        case 64: hipLaunchKernelGGL((decode_mfma_kernel<D, KVT, 64>), dim3(grid), block, lds, s, a); break;
+        case 128: hipLaunchKernelGGL((decode_mfma_kernel<D, KVT, 128>), dim3(grid), block, lds, s, a); break;
+        case 256: hipLaunchKernelGGL((decode_mfma_kernel<D, KVT, 256>), dim3(grid), block, lds, s, a); break;
         default: return hipErrorInvalidValue;
     }
     return hipSuccess;

@@ -18,7 +18,7 @@ constexpr int kMaxDecodeChunks = 128;   // split-KV chunks per (sequence, KV hea
 // longer); the f32 path runs four wavefronts of one page each.  A workgroup
 // takes one chunk of the attended page list.
 constexpr int kDecodeWaves = 4;
-constexpr int kMaxChunkPages = 16;
+constexpr int kMaxChunkPages = 32;
 constexpr int kDecodeWaveTokens = 128;
 // XCDs of the part; workgroups are handed to them round robin in number order
 constexpr int kXcds = 8;
@@ -78,16 +78,18 @@ __device__ __forceinline__ uint32_t load_stream4(const void *p) {
 }
 
 // ----------------------------------------------------------------------------
-// page layout: a page of N_P tokens of one KV head is N_P/32 blocks of 32
-// tokens; keys are [block][D/32][32 tokens][32 channels] tiles, values are
-// [block][D][32 tokens] rows.  Offsets are in elements (int4: halve for the
-// byte of an even channel / token).
+// page layout: a page of N_P tokens of one KV head is a run of blocks of BT =
+// min(N_P, 32) tokens (N_P/32 blocks of 32, or one block of 16 for 16-token
+// pages); keys are [block][D/32][BT tokens][32 channels] tiles, values are
+// [block][D][BT tokens] rows.  Offsets are in elements (int4: halve for the
+// byte of an even channel / token).  bs = log2(BT).
 // ----------------------------------------------------------------------------
-__device__ __forceinline__ size_t key_offset(int s, int c, int D) {
-    return ((size_t)(s >> 5) * (D >> 5) + (c >> 5)) * 1024 + (size_t)(s & 31) * 32 + (c & 31);
+__host__ __device__ constexpr int block_shift(int page_size) { return page_size < 32 ? 4 : 5; }
+__device__ __forceinline__ size_t key_offset(int s, int c, int D, int bs = 5) {
+    return (((size_t)(s >> bs) * (D >> 5) + (c >> 5)) << (bs + 5)) + (size_t)(s & ((1 << bs) - 1)) * 32 + (c & 31);
 }
-__device__ __forceinline__ size_t value_offset(int s, int c, int D) {
-    return (size_t)(s >> 5) * D * 32 + (size_t)c * 32 + (s & 31);
+__device__ __forceinline__ size_t value_offset(int s, int c, int D, int bs = 5) {
+    return (((size_t)(s >> bs) * D + c) << bs) + (s & ((1 << bs) - 1));
 }
 
 // ----------------------------------------------------------------------------

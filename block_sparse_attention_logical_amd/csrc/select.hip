@@ -113,6 +113,7 @@ __device__ __forceinline__ void current_page_minmax(const ScoreArgs &a, size_t p
                                                     int ch0, float (&kmin)[C], float (&kmax)[C]) {
 #pragma unroll
     for (int c = 0; c < C; ++c) { kmin[c] = __builtin_inff(); kmax[c] = -__builtin_inff(); }
+    const int bs = block_shift(a.page_size);
     constexpr int RB = 4;                       // rows per lane and batch, loaded together
     for (int r0 = 0; r0 < rows; r0 += RB * LPP) {
         if constexpr (KV_DT == LSA_INT4) {
@@ -121,7 +122,7 @@ __device__ __forceinline__ void current_page_minmax(const ScoreArgs &a, size_t p
             for (int i = 0; i < RB; ++i) {
                 const int rr = r0 + q + i * LPP;
                 u[i] = rr < rows ? *reinterpret_cast<const uint2 *>(static_cast<const uint8_t *>(a.k) +
-                                                                    (page_base + key_offset(row0 + rr, ch0, D)) / 2)
+                                                                    (page_base + key_offset(row0 + rr, ch0, D, bs)) / 2)
                                  : make_uint2(0xFFFFFFFFu, 0xFFFFFFFFu);
             }
 #pragma unroll
@@ -141,7 +142,7 @@ __device__ __forceinline__ void current_page_minmax(const ScoreArgs &a, size_t p
             for (int i = 0; i < RB; ++i) {
                 const int rr = r0 + q + i * LPP;
                 u[i] = rr < rows ? *reinterpret_cast<const uint4 *>(static_cast<const char *>(a.k) +
-                                                                    (page_base + key_offset(row0 + rr, ch0, D)) *
+                                                                    (page_base + key_offset(row0 + rr, ch0, D, bs)) *
                                                                         (KV_DT == LSA_F32 ? 4 : 2))
                                  : make_uint4(0, 0, 0, 0);
             }

@@ -57,7 +57,7 @@ __global__ __launch_bounds__(256) void stats_float_kernel(StatsArgs a) {
 #pragma unroll
     for (int c = 0; c < CPL; ++c) { mn[c] = __builtin_inff(); mx[c] = -__builtin_inff(); }
     for (int r = 0; r < it.rows; ++r) {
-        const Elem *row = k + page_base + key_offset(it.row0 + r, lane * CPL, D);
+        const Elem *row = k + page_base + key_offset(it.row0 + r, lane * CPL, D, block_shift(a.page_size));
 #pragma unroll
         for (int c = 0; c < CPL; ++c) {
             float x;
@@ -95,7 +95,7 @@ __global__ __launch_bounds__(256) void stats_int4_kernel(StatsArgs a) {
     const uint8_t *k = static_cast<const uint8_t *>(a.k);
     uint32_t lo_min = 15, lo_max = 0, hi_min = 15, hi_max = 0;
     for (int r = 0; r < it.rows; ++r) {
-        const uint32_t byte = k[(page_base + key_offset(it.row0 + r, 2 * lane, D)) / 2];
+        const uint32_t byte = k[(page_base + key_offset(it.row0 + r, 2 * lane, D, block_shift(a.page_size))) / 2];
         const uint32_t lo = byte & 15u, hi = byte >> 4;
         lo_min = min(lo_min, lo); lo_max = max(lo_max, lo);
         hi_min = min(hi_min, hi); hi_max = max(hi_max, hi);

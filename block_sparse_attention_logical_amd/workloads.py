@@ -29,9 +29,9 @@ clamped to [0, 15], so (c - z) * s is exact in fp32; codes
 c = clamp(round(x / s + z), 0, 15); keys packed two channels per byte (even
 channel in the low nibble), values two tokens per byte.
 
-Every pool is written in the library's page layout: keys as 32 x 32 tiles
-[P][H_kv][N_P/32][D/32][32][32], values as rows [P][H_kv][N_P/32][D][32]
-(int4: the same with code pairs packed into bytes).
+Every pool is written in the library's page layout: keys as BT x 32 tiles
+[P][H_kv][N_P/BT][D/32][BT][32], values as rows [P][H_kv][N_P/BT][D][BT],
+BT = min(N_P, 32) (int4: the same with code pairs packed into bytes).
 """
 from __future__ import annotations
 
@@ -172,15 +172,18 @@ def pack_int4(c: torch.Tensor) -> torch.Tensor:
 
 
 def tile_keys(x: torch.Tensor) -> torch.Tensor:
-    """Keys [..., N_P, D] of pages -> the pool's key tiles [..., N_P/32, D/32, 32, 32]."""
+    """Keys [..., N_P, D] of pages -> the pool's key tiles [..., N_P/BT, D/32, BT, 32],
+    BT = min(N_P, 32)."""
     *lead, NP, D = x.shape
-    return x.reshape(*lead, NP // 32, 32, D // 32, 32).transpose(-3, -2).contiguous()
+    bt = min(NP, 32)
+    return x.reshape(*lead, NP // bt, bt, D // 32, 32).transpose(-3, -2).contiguous()
 
 
 def tile_values(x: torch.Tensor) -> torch.Tensor:
-    """Values [..., D, N_P] (channel-major) of pages -> the pool's value rows [..., N_P/32, D, 32]."""
+    """Values [..., D, N_P] (channel-major) of pages -> the pool's value rows [..., N_P/BT, D, BT]."""
     *lead, D, NP = x.shape
-    return x.reshape(*lead, D, NP // 32, 32).transpose(-3, -2).contiguous()
+    bt = min(NP, 32)
+    return x.reshape(*lead, D, NP // bt, bt).transpose(-3, -2).contiguous()
 
 
 def make_decode(cfg: int, device="cpu", *, batch: Optional[int] = None, ctx=None, window: Optional[int] = None,
@@ -243,11 +246,12 @@ def make_decode(cfg: int, device="cpu", *, batch: Optional[int] = None, ctx=None
         kscale.scatter_(1, outl, 8.0)
 
     # keys, as tiles [P][H_kv][N_P/32][D/32][32][32] (int4: codes packed in pairs)
+    bt = min(NP, 32)                  # tokens per layout block
     if dt == INT4:
-        k = torch.empty((P, H_kv, NP // 32, D // 32, 32, 16), dtype=torch.uint8, device=device)
+        k = torch.empty((P, H_kv, NP // bt, D // 32, bt, 16), dtype=torch.uint8, device=device)
         k_sz = torch.empty((P, H_kv, 2), dtype=torch.float16, device=device)
     else:
-        k = torch.empty((P, H_kv, NP // 32, D // 32, 32, 32), dtype=qdt, device=device)
+        k = torch.empty((P, H_kv, NP // bt, D // 32, bt, 32), dtype=qdt, device=device)
         k_sz = None
     for p0 in range(0, P, chunk_pages):
         p1 = min(P, p0 + chunk_pages)
@@ -266,10 +270,10 @@ def make_decode(cfg: int, device="cpu", *, batch: Optional[int] = None, ctx=None
     # values, drawn channel-major per page ([D][N_P]) and stored as rows
     # [P][H_kv][N_P/32][D][32] (int4: token codes packed in pairs)
     if dt == INT4:
-        v = torch.empty((P, H_kv, NP // 32, D, 16), dtype=torch.uint8, device=device)
+        v = torch.empty((P, H_kv, NP // bt, D, bt // 2), dtype=torch.uint8, device=device)
         v_sz = torch.empty((P, H_kv, 2), dtype=torch.float16, device=device)
     else:
-        v = torch.empty((P, H_kv, NP // 32, D, 32), dtype=qdt, device=device)
+        v = torch.empty((P, H_kv, NP // bt, D, bt), dtype=qdt, device=device)
         v_sz = None
     for p0 in range(0, P, chunk_pages):
         p1 = min(P, p0 + chunk_pages)

@@ -35,25 +35,26 @@
  *   - Device-side contents are trusted: page ids outside [0, num_pages),
  *     seq_lens above max_pages * page_size or selected pages beyond the
  *     sequence are undefined behaviour.
- *   - Supported shapes: head_dim 64 or 128; page_size a multiple of
- *     logical_page; logical_page in {8, 16, 32, 64}; page_size <= 256 and a
- *     multiple of 32; num_q_heads a multiple of num_kv_heads with group size
+ *   - Supported shapes: head_dim 64 or 128; page_size in {16, 32, 64, 128,
+ *     256} and a multiple of logical_page; logical_page in {8, 16, 32, 64};
+ *     num_q_heads a multiple of num_kv_heads with group size
  *     G = num_q_heads / num_kv_heads <= 16.  Query head h uses KV head h / G.
  *
  * Paged KV pool layout (caller-owned, fixed).  A page holds page_size tokens
- * of one KV head as page_size/32 blocks of 32 consecutive tokens; inside a
- * block, keys are tiles of 32 tokens x 32 channels and values are
- * channel-major rows of 32 tokens:
- *   K, f32/bf16:  [num_pages][H_kv][page_size/32][head_dim/32][32][32]
+ * of one KV head as page_size/BT blocks of BT consecutive tokens, BT =
+ * min(page_size, 32) (one block of 16 tokens for 16-token pages); inside a
+ * block, keys are tiles of BT tokens x 32 channels and values are
+ * channel-major rows of BT tokens:
+ *   K, f32/bf16:  [num_pages][H_kv][page_size/BT][head_dim/32][BT][32]
  *                 key (token p, channel c) of a page at
- *                 [p/32][c/32][p%32][c%32]
- *   V, f32/bf16:  [num_pages][H_kv][page_size/32][head_dim][32]
- *                 value (p, c) at [p/32][c][p%32]
- *   K, int4:      [num_pages][H_kv][page_size/32][head_dim/32][32][16] bytes:
+ *                 [p/BT][c/32][p%BT][c%32]
+ *   V, f32/bf16:  [num_pages][H_kv][page_size/BT][head_dim][BT]
+ *                 value (p, c) at [p/BT][c][p%BT]
+ *   K, int4:      [num_pages][H_kv][page_size/BT][head_dim/32][BT][16] bytes:
  *                 the K tile with channels 2i, 2i+1 of a tile row packed in
  *                 byte i (2i in the low nibble)
- *   V, int4:      [num_pages][H_kv][page_size/32][head_dim][16] bytes: the V
- *                 rows with tokens 2j, 2j+1 packed in byte j (2j low nibble)
+ *   V, int4:      [num_pages][H_kv][page_size/BT][head_dim][BT/2] bytes: the
+ *                 V rows with tokens 2j, 2j+1 packed in byte j (2j low nibble)
  *   k_sz, v_sz:   int4 only, [num_pages][H_kv][2] IEEE fp16 {scale s, zero z},
  *                 s > 0; a stored code c means (c - z) * s.
  *   Every 16-byte group a kernel loads is a run of one tile row, so the

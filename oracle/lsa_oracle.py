@@ -23,14 +23,14 @@ that takes it (readings Z1..Z27, listed together in the design notes of the
 repository).
 
 Data conventions (the layout of the caller-owned paged KV pool; a page is
-N_P/32 blocks of 32 consecutive tokens):
-  * K  (f32 / bf16): [P][H_kv][N_P/32][D/32][32][32]   key (p, c) of a page at
-                     [p // 32][c // 32][p % 32][c % 32]
-  * V  (f32 / bf16): [P][H_kv][N_P/32][D][32]          value (p, c) at
-                     [p // 32][c][p % 32]
-  * K  (int4):       [P][H_kv][N_P/32][D/32][32][16] u8, the K tiles with
+N_P/BT blocks of BT = min(N_P, 32) consecutive tokens):
+  * K  (f32 / bf16): [P][H_kv][N_P/BT][D/32][BT][32]   key (p, c) of a page at
+                     [p // BT][c // 32][p % BT][c % 32]
+  * V  (f32 / bf16): [P][H_kv][N_P/BT][D][BT]          value (p, c) at
+                     [p // BT][c][p % BT]
+  * K  (int4):       [P][H_kv][N_P/BT][D/32][BT][16] u8, the K tiles with
                      channels 2i, 2i+1 of a row in byte i (2i in the low nibble)
-  * V  (int4):       [P][H_kv][N_P/32][D][16] u8, the V rows with tokens 2j,
+  * V  (int4):       [P][H_kv][N_P/BT][D][BT/2] u8, the V rows with tokens 2j,
                      2j+1 in byte j (2j in the low nibble)
   * k_sz, v_sz:      [P][H_kv][2] fp16 bits   (scale s, zero z); x = (c - z) * s
   * bf16 arrays are passed as uint16 bit patterns, fp16 as uint16 bit patterns.
@@ -98,13 +98,15 @@ class Pool:
     v_sz: Optional[np.ndarray] = None
 
     def _untile_k(self, a: np.ndarray) -> np.ndarray:
-        """[N_P/32][D/32][32][32] key tiles of one page -> [N_P][D]."""
-        a = np.asarray(a).reshape(self.page_size // 32, self.head_dim // 32, 32, 32)
+        """[N_P/BT][D/32][BT][32] key tiles of one page -> [N_P][D]."""
+        bt = min(self.page_size, 32)
+        a = np.asarray(a).reshape(self.page_size // bt, self.head_dim // 32, bt, 32)
         return a.transpose(0, 2, 1, 3).reshape(self.page_size, self.head_dim)
 
     def _untile_v(self, a: np.ndarray) -> np.ndarray:
-        """[N_P/32][D][32] value rows of one page -> [N_P][D]."""
-        a = np.asarray(a).reshape(self.page_size // 32, self.head_dim, 32)
+        """[N_P/BT][D][BT] value rows of one page -> [N_P][D]."""
+        bt = min(self.page_size, 32)
+        a = np.asarray(a).reshape(self.page_size // bt, self.head_dim, bt)
         return a.transpose(0, 2, 1).reshape(self.page_size, self.head_dim)
 
     def _page_codes_k(self, page: int, kv: int) -> np.ndarray:

@@ -83,7 +83,9 @@ def test_stats_bytes_sizes(lib):
     (dict(D=96), lsa.LSA_ERR_UNSUPPORTED),
     (dict(NP=48, NL=16), lsa.LSA_ERR_UNSUPPORTED),      # 3 logical pages: not a power of two
     (dict(NP=64, NL=24), lsa.LSA_ERR_UNSUPPORTED),
-    (dict(NP=40, NL=8), lsa.LSA_ERR_UNSUPPORTED),       # not a multiple of 32
+    (dict(NP=40, NL=8), lsa.LSA_ERR_UNSUPPORTED),       # not a power of two
+    (dict(NP=96, NL=32), lsa.LSA_ERR_UNSUPPORTED),
+    (dict(NP=16, NL=32), lsa.LSA_ERR_INVALID_ARG),      # logical page longer than the page
     (dict(NP=8, NL=16), lsa.LSA_ERR_INVALID_ARG),
     (dict(heads=0), lsa.LSA_ERR_UNSUPPORTED),
     (dict(heads=65), lsa.LSA_ERR_UNSUPPORTED),
@@ -297,3 +299,11 @@ def test_decode_noalloc_validation(lib):
     assert call(B=128) == lsa.LSA_ERR_UNSUPPORTED
     assert "16777216-byte static scratch" in lsa.last_error()
     assert call(B=0) == lsa.LSA_OK                      # an empty batch launches nothing
+
+
+@pytest.mark.parametrize("NP,NL", [(16, 16), (16, 8), (32, 16), (256, 16)])
+def test_kv_page_sizes_accepted(lib, NP, NL):
+    """16-token pages (one 16-token layout block) and 32..256-token pages."""
+    st, nbytes = stats_bytes(lib, kv_desc(NP=NP, NL=NL))
+    assert st == lsa.LSA_OK
+    assert nbytes == 100 * 8 * (NP // NL) * 2 * 128 * 2

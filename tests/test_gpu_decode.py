@@ -279,14 +279,21 @@ def test_decode_reuse_interval(R):
     print("max abs err", check_window(w, kv_heads=ret + st))
 
 
-@pytest.mark.parametrize("NP,NL", [(32, 16), (32, 32), (128, 16), (128, 64), (256, 32), (256, 16)])
-def test_decode_page_geometry(NP, NL):
-    """The config 2 layer with other physical / logical page sizes (g = N_P /
-    N_L from 1 to 16; the same 4096-token budget): the window's outputs match
-    the oracle and the statistics refreshed by the decode calls equal a full
-    build."""
+@pytest.mark.parametrize("cfg,NP,NL", [(2, 16, 16), (2, 16, 8), (2, 32, 16), (2, 32, 32), (2, 128, 16),
+                                        (2, 128, 64), (2, 256, 32), (2, 256, 16), (5, 16, 16), (5, 16, 8),
+                                        (5, 32, 16), (1, 16, 16)])
+def test_decode_page_geometry(cfg, NP, NL):
+    """The config 2 layer (and the int4 config 5 and f32 config 1 layers) with
+    other physical / logical page sizes, down to Quest's 16-token pages (g =
+    N_P / N_L from 1 to 16; the same token budget, so 256 pages of 16 tokens):
+    the window's selections match the oracle bit for bit and its outputs within
+    the tolerance, and the statistics refreshed by the decode calls equal a
+    full build."""
     import tests.test_gpu_stats_select as S
-    w = W.make_decode(2, DEV, batch=2, ctx=[6000, 9000], page_size=NP, logical_page=NL)
+    if cfg == 1:
+        w = W.make_decode(1, DEV, page_size=NP, logical_page=NL)
+    else:
+        w = W.make_decode(cfg, DEV, batch=2, ctx=[6000, 9000], page_size=NP, logical_page=NL)
     ret = [kv for kv in range(w.num_kv_heads) if w.head_kind[kv] == 0][:2]
     st = [kv for kv in range(w.num_kv_heads) if w.head_kind[kv] == 1][:1]
     print("max abs err", check_window(w, kv_heads=ret + st))

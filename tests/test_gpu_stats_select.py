@@ -64,6 +64,8 @@ def check_stats(w, stats, lens, kinds=None):
 
 CASES = [
     ("cfg1-f32", lambda: W.make_decode(1, DEV)),
+    ("cfg2-bf16-np16", lambda: W.make_decode(2, DEV, batch=2, ctx=[1000, 4100], page_size=16, logical_page=16)),
+    ("cfg5-int4-np16-nl8", lambda: W.make_decode(5, DEV, batch=2, ctx=[2100, 5000], page_size=16, logical_page=8)),
     ("cfg2-bf16-small", lambda: W.make_decode(2, DEV, batch=3, ctx=[1000, 2500, 4096])),
     ("cfg4-bf16-np128-small", lambda: W.make_decode(4, DEV, batch=3, ctx=(1500, 6000))),
     ("cfg5-int4-small", lambda: W.make_decode(5, DEV, batch=2, ctx=[2100, 3333])),

@@ -442,25 +442,28 @@ def test_conversions_exact():
     assert O.unpack_int4(np.array([[0x21, 0xF3]], np.uint8)).tolist() == [[1, 2, 3, 15]]
 
 
-def test_pool_gather_follows_page_table():
+@pytest.mark.parametrize("NP", [64, 16])
+def test_pool_gather_follows_page_table(NP):
     """Token p, channel c of a sequence sits in pool page table[p // N_P] at
-    key tile [s // 32][c // 32][s % 32][c % 32] and value row [s // 32][c][s % 32]
-    with s = p % N_P (the header's layout statement), element by element."""
+    key tile [s // BT][c // 32][s % BT][c % 32] and value row [s // BT][c][s % BT]
+    with s = p % N_P and BT = min(N_P, 32) (the header's layout statement),
+    element by element, for 32-token blocks and for 16-token pages."""
     rng = np.random.default_rng(10)
-    P, H, NP, D = 5, 2, 64, 64
-    k = rng.standard_normal((P, H, NP // 32, D // 32, 32, 32)).astype(np.float32)
-    v = rng.standard_normal((P, H, NP // 32, D, 32)).astype(np.float32)
+    P, H, D = 5, 2, 64
+    bt = min(NP, 32)
+    k = rng.standard_normal((P, H, NP // bt, D // 32, bt, 32)).astype(np.float32)
+    v = rng.standard_normal((P, H, NP // bt, D, bt)).astype(np.float32)
     pool = O.Pool("f32", k, v, NP, D)
     table = [3, 0, 4]
-    L = 150
+    L = 2 * NP + NP // 2 + 3
     K = pool.keys(table, 1, L)
     V = pool.values(table, 1, L)
     assert K.shape == (L, D) and V.shape == (L, D)
     for p in range(L):
         pg, sl = table[p // NP], p % NP
         for c in range(D):
-            assert K[p, c] == k[pg, 1, sl // 32, c // 32, sl % 32, c % 32]
-            assert V[p, c] == v[pg, 1, sl // 32, c, sl % 32]
+            assert K[p, c] == k[pg, 1, sl // bt, c // 32, sl % bt, c % 32]
+            assert V[p, c] == v[pg, 1, sl // bt, c, sl % bt]
 
 
 def test_pool_int4_codes_follow_layout():
