@@ -19,7 +19,7 @@ INCLUDE = os.path.join(ROOT, "include")
 OUT = os.path.join(PKG, "liblsa.so")
 OBJ_DIR = os.path.join(PKG, "_build")
 
-SOURCES = ["abi.hip", "stats.hip", "select.hip", "decode.hip", "prefill.hip"]
+SOURCES = ["abi.hip", "stats.hip", "select.hip", "decode.hip", "prefill.hip", "append.hip"]
 
 ARCH = os.environ.get("LSA_OFFLOAD_ARCH", "gfx950")
 

@@ -105,6 +105,45 @@ int count_kind(const lsa_heads *hd, int h_kv, int kind) {
     return n;
 }
 
+// Head slots of the pool: every KV head, or only the retrieval heads (in
+// KV-head order) when the streaming heads live in a stream cache; and the
+// rank of each streaming head among the streaming heads.
+void pool_heads_of(const lsa_kv *kv, const lsa_heads *hd, PoolHeads &ph, int *n_str = nullptr,
+                   uint8_t *str_slot = nullptr) {
+    int r = 0, st = 0;
+    for (int i = 0; i < kv->num_kv_heads; ++i) {
+        const bool ret = !hd || hd->head_kind[i] == LSA_RETRIEVAL_HEAD;
+        ph.pool_slot[i] = (uint8_t)(kv->stream_cache ? (ret ? r : 0) : i);
+        if (str_slot) str_slot[i] = (uint8_t)(ret ? 0 : st);
+        r += ret;
+        st += !ret;
+    }
+    ph.pool_heads = kv->stream_cache ? r : kv->num_kv_heads;
+    if (n_str) *n_str = st;
+}
+
+lsa_status check_stream_cache(const lsa_stream_cache *sc, const lsa_kv *kv, const lsa_heads *hd) {
+    if (!hd) return fail(LSA_ERR_INVALID_ARG, "a pool with a stream cache needs the head classification");
+    if (sc->sink_pages < 0 || sc->ring_pages < 1)
+        return fail(LSA_ERR_INVALID_ARG, "stream cache: sink_pages %d, ring_pages %d", sc->sink_pages, sc->ring_pages);
+    const int NP = kv->page_size;
+    const int need_sink = (hd->sink_tokens + NP - 1) / NP, need_ring = (hd->local_tokens + NP - 1) / NP + 1;
+    if (sc->sink_pages < need_sink || sc->ring_pages < need_ring)
+        return fail(LSA_ERR_INVALID_ARG,
+                    "stream cache of %d sink + %d ring pages cannot hold %d sink + %d local tokens (need %d + %d)",
+                    sc->sink_pages, sc->ring_pages, hd->sink_tokens, hd->local_tokens, need_sink, need_ring);
+    if (!sc->k || !sc->v) return fail(LSA_ERR_INVALID_ARG, "stream cache k and v must be non-NULL");
+    if ((kv->kv_dtype == LSA_INT4) != (sc->k_sz != nullptr && sc->v_sz != nullptr))
+        return fail(LSA_ERR_INVALID_ARG, "stream cache k_sz / v_sz are needed for int4 pools and only for them");
+    return LSA_OK;
+}
+
+// Validation of a pool descriptor together with the head classification.
+lsa_status check_pool(const lsa_kv *kv, const lsa_heads *hd) {
+    if (kv->stream_cache) return check_stream_cache(kv->stream_cache, kv, hd);
+    return LSA_OK;
+}
+
 struct DecodeGeom {
     int K, chunks_ret, chunks_str, chunks_max, rec_floats;
 };
@@ -131,6 +170,8 @@ lsa_status prefill_setup(PrefillArgs &p, const void *q, int32_t q_dtype, const l
                          int32_t seq_len, int32_t num_q_heads, int32_t block, float softmax_scale, void *out,
                          int64_t *tile_counter, bool &empty) {
     if (block != 64) return fail(LSA_ERR_UNSUPPORTED, "block %d: only 64-token tiles are built", block);
+    if (kv->stream_cache)
+        return fail(LSA_ERR_UNSUPPORTED, "prefill reads every head from the pool: pass a pool without a stream cache");
     if (kv->page_size % 64 != 0)
         return fail(LSA_ERR_UNSUPPORTED, "prefill needs page_size a multiple of 64 (got %d)", kv->page_size);
     const bool pair_ok = (q_dtype == LSA_F32 && kv->kv_dtype == LSA_F32) ||
@@ -226,14 +267,106 @@ const char *lsa_last_error(void) { return g_last_error.c_str(); }
 
 const char *lsa_version(void) { return "lsa 0.1.0 gfx950"; }
 
-lsa_status lsa_page_stats_bytes(const lsa_kv *kv, size_t *bytes) {
+lsa_status lsa_page_stats_bytes(const lsa_kv *kv, const lsa_heads *heads, size_t *bytes) {
     if (lsa_status s = check_kv(kv)) return s;
+    if (lsa_status s = check_heads(heads, kv, kv->stream_cache != nullptr)) return s;
+    if (lsa_status s = check_pool(kv, heads)) return s;
     if (!bytes) return fail(LSA_ERR_INVALID_ARG, "bytes is NULL");
+    PoolHeads ph;
+    pool_heads_of(kv, heads, ph);
     const size_t g = kv->page_size / kv->logical_page;
     const size_t per = kv->kv_dtype == LSA_INT4 ? (size_t)kv->head_dim
                                                  : 2 * (size_t)kv->head_dim * (kv->kv_dtype == LSA_F32 ? 4 : 2);
-    *bytes = (size_t)kv->num_pages * kv->num_kv_heads * g * per;
+    *bytes = (size_t)kv->num_pages * ph.pool_heads * g * per;
     return ok();
+}
+
+lsa_status lsa_stream_cache_pages(const lsa_kv *kv, const lsa_heads *heads, int32_t *sink_pages,
+                                  int32_t *ring_pages) {
+    if (lsa_status s = check_kv(kv)) return s;
+    if (lsa_status s = check_heads(heads, kv, true)) return s;
+    if (!sink_pages || !ring_pages) return fail(LSA_ERR_INVALID_ARG, "sink_pages and ring_pages must be non-NULL");
+    const int NP = kv->page_size;
+    *sink_pages = (heads->sink_tokens + NP - 1) / NP;
+    *ring_pages = (heads->local_tokens + NP - 1) / NP + 1;
+    return ok();
+}
+
+lsa_status lsa_stream_cache_fill(const lsa_kv *src, const lsa_seqs *seqs, const lsa_heads *heads,
+                                 const lsa_stream_cache *cache, void *stream) {
+    if (lsa_status s = check_kv(src)) return s;
+    if (lsa_status s = check_seqs(seqs)) return s;
+    if (lsa_status s = check_heads(heads, src, true)) return s;
+    if (src->stream_cache) return fail(LSA_ERR_INVALID_ARG, "the source pool must hold every head");
+    if (!cache) return fail(LSA_ERR_INVALID_ARG, "cache is NULL");
+    if (lsa_status s = check_stream_cache(cache, src, heads)) return s;
+    FillArgs a{};
+    a.k = src->k;
+    a.v = src->v;
+    a.k_sz = src->k_sz;
+    a.v_sz = src->v_sz;
+    a.page_table = seqs->page_table;
+    a.seq_lens = seqs->seq_lens;
+    a.sc_k = cache->k;
+    a.sc_v = cache->v;
+    a.sc_k_sz = cache->k_sz;
+    a.sc_v_sz = cache->v_sz;
+    a.batch = seqs->batch;
+    a.max_pages = seqs->max_pages;
+    a.num_kv_heads = src->num_kv_heads;
+    a.head_dim = src->head_dim;
+    a.page_size = src->page_size;
+    a.dtype = src->kv_dtype;
+    a.sc_sink = cache->sink_pages;
+    a.sc_ring = cache->ring_pages;
+    a.n_str = 0;
+    for (int i = 0; i < src->num_kv_heads; ++i)
+        if (heads->head_kind[i] == LSA_STREAMING_HEAD) a.str_heads[a.n_str++] = (uint8_t)i;
+    if ((long long)a.batch * a.n_str * (a.sc_sink + a.sc_ring) > (long long)INT32_MAX)
+        return fail(LSA_ERR_UNSUPPORTED, "stream cache too large");
+    return from_hip(launch_stream_fill(a, (hipStream_t)stream), "stream cache fill launch");
+}
+
+lsa_status lsa_append_kv(const lsa_kv *kv, const lsa_seqs *seqs, const lsa_heads *heads, const void *k_new,
+                         const void *v_new, const uint16_t *k_new_sz, const uint16_t *v_new_sz, void *stats,
+                         void *stream) {
+    if (lsa_status s = check_kv(kv)) return s;
+    if (lsa_status s = check_seqs(seqs)) return s;
+    if (lsa_status s = check_heads(heads, kv, true)) return s;
+    if (lsa_status s = check_pool(kv, heads)) return s;
+    if (!k_new || !v_new) return fail(LSA_ERR_INVALID_ARG, "k_new and v_new must be non-NULL");
+    if ((kv->kv_dtype == LSA_INT4) != (k_new_sz != nullptr && v_new_sz != nullptr))
+        return fail(LSA_ERR_INVALID_ARG, "k_new_sz / v_new_sz are needed for int4 pools and only for them");
+    AppendArgs a{};
+    a.k_new = k_new;
+    a.v_new = v_new;
+    a.k_new_sz = k_new_sz;
+    a.v_new_sz = v_new_sz;
+    a.k = const_cast<void *>(kv->k);
+    a.v = const_cast<void *>(kv->v);
+    a.k_sz = const_cast<uint16_t *>(kv->k_sz);
+    a.v_sz = const_cast<uint16_t *>(kv->v_sz);
+    a.stats = stats;
+    a.page_table = seqs->page_table;
+    a.seq_lens = seqs->seq_lens;
+    a.batch = seqs->batch;
+    a.max_pages = seqs->max_pages;
+    a.num_kv_heads = kv->num_kv_heads;
+    a.head_dim = kv->head_dim;
+    a.page_size = kv->page_size;
+    a.logical_page = kv->logical_page;
+    a.dtype = kv->kv_dtype;
+    for (int i = 0; i < kv->num_kv_heads; ++i) a.kind[i] = heads->head_kind[i];
+    pool_heads_of(kv, heads, a.ph, &a.n_str, a.str_slot);
+    if (const lsa_stream_cache *sc = kv->stream_cache) {
+        a.sc_k = sc->k;
+        a.sc_v = sc->v;
+        a.sc_k_sz = sc->k_sz;
+        a.sc_v_sz = sc->v_sz;
+        a.sc_sink = sc->sink_pages;
+        a.sc_ring = sc->ring_pages;
+    }
+    return from_hip(launch_append(a, (hipStream_t)stream), "append launch");
 }
 
 lsa_status lsa_build_page_stats(const lsa_kv *kv, const lsa_seqs *seqs, const lsa_heads *heads,
@@ -241,10 +374,12 @@ lsa_status lsa_build_page_stats(const lsa_kv *kv, const lsa_seqs *seqs, const ls
                                 void *stream) {
     if (lsa_status s = check_kv(kv)) return s;
     if (lsa_status s = check_seqs(seqs)) return s;
-    if (lsa_status s = check_heads(heads, kv, false)) return s;
+    if (lsa_status s = check_heads(heads, kv, kv->stream_cache != nullptr)) return s;
+    if (lsa_status s = check_pool(kv, heads)) return s;
     if (!stats) return fail(LSA_ERR_INVALID_ARG, "stats is NULL");
     if (max_new_tokens < 0) return fail(LSA_ERR_INVALID_ARG, "max_new_tokens < 0");
     StatsArgs a{};
+    pool_heads_of(kv, heads, a.ph);
     a.k = kv->k;
     a.k_sz = kv->k_sz;
     a.stats = stats;
@@ -299,6 +434,7 @@ lsa_status lsa_select_pages(const void *q, int32_t q_dtype, const lsa_kv *kv, co
                     kv->page_size);
     if (reuse_interval < 1) return fail(LSA_ERR_INVALID_ARG, "reuse_interval %d < 1", reuse_interval);
     if (decode_step < 0) return fail(LSA_ERR_INVALID_ARG, "decode_step %d < 0", decode_step);
+    if (lsa_status s = check_pool(kv, heads)) return s;
     if (!q || !stats || !selected) return fail(LSA_ERR_INVALID_ARG, "q, stats and selected must be non-NULL");
     size_t need = 0;
     lsa_select_pages_workspace(kv, seqs, heads, &need);
@@ -312,6 +448,7 @@ lsa_status lsa_select_pages(const void *q, int32_t q_dtype, const lsa_kv *kv, co
     if (n_ret == 0 || seqs->batch == 0) return ok();
 
     ScoreArgs sa{};
+    pool_heads_of(kv, heads, sa.ph);
     sa.q = q;
     sa.stats = stats;
     sa.k = kv->k;
@@ -405,6 +542,7 @@ lsa_status decode_attn_impl(const void *q, int32_t q_dtype, const lsa_kv *kv, co
                          (q_dtype == LSA_BF16 && kv->kv_dtype == LSA_INT4);
     if (!pair_ok)
         return fail(LSA_ERR_UNSUPPORTED, "(q_dtype %d, kv_dtype %d) is not a supported pair", q_dtype, kv->kv_dtype);
+    if (lsa_status s = check_pool(kv, heads)) return s;
     if (!q || !out) return fail(LSA_ERR_INVALID_ARG, "q and out must be non-NULL");
     const int n_ret = count_kind(heads, kv->num_kv_heads, LSA_RETRIEVAL_HEAD);
     if (n_ret > 0 && !selected) return fail(LSA_ERR_INVALID_ARG, "selected is NULL but retrieval heads exist");
@@ -458,6 +596,15 @@ lsa_status decode_attn_impl(const void *q, int32_t q_dtype, const lsa_kv *kv, co
     const float scale = softmax_scale > 0.f ? softmax_scale : 1.f / std::sqrt((float)kv->head_dim);
     a.scale_log2 = scale * 1.4426950408889634f;
     for (int i = 0; i < kv->num_kv_heads; ++i) a.kind[i] = heads->head_kind[i];
+    pool_heads_of(kv, heads, a.ph, &a.n_str, a.str_slot);
+    if (const lsa_stream_cache *sc = kv->stream_cache) {
+        a.sc_k = sc->k;
+        a.sc_v = sc->v;
+        a.sc_k_sz = sc->k_sz;
+        a.sc_v_sz = sc->v_sz;
+        a.sc_sink = sc->sink_pages;
+        a.sc_ring = sc->ring_pages;
+    }
     if (use_static) {
         // the static scratch keeps whatever the previous call left: zero the
         // arrival counters with a fill kernel (no memset node in a captured graph)

@@ -117,8 +117,11 @@ __device__ __forceinline__ void wg_pages(const DecodeArgs &a, const WorkItem &w,
         const int n = cnt + (in ? 0 : 1);
         if (i < n) page = i < cnt ? m_i : cur;
     }
-    int pool = -1;
-    if (lane < CP && page >= 0) pool = a.page_table[(size_t)w.b * a.max_pages + page];
+    int pool = -1;                    // pool page, or the stream-cache page of a streaming head
+    if (lane < CP && page >= 0)
+        pool = w.streaming && a.sc_k
+                   ? (int)stream_cache_page(w.b, a.str_slot[w.kv], page, a.n_str, a.sc_sink, a.sc_ring)
+                   : a.page_table[(size_t)w.b * a.max_pages + page];
     if (lane == 0) { list[0] = t; list[1] = L; }
     if (lane < CP) { list[2 + lane] = page; list[2 + CP + lane] = pool; }
 }
@@ -146,7 +149,7 @@ __device__ __forceinline__ void refresh_current_stats(const DecodeArgs &a, const
     const int m = j / g, jl = j % g;
     const int row0 = jl * NL, rows = w.t - j * NL + 1;
     const int pool = a.page_table[(size_t)w.b * a.max_pages + m];
-    const size_t hp = (size_t)pool * a.num_kv_heads + w.kv;
+    const size_t hp = (size_t)pool * a.ph.pool_heads + a.ph.pool_slot[w.kv];
     const size_t page_base = hp * NP * D;
     if (kv_dtype == LSA_INT4) {
         if (lane >= D / 2) return;
@@ -377,14 +380,22 @@ __global__ __launch_bounds__(kDecodeWaves * kWave, 2) void decode_mfma_kernel(De
     w.t = __builtin_amdgcn_readfirstlane(s_list[0]);
     w.L = __builtin_amdgcn_readfirstlane(s_list[1]);
 
-    // this wavefront's pages: chunk slots PPW*wave .. PPW*wave + PPW - 1
+    // this wavefront's pages: chunk slots PPW*wave .. PPW*wave + PPW - 1, as
+    // (page, head) units of the pool, or pages of the stream cache
+    const bool in_cache = w.streaming && a.sc_k != nullptr;
+    const void *kpool = in_cache ? a.sc_k : a.k;
+    const void *vpool = in_cache ? a.sc_v : a.v;
+    const uint16_t *kszp = in_cache ? a.sc_k_sz : a.k_sz;
+    const uint16_t *vszp = in_cache ? a.sc_v_sz : a.v_sz;
+    const size_t hp_mul = in_cache ? 1 : (size_t)a.ph.pool_heads;
+    const size_t hp_add = in_cache ? 0 : a.ph.pool_slot[w.kv];
     int pg[PPW];
     size_t hp[PPW];
 #pragma unroll
     for (int j = 0; j < PPW; ++j) {
         pg[j] = __builtin_amdgcn_readfirstlane(s_list[2 + PPW * wave + j]);
         const int pool = __builtin_amdgcn_readfirstlane(s_list[2 + CP + PPW * wave + j]);
-        hp[j] = (size_t)max(pool, 0) * a.num_kv_heads + w.kv;
+        hp[j] = (size_t)max(pool, 0) * hp_mul + hp_add;
     }
     // block i of the wavefront: page slot i / NB, 32-token block i % NB of that
     // page; with 16-token pages, tile T of block i is page slot 2i + T.  For
@@ -431,8 +442,8 @@ __global__ __launch_bounds__(kDecodeWaves * kWave, 2) void decode_mfma_kernel(De
             sk[j] = 1.f; zk[j] = 0.f; sv[j] = 1.f; zv[j] = 0.f;
             if constexpr (I4) {
                 if (pg[j] >= 0) {
-                    const uint32_t ksz = *reinterpret_cast<const uint32_t *>(a.k_sz + hp[j] * 2);
-                    const uint32_t vsz = *reinterpret_cast<const uint32_t *>(a.v_sz + hp[j] * 2);
+                    const uint32_t ksz = *reinterpret_cast<const uint32_t *>(kszp + hp[j] * 2);
+                    const uint32_t vsz = *reinterpret_cast<const uint32_t *>(vszp + hp[j] * 2);
                     sk[j] = fp16_bits_to_f32(uint16_t(ksz)); zk[j] = fp16_bits_to_f32(uint16_t(ksz >> 16));
                     sv[j] = fp16_bits_to_f32(uint16_t(vsz)); zv[j] = fp16_bits_to_f32(uint16_t(vsz >> 16));
                 }
@@ -474,7 +485,7 @@ __global__ __launch_bounds__(kDecodeWaves * kWave, 2) void decode_mfma_kernel(De
             const size_t vbase = HALF ? (g4 < 2 ? kbase[0] : kbase[1]) : kbase[0];
             const int vtok = HALF ? 8 * (g4 & 1) : 32 * kb + 8 * g4;
             if constexpr (I4) {
-                const uint8_t *k8 = static_cast<const uint8_t *>(a.k);
+                const uint8_t *k8 = static_cast<const uint8_t *>(kpool);
 #pragma unroll
                 for (int T = 0; T < 2; ++T) {
                     const int row_tok = HALF ? rho : 32 * kb + 16 * T + rho;
@@ -486,12 +497,12 @@ __global__ __launch_bounds__(kDecodeWaves * kWave, 2) void decode_mfma_kernel(De
                         kr[e][T][0] = make_uint4(u.x, u.y, 0, 0);
                     }
                 }
-                const uint8_t *v8 = static_cast<const uint8_t *>(a.v);
+                const uint8_t *v8 = static_cast<const uint8_t *>(vpool);
 #pragma unroll
                 for (int dt = 0; dt < NDT; ++dt)
                     vr4[e][dt] = load_stream4(v8 + (vbase + value_offset(vtok, 16 * dt + h, D, BS)) / 2);
             } else {
-                const uint16_t *kp = static_cast<const uint16_t *>(a.k);
+                const uint16_t *kp = static_cast<const uint16_t *>(kpool);
 #pragma unroll
                 for (int T = 0; T < 2; ++T) {
                     const int row_tok = HALF ? rho : 32 * kb + 16 * T + rho;
@@ -499,7 +510,7 @@ __global__ __launch_bounds__(kDecodeWaves * kWave, 2) void decode_mfma_kernel(De
                     for (int s = 0; s < NS; ++s)
                         kr[e][T][s] = load_stream16(kp + kbase[T] + key_offset(row_tok, 32 * s + 8 * g4, D, BS));
                 }
-                const uint16_t *vp = static_cast<const uint16_t *>(a.v) + vbase;
+                const uint16_t *vp = static_cast<const uint16_t *>(vpool) + vbase;
 #pragma unroll
                 for (int dt = 0; dt < NDT; ++dt)
                     vr[e][dt] = load_stream16(vp + value_offset(vtok, 16 * dt + h, D, BS));
@@ -680,13 +691,14 @@ __global__ __launch_bounds__(256) void decode_f32_kernel(DecodeArgs a) {
         for (int c = 0; c < CPL; ++c) o[hh][c] = 0.f;
     }
 
-    const float *kpool = static_cast<const float *>(a.k);
-    const float *vpool = static_cast<const float *>(a.v);
+    const bool in_cache = w.streaming && a.sc_k != nullptr;
+    const float *kpool = static_cast<const float *>(in_cache ? a.sc_k : a.k);
+    const float *vpool = static_cast<const float *>(in_cache ? a.sc_v : a.v);
     const int bs = block_shift(NP);
 
     if (my_page >= 0) {
         const int page = my_page;
-        const size_t head_page = (size_t)my_pool * a.num_kv_heads + w.kv;
+        const size_t head_page = in_cache ? (size_t)my_pool : (size_t)my_pool * a.ph.pool_heads + a.ph.pool_slot[w.kv];
         const float *kp = kpool + head_page * NP * D;
         const float *vp = vpool + head_page * NP * D;
         for (int s0 = 0; s0 < NP; s0 += kWave) {

@@ -223,6 +223,14 @@ __device__ __forceinline__ void wave_and_or(unsigned long long &a, unsigned long
 // launch arguments
 // ----------------------------------------------------------------------------
 
+// Where a KV head's pages sit in the pool: pool page p, head slot pool_slot[kv]
+// of pool_heads (every KV head, or only the retrieval heads when the streaming
+// heads live in a stream cache), at element ((p * pool_heads + slot) * N_P * D).
+struct PoolHeads {
+    int32_t pool_heads;
+    uint8_t pool_slot[kMaxKvHeads];
+};
+
 struct StatsArgs {
     const void *k;
     const uint16_t *k_sz;
@@ -235,6 +243,7 @@ struct StatsArgs {
     int32_t lp_per_seq;           // logical pages covered per (sequence, head)
     int32_t dtype;
     uint8_t heads_sel[kMaxKvHeads];
+    PoolHeads ph;
 };
 
 struct ScoreArgs {
@@ -259,6 +268,7 @@ struct ScoreArgs {
     int32_t *selected;            // [B][H_kv][K]
     int32_t k_pages;              // K
     int32_t fused_pt;
+    PoolHeads ph;
 };
 
 struct TopkArgs {
@@ -291,6 +301,50 @@ struct DecodeArgs {
     int32_t chunks_per_seq;           // workgroups per sequence
     float scale_log2;                 // softmax scale * log2(e)
     uint8_t kind[kMaxKvHeads];
+    PoolHeads ph;
+    // streaming heads in a stream cache (sc_k == null: they are in the pool):
+    // page m of (b, s = str_slot[kv]) is cache page (b * n_str + s) * (sink + ring)
+    // + (m < sink ? m : sink + (m - sink) % ring)
+    const void *sc_k;
+    const void *sc_v;
+    const uint16_t *sc_k_sz;
+    const uint16_t *sc_v_sz;
+    int32_t sc_sink, sc_ring, n_str;
+    uint8_t str_slot[kMaxKvHeads];
+};
+
+// The cache page of sequence page m of (b, s) in a stream cache.
+__host__ __device__ __forceinline__ int64_t stream_cache_page(int b, int s, int m, int n_str, int sink, int ring) {
+    return ((int64_t)b * n_str + s) * (sink + ring) + (m < sink ? m : sink + (m - sink) % ring);
+}
+
+struct AppendArgs {
+    const void *k_new, *v_new;        // [B][H_kv][D] (int4: [B][H_kv][D/2] bytes)
+    const uint16_t *k_new_sz, *v_new_sz;   // int4: [B][H_kv][2]
+    void *k, *v;                      // pool
+    uint16_t *k_sz, *v_sz;
+    void *stats;                      // may be null
+    const int32_t *page_table;
+    const int32_t *seq_lens;
+    int32_t batch, max_pages, num_kv_heads, head_dim, page_size, logical_page, dtype;
+    uint8_t kind[kMaxKvHeads];
+    PoolHeads ph;
+    void *sc_k, *sc_v;                // stream cache (null: streaming heads are in the pool)
+    uint16_t *sc_k_sz, *sc_v_sz;
+    int32_t sc_sink, sc_ring, n_str;
+    uint8_t str_slot[kMaxKvHeads];
+};
+
+struct FillArgs {
+    const void *k, *v;                // source pool, every KV head
+    const uint16_t *k_sz, *v_sz;
+    const int32_t *page_table;
+    const int32_t *seq_lens;
+    void *sc_k, *sc_v;
+    uint16_t *sc_k_sz, *sc_v_sz;
+    int32_t batch, max_pages, num_kv_heads, head_dim, page_size, dtype;
+    int32_t sc_sink, sc_ring, n_str;
+    uint8_t str_heads[kMaxKvHeads];   // the KV head of streaming slot s
 };
 
 struct PrefillArgs {
@@ -332,5 +386,7 @@ int score_fused_pt(int max_pages);   // top-K pages per thread inside the score 
 hipError_t launch_topk(const TopkArgs &a, hipStream_t s);
 hipError_t launch_decode(const DecodeArgs &a, int q_dtype, int kv_dtype, hipStream_t s);
 hipError_t launch_prefill(const PrefillArgs &a, int dtype, hipStream_t s);
+hipError_t launch_append(const AppendArgs &a, hipStream_t s);
+hipError_t launch_stream_fill(const FillArgs &a, hipStream_t s);
 
 }  // namespace lsa

@@ -397,7 +397,7 @@ __global__ __launch_bounds__(kScoreThreads) void score_kernel(ScoreArgs a) {
         st_hi[it] = make_uint4(0, 0, 0, 0);
         szw[it] = 0;
         if (j < j1 && j != j_cur) {
-            const size_t hp = (size_t)pools[it] * a.num_kv_heads + kv;
+            const size_t hp = (size_t)pools[it] * a.ph.pool_heads + a.ph.pool_slot[kv];
             const int jl = j % g;
             if constexpr (KV_DT == LSA_INT4) {
                 st_lo[it] = load_stream16(static_cast<const uint8_t *>(a.stats) + hp * head_stride + (size_t)jl * D + ch0);
@@ -416,7 +416,7 @@ __global__ __launch_bounds__(kScoreThreads) void score_kernel(ScoreArgs a) {
     uint32_t sz_cur = 0;
     if (own_cur) {
         const int pool = a.page_table[(size_t)b * a.max_pages + j_cur / g];
-        const size_t hp = (size_t)pool * a.num_kv_heads + kv;
+        const size_t hp = (size_t)pool * a.ph.pool_heads + a.ph.pool_slot[kv];
         if constexpr (KV_DT == LSA_INT4) sz_cur = *reinterpret_cast<const uint32_t *>(a.k_sz + hp * 2);
         current_page_minmax<KV_DT, D, C, LPL, LPP>(a, hp * a.page_size * D, (j_cur % g) * a.logical_page,
                                                    L - j_cur * a.logical_page, lane / LPL, ch0, cmin, cmax);

@@ -29,6 +29,9 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "liblsa.so")
 # every function include/lsa.h declares
 EXPORTED = (
     "lsa_page_stats_bytes",
+    "lsa_stream_cache_pages",
+    "lsa_stream_cache_fill",
+    "lsa_append_kv",
     "lsa_build_page_stats",
     "lsa_select_pages_workspace",
     "lsa_select_pages",
@@ -50,6 +53,17 @@ class LsaError(RuntimeError):
         self.status = status
 
 
+class LsaStreamCache(ctypes.Structure):
+    _fields_ = [
+        ("sink_pages", ctypes.c_int32),
+        ("ring_pages", ctypes.c_int32),
+        ("k", ctypes.c_void_p),
+        ("v", ctypes.c_void_p),
+        ("k_sz", ctypes.c_void_p),
+        ("v_sz", ctypes.c_void_p),
+    ]
+
+
 class LsaKV(ctypes.Structure):
     _fields_ = [
         ("kv_dtype", ctypes.c_int32),
@@ -63,6 +77,7 @@ class LsaKV(ctypes.Structure):
         ("v", ctypes.c_void_p),
         ("k_sz", ctypes.c_void_p),
         ("v_sz", ctypes.c_void_p),
+        ("stream_cache", ctypes.c_void_p),
     ]
 
 
@@ -103,7 +118,10 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     st = ctypes.c_int32
     vp = ctypes.c_void_p
     sz = P(ctypes.c_size_t)
-    lib.lsa_page_stats_bytes.argtypes = [P(LsaKV), sz]
+    lib.lsa_page_stats_bytes.argtypes = [P(LsaKV), P(LsaHeads), sz]
+    lib.lsa_stream_cache_pages.argtypes = [P(LsaKV), P(LsaHeads), P(ctypes.c_int32), P(ctypes.c_int32)]
+    lib.lsa_stream_cache_fill.argtypes = [P(LsaKV), P(LsaSeqs), P(LsaHeads), P(LsaStreamCache), vp]
+    lib.lsa_append_kv.argtypes = [P(LsaKV), P(LsaSeqs), P(LsaHeads), vp, vp, vp, vp, vp, vp]
     lib.lsa_build_page_stats.argtypes = [P(LsaKV), P(LsaSeqs), P(LsaHeads), vp, ctypes.c_int32, vp, vp]
     lib.lsa_select_pages_workspace.argtypes = [P(LsaKV), P(LsaSeqs), P(LsaHeads), sz]
     lib.lsa_select_pages.argtypes = [vp, ctypes.c_int32, P(LsaKV), vp, P(LsaSeqs), P(LsaHeads), ctypes.c_int32,
@@ -168,8 +186,25 @@ def dtype_code(t: torch.Tensor) -> int:
 
 
 @dataclass
+class StreamCache:
+    """The constant-size cache of the streaming heads (lsa_stream_cache): K and V
+    pages [B][H_s][sink_pages + ring_pages] in the pool's page layout."""
+    sink_pages: int
+    ring_pages: int
+    k: torch.Tensor
+    v: torch.Tensor
+    k_sz: Optional[torch.Tensor] = None     # int4: [B][H_s][pages][2] fp16
+    v_sz: Optional[torch.Tensor] = None
+
+    def desc(self) -> LsaStreamCache:
+        return LsaStreamCache(self.sink_pages, self.ring_pages, _ptr(self.k), _ptr(self.v), _ptr(self.k_sz),
+                              _ptr(self.v_sz))
+
+
+@dataclass
 class KVPool:
-    """A caller-owned paged KV pool (layouts in include/lsa.h)."""
+    """A caller-owned paged KV pool (layouts in include/lsa.h).  With a
+    stream_cache, the pool pages hold only the retrieval heads."""
     dtype: int
     k: torch.Tensor
     v: torch.Tensor
@@ -180,10 +215,16 @@ class KVPool:
     num_pages: int
     k_sz: Optional[torch.Tensor] = None     # int4: [P][H_kv][2] fp16
     v_sz: Optional[torch.Tensor] = None
+    stream_cache: Optional[StreamCache] = None
+    _sc: object = field(default=None, repr=False)
 
     def desc(self) -> LsaKV:
+        sc = None
+        if self.stream_cache is not None:
+            self._sc = self.stream_cache.desc()
+            sc = ctypes.cast(ctypes.pointer(self._sc), ctypes.c_void_p)
         return LsaKV(self.dtype, self.num_kv_heads, self.head_dim, self.page_size, self.logical_page, 0,
-                     self.num_pages, _ptr(self.k), _ptr(self.v), _ptr(self.k_sz), _ptr(self.v_sz))
+                     self.num_pages, _ptr(self.k), _ptr(self.v), _ptr(self.k_sz), _ptr(self.v_sz), sc)
 
 
 @dataclass
@@ -213,10 +254,38 @@ def seqs_desc(page_table: torch.Tensor, seq_lens: torch.Tensor) -> LsaSeqs:
 # the four entry points and their size queries
 # ---------------------------------------------------------------------------
 
-def page_stats_bytes(kv: KVPool) -> int:
+def page_stats_bytes(kv: KVPool, heads: Optional[Heads] = None) -> int:
     out = ctypes.c_size_t(0)
-    _check(load().lsa_page_stats_bytes(ctypes.byref(kv.desc()), ctypes.byref(out)))
+    hd = ctypes.byref(heads.desc()) if heads is not None else None
+    _check(load().lsa_page_stats_bytes(ctypes.byref(kv.desc()), hd, ctypes.byref(out)))
     return out.value
+
+
+def stream_cache_pages(kv: KVPool, heads: Heads) -> "tuple[int, int]":
+    """(sink_pages, ring_pages) of the smallest streaming-head cache for these shapes."""
+    sink, ring = ctypes.c_int32(0), ctypes.c_int32(0)
+    _check(load().lsa_stream_cache_pages(ctypes.byref(kv.desc()), ctypes.byref(heads.desc()), ctypes.byref(sink),
+                                         ctypes.byref(ring)))
+    return sink.value, ring.value
+
+
+def stream_cache_fill(src: KVPool, page_table: torch.Tensor, seq_lens: torch.Tensor, heads: Heads,
+                      cache: StreamCache, stream=None) -> None:
+    """lsa_stream_cache_fill: copy the sink and most recent pages of every streaming head from a
+    pool that holds every head into the cache."""
+    _check(load().lsa_stream_cache_fill(ctypes.byref(src.desc()), ctypes.byref(seqs_desc(page_table, seq_lens)),
+                                        ctypes.byref(heads.desc()), ctypes.byref(cache.desc()), _stream(stream)))
+
+
+def append_kv(kv: KVPool, page_table: torch.Tensor, seq_lens: torch.Tensor, heads: Heads, k_new: torch.Tensor,
+              v_new: torch.Tensor, k_new_sz: Optional[torch.Tensor] = None, v_new_sz: Optional[torch.Tensor] = None,
+              stats: Optional[torch.Tensor] = None, stream=None) -> None:
+    """lsa_append_kv: write the K/V of token seq_lens[b] - 1 of every sequence ([B][H_kv][D], int4:
+    [B][H_kv][D/2] codes with the page's [B][H_kv][2] fp16 scale and zero), updating the statistics
+    of its logical page when stats is given."""
+    _check(load().lsa_append_kv(ctypes.byref(kv.desc()), ctypes.byref(seqs_desc(page_table, seq_lens)),
+                                ctypes.byref(heads.desc()), _ptr(k_new), _ptr(v_new), _ptr(k_new_sz),
+                                _ptr(v_new_sz), _ptr(stats), _stream(stream)))
 
 
 def build_page_stats(kv: KVPool, page_table: torch.Tensor, seq_lens: torch.Tensor, stats: torch.Tensor,

@@ -365,3 +365,63 @@ def random_tile_masks(num_kv_heads: int, n_blocks: int, density: float, seed: in
     if diagonal:
         m |= torch.eye(n_blocks, dtype=torch.bool)[None]
     return m
+
+
+# ---------------------------------------------------------------------------
+# the streaming heads' constant-size cache and the token rows a decode step
+# appends (input preparation: copies and gathers of the generated pool)
+# ---------------------------------------------------------------------------
+
+def retrieval_pool(w: DecodeWorkload):
+    """The pool pages of the retrieval heads only ([P][H_r] pages, KV-head
+    order), copied from a workload's every-head pool: (k, v, k_sz, v_sz)."""
+    ret = torch.tensor([h for h in range(w.num_kv_heads) if w.head_kind[h] == 0], device=w.k.device)
+    pick = lambda t: None if t is None else t.index_select(1, ret).contiguous()   # noqa: E731
+    return pick(w.k), pick(w.v), pick(w.k_sz), pick(w.v_sz)
+
+
+def empty_stream_cache(w: DecodeWorkload, sink_pages: int, ring_pages: int, fill_byte: int = 0xFF):
+    """Tensors of a streaming-head cache for the workload's batch, every byte
+    set to fill_byte: (k, v, k_sz, v_sz), pages [B][H_s][sink + ring] shaped
+    like one (page, head) of the pool."""
+    n_str = sum(1 for x in w.head_kind if x == 1)
+    shape = (w.batch, n_str, sink_pages + ring_pages)
+    k = torch.empty(shape + tuple(w.k.shape[2:]), dtype=w.k.dtype, device=w.k.device)
+    v = torch.empty(shape + tuple(w.v.shape[2:]), dtype=w.v.dtype, device=w.v.device)
+    k.view(torch.uint8).fill_(fill_byte)
+    v.view(torch.uint8).fill_(fill_byte)
+    k_sz = v_sz = None
+    if w.k_sz is not None:
+        k_sz = torch.empty(shape + (2,), dtype=torch.float16, device=w.k.device)
+        v_sz = torch.empty_like(k_sz)
+        k_sz.view(torch.uint8).fill_(fill_byte)
+        v_sz.view(torch.uint8).fill_(fill_byte)
+    return k, v, k_sz, v_sz
+
+
+def token_rows(w: DecodeWorkload, step: int):
+    """The K and V rows of the token each sequence appends at window step
+    `step` (position ctx + step), every KV head, read out of the generated
+    pool: ([B][H_kv][D], [B][H_kv][D]) in the pool dtype, or for int4 the codes
+    ([B][H_kv][D/2] bytes, channel 2i in the low nibble) followed by the fp16
+    (scale, zero) pairs of the token's page, ([B][H_kv][2], [B][H_kv][2])."""
+    NP, D = w.page_size, w.head_dim
+    bt = min(NP, 32)
+    pos = torch.tensor([c + step for c in w.ctx], device=w.k.device)
+    pages = w.page_table.long().gather(1, (pos // NP)[:, None])[:, 0]
+    slot = pos % NP
+    blk, r = slot // bt, slot % bt
+    ks, vs = [], []
+    for b in range(w.batch):
+        kt = w.k[pages[b], :, blk[b], :, r[b], :]               # [H_kv][D/32][32 or 16 bytes]
+        ks.append(kt.reshape(w.num_kv_heads, -1))
+        if w.dtype == INT4:
+            vb = w.v[pages[b], :, blk[b], :, r[b] // 2]          # [H_kv][D] bytes holding the token's nibble
+            codes = (vb >> (4 * (int(r[b]) % 2))) & 15
+            vs.append(codes[:, 0::2] | (codes[:, 1::2] << 4))
+        else:
+            vs.append(w.v[pages[b], :, blk[b], :, r[b]])          # [H_kv][D]
+    k_new, v_new = torch.stack(ks).contiguous(), torch.stack(vs).contiguous()
+    if w.dtype != INT4:
+        return k_new, v_new
+    return k_new, v_new, w.k_sz[pages].contiguous(), w.v_sz[pages].contiguous()

@@ -92,6 +92,31 @@ typedef int32_t lsa_status;
 #define LSA_AGG_SUM 0
 #define LSA_AGG_MAX 1
 
+/* [host] descriptor of the constant-size cache of the streaming heads
+ * ([LS-X] 静的スパーシティ: a streaming head only ever attends its sink and
+ * its most recent tokens, so its cost, and here its memory, does not grow with
+ * the context).  For every sequence b and streaming KV head (H_s of them,
+ * numbered s = 0 .. H_s - 1 in KV-head order) the cache holds sink_pages +
+ * ring_pages pages of page_size tokens in the pool's page layout:
+ *   K, V:        [B][H_s][sink_pages + ring_pages] pages, each laid out as one
+ *                (pool page, KV head) of the paged pool (layout above);
+ *   k_sz, v_sz:  int4 only, [B][H_s][sink_pages + ring_pages][2] fp16 {s, z}.
+ * Sequence page m (tokens m*N_P .. m*N_P + N_P - 1) of (b, s) is cache page
+ *   m                                          if m < sink_pages,
+ *   sink_pages + (m - sink_pages) % ring_pages otherwise,
+ * so the ring keeps the ring_pages most recent pages past the sink.  With
+ * sink_pages >= ceil(sink_tokens / N_P) and ring_pages >= ceil(local_tokens /
+ * N_P) + 1 (lsa_stream_cache_pages) every token a streaming head attends is
+ * in the cache.  Its size is independent of the context length. */
+typedef struct lsa_stream_cache {
+    int32_t sink_pages;     /* pages kept from the start of each sequence           */
+    int32_t ring_pages;     /* pages of the ring of recent pages                    */
+    void *k;                /* K pages                                              */
+    void *v;                /* V pages                                              */
+    uint16_t *k_sz;         /* int4 only, else NULL                                 */
+    uint16_t *v_sz;         /* int4 only, else NULL                                 */
+} lsa_stream_cache;
+
 /* [host] descriptor of the paged KV pool (layout above). */
 typedef struct lsa_kv {
     int32_t kv_dtype;       /* LSA_F32 | LSA_BF16 | LSA_INT4                      */
@@ -105,6 +130,13 @@ typedef struct lsa_kv {
     const void *v;          /* V pool                                             */
     const uint16_t *k_sz;   /* int4 only, else NULL                               */
     const uint16_t *v_sz;   /* int4 only, else NULL                               */
+    /* NULL: every KV head lives in the pool ([P][H_kv] pages, as above).
+     * Non-NULL: the pool pages hold only the retrieval heads, [P][H_r] with
+     * the H_r retrieval heads in KV-head order (the statistics pool likewise),
+     * and the streaming heads live in this cache.  A pool of this kind needs
+     * the head classification (lsa_heads) in every call, and prefill, which
+     * reads every head, does not take it. */
+    const lsa_stream_cache *stream_cache;
 } lsa_kv;
 
 /* [host] descriptor of a decode batch. */
@@ -131,12 +163,52 @@ typedef struct lsa_heads {
 } lsa_heads;
 
 /* Bytes of the logical-page statistics pool that matches `kv`:
- *   f32/bf16: [num_pages][H_kv][g][2][head_dim] elements of kv_dtype
+ *   f32/bf16: [num_pages][H][g][2][head_dim] elements of kv_dtype
  *             (index 0 = channel minimum, 1 = channel maximum), g = N_P / N_L;
- *   int4:     [num_pages][H_kv][g][head_dim] bytes, byte = c_min | c_max << 4.
+ *   int4:     [num_pages][H][g][head_dim] bytes, byte = c_min | c_max << 4;
+ * H = H_kv, or the number of retrieval heads when kv->stream_cache is set
+ * (pass their count in `heads`; NULL heads means every head is in the pool).
  * Source: [LS-X] 動的スパーシティ and 階層的ページング (channel-wise k_min /
  * k_max per logical page, kept beside each physical page). */
-lsa_status lsa_page_stats_bytes(const lsa_kv *kv, size_t *bytes /* [host] out */);
+lsa_status lsa_page_stats_bytes(const lsa_kv *kv, const lsa_heads *heads /* nullable */,
+                                size_t *bytes /* [host] out */);
+
+/* The smallest streaming-head cache for these shapes: *sink_pages =
+ * ceil(sink_tokens / N_P) and *ring_pages = ceil(local_tokens / N_P) + 1 (the
+ * local window of a token spans at most that many pages).  Source: [LS-X]
+ * 静的スパーシティ (sink + local tokens of a streaming head). */
+lsa_status lsa_stream_cache_pages(const lsa_kv *kv, const lsa_heads *heads, int32_t *sink_pages /* [host] out */,
+                                  int32_t *ring_pages /* [host] out */);
+
+/* Fill a streaming-head cache from a paged pool that holds every head (src,
+ * stream_cache NULL): for every sequence b, with tokens 0 .. seq_lens[b] - 1
+ * in src, each cache page receives the whole src page it stands for (the sink
+ * pages, and the ring_pages most recent pages past them; pages past the
+ * sequence are left untouched), int4 scale and zero point included.  This is
+ * the hand-over after a prefill over a full pool.  cache: the destination,
+ * shapes as in lsa_stream_cache. */
+lsa_status lsa_stream_cache_fill(const lsa_kv *src, const lsa_seqs *seqs, const lsa_heads *heads,
+                                 const lsa_stream_cache *cache, void *stream);
+
+/* Append the key and value of the newest token t = seq_lens[b] - 1 of every
+ * sequence b, for every KV head ([LS-X] Reusable Page Selection: a decode step
+ * appends its token's K/V before selecting and attending).  Retrieval heads
+ * (and streaming heads when kv->stream_cache is NULL) are written to slot
+ * t % N_P of pool page page_table[b][t / N_P]; streaming heads go to their
+ * cache page when kv->stream_cache is set.
+ * k_new, v_new: [B][H_kv][head_dim] of kv_dtype (f32 / bf16), or for int4 the
+ * codes [B][H_kv][head_dim / 2] bytes (channel 2i in the low nibble of byte i)
+ * with k_new_sz, v_new_sz: [B][H_kv][2] fp16 {s, z} of the token's page,
+ * written to the page's entry (every token of a page shares it).
+ * stats: NULL, or the statistics pool: the statistics of the logical page that
+ * holds t are updated for every retrieval head (a new logical page starts
+ * from the token; otherwise the minimum / maximum take the token in), which
+ * is what lsa_build_page_stats(first_token = t) computes, so a decode step
+ * then needs no statistics refresh in lsa_sparse_decode_attn (stats NULL).
+ * One kernel launch. */
+lsa_status lsa_append_kv(const lsa_kv *kv, const lsa_seqs *seqs, const lsa_heads *heads, const void *k_new,
+                         const void *v_new, const uint16_t *k_new_sz, const uint16_t *v_new_sz, void *stats,
+                         void *stream);
 
 /* Build the channel-wise min / max of the keys of logical pages
  * ([LS-X] 動的スパーシティ: statistics of logical page j; 階層的ページング:

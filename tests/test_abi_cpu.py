@@ -69,7 +69,7 @@ def heads_desc(kinds=(0, 1, 0, 1, 0, 1, 0, 1), hq=32, sink=64, local=1024, sb=1,
 
 def stats_bytes(lib, kv):
     out = ctypes.c_size_t(0)
-    st = lib.lsa_page_stats_bytes(ctypes.byref(kv), ctypes.byref(out))
+    st = lib.lsa_page_stats_bytes(ctypes.byref(kv), None, ctypes.byref(out))
     return st, out.value
 
 
@@ -102,7 +102,7 @@ def test_kv_validation(lib, kw, code):
 
 def test_null_descriptor_and_reserved(lib):
     out = ctypes.c_size_t(0)
-    assert lib.lsa_page_stats_bytes(None, ctypes.byref(out)) == lsa.LSA_ERR_INVALID_ARG
+    assert lib.lsa_page_stats_bytes(None, None, ctypes.byref(out)) == lsa.LSA_ERR_INVALID_ARG
     kv = kv_desc()
     kv.reserved = 1
     assert stats_bytes(lib, kv)[0] == lsa.LSA_ERR_INVALID_ARG
@@ -307,3 +307,55 @@ def test_kv_page_sizes_accepted(lib, NP, NL):
     st, nbytes = stats_bytes(lib, kv_desc(NP=NP, NL=NL))
     assert st == lsa.LSA_OK
     assert nbytes == 100 * 8 * (NP // NL) * 2 * 128 * 2
+
+
+def test_stream_cache_pages_follow_the_lambda_window_only(lib):
+    """The streaming-head cache needs ceil(sink / N_P) sink pages and
+    ceil(local / N_P) + 1 ring pages, whatever the context length."""
+    kv = kv_desc(NP=64, NL=16)
+    sink, ring = ctypes.c_int32(0), ctypes.c_int32(0)
+    for local, expect in ((1024, 17), (2048, 33), (1, 2), (64, 2), (65, 3)):
+        st = lib.lsa_stream_cache_pages(ctypes.byref(kv), ctypes.byref(heads_desc(sink=64, local=local)),
+                                        ctypes.byref(sink), ctypes.byref(ring))
+        assert st == lsa.LSA_OK and (sink.value, ring.value) == (1, expect)
+    st = lib.lsa_stream_cache_pages(ctypes.byref(kv_desc(NP=16, NL=16)), ctypes.byref(heads_desc(sink=64, local=1024)),
+                                    ctypes.byref(sink), ctypes.byref(ring))
+    assert st == lsa.LSA_OK and (sink.value, ring.value) == (4, 65)
+
+
+def test_stream_cache_validation(lib):
+    """A pool with a stream cache needs the head classification, a cache
+    large enough for the Lambda window, and no prefill."""
+    kv = kv_desc()
+    small = lsa.LsaStreamCache(1, 16, FAKE, FAKE, None, None)      # ring 16 < ceil(1024 / 64) + 1
+    kv.stream_cache = ctypes.cast(ctypes.pointer(small), ctypes.c_void_p)
+    out = ctypes.c_size_t(0)
+    assert lib.lsa_page_stats_bytes(ctypes.byref(kv), None, ctypes.byref(out)) == lsa.LSA_ERR_INVALID_ARG
+    assert lib.lsa_page_stats_bytes(ctypes.byref(kv), ctypes.byref(heads_desc()), ctypes.byref(out)) == \
+        lsa.LSA_ERR_INVALID_ARG
+    good = lsa.LsaStreamCache(1, 17, FAKE, FAKE, None, None)
+    kv.stream_cache = ctypes.cast(ctypes.pointer(good), ctypes.c_void_p)
+    assert lib.lsa_page_stats_bytes(ctypes.byref(kv), ctypes.byref(heads_desc()), ctypes.byref(out)) == lsa.LSA_OK
+    assert out.value == 100 * 4 * 4 * 2 * 128 * 2        # four retrieval heads in the pool
+    assert lib.lsa_sparse_prefill_attn(FAKE, lsa.BF16, ctypes.byref(kv), FAKE, 1000, ctypes.byref(heads_desc()),
+                                       64, 0.0, FAKE, None, None) == lsa.LSA_ERR_UNSUPPORTED
+    # an int4 cache needs its scale / zero arrays, a bf16 one must not have them
+    bad = lsa.LsaStreamCache(1, 17, FAKE, FAKE, FAKE, FAKE)
+    kv.stream_cache = ctypes.cast(ctypes.pointer(bad), ctypes.c_void_p)
+    assert lib.lsa_page_stats_bytes(ctypes.byref(kv), ctypes.byref(heads_desc()), ctypes.byref(out)) == \
+        lsa.LSA_ERR_INVALID_ARG
+
+
+def test_append_validation(lib):
+    kv = kv_desc()
+    h = heads_desc()
+    seqs = seqs_desc()
+    assert lib.lsa_append_kv(ctypes.byref(kv), ctypes.byref(seqs), ctypes.byref(h), None, FAKE, None, None, None,
+                             None) == lsa.LSA_ERR_INVALID_ARG
+    assert lib.lsa_append_kv(ctypes.byref(kv), ctypes.byref(seqs), ctypes.byref(h), FAKE, FAKE, FAKE, FAKE, None,
+                             None) == lsa.LSA_ERR_INVALID_ARG       # (s, z) rows for a bf16 pool
+    kv4 = kv_desc(dtype=lsa.INT4, sz=True)
+    assert lib.lsa_append_kv(ctypes.byref(kv4), ctypes.byref(seqs), ctypes.byref(h), FAKE, FAKE, None, None, None,
+                             None) == lsa.LSA_ERR_INVALID_ARG       # int4 without (s, z) rows
+    assert lib.lsa_append_kv(ctypes.byref(kv), ctypes.byref(seqs), None, FAKE, FAKE, None, None, None,
+                             None) == lsa.LSA_ERR_INVALID_ARG       # heads are required
