@@ -6,9 +6,13 @@ Metric: sparse decode attention tokens/s and HBM GB/s at a 64K context
 at a 128K context.  One printed JSON line.
 
 Decode.  A step is one decode step of one attention layer for the whole batch:
-select pages (every R = 4 steps, reused otherwise; the current logical page
-is scored from its keys), then sparse decode attention, which also refreshes
-the statistics of the current logical page.  Steps cycle over
+append the step's token K/V (retrieval heads into the paged pool, which holds
+only them, with their logical page's statistics; streaming heads into a
+constant-size cache of sink pages and a ring of recent pages), select pages
+(every R = 4 steps, reused otherwise; the current logical page is scored from
+its keys), then sparse decode attention.  --no-append times the step without
+the append (every head in the paged pool with the window tokens already in it;
+attention refreshes the statistics of the current logical page).  Steps cycle over
 `--replicas` independent copies of the layer's KV pool (distinct layers of a
 model), so every step reads its pages from HBM rather than from the 256 MB
 last-level cache.  A cycle of replicas x R steps is captured once as a HIP
@@ -60,6 +64,9 @@ def parse():
     ap.add_argument("--reuse", type=int, default=None, help="selection reuse interval R (default: 4)")
     ap.add_argument("--aggregation", choices=["sum", "max"], default="sum",
                     help="how a KV head's query group combines its page scores")
+    ap.add_argument("--no-append", action="store_true",
+                    help="time the step without the append: every head in the paged pool (its window tokens "
+                         "already written), selection + attention with the statistics refresh")
     ap.add_argument("--page-size", type=int, default=None, help="physical page size N_P of the decode pool")
     ap.add_argument("--logical-page", type=int, default=None, help="logical page size N_L of the statistics")
     ap.add_argument("--steps", type=int, default=640, help="timed decode steps (rounded up to whole cycles)")
@@ -181,7 +188,7 @@ def counters_for(kernel_tag, source_file, launch_bytes):
 # decode (config 2)
 # ---------------------------------------------------------------------------
 
-def bench_decode(args, torch, lsa, W):
+def bench_decode(args, torch, lsa, W, append=True):
     dev = "cuda"
     cfg = WORKLOADS[args.workload][0]
     R = args.reuse or W.DECODE_CONFIGS[cfg]["reuse_interval"]
@@ -193,19 +200,32 @@ def bench_decode(args, torch, lsa, W):
     agg = lsa.AGG_MAX if args.aggregation == "max" else lsa.AGG_SUM
     hd = lsa.Heads(w.head_kind, Hq, w.sink_tokens, w.local_tokens, w.sink_blocks, w.local_blocks, agg)
     nrep = max(1, args.replicas)
+    lens0 = torch.tensor(w.ctx, dtype=torch.int32, device=dev)
+    full = lsa.KVPool(w.dtype, w.k, w.v, Hkv, D, NP, w.logical_page, w.num_pages, k_sz=w.k_sz, v_sz=w.v_sz)
     layers = []
     for r in range(nrep):
-        k = w.k if r == 0 else w.k.clone()
-        v = w.v if r == 0 else w.v.clone()
-        k_sz = w.k_sz if (r == 0 or w.k_sz is None) else w.k_sz.clone()
-        v_sz = w.v_sz if (r == 0 or w.v_sz is None) else w.v_sz.clone()
-        kv = lsa.KVPool(w.dtype, k, v, Hkv, D, NP, w.logical_page, w.num_pages, k_sz=k_sz, v_sz=v_sz)
-        stats = torch.zeros(lsa.page_stats_bytes(kv), dtype=torch.uint8, device=dev)
-        lens0 = torch.tensor(w.ctx, dtype=torch.int32, device=dev)
+        if append:
+            # the retrieval heads in a pool of their own, the streaming heads in
+            # a constant-size cache filled from the prompt (tokens < ctx)
+            k, v, k_sz, v_sz = W.retrieval_pool(w)
+            sink, ring = lsa.stream_cache_pages(full, hd)
+            cache = lsa.StreamCache(sink, ring, *W.empty_stream_cache(w, sink, ring, fill_byte=0))
+            lsa.stream_cache_fill(full, w.page_table, lens0, hd, cache)
+            kv = lsa.KVPool(w.dtype, k, v, Hkv, D, NP, w.logical_page, w.num_pages, k_sz=k_sz, v_sz=v_sz,
+                            stream_cache=cache)
+        else:
+            k = w.k if r == 0 else w.k.clone()
+            v = w.v if r == 0 else w.v.clone()
+            k_sz = w.k_sz if (r == 0 or w.k_sz is None) else w.k_sz.clone()
+            v_sz = w.v_sz if (r == 0 or w.v_sz is None) else w.v_sz.clone()
+            kv = lsa.KVPool(w.dtype, k, v, Hkv, D, NP, w.logical_page, w.num_pages, k_sz=k_sz, v_sz=v_sz)
+        stats = torch.zeros(lsa.page_stats_bytes(kv, hd), dtype=torch.uint8, device=dev)
         lsa.build_page_stats(kv, w.page_table, lens0, stats, heads=hd)
         sel = torch.full((B, Hkv, K), -1, dtype=torch.int32, device=dev)
         layers.append((kv, stats, sel))
+    torch.cuda.synchronize()
     lens = [w.seq_lens(s) for s in range(R)]
+    rows = [W.token_rows(w, s) for s in range(R)] if append else None
     ws_sel = torch.zeros(lsa.select_pages_workspace(layers[0][0], w.page_table, lens[0], hd), dtype=torch.uint8,
                          device=dev)
     ws_dec = torch.zeros(lsa.decode_workspace(layers[0][0], w.page_table, lens[0], hd, w.token_budget),
@@ -216,11 +236,13 @@ def bench_decode(args, torch, lsa, W):
     def step(k, timers=None):
         l, s = k % nrep, (k // nrep) % R
         kv, stats, sel = layers[l]
+        if append:             # the step's token, with its logical page's statistics
+            lsa.append_kv(kv, w.page_table, lens[s], hd, *rows[s], stats=stats)
         lsa.select_pages(w.q[s], kv, stats, w.page_table, lens[s], hd, w.token_budget, s, R, sel, ws_sel)
         if timers is not None:
             timers[0].record()
         lsa.sparse_decode_attn(w.q[s], kv, w.page_table, lens[s], hd, sel, w.token_budget, out, ws_dec,
-                               stats=stats)
+                               stats=None if append else stats)
         if timers is not None:
             timers[1].record()
 
@@ -275,7 +297,7 @@ def bench_decode(args, torch, lsa, W):
         l, s = k % nrep, (k // nrep) % R
         kv, stats, sel = layers[l]
         lsa.sparse_decode_attn(w.q[s], kv, w.page_table, lens[s], hd, sel, w.token_budget, out, ws_dec,
-                               stats=stats)
+                               stats=None if append else stats)
 
     kernel_reps = 10
     kt = None
@@ -309,6 +331,31 @@ def bench_decode(args, torch, lsa, W):
         kt = sorted(a_.elapsed_time(b_) / 1e3 for a_, b_ in timers)
     kernel_avg = sum(kt) / len(kt)
 
+    # duration of one selection call (score kernel, fused or separate top-K):
+    # the selections of one cycle (one per replica) captured alone and replayed
+    sel_time = None
+    if graph is not None:
+        try:
+            g3 = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g3):
+                for l in range(nrep):
+                    kv, stats, sel = layers[l]
+                    lsa.select_pages(w.q[0], kv, stats, w.page_table, lens[0], hd, w.token_budget, 0, R, sel,
+                                     ws_sel)
+            g3.replay()
+            torch.cuda.synchronize()
+            a = torch.cuda.Event(enable_timing=True)
+            b = torch.cuda.Event(enable_timing=True)
+            a.record()
+            for _ in range(kernel_reps):
+                g3.replay()
+            b.record()
+            torch.cuda.synchronize()
+            sel_time = a.elapsed_time(b) / 1e3 / (kernel_reps * nrep)
+            del g3
+        except Exception as e:  # pragma: no cover
+            print(f"# selection-only graph failed ({e})", file=sys.stderr)
+
     # algorithmic bytes of one attention launch: the attended keys and values
     # of every (sequence, KV head) at the measured window steps, plus q and o
     # (bytes per K or V element: 2 for bf16, 4 for f32, half a byte for int4
@@ -340,18 +387,26 @@ def bench_decode(args, torch, lsa, W):
     # one byte per channel plus the page's (scale, zero))
     n_ret = sum(1 for x in w.head_kind if x == 0)
     lp_bytes = D + 4 / (NP // w.logical_page) if w.dtype == W.INT4 else 2 * D * eb
-    sel_bytes = n_ret * sum(-(-(c + 1) // w.logical_page) for c in w.ctx) * lp_bytes / R
-    step_bytes = launch_bytes + sel_bytes
+    sel_call_bytes = n_ret * sum(-(-(c + 1) // w.logical_page) for c in w.ctx) * lp_bytes
+    sel_bytes = sel_call_bytes / R
+    # the append writes one K and one V row per (sequence, KV head) and, for
+    # retrieval heads, reads and writes one logical page's statistics
+    app_bytes = (B * Hkv * 2 * D * eb + B * n_ret * (2 * lp_bytes)) if append else 0
+    step_bytes = launch_bytes + sel_bytes + app_bytes
     tok_s = B * steps / elapsed
     src = os.path.join(ROOT, "block_sparse_attention_logical_amd", "csrc", "decode.hip")
     # the workload the counter summary covers
     default = args.workload == "llama3-8b" and R == 4 and args.page_size in (None, 64) and \
-        args.logical_page in (None, 16)
+        args.logical_page in (None, 16) and append and args.aggregation == "sum"
+    traffic = counters_for("decode_attn_cfg2", src, launch_bytes) if default else None
     return dict(
         w=w, agg=args.aggregation, steps=steps, elapsed=elapsed, tok_s=tok_s, ms_per_step=elapsed / steps * 1e3,
         step_bytes=step_bytes, launch_bytes=launch_bytes, kernel_avg=kernel_avg,
-        kernel_p50=kt[len(kt) // 2], timing=timing,
-        traffic=counters_for("decode_attn_cfg2", src, launch_bytes) if default else None,
+        kernel_p50=kt[len(kt) // 2], timing=timing, append=append,
+        traffic=traffic,
+        traffic_source=(f"profiles/decode_attn_cfg2_counters.txt, taken on decode.hip sha {sha_of(src)}"
+                        if traffic is not None else None),
+        sel_time=sel_time, sel_call_bytes=sel_call_bytes,
     )
 
 
@@ -378,6 +433,12 @@ def bench_prefill(args, torch, lsa, W, O):
         times.append(a.elapsed_time(b) / 1e3)
     n = -(-p.seq_len // 64)
     G = p.num_q_heads // p.num_kv_heads
+    # the kernel's own count of the (query head, tile) pairs it computed, from
+    # one more (untimed) call, against the oracle's block accounting
+    counter = torch.zeros(1, dtype=torch.int64, device=dev)
+    lsa.sparse_prefill_attn(p.q, kv, p.page_table, p.seq_len, hd, out, tile_counter=counter)
+    torch.cuda.synchronize()
+    kernel_tiles = int(counter.item())
     tiles = sum(G * O.block_counts(n, p.head_kind[kvh], p.sink_blocks, p.local_blocks)[0]
                 for kvh in range(p.num_kv_heads))
     dense = p.num_q_heads * n * (n + 1) // 2
@@ -426,9 +487,11 @@ def bench_prefill(args, torch, lsa, W, O):
         del row_ptr, col_idx, order
     shape = dict(T=p.seq_len, Hq=p.num_q_heads, Hkv=p.num_kv_heads, D=p.head_dim,
                  n_str=sum(1 for x in p.head_kind if x == 1), sink=p.sink_blocks, local=p.local_blocks)
+    cpu = None if args.no_cpu_baseline else prefill_cpu_baseline(p, torch, O, args.cpu_seconds / 2, flop)
     del out, p
     torch.cuda.empty_cache()
-    return dict(seconds=t, flop=flop, tiles=tiles, dense_tiles=dense, tflops=flop / t / 1e12,
+    return dict(seconds=t, flop=flop, tiles=tiles, kernel_tiles=kernel_tiles, cpu=cpu, dense_tiles=dense,
+                tflops=flop / t / 1e12,
                 causal_seconds=t_causal, causal_tflops=causal_flop / t_causal / 1e12, csr_seconds=t_csr, **shape)
 
 
@@ -436,13 +499,78 @@ def bench_prefill(args, torch, lsa, W, O):
 # oracle CPU baseline (bounded sample)
 # ---------------------------------------------------------------------------
 
-def cpu_baseline(dec, torch, O, budget_s):
+def host_details():
+    """The host the oracle runs on: cores this process may use, CPU model,
+    NumPy and its BLAS with the BLAS thread count."""
     import numpy as np
+    cores = len(os.sched_getaffinity(0))
+    model = "unknown"
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                model = line.split(":", 1)[1].strip()
+                break
+    except OSError:  # pragma: no cover
+        pass
+    blas, threads = "unknown", None
     try:
         from threadpoolctl import threadpool_info
-        threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+        info = [i for i in threadpool_info() if i.get("user_api") == "blas"]
+        if info:
+            blas = f"{info[0].get('internal_api')} {info[0].get('version')}"
+            threads = info[0].get("num_threads")
     except Exception:  # pragma: no cover
-        threads = 1
+        pass
+    return dict(cores=cores, cpu_model=model, numpy=np.__version__, blas=blas, blas_threads=threads)
+
+
+def prefill_cpu_baseline(p, torch, O, budget_s, total_flop):
+    """The oracle's block-sparse prefill on a stratified sample of query rows
+    (for each of a causal and a Lambda head, rows spread evenly over the
+    sequence), timed on the host; its throughput (fp64 flop of the rows'
+    visible keys per second) extrapolates the whole prefill's time by flop."""
+    import numpy as np
+    G = p.num_q_heads // p.num_kv_heads
+    table = list(range(p.page_table.numel()))
+    rows_idx = p.page_table.long()
+    done_flop, t_total, n_rows = 0.0, 0.0, 0
+    kinds = sorted({p.head_kind[kvh]: kvh for kvh in range(p.num_kv_heads)}.items())
+    strata = 512
+    host = {}
+    for kind, kvh in kinds:
+        pool = O.Pool("bf16", p.k[rows_idx, kvh][:, None].cpu().view(torch.int16).numpy().view(np.uint16),
+                      p.v[rows_idx, kvh][:, None].cpu().view(torch.int16).numpy().view(np.uint16),
+                      p.page_size, p.head_dim)
+        q = O.bf16_bits_to_f64(p.q[:, kvh * G].cpu().view(torch.int16).numpy().view(np.uint16))
+        host[kind] = (pool.keys(table, 0, p.seq_len), pool.values(table, 0, p.seq_len), q, kvh)
+    scale = 1 / np.sqrt(p.head_dim)
+    k_i = 0
+    while t_total < budget_s and k_i < strata:
+        # stratum k_i: a row in the k_i-th of `strata` equal spans of the
+        # sequence, the spans visited in bit-reversed order so that any prefix
+        # of the sample spreads over the whole sequence
+        j = int(format(k_i, "09b")[::-1], 2)
+        row = int((j + 0.5) * p.seq_len / strata)
+        for kind, (keys, values, q, kvh) in host.items():
+            a = row // 64
+            vis = sum(min(64 * (c + 1), row + 1) - 64 * c for c in range(a + 1)
+                      if O.tile_visible(a, c, kind, p.sink_blocks, p.local_blocks))
+            t0 = time.perf_counter()
+            O.prefill_attention(q, keys, values, kind, 64, p.sink_blocks, p.local_blocks, scale, rows=[row])
+            t_total += time.perf_counter() - t0
+            done_flop += 4.0 * vis * p.head_dim
+            n_rows += 1
+        k_i += 1
+    rate = done_flop / t_total
+    return dict(value=round(rate / 1e12, 6), unit="TFLOP/s", kind="oracle", **host_details(),
+                extrapolated_seconds=round(total_flop / rate, 1),
+                sample=f"extrapolated: {n_rows} query rows of a causal and a Lambda head, one in each of "
+                       f"{k_i} of {strata} equal spans of the {p.seq_len}-token sequence (fp64 NumPy), "
+                       f"{t_total:.1f} s; the whole prefill's flop / this rate gives the extrapolated time")
+
+
+def cpu_baseline(dec, torch, O, budget_s):
+    import numpy as np
     w = dec["w"]
     G = w.num_q_heads // w.num_kv_heads
     spec = O.DecodeSpec(w.num_q_heads, w.num_kv_heads, list(w.head_kind), w.logical_page, w.page_size,
@@ -471,7 +599,7 @@ def cpu_baseline(dec, torch, O, budget_s):
         done += 1
     # one selection step per sequence; a window of R steps selects once, so
     # the steady-state cost per token is below this selection-step cost
-    return dict(value=done / t_total, unit="tokens/s", cores=threads, kind="oracle",
+    return dict(value=done / t_total, unit="tokens/s", kind="oracle", **host_details(),
                 sample=f"{done} decode steps with page selection, one sequence each ({w.ctx[0] // 1024}K context, "
                        f"all {w.num_kv_heads} KV heads, fp64 NumPy), {t_total:.1f} s")
 
@@ -507,7 +635,12 @@ def main():
                           "csr_mask_ms": round(pre["csr_seconds"] * 1e3, 3),
                           "measured_speedup": round(pre["causal_seconds"] / pre["seconds"], 4)}))
         return
-    dec = bench_decode(args, torch, lsa, W)
+    dec = bench_decode(args, torch, lsa, W, append=not args.no_append)
+    torch.cuda.empty_cache()
+    # the same layer's step without the append (every head in the paged pool),
+    # the step the previous measurements used
+    plain = None if args.no_append else bench_decode(args, torch, lsa, W, append=False)
+    torch.cuda.empty_cache()
     pre = None if args.no_prefill else bench_prefill(args, torch, lsa, W, O)
     cpu = None if args.no_cpu_baseline else cpu_baseline(dec, torch, O, args.cpu_seconds)
 
@@ -536,8 +669,13 @@ def main():
                         f"{w.num_kv_heads} KV heads ({n_str} streaming: sink {w.sink_tokens} + local "
                         f"{w.local_tokens} tokens), D={w.head_dim}, N_L={w.logical_page}, N_P={w.page_size}, "
                         f"token budget {w.token_budget}, reuse interval {w.reuse_interval}, group page scores "
-                        f"combined by {args.aggregation}; one step = selection (every {w.reuse_interval}th step) "
-                        f"+ attention with the stats refresh",
+                        f"combined by {args.aggregation}; " + (
+                            f"one step = append of the step's K/V (retrieval heads into the paged pool with "
+                            f"their statistics, streaming heads into a constant-size cache of sink + ring "
+                            f"pages) + selection (every {w.reuse_interval}th step) + attention"
+                            if dec["append"] else
+                            f"one step = selection (every {w.reuse_interval}th step) + attention with the "
+                            f"stats refresh (every head in the paged pool, window tokens pre-written)"),
             "global_batch": w.batch, "seq_len": max(w.ctx), "parallelism": "none (1 GPU)",
             "kv_replicas": args.replicas, "timing": dec["timing"],
         },
@@ -548,11 +686,32 @@ def main():
             "bound": "hbm", "achieved": round(achieved / 1e9, 1), "peak": PEAK_HBM / 1e9, "unit": "GB/s",
             "frac": round(achieved / PEAK_HBM, 4),
             "traffic": dec["traffic"],
+            "traffic_source": dec["traffic_source"] or
+            "none: no committed counter summary covers this workload on this version of decode.hip",
             "bytes_per_launch": int(dec["launch_bytes"]),
             "launch_us": round(dec["kernel_avg"] * 1e6, 2),
         },
         "cpu_baseline": cpu,
+        "lsa_version": lsa.version(),
     }
+    if dec["sel_time"]:
+        sel_bw = dec["sel_call_bytes"] / dec["sel_time"]
+        line["selection"] = {
+            "kernel": "lsa_select_pages: score_kernel (top-K in its last workgroups, or topk_kernel above "
+                      "4096 pages); one call every reuse interval",
+            "bound": "hbm", "achieved": round(sel_bw / 1e9, 1), "peak": PEAK_HBM / 1e9, "unit": "GB/s",
+            "frac": round(sel_bw / PEAK_HBM, 4), "bytes_per_call": int(dec["sel_call_bytes"]),
+            "call_us": round(dec["sel_time"] * 1e6, 2),
+        }
+    if plain is not None:
+        line["decode_without_append"] = {
+            "value": round(plain["tok_s"], 1), "unit": "tokens/s", "ms_per_step": round(plain["ms_per_step"], 5),
+            "launch_us": round(plain["kernel_avg"] * 1e6, 2),
+            "frac": round(plain["launch_bytes"] / plain["kernel_avg"] / PEAK_HBM, 4),
+            "traffic": plain["traffic"], "traffic_source": plain["traffic_source"],
+            "step": "selection (every 4th step) + attention with the statistics refresh; every head in the "
+                    "paged pool, window tokens already written",
+        }
     if pre is not None:
         line["prefill"] = {
             "workload": f"prefill, {pre['T']} tokens, {pre['Hq']} q heads / {pre['Hkv']} KV heads "
@@ -567,6 +726,9 @@ def main():
             "all_causal_tflops": round(pre["causal_tflops"], 1),
             "measured_speedup": round(pre["causal_seconds"] / pre["seconds"], 4),
             "csr_mask_ms": round(pre["csr_seconds"] * 1e3, 3),
+            "kernel_tile_counter": pre["kernel_tiles"],
+            "tile_counter_equals_oracle": pre["kernel_tiles"] == pre["tiles"],
+            "cpu_baseline": pre["cpu"],
             "roofline": {"bound": "mfma", "achieved": round(pre["tflops"], 1), "peak": PEAK_BF16 / 1e12,
                          "unit": "TFLOP/s", "frac": round(pre["tflops"] * 1e12 / PEAK_BF16, 4), "traffic": None},
         }

@@ -265,7 +265,10 @@ extern "C" {
 
 const char *lsa_last_error(void) { return g_last_error.c_str(); }
 
-const char *lsa_version(void) { return "lsa 0.1.0 gfx950"; }
+#ifndef LSA_SOURCE_SHA
+#define LSA_SOURCE_SHA "unknown"
+#endif
+const char *lsa_version(void) { return "lsa 0.2.0 gfx950 src " LSA_SOURCE_SHA; }
 
 lsa_status lsa_page_stats_bytes(const lsa_kv *kv, const lsa_heads *heads, size_t *bytes) {
     if (lsa_status s = check_kv(kv)) return s;

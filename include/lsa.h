@@ -411,7 +411,8 @@ lsa_status lsa_check_block_mask(const int32_t *row_ptr, const int32_t *col_idx,
 /* Message of the last failed call on this thread ("" if none); never NULL. */
 const char *lsa_last_error(void);
 
-/* Library version string, e.g. "lsa 0.1.0 gfx950". */
+/* Library version string, "lsa <version> gfx950 src <sha>", with the first 16
+ * hex digits of the SHA-256 of the sources the library was built from. */
 const char *lsa_version(void);
 
 #ifdef __cplusplus

@@ -51,6 +51,13 @@ def test_version(lib):
     assert lsa.version().startswith("lsa ") and "gfx950" in lsa.version()
 
 
+def test_version_names_the_sources_of_this_tree(lib):
+    """The loaded library was built from the sources in this tree: its version
+    carries their hash (a stale build fails here)."""
+    from block_sparse_attention_logical_amd import build
+    assert lsa.version().endswith("src " + build.source_sha())
+
+
 def kv_desc(dtype=lsa.BF16, heads=8, D=128, NP=64, NL=16, P=100, sz=False):
     k_sz = FAKE if sz else None
     return lsa.LsaKV(dtype, heads, D, NP, NL, 0, P, FAKE, FAKE, k_sz, k_sz)
