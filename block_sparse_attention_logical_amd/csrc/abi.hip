@@ -478,8 +478,9 @@ lsa_status lsa_select_pages(const void *q, int32_t q_dtype, const lsa_kv *kv, co
     for (int i = 0; i < kv->num_kv_heads; ++i)
         if (heads->head_kind[i] == LSA_RETRIEVAL_HEAD) sa.ret_heads[sa.n_ret++] = (uint8_t)i;
     sa.pages_per_block =
-        score_pages_per_block(kv->kv_dtype, kv->head_dim, kv->page_size, kv->logical_page, sa.fused_pt,
-                              sa.aggregation == LSA_AGG_MAX);
+        sa.aggregation == LSA_AGG_MAX
+            ? score_pages_per_block(kv->kv_dtype, kv->head_dim, kv->page_size, kv->logical_page, sa.fused_pt, true)
+            : score_loop_pages_per_block(seqs->batch, sa.n_ret, seqs->max_pages, kv->page_size, kv->logical_page);
     sa.blocks_per_head = (seqs->max_pages + sa.pages_per_block - 1) / sa.pages_per_block;
     if (lsa_status s = from_hip(launch_score(sa, (hipStream_t)stream), "select_pages score launch")) return s;
     if (sa.fused_pt > 0) return ok();              // the score kernel's last workgroups have selected

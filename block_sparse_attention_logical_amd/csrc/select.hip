@@ -540,14 +540,205 @@ __global__ __launch_bounds__(kScoreThreads) void score_kernel(ScoreArgs a) {
     }
 }
 
+// ---------------------------------------------------------------------------
+// Scoring with the group's scores summed, as a loop with a ring of loads.  A
+// workgroup covers pages_per_block physical pages of one (sequence, retrieval
+// head), several workgroups per head so that about three run on every CU.
+// The pool ids of the range are staged in LDS first; each lane group then
+// walks its logical pages j0 + lg, j0 + lg + GROUPS, ... through a ring of
+// kRing register slots: the statistics of the (k + kRing)-th page are
+// requested as the k-th is scored, so a workgroup's memory stream does not
+// drain between pages.  Every slot is always loaded (a slot past the range
+// reads the range's first page and is discarded), so the wait before a slot
+// counts exactly the loads issued after it.
+// ---------------------------------------------------------------------------
+constexpr int kRing = 8;
+constexpr int kMaxRangePages = 1024;      // physical pages per workgroup (pool ids in LDS)
+constexpr int kMaxRangeLogical = 2048;    // logical pages per workgroup (scores in LDS)
+
+template <int KV_DT, int D, int FPT>
+__global__ __launch_bounds__(kScoreThreads) void score_loop_kernel(ScoreArgs a) {
+    constexpr int EB = KV_DT == LSA_F32 ? 4 : (KV_DT == LSA_BF16 ? 2 : 1);
+    using S = ScoreShape<EB, D>;
+    constexpr int C = S::C, LPL = S::LPL, LPP = S::LPP;
+    constexpr int GROUPS = (kScoreThreads / kWave) * LPP;   // lane groups per workgroup
+    __shared__ double s_log[kMaxRangeLogical];
+    __shared__ int s_pool[kMaxRangePages];
+
+    const int blk = blockIdx.x % a.blocks_per_head;
+    const int rest = blockIdx.x / a.blocks_per_head;
+    const int r = rest % a.n_ret;
+    const int b = rest / a.n_ret;
+    const int kv = a.ret_heads[r];
+    const int lane = threadIdx.x % kWave;
+    const int wave = threadIdx.x / kWave;
+    const int lg = wave * LPP + lane / LPL;       // lane group in the workgroup
+    const int ch0 = (lane % LPL) * C;
+
+    const int g = a.page_size / a.logical_page;
+    const int m0 = blk * a.pages_per_block;
+    const int j0 = m0 * g;
+    const int L = a.seq_lens[b];
+    const int G = a.num_q_heads / a.num_kv_heads;
+    const int n_pages = (L + a.page_size - 1) / a.page_size;
+    if (m0 < n_pages) {                           // (uniform: a workgroup past the last page only arrives)
+    const int m1 = min(m0 + a.pages_per_block, n_pages);
+    const int nlog = (L + a.logical_page - 1) / a.logical_page;
+    const int j1 = min(m1 * g, nlog);
+    const int j_cur = (L - 1) / a.logical_page;   // the logical page that holds the current token
+    const size_t head_stride = (size_t)g * (KV_DT == LSA_INT4 ? D : 2 * D);
+    const size_t slot_kv = a.ph.pool_slot[kv];
+
+    for (int i = threadIdx.x; i < m1 - m0; i += kScoreThreads)
+        s_pool[i] = a.page_table[(size_t)b * a.max_pages + m0 + i];
+    double qp[C], qn[C];
+    load_q_pos_neg<C>(a, b, kv, ch0, 0, G, qp, qn);
+    double qsum = 0.0;                            // int4 only: sum over all channels of Qp + Qn
+    if constexpr (KV_DT == LSA_INT4) {
+#pragma unroll
+        for (int c = 0; c < C; ++c) qsum += qp[c] + qn[c];
+        qsum = group_sum_d<LPL>(qsum);
+    }
+    __syncthreads();
+
+    // int4: S = s * (sum_i Qp c_max + Qn c_min - z * sum_i (Qp + Qn))
+    auto finish = [&](double dot, uint32_t sz) {
+        if constexpr (KV_DT == LSA_INT4)
+            return (double)fp16_bits_to_f32(uint16_t(sz)) * (dot - (double)fp16_bits_to_f32(uint16_t(sz >> 16)) * qsum);
+        return dot;
+    };
+
+    // the current logical page, from its keys, by the wavefront whose lane
+    // groups would hold it
+    if (j_cur >= j0 && j_cur < j1 && wave == ((j_cur - j0) % GROUPS) / LPP) {
+        float cmin[C], cmax[C];
+        const size_t hp = (size_t)s_pool[j_cur / g - m0] * a.ph.pool_heads + slot_kv;
+        uint32_t sz_cur = 0;
+        if constexpr (KV_DT == LSA_INT4) sz_cur = *reinterpret_cast<const uint32_t *>(a.k_sz + hp * 2);
+        current_page_minmax<KV_DT, D, C, LPL, LPP>(a, hp * a.page_size * D, (j_cur % g) * a.logical_page,
+                                                   L - j_cur * a.logical_page, lane / LPL, ch0, cmin, cmax);
+        double c0 = 0.0, c1 = 0.0;
+#pragma unroll
+        for (int c = 0; c < C; ++c) {
+            c0 = fma(qp[c], (double)cmax[c], c0);
+            c1 = fma(qn[c], (double)cmin[c], c1);
+        }
+        const double sj = finish(group_sum_d<LPL>(c0 + c1), sz_cur);
+        if (lane == 0) s_log[j_cur - j0] = sj;
+    }
+
+    // the ring over this lane group's logical pages; the trip count is the
+    // wavefront's largest (its first lane group's), the rest is discarded
+    const int K_w = max(0, (j1 - j0 - wave * LPP + GROUPS - 1) / GROUPS);
+    uint4 rl[kRing], rh[kRing];
+    uint32_t rs[kRing];
+    auto issue = [&](int s, int k) {
+        int j = j0 + lg + k * GROUPS;
+        if (j >= j1) j = j0;                      // past the range: any page of it, discarded
+        const size_t hp = (size_t)s_pool[j / g - m0] * a.ph.pool_heads + slot_kv;
+        const int jl = j % g;
+        if constexpr (KV_DT == LSA_INT4) {
+            rl[s] = load_stream16(static_cast<const uint8_t *>(a.stats) + hp * head_stride + (size_t)jl * D + ch0);
+            rs[s] = load_stream4(a.k_sz + hp * 2);
+        } else {
+            const char *st = static_cast<const char *>(a.stats) + (hp * head_stride + (size_t)jl * 2 * D + ch0) * EB;
+            rl[s] = load_stream16(st);
+            rh[s] = load_stream16(st + (size_t)D * EB);
+        }
+    };
+#pragma unroll
+    for (int s = 0; s < kRing; ++s) issue(s, s);
+    for (int k0 = 0; k0 < K_w; k0 += kRing) {
+#pragma unroll
+        for (int s = 0; s < kRing; ++s) {
+            const int k = k0 + s;
+            double c0 = 0.0, c1 = 0.0;
+            if constexpr (KV_DT == LSA_INT4) {
+                const uint32_t wd[4] = {rl[s].x, rl[s].y, rl[s].z, rl[s].w};
+#pragma unroll
+                for (int c = 0; c < C; ++c) {
+                    const uint32_t byte = (wd[c / 4] >> (8 * (c % 4))) & 0xFFu;
+                    c0 = fma(qp[c], (double)(byte >> 4), c0);
+                    c1 = fma(qn[c], (double)(byte & 15u), c1);
+                }
+            } else {
+                const uint32_t wl[4] = {rl[s].x, rl[s].y, rl[s].z, rl[s].w};
+                const uint32_t wh[4] = {rh[s].x, rh[s].y, rh[s].z, rh[s].w};
+#pragma unroll
+                for (int c = 0; c < C; ++c) {
+                    float kmin, kmax;
+                    if constexpr (KV_DT == LSA_BF16) {
+                        kmin = (c & 1) ? bf16_hi(wl[c / 2]) : bf16_lo(wl[c / 2]);
+                        kmax = (c & 1) ? bf16_hi(wh[c / 2]) : bf16_lo(wh[c / 2]);
+                    } else {
+                        kmin = __uint_as_float(wl[c]);
+                        kmax = __uint_as_float(wh[c]);
+                    }
+                    c0 = fma(qp[c], (double)kmax, c0);
+                    c1 = fma(qn[c], (double)kmin, c1);
+                }
+            }
+            const double sj = finish(group_sum_d<LPL>(c0 + c1), rs[s]);
+            const int j = j0 + lg + k * GROUPS;
+            if (k < K_w && j < j1 && j != j_cur && lane % LPL == 0) s_log[j - j0] = sj;
+            issue(s, k + kRing);                  // (past the range: a discarded reload)
+        }
+    }
+    __syncthreads();
+    // P_m = max over the logical pages of physical page m
+    for (int m = m0 + threadIdx.x; m < m1; m += blockDim.x) {
+        const int ja = m * g - j0, jb = min((m + 1) * g, j1) - j0;
+        double best = s_log[ja];
+        for (int jj = ja + 1; jj < jb; ++jj) best = fmax(best, s_log[jj]);
+        double *dst = a.phys + ((size_t)b * a.num_kv_heads + kv) * a.max_pages + m;
+        if constexpr (FPT > 0) store_agent_d(dst, best + 0.0);
+        else *dst = best + 0.0;
+    }
+    }
+    if constexpr (FPT > 0) {
+        __shared__ int s_last;
+        // this wavefront's score stores have reached the coherence point
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        __syncthreads();
+        if (threadIdx.x == 0) {
+            int32_t *cnt = a.counters + (size_t)b * a.num_kv_heads + kv;
+            const int old = __hip_atomic_fetch_add(cnt, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            const int last = old == a.blocks_per_head - 1;
+            if (last) __hip_atomic_store(cnt, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            s_last = last;
+        }
+        __syncthreads();
+        if (s_last)
+            topk_rows<kScoreThreads, (FPT > 0 ? FPT : 1), true>(
+                a.phys + ((size_t)b * a.num_kv_heads + kv) * a.max_pages, L, a.page_size, a.max_pages, a.k_pages,
+                a.selected + ((size_t)b * a.num_kv_heads + kv) * a.k_pages);
+    }
+}
+
 template <int KV_DT, bool AGG_MAX, int FPT>
 void launch_score_fpt(const ScoreArgs &a, unsigned grid, hipStream_t s) {
     if (a.head_dim == 128) hipLaunchKernelGGL((score_kernel<KV_DT, 128, AGG_MAX, FPT>), dim3(grid), dim3(kScoreThreads), 0, s, a);
     else hipLaunchKernelGGL((score_kernel<KV_DT, 64, AGG_MAX, FPT>), dim3(grid), dim3(kScoreThreads), 0, s, a);
 }
 
+template <int KV_DT, int FPT>
+void launch_score_loop_fpt(const ScoreArgs &a, unsigned grid, hipStream_t s) {
+    if (a.head_dim == 128) hipLaunchKernelGGL((score_loop_kernel<KV_DT, 128, FPT>), dim3(grid), dim3(kScoreThreads), 0, s, a);
+    else hipLaunchKernelGGL((score_loop_kernel<KV_DT, 64, FPT>), dim3(grid), dim3(kScoreThreads), 0, s, a);
+}
+
 template <int KV_DT, bool AGG_MAX>
 hipError_t launch_score_agg(const ScoreArgs &a, unsigned grid, hipStream_t s) {
+    if constexpr (!AGG_MAX) {
+        switch (a.fused_pt) {
+            case 0: launch_score_loop_fpt<KV_DT, 0>(a, grid, s); break;
+            case 4: launch_score_loop_fpt<KV_DT, 4>(a, grid, s); break;
+            case 8: launch_score_loop_fpt<KV_DT, 8>(a, grid, s); break;
+            case 16: launch_score_loop_fpt<KV_DT, 16>(a, grid, s); break;
+            default: return hipErrorInvalidValue;
+        }
+        return hipGetLastError();
+    }
     switch (a.fused_pt) {
         case 0: launch_score_fpt<KV_DT, AGG_MAX, 0>(a, grid, s); break;
         case 4: launch_score_fpt<KV_DT, AGG_MAX, 4>(a, grid, s); break;
@@ -565,6 +756,18 @@ hipError_t launch_score_dt(const ScoreArgs &a, unsigned grid, hipStream_t s) {
 }
 
 }  // namespace
+
+int score_loop_pages_per_block(int batch, int n_ret, int max_pages, int page_size, int logical_page) {
+    // about three workgroups per CU over the chip, within the LDS range limits
+    const long long heads = (long long)batch * n_ret;
+    const long long slots = 3LL * 256;
+    const long long wph = heads >= slots ? 1 : (slots + heads - 1) / heads;
+    long long ppb = (max_pages + wph - 1) / wph;
+    const int g = page_size / logical_page;
+    ppb = ppb < kMaxRangeLogical / g ? ppb : kMaxRangeLogical / g;
+    ppb = ppb < kMaxRangePages ? ppb : kMaxRangePages;
+    return (int)(ppb < 1 ? 1 : ppb);
+}
 
 int score_pages_per_block(int kv_dtype, int head_dim, int page_size, int logical_page, int fused_pt, bool agg_max) {
     // lane groups per workgroup x iterations, in logical pages, over g
