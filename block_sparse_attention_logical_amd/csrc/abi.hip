@@ -463,7 +463,7 @@ lsa_status lsa_select_pages(const void *q, int32_t q_dtype, const lsa_kv *kv, co
                                          decode_counter_bytes(seqs->batch, kv->num_kv_heads));
     sa.selected = selected;
     sa.k_pages = token_budget / kv->page_size;
-    sa.fused_pt = score_fused_pt(seqs->max_pages);
+    sa.fused_pt = score_fused_pt(seqs->max_pages, heads->score_aggregation == LSA_AGG_MAX);
     sa.batch = seqs->batch;
     sa.max_pages = seqs->max_pages;
     sa.num_q_heads = heads->num_q_heads;

@@ -383,7 +383,7 @@ hipError_t launch_score(const ScoreArgs &a, hipStream_t s);
 int score_pages_per_block(int kv_dtype, int head_dim, int page_size, int logical_page, int fused_pt, bool agg_max);
 int score_loop_pages_per_block(int batch, int n_ret, int max_pages, int page_size, int logical_page);
 int topk_max_pages();
-int score_fused_pt(int max_pages);   // top-K pages per thread inside the score kernel, 0: a separate launch
+int score_fused_pt(int max_pages, bool agg_max);   // top-K pages per thread inside the score kernel, 0: a separate launch
 hipError_t launch_topk(const TopkArgs &a, hipStream_t s);
 hipError_t launch_decode(const DecodeArgs &a, int q_dtype, int kv_dtype, hipStream_t s);
 hipError_t launch_prefill(const PrefillArgs &a, int dtype, hipStream_t s);

@@ -229,17 +229,10 @@ __device__ __forceinline__ void topk_rows(const double *P, int L, int page_size,
     __shared__ unsigned long long sh_and[NT / kWave], sh_or[NT / kWave];
     const int tid = threadIdx.x;
 
-    // thread t owns the contiguous pages [t*seg, t*seg + cnt); the scores are
-    // loaded for every row slot at once, and the entries past the sequence's
-    // last page are dropped afterwards
+    // thread t owns the contiguous pages [t*seg, t*seg + cnt); the scores of
+    // its pages are loaded together and turned into keys as they arrive
     constexpr int seg = PT;
     const int i0 = min(max_pages, tid * seg);
-    double pv[PT];
-#pragma unroll
-    for (int e = 0; e < PT; ++e) {
-        if constexpr (AGENT) pv[e] = i0 + e < max_pages ? load_agent_d(P + i0 + e) : 0.0;
-        else pv[e] = i0 + e < max_pages ? P[i0 + e] : 0.0;
-    }
     const int n = (L + page_size - 1) / page_size;
     if (n <= K) {                                 // every page, ascending, padded with -1
         for (int i = tid; i < K; i += NT) out[i] = i < n ? i : -1;
@@ -248,7 +241,11 @@ __device__ __forceinline__ void topk_rows(const double *P, int L, int page_size,
     const int cnt = max(0, min(n, i0 + seg) - i0);
     unsigned long long key[PT];
 #pragma unroll
-    for (int e = 0; e < PT; ++e) key[e] = e < cnt ? order_key(pv[e]) : 0ull;
+    for (int e = 0; e < PT; ++e) {
+        double v = 0.0;
+        if (e < cnt) v = AGENT ? load_agent_d(P + i0 + e) : P[i0 + e];
+        key[e] = e < cnt ? order_key(v) : 0ull;
+    }
 
     // The bits above the highest one that differs between keys are shared by
     // every key and decide nothing: the radix passes start there, each pass
@@ -543,7 +540,7 @@ __global__ __launch_bounds__(kScoreThreads) void score_kernel(ScoreArgs a) {
 // ---------------------------------------------------------------------------
 // Scoring with the group's scores summed, as a loop with a ring of loads.  A
 // workgroup covers pages_per_block physical pages of one (sequence, retrieval
-// head), several workgroups per head so that about three run on every CU.
+// head), several workgroups per head so that about four run on every CU.
 // The pool ids of the range are staged in LDS first; each lane group then
 // walks its logical pages j0 + lg, j0 + lg + GROUPS, ... through a ring of
 // kRing register slots: the statistics of the (k + kRing)-th page are
@@ -563,7 +560,7 @@ __global__ __launch_bounds__(kScoreThreads) void score_loop_kernel(ScoreArgs a) 
     constexpr int C = S::C, LPL = S::LPL, LPP = S::LPP;
     constexpr int GROUPS = (kScoreThreads / kWave) * LPP;   // lane groups per workgroup
     __shared__ double s_log[kMaxRangeLogical];
-    __shared__ int s_pool[kMaxRangePages];
+    __shared__ unsigned long long s_hp[kMaxRangePages];   // (pool page, head) unit of each page of the range
 
     const int blk = blockIdx.x % a.blocks_per_head;
     const int rest = blockIdx.x / a.blocks_per_head;
@@ -586,11 +583,16 @@ __global__ __launch_bounds__(kScoreThreads) void score_loop_kernel(ScoreArgs a) 
     const int nlog = (L + a.logical_page - 1) / a.logical_page;
     const int j1 = min(m1 * g, nlog);
     const int j_cur = (L - 1) / a.logical_page;   // the logical page that holds the current token
-    const size_t head_stride = (size_t)g * (KV_DT == LSA_INT4 ? D : 2 * D);
     const size_t slot_kv = a.ph.pool_slot[kv];
+    // g, the statistics of one (page, head) unit (g * D bytes for int4, g * 2D
+    // elements otherwise) and the row of a logical page are powers of two:
+    // addresses are shifts
+    const int gs = __builtin_ctz(g);
+    const int unit_shift = gs + __builtin_ctz(D) + (KV_DT == LSA_INT4 ? 0 : 1 + __builtin_ctz(EB));
+    const int row_shift = __builtin_ctz(D) + (KV_DT == LSA_INT4 ? 0 : 1 + __builtin_ctz(EB));
 
     for (int i = threadIdx.x; i < m1 - m0; i += kScoreThreads)
-        s_pool[i] = a.page_table[(size_t)b * a.max_pages + m0 + i];
+        s_hp[i] = (unsigned long long)a.page_table[(size_t)b * a.max_pages + m0 + i] * a.ph.pool_heads + slot_kv;
     double qp[C], qn[C];
     load_q_pos_neg<C>(a, b, kv, ch0, 0, G, qp, qn);
     double qsum = 0.0;                            // int4 only: sum over all channels of Qp + Qn
@@ -612,7 +614,7 @@ __global__ __launch_bounds__(kScoreThreads) void score_loop_kernel(ScoreArgs a) 
     // groups would hold it
     if (j_cur >= j0 && j_cur < j1 && wave == ((j_cur - j0) % GROUPS) / LPP) {
         float cmin[C], cmax[C];
-        const size_t hp = (size_t)s_pool[j_cur / g - m0] * a.ph.pool_heads + slot_kv;
+        const size_t hp = s_hp[(j_cur >> gs) - m0];
         uint32_t sz_cur = 0;
         if constexpr (KV_DT == LSA_INT4) sz_cur = *reinterpret_cast<const uint32_t *>(a.k_sz + hp * 2);
         current_page_minmax<KV_DT, D, C, LPL, LPP>(a, hp * a.page_size * D, (j_cur % g) * a.logical_page,
@@ -635,16 +637,12 @@ __global__ __launch_bounds__(kScoreThreads) void score_loop_kernel(ScoreArgs a) 
     auto issue = [&](int s, int k) {
         int j = j0 + lg + k * GROUPS;
         if (j >= j1) j = j0;                      // past the range: any page of it, discarded
-        const size_t hp = (size_t)s_pool[j / g - m0] * a.ph.pool_heads + slot_kv;
-        const int jl = j % g;
-        if constexpr (KV_DT == LSA_INT4) {
-            rl[s] = load_stream16(static_cast<const uint8_t *>(a.stats) + hp * head_stride + (size_t)jl * D + ch0);
-            rs[s] = load_stream4(a.k_sz + hp * 2);
-        } else {
-            const char *st = static_cast<const char *>(a.stats) + (hp * head_stride + (size_t)jl * 2 * D + ch0) * EB;
-            rl[s] = load_stream16(st);
-            rh[s] = load_stream16(st + (size_t)D * EB);
-        }
+        const unsigned long long hp = s_hp[(j >> gs) - m0];
+        const char *st = static_cast<const char *>(a.stats) + (hp << unit_shift) +
+                         (((j & (g - 1)) << row_shift) + ch0 * EB);
+        rl[s] = load_stream16(st);
+        if constexpr (KV_DT == LSA_INT4) rs[s] = load_stream4(a.k_sz + hp * 2);
+        else rh[s] = load_stream16(st + D * EB);
     };
 #pragma unroll
     for (int s = 0; s < kRing; ++s) issue(s, s);
@@ -654,13 +652,20 @@ __global__ __launch_bounds__(kScoreThreads) void score_loop_kernel(ScoreArgs a) 
             const int k = k0 + s;
             double c0 = 0.0, c1 = 0.0;
             if constexpr (KV_DT == LSA_INT4) {
+                // four independent product chains (even / odd channels)
                 const uint32_t wd[4] = {rl[s].x, rl[s].y, rl[s].z, rl[s].w};
+                double c2 = 0.0, c3 = 0.0;
 #pragma unroll
-                for (int c = 0; c < C; ++c) {
-                    const uint32_t byte = (wd[c / 4] >> (8 * (c % 4))) & 0xFFu;
-                    c0 = fma(qp[c], (double)(byte >> 4), c0);
-                    c1 = fma(qn[c], (double)(byte & 15u), c1);
+                for (int c = 0; c < C; c += 2) {
+                    const uint32_t b0 = (wd[c / 4] >> (8 * (c % 4))) & 0xFFu;
+                    const uint32_t b1 = (wd[c / 4] >> (8 * (c % 4) + 8)) & 0xFFu;
+                    c0 = fma(qp[c], (double)(b0 >> 4), c0);
+                    c1 = fma(qn[c], (double)(b0 & 15u), c1);
+                    c2 = fma(qp[c + 1], (double)(b1 >> 4), c2);
+                    c3 = fma(qn[c + 1], (double)(b1 & 15u), c3);
                 }
+                c0 += c2;
+                c1 += c3;
             } else {
                 const uint32_t wl[4] = {rl[s].x, rl[s].y, rl[s].z, rl[s].w};
                 const uint32_t wh[4] = {rh[s].x, rh[s].y, rh[s].z, rh[s].w};
@@ -758,9 +763,10 @@ hipError_t launch_score_dt(const ScoreArgs &a, unsigned grid, hipStream_t s) {
 }  // namespace
 
 int score_loop_pages_per_block(int batch, int n_ret, int max_pages, int page_size, int logical_page) {
-    // about three workgroups per CU over the chip, within the LDS range limits
+    // about four workgroups per CU over the chip (the kernel fits four
+    // wavefronts per SIMD), within the LDS range limits
     const long long heads = (long long)batch * n_ret;
-    const long long slots = 3LL * 256;
+    const long long slots = 4LL * 256;
     const long long wph = heads >= slots ? 1 : (slots + heads - 1) / heads;
     long long ppb = (max_pages + wph - 1) / wph;
     const int g = page_size / logical_page;
@@ -782,8 +788,11 @@ int score_pages_per_block(int kv_dtype, int head_dim, int page_size, int logical
 
 int topk_max_pages() { return kTopkThreads * kTopkPerThread; }
 
-int score_fused_pt(int max_pages) {
+int score_fused_pt(int max_pages, bool agg_max) {
     const int per = (max_pages + kScoreThreads - 1) / kScoreThreads;
+    // (a 32-page instance was slower: it cost the scoring kernel a wavefront
+    // per SIMD, and its ranking left half the threads idle)
+    (void)agg_max;
     return per <= 4 ? 4 : per <= 8 ? 8 : per <= 16 ? 16 : 0;
 }
 
