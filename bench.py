@@ -10,7 +10,10 @@ append the step's token K/V (retrieval heads into the paged pool, which holds
 only them, with their logical page's statistics; streaming heads into a
 constant-size cache of sink pages and a ring of recent pages), select pages
 (every R = 4 steps, reused otherwise; the current logical page is scored from
-its keys), then sparse decode attention.  --no-append times the step without
+its keys), then sparse decode attention, in two launches (lsa_decode_step: the
+selection takes the new key from the step's rows, the attention kernel attends
+the new token from them and writes it to its page).  --unfused times the same
+step as three calls (append, select, attend).  --no-append times the step without
 the append (every head in the paged pool with the window tokens already in it;
 attention refreshes the statistics of the current logical page).  Steps cycle over
 `--replicas` independent copies of the layer's KV pool (distinct layers of a
@@ -67,6 +70,9 @@ def parse():
     ap.add_argument("--no-append", action="store_true",
                     help="time the step without the append: every head in the paged pool (its window tokens "
                          "already written), selection + attention with the statistics refresh")
+    ap.add_argument("--unfused", action="store_true",
+                    help="time the appending step as three calls (append, select, attend) instead of "
+                         "lsa_decode_step's two launches")
     ap.add_argument("--page-size", type=int, default=None, help="physical page size N_P of the decode pool")
     ap.add_argument("--logical-page", type=int, default=None, help="logical page size N_L of the statistics")
     ap.add_argument("--steps", type=int, default=640, help="timed decode steps (rounded up to whole cycles)")
@@ -188,7 +194,7 @@ def counters_for(kernel_tag, source_file, launch_bytes):
 # decode (config 2)
 # ---------------------------------------------------------------------------
 
-def bench_decode(args, torch, lsa, W, append=True):
+def bench_decode(args, torch, lsa, W, append=True, fused=True):
     dev = "cuda"
     cfg = WORKLOADS[args.workload][0]
     R = args.reuse or W.DECODE_CONFIGS[cfg]["reuse_interval"]
@@ -230,21 +236,24 @@ def bench_decode(args, torch, lsa, W, append=True):
                          device=dev)
     ws_dec = torch.zeros(lsa.decode_workspace(layers[0][0], w.page_table, lens[0], hd, w.token_budget),
                          dtype=torch.uint8, device=dev)
+    ws_step = torch.zeros(lsa.decode_step_workspace(layers[0][0], w.page_table, lens[0], hd, w.token_budget),
+                          dtype=torch.uint8, device=dev)
     out = torch.empty_like(w.q[0])
     cycle = nrep * R
+    fused = fused and append
 
-    def step(k, timers=None):
+    def step(k):
         l, s = k % nrep, (k // nrep) % R
         kv, stats, sel = layers[l]
+        if fused:              # append + select + attend in two launches
+            lsa.decode_step(w.q[s], kv, w.page_table, lens[s], hd, rows[s][0], rows[s][1], stats, w.token_budget,
+                            s, R, sel, out, ws_step, *rows[s][2:])
+            return
         if append:             # the step's token, with its logical page's statistics
             lsa.append_kv(kv, w.page_table, lens[s], hd, *rows[s], stats=stats)
         lsa.select_pages(w.q[s], kv, stats, w.page_table, lens[s], hd, w.token_budget, s, R, sel, ws_sel)
-        if timers is not None:
-            timers[0].record()
         lsa.sparse_decode_attn(w.q[s], kv, w.page_table, lens[s], hd, sel, w.token_budget, out, ws_dec,
                                stats=None if append else stats)
-        if timers is not None:
-            timers[1].record()
 
     # warm-up (eager): every layer selects at least once
     for k in range(max(args.warmup, cycle)):
@@ -289,13 +298,20 @@ def bench_decode(args, torch, lsa, W, append=True):
     elapsed = t0.elapsed_time(t1) / 1e3
 
     # per-launch duration of the decode attention kernel: the attention calls
-    # of one cycle (every replica and step, with the statistics refresh) are
-    # captured alone in a graph and replayed between two HIP events on the
-    # stream they run on; without a graph, events bracket eager launches held
-    # back by a spin kernel
+    # of one cycle (every replica and step; with the statistics refresh, or
+    # in the fused step with the append) are captured alone in a graph and
+    # replayed between two HIP events on the stream they run on; without a
+    # graph, events bracket eager launches held back by a spin kernel.  The
+    # fused step's attention launch alone is lsa_decode_step on a step that
+    # reuses the selection (decode_step 1 with reuse interval 2); writing the
+    # same token again is idempotent.
     def attend(k):
         l, s = k % nrep, (k // nrep) % R
         kv, stats, sel = layers[l]
+        if fused:
+            lsa.decode_step(w.q[s], kv, w.page_table, lens[s], hd, rows[s][0], rows[s][1], stats, w.token_budget,
+                            1, 2, sel, out, ws_step, *rows[s][2:])
+            return
         lsa.sparse_decode_attn(w.q[s], kv, w.page_table, lens[s], hd, sel, w.token_budget, out, ws_dec,
                                stats=None if append else stats)
 
@@ -326,7 +342,9 @@ def bench_decode(args, torch, lsa, W, append=True):
         torch.cuda.synchronize()
         torch.cuda._sleep(int(2.4e9 * 0.25))        # ~0.25 s at 2.4 GHz
         for k in range(n_kt):
-            step(k, timers[k])
+            timers[k][0].record()
+            attend(k)
+            timers[k][1].record()
         torch.cuda.synchronize()
         kt = sorted(a_.elapsed_time(b_) / 1e3 for a_, b_ in timers)
     kernel_avg = sum(kt) / len(kt)
@@ -393,18 +411,20 @@ def bench_decode(args, torch, lsa, W, append=True):
     # retrieval heads, reads and writes one logical page's statistics
     app_bytes = (B * Hkv * 2 * D * eb + B * n_ret * (2 * lp_bytes)) if append else 0
     step_bytes = launch_bytes + sel_bytes + app_bytes
+    if fused:              # the attention launch does the append's writes
+        launch_bytes += app_bytes
     tok_s = B * steps / elapsed
     src = os.path.join(ROOT, "block_sparse_attention_logical_amd", "csrc", "decode.hip")
     # the workload the counter summary covers
     default = args.workload == "llama3-8b" and R == 4 and args.page_size in (None, 64) and \
-        args.logical_page in (None, 16) and append and args.aggregation == "sum"
-    traffic = counters_for("decode_attn_cfg2", src, launch_bytes) if default else None
+        args.logical_page in (None, 16) and fused and args.aggregation == "sum"
+    traffic = counters_for("decode_step_cfg2", src, launch_bytes) if default else None
     return dict(
         w=w, agg=args.aggregation, steps=steps, elapsed=elapsed, tok_s=tok_s, ms_per_step=elapsed / steps * 1e3,
         step_bytes=step_bytes, launch_bytes=launch_bytes, kernel_avg=kernel_avg,
-        kernel_p50=kt[len(kt) // 2], timing=timing, append=append,
+        kernel_p50=kt[len(kt) // 2], timing=timing, append=append, fused=fused,
         traffic=traffic,
-        traffic_source=(f"profiles/decode_attn_cfg2_counters.txt, taken on decode.hip sha {sha_of(src)}"
+        traffic_source=(f"profiles/decode_step_cfg2_counters.txt, taken on decode.hip sha {sha_of(src)}"
                         if traffic is not None else None),
         sel_time=sel_time, sel_call_bytes=sel_call_bytes,
     )
@@ -635,10 +655,12 @@ def main():
                           "csr_mask_ms": round(pre["csr_seconds"] * 1e3, 3),
                           "measured_speedup": round(pre["causal_seconds"] / pre["seconds"], 4)}))
         return
-    dec = bench_decode(args, torch, lsa, W, append=not args.no_append)
+    dec = bench_decode(args, torch, lsa, W, append=not args.no_append, fused=not args.unfused)
     torch.cuda.empty_cache()
-    # the same layer's step without the append (every head in the paged pool),
-    # the step the previous measurements used
+    # the same step as three calls (append, select, attend), and the step
+    # without the append (every head in the paged pool)
+    three = None if (args.no_append or args.unfused) else bench_decode(args, torch, lsa, W, append=True, fused=False)
+    torch.cuda.empty_cache()
     plain = None if args.no_append else bench_decode(args, torch, lsa, W, append=False)
     torch.cuda.empty_cache()
     pre = None if args.no_prefill else bench_prefill(args, torch, lsa, W, O)
@@ -673,6 +695,8 @@ def main():
                             f"one step = append of the step's K/V (retrieval heads into the paged pool with "
                             f"their statistics, streaming heads into a constant-size cache of sink + ring "
                             f"pages) + selection (every {w.reuse_interval}th step) + attention"
+                            + (" in two launches (lsa_decode_step: the attention kernel appends)"
+                               if dec["fused"] else " as three calls")
                             if dec["append"] else
                             f"one step = selection (every {w.reuse_interval}th step) + attention with the "
                             f"stats refresh (every head in the paged pool, window tokens pre-written)"),
@@ -682,7 +706,9 @@ def main():
         "decode_hbm_gbps": round(dec["step_bytes"] / (dec["ms_per_step"] / 1e3) / 1e9, 1),
         "decode_step_bytes": int(dec["step_bytes"]),
         "roofline": {
-            "kernel": "lsa_sparse_decode_attn: decode_mfma_kernel (split-KV pass with the merge in its last workgroup per head)",
+            "kernel": ("lsa_decode_step: decode_mfma_kernel with the fused append" if dec["fused"] else
+                       "lsa_sparse_decode_attn: decode_mfma_kernel") +
+                      " (split-KV pass with the merge in its last workgroup per head)",
             "bound": "hbm", "achieved": round(achieved / 1e9, 1), "peak": PEAK_HBM / 1e9, "unit": "GB/s",
             "frac": round(achieved / PEAK_HBM, 4),
             "traffic": dec["traffic"],
@@ -702,6 +728,13 @@ def main():
             "bound": "hbm", "achieved": round(sel_bw / 1e9, 1), "peak": PEAK_HBM / 1e9, "unit": "GB/s",
             "frac": round(sel_bw / PEAK_HBM, 4), "bytes_per_call": int(dec["sel_call_bytes"]),
             "call_us": round(dec["sel_time"] * 1e6, 2),
+        }
+    if three is not None:
+        line["decode_three_calls"] = {
+            "value": round(three["tok_s"], 1), "unit": "tokens/s", "ms_per_step": round(three["ms_per_step"], 5),
+            "launch_us": round(three["kernel_avg"] * 1e6, 2),
+            "frac": round(three["launch_bytes"] / three["kernel_avg"] / PEAK_HBM, 4),
+            "step": "the same step as lsa_append_kv + lsa_select_pages + lsa_sparse_decode_attn",
         }
     if plain is not None:
         line["decode_without_append"] = {

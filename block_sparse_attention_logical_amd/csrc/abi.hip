@@ -251,10 +251,28 @@ __global__ void zero_i32_kernel(int32_t *p, int n) {
     if (i < n) p[i] = 0;
 }
 
+// The newest token's rows that a decode step appends (all NULL: none).
+struct NewToken {
+    const void *k = nullptr, *v = nullptr;
+    const uint16_t *k_sz = nullptr, *v_sz = nullptr;
+};
+
 lsa_status decode_attn_impl(const void *q, int32_t q_dtype, const lsa_kv *kv, const lsa_seqs *seqs,
                             const lsa_heads *heads, const int32_t *selected, int32_t token_budget,
                             float softmax_scale, void *out, void *stats, void *workspace, size_t workspace_bytes,
-                            bool clear_counters, hipStream_t stream);
+                            bool clear_counters, const NewToken &nt, hipStream_t stream, bool check_only = false);
+
+lsa_status select_impl(const void *q, int32_t q_dtype, const lsa_kv *kv, const void *stats, const lsa_seqs *seqs,
+                       const lsa_heads *heads, int32_t token_budget, int32_t decode_step, int32_t reuse_interval,
+                       int32_t *selected, void *workspace, size_t workspace_bytes, const NewToken &nt,
+                       hipStream_t stream, bool check_only = false);
+
+lsa_status check_new_token(const lsa_kv *kv, const NewToken &nt) {
+    if (!nt.k || !nt.v) return fail(LSA_ERR_INVALID_ARG, "k_new and v_new must be non-NULL");
+    if ((kv->kv_dtype == LSA_INT4) != (nt.k_sz != nullptr && nt.v_sz != nullptr))
+        return fail(LSA_ERR_INVALID_ARG, "k_new_sz / v_new_sz are needed for int4 pools and only for them");
+    return LSA_OK;
+}
 
 }  // namespace
 }  // namespace lsa
@@ -337,9 +355,7 @@ lsa_status lsa_append_kv(const lsa_kv *kv, const lsa_seqs *seqs, const lsa_heads
     if (lsa_status s = check_seqs(seqs)) return s;
     if (lsa_status s = check_heads(heads, kv, true)) return s;
     if (lsa_status s = check_pool(kv, heads)) return s;
-    if (!k_new || !v_new) return fail(LSA_ERR_INVALID_ARG, "k_new and v_new must be non-NULL");
-    if ((kv->kv_dtype == LSA_INT4) != (k_new_sz != nullptr && v_new_sz != nullptr))
-        return fail(LSA_ERR_INVALID_ARG, "k_new_sz / v_new_sz are needed for int4 pools and only for them");
+    if (lsa_status s = check_new_token(kv, NewToken{k_new, v_new, k_new_sz, v_new_sz})) return s;
     AppendArgs a{};
     a.k_new = k_new;
     a.v_new = v_new;
@@ -427,6 +443,95 @@ lsa_status lsa_select_pages(const void *q, int32_t q_dtype, const lsa_kv *kv, co
                             const lsa_seqs *seqs, const lsa_heads *heads, int32_t token_budget,
                             int32_t decode_step, int32_t reuse_interval, int32_t *selected,
                             void *workspace, size_t workspace_bytes, void *stream) {
+    return select_impl(q, q_dtype, kv, stats, seqs, heads, token_budget, decode_step, reuse_interval, selected,
+                       workspace, workspace_bytes, NewToken{}, (hipStream_t)stream);
+}
+
+lsa_status lsa_decode_workspace(const lsa_kv *kv, const lsa_seqs *seqs, const lsa_heads *heads,
+                                int32_t token_budget, size_t *bytes) {
+    if (lsa_status s = check_kv(kv)) return s;
+    if (lsa_status s = check_seqs(seqs)) return s;
+    if (lsa_status s = check_heads(heads, kv, true)) return s;
+    if (!bytes) return fail(LSA_ERR_INVALID_ARG, "bytes is NULL");
+    if (token_budget < kv->page_size || token_budget % kv->page_size != 0)
+        return fail(LSA_ERR_INVALID_ARG, "token_budget %d is not a positive multiple of page_size %d", token_budget,
+                    kv->page_size);
+    const DecodeGeom g = decode_geometry(kv, heads, token_budget);
+    *bytes = decode_counter_bytes(seqs->batch, kv->num_kv_heads) +
+             align_up((size_t)seqs->batch * kv->num_kv_heads * g.chunks_max * g.rec_floats * sizeof(float));
+    return ok();
+}
+
+lsa_status lsa_sparse_decode_attn(const void *q, int32_t q_dtype, const lsa_kv *kv, const lsa_seqs *seqs,
+                                  const lsa_heads *heads, const int32_t *selected, int32_t token_budget,
+                                  float softmax_scale, void *out, void *stats, void *workspace,
+                                  size_t workspace_bytes, void *stream) {
+    return decode_attn_impl(q, q_dtype, kv, seqs, heads, selected, token_budget, softmax_scale, out, stats,
+                            workspace, workspace_bytes, false, NewToken{}, (hipStream_t)stream);
+}
+
+lsa_status lsa_sparse_decode_attn_noalloc(const void *q, int32_t q_dtype, const lsa_kv *kv, const lsa_seqs *seqs,
+                                          const lsa_heads *heads, const int32_t *selected, int32_t token_budget,
+                                          float softmax_scale, void *out, void *stats, void *stream) {
+    return decode_attn_impl(q, q_dtype, kv, seqs, heads, selected, token_budget, softmax_scale, out, stats,
+                            nullptr, 0, true, NewToken{}, (hipStream_t)stream);
+}
+
+
+lsa_status lsa_decode_step_workspace(const lsa_kv *kv, const lsa_seqs *seqs, const lsa_heads *heads,
+                                     int32_t token_budget, size_t *bytes) {
+    size_t sel = 0, dec = 0;
+    if (lsa_status s = lsa_select_pages_workspace(kv, seqs, heads, &sel)) return s;
+    if (lsa_status s = lsa_decode_workspace(kv, seqs, heads, token_budget, &dec)) return s;
+    *bytes = std::max(sel, dec);
+    return ok();
+}
+
+lsa_status lsa_decode_step(const void *q, int32_t q_dtype, const lsa_kv *kv, const lsa_seqs *seqs,
+                           const lsa_heads *heads, const void *k_new, const void *v_new, const uint16_t *k_new_sz,
+                           const uint16_t *v_new_sz, void *stats, int32_t token_budget, int32_t decode_step,
+                           int32_t reuse_interval, int32_t *selected, float softmax_scale, void *out,
+                           void *workspace, size_t workspace_bytes, void *stream) {
+    if (lsa_status s = check_kv(kv)) return s;
+    if (lsa_status s = check_seqs(seqs)) return s;
+    if (lsa_status s = check_heads(heads, kv, true)) return s;
+    const NewToken nt{k_new, v_new, k_new_sz, v_new_sz};
+    if (lsa_status s = check_new_token(kv, nt)) return s;
+    const bool any_ret = count_kind(heads, kv->num_kv_heads, LSA_RETRIEVAL_HEAD) > 0;
+    if (any_ret && !stats) return fail(LSA_ERR_INVALID_ARG, "stats is NULL but retrieval heads exist");
+    size_t need = 0;
+    if (lsa_status s = lsa_decode_step_workspace(kv, seqs, heads, token_budget, &need)) return s;
+    if (!workspace || workspace_bytes < need)
+        return fail(LSA_ERR_WORKSPACE, "workspace of %zu bytes, need %zu", workspace_bytes, need);
+    const hipStream_t st = (hipStream_t)stream;
+    // every argument of both launches is checked before the first one
+    if (any_ret)
+        if (lsa_status s = select_impl(q, q_dtype, kv, stats, seqs, heads, token_budget, decode_step, reuse_interval,
+                                       selected, workspace, workspace_bytes, nt, st, true))
+            return s;
+    if (lsa_status s = decode_attn_impl(q, q_dtype, kv, seqs, heads, selected, token_budget, softmax_scale, out,
+                                        stats, workspace, workspace_bytes, false, nt, st, true))
+        return s;
+    // both launches start from zero arrival counters and leave them zero, so
+    // they share the workspace in stream order
+    if (any_ret) {
+        if (lsa_status s = select_impl(q, q_dtype, kv, stats, seqs, heads, token_budget, decode_step, reuse_interval,
+                                       selected, workspace, workspace_bytes, nt, st))
+            return s;
+    }
+    return decode_attn_impl(q, q_dtype, kv, seqs, heads, selected, token_budget, softmax_scale, out, stats,
+                            workspace, workspace_bytes, false, nt, st);
+}
+
+}  // extern "C"
+
+namespace lsa {
+namespace {
+
+lsa_status select_impl(const void *q, int32_t q_dtype, const lsa_kv *kv, const void *stats, const lsa_seqs *seqs,
+                       const lsa_heads *heads, int32_t token_budget, int32_t decode_step, int32_t reuse_interval,
+                       int32_t *selected, void *workspace, size_t workspace_bytes, const NewToken &nt,
+                       hipStream_t stream, bool check_only) {
     if (lsa_status s = check_kv(kv)) return s;
     if (lsa_status s = check_seqs(seqs)) return s;
     if (lsa_status s = check_heads(heads, kv, true)) return s;
@@ -446,6 +551,7 @@ lsa_status lsa_select_pages(const void *q, int32_t q_dtype, const lsa_kv *kv, co
     if (seqs->max_pages > topk_max_pages())
         return fail(LSA_ERR_UNSUPPORTED, "max_pages %d: page selection handles at most %d pages per sequence",
                     seqs->max_pages, topk_max_pages());
+    if (check_only) return ok();
     if (decode_step % reuse_interval != 0) return ok();     // reuse the previous selection
     const int n_ret = count_kind(heads, kv->num_kv_heads, LSA_RETRIEVAL_HEAD);
     if (n_ret == 0 || seqs->batch == 0) return ok();
@@ -456,6 +562,8 @@ lsa_status lsa_select_pages(const void *q, int32_t q_dtype, const lsa_kv *kv, co
     sa.stats = stats;
     sa.k = kv->k;
     sa.k_sz = kv->k_sz;
+    sa.k_new = nt.k;
+    sa.k_new_sz = nt.k_sz;
     sa.page_table = seqs->page_table;
     sa.seq_lens = seqs->seq_lens;
     sa.counters = static_cast<int32_t *>(workspace);
@@ -482,7 +590,7 @@ lsa_status lsa_select_pages(const void *q, int32_t q_dtype, const lsa_kv *kv, co
             ? score_pages_per_block(kv->kv_dtype, kv->head_dim, kv->page_size, kv->logical_page, sa.fused_pt, true)
             : score_loop_pages_per_block(seqs->batch, sa.n_ret, seqs->max_pages, kv->page_size, kv->logical_page);
     sa.blocks_per_head = (seqs->max_pages + sa.pages_per_block - 1) / sa.pages_per_block;
-    if (lsa_status s = from_hip(launch_score(sa, (hipStream_t)stream), "select_pages score launch")) return s;
+    if (lsa_status s = from_hip(launch_score(sa, stream), "select_pages score launch")) return s;
     if (sa.fused_pt > 0) return ok();              // the score kernel's last workgroups have selected
 
     TopkArgs ta{};
@@ -496,48 +604,13 @@ lsa_status lsa_select_pages(const void *q, int32_t q_dtype, const lsa_kv *kv, co
     ta.k = token_budget / kv->page_size;
     ta.n_ret = sa.n_ret;
     std::memcpy(ta.ret_heads, sa.ret_heads, sizeof(ta.ret_heads));
-    return from_hip(launch_topk(ta, (hipStream_t)stream), "select_pages top-K launch");
+    return from_hip(launch_topk(ta, stream), "select_pages top-K launch");
 }
-
-lsa_status lsa_decode_workspace(const lsa_kv *kv, const lsa_seqs *seqs, const lsa_heads *heads,
-                                int32_t token_budget, size_t *bytes) {
-    if (lsa_status s = check_kv(kv)) return s;
-    if (lsa_status s = check_seqs(seqs)) return s;
-    if (lsa_status s = check_heads(heads, kv, true)) return s;
-    if (!bytes) return fail(LSA_ERR_INVALID_ARG, "bytes is NULL");
-    if (token_budget < kv->page_size || token_budget % kv->page_size != 0)
-        return fail(LSA_ERR_INVALID_ARG, "token_budget %d is not a positive multiple of page_size %d", token_budget,
-                    kv->page_size);
-    const DecodeGeom g = decode_geometry(kv, heads, token_budget);
-    *bytes = decode_counter_bytes(seqs->batch, kv->num_kv_heads) +
-             align_up((size_t)seqs->batch * kv->num_kv_heads * g.chunks_max * g.rec_floats * sizeof(float));
-    return ok();
-}
-
-lsa_status lsa_sparse_decode_attn(const void *q, int32_t q_dtype, const lsa_kv *kv, const lsa_seqs *seqs,
-                                  const lsa_heads *heads, const int32_t *selected, int32_t token_budget,
-                                  float softmax_scale, void *out, void *stats, void *workspace,
-                                  size_t workspace_bytes, void *stream) {
-    return decode_attn_impl(q, q_dtype, kv, seqs, heads, selected, token_budget, softmax_scale, out, stats,
-                            workspace, workspace_bytes, false, (hipStream_t)stream);
-}
-
-lsa_status lsa_sparse_decode_attn_noalloc(const void *q, int32_t q_dtype, const lsa_kv *kv, const lsa_seqs *seqs,
-                                          const lsa_heads *heads, const int32_t *selected, int32_t token_budget,
-                                          float softmax_scale, void *out, void *stats, void *stream) {
-    return decode_attn_impl(q, q_dtype, kv, seqs, heads, selected, token_budget, softmax_scale, out, stats,
-                            nullptr, 0, true, (hipStream_t)stream);
-}
-
-}  // extern "C"
-
-namespace lsa {
-namespace {
 
 lsa_status decode_attn_impl(const void *q, int32_t q_dtype, const lsa_kv *kv, const lsa_seqs *seqs,
                             const lsa_heads *heads, const int32_t *selected, int32_t token_budget,
                             float softmax_scale, void *out, void *stats, void *workspace, size_t workspace_bytes,
-                            bool use_static, hipStream_t stream) {
+                            bool use_static, const NewToken &nt, hipStream_t stream, bool check_only) {
     if (lsa_status s = check_kv(kv)) return s;
     if (lsa_status s = check_seqs(seqs)) return s;
     if (lsa_status s = check_heads(heads, kv, true)) return s;
@@ -565,6 +638,7 @@ lsa_status decode_attn_impl(const void *q, int32_t q_dtype, const lsa_kv *kv, co
     if (g.chunks_max > kMaxDecodeChunks)
         return fail(LSA_ERR_UNSUPPORTED, "token budget / Lambda window spans %d split-KV chunks (limit %d)",
                     g.chunks_max, kMaxDecodeChunks);
+    if (check_only) return ok();
     if (seqs->batch == 0) return ok();
     if (use_static)                       // every argument is valid: now touch the device
         if (lsa_status s = static_scratch(&workspace)) return s;
@@ -582,6 +656,10 @@ lsa_status decode_attn_impl(const void *q, int32_t q_dtype, const lsa_kv *kv, co
     a.part = reinterpret_cast<float *>(static_cast<char *>(workspace) +
                                        decode_counter_bytes(seqs->batch, kv->num_kv_heads));
     a.stats = stats;
+    a.k_new = nt.k;
+    a.v_new = nt.v;
+    a.k_new_sz = nt.k_sz;
+    a.v_new_sz = nt.v_sz;
     a.logical_page = kv->logical_page;
     a.batch = seqs->batch;
     a.max_pages = seqs->max_pages;

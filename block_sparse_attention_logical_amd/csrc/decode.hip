@@ -55,6 +55,7 @@ typedef float floatx4 __attribute__((ext_vector_type(4)));
 
 struct WorkItem {
     int b, kv, chunk, t, L;
+    int t_pool;          // the last token read from memory: t, or t - 1 when this launch appends t
     bool streaming;
 };
 
@@ -126,16 +127,17 @@ __device__ __forceinline__ void wg_pages(const DecodeArgs &a, const WorkItem &w,
     if (lane < CP) { list[2 + lane] = page; list[2 + CP + lane] = pool; }
 }
 
+// Is token p attended and read from memory (p <= t_pool)?
 __device__ __forceinline__ bool token_visible(const DecodeArgs &a, const WorkItem &w, int p) {
     // bitwise, not short-circuit: no branch inside the block compute
-    return (p <= w.t) & (!w.streaming | (p < a.sink) | ((w.t - p) < a.local));
+    return (p <= w.t_pool) & (!w.streaming | (p < a.sink) | ((w.t - p) < a.local));
 }
 
-// Does the run of n tokens starting at tok0 hold any attended token?
+// Does the run of n tokens starting at tok0 hold any attended token read from memory?
 __device__ __forceinline__ bool block_needed(const DecodeArgs &a, const WorkItem &w, int tok0, int n) {
-    if (tok0 > w.t) return false;
+    if (tok0 > w.t_pool) return false;
     if (!w.streaming) return true;
-    const int p_last = min(tok0 + n - 1, w.t);
+    const int p_last = min(tok0 + n - 1, w.t_pool);
     return tok0 < a.sink || (w.t - p_last) < a.local;
 }
 
@@ -189,6 +191,76 @@ __device__ __forceinline__ void refresh_current_stats(const DecodeArgs &a, const
     }
 }
 
+// The value itself, hidden from the optimiser: the query's channels are
+// converted to fp32 once for the int4 query sum before the key loop and again
+// for the appended token's logit after it; without this the first conversions
+// would be kept live across the whole loop to serve the second.
+__device__ __forceinline__ uint4 opaque(uint4 v) {
+    asm volatile("" : "+v"(v.x), "+v"(v.y), "+v"(v.z), "+v"(v.w));
+    return v;
+}
+
+// Fused append: write token t (its K / V rows staged in LDS) into its page
+// and, for retrieval heads, fold it into the statistics of its logical page
+// (a logical page the token opens starts from it; otherwise min / max take it
+// in, exactly).  Lanes own channels; an int4 value byte also holds the
+// neighbouring token's code, which is kept.
+template <int KVT, int D, int NP, int PPW>
+__device__ __forceinline__ void append_write(const DecodeArgs &a, const WorkItem &w, int j_new, const size_t (&hp)[PPW],
+                                             const int (&pg)[PPW], const void *kpool, const void *vpool,
+                                             const uint16_t *kszp, const uint16_t *vszp, uint32_t ksz_n,
+                                             uint32_t vsz_n, const uint8_t *row8, int lane) {
+    (void)pg;
+    constexpr int BS = block_shift(NP);
+    constexpr int ROW = KVT == LSA_INT4 ? D / 2 : 2 * D;     // bytes of the staged K row (then the V row)
+    size_t hpn = 0;                                          // hp[j_new], without a dynamic register index
+#pragma unroll
+    for (int j = 0; j < PPW; ++j) hpn = j == j_new ? hp[j] : hpn;
+    const size_t base = hpn * NP * D;
+    const int slot = w.t % NP, NL = a.logical_page, g = NP / NL, jl = slot / NL;
+    const bool opens = slot % NL == 0;
+    const bool upd = a.stats != nullptr && !w.streaming;
+    if constexpr (KVT == LSA_INT4) {
+        uint8_t *k8 = const_cast<uint8_t *>(static_cast<const uint8_t *>(kpool));
+        uint8_t *v8 = const_cast<uint8_t *>(static_cast<const uint8_t *>(vpool));
+        for (int i = lane; i < D / 2; i += kWave)             // key byte i: channels 2i, 2i + 1
+            k8[(base + key_offset(slot, 2 * i, D, BS)) / 2] = row8[i];
+        for (int c = lane; c < D; c += kWave) {
+            const uint32_t code = (row8[ROW + c / 2] >> (4 * (c & 1))) & 15u;
+            uint8_t *vb = v8 + (base + value_offset(slot, c, D, BS)) / 2;
+            const uint32_t old = *vb;
+            *vb = (uint8_t)((slot & 1) ? ((old & 0x0Fu) | (code << 4)) : ((old & 0xF0u) | code));
+            if (upd) {
+                const uint32_t kc = (row8[c / 2] >> (4 * (c & 1))) & 15u;
+                uint8_t *st = static_cast<uint8_t *>(a.stats) + (hpn * g + jl) * D + c;
+                const uint32_t ob = opens ? 0u : *st;
+                *st = (uint8_t)(opens ? (kc | (kc << 4)) : (min(ob & 15u, kc) | (max(ob >> 4, kc) << 4)));
+            }
+        }
+        if (lane == 0) {
+            *reinterpret_cast<uint32_t *>(const_cast<uint16_t *>(kszp) + hpn * 2) = ksz_n;
+            *reinterpret_cast<uint32_t *>(const_cast<uint16_t *>(vszp) + hpn * 2) = vsz_n;
+        }
+    } else {
+        uint16_t *kd = const_cast<uint16_t *>(static_cast<const uint16_t *>(kpool)) + base;
+        uint16_t *vd = const_cast<uint16_t *>(static_cast<const uint16_t *>(vpool)) + base;
+        const uint16_t *kr = reinterpret_cast<const uint16_t *>(row8);
+        const uint16_t *vr = reinterpret_cast<const uint16_t *>(row8 + ROW);
+        uint16_t *st = static_cast<uint16_t *>(a.stats) + ((hpn * g + jl) * 2) * D;
+        for (int c = lane; c < D; c += kWave) {
+            kd[key_offset(slot, c, D, BS)] = kr[c];
+            vd[value_offset(slot, c, D, BS)] = vr[c];
+            if (upd) {
+                const float x = bf16_to_f32(kr[c]);
+                const float mn = opens ? x : fminf(bf16_to_f32(st[c]), x);
+                const float mx = opens ? x : fmaxf(bf16_to_f32(st[D + c]), x);
+                st[c] = uint16_t(__float_as_uint(mn) >> 16);          // exact: bf16 values
+                st[D + c] = uint16_t(__float_as_uint(mx) >> 16);
+            }
+        }
+    }
+}
+
 __device__ __forceinline__ void store_agent(float *p, float v) {
     __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
@@ -208,18 +280,24 @@ __device__ __forceinline__ float2 load_agent2(const float *p) {
 // Merge the softmax states of the NW wavefronts held in LDS and write this
 // chunk's record (m[16], l[16], o[G][D]) with agent-scope stores.  LDS layout
 // per wave: m[16], l[16], o[16][D].
+// With `extra`, a one-token state follows the NW wavefront states: a logit
+// per head (16 floats) and the token's value row (D floats), weight 1; its
+// logit is -inf in workgroups that do not hold the token.
 template <int NW>
 __device__ __forceinline__ void merge_waves_and_store(const DecodeArgs &a, const WorkItem &w,
-                                                      const float *lds, int D) {
+                                                      const float *lds, int D, bool extra) {
     const int G = a.group;
     const int wave_stride = 32 + 16 * D;
     const size_t rec_size = 32 + (size_t)G * D;
+    const float *nt = lds + NW * wave_stride;
     float *rec = a.part + (((size_t)w.b * a.num_kv_heads + w.kv) * a.chunks_max + w.chunk) * rec_size;
     for (int pi = threadIdx.x; pi < G * D / 2; pi += blockDim.x) {
         const int h = (2 * pi) / D, d = 2 * pi - h * D;
         float M = -__builtin_inff();
 #pragma unroll
         for (int wv = 0; wv < NW; ++wv) M = fmaxf(M, lds[wv * wave_stride + h]);
+        const float mt = extra ? nt[h] : -__builtin_inff();
+        M = fmaxf(M, mt);
         float acc0 = 0.f, acc1 = 0.f, lsum = 0.f;
         if (M != -__builtin_inff()) {
 #pragma unroll
@@ -229,6 +307,12 @@ __device__ __forceinline__ void merge_waves_and_store(const DecodeArgs &a, const
                 acc0 += wt * lds[wv * wave_stride + 32 + h * D + d];
                 acc1 += wt * lds[wv * wave_stride + 32 + h * D + d + 1];
                 lsum += wt * lds[wv * wave_stride + 16 + h];
+            }
+            if (mt != -__builtin_inff()) {
+                const float wt = exp2_fast(mt - M);
+                acc0 += wt * nt[16 + d];
+                acc1 += wt * nt[16 + d + 1];
+                lsum += wt;
             }
         }
         store_agent2(rec + 32 + 2 * pi, acc0, acc1);
@@ -325,6 +409,12 @@ __device__ __forceinline__ uint4 nibbles_bf16x8(uint32_t w) {
                       __builtin_amdgcn_perm(hi, lo, 0x0C070C03u) | 0x43004300u);
 }
 
+// a where the mask bits are 0, b where they are 1
+__device__ __forceinline__ uint4 blend(uint4 a, uint4 b, uint32_t m) {
+    return make_uint4(a.x ^ ((a.x ^ b.x) & m), a.y ^ ((a.y ^ b.y) & m), a.z ^ ((a.z ^ b.z) & m),
+                      a.w ^ ((a.w ^ b.w) & m));
+}
+
 __device__ __forceinline__ uint32_t pick(const uint4 &u, int i) {
     return i == 0 ? u.x : i == 1 ? u.y : i == 2 ? u.z : u.w;
 }
@@ -375,10 +465,28 @@ __global__ __launch_bounds__(kDecodeWaves * kWave, 2) void decode_mfma_kernel(De
         }
     }
     __shared__ int s_list[kListSlots];
+    // fused append: the token's K row, V row and (int4) its (s, z) pairs
+    constexpr int kNewRow = I4 ? D / 2 : 2 * D;       // bytes of one row
+    __shared__ uint4 s_new[2 * kNewRow / 16 + 1];
     if (wave == 0) wg_pages<CP>(a, w, s_list);
+    if (wave == 2 && a.k_new && lane < 16) lds[kDecodeWaves * (32 + 16 * D) + lane] = -__builtin_inff();
+    if (wave == 1 && a.k_new) {
+        const size_t row = ((size_t)w.b * a.num_kv_heads + w.kv) * kNewRow;
+        if (lane < kNewRow / 16) {
+            s_new[lane] = *reinterpret_cast<const uint4 *>(static_cast<const uint8_t *>(a.k_new) + row + 16 * lane);
+            s_new[kNewRow / 16 + lane] =
+                *reinterpret_cast<const uint4 *>(static_cast<const uint8_t *>(a.v_new) + row + 16 * lane);
+        }
+        if (I4 && lane == 0) {
+            const size_t i2 = ((size_t)w.b * a.num_kv_heads + w.kv) * 2;
+            s_new[2 * kNewRow / 16] = make_uint4(*reinterpret_cast<const uint32_t *>(a.k_new_sz + i2),
+                                                 *reinterpret_cast<const uint32_t *>(a.v_new_sz + i2), 0u, 0u);
+        }
+    }
     __syncthreads();
     w.t = __builtin_amdgcn_readfirstlane(s_list[0]);
     w.L = __builtin_amdgcn_readfirstlane(s_list[1]);
+    w.t_pool = a.k_new ? w.t - 1 : w.t;
 
     // this wavefront's pages: chunk slots PPW*wave .. PPW*wave + PPW - 1, as
     // (page, head) units of the pool, or pages of the stream cache
@@ -430,6 +538,23 @@ __global__ __launch_bounds__(kDecodeWaves * kWave, 2) void decode_mfma_kernel(De
     float m_run = -__builtin_inff(), l_run = 0.f;
     float corr = 0.f;                      // int4: (128 + z_v) * sum of fed weights (per lane)
 
+    // fused append: the page slot of token t in this wavefront (-1: none;
+    // wavefront-uniform).  The ring reads tokens up to t - 1; this wavefront
+    // adds token t from the staged rows after the ring and writes it out.
+    int j_new = -1;
+    if (a.k_new) {
+#pragma unroll
+        for (int j = 0; j < PPW; ++j) j_new = pg[j] == w.t / NP ? j : j_new;
+    }
+    // the token's K and V rows and (int4) its page's scale and zero point,
+    // staged in LDS by wavefront 1 while wavefront 0 resolved the page list
+    const uint8_t *s_new8 = reinterpret_cast<const uint8_t *>(s_new);
+    uint32_t ksz_n = 0, vsz_n = 0;
+    if (I4 && j_new >= 0) {
+        ksz_n = s_new[2 * kNewRow / 16].x;
+        vsz_n = s_new[2 * kNewRow / 16].y;
+    }
+
     // QK^T tile T of a 32-token block holds tokens 16T .. 16T + 15 on MFMA
     // rows (row rho = token 16T + rho, one contiguous 1 KiB key-tile read per
     // channel step); a lane's result registers hold tokens 16T + 4*g4 + r.
@@ -442,8 +567,9 @@ __global__ __launch_bounds__(kDecodeWaves * kWave, 2) void decode_mfma_kernel(De
             sk[j] = 1.f; zk[j] = 0.f; sv[j] = 1.f; zv[j] = 0.f;
             if constexpr (I4) {
                 if (pg[j] >= 0) {
-                    const uint32_t ksz = *reinterpret_cast<const uint32_t *>(kszp + hp[j] * 2);
-                    const uint32_t vsz = *reinterpret_cast<const uint32_t *>(vszp + hp[j] * 2);
+                    // (the page of a token being appended may not have its pair in memory yet)
+                    const uint32_t ksz = j == j_new ? ksz_n : *reinterpret_cast<const uint32_t *>(kszp + hp[j] * 2);
+                    const uint32_t vsz = j == j_new ? vsz_n : *reinterpret_cast<const uint32_t *>(vszp + hp[j] * 2);
                     sk[j] = fp16_bits_to_f32(uint16_t(ksz)); zk[j] = fp16_bits_to_f32(uint16_t(ksz >> 16));
                     sv[j] = fp16_bits_to_f32(uint16_t(vsz)); zv[j] = fp16_bits_to_f32(uint16_t(vsz >> 16));
                 }
@@ -477,7 +603,7 @@ __global__ __launch_bounds__(kDecodeWaves * kWave, 2) void decode_mfma_kernel(De
         uint4 vr[BIF][I4 ? 1 : NDT];
         uint32_t vr4[BIF][I4 ? NDT : 1];
         // ---- issue every K and V load of block i into ring slot e
-        auto issue = [&](int e, int i) {
+        auto issue = [&](int e, int i) __attribute__((always_inline)) {
             const int kb = src_kb[i];
             // key rows of tile T; the value rows this lane reads (tokens 8*g4 ..
             // 8*g4 + 7 of the block: page 2i + g4/2, tokens 8*(g4%2).. with 16-token pages)
@@ -522,7 +648,7 @@ __global__ __launch_bounds__(kDecodeWaves * kWave, 2) void decode_mfma_kernel(De
         // needs no keys is computed fully masked with its values zeroed (its slot
         // holds another block's data); there is no branch around it, so the
         // compiler keeps every ring load where it is issued.
-        auto consume = [&](int e, int i) {
+        auto consume = [&](int e, int i) __attribute__((always_inline)) {
             // the page slot of each tile (for the int4 scale and zero point)
             const int jt[2] = {HALF ? 2 * i : i / NB, HALF ? 2 * i + 1 : i / NB};
             // scores of the 32 keys (two 16-row tiles)
@@ -604,9 +730,9 @@ __global__ __launch_bounds__(kDecodeWaves * kWave, 2) void decode_mfma_kernel(De
             const bf16x8 pbv = __builtin_bit_cast(bf16x8, make_uint4(pv[0], pv[1], pv[2], pv[3]));
             // slots after the current token may hold any bits: zero their values so a
             // zero probability never meets a NaN in the PV product
-            const bool tail = !(need_t[i][0] & need_t[i][1]) || max(tok_t[i][0], tok_t[i][1]) + 15 > w.t;
+            const bool tail = !(need_t[i][0] & need_t[i][1]) || max(tok_t[i][0], tok_t[i][1]) + 15 > w.t_pool;
             const int vt = HALF ? g4 >> 1 : 0;       // the tile whose tokens this lane's value rows hold
-            const int nvalid = need_t[i][vt] ? w.t - (tok_t[i][vt] + (HALF ? 8 * (g4 & 1) : 8 * g4)) + 1 : 0;
+            const int nvalid = need_t[i][vt] ? w.t_pool - (tok_t[i][vt] + (HALF ? 8 * (g4 & 1) : 8 * g4)) + 1 : 0;
             uint32_t keep[4] = {~0u, ~0u, ~0u, ~0u};
             if (tail) {
 #pragma unroll
@@ -651,9 +777,57 @@ __global__ __launch_bounds__(kDecodeWaves * kWave, 2) void decode_mfma_kernel(De
     for (int dt = 0; dt < NDT; ++dt)
 #pragma unroll
         for (int r = 0; r < 4; ++r) my[32 + h * D + 16 * dt + 4 * g4 + r] = o[dt][r] - corr;
-    if (a.stats && !w.streaming && w.chunk == 0 && wave == 0) refresh_current_stats(a, w, KVT);
+    if (a.stats && !a.k_new && !w.streaming && w.chunk == 0 && wave == 0) refresh_current_stats(a, w, KVT);
+    if (j_new >= 0) {
+        // token t as a one-token partial state (log2-domain logit per head, its
+        // value row) next to the wavefronts' states, then written to its page
+        float sk_n = 1.f, zk_n = 0.f, sv_n = 1.f, zv_n = 0.f;
+        if constexpr (I4) {
+            sk_n = fp16_bits_to_f32(uint16_t(ksz_n)); zk_n = fp16_bits_to_f32(uint16_t(ksz_n >> 16));
+            sv_n = fp16_bits_to_f32(uint16_t(vsz_n)); zv_n = fp16_bits_to_f32(uint16_t(vsz_n >> 16));
+        }
+        float dot = 0.f;
+        if constexpr (I4) {
+            // this lane's codes: channels (D/4)*g4 .. + D/4 - 1, the order of qb
+            const uint4 kc = D == 128 ? s_new[g4]
+                                      : make_uint4(reinterpret_cast<const uint2 *>(s_new)[g4].x,
+                                                   reinterpret_cast<const uint2 *>(s_new)[g4].y, 0u, 0u);
+            const uint32_t kw[4] = {kc.x, kc.y, kc.z, kc.w};
+#pragma unroll
+            for (int s = 0; s < NS; ++s) {
+                const uint4 qraw = opaque(__builtin_bit_cast(uint4, qb[s]));
+                const uint32_t qw[4] = {qraw.x, qraw.y, qraw.z, qraw.w};
+#pragma unroll
+                for (int j = 0; j < 8; ++j) {
+                    const int c = 8 * s + j;                       // code c of the lane's run
+                    const float kj = (float)((kw[c / 8] >> (4 * (c % 8))) & 15u) - zk_n;
+                    dot = fmaf((j & 1) ? bf16_hi(qw[j / 2]) : bf16_lo(qw[j / 2]), kj, dot);
+                }
+            }
+        } else {
+#pragma unroll
+            for (int s = 0; s < NS; ++s) {
+                const uint4 qraw = opaque(__builtin_bit_cast(uint4, qb[s])), kraw = s_new[4 * s + g4];   // channels 32s + 8*g4 ..
+                const uint32_t qw[4] = {qraw.x, qraw.y, qraw.z, qraw.w}, kw[4] = {kraw.x, kraw.y, kraw.z, kraw.w};
+#pragma unroll
+                for (int j = 0; j < 8; ++j)
+                    dot = fmaf((j & 1) ? bf16_hi(qw[j / 2]) : bf16_lo(qw[j / 2]),
+                               (j & 1) ? bf16_hi(kw[j / 2]) : bf16_lo(kw[j / 2]), dot);
+            }
+        }
+        dot = sum_xor32(sum_xor16(dot));
+        float *nt = lds + kDecodeWaves * (32 + 16 * D);
+        if (g4 == 0) nt[h] = dot * sk_n * a.scale_log2;
+        for (int c = lane; c < D; c += kWave) {
+            float vc;
+            if constexpr (I4) vc = ((float)((s_new8[kNewRow + c / 2] >> (4 * (c & 1))) & 15u) - zv_n) * sv_n;
+            else vc = bf16_to_f32(*reinterpret_cast<const uint16_t *>(s_new8 + kNewRow + 2 * c));
+            nt[16 + c] = vc;
+        }
+        append_write<KVT, D, NP, PPW>(a, w, j_new, hp, pg, kpool, vpool, kszp, vszp, ksz_n, vsz_n, s_new8, lane);
+    }
     __syncthreads();
-    merge_waves_and_store<kDecodeWaves>(a, w, lds, D);
+    merge_waves_and_store<kDecodeWaves>(a, w, lds, D, a.k_new != nullptr);
     // one batch of records covers a 4096-token budget (its pages plus the current one)
     constexpr int CB = (4096 / NP + CP) / CP < 17 ? (4096 / NP + CP) / CP : 17;
     finish_head<uint16_t, CB>(a, w, D);
@@ -679,6 +853,7 @@ __global__ __launch_bounds__(256) void decode_f32_kernel(DecodeArgs a) {
     __syncthreads();
     w.t = s_list[0];
     w.L = s_list[1];
+    w.t_pool = w.t;                                // (the f32 path substitutes the new token itself)
     const int my_page = s_list[2 + wave], my_pool = s_list[6 + wave];
 
     float o[16][CPL];
@@ -696,6 +871,13 @@ __global__ __launch_bounds__(256) void decode_f32_kernel(DecodeArgs a) {
     const float *vpool = static_cast<const float *>(in_cache ? a.sc_v : a.v);
     const int bs = block_shift(NP);
 
+    // fused append: this wavefront reads the page of token t and takes the
+    // token from the new rows (its page does not hold it yet), then writes it
+    const bool put_new = a.k_new != nullptr && my_page >= 0 && my_page == w.t / NP;
+    const size_t new_row = ((size_t)w.b * a.num_kv_heads + w.kv) * D;
+    const float *k_new = static_cast<const float *>(a.k_new) + new_row;
+    const float *v_new = static_cast<const float *>(a.v_new) + new_row;
+
     if (my_page >= 0) {
         const int page = my_page;
         const size_t head_page = in_cache ? (size_t)my_pool : (size_t)my_pool * a.ph.pool_heads + a.ph.pool_slot[w.kv];
@@ -709,8 +891,10 @@ __global__ __launch_bounds__(256) void decode_f32_kernel(DecodeArgs a) {
 #pragma unroll
             for (int hh = 0; hh < 16; ++hh) sc[hh] = 0.f;
             if (slot < NP) {
+                const bool mine = put_new && p == w.t;
                 for (int d = 0; d < D; d += 4) {
-                    const float4 kv4 = *reinterpret_cast<const float4 *>(kp + key_offset(slot, d, D, bs));
+                    const float4 kv4 = *reinterpret_cast<const float4 *>(mine ? k_new + d
+                                                                               : kp + key_offset(slot, d, D, bs));
 #pragma unroll
                     for (int hh = 0; hh < 16; ++hh) {
                         if (hh < G) {
@@ -748,7 +932,8 @@ __global__ __launch_bounds__(256) void decode_f32_kernel(DecodeArgs a) {
 #pragma unroll
                 for (int hh = 0; hh < 16; ++hh) acc[hh] = o[hh][c] * alpha[hh];
                 for (int sl = 0; sl < nslots; ++sl) {
-                    const float vv = vp[value_offset(s0 + sl, d, D, bs)];
+                    const float vv = put_new && page * NP + s0 + sl == w.t ? v_new[d]
+                                                                           : vp[value_offset(s0 + sl, d, D, bs)];
 #pragma unroll
                     for (int hh = 0; hh < 16; ++hh)
                         if (hh < G) acc[hh] = fmaf(ps[hh * 64 + sl], vv, acc[hh]);
@@ -760,6 +945,25 @@ __global__ __launch_bounds__(256) void decode_f32_kernel(DecodeArgs a) {
         }
     }
 
+    if (put_new) {
+        // the token into its page, and into its logical page's statistics
+        const size_t head_page = in_cache ? (size_t)my_pool : (size_t)my_pool * a.ph.pool_heads + a.ph.pool_slot[w.kv];
+        float *kp = const_cast<float *>(kpool) + head_page * NP * D;
+        float *vp = const_cast<float *>(vpool) + head_page * NP * D;
+        const int slot = w.t % NP, NL = a.logical_page, jl = slot / NL, g = NP / NL;
+        const bool opens = slot % NL == 0;
+        float *st = static_cast<float *>(a.stats) + ((head_page * g + jl) * 2) * D;
+        for (int c = lane; c < D; c += kWave) {
+            const float x = k_new[c];
+            kp[key_offset(slot, c, D, bs)] = x;
+            vp[value_offset(slot, c, D, bs)] = v_new[c];
+            if (a.stats && !w.streaming) {
+                st[c] = opens ? x : fminf(st[c], x);
+                st[D + c] = opens ? x : fmaxf(st[D + c], x);
+            }
+        }
+    }
+
     float *my = lds + wave * (32 + 16 * D);
 #pragma unroll
     for (int hh = 0; hh < 16; ++hh) {
@@ -767,9 +971,9 @@ __global__ __launch_bounds__(256) void decode_f32_kernel(DecodeArgs a) {
 #pragma unroll
         for (int c = 0; c < CPL; ++c) my[32 + hh * D + lane * CPL + c] = o[hh][c];
     }
-    if (a.stats && !w.streaming && w.chunk == 0 && wave == 0) refresh_current_stats(a, w, LSA_F32);
+    if (a.stats && !a.k_new && !w.streaming && w.chunk == 0 && wave == 0) refresh_current_stats(a, w, LSA_F32);
     __syncthreads();
-    merge_waves_and_store<4>(a, w, lds, D);
+    merge_waves_and_store<4>(a, w, lds, D, false);
     finish_head<float, 17>(a, w, D);
 }
 
@@ -779,7 +983,8 @@ namespace {
 
 template <int D, int KVT>
 hipError_t launch_mfma(const DecodeArgs &a, unsigned grid, hipStream_t s) {
-    const size_t lds = kDecodeWaves * (32 + 16 * (size_t)D) * sizeof(float);
+    // the wavefronts' states, then the appended token's one-token state
+    const size_t lds = (kDecodeWaves * (32 + 16 * (size_t)D) + 16 + D) * sizeof(float);
     const dim3 block(kDecodeWaves * kWave);
     switch (a.page_size) {
         case 16: hipLaunchKernelGGL((decode_mfma_kernel<D, KVT, 16>), dim3(grid), block, lds, s, a); break;

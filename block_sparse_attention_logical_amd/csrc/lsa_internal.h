@@ -269,6 +269,12 @@ struct ScoreArgs {
     int32_t k_pages;              // K
     int32_t fused_pt;
     PoolHeads ph;
+    // the newest token's key rows [B][H_kv][D] (int4: D/2 bytes), or null: the
+    // current logical page's last row (token t) is then read from the pool.
+    // int4: k_new_sz [B][H_kv][2] holds t's page (s, z), used in place of the
+    // pool's entry
+    const void *k_new;
+    const uint16_t *k_new_sz;
 };
 
 struct TopkArgs {
@@ -311,6 +317,15 @@ struct DecodeArgs {
     const uint16_t *sc_v_sz;
     int32_t sc_sink, sc_ring, n_str;
     uint8_t str_slot[kMaxKvHeads];
+    // fused append (k_new != null): the newest token's K / V rows [B][H_kv][D]
+    // (int4: [B][H_kv][D/2] codes and the page's (s, z) rows [B][H_kv][2]).  The
+    // wavefront that reads the page of token t takes the token from these rows
+    // and writes it to its page (pool or cache); for retrieval heads it also
+    // updates the statistics of t's logical page (stats)
+    const void *k_new;
+    const void *v_new;
+    const uint16_t *k_new_sz;
+    const uint16_t *v_new_sz;
 };
 
 // The cache page of sequence page m of (b, s) in a stream cache.

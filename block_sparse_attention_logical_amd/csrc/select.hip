@@ -110,7 +110,7 @@ __device__ __forceinline__ void load_q_pos_neg(const ScoreArgs &a, int b, int kv
 // channels for f32 / bf16 pools, 4-bit codes (as floats) for int4 pools.
 template <int KV_DT, int D, int C, int LPL, int LPP>
 __device__ __forceinline__ void current_page_minmax(const ScoreArgs &a, size_t page_base, int row0, int rows, int q,
-                                                    int ch0, float (&kmin)[C], float (&kmax)[C]) {
+                                                    int ch0, const void *knew_row, float (&kmin)[C], float (&kmax)[C]) {
 #pragma unroll
     for (int c = 0; c < C; ++c) { kmin[c] = __builtin_inff(); kmax[c] = -__builtin_inff(); }
     const int bs = block_shift(a.page_size);
@@ -121,9 +121,10 @@ __device__ __forceinline__ void current_page_minmax(const ScoreArgs &a, size_t p
 #pragma unroll
             for (int i = 0; i < RB; ++i) {
                 const int rr = r0 + q + i * LPP;
-                u[i] = rr < rows ? *reinterpret_cast<const uint2 *>(static_cast<const uint8_t *>(a.k) +
-                                                                    (page_base + key_offset(row0 + rr, ch0, D, bs)) / 2)
-                                 : make_uint2(0xFFFFFFFFu, 0xFFFFFFFFu);
+                const uint8_t *src = knew_row && rr == rows - 1
+                                         ? static_cast<const uint8_t *>(knew_row) + ch0 / 2
+                                         : static_cast<const uint8_t *>(a.k) + (page_base + key_offset(row0 + rr, ch0, D, bs)) / 2;
+                u[i] = rr < rows ? *reinterpret_cast<const uint2 *>(src) : make_uint2(0xFFFFFFFFu, 0xFFFFFFFFu);
             }
 #pragma unroll
             for (int i = 0; i < RB; ++i) {
@@ -141,10 +142,11 @@ __device__ __forceinline__ void current_page_minmax(const ScoreArgs &a, size_t p
 #pragma unroll
             for (int i = 0; i < RB; ++i) {
                 const int rr = r0 + q + i * LPP;
-                u[i] = rr < rows ? *reinterpret_cast<const uint4 *>(static_cast<const char *>(a.k) +
-                                                                    (page_base + key_offset(row0 + rr, ch0, D, bs)) *
-                                                                        (KV_DT == LSA_F32 ? 4 : 2))
-                                 : make_uint4(0, 0, 0, 0);
+                constexpr int EBk = KV_DT == LSA_F32 ? 4 : 2;
+                const char *src = knew_row && rr == rows - 1
+                                      ? static_cast<const char *>(knew_row) + (size_t)ch0 * EBk
+                                      : static_cast<const char *>(a.k) + (page_base + key_offset(row0 + rr, ch0, D, bs)) * EBk;
+                u[i] = rr < rows ? *reinterpret_cast<const uint4 *>(src) : make_uint4(0, 0, 0, 0);
             }
 #pragma unroll
             for (int i = 0; i < RB; ++i) {
@@ -414,9 +416,14 @@ __global__ __launch_bounds__(kScoreThreads) void score_kernel(ScoreArgs a) {
     if (own_cur) {
         const int pool = a.page_table[(size_t)b * a.max_pages + j_cur / g];
         const size_t hp = (size_t)pool * a.ph.pool_heads + a.ph.pool_slot[kv];
-        if constexpr (KV_DT == LSA_INT4) sz_cur = *reinterpret_cast<const uint32_t *>(a.k_sz + hp * 2);
+        if constexpr (KV_DT == LSA_INT4)     // (t's page may not have its pair in memory yet)
+            sz_cur = *reinterpret_cast<const uint32_t *>(a.k_new ? a.k_new_sz + ((size_t)b * a.num_kv_heads + kv) * 2
+                                                                  : a.k_sz + hp * 2);
+        const void *knew_row = a.k_new ? static_cast<const char *>(a.k_new) +
+                                             ((size_t)b * a.num_kv_heads + kv) * D * EB / (KV_DT == LSA_INT4 ? 2 : 1)
+                                       : nullptr;
         current_page_minmax<KV_DT, D, C, LPL, LPP>(a, hp * a.page_size * D, (j_cur % g) * a.logical_page,
-                                                   L - j_cur * a.logical_page, lane / LPL, ch0, cmin, cmax);
+                                                   L - j_cur * a.logical_page, lane / LPL, ch0, knew_row, cmin, cmax);
     }
 
     // int4: S = s * (sum_i Qp c_max + Qn c_min - z * sum_i (Qp + Qn))
@@ -616,9 +623,14 @@ __global__ __launch_bounds__(kScoreThreads) void score_loop_kernel(ScoreArgs a) 
         float cmin[C], cmax[C];
         const size_t hp = s_hp[(j_cur >> gs) - m0];
         uint32_t sz_cur = 0;
-        if constexpr (KV_DT == LSA_INT4) sz_cur = *reinterpret_cast<const uint32_t *>(a.k_sz + hp * 2);
+        if constexpr (KV_DT == LSA_INT4)     // (t's page may not have its pair in memory yet)
+            sz_cur = *reinterpret_cast<const uint32_t *>(a.k_new ? a.k_new_sz + ((size_t)b * a.num_kv_heads + kv) * 2
+                                                                  : a.k_sz + hp * 2);
+        const void *knew_row = a.k_new ? static_cast<const char *>(a.k_new) +
+                                             ((size_t)b * a.num_kv_heads + kv) * D * EB / (KV_DT == LSA_INT4 ? 2 : 1)
+                                       : nullptr;
         current_page_minmax<KV_DT, D, C, LPL, LPP>(a, hp * a.page_size * D, (j_cur % g) * a.logical_page,
-                                                   L - j_cur * a.logical_page, lane / LPL, ch0, cmin, cmax);
+                                                   L - j_cur * a.logical_page, lane / LPL, ch0, knew_row, cmin, cmax);
         double c0 = 0.0, c1 = 0.0;
 #pragma unroll
         for (int c = 0; c < C; ++c) {

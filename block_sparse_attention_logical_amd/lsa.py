@@ -38,6 +38,8 @@ EXPORTED = (
     "lsa_decode_workspace",
     "lsa_sparse_decode_attn",
     "lsa_sparse_decode_attn_noalloc",
+    "lsa_decode_step_workspace",
+    "lsa_decode_step",
     "lsa_sparse_prefill_attn",
     "lsa_sparse_prefill_attn_csr",
     "lsa_block_mask_schedule",
@@ -131,6 +133,10 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
                                            ctypes.c_int32, ctypes.c_float, vp, vp, vp, ctypes.c_size_t, vp]
     lib.lsa_sparse_decode_attn_noalloc.argtypes = [vp, ctypes.c_int32, P(LsaKV), P(LsaSeqs), P(LsaHeads), vp,
                                                    ctypes.c_int32, ctypes.c_float, vp, vp, vp]
+    lib.lsa_decode_step_workspace.argtypes = [P(LsaKV), P(LsaSeqs), P(LsaHeads), ctypes.c_int32, sz]
+    lib.lsa_decode_step.argtypes = [vp, ctypes.c_int32, P(LsaKV), P(LsaSeqs), P(LsaHeads), vp, vp, vp, vp, vp,
+                                    ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, vp, ctypes.c_float, vp, vp,
+                                    ctypes.c_size_t, vp]
     lib.lsa_sparse_prefill_attn.argtypes = [vp, ctypes.c_int32, P(LsaKV), vp, ctypes.c_int32, P(LsaHeads),
                                             ctypes.c_int32, ctypes.c_float, vp, vp, vp]
     lib.lsa_sparse_prefill_attn_csr.argtypes = [vp, ctypes.c_int32, P(LsaKV), vp, ctypes.c_int32, ctypes.c_int32,
@@ -352,6 +358,32 @@ def sparse_decode_attn_noalloc(q: torch.Tensor, kv: KVPool, page_table: torch.Te
                                                  ctypes.byref(seqs_desc(page_table, seq_lens)),
                                                  ctypes.byref(heads.desc()), _ptr(selected), token_budget,
                                                  softmax_scale, _ptr(out), _ptr(stats), _stream(stream)))
+
+
+def decode_step_workspace(kv: KVPool, page_table: torch.Tensor, seq_lens: torch.Tensor, heads: Heads,
+                          token_budget: int) -> int:
+    """Bytes of the decode_step workspace (lsa_decode_step_workspace)."""
+    out = ctypes.c_size_t(0)
+    _check(load().lsa_decode_step_workspace(ctypes.byref(kv.desc()), ctypes.byref(seqs_desc(page_table, seq_lens)),
+                                            ctypes.byref(heads.desc()), token_budget, ctypes.byref(out)))
+    return out.value
+
+
+def decode_step(q: torch.Tensor, kv: KVPool, page_table: torch.Tensor, seq_lens: torch.Tensor, heads: Heads,
+                k_new: torch.Tensor, v_new: torch.Tensor, stats: Optional[torch.Tensor], token_budget: int,
+                decode_step: int, reuse_interval: int, selected: Optional[torch.Tensor], out: torch.Tensor,
+                workspace: torch.Tensor, k_new_sz: Optional[torch.Tensor] = None,
+                v_new_sz: Optional[torch.Tensor] = None, softmax_scale: float = 0.0, stream=None) -> None:
+    """lsa_decode_step: append token seq_lens[b] - 1 (k_new, v_new as in append_kv), select pages
+    (every reuse_interval steps) and attend, in two launches.  The workspace (uint8,
+    decode_step_workspace bytes) must be zero-filled before its first use; calls that share it
+    must not overlap."""
+    _check(load().lsa_decode_step(_ptr(q), dtype_code(q), ctypes.byref(kv.desc()),
+                                  ctypes.byref(seqs_desc(page_table, seq_lens)), ctypes.byref(heads.desc()),
+                                  _ptr(k_new), _ptr(v_new), _ptr(k_new_sz), _ptr(v_new_sz), _ptr(stats),
+                                  token_budget, decode_step, reuse_interval, _ptr(selected), softmax_scale,
+                                  _ptr(out), _ptr(workspace), workspace.numel() * workspace.element_size(),
+                                  _stream(stream)))
 
 
 def sparse_prefill_attn(q: torch.Tensor, kv: KVPool, page_table: torch.Tensor, seq_len: int, heads: Heads,

@@ -332,6 +332,43 @@ lsa_status lsa_sparse_decode_attn_noalloc(const void *q, int32_t q_dtype, const 
                                           const int32_t *selected, int32_t token_budget,
                                           float softmax_scale, void *out, void *stats, void *stream);
 
+/* Workspace of lsa_decode_step, in bytes: the larger of
+ * lsa_select_pages_workspace and lsa_decode_workspace. */
+lsa_status lsa_decode_step_workspace(const lsa_kv *kv, const lsa_seqs *seqs, const lsa_heads *heads,
+                                     int32_t token_budget, size_t *bytes /* [host] out */);
+
+/* One whole decode step of every sequence b, t = seq_lens[b] - 1 being the
+ * newest token ([LS-X] Reusable Page Selection: a step appends the token's
+ * K/V, selects pages (every reuse_interval steps) and attends; 動的スパーシティ
+ * and 階層的ページング for the selection; 統一ブロックスパースアテンション for the
+ * attention).  Its results are those of
+ *   lsa_append_kv(kv, seqs, heads, k_new, v_new, k_new_sz, v_new_sz, stats);
+ *   lsa_select_pages(q, q_dtype, kv, stats, seqs, heads, token_budget,
+ *                    decode_step, reuse_interval, selected);
+ *   lsa_sparse_decode_attn(q, q_dtype, kv, seqs, heads, selected,
+ *                          token_budget, softmax_scale, out, stats = NULL);
+ * in two launches instead of three: the selection takes token t's key row
+ * (and int4 page scale / zero point) from k_new (k_new_sz) instead of the
+ * pool, and the decode kernel's workgroup that reads t's page attends t from
+ * the staged rows and writes them to the pool or the stream cache (and, for
+ * retrieval heads, folds t into its logical page's statistics), so the token
+ * does not make a round trip through memory before it is attended.
+ * Arguments are those of the three calls; stats must be non-NULL when a
+ * retrieval head exists.  selected may be NULL only when every head is a
+ * streaming head.  workspace: at least lsa_decode_step_workspace bytes,
+ * 256-byte aligned, zero-filled before its first use, with the counter
+ * contract of lsa_select_pages and lsa_sparse_decode_attn (both launches use
+ * it in stream order).  The pool slots of token t and the statistics of its
+ * logical page may be read and written by this call only: calls on other
+ * streams that read them race.  Errors: those of the three calls, all
+ * checked before anything is launched. */
+lsa_status lsa_decode_step(const void *q, int32_t q_dtype, const lsa_kv *kv, const lsa_seqs *seqs,
+                           const lsa_heads *heads, const void *k_new, const void *v_new,
+                           const uint16_t *k_new_sz, const uint16_t *v_new_sz, void *stats,
+                           int32_t token_budget, int32_t decode_step, int32_t reuse_interval,
+                           int32_t *selected, float softmax_scale, void *out, void *workspace,
+                           size_t workspace_bytes, void *stream);
+
 /* Block-sparse causal prefill attention of one sequence over non-empty tiles
  * only ([LS-X] 統一ブロックスパースアテンション: iterate the non-empty blocks;
  * the figure's retrieval heads use a static causal pattern in prefill and

@@ -353,6 +353,40 @@ def test_stream_cache_validation(lib):
         lsa.LSA_ERR_INVALID_ARG
 
 
+def test_decode_step_validation(lib):
+    """lsa_decode_step rejects bad arguments of any of its three parts before
+    it launches anything (the fake device addresses are never touched)."""
+    kv, h, seqs = kv_desc(), heads_desc(), seqs_desc()
+    need = ctypes.c_size_t(0)
+    assert lib.lsa_decode_step_workspace(ctypes.byref(kv), ctypes.byref(seqs), ctypes.byref(h), 4096,
+                                         ctypes.byref(need)) == lsa.LSA_OK
+    sel, dec = ctypes.c_size_t(0), ctypes.c_size_t(0)
+    lib.lsa_select_pages_workspace(ctypes.byref(kv), ctypes.byref(seqs), ctypes.byref(h), ctypes.byref(sel))
+    lib.lsa_decode_workspace(ctypes.byref(kv), ctypes.byref(seqs), ctypes.byref(h), 4096, ctypes.byref(dec))
+    assert need.value == max(sel.value, dec.value) > 0
+
+    def call(kvd=kv, hd=h, q_dtype=lsa.BF16, k_new=FAKE, sz=None, stats=FAKE, budget=4096, step=0, R=4,
+             selected=FAKE, scale=0.0, out=FAKE, ws_bytes=None):
+        return lib.lsa_decode_step(FAKE, q_dtype, ctypes.byref(kvd), ctypes.byref(seqs), ctypes.byref(hd), k_new,
+                                   FAKE, sz, sz, stats, budget, step, R, selected, scale, out, FAKE,
+                                   need.value if ws_bytes is None else ws_bytes, None)
+
+    assert call(k_new=None) == lsa.LSA_ERR_INVALID_ARG
+    assert call(sz=FAKE) == lsa.LSA_ERR_INVALID_ARG                  # (s, z) rows for a bf16 pool
+    assert call(kvd=kv_desc(dtype=lsa.INT4, sz=True)) == lsa.LSA_ERR_INVALID_ARG   # int4 without them
+    assert call(stats=None) == lsa.LSA_ERR_INVALID_ARG               # retrieval heads need statistics
+    assert call(selected=None) == lsa.LSA_ERR_INVALID_ARG
+    assert call(ws_bytes=need.value - 1) == lsa.LSA_ERR_WORKSPACE
+    assert call(budget=100) == lsa.LSA_ERR_INVALID_ARG
+    assert call(R=0) == lsa.LSA_ERR_INVALID_ARG
+    assert call(step=-1) == lsa.LSA_ERR_INVALID_ARG
+    assert call(out=None) == lsa.LSA_ERR_INVALID_ARG                 # a decode-only check, still before any launch
+    assert call(scale=float("nan")) == lsa.LSA_ERR_INVALID_ARG
+    assert call(q_dtype=lsa.F32) == lsa.LSA_ERR_UNSUPPORTED          # f32 queries on a bf16 pool
+    # reuse steps skip the selection, not the checks
+    assert call(step=1, out=None) == lsa.LSA_ERR_INVALID_ARG
+
+
 def test_append_validation(lib):
     kv = kv_desc()
     h = heads_desc()

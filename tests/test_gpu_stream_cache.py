@@ -43,8 +43,9 @@ class CacheRunner:
     """Decode through append + select + attend with the streaming heads in a
     stream cache filled from the prompt, the retrieval heads in a pool of their own."""
 
-    def __init__(self, w):
+    def __init__(self, w, fused=False):
         self.w = w
+        self.fused = fused
         full = H.kv_pool(w)
         self.hd = H.heads(w)
         sink, ring = lsa.stream_cache_pages(full, self.hd)
@@ -66,6 +67,8 @@ class CacheRunner:
                                   dtype=torch.uint8, device=DEV)
         self.ws_dec = torch.zeros(lsa.decode_workspace(self.kv, w.page_table, lens0, self.hd, w.token_budget),
                                   dtype=torch.uint8, device=DEV)
+        self.ws_step = torch.zeros(lsa.decode_step_workspace(self.kv, w.page_table, lens0, self.hd, w.token_budget),
+                                   dtype=torch.uint8, device=DEV)
         self.rows = [W.token_rows(w, i) for i in range(w.window)]
         self.history = []
 
@@ -98,6 +101,15 @@ class CacheRunner:
     def step(self, i):
         w = self.w
         lens = w.seq_lens(i)
+        if self.fused:
+            out = torch.empty_like(w.q[i])
+            rows = self.rows[i]
+            lsa.decode_step(w.q[i], self.kv, w.page_table, lens, self.hd, rows[0], rows[1], self.stats,
+                            w.token_budget, i, w.reuse_interval, self.selected, out, self.ws_step,
+                            *rows[2:])
+            torch.cuda.synchronize()
+            self.history.append(self.selected.cpu().numpy().copy())
+            return out
         lsa.append_kv(self.kv, w.page_table, lens, self.hd, *self.rows[i], stats=self.stats)
         lsa.select_pages(w.q[i], self.kv, self.stats, w.page_table, lens, self.hd, w.token_budget, i,
                          w.reuse_interval, self.selected, self.ws_sel)
@@ -109,8 +121,8 @@ class CacheRunner:
         return out
 
 
-def check_cache_window(w, batches=None, kv_heads=None):
-    r = CacheRunner(w)
+def check_cache_window(w, batches=None, kv_heads=None, fused=False):
+    r = CacheRunner(w, fused=fused)
     gpu = [H.to_f64(r.step(i)) for i in range(w.window)]
     assert not any(np.isnan(g).any() for g in gpu)
     worst = 0.0
@@ -149,13 +161,15 @@ CASES = [
 ]
 
 
+@pytest.mark.parametrize("fused", [False, True], ids=["3calls", "fused"])
 @pytest.mark.parametrize("name,make", CASES, ids=[c[0] for c in CASES])
-def test_append_select_attend_window_with_stream_cache(name, make):
-    """The whole window through append + select + attend: selections and
-    outputs match the oracle (which reads every token of every head), and
-    the statistics the appends updated equal the oracle's at the final length."""
+def test_append_select_attend_window_with_stream_cache(name, make, fused):
+    """The whole window through append + select + attend (three calls, or
+    lsa_decode_step's two launches): selections and outputs match the oracle
+    (which reads every token of every head), and the statistics the appends
+    updated equal the oracle's at the final length."""
     w = make()
-    r, worst = check_cache_window(w)
+    r, worst = check_cache_window(w, fused=fused)
     print("max abs err", worst)
     S.check_stats(w, stats_as_full_layout(w, r), [c + w.window for c in w.ctx], kinds=w.head_kind)
 
