@@ -588,7 +588,8 @@ lsa_status select_impl(const void *q, int32_t q_dtype, const lsa_kv *kv, const v
     sa.pages_per_block =
         sa.aggregation == LSA_AGG_MAX
             ? score_pages_per_block(kv->kv_dtype, kv->head_dim, kv->page_size, kv->logical_page, sa.fused_pt, true)
-            : score_loop_pages_per_block(seqs->batch, sa.n_ret, seqs->max_pages, kv->page_size, kv->logical_page);
+            : score_loop_pages_per_block(seqs->batch, sa.n_ret, seqs->max_pages, kv->page_size, kv->logical_page,
+                                         kv->kv_dtype);
     sa.blocks_per_head = (seqs->max_pages + sa.pages_per_block - 1) / sa.pages_per_block;
     if (lsa_status s = from_hip(launch_score(sa, stream), "select_pages score launch")) return s;
     if (sa.fused_pt > 0) return ok();              // the score kernel's last workgroups have selected

@@ -547,16 +547,27 @@ __global__ __launch_bounds__(kScoreThreads) void score_kernel(ScoreArgs a) {
 // ---------------------------------------------------------------------------
 // Scoring with the group's scores summed, as a loop with a ring of loads.  A
 // workgroup covers pages_per_block physical pages of one (sequence, retrieval
-// head), several workgroups per head so that about four run on every CU.
-// The pool ids of the range are staged in LDS first; each lane group then
-// walks its logical pages j0 + lg, j0 + lg + GROUPS, ... through a ring of
-// kRing register slots: the statistics of the (k + kRing)-th page are
-// requested as the k-th is scored, so a workgroup's memory stream does not
-// drain between pages.  Every slot is always loaded (a slot past the range
-// reads the range's first page and is discarded), so the wait before a slot
-// counts exactly the loads issued after it.
+// head), several workgroups per head so that a fixed number run on every CU
+// (score_loop_wgs_per_cu).  The pool ids of the range are staged in LDS
+// first; each lane group then walks its logical pages j0 + lg, j0 + lg +
+// GROUPS, ... through a ring of score_ring register slots: the statistics of
+// the (k + ring)-th page are requested as the k-th is scored, so a
+// workgroup's memory stream does not drain between pages.  Every slot is
+// always loaded (a slot past the range reads the range's first page and is
+// discarded), so the wait before a slot counts exactly the loads issued after
+// it.  The depth is what keeps HBM busy and no more: every request beyond
+// that only lengthens the memory queues, and the loads that start a
+// workgroup (its page ids, its queries) then wait behind the other
+// workgroups' streams.  Measured on MI355X (selection call, 8 x 4 heads at
+// 64K tokens, 67 MB of bf16 statistics): a ring of 2 at two workgroups per
+// CU takes 23.5 us, a ring of 8 at four per CU 29.1 us.  int4 statistics
+// (16 bytes per lane and page instead of 32, and more arithmetic per byte)
+// keep a ring of 8 at four per CU (60 us against 72 us for 16 x 4 heads at
+// 256K tokens).
 // ---------------------------------------------------------------------------
-constexpr int kRing = 8;
+template <int KV_DT>
+__host__ __device__ constexpr int score_ring() { return KV_DT == LSA_INT4 ? 8 : 2; }
+constexpr int kMaxRing = 8;
 constexpr int kMaxRangePages = 1024;      // physical pages per workgroup (pool ids in LDS)
 constexpr int kMaxRangeLogical = 2048;    // logical pages per workgroup (scores in LDS)
 
@@ -644,6 +655,8 @@ __global__ __launch_bounds__(kScoreThreads) void score_loop_kernel(ScoreArgs a) 
     // the ring over this lane group's logical pages; the trip count is the
     // wavefront's largest (its first lane group's), the rest is discarded
     const int K_w = max(0, (j1 - j0 - wave * LPP + GROUPS - 1) / GROUPS);
+    constexpr int kRing = score_ring<KV_DT>();
+    static_assert(kRing <= kMaxRing, "ring");
     uint4 rl[kRing], rh[kRing];
     uint32_t rs[kRing];
     auto issue = [&](int s, int k) {
@@ -774,11 +787,13 @@ hipError_t launch_score_dt(const ScoreArgs &a, unsigned grid, hipStream_t s) {
 
 }  // namespace
 
-int score_loop_pages_per_block(int batch, int n_ret, int max_pages, int page_size, int logical_page) {
-    // about four workgroups per CU over the chip (the kernel fits four
-    // wavefronts per SIMD), within the LDS range limits
+int score_loop_wgs_per_cu(int kv_dtype) { return kv_dtype == LSA_INT4 ? 4 : 2; }
+
+int score_loop_pages_per_block(int batch, int n_ret, int max_pages, int page_size, int logical_page, int kv_dtype) {
+    // score_loop_wgs_per_cu workgroups per CU over the chip, within the LDS
+    // range limits
     const long long heads = (long long)batch * n_ret;
-    const long long slots = 4LL * 256;
+    const long long slots = (long long)score_loop_wgs_per_cu(kv_dtype) * 256;
     const long long wph = heads >= slots ? 1 : (slots + heads - 1) / heads;
     long long ppb = (max_pages + wph - 1) / wph;
     const int g = page_size / logical_page;
