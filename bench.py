@@ -122,7 +122,58 @@ def hbm_reference(torch):
         ms = e0.elapsed_time(e1) / reps
         out[name] = {"ms": round(ms, 4), "gbps": round(nbytes / ms / 1e6, 1), "frac_of_8000": round(nbytes / ms / 1e6 / 8000, 4)}
     del a, b
-    return {"hbm": "4 GiB fp32 streams through torch", **out}
+    out["hip_read"] = hip_read_reference(torch)
+    return {"hbm": "4 GiB fp32 streams through torch; plain HIP streaming reads of 85 MB to 1 GiB", **out}
+
+
+def hip_read_reference(torch):
+    """A plain streaming-read kernel (block_sparse_attention_logical_amd/calib)
+    over buffers of the decode launch's size and larger: what a read of that
+    size sustains, ramp-up and tail included.  Eight buffers (two of 1 GiB)
+    are read in turn inside a HIP graph, so no read hits the last-level cache."""
+    import ctypes
+    path = os.path.join(ROOT, "block_sparse_attention_logical_amd", "libcalib.so")
+    lib = ctypes.CDLL(path)
+    lib.calib_read_stream.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int, ctypes.c_void_p,
+                                      ctypes.c_void_p]
+    out = torch.zeros(1 << 16, dtype=torch.int32, device="cuda")
+    res = []
+    for mb in (85, 170, 1024):
+        nbuf = 2 if mb > 256 else 8
+        bufs = [torch.ones(mb * 1000 * 1000 // 16 * 16, dtype=torch.uint8, device="cuda") for _ in range(nbuf)]
+        for grid in (1024, 4096):
+            def run():
+                for b_ in bufs:
+                    st = lib.calib_read_stream(b_.data_ptr(), b_.numel(), grid, out.data_ptr(),
+                                               torch.cuda.current_stream().cuda_stream)
+                    if st != 0:
+                        raise RuntimeError(f"calib_read_stream: hip error {st}")
+            s_ = torch.cuda.Stream()
+            s_.wait_stream(torch.cuda.current_stream())
+            with torch.cuda.stream(s_):
+                run()
+            torch.cuda.current_stream().wait_stream(s_)
+            torch.cuda.synchronize()
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                run()
+            g.replay()
+            torch.cuda.synchronize()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            reps = 10
+            e0.record()
+            for _ in range(reps):
+                g.replay()
+            e1.record()
+            torch.cuda.synchronize()
+            t = e0.elapsed_time(e1) / 1e3 / (reps * nbuf)
+            res.append({"MB": round(bufs[0].numel() / 1e6, 1), "workgroups": grid, "us": round(t * 1e6, 2),
+                        "gbps": round(bufs[0].numel() / t / 1e9, 1),
+                        "frac_of_8000": round(bufs[0].numel() / t / 8e12, 4)})
+            del g
+        del bufs
+        torch.cuda.empty_cache()
+    return res
 
 
 def gemm_reference(torch):
@@ -419,6 +470,8 @@ def bench_decode(args, torch, lsa, W, append=True, fused=True):
     default = args.workload == "llama3-8b" and R == 4 and args.page_size in (None, 64) and \
         args.logical_page in (None, 16) and fused and args.aggregation == "sum"
     traffic = counters_for("decode_step_cfg2", src, launch_bytes) if default else None
+    sel_src = os.path.join(ROOT, "block_sparse_attention_logical_amd", "csrc", "select.hip")
+    sel_traffic = counters_for("score_cfg2", sel_src, sel_call_bytes) if default else None
     return dict(
         w=w, agg=args.aggregation, steps=steps, elapsed=elapsed, tok_s=tok_s, ms_per_step=elapsed / steps * 1e3,
         step_bytes=step_bytes, launch_bytes=launch_bytes, kernel_avg=kernel_avg,
@@ -426,7 +479,9 @@ def bench_decode(args, torch, lsa, W, append=True, fused=True):
         traffic=traffic,
         traffic_source=(f"profiles/decode_step_cfg2_counters.txt, taken on decode.hip sha {sha_of(src)}"
                         if traffic is not None else None),
-        sel_time=sel_time, sel_call_bytes=sel_call_bytes,
+        sel_time=sel_time, sel_call_bytes=sel_call_bytes, sel_traffic=sel_traffic,
+        sel_traffic_source=(f"profiles/score_cfg2_counters.txt, taken on select.hip sha {sha_of(sel_src)}"
+                            if sel_traffic is not None else None),
     )
 
 
@@ -728,6 +783,9 @@ def main():
             "bound": "hbm", "achieved": round(sel_bw / 1e9, 1), "peak": PEAK_HBM / 1e9, "unit": "GB/s",
             "frac": round(sel_bw / PEAK_HBM, 4), "bytes_per_call": int(dec["sel_call_bytes"]),
             "call_us": round(dec["sel_time"] * 1e6, 2),
+            "traffic": dec["sel_traffic"],
+            "traffic_source": dec["sel_traffic_source"] or
+            "none: no committed counter summary covers this workload on this version of select.hip",
         }
     if three is not None:
         line["decode_three_calls"] = {

@@ -1,4 +1,6 @@
-"""Build liblsa.so (HIP for gfx950) in-tree with hipcc.
+"""Build liblsa.so (HIP for gfx950) in-tree with hipcc, and the calibration
+library libcalib.so (a plain streaming-read kernel that bench.py times as the
+HBM reference; not part of the C ABI).
 
     python -m block_sparse_attention_logical_amd.build
 
@@ -18,6 +20,8 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 OUT = os.path.join(PKG, "liblsa.so")
+CALIB_SRC = os.path.join(PKG, "calib", "read_stream.hip")
+CALIB_OUT = os.path.join(PKG, "libcalib.so")
 OBJ_DIR = os.path.join(PKG, "_build")
 
 SOURCES = ["abi.hip", "stats.hip", "select.hip", "decode.hip", "prefill.hip", "append.hip"]
@@ -80,7 +84,20 @@ def build(verbose: bool = True) -> str:
     os.replace(tmp, OUT)
     if verbose:
         print(f"built {OUT}")
+    build_calib(verbose)
     return OUT
+
+
+def build_calib(verbose: bool = True) -> str:
+    tmp = CALIB_OUT + ".tmp"
+    cmd = [hipcc(), *COMMON_FLAGS, "-shared", "-o", tmp, CALIB_SRC]
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    if res.returncode != 0:
+        raise RuntimeError(f"hipcc failed on {CALIB_SRC}:\n{' '.join(cmd)}\n{res.stdout}\n{res.stderr}")
+    os.replace(tmp, CALIB_OUT)
+    if verbose:
+        print(f"built {CALIB_OUT}")
+    return CALIB_OUT
 
 
 if __name__ == "__main__":
