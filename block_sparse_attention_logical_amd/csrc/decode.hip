@@ -422,8 +422,16 @@ __device__ __forceinline__ uint32_t pick(const uint4 &u, int i) {
 // ---------------------------------------------------------------------------
 // MFMA kernel, bf16 or int4 pool, bf16 q
 // ---------------------------------------------------------------------------
+// Wavefronts per SIMD the register budget is set for: three for the int4
+// instances with 64- and 128-token pages (at most 168 VGPRs: past that, with
+// the allocation granule of 8, a SIMD holds two, and a launch of 768
+// workgroups, B = 16 at a 4096-token budget, no longer fits the chip in one
+// round), two otherwise (the 16- and 32-token int4 instances spill at 168).
+__host__ __device__ constexpr int decode_waves_per_simd(int kvt, int np) {
+    return kvt == LSA_INT4 && (np == 64 || np == 128) ? 3 : 2;
+}
 template <int D, int KVT, int NP>
-__global__ __launch_bounds__(kDecodeWaves * kWave, 2) void decode_mfma_kernel(DecodeArgs a) {
+__global__ __launch_bounds__(kDecodeWaves * kWave, decode_waves_per_simd(KVT, NP)) void decode_mfma_kernel(DecodeArgs a) {
     constexpr bool I4 = KVT == LSA_INT4;
     // 16-token pages: a 32-token block is two pages, QK^T tile T (and the
     // value rows of lanes with g4 / 2 == T) coming from page 2i + T of block i
@@ -550,9 +558,9 @@ __global__ __launch_bounds__(kDecodeWaves * kWave, 2) void decode_mfma_kernel(De
     // staged in LDS by wavefront 1 while wavefront 0 resolved the page list
     const uint8_t *s_new8 = reinterpret_cast<const uint8_t *>(s_new);
     uint32_t ksz_n = 0, vsz_n = 0;
-    if (I4 && j_new >= 0) {
-        ksz_n = s_new[2 * kNewRow / 16].x;
-        vsz_n = s_new[2 * kNewRow / 16].y;
+    if (I4 && j_new >= 0) {               // (wavefront-uniform: scalar registers)
+        ksz_n = (uint32_t)__builtin_amdgcn_readfirstlane((int)s_new[2 * kNewRow / 16].x);
+        vsz_n = (uint32_t)__builtin_amdgcn_readfirstlane((int)s_new[2 * kNewRow / 16].y);
     }
 
     // QK^T tile T of a 32-token block holds tokens 16T .. 16T + 15 on MFMA
