@@ -151,6 +151,18 @@ __device__ __forceinline__ uint32_t dpp_u(uint32_t v) {
     return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, CTRL, 0xf, 0xf, false);
 }
 
+// Minimum (MAX = false) or maximum of v over aligned groups of N lanes (N = 1,
+// 2, 4, 8, 16), result in every lane of the group.
+template <int N, bool MAX>
+__device__ __forceinline__ int group_minmax_i(int v) {
+    auto op = [](int x, int y) { return MAX ? max(x, y) : min(x, y); };
+    if constexpr (N >= 2) v = op(v, (int)dpp_u<kDppQuadSwap1>((uint32_t)v));
+    if constexpr (N >= 4) v = op(v, (int)dpp_u<kDppQuadSwap2>((uint32_t)v));
+    if constexpr (N >= 8) v = op(v, (int)dpp_u<kDppHalfMirror>((uint32_t)v));
+    if constexpr (N >= 16) v = op(v, (int)dpp_u<kDppMirror>((uint32_t)v));
+    return v;
+}
+
 // Sum of v over aligned groups of N lanes (N = 1, 2, 4, 8, 16, 32), result in every lane of the group.
 template <int N>
 __device__ __forceinline__ double group_sum_d(double v) {

@@ -669,12 +669,8 @@ __global__ __launch_bounds__(kScoreThreads) void score_loop_kernel(ScoreArgs a) 
         if constexpr (KV_DT == LSA_INT4) rs[s] = load_stream4(a.k_sz + hp * 2);
         else rh[s] = load_stream16(st + D * EB);
     };
-#pragma unroll
-    for (int s = 0; s < kRing; ++s) issue(s, s);
-    for (int k0 = 0; k0 < K_w; k0 += kRing) {
-#pragma unroll
-        for (int s = 0; s < kRing; ++s) {
-            const int k = k0 + s;
+    // the score of the logical page in ring slot s, from fp64 products
+    auto fp_slot = [&](int s) __attribute__((always_inline)) -> double {
             double c0 = 0.0, c1 = 0.0;
             if constexpr (KV_DT == LSA_INT4) {
                 // four independent product chains (even / odd channels)
@@ -708,11 +704,89 @@ __global__ __launch_bounds__(kScoreThreads) void score_loop_kernel(ScoreArgs a) 
                     c1 = fma(qn[c], (double)kmin, c1);
                 }
             }
-            const double sj = finish(group_sum_d<LPL>(c0 + c1), rs[s]);
-            const int j = j0 + lg + k * GROUPS;
-            if (k < K_w && j < j1 && j != j_cur && lane % LPL == 0) s_log[j - j0] = sj;
-            issue(s, k + kRing);                  // (past the range: a discarded reload)
+            return finish(group_sum_d<LPL>(c0 + c1), rs[s]);
+    };
+    auto ring = [&](auto slot_score) __attribute__((always_inline)) {
+#pragma unroll
+        for (int s = 0; s < kRing; ++s) issue(s, s);
+        for (int k0 = 0; k0 < K_w; k0 += kRing) {
+#pragma unroll
+            for (int s = 0; s < kRing; ++s) {
+                const int k = k0 + s;
+                const double sj = slot_score(s);
+                const int j = j0 + lg + k * GROUPS;
+                if (k < K_w && j < j1 && j != j_cur && lane % LPL == 0) s_log[j - j0] = sj;
+                issue(s, k + kRing);              // (past the range: a discarded reload)
+            }
         }
+    };
+    if constexpr (KV_DT == LSA_INT4) {
+        // int4: Qp and -Qn as exact integers on the grid 2^lo when every term is
+        // below 2^32 grid steps (bf16 queries of ordinary range span about 21
+        // bits).  A page's sum then takes byte-digit dot products of the codes
+        // (v_dot4_u32_u8) instead of a conversion and an fp64 product per code.
+        // Every partial sum is an integer below 2^43 grid steps, so it is exact,
+        // and so is the fp64 sum of the other path: both give the same double.
+        int lo = 0x7FFFFFFF, hi = -0x7FFFFFFF;
+#pragma unroll
+        for (int c = 0; c < C; ++c)
+#pragma unroll
+            for (int side = 0; side < 2; ++side) {
+                const double x = side ? -qn[c] : qp[c];
+                if (x != 0.0) {
+                    const unsigned long long u = (unsigned long long)__double_as_longlong(x);
+                    const int ex = int((u >> 52) & 0x7FFu);
+                    const unsigned long long m = (u & 0xFFFFFFFFFFFFFull) | (1ull << 52);
+                    lo = min(lo, ex - 1075 + __builtin_ctzll(m));     // exponent of the lowest set bit
+                    hi = max(hi, ex - 1023);                          // exponent of the leading bit
+                }
+            }
+        // every lane group holds every channel: the same bounds in every lane
+        lo = __builtin_amdgcn_readfirstlane(group_minmax_i<LPL, false>(lo));
+        hi = __builtin_amdgcn_readfirstlane(group_minmax_i<LPL, true>(hi));
+        if (lo > hi) lo = hi = 0;                 // every term is zero
+        if (hi - lo < 32) {
+            // byte digits d of the integers, four channels per register
+            uint32_t dgp[C / 4][4], dgn[C / 4][4];
+#pragma unroll
+            for (int q4 = 0; q4 < C / 4; ++q4)
+#pragma unroll
+                for (int d = 0; d < 4; ++d) { dgp[q4][d] = 0; dgn[q4][d] = 0; }
+#pragma unroll
+            for (int c = 0; c < C; ++c) {
+                const uint32_t ip = (uint32_t)ldexp(qp[c], -lo), in = (uint32_t)ldexp(-qn[c], -lo);
+#pragma unroll
+                for (int d = 0; d < 4; ++d) {
+                    dgp[c / 4][d] |= ((ip >> (8 * d)) & 0xFFu) << (8 * (c % 4));
+                    dgn[c / 4][d] |= ((in >> (8 * d)) & 0xFFu) << (8 * (c % 4));
+                }
+            }
+            const double grid = ldexp(1.0, lo);
+            // (the fp64 terms die here: keep the ring's first loads below this point)
+            __builtin_amdgcn_sched_barrier(0);
+            // sum_c Qp c_max + Qn c_min = grid * sum_d 256^d (digit_d(Qp) . c_max - digit_d(-Qn) . c_min)
+            ring([&](int s) __attribute__((always_inline)) -> double {
+                const uint32_t wd[4] = {rl[s].x, rl[s].y, rl[s].z, rl[s].w};
+                uint32_t ap[4] = {0u, 0u, 0u, 0u}, an[4] = {0u, 0u, 0u, 0u};
+#pragma unroll
+                for (int q4 = 0; q4 < C / 4; ++q4) {
+                    const uint32_t cmax = (wd[q4] >> 4) & 0x0F0F0F0Fu, cmin = wd[q4] & 0x0F0F0F0Fu;
+#pragma unroll
+                    for (int d = 0; d < 4; ++d) {
+                        ap[d] = __builtin_amdgcn_udot4(cmax, dgp[q4][d], ap[d], false);
+                        an[d] = __builtin_amdgcn_udot4(cmin, dgn[q4][d], an[d], false);
+                    }
+                }
+                // each ap / an < 16 * 15 * 255: the two halves fit int32, the sum 2^40
+                const int lo_i = int(ap[0] + (ap[1] << 8)) - int(an[0] + (an[1] << 8));
+                const int hi_i = int(ap[2] + (ap[3] << 8)) - int(an[2] + (an[3] << 8));
+                return finish(group_sum_d<LPL>(fma((double)hi_i, 65536.0, (double)lo_i)) * grid, rs[s]);
+            });
+        } else {
+            ring(fp_slot);                        // terms too wide for one 32-bit grid (rare)
+        }
+    } else {
+        ring(fp_slot);
     }
     __syncthreads();
     // P_m = max over the logical pages of physical page m
@@ -787,7 +861,7 @@ hipError_t launch_score_dt(const ScoreArgs &a, unsigned grid, hipStream_t s) {
 
 }  // namespace
 
-int score_loop_wgs_per_cu(int kv_dtype) { return kv_dtype == LSA_INT4 ? 4 : 2; }
+int score_loop_wgs_per_cu(int kv_dtype) { return kv_dtype == LSA_INT4 ? 3 : 2; }
 
 int score_loop_pages_per_block(int batch, int n_ret, int max_pages, int page_size, int logical_page, int kv_dtype) {
     // score_loop_wgs_per_cu workgroups per CU over the chip, within the LDS

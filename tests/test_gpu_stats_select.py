@@ -264,3 +264,32 @@ def test_select_either_side_of_one_kernel_limit(cfg, pages):
     del w
     torch.cuda.empty_cache()
 
+
+
+@pytest.mark.parametrize("mode", ["wide-span", "zero-group", "ordinary"])
+def test_select_int4_query_terms_and_the_integer_grid(mode):
+    """int4 scoring takes a group's folded query terms (Qp, -Qn) as integers on
+    one grid of 32 bits when they fit, which every generated query does
+    ("ordinary"): then every score is exact.  A query whose terms span more
+    than 32 bits ("wide-span": one channel of one head set to 2^-30, one of
+    another group's to -1.25 * 2^-33) takes the fp64 products instead; a group
+    whose query is all zero ("zero-group") scores every page 0 and keeps the
+    lowest pages.  Each ranks as the oracle does.  (In the wide-span case
+    neither side's fp64 sums need be exact; the K-th / (K+1)-th gap printed
+    below is far above any rounding difference.)"""
+    w = W.make_decode(5, DEV, batch=2, ctx=[6000, 9000])      # 94 and 141 pages for K = 64
+    G = w.num_q_heads // w.num_kv_heads
+    ret = [kv for kv in range(w.num_kv_heads) if w.head_kind[kv] == 0]
+    if mode == "wide-span":
+        w.q[0, 0, ret[0] * G, 5] = 2.0 ** -30
+        w.q[0, 1, ret[1] * G + 1, 17] = -1.25 * 2.0 ** -33
+    elif mode == "zero-group":
+        w.q[0, 0, ret[0] * G:(ret[0] + 1) * G] = 0
+    lens = [c + 1 for c in w.ctx]
+    sel = run_select(w, 0, lens)
+    gaps = []
+    check_selection(w, 0, lens, sel, report=gaps)
+    print("smallest relative K / K+1 gap", min(gaps))
+    if mode == "zero-group":
+        K = w.token_budget // w.page_size
+        assert sel[0, ret[0]].cpu().tolist() == list(range(K))
