@@ -231,16 +231,17 @@ __device__ __forceinline__ void topk_rows(const double *P, int L, int page_size,
     __shared__ unsigned long long sh_and[NT / kWave], sh_or[NT / kWave];
     const int tid = threadIdx.x;
 
-    // thread t owns the contiguous pages [t*seg, t*seg + cnt); the scores of
-    // its pages are loaded together and turned into keys as they arrive
-    constexpr int seg = PT;
-    const int i0 = min(max_pages, tid * seg);
+    // thread t owns the contiguous pages [t*seg, t*seg + cnt), seg = ceil(n /
+    // NT) <= PT; the scores of its pages are loaded together and turned into
+    // keys as they arrive
     const int n = (L + page_size - 1) / page_size;
     if (n <= K) {                                 // every page, ascending, padded with -1
         for (int i = tid; i < K; i += NT) out[i] = i < n ? i : -1;
         return;
     }
-    const int cnt = max(0, min(n, i0 + seg) - i0);
+    const int seg = (n + NT - 1) / NT;
+    const int i0 = min(n, tid * seg);
+    const int cnt = min(n, i0 + seg) - i0;
     unsigned long long key[PT];
 #pragma unroll
     for (int e = 0; e < PT; ++e) {
@@ -891,8 +892,10 @@ int topk_max_pages() { return kTopkThreads * kTopkPerThread; }
 
 int score_fused_pt(int max_pages, bool agg_max) {
     const int per = (max_pages + kScoreThreads - 1) / kScoreThreads;
-    // (a 32-page instance was slower: it cost the scoring kernel a wavefront
-    // per SIMD, and its ranking left half the threads idle)
+    // (32 pages per thread cost the max-aggregation kernel a wavefront per
+    // SIMD; in the sum kernel one 256-thread ranking of 4097 pages at the end
+    // took longer than the separate 1024-thread kernel: 62.9 against 51.9 us
+    // per int4 selection call at 256K tokens)
     (void)agg_max;
     return per <= 4 ? 4 : per <= 8 ? 8 : per <= 16 ? 16 : 0;
 }

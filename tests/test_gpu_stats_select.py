@@ -247,19 +247,22 @@ def test_select_full_size_cfg2():
     print(f"smallest relative gap between the K-th and (K+1)-th page scores: {min(gaps):.3e}")
 
 
-@pytest.mark.parametrize("cfg,pages", [(2, 4096), (2, 4097), (5, 4096), (5, 4097)])
-def test_select_either_side_of_one_kernel_limit(cfg, pages):
+@pytest.mark.parametrize("cfg,pages,agg", [(2, 4096, lsa.AGG_SUM), (2, 4097, lsa.AGG_SUM), (5, 4096, lsa.AGG_SUM),
+                                            (5, 4097, lsa.AGG_SUM), (2, 4096, lsa.AGG_MAX), (2, 4097, lsa.AGG_MAX)],
+                         ids=["bf16-4096", "bf16-4097", "int4-4096", "int4-4097", "bf16-max-4096", "bf16-max-4097"])
+def test_select_either_side_of_one_kernel_limit(cfg, pages, agg):
     """Up to 4096 pages per sequence the last score workgroup of a (sequence,
     head) runs its top-K; from 4097 pages a separate top-K kernel does.  Both
-    sides of that limit, for the bf16 pool (config 2) and the int4 pool
-    (config 5, whose 256K context has 4097 pages), with a shorter second
-    sequence in the batch; every retrieval head, bit for bit."""
+    sides of that limit, for the bf16 pool (config 2) with the group's scores
+    summed and combined by max, and the int4 pool (config 5, whose 256K
+    context has 4097 pages), with a shorter second sequence in the batch;
+    every retrieval head, bit for bit."""
     w = W.make_decode(cfg, DEV, batch=2, ctx=[pages * 64 - 4, 3000])      # + 4 window tokens
     assert w.max_pages == pages
     lens = [c + 1 for c in w.ctx]
-    sel = run_select(w, 0, lens)
+    sel = run_select(w, 0, lens, agg=agg)
     gaps = []
-    check_selection(w, 0, lens, sel, report=gaps)
+    check_selection(w, 0, lens, sel, report=gaps, agg=agg)
     print(f"smallest relative gap between the K-th and (K+1)-th page scores: {min(gaps):.3e}")
     del w
     torch.cuda.empty_cache()
