@@ -843,15 +843,16 @@ hipError_t launch_score_agg(const ScoreArgs &a, unsigned grid, hipStream_t s) {
             default: return hipErrorInvalidValue;
         }
         return hipGetLastError();
+    } else {
+        switch (a.fused_pt) {
+            case 0: launch_score_fpt<KV_DT, AGG_MAX, 0>(a, grid, s); break;
+            case 4: launch_score_fpt<KV_DT, AGG_MAX, 4>(a, grid, s); break;
+            case 8: launch_score_fpt<KV_DT, AGG_MAX, 8>(a, grid, s); break;
+            case 16: launch_score_fpt<KV_DT, AGG_MAX, 16>(a, grid, s); break;
+            default: return hipErrorInvalidValue;
+        }
+        return hipGetLastError();
     }
-    switch (a.fused_pt) {
-        case 0: launch_score_fpt<KV_DT, AGG_MAX, 0>(a, grid, s); break;
-        case 4: launch_score_fpt<KV_DT, AGG_MAX, 4>(a, grid, s); break;
-        case 8: launch_score_fpt<KV_DT, AGG_MAX, 8>(a, grid, s); break;
-        case 16: launch_score_fpt<KV_DT, AGG_MAX, 16>(a, grid, s); break;
-        default: return hipErrorInvalidValue;
-    }
-    return hipGetLastError();
 }
 
 template <int KV_DT>
