@@ -105,20 +105,20 @@ int count_kind(const lsa_heads *hd, int h_kv, int kind) {
     return n;
 }
 
-// Head slots of the pool: every KV head, or only the retrieval heads (in
-// KV-head order) when the streaming heads live in a stream cache; and the
-// rank of each streaming head among the streaming heads.
-void pool_heads_of(const lsa_kv *kv, const lsa_heads *hd, PoolHeads &ph, int *n_str = nullptr,
-                   uint8_t *str_slot = nullptr) {
+// The head map of a layer: the streaming heads as a bit mask, and the head
+// slots of the pool: every KV head, or only the retrieval heads (in KV-head
+// order) when the streaming heads live in a stream cache.
+void pool_heads_of(const lsa_kv *kv, const lsa_heads *hd, HeadMap &hm, int *n_str = nullptr) {
+    hm.str_mask = 0;
     int r = 0, st = 0;
     for (int i = 0; i < kv->num_kv_heads; ++i) {
         const bool ret = !hd || hd->head_kind[i] == LSA_RETRIEVAL_HEAD;
-        ph.pool_slot[i] = (uint8_t)(kv->stream_cache ? (ret ? r : 0) : i);
-        if (str_slot) str_slot[i] = (uint8_t)(ret ? 0 : st);
+        if (!ret) hm.str_mask |= 1ull << i;
         r += ret;
         st += !ret;
     }
-    ph.pool_heads = kv->stream_cache ? r : kv->num_kv_heads;
+    hm.pool_heads = kv->stream_cache ? r : kv->num_kv_heads;
+    hm.by_rank = kv->stream_cache ? 1 : 0;
     if (n_str) *n_str = st;
 }
 
@@ -293,12 +293,12 @@ lsa_status lsa_page_stats_bytes(const lsa_kv *kv, const lsa_heads *heads, size_t
     if (lsa_status s = check_heads(heads, kv, kv->stream_cache != nullptr)) return s;
     if (lsa_status s = check_pool(kv, heads)) return s;
     if (!bytes) return fail(LSA_ERR_INVALID_ARG, "bytes is NULL");
-    PoolHeads ph;
-    pool_heads_of(kv, heads, ph);
+    HeadMap hm;
+    pool_heads_of(kv, heads, hm);
     const size_t g = kv->page_size / kv->logical_page;
     const size_t per = kv->kv_dtype == LSA_INT4 ? (size_t)kv->head_dim
                                                  : 2 * (size_t)kv->head_dim * (kv->kv_dtype == LSA_F32 ? 4 : 2);
-    *bytes = (size_t)kv->num_pages * ph.pool_heads * g * per;
+    *bytes = (size_t)kv->num_pages * hm.pool_heads * g * per;
     return ok();
 }
 
@@ -375,8 +375,7 @@ lsa_status lsa_append_kv(const lsa_kv *kv, const lsa_seqs *seqs, const lsa_heads
     a.page_size = kv->page_size;
     a.logical_page = kv->logical_page;
     a.dtype = kv->kv_dtype;
-    for (int i = 0; i < kv->num_kv_heads; ++i) a.kind[i] = heads->head_kind[i];
-    pool_heads_of(kv, heads, a.ph, &a.n_str, a.str_slot);
+    pool_heads_of(kv, heads, a.hm, &a.n_str);
     if (const lsa_stream_cache *sc = kv->stream_cache) {
         a.sc_k = sc->k;
         a.sc_v = sc->v;
@@ -398,7 +397,7 @@ lsa_status lsa_build_page_stats(const lsa_kv *kv, const lsa_seqs *seqs, const ls
     if (!stats) return fail(LSA_ERR_INVALID_ARG, "stats is NULL");
     if (max_new_tokens < 0) return fail(LSA_ERR_INVALID_ARG, "max_new_tokens < 0");
     StatsArgs a{};
-    pool_heads_of(kv, heads, a.ph);
+    pool_heads_of(kv, heads, a.hm);
     a.k = kv->k;
     a.k_sz = kv->k_sz;
     a.stats = stats;
@@ -557,7 +556,7 @@ lsa_status select_impl(const void *q, int32_t q_dtype, const lsa_kv *kv, const v
     if (n_ret == 0 || seqs->batch == 0) return ok();
 
     ScoreArgs sa{};
-    pool_heads_of(kv, heads, sa.ph);
+    pool_heads_of(kv, heads, sa.hm);
     sa.q = q;
     sa.stats = stats;
     sa.k = kv->k;
@@ -582,9 +581,7 @@ lsa_status select_impl(const void *q, int32_t q_dtype, const lsa_kv *kv, const v
     sa.q_dtype = q_dtype;
     sa.kv_dtype = kv->kv_dtype;
     sa.aggregation = heads->score_aggregation;
-    sa.n_ret = 0;
-    for (int i = 0; i < kv->num_kv_heads; ++i)
-        if (heads->head_kind[i] == LSA_RETRIEVAL_HEAD) sa.ret_heads[sa.n_ret++] = (uint8_t)i;
+    sa.n_ret = n_ret;
     sa.pages_per_block =
         sa.aggregation == LSA_AGG_MAX
             ? score_pages_per_block(kv->kv_dtype, kv->head_dim, kv->page_size, kv->logical_page, sa.fused_pt, true)
@@ -604,7 +601,7 @@ lsa_status select_impl(const void *q, int32_t q_dtype, const lsa_kv *kv, const v
     ta.page_size = kv->page_size;
     ta.k = token_budget / kv->page_size;
     ta.n_ret = sa.n_ret;
-    std::memcpy(ta.ret_heads, sa.ret_heads, sizeof(ta.ret_heads));
+    ta.hm = sa.hm;
     return from_hip(launch_topk(ta, stream), "select_pages top-K launch");
 }
 
@@ -678,8 +675,7 @@ lsa_status decode_attn_impl(const void *q, int32_t q_dtype, const lsa_kv *kv, co
     a.chunks_per_seq = n_ret * g.chunks_ret + (kv->num_kv_heads - n_ret) * g.chunks_str;
     const float scale = softmax_scale > 0.f ? softmax_scale : 1.f / std::sqrt((float)kv->head_dim);
     a.scale_log2 = scale * 1.4426950408889634f;
-    for (int i = 0; i < kv->num_kv_heads; ++i) a.kind[i] = heads->head_kind[i];
-    pool_heads_of(kv, heads, a.ph, &a.n_str, a.str_slot);
+    pool_heads_of(kv, heads, a.hm, &a.n_str);
     if (const lsa_stream_cache *sc = kv->stream_cache) {
         a.sc_k = sc->k;
         a.sc_v = sc->v;

@@ -30,11 +30,11 @@ __global__ __launch_bounds__(kAppendWaves * kWave) void append_kernel(AppendArgs
     const int bs = block_shift(NP);
     const int t = a.seq_lens[b] - 1;
     const int m = t / NP, slot = t % NP;
-    const bool streaming = a.kind[kv] != 0;
+    const bool streaming = head_streaming(a.hm, kv);
     const bool in_cache = streaming && a.sc_k != nullptr;
-    const size_t hp = in_cache ? (size_t)stream_cache_page(b, a.str_slot[kv], m, a.n_str, a.sc_sink, a.sc_ring)
-                               : (size_t)a.page_table[(size_t)b * a.max_pages + m] * a.ph.pool_heads +
-                                     a.ph.pool_slot[kv];
+    const size_t hp = in_cache ? (size_t)stream_cache_page(b, streaming_rank(a.hm, kv), m, a.n_str, a.sc_sink, a.sc_ring)
+                               : (size_t)a.page_table[(size_t)b * a.max_pages + m] * a.hm.pool_heads +
+                                     pool_slot(a.hm, kv);
     const size_t page_base = hp * NP * D;
     const size_t row = (size_t)item * D;          // the token's K / V row in k_new, v_new
     const bool upd = a.stats != nullptr && !streaming;

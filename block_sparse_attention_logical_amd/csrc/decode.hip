@@ -65,13 +65,13 @@ __device__ __forceinline__ WorkItem decode_item(const DecodeArgs &a) {
     int off = blockIdx.x % a.chunks_per_seq;
     int kv = 0;
     for (; kv < a.num_kv_heads; ++kv) {
-        const int c = a.kind[kv] ? a.chunks_str : a.chunks_ret;
+        const int c = head_streaming(a.hm, kv) ? a.chunks_str : a.chunks_ret;
         if (off < c) break;
         off -= c;
     }
     w.kv = kv;
     w.chunk = off;
-    w.streaming = a.kind[kv] != 0;
+    w.streaming = head_streaming(a.hm, kv);
     return w;
 }
 
@@ -121,7 +121,7 @@ __device__ __forceinline__ void wg_pages(const DecodeArgs &a, const WorkItem &w,
     int pool = -1;                    // pool page, or the stream-cache page of a streaming head
     if (lane < CP && page >= 0)
         pool = w.streaming && a.sc_k
-                   ? (int)stream_cache_page(w.b, a.str_slot[w.kv], page, a.n_str, a.sc_sink, a.sc_ring)
+                   ? (int)stream_cache_page(w.b, streaming_rank(a.hm, w.kv), page, a.n_str, a.sc_sink, a.sc_ring)
                    : a.page_table[(size_t)w.b * a.max_pages + page];
     if (lane == 0) { list[0] = t; list[1] = L; }
     if (lane < CP) { list[2 + lane] = page; list[2 + CP + lane] = pool; }
@@ -151,7 +151,7 @@ __device__ __forceinline__ void refresh_current_stats(const DecodeArgs &a, const
     const int m = j / g, jl = j % g;
     const int row0 = jl * NL, rows = w.t - j * NL + 1;
     const int pool = a.page_table[(size_t)w.b * a.max_pages + m];
-    const size_t hp = (size_t)pool * a.ph.pool_heads + a.ph.pool_slot[w.kv];
+    const size_t hp = (size_t)pool * a.hm.pool_heads + pool_slot(a.hm, w.kv);
     const size_t page_base = hp * NP * D;
     if (kv_dtype == LSA_INT4) {
         if (lane >= D / 2) return;
@@ -503,8 +503,8 @@ __global__ __launch_bounds__(kDecodeWaves * kWave, decode_waves_per_simd(KVT, NP
     const void *vpool = in_cache ? a.sc_v : a.v;
     const uint16_t *kszp = in_cache ? a.sc_k_sz : a.k_sz;
     const uint16_t *vszp = in_cache ? a.sc_v_sz : a.v_sz;
-    const size_t hp_mul = in_cache ? 1 : (size_t)a.ph.pool_heads;
-    const size_t hp_add = in_cache ? 0 : a.ph.pool_slot[w.kv];
+    const size_t hp_mul = in_cache ? 1 : (size_t)a.hm.pool_heads;
+    const size_t hp_add = in_cache ? 0 : pool_slot(a.hm, w.kv);
     int pg[PPW];
     size_t hp[PPW];
 #pragma unroll
@@ -888,7 +888,7 @@ __global__ __launch_bounds__(256) void decode_f32_kernel(DecodeArgs a) {
 
     if (my_page >= 0) {
         const int page = my_page;
-        const size_t head_page = in_cache ? (size_t)my_pool : (size_t)my_pool * a.ph.pool_heads + a.ph.pool_slot[w.kv];
+        const size_t head_page = in_cache ? (size_t)my_pool : (size_t)my_pool * a.hm.pool_heads + pool_slot(a.hm, w.kv);
         const float *kp = kpool + head_page * NP * D;
         const float *vp = vpool + head_page * NP * D;
         for (int s0 = 0; s0 < NP; s0 += kWave) {
@@ -955,7 +955,7 @@ __global__ __launch_bounds__(256) void decode_f32_kernel(DecodeArgs a) {
 
     if (put_new) {
         // the token into its page, and into its logical page's statistics
-        const size_t head_page = in_cache ? (size_t)my_pool : (size_t)my_pool * a.ph.pool_heads + a.ph.pool_slot[w.kv];
+        const size_t head_page = in_cache ? (size_t)my_pool : (size_t)my_pool * a.hm.pool_heads + pool_slot(a.hm, w.kv);
         float *kp = const_cast<float *>(kpool) + head_page * NP * D;
         float *vp = const_cast<float *>(vpool) + head_page * NP * D;
         const int slot = w.t % NP, NL = a.logical_page, jl = slot / NL, g = NP / NL;

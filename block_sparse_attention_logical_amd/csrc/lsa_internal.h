@@ -9,7 +9,7 @@
 
 namespace lsa {
 
-constexpr int kMaxKvHeads = 64;   // H_kv limit (host-side tables live in kernel args)
+constexpr int kMaxKvHeads = 64;   // H_kv limit (the head kinds travel as a 64-bit mask)
 constexpr int kWave = 64;         // CDNA wavefront width
 constexpr int kMaxDecodeChunks = 128;   // split-KV chunks per (sequence, KV head)
 
@@ -235,13 +235,37 @@ __device__ __forceinline__ void wave_and_or(unsigned long long &a, unsigned long
 // launch arguments
 // ----------------------------------------------------------------------------
 
-// Where a KV head's pages sit in the pool: pool page p, head slot pool_slot[kv]
-// of pool_heads (every KV head, or only the retrieval heads when the streaming
-// heads live in a stream cache), at element ((p * pool_heads + slot) * N_P * D).
-struct PoolHeads {
+// The layer's KV heads as the kernels see them: the streaming heads as a bit
+// mask (bit kv set: KV head kv is a streaming head), and where each head's
+// pages sit in the pool: pool page p, head slot s of pool_heads, at element
+// ((p * pool_heads + s) * N_P * D).  The pool holds every KV head (slot kv)
+// or, when the streaming heads live in a stream cache, only the retrieval
+// heads (slot = the head's rank among them).  Kernels take a head's kind,
+// slot and rank from the mask with scalar bit operations: a per-head table in
+// the kernel arguments, indexed by a head number known only at run time, is
+// read through the memory hierarchy, one dependent round trip per access, in
+// front of the first K/V or statistics load.
+struct HeadMap {
+    uint64_t str_mask;
     int32_t pool_heads;
-    uint8_t pool_slot[kMaxKvHeads];
+    int32_t by_rank;              // 1: the pool holds the retrieval heads only
 };
+__host__ __device__ __forceinline__ bool head_streaming(const HeadMap &m, int kv) {
+    return (m.str_mask >> kv) & 1u;
+}
+// rank of KV head kv among the streaming heads below it
+__host__ __device__ __forceinline__ int streaming_rank(const HeadMap &m, int kv) {
+    return __builtin_popcountll(m.str_mask & ((1ull << kv) - 1ull));
+}
+__host__ __device__ __forceinline__ int pool_slot(const HeadMap &m, int kv) {
+    return m.by_rank ? kv - streaming_rank(m, kv) : kv;
+}
+// the KV head of the r-th retrieval head (r below the number of retrieval heads)
+__host__ __device__ __forceinline__ int retrieval_head(const HeadMap &m, int r) {
+    uint64_t z = ~m.str_mask;
+    for (int i = 0; i < r; ++i) z &= z - 1ull;
+    return __builtin_ctzll(z);
+}
 
 struct StatsArgs {
     const void *k;
@@ -255,7 +279,7 @@ struct StatsArgs {
     int32_t lp_per_seq;           // logical pages covered per (sequence, head)
     int32_t dtype;
     uint8_t heads_sel[kMaxKvHeads];
-    PoolHeads ph;
+    HeadMap hm;
 };
 
 struct ScoreArgs {
@@ -272,7 +296,6 @@ struct ScoreArgs {
     int32_t n_ret;                // number of retrieval heads
     int32_t pages_per_block;      // physical pages per workgroup
     int32_t blocks_per_head;      // workgroups per (sequence, retrieval head)
-    uint8_t ret_heads[kMaxKvHeads];
     // fused top-K: the last score workgroup of a (sequence, head) selects its
     // pages; arrival counters [B][H_kv] head the workspace.  fused_pt is the
     // top-K's pages per thread (4, 8 or 16), 0 for a separate top-K launch.
@@ -280,7 +303,7 @@ struct ScoreArgs {
     int32_t *selected;            // [B][H_kv][K]
     int32_t k_pages;              // K
     int32_t fused_pt;
-    PoolHeads ph;
+    HeadMap hm;                   // retrieval head r of the workgroups: retrieval_head(hm, r)
     // the newest token's key rows [B][H_kv][D] (int4: D/2 bytes), or null: the
     // current logical page's last row (token t) is then read from the pool.
     // int4: k_new_sz [B][H_kv][2] holds t's page (s, z), used in place of the
@@ -295,7 +318,7 @@ struct TopkArgs {
     int32_t *selected;            // [B][H_kv][K]
     int32_t batch, max_pages, num_kv_heads, page_size, k;
     int32_t n_ret;
-    uint8_t ret_heads[kMaxKvHeads];
+    HeadMap hm;
 };
 
 struct DecodeArgs {
@@ -318,17 +341,15 @@ struct DecodeArgs {
     int32_t chunks_max;               // record slots per (sequence, head)
     int32_t chunks_per_seq;           // workgroups per sequence
     float scale_log2;                 // softmax scale * log2(e)
-    uint8_t kind[kMaxKvHeads];
-    PoolHeads ph;
+    HeadMap hm;
     // streaming heads in a stream cache (sc_k == null: they are in the pool):
-    // page m of (b, s = str_slot[kv]) is cache page (b * n_str + s) * (sink + ring)
-    // + (m < sink ? m : sink + (m - sink) % ring)
+    // page m of (b, s = streaming_rank(hm, kv)) is cache page
+    // (b * n_str + s) * (sink + ring) + (m < sink ? m : sink + (m - sink) % ring)
     const void *sc_k;
     const void *sc_v;
     const uint16_t *sc_k_sz;
     const uint16_t *sc_v_sz;
     int32_t sc_sink, sc_ring, n_str;
-    uint8_t str_slot[kMaxKvHeads];
     // fused append (k_new != null): the newest token's K / V rows [B][H_kv][D]
     // (int4: [B][H_kv][D/2] codes and the page's (s, z) rows [B][H_kv][2]).  The
     // wavefront that reads the page of token t takes the token from these rows
@@ -354,12 +375,10 @@ struct AppendArgs {
     const int32_t *page_table;
     const int32_t *seq_lens;
     int32_t batch, max_pages, num_kv_heads, head_dim, page_size, logical_page, dtype;
-    uint8_t kind[kMaxKvHeads];
-    PoolHeads ph;
+    HeadMap hm;
     void *sc_k, *sc_v;                // stream cache (null: streaming heads are in the pool)
     uint16_t *sc_k_sz, *sc_v_sz;
     int32_t sc_sink, sc_ring, n_str;
-    uint8_t str_slot[kMaxKvHeads];
 };
 
 struct FillArgs {

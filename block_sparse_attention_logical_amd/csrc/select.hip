@@ -335,7 +335,7 @@ template <int PT>
 __global__ __launch_bounds__(kTopkThreads) void topk_kernel(TopkArgs a) {
     const int r = blockIdx.x % a.n_ret;
     const int b = blockIdx.x / a.n_ret;
-    const int kv = a.ret_heads[r];
+    const int kv = retrieval_head(a.hm, r);
     topk_rows<kTopkThreads, PT, false>(a.phys + ((size_t)b * a.num_kv_heads + kv) * a.max_pages, a.seq_lens[b],
                                        a.page_size, a.max_pages, a.k,
                                        a.selected + ((size_t)b * a.num_kv_heads + kv) * a.k);
@@ -360,7 +360,7 @@ __global__ __launch_bounds__(kScoreThreads) void score_kernel(ScoreArgs a) {
     const int rest = blockIdx.x / a.blocks_per_head;
     const int r = rest % a.n_ret;
     const int b = rest / a.n_ret;
-    const int kv = a.ret_heads[r];
+    const int kv = retrieval_head(a.hm, r);
     const int lane = threadIdx.x % kWave;
     const int wave = threadIdx.x / kWave;
     const int lg = wave * LPP + lane / LPL;       // lane group in the workgroup
@@ -397,7 +397,7 @@ __global__ __launch_bounds__(kScoreThreads) void score_kernel(ScoreArgs a) {
         st_hi[it] = make_uint4(0, 0, 0, 0);
         szw[it] = 0;
         if (j < j1 && j != j_cur) {
-            const size_t hp = (size_t)pools[it] * a.ph.pool_heads + a.ph.pool_slot[kv];
+            const size_t hp = (size_t)pools[it] * a.hm.pool_heads + pool_slot(a.hm, kv);
             const int jl = j % g;
             if constexpr (KV_DT == LSA_INT4) {
                 st_lo[it] = load_stream16(static_cast<const uint8_t *>(a.stats) + hp * head_stride + (size_t)jl * D + ch0);
@@ -416,7 +416,7 @@ __global__ __launch_bounds__(kScoreThreads) void score_kernel(ScoreArgs a) {
     uint32_t sz_cur = 0;
     if (own_cur) {
         const int pool = a.page_table[(size_t)b * a.max_pages + j_cur / g];
-        const size_t hp = (size_t)pool * a.ph.pool_heads + a.ph.pool_slot[kv];
+        const size_t hp = (size_t)pool * a.hm.pool_heads + pool_slot(a.hm, kv);
         if constexpr (KV_DT == LSA_INT4)     // (t's page may not have its pair in memory yet)
             sz_cur = *reinterpret_cast<const uint32_t *>(a.k_new ? a.k_new_sz + ((size_t)b * a.num_kv_heads + kv) * 2
                                                                   : a.k_sz + hp * 2);
@@ -585,7 +585,7 @@ __global__ __launch_bounds__(kScoreThreads) void score_loop_kernel(ScoreArgs a) 
     const int rest = blockIdx.x / a.blocks_per_head;
     const int r = rest % a.n_ret;
     const int b = rest / a.n_ret;
-    const int kv = a.ret_heads[r];
+    const int kv = retrieval_head(a.hm, r);
     const int lane = threadIdx.x % kWave;
     const int wave = threadIdx.x / kWave;
     const int lg = wave * LPP + lane / LPL;       // lane group in the workgroup
@@ -602,7 +602,7 @@ __global__ __launch_bounds__(kScoreThreads) void score_loop_kernel(ScoreArgs a) 
     const int nlog = (L + a.logical_page - 1) / a.logical_page;
     const int j1 = min(m1 * g, nlog);
     const int j_cur = (L - 1) / a.logical_page;   // the logical page that holds the current token
-    const size_t slot_kv = a.ph.pool_slot[kv];
+    const size_t slot_kv = pool_slot(a.hm, kv);
     // g, the statistics of one (page, head) unit (g * D bytes for int4, g * 2D
     // elements otherwise) and the row of a logical page are powers of two:
     // addresses are shifts
@@ -611,7 +611,7 @@ __global__ __launch_bounds__(kScoreThreads) void score_loop_kernel(ScoreArgs a) 
     const int row_shift = __builtin_ctz(D) + (KV_DT == LSA_INT4 ? 0 : 1 + __builtin_ctz(EB));
 
     for (int i = threadIdx.x; i < m1 - m0; i += kScoreThreads)
-        s_hp[i] = (unsigned long long)a.page_table[(size_t)b * a.max_pages + m0 + i] * a.ph.pool_heads + slot_kv;
+        s_hp[i] = (unsigned long long)a.page_table[(size_t)b * a.max_pages + m0 + i] * a.hm.pool_heads + slot_kv;
     double qp[C], qn[C];
     load_q_pos_neg<C>(a, b, kv, ch0, 0, G, qp, qn);
     double qsum = 0.0;                            // int4 only: sum over all channels of Qp + Qn

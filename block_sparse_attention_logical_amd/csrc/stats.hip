@@ -51,7 +51,7 @@ __global__ __launch_bounds__(256) void stats_float_kernel(StatsArgs a) {
     const int lane = threadIdx.x % kWave;
     const int D = a.head_dim;
     const int g = a.page_size / a.logical_page;
-    const size_t page_base = ((size_t)it.pool * a.ph.pool_heads + a.ph.pool_slot[it.kv]) * a.page_size * D;
+    const size_t page_base = ((size_t)it.pool * a.hm.pool_heads + pool_slot(a.hm, it.kv)) * a.page_size * D;
     const Elem *k = static_cast<const Elem *>(a.k);
     float mn[CPL], mx[CPL];
 #pragma unroll
@@ -68,7 +68,7 @@ __global__ __launch_bounds__(256) void stats_float_kernel(StatsArgs a) {
         }
     }
     Elem *out = static_cast<Elem *>(a.stats) +
-                ((((size_t)it.pool * a.ph.pool_heads + a.ph.pool_slot[it.kv]) * g + it.jl) * 2) * D + lane * CPL;
+                ((((size_t)it.pool * a.hm.pool_heads + pool_slot(a.hm, it.kv)) * g + it.jl) * 2) * D + lane * CPL;
 #pragma unroll
     for (int c = 0; c < CPL; ++c) {
         if constexpr (sizeof(Elem) == 2) {
@@ -91,7 +91,7 @@ __global__ __launch_bounds__(256) void stats_int4_kernel(StatsArgs a) {
     const int row_bytes = D / 2;
     if (lane >= row_bytes) return;
     const int g = a.page_size / a.logical_page;
-    const size_t page_base = ((size_t)it.pool * a.ph.pool_heads + a.ph.pool_slot[it.kv]) * a.page_size * D;
+    const size_t page_base = ((size_t)it.pool * a.hm.pool_heads + pool_slot(a.hm, it.kv)) * a.page_size * D;
     const uint8_t *k = static_cast<const uint8_t *>(a.k);
     uint32_t lo_min = 15, lo_max = 0, hi_min = 15, hi_max = 0;
     for (int r = 0; r < it.rows; ++r) {
@@ -101,7 +101,7 @@ __global__ __launch_bounds__(256) void stats_int4_kernel(StatsArgs a) {
         hi_min = min(hi_min, hi); hi_max = max(hi_max, hi);
     }
     uint8_t *out = static_cast<uint8_t *>(a.stats) +
-                   (((size_t)it.pool * a.ph.pool_heads + a.ph.pool_slot[it.kv]) * g + it.jl) * D + 2 * lane;
+                   (((size_t)it.pool * a.hm.pool_heads + pool_slot(a.hm, it.kv)) * g + it.jl) * D + 2 * lane;
     const uint16_t pair = uint16_t((lo_min | (lo_max << 4)) | ((hi_min | (hi_max << 4)) << 8));
     *reinterpret_cast<uint16_t *>(out) = pair;
 }
