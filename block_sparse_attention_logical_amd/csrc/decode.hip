@@ -51,7 +51,9 @@ namespace lsa {
 namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float floatx4 __attribute__((ext_vector_type(4)));
+typedef float floatx2 __attribute__((ext_vector_type(2)));
 
 struct WorkItem {
     int b, kv, chunk, t, L;
@@ -394,25 +396,25 @@ __device__ __forceinline__ void finish_head(const DecodeArgs &a, const WorkItem 
     }
 }
 
-// The eight codes of `w` as bf16 bit patterns 0x4300 | c (= 128 + c): dword
-// k holds the low nibble of byte k in its low half and the high nibble in its
-// high half.  The low and high nibbles are masked out once; one byte permute
-// per dword then places byte k of each in bytes 0 and 2 (bytes 1 and 3 zero,
-// selector 12), and one OR sets the exponent bytes.
-__device__ __forceinline__ uint4 nibbles_bf16x8(uint32_t w) {
+// The eight codes of `w` (byte k: code 2k in its low nibble, code 2k + 1 in
+// its high nibble) as bf16 bit patterns 0x4300 | c (= 128 + c), in the order
+// c0 c2 c4 c6 c1 c3 c5 c7.  The low and the high nibbles are masked out once;
+// one byte permute per dword then interleaves two of them with the exponent
+// byte 0x43 of a constant operand (v_perm_b32 selector bytes 0..3 pick bytes
+// of the second operand, 4..7 bytes of the first).  The operand that meets
+// these in the MFMA k dimension is stored in the same order.
+__device__ __forceinline__ uint4 nibbles_bf16x8_split(uint32_t w) {
     const uint32_t lo = w & 0x0F0F0F0Fu, hi = (w >> 4) & 0x0F0F0F0Fu;
-    // v_perm_b32 selector bytes: 0..3 pick bytes of the second operand (lo),
-    // 4..7 bytes of the first (hi), 12 gives 0x00
-    return make_uint4(__builtin_amdgcn_perm(hi, lo, 0x0C040C00u) | 0x43004300u,
-                      __builtin_amdgcn_perm(hi, lo, 0x0C050C01u) | 0x43004300u,
-                      __builtin_amdgcn_perm(hi, lo, 0x0C060C02u) | 0x43004300u,
-                      __builtin_amdgcn_perm(hi, lo, 0x0C070C03u) | 0x43004300u);
+    constexpr uint32_t E = 0x43434343u;
+    return make_uint4(__builtin_amdgcn_perm(E, lo, 0x04010400u), __builtin_amdgcn_perm(E, lo, 0x04030402u),
+                      __builtin_amdgcn_perm(E, hi, 0x04010400u), __builtin_amdgcn_perm(E, hi, 0x04030402u));
 }
 
-// a where the mask bits are 0, b where they are 1
-__device__ __forceinline__ uint4 blend(uint4 a, uint4 b, uint32_t m) {
-    return make_uint4(a.x ^ ((a.x ^ b.x) & m), a.y ^ ((a.y ^ b.y) & m), a.z ^ ((a.z ^ b.z) & m),
-                      a.w ^ ((a.w ^ b.w) & m));
+// Eight bf16 values (x0 .. x7, two to a dword) reordered to x0 x2 x4 x6 x1 x3
+// x5 x7, the order of nibbles_bf16x8_split.
+__device__ __forceinline__ uint4 split_order(uint32_t d0, uint32_t d1, uint32_t d2, uint32_t d3) {
+    return make_uint4(__builtin_amdgcn_perm(d1, d0, 0x05040100u), __builtin_amdgcn_perm(d3, d2, 0x05040100u),
+                      __builtin_amdgcn_perm(d1, d0, 0x07060302u), __builtin_amdgcn_perm(d3, d2, 0x07060302u));
 }
 
 __device__ __forceinline__ uint32_t pick(const uint4 &u, int i) {
@@ -451,8 +453,9 @@ __global__ __launch_bounds__(kDecodeWaves * kWave, decode_waves_per_simd(KVT, NP
     const int G = a.group;
 
     // B operand of QK^T: column h = query head.  bf16 pools: step s holds
-    // channels 32s + 8*g4 + j; int4 pools: channels (D/4)*g4 + 8s + j, so that a
-    // lane's steps cover one contiguous run of codes of its key row.
+    // channels 32s + 8*g4 + j; int4 pools: channels (D/4)*g4 + 8s + j (so that a
+    // lane's steps cover one contiguous run of codes of its key row), stored
+    // in the order j = 0 2 4 6 1 3 5 7 of the unpacked codes.
     bf16x8 qb[NS];
     float qsum = 0.f;                      // int4: sum over channels of q_h
     {
@@ -465,6 +468,7 @@ __global__ __launch_bounds__(kDecodeWaves * kWave, decode_waves_per_simd(KVT, NP
             if constexpr (I4) {
 #pragma unroll
                 for (int e = 0; e < 4; ++e) qsum += bf16_lo(pick(raw, e)) + bf16_hi(pick(raw, e));
+                raw = split_order(raw.x, raw.y, raw.z, raw.w);     // the order of the unpacked codes
             }
             qb[s] = __builtin_bit_cast(bf16x8, raw);
         }
@@ -538,6 +542,19 @@ __global__ __launch_bounds__(kDecodeWaves * kWave, decode_waves_per_simd(KVT, NP
         }
         need[i] = need_t[i][0] | need_t[i][1];
         any |= need[i];
+    }
+    // blocks whose 32 tokens are all attended and read from memory: their
+    // scores and values need no masking (wavefront-uniform)
+    bool full[NBW];
+#pragma unroll
+    for (int i = 0; i < NBW; ++i) {
+        bool f = need_t[i][0] & need_t[i][1];
+#pragma unroll
+        for (int T = 0; T < 2; ++T) {
+            const int p0 = tok_t[i][T], p1 = p0 + 15;
+            f &= (p1 <= w.t_pool) & (!w.streaming | (p1 < a.sink) | (w.t - p0 < a.local));
+        }
+        full[i] = f;
     }
 
     floatx4 o[NDT];
@@ -666,8 +683,8 @@ __global__ __launch_bounds__(kDecodeWaves * kWave, decode_waves_per_simd(KVT, NP
                 bf16x8 k0, k1;
                 if constexpr (I4) {
                     const uint32_t w0 = pick(kr[e][0][0], s), w1 = pick(kr[e][1][0], s);
-                    k0 = __builtin_bit_cast(bf16x8, nibbles_bf16x8(w0));
-                    k1 = __builtin_bit_cast(bf16x8, nibbles_bf16x8(w1));
+                    k0 = __builtin_bit_cast(bf16x8, nibbles_bf16x8_split(w0));
+                    k1 = __builtin_bit_cast(bf16x8, nibbles_bf16x8_split(w1));
                 } else {
                     k0 = __builtin_bit_cast(bf16x8, kr[e][0][s]);
                     k1 = __builtin_bit_cast(bf16x8, kr[e][1][s]);
@@ -687,14 +704,17 @@ __global__ __launch_bounds__(kDecodeWaves * kWave, decode_waves_per_simd(KVT, NP
 #pragma unroll
                 for (int r = 0; r < 4; ++r) { x[r] = s0[r] * a.scale_log2; x[4 + r] = s1[r] * a.scale_log2; }
             }
+            if (!full[i]) {                     // (wavefront-uniform branch)
+#pragma unroll
+                for (int jj = 0; jj < 8; ++jj) {
+                    const int T = jj >> 2;
+                    const bool vis = need_t[i][T] & token_visible(a, w, tok_t[i][T] + 4 * g4 + (jj & 3));
+                    x[jj] = vis ? x[jj] : -__builtin_inff();
+                }
+            }
             float mb = -__builtin_inff();
 #pragma unroll
-            for (int jj = 0; jj < 8; ++jj) {
-                const int T = jj >> 2;
-                const bool vis = need_t[i][T] & token_visible(a, w, tok_t[i][T] + 4 * g4 + (jj & 3));
-                x[jj] = vis ? x[jj] : -__builtin_inff();        // a select, not a branch
-                mb = fmaxf(mb, x[jj]);
-            }
+            for (int jj = 0; jj < 8; ++jj) mb = fmaxf(mb, x[jj]);
             mb = max_xor32(max_xor16(mb));
             const float m_new = fmaxf(m_run, mb);
             // reference of the exponentials: any finite value while nothing is visible yet
@@ -707,17 +727,16 @@ __global__ __launch_bounds__(kDecodeWaves * kWave, decode_waves_per_simd(KVT, NP
                 const float pa = exp2_fast(x[jj] - m_ref);
                 const float pb = exp2_fast(x[jj + 1] - m_ref);
                 psum += pa + pb;
-                uint16_t ba, bb;
+                // v_cvt_pk_bf16_f32: round to nearest even
+                uint32_t u;
                 if constexpr (I4) {
                     const float svt = sv[jt[jj >> 2]];
-                    ba = f32_to_bf16_rne(pa * svt);
-                    bb = f32_to_bf16_rne(pb * svt);
-                    fed[jj >> 2] += bf16_to_f32(ba) + bf16_to_f32(bb);
+                    u = __builtin_bit_cast(uint32_t, __builtin_convertvector(floatx2{pa * svt, pb * svt}, bf16x2));
+                    fed[jj >> 2] += bf16_lo(u) + bf16_hi(u);
                 } else {
-                    ba = f32_to_bf16_rne(pa);
-                    bb = f32_to_bf16_rne(pb);
+                    u = __builtin_bit_cast(uint32_t, __builtin_convertvector(floatx2{pa, pb}, bf16x2));
                 }
-                pk[jj / 2] = uint32_t(ba) | (uint32_t(bb) << 16);
+                pk[jj / 2] = u;
             }
             l_run = l_run * alpha + psum;
             if constexpr (I4) corr = corr * alpha + (128.f + zv[jt[0]]) * fed[0] + (128.f + zv[jt[1]]) * fed[1];
@@ -735,32 +754,42 @@ __global__ __launch_bounds__(kDecodeWaves * kWave, decode_waves_per_simd(KVT, NP
                 pv[d] = r16[0];
                 pv[2 + d] = r16[1];
             }
-            const bf16x8 pbv = __builtin_bit_cast(bf16x8, make_uint4(pv[0], pv[1], pv[2], pv[3]));
-            // slots after the current token may hold any bits: zero their values so a
-            // zero probability never meets a NaN in the PV product
-            const bool tail = !(need_t[i][0] & need_t[i][1]) || max(tok_t[i][0], tok_t[i][1]) + 15 > w.t_pool;
-            const int vt = HALF ? g4 >> 1 : 0;       // the tile whose tokens this lane's value rows hold
-            const int nvalid = need_t[i][vt] ? w.t_pool - (tok_t[i][vt] + (HALF ? 8 * (g4 & 1) : 8 * g4)) + 1 : 0;
+            // int4: the unpacked values come in the token order 0 2 4 6 1 3 5 7
+            const bf16x8 pbv = __builtin_bit_cast(bf16x8, I4 ? split_order(pv[0], pv[1], pv[2], pv[3])
+                                                             : make_uint4(pv[0], pv[1], pv[2], pv[3]));
+            // bf16 value slots after the current token may hold any bits: zero them
+            // so a zero probability never meets a NaN in the PV product (int4 codes
+            // always unpack to finite values)
             uint32_t keep[4] = {~0u, ~0u, ~0u, ~0u};
-            if (tail) {
+            bool tail = false;
+            if constexpr (!I4) {
+                if (!full[i]) {                 // (wavefront-uniform branch)
+                    tail = !(need_t[i][0] & need_t[i][1]) || max(tok_t[i][0], tok_t[i][1]) + 15 > w.t_pool;
+                    const int vt = HALF ? g4 >> 1 : 0;   // the tile whose tokens this lane's value rows hold
+                    const int nvalid =
+                        need_t[i][vt] ? w.t_pool - (tok_t[i][vt] + (HALF ? 8 * (g4 & 1) : 8 * g4)) + 1 : 0;
 #pragma unroll
-                for (int q2 = 0; q2 < 4; ++q2)
-                    keep[q2] = (2 * q2 < nvalid ? 0x0000FFFFu : 0u) | (2 * q2 + 1 < nvalid ? 0xFFFF0000u : 0u);
+                    for (int q2 = 0; q2 < 4; ++q2)
+                        keep[q2] = (2 * q2 < nvalid ? 0x0000FFFFu : 0u) | (2 * q2 + 1 < nvalid ? 0xFFFF0000u : 0u);
+                }
+            }
+            // rescale the accumulators only when some head's running maximum moved
+            if (__ballot(alpha != 1.f)) {
+#pragma unroll
+                for (int dt = 0; dt < NDT; ++dt) o[dt] *= alpha;
             }
 #pragma unroll
             for (int dt = 0; dt < NDT; ++dt) {
                 uint4 va;
                 if constexpr (I4) {
                     // 4 bytes = tokens 8*g4 .. 8*g4+7 of channel 16*dt + h
-                    const uint32_t wv4 = vr4[e][dt];
-                    va = nibbles_bf16x8(wv4);
+                    va = nibbles_bf16x8_split(vr4[e][dt]);
                 } else {
                     va = vr[e][dt];
+                    if (tail) {
+                        va.x &= keep[0]; va.y &= keep[1]; va.z &= keep[2]; va.w &= keep[3];
+                    }
                 }
-                if (tail) {
-                    va.x &= keep[0]; va.y &= keep[1]; va.z &= keep[2]; va.w &= keep[3];
-                }
-                o[dt] *= alpha;
                 o[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, va), pbv, o[dt], 0, 0, 0);
             }
         };
@@ -807,7 +836,7 @@ __global__ __launch_bounds__(kDecodeWaves * kWave, decode_waves_per_simd(KVT, NP
                 const uint32_t qw[4] = {qraw.x, qraw.y, qraw.z, qraw.w};
 #pragma unroll
                 for (int j = 0; j < 8; ++j) {
-                    const int c = 8 * s + j;                       // code c of the lane's run
+                    const int c = 8 * s + (j < 4 ? 2 * j : 2 * j - 7);   // code c of the lane's run (qb order)
                     const float kj = (float)((kw[c / 8] >> (4 * (c % 8))) & 15u) - zk_n;
                     dot = fmaf((j & 1) ? bf16_hi(qw[j / 2]) : bf16_lo(qw[j / 2]), kj, dot);
                 }
