@@ -760,17 +760,22 @@ __global__ __launch_bounds__(kDecodeWaves * kWave, decode_waves_per_simd(KVT, NP
             // bf16 value slots after the current token may hold any bits: zero them
             // so a zero probability never meets a NaN in the PV product (int4 codes
             // always unpack to finite values)
-            uint32_t keep[4] = {~0u, ~0u, ~0u, ~0u};
-            bool tail = false;
             if constexpr (!I4) {
-                if (!full[i]) {                 // (wavefront-uniform branch)
-                    tail = !(need_t[i][0] & need_t[i][1]) || max(tok_t[i][0], tok_t[i][1]) + 15 > w.t_pool;
+                const bool tail =
+                    !full[i] && (!(need_t[i][0] & need_t[i][1]) || max(tok_t[i][0], tok_t[i][1]) + 15 > w.t_pool);
+                if (tail) {                     // (wavefront-uniform branch: masks the ring slot in place)
                     const int vt = HALF ? g4 >> 1 : 0;   // the tile whose tokens this lane's value rows hold
                     const int nvalid =
                         need_t[i][vt] ? w.t_pool - (tok_t[i][vt] + (HALF ? 8 * (g4 & 1) : 8 * g4)) + 1 : 0;
+                    uint32_t keep[4];
 #pragma unroll
                     for (int q2 = 0; q2 < 4; ++q2)
                         keep[q2] = (2 * q2 < nvalid ? 0x0000FFFFu : 0u) | (2 * q2 + 1 < nvalid ? 0xFFFF0000u : 0u);
+#pragma unroll
+                    for (int dt = 0; dt < NDT; ++dt) {
+                        vr[e][dt].x &= keep[0]; vr[e][dt].y &= keep[1];
+                        vr[e][dt].z &= keep[2]; vr[e][dt].w &= keep[3];
+                    }
                 }
             }
             // rescale the accumulators only when some head's running maximum moved
@@ -786,9 +791,6 @@ __global__ __launch_bounds__(kDecodeWaves * kWave, decode_waves_per_simd(KVT, NP
                     va = nibbles_bf16x8_split(vr4[e][dt]);
                 } else {
                     va = vr[e][dt];
-                    if (tail) {
-                        va.x &= keep[0]; va.y &= keep[1]; va.z &= keep[2]; va.w &= keep[3];
-                    }
                 }
                 o[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, va), pbv, o[dt], 0, 0, 0);
             }
