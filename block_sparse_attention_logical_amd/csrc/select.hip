@@ -36,6 +36,24 @@
 namespace lsa {
 namespace {
 
+typedef int int32x4 __attribute__((ext_vector_type(4)));
+
+// sum of v over the lanes l, l ^ 16, l ^ 32, l ^ 48 (the four k-groups of a
+// 16 x 16 MFMA tile column), in every lane
+__device__ __forceinline__ double sum_kgroups_d(double v) {
+    uint32_t l0, l1, h0, h1;
+    unsigned long long u = __double_as_longlong(v);
+    pair16((uint32_t)u, l0, l1);
+    pair16((uint32_t)(u >> 32), h0, h1);
+    v = __longlong_as_double((long long)(((unsigned long long)h0 << 32) | l0)) +
+        __longlong_as_double((long long)(((unsigned long long)h1 << 32) | l1));
+    u = __double_as_longlong(v);
+    pair32((uint32_t)u, l0, l1);
+    pair32((uint32_t)(u >> 32), h0, h1);
+    return __longlong_as_double((long long)(((unsigned long long)h0 << 32) | l0)) +
+           __longlong_as_double((long long)(((unsigned long long)h1 << 32) | l1));
+}
+
 template <int EB, int D>
 struct ScoreShape {
     static constexpr int C = 16 / EB;        // channels per lane (one 16-byte load)
@@ -567,18 +585,20 @@ __global__ __launch_bounds__(kScoreThreads) void score_kernel(ScoreArgs a) {
 // 256K tokens).
 // ---------------------------------------------------------------------------
 template <int KV_DT>
-__host__ __device__ constexpr int score_ring() { return KV_DT == LSA_INT4 ? 8 : 2; }
+__host__ __device__ constexpr int score_ring() { return KV_DT == LSA_INT4 ? 4 : 2; }
 constexpr int kMaxRing = 8;
+constexpr int kScoreTiles = 4;            // int4 MFMA scoring: 16-page tiles in flight per wavefront
 constexpr int kMaxRangePages = 1024;      // physical pages per workgroup (pool ids in LDS)
 constexpr int kMaxRangeLogical = 2048;    // logical pages per workgroup (scores in LDS)
 
 template <int KV_DT, int D, int FPT>
-__global__ __launch_bounds__(kScoreThreads) void score_loop_kernel(ScoreArgs a) {
+__global__ __launch_bounds__(kScoreThreads, 3) void score_loop_kernel(ScoreArgs a) {
     constexpr int EB = KV_DT == LSA_F32 ? 4 : (KV_DT == LSA_BF16 ? 2 : 1);
     using S = ScoreShape<EB, D>;
     constexpr int C = S::C, LPL = S::LPL, LPP = S::LPP;
     constexpr int GROUPS = (kScoreThreads / kWave) * LPP;   // lane groups per workgroup
-    __shared__ double s_log[kMaxRangeLogical];
+    // logical scores, then one slot per lane that stores a score no page keeps
+    __shared__ double s_log[kMaxRangeLogical + kWave];
     __shared__ unsigned long long s_hp[kMaxRangePages];   // (pool page, head) unit of each page of the range
 
     const int blk = blockIdx.x % a.blocks_per_head;
@@ -587,7 +607,7 @@ __global__ __launch_bounds__(kScoreThreads) void score_loop_kernel(ScoreArgs a) 
     const int b = rest / a.n_ret;
     const int kv = retrieval_head(a.hm, r);
     const int lane = threadIdx.x % kWave;
-    const int wave = threadIdx.x / kWave;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);   // (a scalar: uniform loops)
     const int lg = wave * LPP + lane / LPL;       // lane group in the workgroup
     const int ch0 = (lane % LPL) * C;
 
@@ -612,15 +632,85 @@ __global__ __launch_bounds__(kScoreThreads) void score_loop_kernel(ScoreArgs a) 
 
     for (int i = threadIdx.x; i < m1 - m0; i += kScoreThreads)
         s_hp[i] = (unsigned long long)a.page_table[(size_t)b * a.max_pages + m0 + i] * a.hm.pool_heads + slot_kv;
-    double qp[C], qn[C];
-    load_q_pos_neg<C>(a, b, kv, ch0, 0, G, qp, qn);
+    double qp[C], qn[C];                          // Qp, Qn of this lane's channels ch0 ..
     double qsum = 0.0;                            // int4 only: sum over all channels of Qp + Qn
-    if constexpr (KV_DT == LSA_INT4) {
+    // int4: whether every Qp and -Qn term is an integer below 2^32 on the grid
+    // 2^lo (bf16 queries of ordinary range span about 21 bits); s_qint then
+    // holds those integers (Qp of channel c at c, -Qn at D + c)
+    bool on_grid = false;
+    int lo = 0;
+    __shared__ uint32_t s_qint[2 * 128];
+    if constexpr (KV_DT != LSA_INT4) {
+        load_q_pos_neg<C>(a, b, kv, ch0, 0, G, qp, qn);
+        __syncthreads();
+    } else {
+        // thread t forms one term once for the workgroup: side t / D (0: Qp,
+        // 1: -Qn) of channel t % D, with the exponents of its lowest and its
+        // leading set bit
+        __shared__ int s_lh[2][kScoreThreads / kWave];
+        __shared__ double s_qs[kScoreThreads / kWave];
+        double v = 0.0;
+        if (threadIdx.x < 2 * D) {
+            const int side = threadIdx.x / D, c = threadIdx.x % D;
+            for (int h = 0; h < G; ++h) {
+                const size_t i = ((size_t)b * a.num_q_heads + (size_t)kv * G + h) * D + c;
+                const double x = a.q_dtype == LSA_BF16 ? (double)bf16_to_f32(static_cast<const uint16_t *>(a.q)[i])
+                                                      : (double)static_cast<const float *>(a.q)[i];
+                v += side ? fmax(-x, 0.0) : fmax(x, 0.0);
+            }
+        }
+        int lo_t = 0x7FFFFFFF, hi_t = -0x7FFFFFFF;
+        if (v != 0.0) {
+            const unsigned long long u = (unsigned long long)__double_as_longlong(v);
+            const int ex = int((u >> 52) & 0x7FFu);
+            const unsigned long long m = (u & 0xFFFFFFFFFFFFFull) | (1ull << 52);
+            lo_t = ex - 1075 + __builtin_ctzll(m);        // exponent of the lowest set bit
+            hi_t = ex - 1023;                             // exponent of the leading bit
+        }
+        lo_t = group_minmax_i<16, false>(lo_t);
+        hi_t = group_minmax_i<16, true>(hi_t);
+        {
+            uint32_t x0, x1;
+            pair16((uint32_t)lo_t, x0, x1); lo_t = min((int)x0, (int)x1);
+            pair32((uint32_t)lo_t, x0, x1); lo_t = min((int)x0, (int)x1);
+            pair16((uint32_t)hi_t, x0, x1); hi_t = max((int)x0, (int)x1);
+            pair32((uint32_t)hi_t, x0, x1); hi_t = max((int)x0, (int)x1);
+        }
+        // the terms' sum over both sides: Qp + Qn = Qp - (-Qn); exact when on_grid
+        double vs = group_sum_d<32>(threadIdx.x / D ? -v : v);
+        {
+            const unsigned long long u = __double_as_longlong(vs);
+            uint32_t l0, l1, h0, h1;
+            pair32((uint32_t)u, l0, l1);
+            pair32((uint32_t)(u >> 32), h0, h1);
+            vs = __longlong_as_double((long long)(((unsigned long long)h0 << 32) | l0)) +
+                 __longlong_as_double((long long)(((unsigned long long)h1 << 32) | l1));
+        }
+        if (lane == 0) { s_lh[0][wave] = lo_t; s_lh[1][wave] = hi_t; s_qs[wave] = vs; }
+        __syncthreads();
+        lo = s_lh[0][0];
+        int hi = s_lh[1][0];
+        double qs = s_qs[0];
 #pragma unroll
-        for (int c = 0; c < C; ++c) qsum += qp[c] + qn[c];
-        qsum = group_sum_d<LPL>(qsum);
+        for (int w2 = 1; w2 < kScoreThreads / kWave; ++w2) {
+            lo = min(lo, s_lh[0][w2]);
+            hi = max(hi, s_lh[1][w2]);
+            qs += s_qs[w2];
+        }
+        if (lo > hi) lo = hi = 0;                 // every term is zero
+        on_grid = hi - lo < 32;
+        if (on_grid) {
+            qsum = qs;
+            if (threadIdx.x < 2 * D) s_qint[threadIdx.x] = (uint32_t)ldexp(v, -lo);
+        } else {
+            // (rare) the fp64 path: this lane's channels, the sum in their order
+            load_q_pos_neg<C>(a, b, kv, ch0, 0, G, qp, qn);
+#pragma unroll
+            for (int c = 0; c < C; ++c) qsum += qp[c] + qn[c];
+            qsum = group_sum_d<LPL>(qsum);
+        }
+        __syncthreads();
     }
-    __syncthreads();
 
     // int4: S = s * (sum_i Qp c_max + Qn c_min - z * sum_i (Qp + Qn))
     auto finish = [&](double dot, uint32_t sz) {
@@ -632,6 +722,8 @@ __global__ __launch_bounds__(kScoreThreads) void score_loop_kernel(ScoreArgs a) 
     // the current logical page, from its keys, by the wavefront whose lane
     // groups would hold it
     if (j_cur >= j0 && j_cur < j1 && wave == ((j_cur - j0) % GROUPS) / LPP) {
+        if constexpr (KV_DT == LSA_INT4)
+            if (on_grid) load_q_pos_neg<C>(a, b, kv, ch0, 0, G, qp, qn);
         float cmin[C], cmax[C];
         const size_t hp = s_hp[(j_cur >> gs) - m0];
         uint32_t sz_cur = 0;
@@ -669,6 +761,9 @@ __global__ __launch_bounds__(kScoreThreads) void score_loop_kernel(ScoreArgs a) 
         rl[s] = load_stream16(st);
         if constexpr (KV_DT == LSA_INT4) rs[s] = load_stream4(a.k_sz + hp * 2);
         else rh[s] = load_stream16(st + D * EB);
+        // issue the slot's loads here, in ring order: the wait before a slot then
+        // counts exactly the loads of the slots after it
+        __builtin_amdgcn_sched_barrier(0);
     };
     // the score of the logical page in ring slot s, from fp64 products
     auto fp_slot = [&](int s) __attribute__((always_inline)) -> double {
@@ -716,73 +811,103 @@ __global__ __launch_bounds__(kScoreThreads) void score_loop_kernel(ScoreArgs a) 
                 const int k = k0 + s;
                 const double sj = slot_score(s);
                 const int j = j0 + lg + k * GROUPS;
-                if (k < K_w && j < j1 && j != j_cur && lane % LPL == 0) s_log[j - j0] = sj;
+                // (no branch: the loads in flight stay countable across iterations)
+                s_log[k < K_w && j < j1 && j != j_cur && lane % LPL == 0 ? j - j0 : kMaxRangeLogical + lane] = sj;
                 issue(s, k + kRing);              // (past the range: a discarded reload)
             }
         }
     };
     if constexpr (KV_DT == LSA_INT4) {
-        // int4: Qp and -Qn as exact integers on the grid 2^lo when every term is
-        // below 2^32 grid steps (bf16 queries of ordinary range span about 21
-        // bits).  A page's sum then takes byte-digit dot products of the codes
-        // (v_dot4_u32_u8) instead of a conversion and an fp64 product per code.
-        // Every partial sum is an integer below 2^43 grid steps, so it is exact,
-        // and so is the fp64 sum of the other path: both give the same double.
-        int lo = 0x7FFFFFFF, hi = -0x7FFFFFFF;
+        if (on_grid) {
+            // Exact integer scoring on the matrix cores.  Qp and -Qn are integers
+            // below 2^32 on the grid 2^lo; their 7-bit digits (v_mfma_i32_16x16x64_i8
+            // takes signed bytes) are the rows of A: rows 0..4 the digits of Qp,
+            // rows 8..12 those of -Qn, the other rows zero.  B holds the codes of 16
+            // logical pages (its columns): c_max against the A that carries the Qp
+            // digits, c_min against the one that carries the -Qn digits, two MFMAs
+            // per 64 channels accumulating into one 16 x 16 tile.  Element (r, n) is
+            // sum_i digit_r(i) code_i(n) < 2^18; weighted by +-128^d(r) and summed
+            // over the rows it is sum_i Qp c_max + Qn c_min of page n in grid steps,
+            // an integer below 2^46, so exact in fp64 like every partial sum: the
+            // same double as the fp64 path.
+            // A lane (row / column lane % 16, k-group kg = lane / 16) supplies the
+            // channels 64 hf + 16 kg + e, e = 0..15, of MFMA half hf in A and in B.
+            constexpr int NH = D / 64;
+            const int rc = lane & 15, kg = lane >> 4;
+            int32x4 amax[NH], amin[NH];
+            {
+                const bool prow = rc < 5, nrow = rc >= 8 && rc < 13;
+                const int sh = prow ? 7 * rc : nrow ? 7 * (rc - 8) : 0;
+                const uint32_t *src = s_qint + (prow ? 0 : D);
 #pragma unroll
-        for (int c = 0; c < C; ++c)
+                for (int hf = 0; hf < NH; ++hf) {
+                    uint32_t wp[4] = {0u, 0u, 0u, 0u}, wn[4] = {0u, 0u, 0u, 0u};
 #pragma unroll
-            for (int side = 0; side < 2; ++side) {
-                const double x = side ? -qn[c] : qp[c];
-                if (x != 0.0) {
-                    const unsigned long long u = (unsigned long long)__double_as_longlong(x);
-                    const int ex = int((u >> 52) & 0x7FFu);
-                    const unsigned long long m = (u & 0xFFFFFFFFFFFFFull) | (1ull << 52);
-                    lo = min(lo, ex - 1075 + __builtin_ctzll(m));     // exponent of the lowest set bit
-                    hi = max(hi, ex - 1023);                          // exponent of the leading bit
+                    for (int e = 0; e < 16; ++e) {
+                        const uint32_t dg = (src[64 * hf + 16 * kg + e] >> sh) & 127u;
+                        wp[e / 4] |= (prow ? dg : 0u) << (8 * (e % 4));
+                        wn[e / 4] |= (nrow ? dg : 0u) << (8 * (e % 4));
+                    }
+                    amax[hf] = int32x4{(int)wp[0], (int)wp[1], (int)wp[2], (int)wp[3]};
+                    amin[hf] = int32x4{(int)wn[0], (int)wn[1], (int)wn[2], (int)wn[3]};
                 }
             }
-        // every lane group holds every channel: the same bounds in every lane
-        lo = __builtin_amdgcn_readfirstlane(group_minmax_i<LPL, false>(lo));
-        hi = __builtin_amdgcn_readfirstlane(group_minmax_i<LPL, true>(hi));
-        if (lo > hi) lo = hi = 0;                 // every term is zero
-        if (hi - lo < 32) {
-            // byte digits d of the integers, four channels per register
-            uint32_t dgp[C / 4][4], dgn[C / 4][4];
+            // weight of the tile rows this lane holds (rows 4 kg .. 4 kg + 3)
+            double wgt[4];
 #pragma unroll
-            for (int q4 = 0; q4 < C / 4; ++q4)
-#pragma unroll
-                for (int d = 0; d < 4; ++d) { dgp[q4][d] = 0; dgn[q4][d] = 0; }
-#pragma unroll
-            for (int c = 0; c < C; ++c) {
-                const uint32_t ip = (uint32_t)ldexp(qp[c], -lo), in = (uint32_t)ldexp(-qn[c], -lo);
-#pragma unroll
-                for (int d = 0; d < 4; ++d) {
-                    dgp[c / 4][d] |= ((ip >> (8 * d)) & 0xFFu) << (8 * (c % 4));
-                    dgn[c / 4][d] |= ((in >> (8 * d)) & 0xFFu) << (8 * (c % 4));
-                }
+            for (int e = 0; e < 4; ++e) {
+                const int rr = 4 * kg + e;
+                const int d = rr < 5 ? rr : (rr >= 8 && rr < 13 ? rr - 8 : -1);
+                wgt[e] = d < 0 ? 0.0 : ldexp(rr < 8 ? 1.0 : -1.0, 7 * d);
             }
             const double grid = ldexp(1.0, lo);
-            // (the fp64 terms die here: keep the ring's first loads below this point)
+            // (the fp64 terms die here: keep the first loads below this point)
             __builtin_amdgcn_sched_barrier(0);
-            // sum_c Qp c_max + Qn c_min = grid * sum_d 256^d (digit_d(Qp) . c_max - digit_d(-Qn) . c_min)
-            ring([&](int s) __attribute__((always_inline)) -> double {
-                const uint32_t wd[4] = {rl[s].x, rl[s].y, rl[s].z, rl[s].w};
-                uint32_t ap[4] = {0u, 0u, 0u, 0u}, an[4] = {0u, 0u, 0u, 0u};
+
+            // tiles of 16 logical pages: wavefront w takes tiles w, w + 4, ...,
+            // kScoreTiles of them in flight
+            constexpr int RT = kScoreTiles;
+            const int n_tiles = (j1 - j0 + 15) / 16;
+            const int T_w = max(0, (n_tiles - wave + 3) / 4);
+            uint4 tb[RT][NH];
+            uint32_t tsz[RT];
+            auto tissue = [&](int s, int k) __attribute__((always_inline)) {
+                int j = j0 + 16 * (wave + 4 * k) + rc;
+                if (j >= j1) j = j0;              // past the range: any page of it, discarded
+                const unsigned long long hp = s_hp[(j >> gs) - m0];
+                const char *st = static_cast<const char *>(a.stats) + (hp << unit_shift) +
+                                 ((j & (g - 1)) << row_shift) + 16 * kg;
 #pragma unroll
-                for (int q4 = 0; q4 < C / 4; ++q4) {
-                    const uint32_t cmax = (wd[q4] >> 4) & 0x0F0F0F0Fu, cmin = wd[q4] & 0x0F0F0F0Fu;
+                for (int hf = 0; hf < NH; ++hf) tb[s][hf] = load_stream16(st + 64 * hf);
+                tsz[s] = load_stream4(a.k_sz + hp * 2);
+                __builtin_amdgcn_sched_barrier(0);   // (in ring order, as above)
+            };
 #pragma unroll
-                    for (int d = 0; d < 4; ++d) {
-                        ap[d] = __builtin_amdgcn_udot4(cmax, dgp[q4][d], ap[d], false);
-                        an[d] = __builtin_amdgcn_udot4(cmin, dgn[q4][d], an[d], false);
+            for (int s = 0; s < RT; ++s) tissue(s, s);
+            for (int k0 = 0; k0 < T_w; k0 += RT) {
+#pragma unroll
+                for (int s = 0; s < RT; ++s) {
+                    const int k = k0 + s;
+                    int32x4 acc = {0, 0, 0, 0};
+#pragma unroll
+                    for (int hf = 0; hf < NH; ++hf) {
+                        const uint4 w = tb[s][hf];
+                        const int32x4 cmax = {(int)((w.x >> 4) & 0x0F0F0F0Fu), (int)((w.y >> 4) & 0x0F0F0F0Fu),
+                                              (int)((w.z >> 4) & 0x0F0F0F0Fu), (int)((w.w >> 4) & 0x0F0F0F0Fu)};
+                        const int32x4 cmin = {(int)(w.x & 0x0F0F0F0Fu), (int)(w.y & 0x0F0F0F0Fu),
+                                              (int)(w.z & 0x0F0F0F0Fu), (int)(w.w & 0x0F0F0F0Fu)};
+                        acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(amax[hf], cmax, acc, 0, 0, 0);
+                        acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(amin[hf], cmin, acc, 0, 0, 0);
                     }
+                    double part = wgt[0] * (double)acc[0];
+#pragma unroll
+                    for (int e = 1; e < 4; ++e) part = fma(wgt[e], (double)acc[e], part);
+                    const double sj = finish(sum_kgroups_d(part) * grid, tsz[s]);
+                    const int j = j0 + 16 * (wave + 4 * k) + rc;
+                    s_log[k < T_w && kg == 0 && j < j1 && j != j_cur ? j - j0 : kMaxRangeLogical + lane] = sj;
+                    tissue(s, k + RT);            // (past the range: a discarded reload)
                 }
-                // each ap / an < 16 * 15 * 255: the two halves fit int32, the sum 2^40
-                const int lo_i = int(ap[0] + (ap[1] << 8)) - int(an[0] + (an[1] << 8));
-                const int hi_i = int(ap[2] + (ap[3] << 8)) - int(an[2] + (an[3] << 8));
-                return finish(group_sum_d<LPL>(fma((double)hi_i, 65536.0, (double)lo_i)) * grid, rs[s]);
-            });
+            }
         } else {
             ring(fp_slot);                        // terms too wide for one 32-bit grid (rare)
         }
