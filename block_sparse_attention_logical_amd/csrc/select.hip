@@ -19,13 +19,12 @@
 // is scored from the keys themselves.  Logical scores go to LDS and one
 // thread per physical page takes their max.
 //
-// Top-K.  Scores are mapped to order-preserving 64-bit keys held in
-// registers; a most significant digit first radix select finds the K-th
-// largest key.  The passes start at the highest bit in which the keys differ
-// (the bits above it are common to all keys) and take the next 8 bits each;
-// the histogram is in LDS, double-buffered so a pass needs two barriers.
-// Equal keys are taken in ascending page order (ties to the lower page
-// index); an ordered compaction writes the selected pages in ascending order.
+// Top-K.  The scores stay in registers; the K-th largest is found by value
+// (linear bins between the smallest and largest score still in question,
+// then one wavefront ranking the few scores that share the bin of the K-th;
+// see topk_rows).  Equal scores are taken in ascending page order (ties to
+// the lower page index); an ordered compaction writes the selected pages in
+// ascending order.
 // Up to 4096 pages per sequence the ranking runs inside the score kernel: the
 // last score workgroup of a (sequence, head) to finish, counted with an
 // arrival counter, ranks that head; above that a separate top-K kernel does.
@@ -209,12 +208,6 @@ __device__ __forceinline__ void current_page_minmax(const ScoreArgs &a, size_t p
 constexpr int kTopkThreads = 1024;
 constexpr int kTopkPerThread = 16;        // pages per thread at most: up to 16384 pages
 
-__device__ __forceinline__ unsigned long long order_key(double x) {
-    x = x + 0.0;                                  // -0 -> +0
-    const unsigned long long u = __double_as_longlong(x);
-    return (u >> 63) ? ~u : (u | 0x8000000000000000ull);
-}
-
 __device__ __forceinline__ void store_agent_d(double *p, double v) {
     __hip_atomic_store(reinterpret_cast<unsigned long long *>(p), (unsigned long long)__double_as_longlong(v),
                        __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -236,22 +229,61 @@ __device__ __forceinline__ uint32_t block_exclusive_scan(uint32_t v, uint32_t *w
     return incl - v + add;
 }
 
+// min and max of doubles over the wavefront (every lane gets both)
+__device__ __forceinline__ void wave_minmax_d(double &lo, double &hi) {
+    lo = fmin(lo, dpp_d<kDppQuadSwap1>(lo)); hi = fmax(hi, dpp_d<kDppQuadSwap1>(hi));
+    lo = fmin(lo, dpp_d<kDppQuadSwap2>(lo)); hi = fmax(hi, dpp_d<kDppQuadSwap2>(hi));
+    lo = fmin(lo, dpp_d<kDppHalfMirror>(lo)); hi = fmax(hi, dpp_d<kDppHalfMirror>(hi));
+    lo = fmin(lo, dpp_d<kDppMirror>(lo)); hi = fmax(hi, dpp_d<kDppMirror>(hi));
+    auto both = [](double v, bool x32, double &p, double &q) {
+        const unsigned long long u = __double_as_longlong(v);
+        uint32_t l0, l1, h0, h1;
+        if (x32) { pair32((uint32_t)u, l0, l1); pair32((uint32_t)(u >> 32), h0, h1); }
+        else { pair16((uint32_t)u, l0, l1); pair16((uint32_t)(u >> 32), h0, h1); }
+        p = __longlong_as_double((long long)(((unsigned long long)h0 << 32) | l0));
+        q = __longlong_as_double((long long)(((unsigned long long)h1 << 32) | l1));
+    };
+    double p, q;
+    both(lo, false, p, q); lo = fmin(p, q);
+    both(hi, false, p, q); hi = fmax(p, q);
+    both(lo, true, p, q); lo = fmin(p, q);
+    both(hi, true, p, q); hi = fmax(p, q);
+}
+
 // The K largest of the n = ceil(L / N_P) scores P[0..n) into out, ascending by
 // page, ties to the lower page, -1 padded; NT threads, PT pages per thread
 // (NT * PT >= max_pages).  AGENT: P was written by other workgroups of this
 // launch and is read with agent-scope loads.
+//
+// The threshold T, the K-th largest score, is found by value: the scores
+// still in question are binned linearly between their minimum and maximum
+// (a monotone map, so a bin holds a contiguous range of values and equal
+// scores share a bin), the bin that holds the K-th largest is found from the
+// histogram, and the scores outside it are settled.  When at most
+// kTopkCand scores share that bin, one wavefront ranks them against each
+// other and T is exact; otherwise the bin is binned again.  Linear bins
+// spread a smooth distribution of scores over the histogram, so few threads
+// meet on one counter.  Pages with scores above T are taken, and of the
+// pages scoring exactly T the lowest ones, K in all, in one ordered
+// compaction.
+constexpr int kTopkBins = 1024;
+constexpr int kTopkCand = 16;
+
 template <int NT, int PT, bool AGENT>
 __device__ __forceinline__ void topk_rows(const double *P, int L, int page_size, int max_pages, int K,
                                           int32_t *out) {
-    __shared__ uint32_t hist[2][256];
-    __shared__ uint32_t sh_digit, sh_above, sh_done;
-    __shared__ uint32_t wave_tot[NT / kWave];
-    __shared__ unsigned long long sh_and[NT / kWave], sh_or[NT / kWave];
-    const int tid = threadIdx.x;
+    static_assert(PT <= 32, "pages per thread");
+    constexpr int NW = NT / kWave;
+    __shared__ uint32_t hist[kTopkBins];
+    __shared__ double sh_lo[NW], sh_hi[NW];
+    __shared__ double cand[kTopkCand];
+    __shared__ uint32_t sh_bin, sh_above, sh_ncand, sh_gt;
+    __shared__ double sh_T;
+    __shared__ uint32_t wave_tot[NW];
+    const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
 
     // thread t owns the contiguous pages [t*seg, t*seg + cnt), seg = ceil(n /
-    // NT) <= PT; the scores of its pages are loaded together and turned into
-    // keys as they arrive
+    // NT) <= PT; their scores are loaded together
     const int n = (L + page_size - 1) / page_size;
     if (n <= K) {                                 // every page, ascending, padded with -1
         for (int i = tid; i < K; i += NT) out[i] = i < n ? i : -1;
@@ -260,88 +292,111 @@ __device__ __forceinline__ void topk_rows(const double *P, int L, int page_size,
     const int seg = (n + NT - 1) / NT;
     const int i0 = min(n, tid * seg);
     const int cnt = min(n, i0 + seg) - i0;
-    unsigned long long key[PT];
+    double sc[PT];
 #pragma unroll
     for (int e = 0; e < PT; ++e) {
         double v = 0.0;
         if (e < cnt) v = AGENT ? load_agent_d(P + i0 + e) : P[i0 + e];
-        key[e] = e < cnt ? order_key(v) : 0ull;
+        sc[e] = v + 0.0;                          // -0 -> +0
     }
-
-    // The bits above the highest one that differs between keys are shared by
-    // every key and decide nothing: the radix passes start there, each pass
-    // resolving the next (up to) 8 bits of the K-th largest key.
-    unsigned long long k_and = ~0ull, k_or = 0ull;
-#pragma unroll
-    for (int e = 0; e < PT; ++e)
-        if (e < cnt) { k_and &= key[e]; k_or |= key[e]; }
-    wave_and_or(k_and, k_or);
-    if (tid % kWave == 0) { sh_and[tid / kWave] = k_and; sh_or[tid / kWave] = k_or; }
-    for (int i = tid; i < 256; i += NT) hist[0][i] = 0;
-    __syncthreads();
-    k_and = ~0ull; k_or = 0ull;
-    for (int w2 = 0; w2 < NT / kWave; ++w2) { k_and &= sh_and[w2]; k_or |= sh_or[w2]; }
-    const unsigned long long differ = k_and ^ k_or;      // bits that are not the same in every key
-    int hi = differ ? 64 - __clzll((long long)differ) : 0;   // one past the highest differing bit
-    unsigned long long mask = hi >= 64 ? 0ull : (~0ull << hi);
-    unsigned long long prefix = k_and & mask;
-    uint32_t need = (uint32_t)K;
-    int buf = 0;
-    while (hi > 0) {
-        const int lo = max(0, hi - 8);
-        const uint32_t dmask = (1u << (hi - lo)) - 1u;
+    uint32_t act = cnt >= 32 ? ~0u : (1u << cnt) - 1u;   // pages still in question
+    uint32_t need = (uint32_t)K;                  // how many of them are taken
+    double T;
+    uint32_t need_eq;                             // pages scoring exactly T that are taken
+    for (;;) {
+        double lo = __builtin_inf(), hi = -__builtin_inf();
 #pragma unroll
         for (int e = 0; e < PT; ++e)
-            if (e < cnt && (key[e] & mask) == prefix) atomicAdd(&hist[buf][uint32_t(key[e] >> lo) & dmask], 1u);
-        for (int i = tid; i < 256; i += NT) hist[buf ^ 1][i] = 0;    // the next pass's histogram
+            if ((act >> e) & 1u) { lo = fmin(lo, sc[e]); hi = fmax(hi, sc[e]); }
+        wave_minmax_d(lo, hi);
+        if (lane == 0) { sh_lo[wave] = lo; sh_hi[wave] = hi; }
+        for (int i = tid; i < kTopkBins; i += NT) hist[i] = 0;
+        if (tid == 0) sh_ncand = 0;
         __syncthreads();
-        if (tid < kWave) {
-            // lane l owns bins 4l..4l+3; count the elements in higher bins
-            const uint32_t *hb = hist[buf];
-            const uint32_t c0 = hb[4 * tid], c1 = hb[4 * tid + 1], c2 = hb[4 * tid + 2], c3 = hb[4 * tid + 3];
-            const uint32_t mine = c0 + c1 + c2 + c3;
+        lo = sh_lo[0];
+        hi = sh_hi[0];
+#pragma unroll
+        for (int w2 = 1; w2 < NW; ++w2) { lo = fmin(lo, sh_lo[w2]); hi = fmax(hi, sh_hi[w2]); }
+        if (!(hi > lo)) { T = hi; need_eq = need; break; }     // every score in question is equal
+        const double scale = (double)kTopkBins / (hi - lo);
+        // (scale may overflow for a range of a few denormals: then lo -> 0, the rest -> last)
+        auto bin_of = [&](double x) {
+            const double f = x == lo ? 0.0 : (x - lo) * scale;
+            return f < (double)(kTopkBins - 1) ? (int)f : kTopkBins - 1;
+        };
+#pragma unroll
+        for (int e = 0; e < PT; ++e)
+            if ((act >> e) & 1u) atomicAdd(&hist[bin_of(sc[e])], 1u);
+        __syncthreads();
+        if (wave == 0) {
+            // lane l owns bins 16 l .. 16 l + 15; count the scores in higher bins
+            constexpr int BPL = kTopkBins / kWave;
+            const uint4 *hl = reinterpret_cast<const uint4 *>(hist + BPL * lane);
+            uint32_t mine = 0;
+#pragma unroll
+            for (int q = 0; q < BPL / 4; ++q) {
+                const uint4 h4 = hl[q];
+                mine += h4.x + h4.y + h4.z + h4.w;
+            }
             const uint32_t incl = wave_inclusive_scan(mine);
             const uint32_t total = (uint32_t)__builtin_amdgcn_readlane((int)incl, kWave - 1);
-            uint32_t above = total - incl;        // elements in bins of higher lanes
-            const uint32_t cs[4] = {c0, c1, c2, c3};
-            for (int qd = 3; qd >= 0; --qd) {
-                if (above < need && above + cs[qd] >= need) {
-                    sh_digit = 4 * tid + qd;
-                    sh_above = above;
-                    sh_done = above + cs[qd] == need;   // the whole bin is taken
+            uint32_t above = total - incl;        // scores in the bins of higher lanes
+            if (above < need && above + mine >= need) {   // (one lane) the bin is among mine
+#pragma unroll
+                for (int q = BPL - 1; q >= 0; --q) {
+                    const uint32_t cq = hist[BPL * lane + q];
+                    if (above < need && above + cq >= need) { sh_bin = BPL * lane + q; sh_above = above; }
+                    above += cq;
                 }
-                above += cs[qd];
             }
         }
         __syncthreads();
+        const int bstar = (int)sh_bin;
         need -= sh_above;
-        prefix |= (unsigned long long)sh_digit << lo;
-        mask |= (unsigned long long)dmask << lo;
-        hi = lo;
-        if (sh_done) break;
-        buf ^= 1;
+        const uint32_t m = hist[bstar];           // scores in the bin that holds T
+#pragma unroll
+        for (int e = 0; e < PT; ++e)
+            if (((act >> e) & 1u) && bin_of(sc[e]) != bstar) act &= ~(1u << e);
+        if (m <= (uint32_t)kTopkCand) {
+#pragma unroll
+            for (int e = 0; e < PT; ++e)
+                if ((act >> e) & 1u) cand[atomicAdd(&sh_ncand, 1u)] = sc[e];
+            __syncthreads();
+            if (wave == 0) {
+                // T is the candidate x with (greater) < need <= (greater or equal)
+                const double x = lane < (int)m ? cand[lane] : 0.0;
+                uint32_t gt = 0, ge = 0;
+                for (uint32_t j = 0; j < m; ++j) {
+                    const double y = cand[j];
+                    gt += y > x;
+                    ge += y >= x;
+                }
+                if (lane < (int)m && gt < need && need <= ge) { sh_T = x; sh_gt = gt; }
+            }
+            __syncthreads();
+            T = sh_T;
+            need_eq = need - sh_gt;
+            break;
+        }
+        __syncthreads();                          // (every thread has read hist[bstar])
     }
 
     // ordered compaction
     uint32_t c = 0;                               // low 16 bits: greater, high 16 bits: equal
 #pragma unroll
-    for (int e = 0; e < PT; ++e) {
-        if (e >= cnt) continue;
-        const unsigned long long km = key[e] & mask;
-        c += km > prefix ? 1u : (km == prefix ? 0x10000u : 0u);
-    }
+    for (int e = 0; e < PT; ++e)
+        if (e < cnt) c += sc[e] > T ? 1u : (sc[e] == T ? 0x10000u : 0u);
     const uint32_t excl = block_exclusive_scan<NT>(c, wave_tot);
     uint32_t gt_before = excl & 0xFFFFu;
     uint32_t eq_before = excl >> 16;
 #pragma unroll
     for (int e = 0; e < PT; ++e) {
         if (e >= cnt) continue;
-        const unsigned long long km = key[e] & mask;
-        if (km > prefix) {
-            out[gt_before + min(eq_before, need)] = i0 + e;
+        if (sc[e] > T) {
+            out[gt_before + min(eq_before, need_eq)] = i0 + e;
             ++gt_before;
-        } else if (km == prefix) {
-            if (eq_before < need) out[gt_before + eq_before] = i0 + e;
+        } else if (sc[e] == T) {
+            if (eq_before < need_eq) out[gt_before + eq_before] = i0 + e;
             ++eq_before;
         }
     }
