@@ -1076,7 +1076,9 @@ int score_fused_pt(int max_pages, bool agg_max) {
     // (32 pages per thread cost the max-aggregation kernel a wavefront per
     // SIMD; in the sum kernel one 256-thread ranking of 4097 pages at the end
     // took longer than the separate 1024-thread kernel: 62.9 against 51.9 us
-    // per int4 selection call at 256K tokens)
+    // per int4 selection call at 256K tokens with the radix ranking, 52.7
+    // against 39.2 us with the value-binned one, whose 32 scores per thread
+    // spill at the 168-register bound)
     (void)agg_max;
     return per <= 4 ? 4 : per <= 8 ? 8 : per <= 16 ? 16 : 0;
 }
