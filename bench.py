@@ -466,21 +466,22 @@ def bench_decode(args, torch, lsa, W, append=True, fused=True, keep_workload=Tru
         launch_bytes += app_bytes
     tok_s = B * steps / elapsed
     src = os.path.join(ROOT, "block_sparse_attention_logical_amd", "csrc", "decode.hip")
-    # the workload the counter summary covers
-    default = args.workload == "llama3-8b" and R == 4 and args.page_size in (None, 64) and \
+    # the workloads the counter summaries cover: configs 2 and 5 in their default geometry
+    tag = {"llama3-8b": "cfg2", "llama3-8b-kv4": "cfg5"}.get(args.workload)
+    covered = tag is not None and R == 4 and args.page_size in (None, 64) and \
         args.logical_page in (None, 16) and fused and args.aggregation == "sum"
-    traffic = counters_for("decode_step_cfg2", src, launch_bytes) if default else None
+    traffic = counters_for(f"decode_step_{tag}", src, launch_bytes) if covered else None
     sel_src = os.path.join(ROOT, "block_sparse_attention_logical_amd", "csrc", "select.hip")
-    sel_traffic = counters_for("score_cfg2", sel_src, sel_call_bytes) if default else None
+    sel_traffic = counters_for(f"score_{tag}", sel_src, sel_call_bytes) if covered else None
     return dict(
         w=w if keep_workload else None, agg=args.aggregation, steps=steps, elapsed=elapsed, tok_s=tok_s, ms_per_step=elapsed / steps * 1e3,
         step_bytes=step_bytes, launch_bytes=launch_bytes, kernel_avg=kernel_avg,
         kernel_p50=kt[len(kt) // 2], timing=timing, append=append, fused=fused,
         traffic=traffic,
-        traffic_source=(f"profiles/decode_step_cfg2_counters.txt, taken on decode.hip sha {sha_of(src)}"
+        traffic_source=(f"profiles/decode_step_{tag}_counters.txt, taken on decode.hip sha {sha_of(src)}"
                         if traffic is not None else None),
         sel_time=sel_time, sel_call_bytes=sel_call_bytes, sel_traffic=sel_traffic,
-        sel_traffic_source=(f"profiles/score_cfg2_counters.txt, taken on select.hip sha {sha_of(sel_src)}"
+        sel_traffic_source=(f"profiles/score_{tag}_counters.txt, taken on select.hip sha {sha_of(sel_src)}"
                             if sel_traffic is not None else None),
     )
 
