@@ -145,21 +145,44 @@ lsa_status check_pool(const lsa_kv *kv, const lsa_heads *hd) {
 }
 
 struct DecodeGeom {
-    int K, chunks_ret, chunks_str, chunks_max, rec_floats;
+    int K, chunk_pages, chunks_ret, chunks_str, chunks_max, rec_floats;
 };
 
 // arrival counters at the start of the decode workspace: one int32 per (sequence, KV head)
 size_t decode_counter_bytes(int batch, int num_kv_heads) { return align_up((size_t)batch * num_kv_heads * 4); }
 
-DecodeGeom decode_geometry(const lsa_kv *kv, const lsa_heads *hd, int token_budget) {
+// Chunks of a (sequence, KV head): its attended pages, at most the kernel's
+// chunk size per workgroup.  A launch that fits the chip's workgroup slots in
+// one round takes smaller chunks while it still fits, its last workgroups
+// still merge a head's records in one batch, and at least three of a
+// workgroup's four wavefronts still have pages: workgroups reach the CUs one
+// per CU per round, so config 2's 384 workgroups of 8 pages put 16 pages on
+// half of the CUs, whose second workgroups then finish their streams about
+// 5 us after the others (448 workgroups of 6 pages: at most 12 pages per CU;
+// 21.5 us per launch against 23.1).  Chunks that leave two wavefronts idle
+// were slower (256-token pages at two per chunk: 24.1 against 22.3 us).
+DecodeGeom decode_geometry(const lsa_kv *kv, const lsa_heads *hd, int token_budget, int batch) {
     DecodeGeom g;
     g.K = token_budget / kv->page_size;
     const int per_chunk = decode_chunk_pages(kv->kv_dtype, kv->page_size);
     const int NP = kv->page_size;
     const int ret_pages = g.K + 1;
     const int str_pages = (hd->sink_tokens + NP - 1) / NP + (hd->local_tokens - 1) / NP + 2;
-    g.chunks_ret = (ret_pages + per_chunk - 1) / per_chunk;
-    g.chunks_str = (str_pages + per_chunk - 1) / per_chunk;
+    const int n_ret = count_kind(hd, kv->num_kv_heads, LSA_RETRIEVAL_HEAD);
+    const int n_str = kv->num_kv_heads - n_ret;
+    auto cdiv = [](int x, int y) { return (x + y - 1) / y; };
+    auto wgs = [&](int c) { return (long long)batch * (n_ret * cdiv(ret_pages, c) + n_str * cdiv(str_pages, c)); };
+    auto most = [&](int c) { return std::max(n_ret ? cdiv(ret_pages, c) : 0, n_str ? cdiv(str_pages, c) : 0); };
+    int cp = per_chunk;
+    if (kv->kv_dtype != LSA_F32) {
+        const int ppw = decode_pages_per_wave(kv->kv_dtype, NP);
+        const long long slots = (long long)decode_waves_per_simd(kv->kv_dtype, NP) * kComputeUnits;
+        if (wgs(cp) <= slots)
+            while (cp - 1 > 2 * ppw && wgs(cp - 1) <= slots && most(cp - 1) <= kDecodeMergeBatch) --cp;
+    }
+    g.chunk_pages = cp;
+    g.chunks_ret = cdiv(ret_pages, cp);
+    g.chunks_str = cdiv(str_pages, cp);
     g.chunks_max = std::max(g.chunks_ret, g.chunks_str);
     g.rec_floats = 32 + (hd->num_q_heads / kv->num_kv_heads) * kv->head_dim;
     return g;
@@ -455,7 +478,7 @@ lsa_status lsa_decode_workspace(const lsa_kv *kv, const lsa_seqs *seqs, const ls
     if (token_budget < kv->page_size || token_budget % kv->page_size != 0)
         return fail(LSA_ERR_INVALID_ARG, "token_budget %d is not a positive multiple of page_size %d", token_budget,
                     kv->page_size);
-    const DecodeGeom g = decode_geometry(kv, heads, token_budget);
+    const DecodeGeom g = decode_geometry(kv, heads, token_budget, seqs->batch);
     *bytes = decode_counter_bytes(seqs->batch, kv->num_kv_heads) +
              align_up((size_t)seqs->batch * kv->num_kv_heads * g.chunks_max * g.rec_floats * sizeof(float));
     return ok();
@@ -632,7 +655,7 @@ lsa_status decode_attn_impl(const void *q, int32_t q_dtype, const lsa_kv *kv, co
                     need, kStaticScratchBytes);
     if (!use_static && (!workspace || workspace_bytes < need))
         return fail(LSA_ERR_WORKSPACE, "workspace of %zu bytes, need %zu", workspace_bytes, need);
-    const DecodeGeom g = decode_geometry(kv, heads, token_budget);
+    const DecodeGeom g = decode_geometry(kv, heads, token_budget, seqs->batch);
     if (g.chunks_max > kMaxDecodeChunks)
         return fail(LSA_ERR_UNSUPPORTED, "token budget / Lambda window spans %d split-KV chunks (limit %d)",
                     g.chunks_max, kMaxDecodeChunks);
@@ -669,6 +692,7 @@ lsa_status decode_attn_impl(const void *q, int32_t q_dtype, const lsa_kv *kv, co
     a.sel_k = g.K;
     a.sink = heads->sink_tokens;
     a.local = heads->local_tokens;
+    a.chunk_pages = g.chunk_pages;
     a.chunks_ret = g.chunks_ret;
     a.chunks_str = g.chunks_str;
     a.chunks_max = g.chunks_max;

@@ -10,8 +10,8 @@
 // the chunk's pool pages into LDS), each wavefront streams its share with an
 // online softmax, the wavefronts' states are merged in LDS and one partial
 // record (max, sum, unnormalised output) is written per chunk.  The MFMA path
-// runs four wavefronts of 128 tokens each (eight pages of 64 tokens per chunk);
-// the f32 path four wavefronts of one page.  The last workgroup of a
+// runs four wavefronts of up to 128 tokens each (up to eight pages of 64
+// tokens per chunk); the f32 path four wavefronts of one page.  The last workgroup of a
 // (sequence, KV head) to finish merges every record in chunk order (so the
 // result does not depend on arrival order) and writes the output.  The
 // hand-off avoids a device-scope fence (an L2 writeback on this part): the
@@ -81,24 +81,26 @@ __device__ __forceinline__ WorkItem decode_item(const DecodeArgs &a) {
 // of the chunk, then their pool pages (-1: no page).
 constexpr int kListSlots = 2 + 2 * kMaxChunkPages;
 
-// Wavefront 0 of a workgroup resolves the CP pages of its chunk: the attended
-// pages of a (sequence, KV head) in ascending order are the selection row
-// (valid entries first, then -1) followed by the current page when the row
-// lacks it (retrieval heads), or the sink pages followed by the local window
-// (streaming heads); the chunk takes list entries CP * chunk .. CP * chunk + CP - 1.
-// seq_lens and the selection entries are loaded together, then the CP
-// page-table entries: two dependent loads in all.
+// Wavefront 0 of a workgroup resolves the pages of its chunk into CP list
+// slots: the attended pages of a (sequence, KV head) in ascending order are
+// the selection row (valid entries first, then -1) followed by the current
+// page when the row lacks it (retrieval heads), or the sink pages followed by
+// the local window (streaming heads); with c = chunk_pages the chunk takes
+// list entries c * chunk .. c * chunk + c - 1 into slots 0 .. c - 1, the other
+// slots hold no page.  seq_lens and the selection entries are loaded
+// together, then the page-table entries: two dependent loads in all.
 template <int CP>
 __device__ __forceinline__ void wg_pages(const DecodeArgs &a, const WorkItem &w, int *list) {
     static_assert(CP <= kMaxChunkPages && (CP & (CP - 1)) == 0, "chunk pages");
     const int lane = threadIdx.x % kWave;
     const int NP = a.page_size;
-    const int i = w.chunk * CP + (lane & (CP - 1));    // list index of this lane's page (lanes 0..CP-1)
+    const bool slot_used = lane < a.chunk_pages;
+    const int i = w.chunk * a.chunk_pages + lane;      // list index of this lane's page (lanes < chunk_pages)
     const int32_t *sel = w.streaming ? nullptr : a.selected + ((size_t)w.b * a.num_kv_heads + w.kv) * a.sel_k;
     int m_row = -1, m_i = -1;
     if (sel) {
         if (lane < a.sel_k) m_row = sel[lane];
-        if (lane < CP && i < a.sel_k) m_i = sel[i];
+        if (slot_used && i < a.sel_k) m_i = sel[i];
     }
     const int L = a.seq_lens[w.b];
     const int t = L - 1, cur = t / NP;
@@ -108,7 +110,7 @@ __device__ __forceinline__ void wg_pages(const DecodeArgs &a, const WorkItem &w,
         const int n_sink = (sink_end + NP - 1) / NP;
         const int local_first = max(max(0, t - a.local + 1) / NP, n_sink);
         const int n = n_sink + max(0, cur - local_first + 1);
-        if (i < n) page = i < n_sink ? i : local_first + (i - n_sink);
+        if (slot_used && i < n) page = i < n_sink ? i : local_first + (i - n_sink);
     } else {
         int cnt = __popcll(__ballot(m_row >= 0));
         bool in = __ballot(m_row == cur) != 0;
@@ -118,7 +120,7 @@ __device__ __forceinline__ void wg_pages(const DecodeArgs &a, const WorkItem &w,
             in |= __ballot(m == cur) != 0;
         }
         const int n = cnt + (in ? 0 : 1);
-        if (i < n) page = i < cnt ? m_i : cur;
+        if (slot_used && i < n) page = i < cnt ? m_i : cur;
     }
     int pool = -1;                    // pool page, or the stream-cache page of a streaming head
     if (lane < CP && page >= 0)
@@ -424,14 +426,6 @@ __device__ __forceinline__ uint32_t pick(const uint4 &u, int i) {
 // ---------------------------------------------------------------------------
 // MFMA kernel, bf16 or int4 pool, bf16 q
 // ---------------------------------------------------------------------------
-// Wavefronts per SIMD the register budget is set for: three for the int4
-// instances with 64- and 128-token pages (at most 168 VGPRs: past that, with
-// the allocation granule of 8, a SIMD holds two, and a launch of 768
-// workgroups, B = 16 at a 4096-token budget, no longer fits the chip in one
-// round), two otherwise (the 16- and 32-token int4 instances spill at 168).
-__host__ __device__ constexpr int decode_waves_per_simd(int kvt, int np) {
-    return kvt == LSA_INT4 && (np == 64 || np == 128) ? 3 : 2;
-}
 template <int D, int KVT, int NP>
 __global__ __launch_bounds__(kDecodeWaves * kWave, decode_waves_per_simd(KVT, NP)) void decode_mfma_kernel(DecodeArgs a) {
     constexpr bool I4 = KVT == LSA_INT4;
@@ -518,44 +512,39 @@ __global__ __launch_bounds__(kDecodeWaves * kWave, decode_waves_per_simd(KVT, NP
         hp[j] = (size_t)max(pool, 0) * hp_mul + hp_add;
     }
     // block i of the wavefront: page slot i / NB, 32-token block i % NB of that
-    // page; with 16-token pages, tile T of block i is page slot 2i + T.  For
-    // every (block, tile): whether it holds an attended token, and its first
-    // token position.
-    bool need_t[NBW][2];
-    int tok_t[NBW][2];
-    bool need[NBW];
-    bool any = false;
+    // page; with 16-token pages, tile T of block i is page slot 2i + T.  Per
+    // (block, tile), as bits of scalar registers (wavefront-uniform; arrays of
+    // flags and positions cost a scalar register or a pair each, and the
+    // instances with many blocks per wavefront ran out of them): need (bit
+    // 2i + T) whether it holds an attended token, full (bit i) whether all 32
+    // tokens of the block are attended and read from memory (its scores and
+    // values then need no masking).  A tile's first token position is
+    // recomputed from the page slot where it is used.
+    auto slot_of = [&](int i, int T) { return HALF ? 2 * i + T : i / NB; };
+    auto tok_of = [&](int i, int T) { return HALF ? pg[2 * i + T] * NP : pg[i / NB] * NP + 32 * (i % NB) + 16 * T; };
+    uint32_t need_bits = 0, full_bits = 0;
 #pragma unroll
     for (int i = 0; i < NBW; ++i) {
-        if constexpr (HALF) {
-#pragma unroll
-            for (int T = 0; T < 2; ++T) {
-                tok_t[i][T] = pg[2 * i + T] * NP;
-                need_t[i][T] = pg[2 * i + T] >= 0 && block_needed(a, w, tok_t[i][T], NP);
-            }
-        } else {
-            const int tok0 = pg[i / NB] * NP + 32 * (i % NB);
-            const bool nd = pg[i / NB] >= 0 && block_needed(a, w, tok0, 32);
-            need_t[i][0] = need_t[i][1] = nd;
-            tok_t[i][0] = tok0;
-            tok_t[i][1] = tok0 + 16;
-        }
-        need[i] = need_t[i][0] | need_t[i][1];
-        any |= need[i];
-    }
-    // blocks whose 32 tokens are all attended and read from memory: their
-    // scores and values need no masking (wavefront-uniform)
-    bool full[NBW];
-#pragma unroll
-    for (int i = 0; i < NBW; ++i) {
-        bool f = need_t[i][0] & need_t[i][1];
+        bool nd[2];
 #pragma unroll
         for (int T = 0; T < 2; ++T) {
-            const int p0 = tok_t[i][T], p1 = p0 + 15;
+            if constexpr (HALF) nd[T] = pg[2 * i + T] >= 0 && block_needed(a, w, tok_of(i, T), NP);
+            else nd[T] = pg[i / NB] >= 0 && block_needed(a, w, tok_of(i, 0), 32);
+        }
+        bool f = nd[0] & nd[1];
+#pragma unroll
+        for (int T = 0; T < 2; ++T) {
+            const int p0 = tok_of(i, T), p1 = p0 + 15;
             f &= (p1 <= w.t_pool) & (!w.streaming | (p1 < a.sink) | (w.t - p0 < a.local));
         }
-        full[i] = f;
+        need_bits |= (nd[0] ? 1u : 0u) << (2 * i);
+        need_bits |= (nd[1] ? 1u : 0u) << (2 * i + 1);
+        full_bits |= (f ? 1u : 0u) << i;
     }
+    need_bits = __builtin_amdgcn_readfirstlane(need_bits);
+    full_bits = __builtin_amdgcn_readfirstlane(full_bits);
+    auto need_t = [&](int i, int T) -> bool { return (need_bits >> (2 * i + T)) & 1u; };
+    const bool any = need_bits != 0;
 
     floatx4 o[NDT];
 #pragma unroll
@@ -600,39 +589,29 @@ __global__ __launch_bounds__(kDecodeWaves * kWave, decode_waves_per_simd(KVT, NP
                 }
             }
         }
-        // source of each ring load: the block (tile) itself, or the first needed one
-        size_t src_hp[NBW][2];
-        int src_kb[NBW];
+        // source of each ring load: the block (tile) itself, or the first
+        // needed tile (its page slot and its block within that page)
+        size_t f_hp = 0;
+        int f_kb = 0;
         {
-            size_t f_hp = 0;
-            int f_kb = 0;
-            bool found = false;
+            const int ft = __builtin_ctz(need_bits), fi = ft >> 1, fT = ft & 1;
 #pragma unroll
-            for (int i = 0; i < NBW; ++i)
-#pragma unroll
-                for (int T = 0; T < 2; ++T)
-                    if (need_t[i][T] && !found) {
-                        f_hp = hp[HALF ? 2 * i + T : i / NB];
-                        f_kb = HALF ? 0 : i % NB;
-                        found = true;
-                    }
-#pragma unroll
-            for (int i = 0; i < NBW; ++i) {
-#pragma unroll
-                for (int T = 0; T < 2; ++T) src_hp[i][T] = need_t[i][T] ? hp[HALF ? 2 * i + T : i / NB] : f_hp;
-                src_kb[i] = need[i] ? (HALF ? 0 : i % NB) : f_kb;
-            }
+            for (int j = 0; j < PPW; ++j)
+                if (j == (HALF ? 2 * fi + fT : fi / NB)) f_hp = hp[j];
+            f_kb = HALF ? 0 : fi % NB;
         }
+        auto src_hp = [&](int i, int T) -> size_t { return need_t(i, T) ? hp[slot_of(i, T)] : f_hp; };
+        auto src_kb = [&](int i) -> int { return ((need_bits >> (2 * i)) & 3u) ? (HALF ? 0 : i % NB) : f_kb; };
 
         uint4 kr[BIF][2][I4 ? 1 : NS];
         uint4 vr[BIF][I4 ? 1 : NDT];
         uint32_t vr4[BIF][I4 ? NDT : 1];
         // ---- issue every K and V load of block i into ring slot e
         auto issue = [&](int e, int i) __attribute__((always_inline)) {
-            const int kb = src_kb[i];
+            const int kb = src_kb(i);
             // key rows of tile T; the value rows this lane reads (tokens 8*g4 ..
             // 8*g4 + 7 of the block: page 2i + g4/2, tokens 8*(g4%2).. with 16-token pages)
-            const size_t kbase[2] = {src_hp[i][0] * NP * D, src_hp[i][1] * NP * D};
+            const size_t kbase[2] = {src_hp(i, 0) * NP * D, src_hp(i, 1) * NP * D};
             const size_t vbase = HALF ? (g4 < 2 ? kbase[0] : kbase[1]) : kbase[0];
             const int vtok = HALF ? 8 * (g4 & 1) : 32 * kb + 8 * g4;
             if constexpr (I4) {
@@ -704,11 +683,12 @@ __global__ __launch_bounds__(kDecodeWaves * kWave, decode_waves_per_simd(KVT, NP
 #pragma unroll
                 for (int r = 0; r < 4; ++r) { x[r] = s0[r] * a.scale_log2; x[4 + r] = s1[r] * a.scale_log2; }
             }
-            if (!full[i]) {                     // (wavefront-uniform branch)
+            const bool full = (full_bits >> i) & 1u;
+            if (!full) {                        // (wavefront-uniform branch)
 #pragma unroll
                 for (int jj = 0; jj < 8; ++jj) {
                     const int T = jj >> 2;
-                    const bool vis = need_t[i][T] & token_visible(a, w, tok_t[i][T] + 4 * g4 + (jj & 3));
+                    const bool vis = need_t(i, T) & token_visible(a, w, tok_of(i, T) + 4 * g4 + (jj & 3));
                     x[jj] = vis ? x[jj] : -__builtin_inff();
                 }
             }
@@ -762,11 +742,11 @@ __global__ __launch_bounds__(kDecodeWaves * kWave, decode_waves_per_simd(KVT, NP
             // always unpack to finite values)
             if constexpr (!I4) {
                 const bool tail =
-                    !full[i] && (!(need_t[i][0] & need_t[i][1]) || max(tok_t[i][0], tok_t[i][1]) + 15 > w.t_pool);
+                    !full && (!(need_t(i, 0) & need_t(i, 1)) || max(tok_of(i, 0), tok_of(i, 1)) + 15 > w.t_pool);
                 if (tail) {                     // (wavefront-uniform branch: masks the ring slot in place)
                     const int vt = HALF ? g4 >> 1 : 0;   // the tile whose tokens this lane's value rows hold
                     const int nvalid =
-                        need_t[i][vt] ? w.t_pool - (tok_t[i][vt] + (HALF ? 8 * (g4 & 1) : 8 * g4)) + 1 : 0;
+                        ((need_bits >> (2 * i + vt)) & 1u) ? w.t_pool - ((vt ? tok_of(i, 1) : tok_of(i, 0)) + (HALF ? 8 * (g4 & 1) : 8 * g4)) + 1 : 0;
                     uint32_t keep[4];
 #pragma unroll
                     for (int q2 = 0; q2 < 4; ++q2)
@@ -867,9 +847,7 @@ __global__ __launch_bounds__(kDecodeWaves * kWave, decode_waves_per_simd(KVT, NP
     }
     __syncthreads();
     merge_waves_and_store<kDecodeWaves>(a, w, lds, D, a.k_new != nullptr);
-    // one batch of records covers a 4096-token budget (its pages plus the current one)
-    constexpr int CB = (4096 / NP + CP) / CP < 17 ? (4096 / NP + CP) / CP : 17;
-    finish_head<uint16_t, CB>(a, w, D);
+    finish_head<uint16_t, kDecodeMergeBatch>(a, w, D);
 }
 
 // ---------------------------------------------------------------------------

@@ -14,9 +14,12 @@ constexpr int kWave = 64;         // CDNA wavefront width
 constexpr int kMaxDecodeChunks = 128;   // split-KV chunks per (sequence, KV head)
 
 // Split-KV geometry of decode attention.  The MFMA path runs kDecodeWaves
-// wavefronts per workgroup, each streaming 128 tokens (one page when pages are
-// longer); the f32 path runs four wavefronts of one page each.  A workgroup
-// takes one chunk of the attended page list.
+// wavefronts per workgroup, each streaming up to 128 tokens (one page when
+// pages are longer); the f32 path runs four wavefronts of one page each.  A
+// workgroup takes one chunk of the attended page list: up to
+// decode_chunk_pages pages, fewer when that spreads a launch that fits the
+// chip in one round more evenly over the CUs (the decode geometry on the
+// host); wavefront w takes the chunk's pages PPW*w .. PPW*w + PPW - 1.
 constexpr int kDecodeWaves = 4;
 constexpr int kMaxChunkPages = 32;
 constexpr int kDecodeWaveTokens = 128;
@@ -36,6 +39,20 @@ __host__ __device__ constexpr int decode_pages_per_wave(int kv_dtype, int page_s
 __host__ __device__ constexpr int decode_chunk_pages(int kv_dtype, int page_size) {
     return kv_dtype == LSA_F32 ? 4 : kDecodeWaves * decode_pages_per_wave(kv_dtype, page_size);
 }
+// Wavefronts per SIMD the MFMA decode kernel's register budget is set for:
+// three for the int4 instances with 64- and 128-token pages (at most 168
+// VGPRs: past that, with the allocation granule of 8, a SIMD holds two, and a
+// launch of 768 workgroups, B = 16 at a 4096-token budget, no longer fits the
+// chip in one round), two otherwise (the 16- and 32-token int4 instances
+// spill at 168).  With four wavefronts per workgroup this is also the
+// workgroups per CU.
+__host__ __device__ constexpr int decode_waves_per_simd(int kvt, int np) {
+    return kvt == LSA_INT4 && (np == 64 || np == 128) ? 3 : 2;
+}
+constexpr int kComputeUnits = 256;        // CUs of the part (MI355X)
+// split-KV records the last workgroup of a (sequence, KV head) loads per
+// memory round trip when it merges them
+constexpr int kDecodeMergeBatch = 12;
 
 // ----------------------------------------------------------------------------
 // numeric helpers (device)
@@ -337,6 +354,7 @@ struct DecodeArgs {
     int32_t batch, max_pages, num_q_heads, num_kv_heads, group, head_dim, page_size, logical_page;
     int32_t sel_k;                // K (row length of selected)
     int32_t sink, local;
+    int32_t chunk_pages;              // pages per chunk (at most the kernel's decode_chunk_pages)
     int32_t chunks_ret, chunks_str;   // workgroups per (sequence, head) by kind
     int32_t chunks_max;               // record slots per (sequence, head)
     int32_t chunks_per_seq;           // workgroups per sequence

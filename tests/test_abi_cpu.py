@@ -180,13 +180,21 @@ def test_decode_validation(lib):
 
 
 def test_decode_workspace_size(lib):
-    out = ctypes.c_size_t(0)
-    st = lib.lsa_decode_workspace(ctypes.byref(kv_desc()), ctypes.byref(seqs_desc(8, 1025)),
-                                  ctypes.byref(heads_desc()), 4096, ctypes.byref(out))
-    assert st == 0
-    # 65 retrieval pages -> 9 chunks of 8 pages (four wavefronts of 128 tokens);
-    # records of 32 + G*D floats per chunk, after one int32 counter per (sequence, KV head)
-    assert out.value == 256 + 8 * 8 * 9 * (32 + 4 * 128) * 4
+    # records of 32 + G*D floats per chunk, after one int32 counter per
+    # (sequence, KV head).  65 retrieval pages and 1 + 15 + 2 = 18 streaming
+    # pages per (sequence, head), chunks of at most 8 pages (four wavefronts of
+    # 128 tokens), and 2 x 256 workgroup slots for the bf16 kernel.
+    def ws(batch):
+        out = ctypes.c_size_t(0)
+        st = lib.lsa_decode_workspace(ctypes.byref(kv_desc()), ctypes.byref(seqs_desc(batch, 1025)),
+                                      ctypes.byref(heads_desc()), 4096, ctypes.byref(out))
+        assert st == 0
+        return out.value
+    # B = 16: 16 x (4 x 9 + 4 x 3) = 768 workgroups of 8 pages, more than the slots: 9 chunks
+    assert ws(16) == 512 + 16 * 8 * 9 * (32 + 4 * 128) * 4
+    # B = 8: 384 workgroups of 8 pages fit; 6 pages per chunk is the smallest size that still
+    # fits (8 x (4 x 11 + 4 x 3) = 448; 5 pages: 544): 11 chunks per retrieval head
+    assert ws(8) == 256 + 8 * 8 * 11 * (32 + 4 * 128) * 4
 
 
 def prefill(lib, kv=None, q_dtype=lsa.BF16, block=64, T=1000):
