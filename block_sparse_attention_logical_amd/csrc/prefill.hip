@@ -36,6 +36,17 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float floatx16 __attribute__((ext_vector_type(16)));
 
 constexpr int kTile = 64;
+// dword 3 of a raw buffer resource on gfx9-family parts (32-bit data format)
+constexpr int kBufferWord3 = 0x00020000;
+
+// 16 bytes per lane from base + voff into LDS (the wavefront's 64 lanes fill
+// 1 KiB at lds), through a raw buffer resource of `bytes` bytes at base: a
+// lane whose offset falls outside it reads zeros instead of memory.
+__device__ __forceinline__ void buffer_to_lds16(const void *base, int bytes, uint32_t voff, void *lds) {
+    const __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), 0, bytes,
+                                                                          kBufferWord3);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (void __attribute__((address_space(3))) *)lds, 16, voff, 0, 0, 0);
+}
 
 struct PItem {
     int kv, a, hg;
@@ -185,7 +196,7 @@ __global__ __launch_bounds__(512, 2) void prefill_bf16_kernel(PrefillArgs p) {
     const PItem it = prefill_item<CSR, QT>(p);
     const TileRow trow = tile_row<CSR, QT>(p, it);
 
-    const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
+    const int tid = threadIdx.x, lane = tid % kWave, wave = __builtin_amdgcn_readfirstlane(tid / kWave);
     const int T = p.seq_len, G = p.group, HQ = p.num_q_heads, NP = p.page_size;
     // wavefront pair `slot`: query head and query tile; with QT > 1 the group is G = 4 / QT
     const int slot = wave >> 1;
@@ -323,17 +334,23 @@ __global__ __launch_bounds__(512, 2) void prefill_bf16_kernel(PrefillArgs p) {
     // 64j .. 64j+63 (16 rows of 4 chunks); lane l writes position l, i.e. row
     // 16j + l/4, position l%4, and so reads the row's logical chunk
     // (l%4) ^ swz(row) from the pool: one contiguous 1 KiB per instruction.
-    auto fetch = [&](const uint16_t *pool, uint16_t *lds, size_t base) {
-        const uint16_t *src = pool + base;
+    // The fetch is a raw buffer load into LDS: the tile's base goes in a
+    // buffer resource (scalar registers) whose size is the tile's, so no access
+    // leaves the tile, and the lane's byte offset within the tile, the same
+    // for every tile, is formed once.
+    uint32_t fetch_off[KPT];
 #pragma unroll
-        for (int e = 0; e < KPT; ++e) {
-            const int j = wave + e * (NT / kWave);
-            const int row = 16 * j + (lane >> 2);                // (block, slice, key) or (block, channel) row
-            const int c = (lane & 3) ^ swz(row);                 // swz(row) = swz(row % 32) = swz(channel)
-            __builtin_amdgcn_global_load_lds(
-                (const void __attribute__((address_space(1))) *)(src + (size_t)row * 32 + c * 8),
-                (void __attribute__((address_space(3))) *)(lds + (size_t)j * 512), 16, 0, 0);
-        }
+    for (int e = 0; e < KPT; ++e) {
+        const int j = wave + e * (NT / kWave);
+        const int row = 16 * j + (lane >> 2);                    // (block, slice, key) or (block, channel) row
+        const int c = (lane & 3) ^ swz(row);                     // swz(row) = swz(row % 32) = swz(channel)
+        fetch_off[e] = (uint32_t)(row * 32 + c * 8) * 2u;
+    }
+    auto fetch = [&](const uint16_t *pool, uint16_t *lds, size_t base) {
+#pragma unroll
+        for (int e = 0; e < KPT; ++e)
+            buffer_to_lds16(pool + base, kTile * D * (int)sizeof(uint16_t), fetch_off[e],
+                            lds + (wave + e * (NT / kWave)) * 512);
     };
     // values of keys >= T (only in the sequence's last tile) may hold any bits:
     // zero them once they have landed, so a zero probability never meets a NaN
@@ -366,7 +383,9 @@ __global__ __launch_bounds__(512, 2) void prefill_bf16_kernel(PrefillArgs p) {
     };
     // online softmax of the scores s (diag: causal mask against key0): rescale
     // O and l when the running max moves, and pack P = exp2(s * sc - m) as the
-    // bf16 B operands of the four k-steps of O^T += V^T P^T
+    // bf16 B operands of the four k-steps of O^T += V^T P^T.  l sums exactly
+    // those bf16 values (two per v_dot2_f32_bf16 against (1, 1)), so numerator
+    // and denominator carry the same rounding.
     auto softmax_p = [&](floatx16 (&s)[2], int key0, bool diag, bf16x8 (&pb)[4]) {
         if (diag) {
             const int qrow = q0 + col;
@@ -391,6 +410,7 @@ __global__ __launch_bounds__(512, 2) void prefill_bf16_kernel(PrefillArgs p) {
             m_run = m_new;
         }
         const float mb = m_run * sc;
+        const bf16x2 ones = __builtin_bit_cast(bf16x2, 0x3F803F80u);
 #pragma unroll
         for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
@@ -400,8 +420,9 @@ __global__ __launch_bounds__(512, 2) void prefill_bf16_kernel(PrefillArgs p) {
                 for (int j = 0; j < 8; j += 2) {
                     const float e0v = exp2_fast(fmaf(s[kt][8 * st + j], sc, -mb));
                     const float e1v = exp2_fast(fmaf(s[kt][8 * st + j + 1], sc, -mb));
-                    l_run += e0v + e1v;
-                    pk[j / 2] = __builtin_bit_cast(uint32_t, __builtin_convertvector(floatx2{e0v, e1v}, bf16x2));
+                    const bf16x2 e01 = __builtin_convertvector(floatx2{e0v, e1v}, bf16x2);
+                    l_run = __builtin_amdgcn_fdot2_f32_bf16(e01, ones, l_run, false);
+                    pk[j / 2] = __builtin_bit_cast(uint32_t, e01);
                 }
                 pb[2 * kt + st] = __builtin_bit_cast(bf16x8, make_uint4(pk[0], pk[1], pk[2], pk[3]));
             }
