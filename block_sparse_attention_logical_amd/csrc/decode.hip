@@ -606,44 +606,67 @@ __global__ __launch_bounds__(kDecodeWaves * kWave, decode_waves_per_simd(KVT, NP
         uint4 kr[BIF][2][I4 ? 1 : NS];
         uint4 vr[BIF][I4 ? 1 : NDT];
         uint32_t vr4[BIF][I4 ? NDT : 1];
+        // Ring loads go through a buffer resource over the page they read (its
+        // base in scalar registers), with the lane's byte offset within a
+        // block, the same for every block, formed here once; the block, tile,
+        // channel-step and output-tile terms are wavefront-uniform scalar
+        // offsets.  Every address is the page layout's own, as with plain
+        // loads.  The value rows of 16-token pages (a lane's page depends on
+        // its token group) stay plain loads.
+        constexpr int kPageBytes = I4 ? NP * D / 2 : NP * D * 2;
+        auto to_bytes = [](size_t elems) -> uint32_t { return (uint32_t)(I4 ? elems / 2 : elems * 2); };
+        const uint32_t k_lane = to_bytes(key_offset(rho, I4 ? (D / 4) * g4 : 8 * g4, D, BS));
+        const uint32_t v_lane = to_bytes(value_offset(8 * g4, h, D, BS));
         // ---- issue every K and V load of block i into ring slot e
         auto issue = [&](int e, int i) __attribute__((always_inline)) {
             const int kb = src_kb(i);
-            // key rows of tile T; the value rows this lane reads (tokens 8*g4 ..
-            // 8*g4 + 7 of the block: page 2i + g4/2, tokens 8*(g4%2).. with 16-token pages)
+            // the pages of tiles 0 and 1 (element offsets), and the block's and
+            // the tiles' offsets within them: tile T holds tokens 16T .. 16T + 15
+            // of block kb, or is page slot 2i + T (16-token pages)
             const size_t kbase[2] = {src_hp(i, 0) * NP * D, src_hp(i, 1) * NP * D};
-            const size_t vbase = HALF ? (g4 < 2 ? kbase[0] : kbase[1]) : kbase[0];
-            const int vtok = HALF ? 8 * (g4 & 1) : 32 * kb + 8 * g4;
+            const uint32_t blk = HALF ? 0u : (uint32_t)(kb * 32 * D);
+            auto tile_el = [&](int T) -> uint32_t { return HALF ? 0u : blk + 512u * T; };
             if constexpr (I4) {
                 const uint8_t *k8 = static_cast<const uint8_t *>(kpool);
 #pragma unroll
                 for (int T = 0; T < 2; ++T) {
-                    const int row_tok = HALF ? rho : 32 * kb + 16 * T + rho;
-                    const uint8_t *row = k8 + (kbase[T] + key_offset(row_tok, (D / 4) * g4, D, BS)) / 2;
+                    const uint8_t *page = k8 + kbase[T] / 2;
                     if constexpr (D == 128) {
-                        kr[e][T][0] = load_stream16(row);
+                        kr[e][T][0] = buffer_stream16(page, kPageBytes, k_lane, to_bytes(tile_el(T)));
                     } else {
-                        const uint2 u = load_stream8(row);
+                        const uint2 u = buffer_stream8(page, kPageBytes, k_lane, to_bytes(tile_el(T)));
                         kr[e][T][0] = make_uint4(u.x, u.y, 0, 0);
                     }
                 }
                 const uint8_t *v8 = static_cast<const uint8_t *>(vpool);
 #pragma unroll
-                for (int dt = 0; dt < NDT; ++dt)
-                    vr4[e][dt] = load_stream4(v8 + (vbase + value_offset(vtok, 16 * dt + h, D, BS)) / 2);
+                for (int dt = 0; dt < NDT; ++dt) {
+                    if constexpr (HALF) {
+                        // tokens 8*(g4%2) .. of page 2i + g4/2
+                        const size_t vbase = g4 < 2 ? kbase[0] : kbase[1];
+                        vr4[e][dt] = load_stream4(v8 + (vbase + value_offset(8 * (g4 & 1), 16 * dt + h, D, BS)) / 2);
+                    } else {
+                        vr4[e][dt] = buffer_stream4(v8 + kbase[0] / 2, kPageBytes, v_lane, to_bytes(blk + 512u * dt));
+                    }
+                }
             } else {
                 const uint16_t *kp = static_cast<const uint16_t *>(kpool);
 #pragma unroll
-                for (int T = 0; T < 2; ++T) {
-                    const int row_tok = HALF ? rho : 32 * kb + 16 * T + rho;
+                for (int T = 0; T < 2; ++T)
 #pragma unroll
                     for (int s = 0; s < NS; ++s)
-                        kr[e][T][s] = load_stream16(kp + kbase[T] + key_offset(row_tok, 32 * s + 8 * g4, D, BS));
-                }
-                const uint16_t *vp = static_cast<const uint16_t *>(vpool) + vbase;
+                        kr[e][T][s] = buffer_stream16(kp + kbase[T], kPageBytes, k_lane,
+                                                      to_bytes(tile_el(T) + ((uint32_t)s << (BS + 5))));
+                const uint16_t *vp = static_cast<const uint16_t *>(vpool);
 #pragma unroll
-                for (int dt = 0; dt < NDT; ++dt)
-                    vr[e][dt] = load_stream16(vp + value_offset(vtok, 16 * dt + h, D, BS));
+                for (int dt = 0; dt < NDT; ++dt) {
+                    if constexpr (HALF) {
+                        const size_t vbase = g4 < 2 ? kbase[0] : kbase[1];
+                        vr[e][dt] = load_stream16(vp + vbase + value_offset(8 * (g4 & 1), 16 * dt + h, D, BS));
+                    } else {
+                        vr[e][dt] = buffer_stream16(vp + kbase[0], kPageBytes, v_lane, to_bytes(blk + 512u * dt));
+                    }
+                }
             }
             // keep the block's loads ahead of the compute that follows them
             __builtin_amdgcn_sched_barrier(0);

@@ -94,6 +94,30 @@ __device__ __forceinline__ uint32_t load_stream4(const void *p) {
     return __builtin_nontemporal_load(static_cast<const uint32_t *>(p));
 }
 
+// Raw buffer resources (gfx9 family: dword 3 selects the 32-bit data format).
+// A load through one takes its base from scalar registers and its lane offset
+// from one VGPR, so a kernel that forms the lane offsets once issues its loads
+// with no per-load vector address arithmetic.  The hardware range check
+// covers the lane offset (plus the instruction's immediate): a lane whose
+// offset is at or past `bytes` reads zeros; the scalar offset is not checked,
+// so callers keep base + soff + voff inside the object themselves.
+constexpr int kBufferWord3 = 0x00020000;
+constexpr int kBufferNt = 2;                      // the non-temporal hint of load_stream*
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void *base, int bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), 0, bytes, kBufferWord3);
+}
+__device__ __forceinline__ uint4 buffer_stream16(const void *base, int bytes, uint32_t voff, uint32_t soff) {
+    return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(buffer_rsrc(base, bytes), voff, soff,
+                                                                            kBufferNt));
+}
+__device__ __forceinline__ uint2 buffer_stream8(const void *base, int bytes, uint32_t voff, uint32_t soff) {
+    return __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(buffer_rsrc(base, bytes), voff, soff,
+                                                                           kBufferNt));
+}
+__device__ __forceinline__ uint32_t buffer_stream4(const void *base, int bytes, uint32_t voff, uint32_t soff) {
+    return __builtin_amdgcn_raw_buffer_load_b32(buffer_rsrc(base, bytes), voff, soff, kBufferNt);
+}
+
 // ----------------------------------------------------------------------------
 // page layout: a page of N_P tokens of one KV head is a run of blocks of BT =
 // min(N_P, 32) tokens (N_P/32 blocks of 32, or one block of 16 for 16-token

@@ -36,16 +36,13 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float floatx16 __attribute__((ext_vector_type(16)));
 
 constexpr int kTile = 64;
-// dword 3 of a raw buffer resource on gfx9-family parts (32-bit data format)
-constexpr int kBufferWord3 = 0x00020000;
 
 // 16 bytes per lane from base + voff into LDS (the wavefront's 64 lanes fill
 // 1 KiB at lds), through a raw buffer resource of `bytes` bytes at base: a
 // lane whose offset falls outside it reads zeros instead of memory.
 __device__ __forceinline__ void buffer_to_lds16(const void *base, int bytes, uint32_t voff, void *lds) {
-    const __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), 0, bytes,
-                                                                          kBufferWord3);
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (void __attribute__((address_space(3))) *)lds, 16, voff, 0, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(buffer_rsrc(base, bytes), (void __attribute__((address_space(3))) *)lds,
+                                             16, voff, 0, 0, 0);
 }
 
 struct PItem {
