@@ -605,7 +605,18 @@ __global__ __launch_bounds__(kDecodeWaves * kWave, decode_waves_per_simd(KVT, NP
 
         uint4 kr[BIF][2][I4 ? 1 : NS];
         uint4 vr[BIF][I4 ? 1 : NDT];
-        uint32_t vr4[BIF][I4 ? NDT : 1];
+        // int4 values.  The PV operand wants, per output tile dt, the 4 bytes
+        // of tokens 8*g4 .. 8*g4+7 of channel 16*dt + h: one dword per tile,
+        // which as loads of their own move 256 bytes per instruction, and
+        // loads that narrow cap the stream far below the HBM rate.  So lane
+        // (h, g4) loads whole 16-byte channel rows (all 32 tokens) instead,
+        // those of tiles (NDT/4)*g4 + j, and a 4 x 4 transpose across the
+        // four lane groups of h (permlane swaps) hands every lane its dwords.
+        // 16-token pages keep per-tile dword loads (a lane's page depends on
+        // its token group there).
+        constexpr int VRW = I4 && !HALF ? NDT / 4 : 1;    // 16-byte value rows per lane and block
+        uint4 vq[BIF][VRW];
+        uint32_t vr4[BIF][I4 && HALF ? NDT : 1];
         // Ring loads go through a buffer resource over the page they read (its
         // base in scalar registers), with the lane's byte offset within a
         // block, the same for every block, formed here once; the block, tile,
@@ -617,6 +628,7 @@ __global__ __launch_bounds__(kDecodeWaves * kWave, decode_waves_per_simd(KVT, NP
         auto to_bytes = [](size_t elems) -> uint32_t { return (uint32_t)(I4 ? elems / 2 : elems * 2); };
         const uint32_t k_lane = to_bytes(key_offset(rho, I4 ? (D / 4) * g4 : 8 * g4, D, BS));
         const uint32_t v_lane = to_bytes(value_offset(8 * g4, h, D, BS));
+        const uint32_t v_row_lane = to_bytes(value_offset(0, 16 * VRW * g4 + h, D, BS));   // int4 value rows
         // ---- issue every K and V load of block i into ring slot e
         auto issue = [&](int e, int i) __attribute__((always_inline)) {
             const int kb = src_kb(i);
@@ -645,9 +657,13 @@ __global__ __launch_bounds__(kDecodeWaves * kWave, decode_waves_per_simd(KVT, NP
                         // tokens 8*(g4%2) .. of page 2i + g4/2
                         const size_t vbase = g4 < 2 ? kbase[0] : kbase[1];
                         vr4[e][dt] = load_stream4(v8 + (vbase + value_offset(8 * (g4 & 1), 16 * dt + h, D, BS)) / 2);
-                    } else {
-                        vr4[e][dt] = buffer_stream4(v8 + kbase[0] / 2, kPageBytes, v_lane, to_bytes(blk + 512u * dt));
                     }
+                }
+                if constexpr (!HALF) {
+                    // the row of channel 16 * (VRW * g4 + j) + h: 16 channels = 512 codes further per j
+#pragma unroll
+                    for (int j = 0; j < VRW; ++j)
+                        vq[e][j] = buffer_stream16(v8 + kbase[0] / 2, kPageBytes, v_row_lane, to_bytes(blk + 512u * j));
                 }
             } else {
                 const uint16_t *kp = static_cast<const uint16_t *>(kpool);
@@ -786,12 +802,29 @@ __global__ __launch_bounds__(kDecodeWaves * kWave, decode_waves_per_simd(KVT, NP
 #pragma unroll
                 for (int dt = 0; dt < NDT; ++dt) o[dt] *= alpha;
             }
+            // int4 rows -> per-tile dwords: before, lane group q's slot c holds
+            // dword c (tokens 8c ..) of channel 16 * (VRW * q + j) + h; after the
+            // swaps lane group g4's slot q holds dword g4 of that same channel,
+            // i.e. the operand of tile VRW * q + j
+            uint32_t vy[I4 && !HALF ? NDT : 1];
+            if constexpr (I4 && !HALF) {
+#pragma unroll
+                for (int j = 0; j < VRW; ++j) {
+                    uint32_t d[4] = {vq[e][j].x, vq[e][j].y, vq[e][j].z, vq[e][j].w};
+                    swap_halves32(d[0], d[2]);
+                    swap_halves32(d[1], d[3]);
+                    swap_rows16(d[0], d[1]);
+                    swap_rows16(d[2], d[3]);
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) vy[VRW * q + j] = d[q];
+                }
+            }
 #pragma unroll
             for (int dt = 0; dt < NDT; ++dt) {
                 uint4 va;
                 if constexpr (I4) {
                     // 4 bytes = tokens 8*g4 .. 8*g4+7 of channel 16*dt + h
-                    va = nibbles_bf16x8_split(vr4[e][dt]);
+                    va = nibbles_bf16x8_split(HALF ? vr4[e][dt] : vy[dt]);
                 } else {
                     va = vr[e][dt];
                 }

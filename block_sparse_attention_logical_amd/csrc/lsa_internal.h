@@ -151,6 +151,18 @@ __device__ __forceinline__ void pair16(uint32_t x, uint32_t &a, uint32_t &b) {
     a = r[0];
     b = r[1];
 }
+// a's lanes 32-63 trade places with b's lanes 0-31
+__device__ __forceinline__ void swap_halves32(uint32_t &a, uint32_t &b) {
+    const auto r = __builtin_amdgcn_permlane32_swap(a, b, false, false);
+    a = r[0];
+    b = r[1];
+}
+// a's odd 16-lane rows (lanes 16-31, 48-63) trade places with b's even rows (0-15, 32-47)
+__device__ __forceinline__ void swap_rows16(uint32_t &a, uint32_t &b) {
+    const auto r = __builtin_amdgcn_permlane16_swap(a, b, false, false);
+    a = r[0];
+    b = r[1];
+}
 __device__ __forceinline__ float max_xor32(float x) {
     uint32_t a, b;
     pair32(__float_as_uint(x), a, b);
