@@ -667,17 +667,26 @@ __global__ __launch_bounds__(kScoreThreads, 3) void score_loop_kernel(ScoreArgs 
     const int ch0 = (lane % LPL) * C;
 
     const int g = a.page_size / a.logical_page;
-    const int m0 = blk * a.pages_per_block;
+    const int m0 = blk * a.pages_per_block;       // < max_pages
     const int j0 = m0 * g;
-    const int L = a.seq_lens[b];
     const int G = a.num_q_heads / a.num_kv_heads;
+    const size_t slot_kv = pool_slot(a.hm, kv);
+    // seq_lens, the page-table entries of the workgroup's whole range (the
+    // row holds max_pages entries; those past the sequence go unused) and,
+    // for bf16 / f32 pools, the query are loaded together: one round trip
+    // before the ring instead of two
+    const int L = a.seq_lens[b];
+    const int m_cap = min(a.pages_per_block, a.max_pages - m0);
+    for (int i = threadIdx.x; i < m_cap; i += kScoreThreads)
+        s_hp[i] = (unsigned long long)a.page_table[(size_t)b * a.max_pages + m0 + i] * a.hm.pool_heads + slot_kv;
+    double qp[C], qn[C];                          // Qp, Qn of this lane's channels ch0 ..
+    if constexpr (KV_DT != LSA_INT4) load_q_pos_neg<C>(a, b, kv, ch0, 0, G, qp, qn);
     const int n_pages = (L + a.page_size - 1) / a.page_size;
     if (m0 < n_pages) {                           // (uniform: a workgroup past the last page only arrives)
     const int m1 = min(m0 + a.pages_per_block, n_pages);
     const int nlog = (L + a.logical_page - 1) / a.logical_page;
     const int j1 = min(m1 * g, nlog);
     const int j_cur = (L - 1) / a.logical_page;   // the logical page that holds the current token
-    const size_t slot_kv = pool_slot(a.hm, kv);
     // g, the statistics of one (page, head) unit (g * D bytes for int4, g * 2D
     // elements otherwise) and the row of a logical page are powers of two:
     // addresses are shifts
@@ -685,9 +694,6 @@ __global__ __launch_bounds__(kScoreThreads, 3) void score_loop_kernel(ScoreArgs 
     const int unit_shift = gs + __builtin_ctz(D) + (KV_DT == LSA_INT4 ? 0 : 1 + __builtin_ctz(EB));
     const int row_shift = __builtin_ctz(D) + (KV_DT == LSA_INT4 ? 0 : 1 + __builtin_ctz(EB));
 
-    for (int i = threadIdx.x; i < m1 - m0; i += kScoreThreads)
-        s_hp[i] = (unsigned long long)a.page_table[(size_t)b * a.max_pages + m0 + i] * a.hm.pool_heads + slot_kv;
-    double qp[C], qn[C];                          // Qp, Qn of this lane's channels ch0 ..
     double qsum = 0.0;                            // int4 only: sum over all channels of Qp + Qn
     // int4: whether every Qp and -Qn term is an integer below 2^32 on the grid
     // 2^lo (bf16 queries of ordinary range span about 21 bits); s_qint then
@@ -696,7 +702,6 @@ __global__ __launch_bounds__(kScoreThreads, 3) void score_loop_kernel(ScoreArgs 
     int lo = 0;
     __shared__ uint32_t s_qint[2 * 128];
     if constexpr (KV_DT != LSA_INT4) {
-        load_q_pos_neg<C>(a, b, kv, ch0, 0, G, qp, qn);
         __syncthreads();
     } else {
         // thread t forms one term once for the workgroup: side t / D (0: Qp,
