@@ -424,17 +424,22 @@ __global__ __launch_bounds__(512, 2) void prefill_bf16_kernel(PrefillArgs p) {
                 pb[2 * kt + st] = __builtin_bit_cast(bf16x8, make_uint4(pk[0], pk[1], pk[2], pk[3]));
             }
     };
-    // O^T += V^T P^T over the tile in V buffer vl; k-step (kt, st) covers keys 32*kt + 16*st + 8*lg + j
-    auto pv = [&](const uint16_t *vl, const bf16x8 (&pb)[4]) {
+    // O^T += V^T P^T over the tile in V buffer vl; k-step (kt, st) covers keys 32*kt + 16*st + 8*lg + j.
+    // The A operands of the first k-step come in `first`, read before the
+    // barrier that opens the MFMA phase (the tile has long landed), so the
+    // phase's first products do not wait for LDS.
+    auto v_at = [&](const uint16_t *vl, int kt, int st, int dt) {
+        const int ch = 32 * dt + col, c = 2 * st + lg;
+        return __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4 *>(&vl[(kt * D + ch) * 32 + ((c ^ swz(ch)) << 3)]));
+    };
+    auto pv = [&](const uint16_t *vl, const bf16x8 (&pb)[4], const bf16x8 (&first)[D / 32]) {
 #pragma unroll
         for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
             for (int st = 0; st < 2; ++st)
 #pragma unroll
                 for (int dt = 0; dt < D / 32; ++dt) {
-                    const int ch = 32 * dt + col, c = 2 * st + lg;
-                    const bf16x8 va = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4 *>(
-                        &vl[(kt * D + ch) * 32 + ((c ^ swz(ch)) << 3)]));
+                    const bf16x8 va = kt == 0 && st == 0 ? first[dt] : v_at(vl, kt, st, dt);
                     o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pb[2 * kt + st], o[dt], 0, 0, 0);
                 }
     };
@@ -496,10 +501,14 @@ __global__ __launch_bounds__(512, 2) void prefill_bf16_kernel(PrefillArgs p) {
         // query tile.  ii > 0 is known in three of the four unrolled steps.
         const bool prev_ok = (B != 0 || ii > 0) && (QT == 1 ? head_ok : sees(c_prev));
         const bool cur_ok = QT == 1 ? head_ok : sees(c_cur);
-        bf16x8 pb[4];
-        if (prev_ok) softmax_p(s_prev, tile_id(c_prev) * kTile, QT > 1 && tile_id(c_prev) == a_s, pb);
+        bf16x8 pb[4], vfirst[D / 32];
+        if (prev_ok) {
+            softmax_p(s_prev, tile_id(c_prev) * kTile, QT > 1 && tile_id(c_prev) == a_s, pb);
+#pragma unroll
+            for (int dt = 0; dt < D / 32; ++dt) vfirst[dt] = v_at(vbuf(Prev{}), 0, 0, dt);
+        }
         bar();
-        if (prev_ok) pv(vbuf(Prev{}), pb);
+        if (prev_ok) pv(vbuf(Prev{}), pb, vfirst);
         if (cur_ok) qk(kbuf(b), s_cur);
         // K(ii+1) and V(ii) have landed and this wavefront's LDS reads are
         // done; this step's own fetches may still be in flight
@@ -532,10 +541,12 @@ __global__ __launch_bounds__(512, 2) void prefill_bf16_kernel(PrefillArgs p) {
     __syncthreads();
     if (head_ok && (QT == 1 || sees(c_last))) {
         const bool diag = QT == 1 || tile_id(c_last) == a_s;
-        bf16x8 pb[4];
+        bf16x8 pb[4], vfirst[D / 32];
         if ((n_iter - 1) & 1) softmax_p(sb, tile_id(c_last) * kTile, diag, pb);
         else softmax_p(sa, tile_id(c_last) * kTile, diag, pb);
-        pv(vl_last, pb);
+#pragma unroll
+        for (int dt = 0; dt < D / 32; ++dt) vfirst[dt] = v_at(vl_last, 0, 0, dt);
+        pv(vl_last, pb, vfirst);
     }
 
     if (p.tile_counter) {
