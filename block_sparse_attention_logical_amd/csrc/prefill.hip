@@ -432,16 +432,14 @@ __global__ __launch_bounds__(512, 2) void prefill_bf16_kernel(PrefillArgs p) {
         const int ch = 32 * dt + col, c = 2 * st + lg;
         return __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4 *>(&vl[(kt * D + ch) * 32 + ((c ^ swz(ch)) << 3)]));
     };
-    auto pv = [&](const uint16_t *vl, const bf16x8 (&pb)[4], const bf16x8 (&first)[D / 32]) {
+    auto pv = [&](const uint16_t *vl, const bf16x8 (&pb)[4], const bf16x8 (&first)[4]) {
 #pragma unroll
-        for (int kt = 0; kt < 2; ++kt)
+        for (int dt = 0; dt < D / 32; ++dt)
 #pragma unroll
-            for (int st = 0; st < 2; ++st)
-#pragma unroll
-                for (int dt = 0; dt < D / 32; ++dt) {
-                    const bf16x8 va = kt == 0 && st == 0 ? first[dt] : v_at(vl, kt, st, dt);
-                    o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pb[2 * kt + st], o[dt], 0, 0, 0);
-                }
+            for (int ks = 0; ks < 4; ++ks) {
+                const bf16x8 va = dt == 0 ? first[ks] : v_at(vl, ks >> 1, ks & 1, dt);
+                o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pb[ks], o[dt], 0, 0, 0);
+            }
     };
 
     // s_waitcnt immediates (vmcnt in bits 3:0 and 15:14, expcnt 6:4, lgkmcnt
@@ -501,11 +499,11 @@ __global__ __launch_bounds__(512, 2) void prefill_bf16_kernel(PrefillArgs p) {
         // query tile.  ii > 0 is known in three of the four unrolled steps.
         const bool prev_ok = (B != 0 || ii > 0) && (QT == 1 ? head_ok : sees(c_prev));
         const bool cur_ok = QT == 1 ? head_ok : sees(c_cur);
-        bf16x8 pb[4], vfirst[D / 32];
+        bf16x8 pb[4], vfirst[4];
         if (prev_ok) {
             softmax_p(s_prev, tile_id(c_prev) * kTile, QT > 1 && tile_id(c_prev) == a_s, pb);
 #pragma unroll
-            for (int dt = 0; dt < D / 32; ++dt) vfirst[dt] = v_at(vbuf(Prev{}), 0, 0, dt);
+            for (int ks = 0; ks < 4; ++ks) vfirst[ks] = v_at(vbuf(Prev{}), ks >> 1, ks & 1, 0);
         }
         bar();
         if (prev_ok) pv(vbuf(Prev{}), pb, vfirst);
@@ -541,11 +539,11 @@ __global__ __launch_bounds__(512, 2) void prefill_bf16_kernel(PrefillArgs p) {
     __syncthreads();
     if (head_ok && (QT == 1 || sees(c_last))) {
         const bool diag = QT == 1 || tile_id(c_last) == a_s;
-        bf16x8 pb[4], vfirst[D / 32];
+        bf16x8 pb[4], vfirst[4];
         if ((n_iter - 1) & 1) softmax_p(sb, tile_id(c_last) * kTile, diag, pb);
         else softmax_p(sa, tile_id(c_last) * kTile, diag, pb);
 #pragma unroll
-        for (int dt = 0; dt < D / 32; ++dt) vfirst[dt] = v_at(vl_last, 0, 0, dt);
+        for (int ks = 0; ks < 4; ++ks) vfirst[ks] = v_at(vl_last, ks >> 1, ks & 1, 0);
         pv(vl_last, pb, vfirst);
     }
 
