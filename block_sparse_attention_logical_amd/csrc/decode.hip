@@ -751,7 +751,10 @@ __global__ __launch_bounds__(kDecodeWaves * kWave, decode_waves_per_simd(KVT, NP
                 if constexpr (I4) {
                     const float svt = sv[jt[jj >> 2]];
                     u = __builtin_bit_cast(uint32_t, __builtin_convertvector(floatx2{pa * svt, pb * svt}, bf16x2));
-                    fed[jj >> 2] += bf16_lo(u) + bf16_hi(u);
+                    // the two fed weights, summed by one v_dot2 against (1, 1)
+                    fed[jj >> 2] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, u),
+                                                                   __builtin_bit_cast(bf16x2, 0x3F803F80u),
+                                                                   fed[jj >> 2], false);
                 } else {
                     u = __builtin_bit_cast(uint32_t, __builtin_convertvector(floatx2{pa, pb}, bf16x2));
                 }
