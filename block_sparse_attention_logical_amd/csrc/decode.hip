@@ -714,10 +714,11 @@ __global__ __launch_bounds__(kDecodeWaves * kWave, decode_waves_per_simd(KVT, NP
             // 16 + 4*g4 + r (x[4 + r]) of the block, r = 0..3
             float x[8];
             if constexpr (I4) {
-                const float off0 = (128.f + zk[jt[0]]) * qsum, off1 = (128.f + zk[jt[1]]) * qsum;
+                // (s - off) * sc as one fma per logit, with off * sc formed once per tile
                 const float sc0 = sk[jt[0]] * a.scale_log2, sc1 = sk[jt[1]] * a.scale_log2;
+                const float noff0 = -((128.f + zk[jt[0]]) * qsum) * sc0, noff1 = -((128.f + zk[jt[1]]) * qsum) * sc1;
 #pragma unroll
-                for (int r = 0; r < 4; ++r) { x[r] = (s0[r] - off0) * sc0; x[4 + r] = (s1[r] - off1) * sc1; }
+                for (int r = 0; r < 4; ++r) { x[r] = fmaf(s0[r], sc0, noff0); x[4 + r] = fmaf(s1[r], sc1, noff1); }
             } else {
 #pragma unroll
                 for (int r = 0; r < 4; ++r) { x[r] = s0[r] * a.scale_log2; x[4 + r] = s1[r] * a.scale_log2; }
