@@ -28,6 +28,30 @@ def to_f64(t: torch.Tensor) -> np.ndarray:
 DTYPE_NAME = {F32: "f32", BF16: "bf16", INT4: "int4"}
 
 
+def bf16_half_ulp(x: np.ndarray) -> np.ndarray:
+    """Half a unit in the last place of bf16 (8 significant bits) at |x|: the
+    rounding error a bf16 output carries even when computed exactly."""
+    a = np.abs(np.asarray(x, dtype=np.float64))
+    e = np.floor(np.log2(np.where(a > 0, a, 1.0))).astype(np.int64)
+    return np.where(a > 0, np.ldexp(1.0, e - 8), 0.0)
+
+
+# Tracked level for rounding_excess on the bf16 and int4 paths, asserted
+# beside the 2e-2 bound: the worst values the suite reaches are 0.0067 (bf16
+# prefill), 0.0047 (int4 decode) and 0.0031 (bf16 decode), so an arithmetic
+# regression shows here well before the outputs reach the bound.
+EXCESS_TOL = 1e-2
+
+
+def rounding_excess(got: np.ndarray, ref: np.ndarray) -> float:
+    """The largest error of a bf16 output beyond its own final rounding:
+    max over elements of |got - ref| - half_ulp(ref).  This isolates the
+    arithmetic error of the path (bf16 probabilities, fp32 accumulation) from
+    the output format's, which alone reaches 2^-9 |ref| (0.0156 at |ref| in
+    [4, 8))."""
+    return float(np.max(np.abs(got - ref) - bf16_half_ulp(ref)))
+
+
 def kv_pool(w) -> lsa.KVPool:
     return lsa.KVPool(w.dtype, w.k, w.v, w.num_kv_heads, w.head_dim, w.page_size, w.logical_page, w.num_pages,
                       w.k_sz, w.v_sz)

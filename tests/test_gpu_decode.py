@@ -101,7 +101,7 @@ def check_window(w, kv_heads=None, batches=None, agg=lsa.AGG_SUM):
     page) and the outputs (within the tolerance) with the oracle."""
     r = Runner(w, agg)
     gpu = [H.to_f64(r.step(i)) for i in range(w.window)]
-    worst = 0.0
+    worst = excess = 0.0
     gaps = []
     for b in (range(w.batch) if batches is None else batches):
         oracle_sel = {}
@@ -115,6 +115,11 @@ def check_window(w, kv_heads=None, batches=None, agg=lsa.AGG_SUM):
                 err = np.max(np.abs(gpu[i][b, h] - ref[i][h]))
                 worst = max(worst, err)
                 assert err <= tol(w), (b, i, h, err)
+                if w.dtype != W.F32:
+                    excess = max(excess, H.rounding_excess(gpu[i][b, h], ref[i][h]))
+    if w.dtype != W.F32:
+        print(f"{H.DTYPE_NAME[w.dtype]} decode: max abs err {worst:.4f}, beyond the output's own rounding {excess:.4f}")
+        assert excess <= H.EXCESS_TOL, excess
     if gaps:
         print(f"selections checked bit for bit; smallest relative gap between the K-th and (K+1)-th page "
               f"scores: {min(gaps):.3e}")

@@ -79,7 +79,7 @@ def check_fused_window(w, agg=lsa.AGG_SUM, batches=None, kv_heads=None):
     gpu = [H.to_f64(r.step(i)) for i in range(w.window)]
     assert not any(np.isnan(g).any() for g in gpu)
     G = w.num_q_heads // w.num_kv_heads
-    worst = 0.0
+    worst = excess = 0.0
     for b in (range(w.batch) if batches is None else batches):
         sel = {}
         ref = D.oracle_window(w, b, kv_heads=kv_heads, agg=agg, selections=sel)
@@ -91,6 +91,12 @@ def check_fused_window(w, agg=lsa.AGG_SUM, batches=None, kv_heads=None):
                 err = np.max(np.abs(gpu[i][b, h] - ref[i][h]))
                 worst = max(worst, err)
                 assert err <= D.tol(w), (b, i, h, err)
+                if w.dtype != W.F32:
+                    excess = max(excess, H.rounding_excess(gpu[i][b, h], ref[i][h]))
+    if w.dtype != W.F32:
+        print(f"{H.DTYPE_NAME[w.dtype]} decode step: max abs err {worst:.4f}, beyond the output's own rounding "
+              f"{excess:.4f}")
+        assert excess <= H.EXCESS_TOL, excess
     s3 = StepRunner(w, fused=False, agg=agg)
     for i in range(w.window):
         s3.step(i)

@@ -45,7 +45,7 @@ def expected_tiles(p):
 def check(p, out, rows=None, heads=None, tol=2e-2):
     G = p.num_q_heads // p.num_kv_heads
     got = H.to_f64(out)
-    worst = 0.0
+    worst = excess = 0.0
     for kv in range(p.num_kv_heads):
         hs = [kv * G + h for h in range(G)]
         if heads is not None:
@@ -61,6 +61,11 @@ def check(p, out, rows=None, heads=None, tol=2e-2):
             err = np.max(np.abs(g - ref))
             worst = max(worst, err)
             assert err <= tol, (kv, h, err)
+            if p.dtype == W.BF16:
+                excess = max(excess, H.rounding_excess(g, ref))
+    if p.dtype == W.BF16:
+        print(f"bf16 prefill: max abs err {worst:.4f}, beyond the output's own rounding {excess:.4f}")
+        assert excess <= H.EXCESS_TOL, excess
     return worst
 
 
@@ -189,7 +194,7 @@ def run_prefill_csr(p, masks, scheduled=True):
 def check_mask(p, out, masks, heads=None, rows=None, tol=2e-2):
     G = p.num_q_heads // p.num_kv_heads
     got = H.to_f64(out)
-    worst = 0.0
+    worst = excess = 0.0
     for kv in range(p.num_kv_heads):
         hs = [kv * G + h for h in range(G) if heads is None or kv * G + h in heads]
         if not hs:
@@ -202,6 +207,11 @@ def check_mask(p, out, masks, heads=None, rows=None, tol=2e-2):
             err = np.max(np.abs(g - ref))
             worst = max(worst, err)
             assert err <= tol, (kv, h, err)
+            if p.dtype == W.BF16:
+                excess = max(excess, H.rounding_excess(g, ref))
+    if p.dtype == W.BF16:
+        print(f"bf16 prefill: max abs err {worst:.4f}, beyond the output's own rounding {excess:.4f}")
+        assert excess <= H.EXCESS_TOL, excess
     return worst
 
 
