@@ -432,3 +432,31 @@ def test_decode_ignores_values_past_the_current_token(cfg):
         for (i, kv), expect in sel.items():
             assert np.array_equal(r.history[i][b, kv], expect)
         assert np.max(np.abs(gpu[b] - ref[0])) <= tol(w)
+
+
+@pytest.mark.parametrize("cfg", [2, 5])
+def test_decode_records_never_leak_between_calls(cfg):
+    """The split-KV records and the selection's physical scores pass between
+    the workgroups of one launch through the workspace.  Here every step of a
+    window is followed, on the same workspaces, by a selection and an attention
+    call for other queries (the outputs of those calls are discarded), so the
+    workspaces hold another call's records and scores whenever the next step
+    starts; a read of a record or score before its store lands would then see
+    different values.  The window's selections and outputs must equal those of
+    the same window run without the interleaved calls, bit for bit."""
+    w = W.make_decode(cfg, DEV, batch=3, ctx=[700, 2100, 1500])
+    plain, mixed = Runner(w), Runner(w)
+    other = torch.flip(w.q[w.window - 1], dims=[1]).contiguous()   # queries no step uses
+    sel_other = torch.full_like(mixed.selected, -1)
+    scratch = torch.empty_like(w.q[0])
+    for i in range(w.window):
+        a = plain.step(i)
+        b = mixed.step(i)
+        assert torch.equal(a.view(torch.int16), b.view(torch.int16)), i
+        assert np.array_equal(plain.history[-1], mixed.history[-1]), i
+        lens = w.seq_lens(i)
+        lsa.select_pages(other, mixed.kv, mixed.stats, w.page_table, lens, mixed.hd, w.token_budget, 0,
+                         w.reuse_interval, sel_other, mixed.ws_sel)
+        lsa.sparse_decode_attn(other, mixed.kv, w.page_table, lens, mixed.hd, sel_other, w.token_budget,
+                               scratch, mixed.ws_dec)
+    torch.cuda.synchronize()
