@@ -252,8 +252,8 @@ __device__ __forceinline__ void wave_minmax_d(double &lo, double &hi) {
 
 // The K largest of the n = ceil(L / N_P) scores P[0..n) into out, ascending by
 // page, ties to the lower page, -1 padded; NT threads, PT pages per thread
-// (NT * PT >= max_pages).  AGENT: P was written by other workgroups of this
-// launch and is read with agent-scope loads.
+// (NT * PT >= max_pages - 1).  AGENT: P was written by other workgroups of
+// this launch and is read with agent-scope loads.
 //
 // The threshold T, the K-th largest score, is found by value: the scores
 // still in question are binned linearly between their minimum and maximum
@@ -266,6 +266,12 @@ __device__ __forceinline__ void wave_minmax_d(double &lo, double &hi) {
 // meet on one counter.  Pages with scores above T are taken, and of the
 // pages scoring exactly T the lowest ones, K in all, in one ordered
 // compaction.
+// One page past the NT * PT the threads hold (n = NT * PT + 1, which the
+// host allows with the group's scores summed at 4 or 8 pages per thread) is
+// ranked apart: it is the last page, n - 1, the highest index, so it loses
+// every tie.  The K largest of the others are found as above; the last page joins
+// them exactly when its score is above their K-th largest T, and the
+// lowest-ranked of them (score T, the highest such page taken) then leaves.
 constexpr int kTopkBins = 1024;
 constexpr int kTopkCand = 16;
 
@@ -282,16 +288,18 @@ __device__ __forceinline__ void topk_rows(const double *P, int L, int page_size,
     __shared__ uint32_t wave_tot[NW];
     const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
 
-    // thread t owns the contiguous pages [t*seg, t*seg + cnt), seg = ceil(n /
-    // NT) <= PT; their scores are loaded together
+    // thread t owns the contiguous pages [t*seg, t*seg + cnt) of the ns held
+    // in registers, seg = ceil(ns / NT) <= PT; their scores are loaded together
     const int n = (L + page_size - 1) / page_size;
     if (n <= K) {                                 // every page, ascending, padded with -1
         for (int i = tid; i < K; i += NT) out[i] = i < n ? i : -1;
         return;
     }
-    const int seg = (n + NT - 1) / NT;
-    const int i0 = min(n, tid * seg);
-    const int cnt = min(n, i0 + seg) - i0;
+    const bool extra = n > NT * PT;               // (then n == NT * PT + 1: the host's bound)
+    const int ns = extra ? n - 1 : n;
+    const int seg = (ns + NT - 1) / NT;
+    const int i0 = min(ns, tid * seg);
+    const int cnt = min(ns, i0 + seg) - i0;
     double sc[PT];
 #pragma unroll
     for (int e = 0; e < PT; ++e) {
@@ -299,6 +307,8 @@ __device__ __forceinline__ void topk_rows(const double *P, int L, int page_size,
         if (e < cnt) v = AGENT ? load_agent_d(P + i0 + e) : P[i0 + e];
         sc[e] = v + 0.0;                          // -0 -> +0
     }
+    double x_last = 0.0;                          // the score of page n - 1 when it is ranked apart
+    if (extra) x_last = (AGENT ? load_agent_d(P + n - 1) : P[n - 1]) + 0.0;
     uint32_t act = cnt >= 32 ? ~0u : (1u << cnt) - 1u;   // pages still in question
     uint32_t need = (uint32_t)K;                  // how many of them are taken
     double T;
@@ -381,6 +391,11 @@ __device__ __forceinline__ void topk_rows(const double *P, int L, int page_size,
         __syncthreads();                          // (every thread has read hist[bstar])
     }
 
+    // the last page ranked apart joins when it beats T; one page scoring T leaves
+    // (need_eq >= 1: T is the K-th largest of the others)
+    const bool take_last = extra && x_last > T;
+    if (take_last) --need_eq;
+
     // ordered compaction
     uint32_t c = 0;                               // low 16 bits: greater, high 16 bits: equal
 #pragma unroll
@@ -400,6 +415,7 @@ __device__ __forceinline__ void topk_rows(const double *P, int L, int page_size,
             ++eq_before;
         }
     }
+    if (take_last && tid == 0) out[K - 1] = n - 1;   // the highest page index: the last slot
 }
 
 // PT: pages per thread, the smallest power of two with kTopkThreads * PT >=
@@ -1078,13 +1094,21 @@ int topk_max_pages() { return kTopkThreads * kTopkPerThread; }
 
 int score_fused_pt(int max_pages, bool agg_max) {
     const int per = (max_pages + kScoreThreads - 1) / kScoreThreads;
+    // With the group's scores summed, topk_rows ranks one page past the
+    // threads' pages apart, so a sequence of 1025 or 2049 pages (config 2 at
+    // 64K tokens plus its window) ranks at 4 or 8 pages per thread instead of
+    // 8 or 16: config 2's selection call 20.5 -> 19.6 us.  At 16 per thread it
+    // does not pay: config 5's 4097 pages ranked in the score kernel that way
+    // took 42.4 us per call against 39.8 with the separate kernel (the
+    // instance holds 168 VGPRs and spills to scratch in its ranking).
     // (32 pages per thread cost the max-aggregation kernel a wavefront per
     // SIMD; in the sum kernel one 256-thread ranking of 4097 pages at the end
     // took longer than the separate 1024-thread kernel: 62.9 against 51.9 us
     // per int4 selection call at 256K tokens with the radix ranking, 52.7
     // against 39.2 us with the value-binned one, whose 32 scores per thread
     // spill at the 168-register bound)
-    (void)agg_max;
+    const int held = (max_pages - 1 + kScoreThreads - 1) / kScoreThreads;
+    if (!agg_max && held <= 8) return held <= 4 ? 4 : 8;
     return per <= 4 ? 4 : per <= 8 ? 8 : per <= 16 ? 16 : 0;
 }
 

@@ -269,6 +269,46 @@ def test_select_either_side_of_one_kernel_limit(cfg, pages, agg):
 
 
 
+@pytest.mark.parametrize("cfg,pages", [(2, 1025), (2, 2049), (5, 1025), (5, 2049)])
+@pytest.mark.parametrize("mode", ["all-equal", "last-high", "random"])
+def test_select_last_page_ranked_apart(cfg, pages, mode):
+    """With the group's scores summed, the fused ranking holds 4 or 8 pages per
+    thread of its 256 threads and ranks one more page apart, the last one
+    (1025 or 2049 pages): it joins the K largest of the others when its
+    score is above their K-th largest, and loses a tie to them.  Every key the
+    same (all pages tie: pages 0 .. K-1 win), the last page's keys scaled up
+    (it ranks first and takes the last slot), and the ordinary data; bit for
+    bit against the oracle."""
+    w = W.make_decode(cfg, DEV, batch=1, ctx=[pages * 64 - 4])
+    lens = [w.ctx[0] + 1]
+    n = -(-lens[0] // w.page_size)
+    assert n == pages
+    tbl = w.page_table[0, :n].long()
+    if mode == "all-equal":
+        if w.k_sz is None:
+            w.k[tbl] = 1.0
+        else:
+            w.k[tbl] = 0x35
+            w.k_sz[tbl] = w.k_sz[tbl[0]].clone()
+    elif mode == "last-high":
+        if w.k_sz is None:
+            w.k[tbl[-1]] = (w.k[tbl[-1]].float() * 8).to(w.k.dtype)
+        else:
+            w.k_sz[tbl[-1], :, 0] *= 8
+    sel = run_select(w, 0, lens)
+    check_selection(w, 0, lens, sel)
+    K = w.token_budget // w.page_size
+    got = sel.cpu().numpy()
+    for kv in range(w.num_kv_heads):
+        if w.head_kind[kv] == 0:
+            if mode == "all-equal":
+                assert list(got[0, kv]) == list(range(K)), kv
+            elif mode == "last-high":
+                assert got[0, kv, K - 1] == n - 1, kv
+    del w
+    torch.cuda.empty_cache()
+
+
 @pytest.mark.parametrize("mode", ["wide-span", "zero-group", "ordinary"])
 def test_select_int4_query_terms_and_the_integer_grid(mode):
     """int4 scoring takes a group's folded query terms (Qp, -Qn) as integers on
