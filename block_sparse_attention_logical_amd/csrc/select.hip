@@ -267,8 +267,8 @@ __device__ __forceinline__ void wave_minmax_d(double &lo, double &hi) {
 // pages scoring exactly T the lowest ones, K in all, in one ordered
 // compaction.
 // One page past the NT * PT the threads hold (n = NT * PT + 1, which the
-// host allows with the group's scores summed at 4 or 8 pages per thread) is
-// ranked apart: it is the last page, n - 1, the highest index, so it loses
+// host allows in the score kernel with the group's scores summed at 4 or 8
+// pages per thread, and in the separate top-K kernel) is ranked apart: it is the last page, n - 1, the highest index, so it loses
 // every tie.  The K largest of the others are found as above; the last page joins
 // them exactly when its score is above their K-th largest T, and the
 // lowest-ranked of them (score T, the highest such page taken) then leaves.
@@ -418,16 +418,18 @@ __device__ __forceinline__ void topk_rows(const double *P, int L, int page_size,
     if (take_last && tid == 0) out[K - 1] = n - 1;   // the highest page index: the last slot
 }
 
-// PT: pages per thread, the smallest power of two with kTopkThreads * PT >=
-// max_pages (every per-page loop is unrolled over PT slots).
-template <int PT>
-__global__ __launch_bounds__(kTopkThreads) void topk_kernel(TopkArgs a) {
+// NT threads, PT pages per thread: the smallest power of two with NT * PT >=
+// max_pages - 1 (every per-page loop is unrolled over PT slots; a last page
+// past NT * PT is ranked apart).  Config 5's 4097 pages then rank at 4 per
+// thread: 38.4-38.8 us per selection call against 39.3-39.5 at 8 per thread;
+// 256 threads at 16 per thread took 41.5-42.1 us.
+template <int NT, int PT>
+__global__ __launch_bounds__(NT) void topk_kernel(TopkArgs a) {
     const int r = blockIdx.x % a.n_ret;
     const int b = blockIdx.x / a.n_ret;
     const int kv = retrieval_head(a.hm, r);
-    topk_rows<kTopkThreads, PT, false>(a.phys + ((size_t)b * a.num_kv_heads + kv) * a.max_pages, a.seq_lens[b],
-                                       a.page_size, a.max_pages, a.k,
-                                       a.selected + ((size_t)b * a.num_kv_heads + kv) * a.k);
+    topk_rows<NT, PT, false>(a.phys + ((size_t)b * a.num_kv_heads + kv) * a.max_pages, a.seq_lens[b], a.page_size,
+                             a.max_pages, a.k, a.selected + ((size_t)b * a.num_kv_heads + kv) * a.k);
 }
 
 // KV_DT: LSA_F32, LSA_BF16 (stats in that type) or LSA_INT4 (code stats).
@@ -1123,13 +1125,13 @@ hipError_t launch_score(const ScoreArgs &a, hipStream_t s) {
 hipError_t launch_topk(const TopkArgs &a, hipStream_t s) {
     const long long grid = (long long)a.batch * a.n_ret;
     if (grid == 0) return hipSuccess;
-    const int per = (a.max_pages + kTopkThreads - 1) / kTopkThreads;
+    const int per = (a.max_pages - 1 + kTopkThreads - 1) / kTopkThreads;   // (at least 1: max_pages > 4096 here)
     const dim3 g((unsigned)grid), blk(kTopkThreads);
-    if (per <= 1) hipLaunchKernelGGL(topk_kernel<1>, g, blk, 0, s, a);
-    else if (per <= 2) hipLaunchKernelGGL(topk_kernel<2>, g, blk, 0, s, a);
-    else if (per <= 4) hipLaunchKernelGGL(topk_kernel<4>, g, blk, 0, s, a);
-    else if (per <= 8) hipLaunchKernelGGL(topk_kernel<8>, g, blk, 0, s, a);
-    else hipLaunchKernelGGL(topk_kernel<kTopkPerThread>, g, blk, 0, s, a);
+    if (per <= 1) hipLaunchKernelGGL((topk_kernel<kTopkThreads, 1>), g, blk, 0, s, a);
+    else if (per <= 2) hipLaunchKernelGGL((topk_kernel<kTopkThreads, 2>), g, blk, 0, s, a);
+    else if (per <= 4) hipLaunchKernelGGL((topk_kernel<kTopkThreads, 4>), g, blk, 0, s, a);
+    else if (per <= 8) hipLaunchKernelGGL((topk_kernel<kTopkThreads, 8>), g, blk, 0, s, a);
+    else hipLaunchKernelGGL((topk_kernel<kTopkThreads, kTopkPerThread>), g, blk, 0, s, a);
     return hipGetLastError();
 }
 
