@@ -156,7 +156,8 @@ size_t decode_counter_bytes(int batch, int num_kv_heads) { return align_up((size
 // one round takes smaller chunks while it still fits, its last workgroups
 // still merge a head's records in one batch, and at least three of a
 // workgroup's four wavefronts still have pages: workgroups reach the CUs one
-// per CU per round, so config 2's 384 workgroups of 8 pages put 16 pages on
+// per CU per round, so the 384 workgroups of 8 pages of a B = 8, 64K-token
+// layer (8 KV heads, half of them streaming, a 4096-token budget) put 16 pages on
 // half of the CUs, whose second workgroups then finish their streams about
 // 5 us after the others (448 workgroups of 6 pages: at most 12 pages per CU;
 // 21.5 us per launch against 23.1).  Chunks that leave two wavefronts idle

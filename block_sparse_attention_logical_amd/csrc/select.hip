@@ -65,19 +65,19 @@ constexpr int kScoreThreads = 256;
 // three wavefronts fit per SIMD (at most 168 VGPRs), which hides one
 // wavefront's statistics loads behind another's arithmetic:
 // - int4 (a lane holds 16 channels of fp64 query terms): seven pages
-//   (config 5: 102 us per score launch at eight pages and two wavefronts per
-//   SIMD, 90 at six, 87 at seven);
+//   (16 sequences x 4 heads at 256K tokens: 102 us per score launch at eight
+//   pages and two wavefronts per SIMD, 90 at six, 87 at seven);
 // - bf16: eleven, fewer and fuller workgroups; 44 physical pages per
 //   workgroup put a 1025-page selection of 8 sequences x 4 heads in 768
-//   workgroups, one per slot of the chip (config 2: 29.1 us per score launch
-//   at eight, 28.4 at ten, 26.8 at eleven);
+//   workgroups, one per slot of the chip (29.1 us per score launch at
+//   eight, 28.4 at ten, 26.8 at eleven);
 // - with the 16-pages-per-thread top-K fused in, one page fewer each (one
 //   more would cross 168 VGPRs);
 // - max aggregation keeps the packed statistics across one pass per query
-//   head: bf16 fits three wavefronts per SIMD at six pages (160 VGPRs;
-//   config 2: 42.9 us per selection against 46.8 at ten and 45.0 at nine,
-//   both at two wavefronts per SIMD); int4 needs over 200 VGPRs at any
-//   count and keeps six.
+//   head: bf16 fits three wavefronts per SIMD at six pages (160 VGPRs; 8
+//   sequences x 4 heads at 64K tokens: 42.9 us per selection against 46.8
+//   at ten and 45.0 at nine, both at two wavefronts per SIMD); int4 needs
+//   over 200 VGPRs at any count and keeps six.
 constexpr int score_iters(int kv_dtype, int fused_pt, bool agg_max) {
     if (kv_dtype == LSA_INT4) return agg_max || fused_pt == 16 ? 6 : 7;
     if (kv_dtype == LSA_BF16) return agg_max ? 6 : fused_pt == 16 ? 10 : 11;
@@ -268,10 +268,11 @@ __device__ __forceinline__ void wave_minmax_d(double &lo, double &hi) {
 // compaction.
 // One page past the NT * PT the threads hold (n = NT * PT + 1, which the
 // host allows in the score kernel with the group's scores summed at 4 or 8
-// pages per thread, and in the separate top-K kernel) is ranked apart: it is the last page, n - 1, the highest index, so it loses
-// every tie.  The K largest of the others are found as above; the last page joins
-// them exactly when its score is above their K-th largest T, and the
-// lowest-ranked of them (score T, the highest such page taken) then leaves.
+// pages per thread, and in the separate top-K kernel) is ranked apart: it is
+// the last page, n - 1, the highest index, so it loses every tie.  The K
+// largest of the others are found as above; the last page joins them exactly
+// when its score is above their K-th largest T, and the lowest-ranked of them
+// (score T, the highest such page taken) then leaves.
 constexpr int kTopkBins = 1024;
 constexpr int kTopkCand = 16;
 
@@ -420,9 +421,10 @@ __device__ __forceinline__ void topk_rows(const double *P, int L, int page_size,
 
 // NT threads, PT pages per thread: the smallest power of two with NT * PT >=
 // max_pages - 1 (every per-page loop is unrolled over PT slots; a last page
-// past NT * PT is ranked apart).  Config 5's 4097 pages then rank at 4 per
-// thread: 38.4-38.8 us per selection call against 39.3-39.5 at 8 per thread;
-// 256 threads at 16 per thread took 41.5-42.1 us.
+// past NT * PT is ranked apart).  The 4097 pages of a 256K-token sequence
+// plus its window then rank at 4 per thread (16 sequences x 4 heads, int4
+// statistics: 38.4-38.8 us per selection call against 39.3-39.5 at 8 per
+// thread; 256 threads at 16 per thread took 41.5-42.1 us).
 template <int NT, int PT>
 __global__ __launch_bounds__(NT) void topk_kernel(TopkArgs a) {
     const int r = blockIdx.x % a.n_ret;
@@ -1097,11 +1099,12 @@ int topk_max_pages() { return kTopkThreads * kTopkPerThread; }
 int score_fused_pt(int max_pages, bool agg_max) {
     const int per = (max_pages + kScoreThreads - 1) / kScoreThreads;
     // With the group's scores summed, topk_rows ranks one page past the
-    // threads' pages apart, so a sequence of 1025 or 2049 pages (config 2 at
-    // 64K tokens plus its window) ranks at 4 or 8 pages per thread instead of
-    // 8 or 16: config 2's selection call 20.5 -> 19.6 us.  At 16 per thread it
-    // does not pay: config 5's 4097 pages ranked in the score kernel that way
-    // took 42.4 us per call against 39.8 with the separate kernel (the
+    // threads' pages apart, so a sequence of 1025 or 2049 pages (64K tokens
+    // plus the decode window at 64-token pages) ranks at 4 or 8 pages per
+    // thread instead of 8 or 16: 8 sequences x 4 heads at 64K, 20.5 -> 19.6
+    // us per selection call.  At 16 per thread it does not pay: 4097 pages
+    // (16 sequences x 4 heads at 256K, int4) ranked in the score kernel that
+    // way took 42.4 us per call against 39.8 with the separate kernel (the
     // instance holds 168 VGPRs and spills to scratch in its ranking).
     // (32 pages per thread cost the max-aggregation kernel a wavefront per
     // SIMD; in the sum kernel one 256-thread ranking of 4097 pages at the end
